@@ -1,0 +1,218 @@
+"""Pins for the oracle's sampling step.
+
+"Softmax-free GPU sampling: Gumbel-max categorical sampling kernel" (mlxcel issue #900):
+  - section Background: argmax of logits/T plus Gumbel noise is an exact sample from the
+    softmax categorical law -> chi-square tests of the oracle's own draws against exact
+    softmax probabilities (section Regression guard: >= 1e6 draws, peaked / flat / bimodal /
+    masked shapes, T = 0.5 and 1.5; the acceptance threshold is documented below);
+  - masked tokens are never sampled; same seed -> same stream; T = 0 is greedy argmax.
+"HLG sampling -- a piecewise tone curve on the logits", section "Greedy is untouched".
+
+Acceptance threshold of every chi-square test here: cells whose expected count is below 5
+are pooled into one cell; the test fails when the upper-tail p-value is below 1e-3. Seeds are
+fixed, so each outcome is deterministic.
+
+A second, fully independent pure-Python implementation of the whole draw (Philox, counter
+layout, Gumbel map, curve, argmax) pins the oracle's sampled indices on tiny inputs.
+"""
+import math
+
+import numpy as np
+import pytest
+from scipy import stats
+
+from tests.test_oracle_philox import py_philox
+
+M32 = 0xFFFFFFFF
+
+
+def _softmax(v):
+    v = np.asarray(v, dtype=np.float64)
+    fin = np.isfinite(v)
+    p = np.zeros_like(v)
+    e = np.exp(v[fin] - v[fin].max())
+    p[fin] = e / e.sum()
+    return p
+
+
+def _chi2_pvalue(counts, probs, n):
+    exp = probs * n
+    keep = exp >= 5
+    c = list(counts[keep])
+    e = list(exp[keep])
+    if (~keep).any() and exp[~keep].sum() > 0:
+        c.append(counts[~keep].sum())
+        e.append(exp[~keep].sum())
+    c = np.array(c, dtype=np.float64)
+    e = np.array(e, dtype=np.float64)
+    chi2 = ((c - e) ** 2 / e).sum()
+    return stats.chi2.sf(chi2, len(c) - 1)
+
+
+N_DRAWS = 1_000_000
+
+
+@pytest.mark.parametrize("T", [0.5, 1.0, 1.5])
+def test_chi_square_linspace(oracle_mod, T):
+    """V = 16 logits linspace(-4, 4), 1e6 draws at offsets 0..1e6-1."""
+    from synth.workloads import chi_square_rows
+    x = chi_square_rows()
+    idx, _, _ = oracle_mod.sample(x[None, :], [T], [0xC0FFEE + int(10 * T)], [0], K=N_DRAWS)
+    counts = np.bincount(idx.ravel(), minlength=16)
+    assert counts.sum() == N_DRAWS
+    p = _chi2_pvalue(counts, _softmax(x / T), N_DRAWS)
+    assert p > 1e-3, p
+
+
+SHAPES = {
+    "peaked": lambda rng: np.concatenate([rng.normal(0, 1, 11), [6.0]]),
+    "flat": lambda rng: rng.normal(0, 0.1, 12),
+    "bimodal": lambda rng: np.where(rng.random(12) < 0.5, rng.normal(-2, 1, 12), rng.normal(2, 0.5, 12)),
+    "masked": lambda rng: np.where(np.arange(12) % 3 == 0, -np.inf, rng.normal(0, 1.5, 12)),
+}
+
+
+@pytest.mark.parametrize("shape", sorted(SHAPES))
+@pytest.mark.parametrize("T", [0.5, 1.5])
+def test_chi_square_shapes(oracle_mod, shape, T):
+    rng = np.random.default_rng(hash(shape) % 1000)
+    x = SHAPES[shape](rng)
+    n = 200_000
+    idx, _, _ = oracle_mod.sample(x[None, :], [T], [77], [5], K=n)
+    counts = np.bincount(idx.ravel(), minlength=x.size)
+    probs = _softmax(x / T)
+    assert np.all(counts[~np.isfinite(x)] == 0)
+    assert _chi2_pvalue(counts, probs, n) > 1e-3
+
+
+@pytest.mark.parametrize("T", [0.5, 1.5])
+def test_chi_square_with_curve(oracle_mod, T):
+    """With the curve on, draws follow softmax(l'/T), l' = g(log-softmax(x) - mu)."""
+    rng = np.random.default_rng(21)
+    x = np.concatenate([rng.normal(0, 2, 15), [-np.inf]])
+    mu = np.float32(-3.0)
+    hlg = (1.5, 1.0, 1.0, 2.0)
+    lp = oracle_mod.hlg_transform(x[None, :], [mu], *hlg)[0]
+    n = 400_000
+    idx, _, _ = oracle_mod.sample(x[None, :], [T], [99], [0], K=n, mu=[mu], hlg=hlg)
+    counts = np.bincount(idx.ravel(), minlength=x.size)
+    assert counts[-1] == 0
+    assert _chi2_pvalue(counts, _softmax(lp / T), n) > 1e-3
+
+
+def test_two_token_closed_form(oracle_mod):
+    """V = 2: P(token 1) = sigmoid((x1 - x0) / T)."""
+    x = np.array([[0.3, 1.1]])
+    T = 0.8
+    n = 400_000
+    idx, _, _ = oracle_mod.sample(x, [T], [5], [0], K=n)
+    p = 1 / (1 + math.exp(-(1.1 - 0.3) / T))
+    phat = idx.mean()
+    assert abs(phat - p) < 4.5 * math.sqrt(p * (1 - p) / n)
+
+
+def test_greedy_and_ties(oracle_mod):
+    x = np.array([[1.0, 3.0, -np.inf, 3.0, 2.0],
+                  [-np.inf, -np.inf, -np.inf, -np.inf, -np.inf],
+                  [0.0, -0.0, -1.0, -np.inf, 0.0]])
+    idx, b1, _ = oracle_mod.sample(x, [0.0, 0.0, 0.0], [1, 2, 3], [0, 0, 0], K=3)
+    assert idx.tolist() == [[1, 1, 1], [-1, -1, -1], [0, 0, 0]]
+    assert b1[0, 0] == 3.0
+    # greedy ignores the curve: argmax of x
+    idx2, _, _ = oracle_mod.sample(x[:1], [0.0], [1], [0], K=1, mu=[-1.0], hlg=(2.0, 0.1, 0.5, 0.5))
+    assert idx2[0, 0] == 1
+
+
+def test_bad_rows(oracle_mod):
+    x = np.zeros((4, 6))
+    idx, _, _ = oracle_mod.sample(x, [-1.0, np.nan, np.inf, 1.0], [1, 1, 1, 1], [0, 0, 0, 0], K=2)
+    assert idx[:3].tolist() == [[-2, -2]] * 3
+    assert np.all((idx[3] >= 0) & (idx[3] < 6))
+    idx, _, _ = oracle_mod.sample(x[:1], [1.0], [1], [0], mu=[np.nan], hlg=(1.0, 1.0, 1.0, 1.0))
+    assert idx[0, 0] == -2
+    with pytest.raises(ValueError):
+        oracle_mod.sample(x[:1], [1.0], [1], [0], mu=[0.0], hlg=(-1.0, 1.0, 1.0, 1.0))
+
+
+def test_masked_never_sampled(oracle_mod):
+    rng = np.random.default_rng(31)
+    x = rng.normal(0, 1, size=(4, 300))
+    x[:, ::2] = -np.inf
+    x[:, 0] = 50.0            # a finite huge logit next to masked ones
+    x[:, 2] = -np.inf
+    idx, _, _ = oracle_mod.sample(x, [5.0] * 4, [1, 2, 3, 4], [0] * 4, K=500)
+    assert np.all(np.isfinite(x[np.arange(4)[:, None], idx]))
+
+
+def test_determinism_and_stream_dependence(oracle_mod):
+    rng = np.random.default_rng(41)
+    x = rng.normal(0, 1, size=(3, 500))
+    a = oracle_mod.sample(x, [1.0] * 3, [7, 8, 9], [0, 0, 0], K=50)[0]
+    b = oracle_mod.sample(x, [1.0] * 3, [7, 8, 9], [0, 0, 0], K=50)[0]
+    np.testing.assert_array_equal(a, b)
+    # draw k of a K-draw call equals a single draw at offset + k
+    c = oracle_mod.sample(x, [1.0] * 3, [7, 8, 9], [20, 20, 20], K=1)[0]
+    np.testing.assert_array_equal(c[:, 0], a[:, 20])
+    d = oracle_mod.sample(x, [1.0] * 3, [70, 80, 90], [0, 0, 0], K=50)[0]
+    assert not np.array_equal(a, d)
+
+
+# --------------------------------------------------------------------------- brute force
+def _py_word(seed, row, off, i):
+    return py_philox((i >> 2, row & M32, off & M32, (off >> 32) & M32),
+                     (seed & M32, (seed >> 32) & M32))[i & 3]
+
+
+def _py_curve(z, m, w, bt, bh):
+    if z < -w:
+        return -m * w - m * bt * math.log1p((-z - w) / bt)
+    if abs(z) <= w:
+        return m * z
+    return m * w + m * bh * math.log1p((z - w) / bh)
+
+
+def _py_draw(x, row, T, seed, off, hlg=None, mu=None):
+    fin = [v for v in x if v > -math.inf]
+    if not fin:
+        return -1
+    if T == 0:
+        best, j = -math.inf, -1
+        for i, v in enumerate(x):
+            if v > -math.inf and (j < 0 or v > best):
+                best, j = v, i
+        return j
+    if hlg is not None:
+        M = max(fin)
+        lse = M + math.log(math.fsum(math.exp(v - M) for v in fin))
+    best, j = -math.inf, -1
+    for i, v in enumerate(x):
+        if not v > -math.inf:
+            continue
+        lp = _py_curve((v - lse) - mu, *hlg) if hlg is not None else v
+        u = (_py_word(seed, row, off, i) + 0.5) / 2.0 ** 32
+        s = lp / T - math.log(-math.log(u))
+        if j < 0 or s > best:
+            best, j = s, i
+    return j
+
+
+@pytest.mark.parametrize("use_hlg", [False, True])
+def test_brute_force_tiny(oracle_mod, use_hlg):
+    rng = np.random.default_rng(51 + use_hlg)
+    B, V, K = 5, 11, 6
+    x = rng.normal(0, 0.7, size=(B, V))
+    x[1, [0, 5]] = -np.inf
+    x[3, :] = -np.inf
+    T = np.array([1.0, 0.5, 1.7, 1.0, 0.0], dtype=np.float32)
+    seed = np.array([0, 2**64 - 1, 0x123456789ABCDEF0, 5, 6], dtype=np.uint64)
+    offset = np.array([0, 2**32 - 3, 2**64 - 2, 7, 9], dtype=np.uint64)
+    row_id = np.array([0, 1, 1023, 3, 77], dtype=np.int64)
+    hlg = (1.5, 0.5, 1.0, 2.0) if use_hlg else None
+    mu = np.array([-2.5, -2.0, -3.0, 0.0, -1.0], dtype=np.float32) if use_hlg else None
+    idx, _, _ = oracle_mod.sample(x, T, seed, offset, K=K, mu=mu, hlg=hlg, row_id=row_id)
+    for b in range(B):
+        for k in range(K):
+            off = (int(offset[b]) + k) % 2**64
+            want = _py_draw(list(x[b]), int(row_id[b]), float(T[b]), int(seed[b]), off,
+                            hlg, float(mu[b]) if use_hlg else None)
+            assert idx[b, k] == want, (b, k)
