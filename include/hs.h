@@ -1,0 +1,155 @@
+/*
+ * hs.h -- C ABI of libhs: batched HLG tone-curve + Gumbel-max token sampling on MI355X.
+ *
+ * Sources for every operation below (cited by page title and section):
+ *   [HLG] "HLG sampling -- a piecewise tone curve on the logits", mlx-bun design document
+ *         docs/design/hlg-sampling.md.
+ *   [GMX] "Softmax-free GPU sampling: Gumbel-max categorical sampling kernel", lablup/mlxcel
+ *         issue #900.
+ *   [P123] Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11
+ *         (Philox4x32-10).
+ *
+ * Conventions shared by every call
+ *   - Array arguments are DEVICE pointers owned by the caller (the library allocates nothing
+ *     and keeps no state between calls). `hs_logits*` and `hs_hlg_params*` are HOST pointers.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls only enqueue
+ *     work on it and return at once; nothing synchronises.
+ *   - The return value reports host-checkable errors only (hs_status). On any error no work
+ *     is enqueued. Device-side per-row conditions are written into the output instead.
+ *   - Logits are row-major [B, ld] with ld >= V elements; values must be finite or -inf
+ *     (NaN / +inf are a precondition violation with undefined result). 16-byte aligned rows
+ *     (data pointer and ld * element size both multiples of 16) take the vector load path;
+ *     other layouts are accepted and read element by element.
+ *   - Results do not depend on the grid the library picks: random numbers are a function of
+ *     (seed, row, element, offset) only [GMX, Background].
+ */
+#ifndef HS_H
+#define HS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    HS_OK = 0,
+    HS_ERR_INVALID_ARG = -1,  /* null pointer, B/V/K <= 0, ld < V, bad curve parameter ...  */
+    HS_ERR_DTYPE = -2,        /* unknown hs_dtype                                          */
+    HS_ERR_WORKSPACE = -3,    /* workspace missing or smaller than hs_workspace_bytes()     */
+    HS_ERR_HIP = -4,          /* a HIP runtime call or kernel launch failed                 */
+    HS_ERR_UNSUPPORTED = -5   /* size outside the supported range (V >= 2^31, ...)         */
+} hs_status;
+
+typedef enum { HS_F32 = 0, HS_BF16 = 1, HS_F16 = 2 } hs_dtype;
+
+/* Logits [B, V] of one of the three input types of [GMX, Task 1] ("f32 or bf16/f16
+ * upcast"); bf16 and f16 are widened to fp32 exactly. */
+typedef struct {
+    const void *data;   /* device pointer, row-major, row stride ld elements */
+    int32_t dtype;      /* hs_dtype */
+    int64_t B;          /* rows (batch) */
+    int64_t V;          /* vocabulary size, 1 <= V < 2^31 */
+    int64_t ld;         /* row stride in elements, ld >= V */
+} hs_logits;
+
+/* The curve knobs of [HLG, Knobs]: mid gain m > 0 (finite), mid half-width w >= 0 (+inf
+ * turns the rolloff off), toe and shoulder rolloff constants beta_t, beta_h > 0 (finite),
+ * all in nats. */
+typedef struct {
+    float m;
+    float w;
+    float beta_t;
+    float beta_h;
+} hs_hlg_params;
+
+/* lse[b] = log(sum_i exp(x[b,i])) over the finite entries of row b, -inf for a row with no
+ * finite entry [HLG, The transfer function: the log-prob space l = x - LSE(x)].
+ * lse: device float[B]. */
+int hs_logsumexp(const hs_logits *x, float *lse, void *stream);
+
+/* out[b*ldo + i] = g(z) with z = (x[b,i] - LSE_b) - mu[b] and g the toe / mid / shoulder
+ * transfer function of [HLG, The transfer function, eq. z and eq. g]; -inf stays -inf.
+ * This is l' before any temperature. mu: device float[B] (pivot, log-prob nats);
+ * p: host pointer; out: device float[B*ldo], ldo >= V. A row with no finite entry is
+ * written as all -inf. */
+int hs_hlg_transform(const hs_logits *x, const float *mu, const hs_hlg_params *p, float *out,
+                     int64_t ldo, void *stream);
+
+/* Gumbel-max draws without the curve [GMX, Task 1]:
+ *   out[b*K + k] = argmax_i ( x[b,i] / T[b] + G(word(seed[b], b, i, offset[b] + k)) ),
+ * G(r) = -log(-log(u)), u = (r + 1/2) 2^-32, word = Philox4x32-10 [P123] with
+ * key = (seed lo, seed hi), counter = (i >> 2, b, off lo, off hi), output word i & 3.
+ * Ties go to the lowest index; -inf entries are never chosen [GMX, Regression guard].
+ * Per-row results: -1 if the row has no finite entry, -2 if T[b] < 0 or not finite.
+ * T[b] == 0 is greedy: argmax of x, the same index for all K draws.
+ * T: device float[B]; seed, offset: device uint64[B]; out: device int32[B*K].
+ * ws / ws_bytes: device workspace of at least hs_workspace_bytes(B, V, K, dtype, 0) bytes,
+ * zero-filled before its first use (hs_workspace_init); every successful call leaves it
+ * zero-filled again. Calls that may run concurrently need separate workspaces. ws may be
+ * NULL with ws_bytes 0, in which case only single-block-per-row kernels are used. */
+int hs_gumbel_argmax(const hs_logits *x, const float *T, const uint64_t *seed,
+                     const uint64_t *offset, int32_t K, int32_t *out, void *ws,
+                     size_t ws_bytes, void *stream);
+
+/* The full sampling step: the optional curve feeds the Gumbel-max draw [HLG, The transfer
+ * function; GMX, Background]:
+ *   l'_i = g((x_i - LSE_b) - mu[b])   when hlg != NULL,   l'_i = x_i   when hlg == NULL,
+ *   out[b*K + k] = argmax_i ( l'_i / T[b] + G(word(seed[b], b, i, offset[b] + k)) ).
+ * With the curve on, mu must be a device float[B] and a row with a non-finite mu gives -2.
+ * T[b] == 0 is greedy on x (the curve is monotone, so it cannot change the argmax
+ * [HLG, Greedy is untouched]). Everything else as hs_gumbel_argmax; the workspace size is
+ * hs_workspace_bytes(B, V, K, dtype, hlg != NULL). */
+int hs_sample(const hs_logits *x, const float *T, const float *mu, const hs_hlg_params *hlg,
+              const uint64_t *seed, const uint64_t *offset, int32_t K, int32_t *out,
+              void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes the multi-block-per-row kernels of hs_sample / hs_gumbel_argmax need for
+ * this shape (0 on invalid arguments). */
+size_t hs_workspace_bytes(int64_t B, int64_t V, int32_t K, int32_t dtype, int32_t hlg_on);
+
+/* Zero-fills a workspace on `stream` with a fill kernel (graph-capture safe). */
+int hs_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
+/* Tuning / test control for hs_sample_ex. Zero-initialised = automatic choices. */
+typedef struct {
+    int32_t variant;     /* 0 automatic, 1 one block per row, 2 split the row over blocks */
+    int32_t nchunk;      /* blocks per row when split (0 = automatic)                      */
+    int32_t no_screen;   /* 1 = evaluate every element exactly (no candidate screening)    */
+    int32_t draw_groups; /* blocks sharing one row's K draws (0 = automatic)               */
+} hs_sample_opts;
+
+/* hs_sample with explicit kernel choices. best (device float[B*K] or NULL) receives the
+ * winning score of each draw (l'/T + G in fp32; the logit for greedy rows; -inf for rows
+ * with a -1/-2 result). Results are identical for every choice of opts up to fp32 rounding
+ * of the row's LSE. */
+int hs_sample_ex(const hs_logits *x, const float *T, const float *mu,
+                 const hs_hlg_params *hlg, const uint64_t *seed, const uint64_t *offset,
+                 int32_t K, int32_t *out, float *best, void *ws, size_t ws_bytes,
+                 const hs_sample_opts *opts, void *stream);
+
+/* Philox4x32-10 [P123] on n (counter, key) pairs: ctr device uint32[4n], key device
+ * uint32[2n], out device uint32[4n]. Uses the same device routine as the samplers. */
+int hs_philox4x32_10(const uint32_t *ctr, const uint32_t *key, uint32_t *out, int64_t n,
+                     void *stream);
+
+/* The random words the samplers use for draw k: out[b*V + i] = word(seed[b], b,
+ * i, offset[b] + k) (layout as in hs_gumbel_argmax). out: device uint32[B*V]. */
+int hs_stream_words(const uint64_t *seed, const uint64_t *offset, int64_t B, int64_t V,
+                    int32_t k, uint32_t *out, void *stream);
+
+/* The samplers' fp32 Gumbel map on n words: g[j] = G(words[j]). */
+int hs_gumbel_f32(const uint32_t *words, float *g, int64_t n, void *stream);
+
+/* Human-readable name of an hs_status value. */
+const char *hs_status_str(int status);
+
+/* Library version string. */
+const char *hs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HS_H */

@@ -1,0 +1,77 @@
+"""Build libhs.so (HIP, gfx950) in-tree with hipcc.
+
+Flags: -O3, -ffp-contract=off (every kernel variant rounds identically), packed fp32
+disabled, no fast-math (it would break -inf masking).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libhs.so")
+SOURCES = ["hs_kernels.hip", "hs_api.hip"]
+HEADERS = ["hs_device.hpp", "hs_internal.hpp"]
+ARCH = os.environ.get("HS_OFFLOAD_ARCH", "gfx950")
+
+
+def hipcc() -> str:
+    p = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(p):
+        raise RuntimeError("hipcc not found")
+    return p
+
+
+def flags():
+    return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
+            "-fno-fast-math", "-mllvm", "-pragma-unroll-threshold=100000", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I" + os.path.join(os.path.dirname(HERE), "include"), "-I" + CSRC, "-Wall"]
+
+
+def _inputs():
+    srcs = [os.path.join(CSRC, s) for s in SOURCES + HEADERS]
+    srcs.append(os.path.join(os.path.dirname(HERE), "include", "hs.h"))
+    return srcs
+
+
+def up_to_date() -> bool:
+    if not os.path.exists(LIB):
+        return False
+    t = os.path.getmtime(LIB)
+    return all(os.path.getmtime(s) <= t for s in _inputs())
+
+
+def build(force: bool = True, verbose: bool = False) -> str:
+    if not force and up_to_date():
+        return LIB
+    objs = []
+    procs = []
+    for s in SOURCES:
+        obj = os.path.join(CSRC, s.replace(".hip", ".o"))
+        cmd = [hipcc()] + flags() + ["-c", os.path.join(CSRC, s), "-o", obj]
+        if verbose:
+            print(" ".join(cmd))
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                      text=True))
+        objs.append(obj)
+    for p in procs:
+        out, _ = p.communicate()
+        lines = [l for l in out.splitlines() if "packed-fp32-ops" not in l and l.strip()]
+        if p.returncode != 0:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(lines))
+        if verbose and lines:
+            print("\n".join(lines))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+    subprocess.run(cmd, check=True, capture_output=not verbose)
+    os.replace(tmp, LIB)
+    for o in objs:
+        os.remove(o)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(force=True, verbose="-v" in sys.argv))

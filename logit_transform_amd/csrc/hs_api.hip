@@ -1,0 +1,344 @@
+// hs_api.hip -- host side of libhs: argument validation, kernel choice and launches behind
+// the C ABI declared in include/hs.h. Every check here runs before any HIP call, so a bad
+// argument never enqueues work.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/hs.h"
+#include "hs_internal.hpp"
+
+namespace {
+
+using hs::SampleArgs;
+
+// Register-resident vectors per thread that kernels are generated for: up to 19 with blocks
+// of up to 1024 threads, 24 / 32 / 40 with blocks of 512 threads.
+constexpr int kNvBuckets1024[] = {1, 2, 4, 6, 8, 12, 16, 18, 19};
+constexpr int kNvBuckets512[] = {24, 32, 40};
+constexpr int64_t kBlockCapacity = 40 * 512;   // vectors one block can hold
+
+inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+inline int epv_of(int dt) { return dt == HS_F32 ? 4 : 8; }
+inline int esize_of(int dt) { return dt == HS_F32 ? 4 : 2; }
+
+int check_logits(const hs_logits *x) {
+    if (!x || !x->data) return HS_ERR_INVALID_ARG;
+    if (x->dtype != HS_F32 && x->dtype != HS_BF16 && x->dtype != HS_F16) return HS_ERR_DTYPE;
+    if (x->B < 1 || x->V < 1 || x->ld < x->V) return HS_ERR_INVALID_ARG;
+    if (x->V >= ((int64_t)1 << 31) || x->B >= ((int64_t)1 << 31)) return HS_ERR_UNSUPPORTED;
+    return HS_OK;
+}
+
+int check_curve(const hs_hlg_params *p) {
+    if (!p) return HS_ERR_INVALID_ARG;
+    if (!(p->m > 0.0f) || !isfinite(p->m)) return HS_ERR_INVALID_ARG;
+    if (!(p->w >= 0.0f)) return HS_ERR_INVALID_ARG;   // +inf allowed (rolloff off)
+    if (!(p->beta_t > 0.0f) || !isfinite(p->beta_t)) return HS_ERR_INVALID_ARG;
+    if (!(p->beta_h > 0.0f) || !isfinite(p->beta_h)) return HS_ERR_INVALID_ARG;
+    return HS_OK;
+}
+
+hs::Curve make_curve(const hs_hlg_params *p) {
+    hs::Curve c;
+    c.m = p->m;
+    c.w = p->w;
+    c.mw = p->m * p->w;
+    c.mbt = p->m * p->beta_t;
+    c.mbh = p->m * p->beta_h;
+    c.ibt = 1.0f / p->beta_t;
+    c.ibh = 1.0f / p->beta_h;
+    return c;
+}
+
+bool rows_aligned(const hs_logits *x) {
+    const size_t es = (size_t)esize_of(x->dtype);
+    return ((uintptr_t)x->data % 16 == 0) && (((size_t)x->ld * es) % 16 == 0);
+}
+
+int num_cus() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64 && cache[dev] > 0) return cache[dev];
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    if (dev < 64) cache[dev] = n;
+    return n;
+}
+
+struct WsLayout {
+    size_t counters, keys, partials, total;
+};
+
+WsLayout ws_layout(int64_t B, int32_t K) {
+    WsLayout L;
+    L.counters = 0;
+    L.keys = align256((size_t)B * 4);
+    L.partials = L.keys + align256((size_t)B * (size_t)K * 8);
+    L.total = L.partials + align256((size_t)B * hs::kMaxChunks * 8);
+    return L;
+}
+
+struct Plan {
+    int nchunk, nv, bs, nkg, kpg;
+    int64_t nvec, cv;
+    int64_t grid;
+};
+
+// Block size and vectors per thread for a chunk of cv vectors.
+bool pick_block(int64_t cv, int *bs, int *nv) {
+    int b = 1024;
+    if (cv <= 256 * 4) b = 256;
+    else if (cv <= 512 * 8) b = 512;
+    int64_t per = (cv + b - 1) / b;
+    if (per > 19 && b == 1024) {
+        b = 512;
+        per = (cv + b - 1) / b;
+    }
+    if (per <= 19) {
+        for (int x : kNvBuckets1024)
+            if (per <= x) { *bs = b; *nv = x; return true; }
+    }
+    if (b == 512) {
+        for (int x : kNvBuckets512)
+            if (per <= x) { *bs = b; *nv = x; return true; }
+    }
+    return false;
+}
+
+// Kernel shape for a call. Rows that fit one block (<= kNvMax * 1024 vectors) keep one
+// block per row unless the batch is too small to fill the GPU, in which case rows are split
+// into chunks of >= 512 vectors; a small grid with several draws also spreads the draws.
+int make_plan(const hs_logits *x, int32_t K, bool ws_ok, const hs_sample_opts *o, Plan *P) {
+    const int64_t B = x->B;
+    const int64_t nvec = (x->V + epv_of(x->dtype) - 1) / epv_of(x->dtype);
+    const int64_t cap = kBlockCapacity;
+    const int64_t nchunk_min = (nvec + cap - 1) / cap;
+    const int64_t target = 2 * (int64_t)num_cus();
+    int64_t nchunk = nchunk_min;
+    const int variant = o ? o->variant : 0;
+    if (variant == 1) {
+        if (nchunk_min > 1) return HS_ERR_UNSUPPORTED;
+        nchunk = 1;
+    } else if (variant == 2 && o->nchunk > 0) {
+        nchunk = o->nchunk;
+    } else if (variant == 2 || (ws_ok && B * nchunk_min < target)) {
+        int64_t want = (target + B - 1) / B;
+        int64_t lim = nvec / 512;
+        if (lim < 1) lim = 1;
+        nchunk = want < lim ? want : lim;
+        if (nchunk < nchunk_min) nchunk = nchunk_min;
+        if (variant == 2 && nchunk < 2 && nvec >= 2) nchunk = 2;
+    }
+    if (nchunk > hs::kMaxChunks) nchunk = hs::kMaxChunks;
+    if (nchunk > nvec) nchunk = nvec;
+    if (nchunk < nchunk_min) return HS_ERR_UNSUPPORTED;
+    if (nchunk < 1) nchunk = 1;
+    int64_t cv = (nvec + nchunk - 1) / nchunk;
+    nchunk = (nvec + cv - 1) / cv;
+    if (nchunk > 1 && !ws_ok) return HS_ERR_WORKSPACE;
+    int bs = 0, nv = 0;
+    if (!pick_block(cv, &bs, &nv)) return HS_ERR_UNSUPPORTED;
+    int64_t nkg = 1;
+    if (o && o->draw_groups > 0) {
+        nkg = o->draw_groups;
+    } else if (K > 1 && B * nchunk < target) {
+        nkg = (target + B * nchunk - 1) / (B * nchunk);
+    }
+    if (nkg > K) nkg = K;
+    int64_t kpg = (K + nkg - 1) / nkg;
+    nkg = (K + kpg - 1) / kpg;
+    const int64_t grid = B * nchunk * nkg;
+    if (grid >= ((int64_t)1 << 31)) return HS_ERR_UNSUPPORTED;
+    P->nchunk = (int)nchunk;
+    P->nv = nv;
+    P->bs = bs;
+    P->nkg = (int)nkg;
+    P->kpg = (int)kpg;
+    P->nvec = nvec;
+    P->cv = cv;
+    P->grid = grid;
+    return HS_OK;
+}
+
+int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hlg_params *hlg,
+                const uint64_t *seed, const uint64_t *offset, int32_t K, int32_t *out,
+                float *best, void *ws, size_t ws_bytes, const hs_sample_opts *opts,
+                void *stream) {
+    int rc = check_logits(x);
+    if (rc) return rc;
+    if (!T || !seed || !offset || !out || K < 1) return HS_ERR_INVALID_ARG;
+    if (hlg) {
+        rc = check_curve(hlg);
+        if (rc) return rc;
+        if (!mu) return HS_ERR_INVALID_ARG;
+    }
+    if ((size_t)x->B * (size_t)K >= ((size_t)1 << 31)) return HS_ERR_UNSUPPORTED;
+    const WsLayout L = ws_layout(x->B, K);
+    const bool ws_ok = ws && ws_bytes >= L.total && ((uintptr_t)ws % 256 == 0);
+    if (ws && !ws_ok && ws_bytes > 0) {
+        // a workspace was given but is unusable: report it rather than silently ignore it
+        if (ws_bytes < L.total) return HS_ERR_WORKSPACE;
+        return HS_ERR_INVALID_ARG;
+    }
+    Plan P;
+    rc = make_plan(x, K, ws_ok, opts, &P);
+    if (rc) return rc;
+
+    SampleArgs a{};
+    a.data = x->data;
+    a.ld = x->ld;
+    a.V = x->V;
+    a.nvec = P.nvec;
+    a.cv = P.cv;
+    a.nchunk = P.nchunk;
+    a.nkg = P.nkg;
+    a.kpg = P.kpg;
+    a.K = K;
+    a.aligned = rows_aligned(x) ? 1 : 0;
+    a.no_screen = (opts && opts->no_screen) ? 1 : 0;
+    a.T = T;
+    a.mu = hlg ? mu : nullptr;
+    a.seed = seed;
+    a.offset = offset;
+    a.out = out;
+    a.best_out = best;
+    if (hlg) a.curve = make_curve(hlg);
+    if (P.nchunk > 1) {
+        char *w = reinterpret_cast<char *>(ws);
+        a.counters = reinterpret_cast<uint32_t *>(w + L.counters);
+        a.keys = reinterpret_cast<uint64_t *>(w + L.keys);
+        a.partials = reinterpret_cast<float2 *>(w + L.partials);
+        a.part_stride = hs::kMaxChunks;
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (hlg && P.nchunk > 1) {
+        const int bs = P.cv >= 4096 ? 1024 : 256;
+        if (hs::launch_lse_partial(x->dtype, a, bs, (int)(x->B * P.nchunk), s) != hipSuccess)
+            return HS_ERR_HIP;
+    }
+    if (hs::launch_sample(x->dtype, hlg != nullptr, a, P.nv, P.bs, (int)P.grid, s) != hipSuccess)
+        return HS_ERR_HIP;
+    return HS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hs_logsumexp(const hs_logits *x, float *lse, void *stream) {
+    int rc = check_logits(x);
+    if (rc) return rc;
+    if (!lse) return HS_ERR_INVALID_ARG;
+    hs::RowOpArgs a{};
+    a.data = x->data;
+    a.ld = x->ld;
+    a.V = x->V;
+    a.aligned = rows_aligned(x) ? 1 : 0;
+    a.lse = lse;
+    return hs::launch_row_lse(x->dtype, false, a, (int)x->B, reinterpret_cast<hipStream_t>(stream))
+                   == hipSuccess ? HS_OK : HS_ERR_HIP;
+}
+
+int hs_hlg_transform(const hs_logits *x, const float *mu, const hs_hlg_params *p, float *out,
+                     int64_t ldo, void *stream) {
+    int rc = check_logits(x);
+    if (rc) return rc;
+    rc = check_curve(p);
+    if (rc) return rc;
+    if (!mu || !out || ldo < x->V) return HS_ERR_INVALID_ARG;
+    hs::RowOpArgs a{};
+    a.data = x->data;
+    a.ld = x->ld;
+    a.V = x->V;
+    a.aligned = rows_aligned(x) ? 1 : 0;
+    a.mu = mu;
+    a.out = out;
+    a.ldo = ldo;
+    a.curve = make_curve(p);
+    return hs::launch_row_lse(x->dtype, true, a, (int)x->B, reinterpret_cast<hipStream_t>(stream))
+                   == hipSuccess ? HS_OK : HS_ERR_HIP;
+}
+
+int hs_gumbel_argmax(const hs_logits *x, const float *T, const uint64_t *seed,
+                     const uint64_t *offset, int32_t K, int32_t *out, void *ws, size_t ws_bytes,
+                     void *stream) {
+    return sample_impl(x, T, nullptr, nullptr, seed, offset, K, out, nullptr, ws, ws_bytes,
+                       nullptr, stream);
+}
+
+int hs_sample(const hs_logits *x, const float *T, const float *mu, const hs_hlg_params *hlg,
+              const uint64_t *seed, const uint64_t *offset, int32_t K, int32_t *out, void *ws,
+              size_t ws_bytes, void *stream) {
+    return sample_impl(x, T, mu, hlg, seed, offset, K, out, nullptr, ws, ws_bytes, nullptr,
+                       stream);
+}
+
+int hs_sample_ex(const hs_logits *x, const float *T, const float *mu, const hs_hlg_params *hlg,
+                 const uint64_t *seed, const uint64_t *offset, int32_t K, int32_t *out,
+                 float *best, void *ws, size_t ws_bytes, const hs_sample_opts *opts,
+                 void *stream) {
+    if (opts && (opts->variant < 0 || opts->variant > 2 || opts->nchunk < 0 ||
+                 opts->nchunk > hs::kMaxChunks || opts->draw_groups < 0))
+        return HS_ERR_INVALID_ARG;
+    return sample_impl(x, T, mu, hlg, seed, offset, K, out, best, ws, ws_bytes, opts, stream);
+}
+
+size_t hs_workspace_bytes(int64_t B, int64_t V, int32_t K, int32_t dtype, int32_t hlg_on) {
+    (void)hlg_on;
+    if (B < 1 || V < 1 || K < 1) return 0;
+    if (dtype != HS_F32 && dtype != HS_BF16 && dtype != HS_F16) return 0;
+    return ws_layout(B, K).total;
+}
+
+int hs_workspace_init(void *ws, size_t ws_bytes, void *stream) {
+    if (!ws || ws_bytes % 4 != 0) return HS_ERR_INVALID_ARG;
+    if (ws_bytes == 0) return HS_OK;
+    return hs::launch_fill_zero(ws, (int64_t)(ws_bytes / 4), reinterpret_cast<hipStream_t>(stream))
+                   == hipSuccess ? HS_OK : HS_ERR_HIP;
+}
+
+int hs_philox4x32_10(const uint32_t *ctr, const uint32_t *key, uint32_t *out, int64_t n,
+                     void *stream) {
+    if (!ctr || !key || !out || n < 0) return HS_ERR_INVALID_ARG;
+    if (n == 0) return HS_OK;
+    if (n >= ((int64_t)1 << 38)) return HS_ERR_UNSUPPORTED;
+    return hs::launch_philox(ctr, key, out, n, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+                   ? HS_OK : HS_ERR_HIP;
+}
+
+int hs_stream_words(const uint64_t *seed, const uint64_t *offset, int64_t B, int64_t V,
+                    int32_t k, uint32_t *out, void *stream) {
+    if (!seed || !offset || !out || B < 1 || V < 1 || k < 0) return HS_ERR_INVALID_ARG;
+    if (V >= ((int64_t)1 << 31) || B >= ((int64_t)1 << 31)) return HS_ERR_UNSUPPORTED;
+    return hs::launch_stream_words(seed, offset, B, V, k, out, reinterpret_cast<hipStream_t>(stream))
+                   == hipSuccess ? HS_OK : HS_ERR_HIP;
+}
+
+int hs_gumbel_f32(const uint32_t *words, float *g, int64_t n, void *stream) {
+    if (!words || !g || n < 0) return HS_ERR_INVALID_ARG;
+    if (n == 0) return HS_OK;
+    if (n >= ((int64_t)1 << 40)) return HS_ERR_UNSUPPORTED;
+    return hs::launch_gumbel(words, g, n, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+                   ? HS_OK : HS_ERR_HIP;
+}
+
+const char *hs_status_str(int status) {
+    switch (status) {
+        case HS_OK: return "HS_OK";
+        case HS_ERR_INVALID_ARG: return "HS_ERR_INVALID_ARG: invalid argument";
+        case HS_ERR_DTYPE: return "HS_ERR_DTYPE: unknown logits dtype";
+        case HS_ERR_WORKSPACE: return "HS_ERR_WORKSPACE: workspace missing or too small";
+        case HS_ERR_HIP: return "HS_ERR_HIP: HIP runtime or launch failure";
+        case HS_ERR_UNSUPPORTED: return "HS_ERR_UNSUPPORTED: size outside the supported range";
+    }
+    return "unknown hs_status";
+}
+
+const char *hs_version(void) { return "libhs 0.1.0 (gfx950)"; }
+
+}  // extern "C"

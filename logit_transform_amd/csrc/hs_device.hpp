@@ -1,0 +1,280 @@
+// hs_device.hpp -- device-side building blocks of libhs (gfx950, wave64).
+//
+// Sources, cited by page title and section:
+//   [HLG]  "HLG sampling -- a piecewise tone curve on the logits" (mlx-bun design document).
+//   [GMX]  "Softmax-free GPU sampling: Gumbel-max categorical sampling kernel" (mlxcel #900).
+//   [P123] Salmon et al., "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11.
+//
+// Every kernel variant evaluates the per-element arithmetic through the functions in this
+// file, compiled with -ffp-contract=off, so that all variants round identically.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hs {
+
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+
+template <int DT> struct dtype_traits;
+template <> struct dtype_traits<DT_F32> {
+    static constexpr int esize = 4, epv = 4;          // elements per 16-byte vector
+    static constexpr uint32_t neg_inf_word = 0xFF800000u;
+};
+template <> struct dtype_traits<DT_BF16> {
+    static constexpr int esize = 2, epv = 8;
+    static constexpr uint32_t neg_inf_word = 0xFF80FF80u;
+};
+template <> struct dtype_traits<DT_F16> {
+    static constexpr int esize = 2, epv = 8;
+    static constexpr uint32_t neg_inf_word = 0xFC00FC00u;
+};
+
+constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kInvLn2 = 1.44269504088896341f;
+constexpr float kLog2e = 1.44269504088896341f;
+
+// ------------------------------------------------------------------------------------------
+// Philox4x32-10 [P123]. Counter words 0 and 2 are multiplied by the two round multipliers
+// into 64-bit products (one v_mad_u64_u32 each); the new counter is (hi1^c1^k0, lo1,
+// hi0^c3^k1, lo0) and the key advances by the Weyl constants between rounds. When some
+// counter or key words are wave-uniform the compiler moves their part of the early rounds
+// to the scalar unit.
+// ------------------------------------------------------------------------------------------
+struct Words4 {
+    uint32_t w[4];
+};
+
+__device__ __forceinline__ Words4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u;
+        const uint64_t p1 = (uint64_t)c2 * 0xCD9E8D57u;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c1 = (uint32_t)p1;
+        c3 = (uint32_t)p0;
+        c0 = n0;
+        c2 = n2;
+    }
+    Words4 o;
+    o.w[0] = c0;
+    o.w[1] = c1;
+    o.w[2] = c2;
+    o.w[3] = c3;
+    return o;
+}
+
+// Random words of the element group q (elements 4q..4q+3) of draw stream (seed, row, off)
+// [GMX, Task 1: "philox(seed, row, i, offset)"]: counter (q, row, off lo, off hi),
+// key (seed lo, seed hi); element i takes word i & 3.
+struct Stream {
+    uint32_t row, off_lo, off_hi, key0, key1;
+};
+
+__device__ __forceinline__ Words4 stream_group(const Stream &s, uint32_t q) {
+    return philox4x32_10(q, s.row, s.off_lo, s.off_hi, s.key0, s.key1);
+}
+
+// Same, for use inside a loop over draws: the group index is made opaque so that the
+// compiler cannot hoist the draw-invariant first multiply of every group out of the loop
+// (which costs two registers per group and spills).
+__device__ __forceinline__ Words4 stream_group_in_loop(const Stream &s, uint32_t q) {
+    asm volatile("" : "+v"(q));
+    return philox4x32_10(q, s.row, s.off_lo, s.off_hi, s.key0, s.key1);
+}
+
+// ------------------------------------------------------------------------------------------
+// Accurate fp32 log1p(t) for t > -1 by the log(1+t) * t / ((1+t) - 1) correction (Goldberg,
+// "What every computer scientist should know about floating-point arithmetic", 1991): the
+// rounding of 1 + t is compensated exactly, leaving a few ulps from logf.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ float log1p_acc(float t) {
+    const float u = 1.0f + t;
+    if (u == 1.0f) return t;
+    if (u == __builtin_inff()) return __builtin_inff();
+    return logf(u) * (t / (u - 1.0f));
+}
+
+// Gumbel noise of one word [GMX, Background: g = -log(-log(u))], u = (r + 1/2) 2^-32.
+// E = -log(u) is formed from u on the lower half and from v = 1 - u = (~r + 1/2) 2^-32 by
+// log1p on the upper half, so E keeps full relative precision where u is close to 1 -- the
+// words that win draws.
+__device__ __forceinline__ float gumbel32(uint32_t r) {
+    float E;
+    if (r < 0x80000000u) {
+        const float u = __builtin_fmaf((float)r, 0x1p-32f, 0x1p-33f);
+        E = -logf(u);
+    } else {
+        const float v = __builtin_fmaf((float)(~r), 0x1p-32f, 0x1p-33f);
+        E = -log1p_acc(-v);
+    }
+    return -logf(E);
+}
+
+// Upper bound on gumbel32(r), cheap: with n = clz(~r), v = 1 - u >= 2^-(n+1) and
+// G = -log(-log u) <= -log(v) <= (n + 1) ln 2. Returned as n (the caller folds the +1).
+__device__ __forceinline__ uint32_t gumbel_bound_bits(uint32_t r) {
+    return __clz(~r);   // 0..32 (32 for r = 0xFFFFFFFF)
+}
+
+// ------------------------------------------------------------------------------------------
+// The HLG transfer function [HLG, The transfer function, eq. g]: toe / mid / shoulder
+// selected on z vs +-w (the unselected branches are never evaluated, so -inf never meets
+// log1p's NaN paths). ln(1 + t) by log1p_acc.
+// ------------------------------------------------------------------------------------------
+struct Curve {
+    float m, w;          // mid gain, mid half-width (w may be +inf)
+    float mw;            // m * w
+    float mbt, mbh;      // m * beta_t, m * beta_h
+    float ibt, ibh;      // 1 / beta_t, 1 / beta_h
+};
+
+__device__ __forceinline__ float hlg32(float z, const Curve &c) {
+    if (z < -c.w) return -c.mw - c.mbt * log1p_acc((-z - c.w) * c.ibt);
+    if (z > c.w) return c.mw + c.mbh * log1p_acc((z - c.w) * c.ibh);
+    return c.m * z;
+}
+
+// ------------------------------------------------------------------------------------------
+// Index-carrying max [GMX, Background: "one index-carrying max-reduction pass"]: a 64-bit
+// key whose high word orders the fp32 score (-0 folded onto +0) and whose low word is
+// 0xFFFFFFFF - i, so the unsigned maximum is the largest score with the lowest index.
+// Key 0 means "no finite element".
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t order_bits(float s) {
+    uint32_t b = __float_as_uint(s);
+    if (b == 0x80000000u) b = 0u;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float order_bits_to_float(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+__device__ __forceinline__ uint64_t make_key(float s, uint32_t i) {
+    return ((uint64_t)order_bits(s) << 32) | (uint64_t)(0xFFFFFFFFu - i);
+}
+
+__device__ __forceinline__ int32_t key_index(uint64_t k) {
+    return k == 0 ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)k);
+}
+
+__device__ __forceinline__ float key_score(uint64_t k) {
+    return k == 0 ? -__builtin_inff() : order_bits_to_float((uint32_t)(k >> 32));
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// ------------------------------------------------------------------------------------------
+// Loads: 16-byte vectors of 4 fp32 or 8 bf16/f16 logits, upcast exactly to fp32 on use.
+// ------------------------------------------------------------------------------------------
+template <int DT>
+__device__ __forceinline__ float elem(const uint4 &v, int e) {
+    const uint32_t w = (e >> (DT == DT_F32 ? 0 : 1)) == 0 ? v.x
+                     : (e >> (DT == DT_F32 ? 0 : 1)) == 1 ? v.y
+                     : (e >> (DT == DT_F32 ? 0 : 1)) == 2 ? v.z : v.w;
+    if constexpr (DT == DT_F32) {
+        return __uint_as_float(w);
+    } else if constexpr (DT == DT_BF16) {
+        return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+    } else {
+        const uint16_t h = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+        return (float)__builtin_bit_cast(_Float16, h);
+    }
+}
+
+// Vector gv of a row (elements gv*epv .. gv*epv+epv-1); elements at or past V read as -inf.
+template <int DT>
+__device__ __forceinline__ uint4 load_vec(const char *__restrict__ rowp, int64_t gv, int64_t V,
+                                          bool aligned) {
+    using tr = dtype_traits<DT>;
+    const int64_t i0 = gv * tr::epv;
+    if (aligned && i0 + tr::epv <= V)
+        return *reinterpret_cast<const uint4 *>(rowp + i0 * tr::esize);
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = tr::neg_inf_word;
+    if constexpr (DT == DT_F32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (i0 + e < V) w[e] = reinterpret_cast<const uint32_t *>(rowp)[i0 + e];
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (i0 + e < V) {
+                const uint32_t h = reinterpret_cast<const uint16_t *>(rowp)[i0 + e];
+                const int j = e >> 1;
+                w[j] = (e & 1) ? ((w[j] & 0x0000FFFFu) | (h << 16)) : ((w[j] & 0xFFFF0000u) | h);
+            }
+        }
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// ------------------------------------------------------------------------------------------
+// Wave64 and block reductions.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint64_t t = __shfl_xor(v, o);
+        v = t > v ? t : v;
+    }
+    return v;
+}
+
+// Block-wide reductions over up to 16 waves through LDS scratch `red` (>= 16 entries).
+// Every thread returns the result. The combine order is fixed (wave 0..nw-1), so the
+// result is a deterministic function of the inputs.
+__device__ __forceinline__ float block_max(float v, float *red) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+    v = wave_max(v);
+    __syncthreads();
+    if (lane == 0) red[wid] = v;
+    __syncthreads();
+    float r = red[0];
+    for (int j = 1; j < nw; ++j) r = fmaxf(r, red[j]);
+    return r;
+}
+
+__device__ __forceinline__ float block_sum(float v, float *red) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+    v = wave_sum(v);
+    __syncthreads();
+    if (lane == 0) red[wid] = v;
+    __syncthreads();
+    float r = red[0];
+    for (int j = 1; j < nw; ++j) r += red[j];
+    return r;
+}
+
+__device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t *red) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+    v = wave_max_u64(v);
+    __syncthreads();
+    if (lane == 0) red[wid] = v;
+    __syncthreads();
+    uint64_t r = red[0];
+    for (int j = 1; j < nw; ++j) r = umax64(r, red[j]);
+    return r;
+}
+
+}  // namespace hs

@@ -1,0 +1,64 @@
+// hs_internal.hpp -- kernel argument blocks and launchers shared by hs_api.hip and
+// hs_kernels.hip. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hs_device.hpp"
+
+namespace hs {
+
+// Rows split over more than this many blocks are not generated; the workspace reserves this
+// many (max, sum) pairs per row.
+constexpr int kMaxChunks = 64;
+
+struct SampleArgs {
+    const void *data;          // logits, row-major [B, ld]
+    int64_t ld;                // row stride (elements)
+    int64_t V;                 // vocabulary
+    int64_t nvec;              // 16-byte vectors per row = ceil(V / epv)
+    int64_t cv;                // vectors per chunk
+    int32_t nchunk;            // blocks per row
+    int32_t nkg;               // blocks sharing a row's draws
+    int32_t kpg;               // draws per such block
+    int32_t K;                 // draws per row
+    int32_t aligned;           // rows are 16-byte aligned
+    int32_t no_screen;         // evaluate every element exactly
+    const float *T;
+    const float *mu;
+    const uint64_t *seed;
+    const uint64_t *offset;
+    int32_t *out;
+    float *best_out;
+    Curve curve;
+    // workspace (split rows only)
+    uint32_t *counters;        // [B]
+    uint64_t *keys;            // [B * K]
+    float2 *partials;          // [B * part_stride]
+    int64_t part_stride;
+};
+
+struct RowOpArgs {
+    const void *data;
+    int64_t ld, V;
+    int32_t aligned;
+    const float *mu;
+    float *lse;
+    float *out;
+    int64_t ldo;
+    Curve curve;
+};
+
+hipError_t launch_sample(int dt, bool hlg, const SampleArgs &a, int nv, int bs, int grid,
+                         hipStream_t s);
+hipError_t launch_lse_partial(int dt, const SampleArgs &a, int bs, int grid, hipStream_t s);
+hipError_t launch_row_lse(int dt, bool transform, const RowOpArgs &a, int grid, hipStream_t s);
+hipError_t launch_philox(const uint32_t *ctr, const uint32_t *key, uint32_t *out, int64_t n,
+                         hipStream_t s);
+hipError_t launch_stream_words(const uint64_t *seed, const uint64_t *offset, int64_t B,
+                               int64_t V, int32_t k, uint32_t *out, hipStream_t s);
+hipError_t launch_gumbel(const uint32_t *w, float *g, int64_t n, hipStream_t s);
+hipError_t launch_fill_zero(void *p, int64_t nwords, hipStream_t s);
+
+}  // namespace hs

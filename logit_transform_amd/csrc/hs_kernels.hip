@@ -1,0 +1,583 @@
+// hs_kernels.hip -- gfx950 kernels of libhs: batched HLG tone curve + Gumbel-max sampling.
+//
+// Sources, cited by page title and section:
+//   [HLG]  "HLG sampling -- a piecewise tone curve on the logits" (mlx-bun design document).
+//   [GMX]  "Softmax-free GPU sampling: Gumbel-max categorical sampling kernel" (mlxcel #900).
+//
+// Work decomposition. A block owns one contiguous chunk of one row and keeps it in VGPRs as
+// raw 16-byte vectors (thread t holds vectors t, t+BS, t+2BS, ...: consecutive lanes read
+// consecutive 16 B, so every wave load is one contiguous 1 KiB). The row is read from HBM
+// once; every pass after the load (max, sum of exponentials, and each draw) runs on the
+// register copy. With one chunk per row the row's log-sum-exp is reduced inside the block
+// (single read). With several chunks per row a pre-pass leaves per-chunk (max, sum) pairs in
+// the workspace, every block of the row folds them in the same fixed order, and the chunks'
+// winning keys meet in a 64-bit atomic max; the last block of the row to finish writes the
+// token ids and zeroes its workspace slots again.
+//
+// Screening. A draw's winner is the exact argmax over all elements, but the expensive part
+// of an element's score (curve branches, two logarithms) is evaluated only when an upper
+// bound on that score reaches the best score already found in the block minus a slack:
+//   score = l'/T + G(r) <= U(x) + (clz(~r) + 1) ln 2,
+// where U(x) = (m/T) * max(x - c, -w) bounds g(x - c)/T (g lies below its mid line past the
+// shoulder knot and below -m*w in the toe) and clz(~r) bounds G from the word's leading
+// ones. The bound is rigorous up to fp32 rounding, which the slack covers many times over,
+// so the screened result equals the exhaustive one bit for bit (a test checks this).
+#include <hip/hip_runtime.h>
+
+#include "hs_device.hpp"
+#include "hs_internal.hpp"
+
+namespace hs {
+
+__device__ __forceinline__ float screen_slack(float s) {
+    return 1e-3f + 1e-5f * (fabsf(s) + 32.0f);
+}
+
+// A block-uniform float moved to a scalar register.
+__device__ __forceinline__ float uniform(float v) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
+// Per-row constants of one block.
+struct RowConst {
+    float invT;      // 1 / T
+    float c;         // LSE + mu (curve on)
+    float mt;        // m / T
+    float mtc;       // (m / T) * c
+    float mtw;       // (m / T) * w
+    Curve curve;
+};
+
+// Element e (run-time index) of a register-held vector.
+template <int DT>
+__device__ __forceinline__ float elem_dyn(const uint4 &v, uint32_t e) {
+    const uint32_t j = (DT == DT_F32) ? e : (e >> 1);
+    const uint32_t w = j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+    if constexpr (DT == DT_F32) {
+        return __uint_as_float(w);
+    } else if constexpr (DT == DT_BF16) {
+        return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+    } else {
+        const uint16_t h = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+        return (float)__builtin_bit_cast(_Float16, h);
+    }
+}
+
+__device__ __forceinline__ uint32_t word_dyn(const Words4 &q, uint32_t j) {
+    return j == 0 ? q.w[0] : j == 1 ? q.w[1] : j == 2 ? q.w[2] : q.w[3];
+}
+
+// The exact fp32 score of one finite element: l'/T + G(r) [GMX, Background], with
+// l' = g(x - (LSE + mu)) when the curve is on [HLG, The transfer function]. Every kernel
+// variant scores elements through this one function.
+template <bool HLG>
+__device__ __noinline__ float exact_score(float x, uint32_t word, RowConst rc) {
+    float a;
+    if constexpr (HLG) {
+        a = hlg32(x - rc.c, rc.curve) * rc.invT;
+    } else {
+        a = x * rc.invT;
+    }
+    return a + gumbel32(word);
+}
+
+template <int DT>
+__device__ __forceinline__ uint64_t greedy_vec(uint4 raw, uint32_t i0, uint64_t best) {
+    constexpr int EPV = dtype_traits<DT>::epv;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+        const float x = elem<DT>(raw, e);
+        if (x > -__builtin_inff()) best = umax64(best, make_key(x, i0 + (uint32_t)e));
+    }
+    return best;
+}
+
+template <int DT, int NV, bool HLG, int MAXBS>
+__global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
+    using tr = dtype_traits<DT>;
+    constexpr int EPV = tr::epv;
+    constexpr int NMASK = (NV * EPV + 31) / 32;
+    __shared__ float redf[16];
+    __shared__ uint64_t redk[16];
+    __shared__ int s_last;
+
+    const int tid = threadIdx.x;
+    const int BS = blockDim.x;
+    int bid = blockIdx.x;
+    const int chunk = bid % a.nchunk;
+    bid /= a.nchunk;
+    const int kg = bid % a.nkg;
+    const int64_t b = bid / a.nkg;
+    const int k0 = kg * a.kpg;
+    const int k1 = min(a.K, k0 + a.kpg);
+
+    // ---- row parameters (wave-uniform) ----
+    const float T = a.T[b];
+    float mu = 0.0f;
+    bool bad = !(T >= 0.0f) || !(T < __builtin_inff());
+    if constexpr (HLG) {
+        mu = a.mu[b];
+        bad = bad || !(fabsf(mu) < __builtin_inff());
+    }
+    const bool greedy = (T == 0.0f);
+
+    // ---- load this chunk into registers ----
+    const int v0 = chunk * (int)a.cv;
+    const int vend = (int)min(a.nvec, (int64_t)v0 + a.cv);
+    const char *rowp = reinterpret_cast<const char *>(a.data) + b * a.ld * tr::esize;
+    uint4 raw[NV];
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+        const int gv = v0 + tid + n * BS;
+        if (gv < vend) {
+            raw[n] = load_vec<DT>(rowp, gv, a.V, a.aligned);
+        } else {
+            raw[n] = make_uint4(tr::neg_inf_word, tr::neg_inf_word, tr::neg_inf_word,
+                                tr::neg_inf_word);
+        }
+    }
+
+    RowConst rc;
+    rc.invT = 1.0f / T;
+    rc.c = 0.0f;
+    rc.mt = rc.mtc = rc.mtw = 0.0f;
+    rc.curve = a.curve;
+    bool skip = bad;
+
+    // ---- log-sum-exp of the row (curve on) [HLG, The transfer function: l = x - LSE(x)].
+    // Computed for every row, greedy and invalid ones included: keeping this block free of
+    // row-dependent branches keeps the register allocator from duplicating the row copy.
+    if constexpr (HLG) {
+        {
+            float lse;
+            if (a.nchunk == 1) {
+                float mx = -__builtin_inff();
+#pragma unroll
+                for (int n = 0; n < NV; ++n)
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) mx = fmaxf(mx, elem<DT>(raw[n], e));
+                const float M = block_max(mx, redf);
+                float s = 0.0f;
+                if (M > -__builtin_inff()) {
+                    const float mb = M * kLog2e;
+#pragma unroll
+                    for (int n = 0; n < NV; ++n) {
+                        // Tie this vector to the running sum: otherwise the scheduler issues
+                        // every exponential of the row first and holds all results at once.
+                        asm volatile("" : "+v"(s), "+v"(raw[n].x), "+v"(raw[n].y),
+                                     "+v"(raw[n].z), "+v"(raw[n].w));
+                        float t = 0.0f;
+#pragma unroll
+                        for (int e = 0; e < EPV; ++e) {
+                            const float x = elem<DT>(raw[n], e);
+                            t += __builtin_amdgcn_exp2f(x * kLog2e - mb);
+                        }
+                        s += t;
+                    }
+                }
+                const float S = block_sum(s, redf);
+                lse = (M > -__builtin_inff()) ? M + logf(S) : -__builtin_inff();
+            } else {
+                const float2 *part = a.partials + b * a.part_stride;
+                float M = -__builtin_inff();
+                for (int j = 0; j < a.nchunk; ++j) M = fmaxf(M, part[j].x);
+                float S = 0.0f;
+                if (M > -__builtin_inff())
+                    for (int j = 0; j < a.nchunk; ++j)
+                        if (part[j].x > -__builtin_inff())
+                            S += part[j].y * __builtin_amdgcn_exp2f((part[j].x - M) * kLog2e);
+                lse = (M > -__builtin_inff()) ? M + logf(S) : -__builtin_inff();
+            }
+            lse = uniform(lse);
+            if (!(lse > -__builtin_inff())) skip = true;   // no finite logit in the row
+            rc.c = uniform(lse + mu);
+            rc.mt = uniform(a.curve.m * rc.invT);
+            rc.mtc = uniform(rc.mt * rc.c);
+            rc.mtw = uniform(rc.mt * a.curve.w);
+        }
+    }
+
+    const uint64_t seed = a.seed[b];
+    const uint64_t off0 = a.offset[b];
+
+    for (int k = k0; k < k1; ++k) {
+        // Keep per-element work inside the draw loop: without this the compiler hoists the
+        // draw-invariant part of the screen (one value per element) out of the loop and runs
+        // out of registers.
+#pragma unroll
+        for (int n = 0; n < NV; ++n)
+            asm volatile("" : "+v"(raw[n].x), "+v"(raw[n].y), "+v"(raw[n].z), "+v"(raw[n].w));
+        // Likewise for everything derived from the lane's element indices.
+        int lane_v = v0 + tid;
+        asm volatile("" : "+v"(lane_v));
+        uint64_t best = 0;
+        if (!skip && greedy) {
+#pragma unroll
+            for (int n = 0; n < NV; ++n) {
+                const int gv = lane_v + n * BS;
+                if (gv < vend) best = greedy_vec<DT>(raw[n], (uint32_t)(gv * EPV), best);
+            }
+        } else if (!skip) {
+            const uint64_t off = off0 + (uint64_t)k;
+            Stream st;
+            st.row = (uint32_t)b;
+            st.off_lo = (uint32_t)off;
+            st.off_hi = (uint32_t)(off >> 32);
+            st.key0 = (uint32_t)seed;
+            st.key1 = (uint32_t)(seed >> 32);
+
+            // words of this lane's first vector (kept for the screen below)
+            const int gv0 = lane_v;
+            const uint32_t i00 = (uint32_t)gv0 * EPV;
+            const Words4 w0a = stream_group_in_loop(st, i00 >> 2);
+            Words4 w0b;
+            if constexpr (EPV == 8) w0b = stream_group_in_loop(st, (i00 >> 2) + 1);
+
+            // Bootstrap: each lane scores the element of its first vector with the largest
+            // word exactly; the block maximum is a score some element reaches, so it lower-
+            // bounds the draw's winning score.
+            float thr_s = -3.0e38f;   // (best known - slack) / ln 2 - 1
+            if (!a.no_screen) {
+                if (gv0 < vend) {
+                    uint32_t be = 0, bw = w0a.w[0];
+#pragma unroll
+                    for (int e = 1; e < EPV; ++e) {
+                        const uint32_t we = (e < 4) ? w0a.w[e & 3] : w0b.w[e & 3];
+                        if (we > bw) { bw = we; be = (uint32_t)e; }
+                    }
+                    const float x = elem_dyn<DT>(raw[0], be);
+                    if (x > -__builtin_inff())
+                        best = make_key(exact_score<HLG>(x, bw, rc), i00 + be);
+                }
+                const uint64_t bb = block_max_u64(best, redk);
+                if (bb != 0) {
+                    const float bs = key_score(bb);
+                    thr_s = uniform((bs - screen_slack(bs)) * kInvLn2 - 1.0f);
+                }
+            }
+
+            // Screen: candidate iff U(x) + (clz(~r) + 1) ln 2 >= best known - slack.
+            uint32_t cm[NMASK];
+#pragma unroll
+            for (int j = 0; j < NMASK; ++j) cm[j] = 0u;
+#pragma unroll
+            for (int n = 0; n < NV; ++n) {
+                const int gv = lane_v + n * BS;
+                if (gv < vend) {
+                    const uint32_t i0 = (uint32_t)gv * EPV;
+                    uint32_t wv[8];
+                    if (n == 0) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) wv[e] = w0a.w[e];
+                        if constexpr (EPV == 8) {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) wv[4 + e] = w0b.w[e];
+                        }
+                    } else {
+                        const Words4 qa = stream_group_in_loop(st, i0 >> 2);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) wv[e] = qa.w[e];
+                        if constexpr (EPV == 8) {
+                            const Words4 qb = stream_group_in_loop(st, (i0 >> 2) + 1);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) wv[4 + e] = qb.w[e];
+                        }
+                    }
+                    uint32_t bits = 0;
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) {
+                        const float x = elem<DT>(raw[n], e);
+                        float U;
+                        if constexpr (HLG) {
+                            U = fmaxf(__builtin_fmaf(x, rc.mt, -rc.mtc), -rc.mtw);
+                        } else {
+                            U = x * rc.invT;
+                        }
+                        const float nb = (float)gumbel_bound_bits(wv[e]);
+                        bits |= (nb >= __builtin_fmaf(U, -kInvLn2, thr_s) ? 1u : 0u) << e;
+                    }
+                    cm[(n * EPV) / 32] |= bits << ((n * EPV) % 32);
+                }
+            }
+
+            // Exact scores of the candidates (rare once the bootstrap has set a threshold).
+            // The barrier stops the compiler from keeping the screen's upcast values alive
+            // until here.
+#pragma unroll
+            for (int n = 0; n < NV; ++n)
+                asm volatile("" : "+v"(raw[n].x), "+v"(raw[n].y), "+v"(raw[n].z), "+v"(raw[n].w));
+#pragma unroll
+            for (int n = 0; n < NV; ++n) {
+                uint32_t bits = (cm[(n * EPV) / 32] >> ((n * EPV) % 32)) & ((1u << EPV) - 1u);
+                const uint32_t i0 = (uint32_t)(lane_v + n * BS) * EPV;
+                while (bits) {
+                    const uint32_t e = (uint32_t)__builtin_ctz(bits);
+                    bits &= bits - 1u;
+                    const float x = elem_dyn<DT>(raw[n], e);
+                    if (x > -__builtin_inff()) {
+                        const uint32_t i = i0 + e;
+                        const Words4 q = stream_group_in_loop(st, i >> 2);
+                        best = umax64(best, make_key(exact_score<HLG>(x, word_dyn(q, i & 3u), rc), i));
+                    }
+                }
+            }
+        }
+        // block reduction of the draw's key
+        const uint64_t kb = block_max_u64(best, redk);
+        if (tid == 0) {
+            const int64_t o = b * a.K + k;
+            if (a.nchunk == 1) {
+                a.out[o] = bad ? -2 : key_index(kb);
+                if (a.best_out) a.best_out[o] = bad ? -__builtin_inff() : key_score(kb);
+            } else if (kb != 0) {
+                atomicMax(reinterpret_cast<unsigned long long *>(a.keys + o),
+                          (unsigned long long)kb);
+            }
+        }
+    }
+
+    // ---- split rows: the last block of the row writes the ids and re-zeroes its slots ----
+    if (a.nchunk > 1) {
+        __threadfence();
+        __syncthreads();
+        if (tid == 0) {
+            const unsigned prev = atomicAdd(a.counters + b, 1u);
+            s_last = (prev == (unsigned)(a.nchunk * a.nkg - 1));
+        }
+        __syncthreads();
+        if (s_last) {
+            __threadfence();
+            for (int k = tid; k < a.K; k += BS) {
+                const int64_t o = b * a.K + k;
+                const uint64_t kk = __hip_atomic_load(a.keys + o, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+                a.out[o] = bad ? -2 : key_index(kk);
+                if (a.best_out) a.best_out[o] = bad ? -__builtin_inff() : key_score(kk);
+                __hip_atomic_store(a.keys + o, (uint64_t)0, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if (tid == 0)
+                __hip_atomic_store(a.counters + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// Per-chunk (max, sum exp(x - max)) pairs for rows split over several blocks.
+template <int DT>
+__global__ __launch_bounds__(1024) void k_lse_partial(SampleArgs a) {
+    using tr = dtype_traits<DT>;
+    constexpr int EPV = tr::epv;
+    __shared__ float redf[16];
+    const int chunk = blockIdx.x % a.nchunk;
+    const int64_t b = blockIdx.x / a.nchunk;
+    const int64_t v0 = (int64_t)chunk * a.cv;
+    const int64_t vend = min(a.nvec, v0 + a.cv);
+    const char *rowp = reinterpret_cast<const char *>(a.data) + b * a.ld * tr::esize;
+    float mx = -__builtin_inff();
+    for (int64_t gv = v0 + threadIdx.x; gv < vend; gv += blockDim.x) {
+        const uint4 v = load_vec<DT>(rowp, gv, a.V, a.aligned);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) mx = fmaxf(mx, elem<DT>(v, e));
+    }
+    const float M = block_max(mx, redf);
+    float s = 0.0f;
+    if (M > -__builtin_inff()) {
+        const float mb = M * kLog2e;
+        for (int64_t gv = v0 + threadIdx.x; gv < vend; gv += blockDim.x) {
+            const uint4 v = load_vec<DT>(rowp, gv, a.V, a.aligned);
+#pragma unroll
+            for (int e = 0; e < EPV; ++e)
+                s += __builtin_amdgcn_exp2f(elem<DT>(v, e) * kLog2e - mb);
+        }
+    }
+    const float S = block_sum(s, redf);
+    if (threadIdx.x == 0) a.partials[b * a.part_stride + chunk] = make_float2(M, S);
+}
+
+// One block per row: log-sum-exp of the row, and (transform) l' = g(x - LSE - mu).
+template <int DT, bool TRANSFORM>
+__global__ __launch_bounds__(1024) void k_row_lse(RowOpArgs a) {
+    using tr = dtype_traits<DT>;
+    constexpr int EPV = tr::epv;
+    __shared__ float redf[16];
+    const int64_t b = blockIdx.x;
+    const int64_t nvec = (a.V + EPV - 1) / EPV;
+    const char *rowp = reinterpret_cast<const char *>(a.data) + b * a.ld * tr::esize;
+    float mx = -__builtin_inff();
+    for (int64_t gv = threadIdx.x; gv < nvec; gv += blockDim.x) {
+        const uint4 v = load_vec<DT>(rowp, gv, a.V, a.aligned);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) mx = fmaxf(mx, elem<DT>(v, e));
+    }
+    const float M = block_max(mx, redf);
+    float s = 0.0f;
+    if (M > -__builtin_inff()) {
+        const float mb = M * kLog2e;
+        for (int64_t gv = threadIdx.x; gv < nvec; gv += blockDim.x) {
+            const uint4 v = load_vec<DT>(rowp, gv, a.V, a.aligned);
+#pragma unroll
+            for (int e = 0; e < EPV; ++e)
+                s += __builtin_amdgcn_exp2f(elem<DT>(v, e) * kLog2e - mb);
+        }
+    }
+    const float S = block_sum(s, redf);
+    const float lse = (M > -__builtin_inff()) ? M + logf(S) : -__builtin_inff();
+    if constexpr (!TRANSFORM) {
+        if (threadIdx.x == 0) a.lse[b] = lse;
+    } else {
+        const float c = lse + a.mu[b];
+        float *orow = a.out + b * a.ldo;
+        for (int64_t gv = threadIdx.x; gv < nvec; gv += blockDim.x) {
+            const uint4 v = load_vec<DT>(rowp, gv, a.V, a.aligned);
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                const int64_t i = gv * EPV + e;
+                if (i < a.V) {
+                    const float x = elem<DT>(v, e);
+                    orow[i] = (x > -__builtin_inff()) ? hlg32(x - c, a.curve) : -__builtin_inff();
+                }
+            }
+        }
+    }
+}
+
+__global__ void k_philox(const uint32_t *__restrict__ ctr, const uint32_t *__restrict__ key,
+                         uint32_t *__restrict__ out, int64_t n) {
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= n) return;
+    const Words4 o = philox4x32_10(ctr[4 * j], ctr[4 * j + 1], ctr[4 * j + 2], ctr[4 * j + 3],
+                                   key[2 * j], key[2 * j + 1]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[4 * j + e] = o.w[e];
+}
+
+__global__ void k_stream_words(const uint64_t *__restrict__ seed,
+                               const uint64_t *__restrict__ offset, int64_t B, int64_t V,
+                               int32_t k, uint32_t *__restrict__ out) {
+    const int64_t ng = (V + 3) / 4;
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= B * ng) return;
+    const int64_t b = j / ng;
+    const uint32_t q = (uint32_t)(j % ng);
+    const uint64_t off = offset[b] + (uint64_t)k;
+    Stream st;
+    st.row = (uint32_t)b;
+    st.off_lo = (uint32_t)off;
+    st.off_hi = (uint32_t)(off >> 32);
+    st.key0 = (uint32_t)seed[b];
+    st.key1 = (uint32_t)(seed[b] >> 32);
+    const Words4 o = stream_group_in_loop(st, q);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int64_t i = (int64_t)q * 4 + e;
+        if (i < V) out[b * V + i] = o.w[e];
+    }
+}
+
+__global__ void k_gumbel(const uint32_t *__restrict__ w, float *__restrict__ g, int64_t n) {
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j < n) g[j] = gumbel32(w[j]);
+}
+
+__global__ void k_fill_zero(uint32_t *__restrict__ p, int64_t n) {
+    for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n;
+         j += (int64_t)gridDim.x * blockDim.x)
+        p[j] = 0u;
+}
+
+// ------------------------------------------------------------------------------------------
+// Host-side launchers (called from hs_api.hip).
+// ------------------------------------------------------------------------------------------
+template <int DT, bool HLG>
+static hipError_t launch_sample_nv(const SampleArgs &a, int nv, int bs, int grid, hipStream_t s) {
+    // Blocks of up to 1024 threads hold up to 19 vectors per thread (128 registers per lane at
+    // 16 waves per CU); longer chunks use blocks of up to 512 threads, which get 256.
+#define HS_CASE(N, MB)                                                                     \
+    case N:                                                                                \
+        if (bs > MB) return hipErrorInvalidValue;                                          \
+        hipLaunchKernelGGL((k_sample<DT, N, HLG, MB>), dim3(grid), dim3(bs), 0, s, a);    \
+        break;
+    switch (nv) {
+        HS_CASE(1, 1024) HS_CASE(2, 1024) HS_CASE(4, 1024) HS_CASE(6, 1024) HS_CASE(8, 1024)
+        HS_CASE(12, 1024) HS_CASE(16, 1024) HS_CASE(18, 1024) HS_CASE(19, 1024)
+        HS_CASE(24, 512) HS_CASE(32, 512) HS_CASE(40, 512)
+        default: return hipErrorInvalidValue;
+    }
+#undef HS_CASE
+    return hipGetLastError();
+}
+
+hipError_t launch_sample(int dt, bool hlg, const SampleArgs &a, int nv, int bs, int grid,
+                         hipStream_t s) {
+    switch (dt) {
+        case DT_F32: return hlg ? launch_sample_nv<DT_F32, true>(a, nv, bs, grid, s)
+                                : launch_sample_nv<DT_F32, false>(a, nv, bs, grid, s);
+        case DT_BF16: return hlg ? launch_sample_nv<DT_BF16, true>(a, nv, bs, grid, s)
+                                 : launch_sample_nv<DT_BF16, false>(a, nv, bs, grid, s);
+        case DT_F16: return hlg ? launch_sample_nv<DT_F16, true>(a, nv, bs, grid, s)
+                                : launch_sample_nv<DT_F16, false>(a, nv, bs, grid, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_lse_partial(int dt, const SampleArgs &a, int bs, int grid, hipStream_t s) {
+    switch (dt) {
+        case DT_F32: hipLaunchKernelGGL((k_lse_partial<DT_F32>), dim3(grid), dim3(bs), 0, s, a); break;
+        case DT_BF16: hipLaunchKernelGGL((k_lse_partial<DT_BF16>), dim3(grid), dim3(bs), 0, s, a); break;
+        case DT_F16: hipLaunchKernelGGL((k_lse_partial<DT_F16>), dim3(grid), dim3(bs), 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_row_lse(int dt, bool transform, const RowOpArgs &a, int grid, hipStream_t s) {
+    const int bs = 1024;
+#define HS_ROW(D)                                                                              \
+    if (transform) hipLaunchKernelGGL((k_row_lse<D, true>), dim3(grid), dim3(bs), 0, s, a);  \
+    else hipLaunchKernelGGL((k_row_lse<D, false>), dim3(grid), dim3(bs), 0, s, a);
+    switch (dt) {
+        case DT_F32: HS_ROW(DT_F32) break;
+        case DT_BF16: HS_ROW(DT_BF16) break;
+        case DT_F16: HS_ROW(DT_F16) break;
+        default: return hipErrorInvalidValue;
+    }
+#undef HS_ROW
+    return hipGetLastError();
+}
+
+hipError_t launch_philox(const uint32_t *ctr, const uint32_t *key, uint32_t *out, int64_t n,
+                         hipStream_t s) {
+    const int bs = 256;
+    const int64_t grid = (n + bs - 1) / bs;
+    hipLaunchKernelGGL(k_philox, dim3((unsigned)grid), dim3(bs), 0, s, ctr, key, out, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_stream_words(const uint64_t *seed, const uint64_t *offset, int64_t B,
+                               int64_t V, int32_t k, uint32_t *out, hipStream_t s) {
+    const int bs = 256;
+    const int64_t n = B * ((V + 3) / 4);
+    const int64_t grid = (n + bs - 1) / bs;
+    hipLaunchKernelGGL(k_stream_words, dim3((unsigned)grid), dim3(bs), 0, s, seed, offset, B, V,
+                       k, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_gumbel(const uint32_t *w, float *g, int64_t n, hipStream_t s) {
+    const int bs = 256;
+    const int64_t grid = (n + bs - 1) / bs;
+    hipLaunchKernelGGL(k_gumbel, dim3((unsigned)grid), dim3(bs), 0, s, w, g, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void *p, int64_t nwords, hipStream_t s) {
+    const int bs = 256;
+    int64_t grid = (nwords + bs - 1) / bs;
+    if (grid > 4096) grid = 4096;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)grid), dim3(bs), 0, s,
+                       reinterpret_cast<uint32_t *>(p), nwords);
+    return hipGetLastError();
+}
+
+}  // namespace hs

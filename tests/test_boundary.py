@@ -1,0 +1,163 @@
+"""The C-ABI boundary without a GPU: the library loads, exports every symbol include/hs.h
+declares, and rejects every host-checkable bad argument with its status code before any
+work is enqueued (no device is touched by these calls)."""
+import ctypes as C
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+hs = pytest.importorskip("logit_transform_amd")
+
+HS_OK, HS_ERR_INVALID_ARG, HS_ERR_DTYPE, HS_ERR_WORKSPACE, HS_ERR_HIP, HS_ERR_UNSUPPORTED = \
+    0, -1, -2, -3, -4, -5
+FAKE = 0x10000            # never dereferenced: every case below fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hs.library_path()):
+        pytest.skip("libhs.so not built")
+    return hs.load()
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "hs.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hs_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    syms = declared_symbols()
+    for name in ("hs_logsumexp", "hs_hlg_transform", "hs_gumbel_argmax", "hs_sample"):
+        assert name in syms
+    assert sorted(hs.EXPORTED_SYMBOLS) == syms
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    for code in (HS_OK, HS_ERR_INVALID_ARG, HS_ERR_DTYPE, HS_ERR_WORKSPACE, HS_ERR_HIP,
+                 HS_ERR_UNSUPPORTED):
+        s = lib.hs_status_str(code).decode()
+        assert s.startswith("HS_")
+    assert "unknown" in lib.hs_status_str(12345).decode()
+    assert "gfx950" in hs.version()
+
+
+def L(B=4, V=100, ld=None, dtype=0, data=FAKE):
+    return hs._Logits(data, dtype, B, V, V if ld is None else ld)
+
+
+def H(m=1.5, w=2.0, bt=1.0, bh=2.0):
+    return hs.HlgParams(m, w, bt, bh)
+
+
+def sample(lib, x, T=FAKE, mu=FAKE, hlg=None, seed=FAKE, off=FAKE, K=1, out=FAKE, ws=None,
+           nbytes=0):
+    return lib.hs_sample(C.byref(x), T, mu, C.byref(hlg) if hlg is not None else None, seed, off,
+                         K, out, ws, nbytes, None)
+
+
+@pytest.mark.parametrize("x,code", [
+    (L(data=0), HS_ERR_INVALID_ARG),
+    (L(B=0), HS_ERR_INVALID_ARG),
+    (L(B=-3), HS_ERR_INVALID_ARG),
+    (L(V=0), HS_ERR_INVALID_ARG),
+    (L(V=100, ld=99), HS_ERR_INVALID_ARG),
+    (L(dtype=7), HS_ERR_DTYPE),
+    (L(dtype=-1), HS_ERR_DTYPE),
+    (L(V=2**31, ld=2**31), HS_ERR_UNSUPPORTED),
+])
+def test_bad_logits(lib, x, code):
+    assert sample(lib, x) == code
+    assert lib.hs_gumbel_argmax(C.byref(x), FAKE, FAKE, FAKE, 1, FAKE, None, 0, None) == code
+    assert lib.hs_logsumexp(C.byref(x), FAKE, None) == code
+    h = H()
+    assert lib.hs_hlg_transform(C.byref(x), FAKE, C.byref(h), FAKE, max(x.V, 1), None) == code
+
+
+def test_null_logits_struct(lib):
+    assert lib.hs_sample(None, FAKE, None, None, FAKE, FAKE, 1, FAKE, None, 0, None) == HS_ERR_INVALID_ARG
+    assert lib.hs_logsumexp(None, FAKE, None) == HS_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(T=None), dict(seed=None), dict(off=None), dict(out=None),
+                                dict(K=0), dict(K=-2)])
+def test_bad_sample_args(lib, kw):
+    assert sample(lib, L(), **kw) == HS_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("h", [H(m=0.0), H(m=-1.0), H(m=math.inf), H(m=math.nan), H(w=-0.5),
+                               H(w=math.nan), H(bt=0.0), H(bt=math.inf), H(bh=-1.0),
+                               H(bh=math.nan)])
+def test_bad_curve(lib, h):
+    assert sample(lib, L(), hlg=h) == HS_ERR_INVALID_ARG
+    x = L()
+    assert lib.hs_hlg_transform(C.byref(x), FAKE, C.byref(h), FAKE, 100, None) == HS_ERR_INVALID_ARG
+
+
+def test_curve_needs_mu(lib):
+    assert sample(lib, L(), hlg=H(), mu=None) == HS_ERR_INVALID_ARG
+
+
+def test_rolloff_off_is_accepted_by_validation(lib):
+    # w = +inf is valid; with a too-small workspace the call stops at the workspace check
+    assert sample(lib, L(), hlg=H(w=math.inf), ws=FAKE, nbytes=8) == HS_ERR_WORKSPACE
+
+
+def test_transform_args(lib):
+    x = L()
+    h = H()
+    assert lib.hs_hlg_transform(C.byref(x), None, C.byref(h), FAKE, 100, None) == HS_ERR_INVALID_ARG
+    assert lib.hs_hlg_transform(C.byref(x), FAKE, None, FAKE, 100, None) == HS_ERR_INVALID_ARG
+    assert lib.hs_hlg_transform(C.byref(x), FAKE, C.byref(h), None, 100, None) == HS_ERR_INVALID_ARG
+    assert lib.hs_hlg_transform(C.byref(x), FAKE, C.byref(h), FAKE, 99, None) == HS_ERR_INVALID_ARG
+    assert lib.hs_logsumexp(C.byref(x), None, None) == HS_ERR_INVALID_ARG
+
+
+def test_workspace_sizes(lib):
+    n = lib.hs_workspace_bytes(256, 151936, 1, 1, 1)
+    assert n > 0 and n % 256 == 0
+    assert lib.hs_workspace_bytes(256, 151936, 16, 1, 1) > n
+    assert lib.hs_workspace_bytes(0, 10, 1, 0, 0) == 0
+    assert lib.hs_workspace_bytes(1, 10, 0, 0, 0) == 0
+    assert lib.hs_workspace_bytes(1, 10, 1, 9, 0) == 0
+    # a given-but-too-small workspace is reported, not ignored
+    assert sample(lib, L(), ws=FAKE, nbytes=n // 1000 or 8) == HS_ERR_WORKSPACE
+    assert lib.hs_workspace_init(None, 256, None) == HS_ERR_INVALID_ARG
+    assert lib.hs_workspace_init(FAKE, 3, None) == HS_ERR_INVALID_ARG
+
+
+def test_sample_ex_opts(lib):
+    x = L()
+    for o in (hs.SampleOpts(variant=3), hs.SampleOpts(variant=-1), hs.SampleOpts(nchunk=-1),
+              hs.SampleOpts(nchunk=65), hs.SampleOpts(draw_groups=-2)):
+        assert lib.hs_sample_ex(C.byref(x), FAKE, None, None, FAKE, FAKE, 1, FAKE, None, None, 0,
+                                C.byref(o), None) == HS_ERR_INVALID_ARG
+
+
+def test_aux_entry_points(lib):
+    assert lib.hs_philox4x32_10(None, FAKE, FAKE, 4, None) == HS_ERR_INVALID_ARG
+    assert lib.hs_philox4x32_10(FAKE, FAKE, FAKE, -1, None) == HS_ERR_INVALID_ARG
+    assert lib.hs_philox4x32_10(FAKE, FAKE, FAKE, 0, None) == HS_OK
+    assert lib.hs_stream_words(FAKE, FAKE, 0, 10, 0, FAKE, None) == HS_ERR_INVALID_ARG
+    assert lib.hs_stream_words(FAKE, FAKE, 1, 10, -1, FAKE, None) == HS_ERR_INVALID_ARG
+    assert lib.hs_stream_words(FAKE, None, 1, 10, 0, FAKE, None) == HS_ERR_INVALID_ARG
+    assert lib.hs_gumbel_f32(None, FAKE, 3, None) == HS_ERR_INVALID_ARG
+    assert lib.hs_gumbel_f32(FAKE, FAKE, 0, None) == HS_OK
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(2, 8)
+    with pytest.raises(ValueError):
+        hs.sample(x, [1.0, 1.0], [1, 2], [0, 0])
+    with pytest.raises(ValueError):
+        hs.logsumexp(x)

@@ -1,0 +1,164 @@
+"""Edge cases, kernel-variant invariance and determinism of the HIP path, against the oracle.
+
+Edge cases: tiny and ragged vocabularies, rows with no finite logit (-1), invalid
+temperatures and pivots (-2), greedy rows with ties (T = 0, curve on or off), rolloff off
+(w = inf), fp16 input, rows that are not 16-byte aligned, offsets that carry across 2^32 and
+wrap at 2^64, and rows split over many blocks.
+
+Invariance: the index of every draw is a function of (seed, row, element, offset) only, so
+one-block-per-row, split rows, screened and exhaustive scoring, and any spreading of draws
+over blocks must agree (mlxcel issue "Softmax-free GPU sampling", section Background:
+stateless and reproducible; section Regression guard: determinism)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from synth import workloads as W
+from tests.gpu_util import assert_parity, gpu_sample, on_device, oracle_sample, require_gpu
+
+pytestmark = pytest.mark.gpu
+HLG_A = {"m": 1.5, "w": 2.0, "beta_t": 1.0, "beta_h": 2.0}
+
+
+@pytest.fixture(scope="module")
+def hs():
+    return require_gpu()
+
+
+def _check(hs, O, w, label, **kw):
+    g = gpu_sample(hs, w, **kw)
+    o, s1, s2 = oracle_sample(O, w)
+    return assert_parity(g, o, s1, s2, w.logits.double().numpy(), label)
+
+
+@pytest.mark.parametrize("V", [1, 2, 3, 5, 8, 9, 31, 33, 1000, 4097, 65537])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("hlg", [None, HLG_A])
+def test_ragged_vocab(hs, oracle_mod, V, dtype, hlg):
+    w = W.generic(3, V, dtype, seed=V, mask_frac=0.1 if V > 4 else 0.0, hlg=hlg, K=3,
+                  offset_max=2**33)
+    _check(hs, oracle_mod, w, "V=%d %s hlg=%s" % (V, dtype, hlg is not None))
+
+
+def test_fp16_and_misaligned_rows(hs, oracle_mod):
+    w = W.generic(6, 3001, torch.float16, seed=21, mask_frac=0.25, hlg=HLG_A, K=2)
+    _check(hs, oracle_mod, w, "f16")
+    big = torch.full((6, 3004), float("-inf"), dtype=torch.float16)
+    big[:, :3001] = w.logits
+    d = on_device(w)
+    x = big.cuda()[:, :3001]
+    g = hs.sample(x, d["T"], d["seed"], d["offset"], mu=d["mu"], hlg=w.hlg, k=2).cpu().numpy()
+    o, s1, s2 = oracle_sample(oracle_mod, w)
+    assert_parity(g, o, s1, s2, w.logits.double().numpy(), "f16 misaligned")
+
+
+def test_special_rows(hs, oracle_mod):
+    V = 777
+    rng = np.random.default_rng(31)
+    x = rng.normal(0, 1, size=(8, V)).astype(np.float32)
+    x[0, :] = -np.inf                                  # no finite logit -> -1
+    x[1, :] = -np.inf
+    x[1, 400] = 2.5                                    # a single finite logit
+    x[2, [3, 50, 600]] = 9.0                           # greedy with a three-way tie
+    x[3, [10, 11]] = 4.0
+    T = np.array([1.0, 0.7, 0.0, 0.0, -1.0, np.nan, np.inf, 1.2], dtype=np.float32)
+    mu = np.array([-5, -5, -5, -5, -5, -5, -5, np.nan], dtype=np.float32)
+    seed = rng.integers(0, 2**64, size=8, dtype=np.uint64)
+    off = np.array([0, 2**32 - 1, 5, 5, 0, 0, 0, 0], dtype=np.uint64)
+    for hlg in (None, HLG_A):
+        w = W.Workload("special", torch.from_numpy(x), T, seed, off, K=3, hlg=hlg,
+                       mu=mu if hlg else None)
+        g = gpu_sample(hs, w)
+        o, s1, s2 = oracle_sample(oracle_mod, w)
+        assert_parity(g, o, s1, s2, x.astype(np.float64), "special rows hlg=%s" % bool(hlg))
+        assert g[0].tolist() == [-1] * 3
+        assert g[1].tolist() == [400] * 3
+        assert g[2].tolist() == [3] * 3 and g[3].tolist() == [10] * 3
+        assert g[4].tolist() == [-2] * 3 and g[5].tolist() == [-2] * 3 and g[6].tolist() == [-2] * 3
+        if hlg:
+            assert g[7].tolist() == [-2] * 3
+
+
+def test_rolloff_off_equals_temperature(hs):
+    """Rolloff off (w = inf) with gain m is temperature 1/m (HLG design document, section
+    "The degeneracies are the safety anchors"): the same draws as the curve-off path at
+    temperature T/m, the log-softmax shift being common to all tokens."""
+    w = W.generic(16, 20000, torch.float32, seed=41, K=4)
+    d = on_device(w)
+    m = 1.0 / 0.7
+    a = hs.sample(d["logits"], d["T"], d["seed"], d["offset"], mu=torch.zeros(16, device="cuda"),
+                  hlg=(m, math.inf, 1.0, 1.0), k=4).cpu().numpy()
+    b = hs.sample(d["logits"], d["T"] / m, d["seed"], d["offset"], k=4).cpu().numpy()
+    # the two paths round differently ((x - LSE - mu) * m/T against x * m/T), which can only
+    # flip a near-tie
+    assert (a != b).sum() <= 1
+
+
+def test_offsets_wrap(hs, oracle_mod):
+    w = W.generic(4, 5000, torch.float32, seed=51, K=5)
+    w.offset = np.array([2**64 - 2, 2**32 - 3, 0, 2**63], dtype=np.uint64)
+    _check(hs, oracle_mod, w, "offset wrap")
+
+
+@pytest.mark.parametrize("hlg", [None, HLG_A])
+def test_variant_invariance(hs, oracle_mod, hlg):
+    w = W.generic(6, 151936, torch.bfloat16, seed=61, scale=0.8, mask_frac=0.05, hlg=hlg, K=3)
+    d = on_device(w)
+    o, s1, s2 = oracle_sample(oracle_mod, w)
+    x64 = w.logits.double().numpy()
+    results = {}
+    for name, opts in [("auto", None),
+                       ("one-block", hs.SampleOpts(variant=1)),
+                       ("split2", hs.SampleOpts(variant=2, nchunk=2)),
+                       ("split7", hs.SampleOpts(variant=2, nchunk=7)),
+                       ("split64", hs.SampleOpts(variant=2, nchunk=64)),
+                       ("one-block-exhaustive", hs.SampleOpts(variant=1, no_screen=1)),
+                       ("split7-exhaustive", hs.SampleOpts(variant=2, nchunk=7, no_screen=1)),
+                       ("draw-groups", hs.SampleOpts(variant=1, draw_groups=3))]:
+        idx, best = hs.sample_ex(d["logits"], d["T"], d["seed"], d["offset"], mu=d.get("mu"),
+                                 hlg=hlg, k=3, opts=opts, want_best=True)
+        idx = idx.cpu().numpy()
+        results[name] = (idx, best.cpu().numpy())
+        assert_parity(idx, o, s1, s2, x64, name)
+    # screening never changes a result: same variant, screened vs exhaustive, bit-identical
+    for a, b in [("one-block", "one-block-exhaustive"), ("split7", "split7-exhaustive")]:
+        np.testing.assert_array_equal(results[a][0], results[b][0])
+        np.testing.assert_array_equal(results[a][1], results[b][1])
+    # without the curve nothing depends on the decomposition at all
+    if hlg is None:
+        for name in results:
+            np.testing.assert_array_equal(results[name][1], results["one-block"][1])
+
+
+def test_determinism(hs):
+    w = W.config4(B=32)
+    d = on_device(w)
+    a = gpu_sample(hs, w, dev=d)
+    for _ in range(3):
+        np.testing.assert_array_equal(gpu_sample(hs, w, dev=d), a)
+
+
+def test_k_draws_equal_single_draws(hs):
+    w = W.generic(5, 30000, torch.bfloat16, seed=71, hlg=HLG_A, K=8)
+    d = on_device(w)
+    allk = gpu_sample(hs, w, dev=d)
+    for k in range(8):
+        one = hs.sample(d["logits"], d["T"], d["seed"], d["offset"] + k, mu=d["mu"], hlg=HLG_A, k=1)
+        np.testing.assert_array_equal(one.cpu().numpy()[:, 0], allk[:, k])
+
+
+def test_workspace_left_clean(hs):
+    """A split call leaves its workspace zero-filled, so calls can reuse it."""
+    w = W.generic(2, 100000, torch.float32, seed=81, hlg=HLG_A, K=4)
+    d = on_device(w)
+    ws = hs.workspace(2, 100000, 4, torch.float32, True)
+    outs = [hs.sample_ex(d["logits"], d["T"], d["seed"], d["offset"], mu=d["mu"], hlg=HLG_A, k=4,
+                         ws=ws, opts=hs.SampleOpts(variant=2, nchunk=9)).cpu().numpy()
+            for _ in range(3)]
+    torch.cuda.synchronize()
+    n_keys = 256 + 2 * 4 * 8
+    assert int(ws[:n_keys].to(torch.int32).abs().sum()) == 0
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0])
