@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Benchmark of the sampling step on one MI355X: sampled rows/s and achieved HBM GB/s for
+[B, V] logits -> token ids.
+
+Default workload: B=256 x V=151936 bf16 logits ~ N(0, 0.5^2), per-row T ~ U[0.3, 1.5],
+per-row seeds and offsets, HLG curve (m=1.25, w=1.5, beta_t=0.5, beta_h=1.0) fused with the
+Gumbel-max draw in one launch. One step = one hs_sample call over the batch. Inputs are
+resident in HBM before timing starts; five copies of the logits (389 MB, more than the
+256 MB last-level cache) are used in turn so every step reads its logits from HBM.
+
+Prints ONE JSON line on stdout (details on stderr). The CPU baseline is the double-precision
+oracle timed on this host's cores on a bounded sample of the same rows.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("sampled rows/sec and achieved HBM GB/s (% of peak) for [B,V] logits → token "
+          "ids")
+HBM_PEAK_GBPS = 8000.0
+# VALU lane-operations per second of MI355X: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.
+ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# Algorithmic VALU operations per element and draw ("Roofline"):
+# Philox4x32-10 share 10 (10 rounds x 2 mul-hi/lo + 2 three-way xor, per 4 words),
+# upcast 1, compare 1; plus, once per element with the curve on, the log-sum-exp's
+# max / exponent-argument / exp / add (4).
+OPS_PER_ELEMENT_DRAW = 12
+OPS_PER_ELEMENT_LSE = 4
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("hs_kernels.hip", "hs_device.hpp", "hs_api.hip", "hs_internal.hpp"):
+        with open(os.path.join(ROOT, "logit_transform_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", "traffic_%s.json" % name)
+    if not os.path.exists(p):
+        return None
+    try:
+        with open(p) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_digest") != kernel_source_digest():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float = 10.0):
+    """The oracle as it stands, on the first rows of the workload, all host cores."""
+    import numpy as np
+    from oracle import oracle as O
+    cores = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+    threads = int(os.environ["OMP_NUM_THREADS"])
+    O.lib()
+    n = min(w.B, max(threads, 8))
+    t0 = time.perf_counter()
+    O.sample(w.logits[:n], w.T[:n], w.seed[:n], w.offset[:n], K=w.K,
+             mu=None if w.hlg is None else w.mu[:n], hlg=w.hlg)
+    t1 = time.perf_counter()
+    per_row = (t1 - t0) / n
+    n2 = int(min(w.B, max(n, budget_s / max(per_row, 1e-9))))
+    if n2 > n:
+        t0 = time.perf_counter()
+        O.sample(w.logits[:n2], w.T[:n2], w.seed[:n2], w.offset[:n2], K=w.K,
+                 mu=None if w.hlg is None else w.mu[:n2], hlg=w.hlg)
+        t1 = time.perf_counter()
+        n = n2
+    return {"value": n / (t1 - t0), "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": "first %d of %d rows of the same workload (%d draw(s) each), "
+                      "%.1f s wall on %d OpenMP threads" % (n, w.B, w.K, t1 - t0, threads)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=4,
+                    help="workload: 4 = the 256 x 151936 bf16 headline (default); 1, 2, 3, 5 "
+                         "for the other workloads of the pages")
+    ap.add_argument("--copies", type=int, default=5, help="rotating input copies (cold cache)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run a plain device copy of MIB MiB five "
+                         "times (reference for scaling the memory-traffic counters)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the sampling step has no multi-GPU path in this "
+              "build (--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import logit_transform_amd as hs
+    from synth import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copied %d bytes x 5" % n)
+        return
+    L = hs.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.CONFIGS[args.config]()
+    B, V, K = w.B, w.V, w.K
+    log("workload:", w.name)
+
+    copies = [w.logits.to(dev)]
+    for _ in range(max(0, args.copies - 1)):
+        copies.append(copies[0].clone())
+    T = torch.from_numpy(w.T).to(dev)
+    seed = torch.from_numpy(w.seed.view(np.int64)).to(dev)
+    off = torch.from_numpy(w.offset.view(np.int64)).to(dev)
+    mu = torch.from_numpy(w.mu).to(dev) if w.hlg is not None else None
+    hp = hs._hlg_struct(w.hlg)
+    out = torch.empty((B, K), dtype=torch.int32, device=dev)
+    ws = hs.workspace(B, V, K, w.dtype, hp is not None, dev)
+    structs = [hs._logits_struct(x) for x in copies]
+    stream = hs._stream(dev)
+    hp_ref = C.byref(hp) if hp is not None else None
+    mu_ptr = mu.data_ptr() if mu is not None else None
+    fn = L.hs_sample
+
+    def step(i):
+        rc = fn(C.byref(structs[i % len(structs)]), T.data_ptr(), mu_ptr, hp_ref,
+                seed.data_ptr(), off.data_ptr(), K, out.data_ptr(), ws.data_ptr(), ws.numel(),
+                stream)
+        if rc != 0:
+            raise hs.HsError(rc, "hs_sample")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ref_ids = out.clone()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_all0.record()
+    for i in range(args.steps):
+        starts[i].record()
+        step(i)
+        ends[i].record()
+    t_all1.record()
+    torch.cuda.synchronize()
+    wall1 = time.perf_counter()
+    total_ms = t_all0.elapsed_time(t_all1)
+    per_launch = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    kern_ms = sum(per_launch) / len(per_launch)
+    ms_per_step = total_ms / args.steps
+    if not torch.equal(out, ref_ids):
+        raise RuntimeError("sampled ids changed between identical steps")
+
+    rows_per_s = B / (ms_per_step / 1e3)
+    logit_bytes = B * V * w.logits.element_size()
+    param_bytes = B * (4 + 8 + 8 + (4 if mu is not None else 0))
+    alg_bytes = logit_bytes + param_bytes + 4 * B * K
+    gbps = alg_bytes / (kern_ms / 1e3) / 1e9
+    ops = B * V * (OPS_PER_ELEMENT_DRAW * K + (OPS_PER_ELEMENT_LSE if mu is not None else 0))
+    tops = ops / (kern_ms / 1e3) / 1e12
+    name = "k_sample_c%d" % args.config
+    traffic = load_traffic(name)
+    log("kernel avg %.4f ms (p10 %.4f p50 %.4f p90 %.4f), step %.4f ms, wall %.4f ms/step"
+        % (kern_ms, per_launch[len(per_launch) // 10], per_launch[len(per_launch) // 2],
+           per_launch[(9 * len(per_launch)) // 10], ms_per_step,
+           (wall1 - wall0) * 1e3 / args.steps))
+    log("HBM %.1f GB/s = %.1f%% of 8 TB/s; VALU %.2f T op/s = %.1f%% of %.1f"
+        % (gbps, 100 * gbps / HBM_PEAK_GBPS, tops, 100 * tops / ALU_PEAK_TOPS, ALU_PEAK_TOPS))
+
+    rec = {
+        "metric": METRIC,
+        "value": rows_per_s,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "V": V, "K": K,
+                   "input_dtype": str(w.dtype).replace("torch.", ""),
+                   "hlg": w.hlg is not None, "input_copies": len(copies),
+                   "algorithmic_bytes_per_step": alg_bytes},
+        "roofline": {"bound": "alu", "achieved": tops, "peak": ALU_PEAK_TOPS,
+                     "unit": "T VALU-op/s", "frac": tops / ALU_PEAK_TOPS, "traffic": traffic,
+                     "kernel": name, "kernel_ms": kern_ms,
+                     "ops_per_step": ops},
+        "hbm": {"achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": gbps / HBM_PEAK_GBPS},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w)
+        log("cpu baseline:", rec["cpu_baseline"])
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

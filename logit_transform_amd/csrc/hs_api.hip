@@ -13,11 +13,10 @@ namespace {
 
 using hs::SampleArgs;
 
-// Register-resident vectors per thread that kernels are generated for: up to 19 with blocks
-// of up to 1024 threads, 24 / 32 / 40 with blocks of 512 threads.
-constexpr int kNvBuckets1024[] = {1, 2, 4, 6, 8, 12, 16, 18, 19};
-constexpr int kNvBuckets512[] = {24, 32, 40};
-constexpr int64_t kBlockCapacity = 40 * 512;   // vectors one block can hold
+// Register-resident vectors per thread that kernels are generated for (blocks of up to 1024
+// threads, 128 registers per lane).
+constexpr int kNvBuckets[] = {1, 2, 4, 6, 8, 12, 16, 19};
+constexpr int64_t kBlockCapacity = 19 * 1024;   // vectors one block can hold
 
 inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
@@ -94,25 +93,16 @@ bool pick_block(int64_t cv, int *bs, int *nv) {
     int b = 1024;
     if (cv <= 256 * 4) b = 256;
     else if (cv <= 512 * 8) b = 512;
-    int64_t per = (cv + b - 1) / b;
-    if (per > 19 && b == 1024) {
-        b = 512;
-        per = (cv + b - 1) / b;
-    }
-    if (per <= 19) {
-        for (int x : kNvBuckets1024)
-            if (per <= x) { *bs = b; *nv = x; return true; }
-    }
-    if (b == 512) {
-        for (int x : kNvBuckets512)
-            if (per <= x) { *bs = b; *nv = x; return true; }
-    }
+    const int64_t per = (cv + b - 1) / b;
+    for (int x : kNvBuckets)
+        if (per <= x) { *bs = b; *nv = x; return true; }
     return false;
 }
 
-// Kernel shape for a call. Rows that fit one block (<= kNvMax * 1024 vectors) keep one
-// block per row unless the batch is too small to fill the GPU, in which case rows are split
-// into chunks of >= 512 vectors; a small grid with several draws also spreads the draws.
+// Kernel shape for a call. Rows that fit one block (kBlockCapacity vectors) keep one block
+// per row, so each row is read once, unless the batch would leave more than half of the
+// CUs idle; then rows are split into chunks of >= 512 vectors (aiming at two blocks per CU).
+// A grid that is still small spreads a row's draws over several blocks.
 int make_plan(const hs_logits *x, int32_t K, bool ws_ok, const hs_sample_opts *o, Plan *P) {
     const int64_t B = x->B;
     const int64_t nvec = (x->V + epv_of(x->dtype) - 1) / epv_of(x->dtype);
@@ -126,7 +116,7 @@ int make_plan(const hs_logits *x, int32_t K, bool ws_ok, const hs_sample_opts *o
         nchunk = 1;
     } else if (variant == 2 && o->nchunk > 0) {
         nchunk = o->nchunk;
-    } else if (variant == 2 || (ws_ok && B * nchunk_min < target)) {
+    } else if (variant == 2 || (ws_ok && 2 * B * nchunk_min < (int64_t)num_cus())) {
         int64_t want = (target + B - 1) / B;
         int64_t lim = nvec / 512;
         if (lim < 1) lim = 1;
@@ -314,7 +304,7 @@ int hs_philox4x32_10(const uint32_t *ctr, const uint32_t *key, uint32_t *out, in
 int hs_stream_words(const uint64_t *seed, const uint64_t *offset, int64_t B, int64_t V,
                     int32_t k, uint32_t *out, void *stream) {
     if (!seed || !offset || !out || B < 1 || V < 1 || k < 0) return HS_ERR_INVALID_ARG;
-    if (V >= ((int64_t)1 << 31) || B >= ((int64_t)1 << 31)) return HS_ERR_UNSUPPORTED;
+    if (V >= ((int64_t)1 << 31) || B > 65535) return HS_ERR_UNSUPPORTED;
     return hs::launch_stream_words(seed, offset, B, V, k, out, reinterpret_cast<hipStream_t>(stream))
                    == hipSuccess ? HS_OK : HS_ERR_HIP;
 }

@@ -70,6 +70,49 @@ __device__ __forceinline__ Words4 philox4x32_10(uint32_t c0, uint32_t c1, uint32
     return o;
 }
 
+// The same function for a wave-uniform key (k0, k1 in scalar registers), as the sampling
+// kernels have it. From the third round on, both counter words that enter the xors are
+// per-lane, and the compiler emits two v_xor_b32 per word; gfx950's three-input bitwise
+// v_bitop3_b32 with truth table 0x96 (a ^ b ^ c) and the round key as its scalar operand
+// does the same work in one. The first two rounds keep plain code: there one operand of each
+// xor is itself uniform and folds into the scalar unit.
+__device__ __forceinline__ uint32_t xor3_sk(uint32_t a, uint32_t b, uint32_t k) {
+    uint32_t r;
+    asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
+    return r;
+}
+
+__device__ __forceinline__ Words4 philox4x32_10_uk(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                   uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u;
+        const uint64_t p1 = (uint64_t)c2 * 0xCD9E8D57u;
+        uint32_t n0, n2;
+        if (r < 2) {
+            n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+            n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        } else {
+            n0 = xor3_sk((uint32_t)(p1 >> 32), c1, k0);
+            n2 = xor3_sk((uint32_t)(p0 >> 32), c3, k1);
+        }
+        c1 = (uint32_t)p1;
+        c3 = (uint32_t)p0;
+        c0 = n0;
+        c2 = n2;
+    }
+    Words4 o;
+    o.w[0] = c0;
+    o.w[1] = c1;
+    o.w[2] = c2;
+    o.w[3] = c3;
+    return o;
+}
+
 // Random words of the element group q (elements 4q..4q+3) of draw stream (seed, row, off)
 // [GMX, Task 1: "philox(seed, row, i, offset)"]: counter (q, row, off lo, off hi),
 // key (seed lo, seed hi); element i takes word i & 3.
@@ -77,8 +120,9 @@ struct Stream {
     uint32_t row, off_lo, off_hi, key0, key1;
 };
 
+// The stream's row, offset and key must be wave-uniform (one row per block).
 __device__ __forceinline__ Words4 stream_group(const Stream &s, uint32_t q) {
-    return philox4x32_10(q, s.row, s.off_lo, s.off_hi, s.key0, s.key1);
+    return philox4x32_10_uk(q, s.row, s.off_lo, s.off_hi, s.key0, s.key1);
 }
 
 // Same, for use inside a loop over draws: the group index is made opaque so that the
@@ -86,7 +130,7 @@ __device__ __forceinline__ Words4 stream_group(const Stream &s, uint32_t q) {
 // (which costs two registers per group and spills).
 __device__ __forceinline__ Words4 stream_group_in_loop(const Stream &s, uint32_t q) {
     asm volatile("" : "+v"(q));
-    return philox4x32_10(q, s.row, s.off_lo, s.off_hi, s.key0, s.key1);
+    return philox4x32_10_uk(q, s.row, s.off_lo, s.off_hi, s.key0, s.key1);
 }
 
 // ------------------------------------------------------------------------------------------

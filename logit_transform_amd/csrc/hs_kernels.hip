@@ -92,17 +92,51 @@ __device__ __forceinline__ uint64_t greedy_vec(uint4 raw, uint32_t i0, uint64_t 
     return best;
 }
 
+__device__ __forceinline__ uint32_t ffbh_u32(uint32_t v) {
+    // leading-zero count; all ones (0xFFFFFFFF) for v == 0
+    uint32_t r;
+    asm("v_ffbh_u32 %0, %1" : "=v"(r) : "v"(v));
+    return r;
+}
+
+// 4-bit screening code of a word: min(clz(~r), 15). With n = clz(~r) the word's Gumbel value
+// is at most (n + 1) ln 2; code 15 stands for "15 or more" (bound 33 ln 2).
+__device__ __forceinline__ uint32_t word_code(uint32_t r) {
+    const uint32_t n = ffbh_u32(~r);      // 0xFFFFFFFF for r = 0xFFFFFFFF
+    return n < 15u ? n : 15u;
+}
+
+// Which of the 8 codes in cw (4 bits each) are >= t (0..15). Bytes serve as 8-bit lanes (no
+// carry crosses a nibble): code 2j is tested in byte j of the low half, code 2j+1 in byte j
+// of the high half. Bit 8j of the result flags code 2j, bit 8j+1 code 2j+1.
+__device__ __forceinline__ uint32_t codes_ge(uint32_t cw, uint32_t t) {
+    const uint32_t add = (16u - t) * 0x01010101u;
+    const uint32_t lo = ((cw & 0x0F0F0F0Fu) + add) & 0x10101010u;
+    const uint32_t hi = (((cw >> 4) & 0x0F0F0F0Fu) + add) & 0x10101010u;
+    return (lo >> 4) | (hi >> 3);
+}
+
+// Element index of a set bit position of codes_ge's result.
+__device__ __forceinline__ uint32_t codes_bit_elem(uint32_t p) { return ((p >> 3) << 1) | (p & 1u); }
+
 template <int DT, int NV, bool HLG, int MAXBS>
 __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     using tr = dtype_traits<DT>;
     constexpr int EPV = tr::epv;
-    constexpr int NMASK = (NV * EPV + 31) / 32;
+    // Dynamic LDS: per lane and vector the word code of the current draw (EPV nibbles), and
+    // with the curve on the vector's largest logit (draw-invariant). Each lane's entries are
+    // contiguous, so every access is one base register plus an immediate offset.
+    extern __shared__ uint32_t s_dyn[];
     __shared__ float redf[16];
     __shared__ uint64_t redk[16];
     __shared__ int s_last;
 
     const int tid = threadIdx.x;
     const int BS = blockDim.x;
+    constexpr int SC = NV | 1;   // per-lane stride (odd: lanes hit distinct banks)
+    uint32_t *s_codes = s_dyn;
+    float *s_vmax = reinterpret_cast<float *>(s_dyn + SC * BS);
+    const int lane_lds = tid * SC;
     int bid = blockIdx.x;
     const int chunk = bid % a.nchunk;
     bid /= a.nchunk;
@@ -120,8 +154,9 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
         bad = bad || !(fabsf(mu) < __builtin_inff());
     }
     const bool greedy = (T == 0.0f);
+    const bool sampled = !bad && !greedy;
 
-    // ---- load this chunk into registers ----
+    // ---- issue the loads of this chunk (registers) ----
     const int v0 = chunk * (int)a.cv;
     const int vend = (int)min(a.nvec, (int64_t)v0 + a.cv);
     const char *rowp = reinterpret_cast<const char *>(a.data) + b * a.ld * tr::esize;
@@ -137,6 +172,47 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
         }
     }
 
+    const uint64_t seed = a.seed[b];
+    const uint64_t off0 = a.offset[b];
+    Stream st;
+    st.row = (uint32_t)b;
+    st.key0 = (uint32_t)seed;
+    st.key1 = (uint32_t)(seed >> 32);
+
+    // Word codes of draw k for this lane's vectors. Needs no logit, so for the first draw it
+    // runs while the loads above are still in flight.
+    auto write_codes = [&](int k) {
+        const uint64_t off = off0 + (uint64_t)k;
+        Stream sk = st;
+        sk.off_lo = (uint32_t)off;
+        sk.off_hi = (uint32_t)(off >> 32);
+        int lane_v = v0 + tid;
+        asm volatile("" : "+v"(lane_v));
+        uint32_t chain = 0;
+#pragma unroll
+        for (int n = 0; n < NV; ++n) {
+            const int gv = lane_v + n * BS;
+            if (gv < vend) {
+                uint32_t q = ((uint32_t)gv * EPV) >> 2;
+                // start this vector's groups only after the previous vector's code is done,
+                // which bounds the registers the interleaved Philox chains hold
+                asm volatile("" : "+v"(q) : "v"(chain));
+                const Words4 qa = philox4x32_10_uk(q, sk.row, sk.off_lo, sk.off_hi, sk.key0, sk.key1);
+                uint32_t cw = word_code(qa.w[0]) | (word_code(qa.w[1]) << 4) |
+                              (word_code(qa.w[2]) << 8) | (word_code(qa.w[3]) << 12);
+                if constexpr (EPV == 8) {
+                    const Words4 qb = philox4x32_10_uk(q + 1, sk.row, sk.off_lo, sk.off_hi,
+                                                       sk.key0, sk.key1);
+                    cw |= (word_code(qb.w[0]) << 16) | (word_code(qb.w[1]) << 20) |
+                          (word_code(qb.w[2]) << 24) | (word_code(qb.w[3]) << 28);
+                }
+                s_codes[lane_lds + n] = cw;
+                chain = cw;
+            }
+        }
+    };
+    if (sampled && k0 < k1) write_codes(k0);
+
     RowConst rc;
     rc.invT = 1.0f / T;
     rc.c = 0.0f;
@@ -144,70 +220,68 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     rc.curve = a.curve;
     bool skip = bad;
 
-    // ---- log-sum-exp of the row (curve on) [HLG, The transfer function: l = x - LSE(x)].
-    // Computed for every row, greedy and invalid ones included: keeping this block free of
-    // row-dependent branches keeps the register allocator from duplicating the row copy.
+    // ---- log-sum-exp of the row (curve on) [HLG, The transfer function: l = x - LSE(x)],
+    // streamed per lane with a running maximum, plus each vector's largest logit. Computed
+    // for every row: keeping this block free of row-dependent branches keeps the register
+    // allocator from duplicating the row copy.
     if constexpr (HLG) {
-        {
-            float lse;
-            if (a.nchunk == 1) {
-                float mx = -__builtin_inff();
+        float M = -__builtin_inff(), S = 0.0f;
 #pragma unroll
-                for (int n = 0; n < NV; ++n)
+        for (int n = 0; n < NV; ++n) {
+            // Tie this vector to the running sum: otherwise the scheduler issues every
+            // exponential of the row first and holds all results at once.
+            asm volatile("" : "+v"(S), "+v"(raw[n].x), "+v"(raw[n].y), "+v"(raw[n].z),
+                         "+v"(raw[n].w));
+            float xv[EPV];
 #pragma unroll
-                    for (int e = 0; e < EPV; ++e) mx = fmaxf(mx, elem<DT>(raw[n], e));
-                const float M = block_max(mx, redf);
-                float s = 0.0f;
-                if (M > -__builtin_inff()) {
-                    const float mb = M * kLog2e;
+            for (int e = 0; e < EPV; ++e) xv[e] = elem<DT>(raw[n], e);
+            float m = xv[0];
 #pragma unroll
-                    for (int n = 0; n < NV; ++n) {
-                        // Tie this vector to the running sum: otherwise the scheduler issues
-                        // every exponential of the row first and holds all results at once.
-                        asm volatile("" : "+v"(s), "+v"(raw[n].x), "+v"(raw[n].y),
-                                     "+v"(raw[n].z), "+v"(raw[n].w));
-                        float t = 0.0f;
+            for (int e = 1; e < EPV; ++e) m = fmaxf(m, xv[e]);
+            s_vmax[lane_lds + n] = m;
+            const float Mn = fmaxf(M, m);
+            const float mb = (Mn > -__builtin_inff()) ? Mn * kLog2e : 0.0f;
+            S = S * __builtin_amdgcn_exp2f(M * kLog2e - mb);
+            float t = 0.0f;
 #pragma unroll
-                        for (int e = 0; e < EPV; ++e) {
-                            const float x = elem<DT>(raw[n], e);
-                            t += __builtin_amdgcn_exp2f(x * kLog2e - mb);
-                        }
-                        s += t;
-                    }
-                }
-                const float S = block_sum(s, redf);
-                lse = (M > -__builtin_inff()) ? M + logf(S) : -__builtin_inff();
-            } else {
-                const float2 *part = a.partials + b * a.part_stride;
-                float M = -__builtin_inff();
-                for (int j = 0; j < a.nchunk; ++j) M = fmaxf(M, part[j].x);
-                float S = 0.0f;
-                if (M > -__builtin_inff())
-                    for (int j = 0; j < a.nchunk; ++j)
-                        if (part[j].x > -__builtin_inff())
-                            S += part[j].y * __builtin_amdgcn_exp2f((part[j].x - M) * kLog2e);
-                lse = (M > -__builtin_inff()) ? M + logf(S) : -__builtin_inff();
-            }
-            lse = uniform(lse);
-            if (!(lse > -__builtin_inff())) skip = true;   // no finite logit in the row
-            rc.c = uniform(lse + mu);
-            rc.mt = uniform(a.curve.m * rc.invT);
-            rc.mtc = uniform(rc.mt * rc.c);
-            rc.mtw = uniform(rc.mt * a.curve.w);
+            for (int e = 0; e < EPV; ++e) t += __builtin_amdgcn_exp2f(xv[e] * kLog2e - mb);
+            S += t;
+            M = Mn;
         }
+        float lse;
+        if (a.nchunk == 1) {
+            const float Mb = block_max(M, redf);
+            const float sc = (M > -__builtin_inff()) ? S * __builtin_amdgcn_exp2f((M - Mb) * kLog2e)
+                                                     : 0.0f;
+            const float Sb = block_sum(sc, redf);
+            lse = (Mb > -__builtin_inff()) ? Mb + logf(Sb) : -__builtin_inff();
+        } else {
+            const float2 *part = a.partials + b * a.part_stride;
+            float Mb = -__builtin_inff();
+            for (int j = 0; j < a.nchunk; ++j) Mb = fmaxf(Mb, part[j].x);
+            float Sb = 0.0f;
+            if (Mb > -__builtin_inff())
+                for (int j = 0; j < a.nchunk; ++j)
+                    if (part[j].x > -__builtin_inff())
+                        Sb += part[j].y * __builtin_amdgcn_exp2f((part[j].x - Mb) * kLog2e);
+            lse = (Mb > -__builtin_inff()) ? Mb + logf(Sb) : -__builtin_inff();
+        }
+        lse = uniform(lse);
+        if (!(lse > -__builtin_inff())) skip = true;   // no finite logit in the row
+        rc.c = uniform(lse + mu);
+        rc.mt = uniform(a.curve.m * rc.invT);
+        rc.mtc = uniform(rc.mt * rc.c);
+        rc.mtw = uniform(rc.mt * a.curve.w);
     }
 
-    const uint64_t seed = a.seed[b];
-    const uint64_t off0 = a.offset[b];
-
     for (int k = k0; k < k1; ++k) {
+        if (k > k0 && sampled) write_codes(k);
         // Keep per-element work inside the draw loop: without this the compiler hoists the
         // draw-invariant part of the screen (one value per element) out of the loop and runs
-        // out of registers.
+        // out of registers. Likewise for everything derived from the element indices.
 #pragma unroll
         for (int n = 0; n < NV; ++n)
             asm volatile("" : "+v"(raw[n].x), "+v"(raw[n].y), "+v"(raw[n].z), "+v"(raw[n].w));
-        // Likewise for everything derived from the lane's element indices.
         int lane_v = v0 + tid;
         asm volatile("" : "+v"(lane_v));
         uint64_t best = 0;
@@ -219,35 +293,30 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             }
         } else if (!skip) {
             const uint64_t off = off0 + (uint64_t)k;
-            Stream st;
-            st.row = (uint32_t)b;
-            st.off_lo = (uint32_t)off;
-            st.off_hi = (uint32_t)(off >> 32);
-            st.key0 = (uint32_t)seed;
-            st.key1 = (uint32_t)(seed >> 32);
+            Stream sk = st;
+            sk.off_lo = (uint32_t)off;
+            sk.off_hi = (uint32_t)(off >> 32);
 
-            // words of this lane's first vector (kept for the screen below)
-            const int gv0 = lane_v;
-            const uint32_t i00 = (uint32_t)gv0 * EPV;
-            const Words4 w0a = stream_group_in_loop(st, i00 >> 2);
-            Words4 w0b;
-            if constexpr (EPV == 8) w0b = stream_group_in_loop(st, (i00 >> 2) + 1);
-
-            // Bootstrap: each lane scores the element of its first vector with the largest
-            // word exactly; the block maximum is a score some element reaches, so it lower-
-            // bounds the draw's winning score.
+            // Bootstrap: each lane scores exactly the element of its first vector with the
+            // largest word code; the block maximum is a score some element reaches, so it
+            // lower-bounds the draw's winning score.
             float thr_s = -3.0e38f;   // (best known - slack) / ln 2 - 1
             if (!a.no_screen) {
+                const int gv0 = lane_v;
                 if (gv0 < vend) {
-                    uint32_t be = 0, bw = w0a.w[0];
+                    const uint32_t cw = s_codes[lane_lds];
+                    uint32_t be = 0, bc = cw & 15u;
 #pragma unroll
                     for (int e = 1; e < EPV; ++e) {
-                        const uint32_t we = (e < 4) ? w0a.w[e & 3] : w0b.w[e & 3];
-                        if (we > bw) { bw = we; be = (uint32_t)e; }
+                        const uint32_t ce = (cw >> (4 * e)) & 15u;
+                        if (ce > bc) { bc = ce; be = (uint32_t)e; }
                     }
                     const float x = elem_dyn<DT>(raw[0], be);
-                    if (x > -__builtin_inff())
-                        best = make_key(exact_score<HLG>(x, bw, rc), i00 + be);
+                    if (x > -__builtin_inff()) {
+                        const uint32_t i = (uint32_t)gv0 * EPV + be;
+                        const Words4 q = stream_group_in_loop(sk, i >> 2);
+                        best = make_key(exact_score<HLG>(x, word_dyn(q, i & 3u), rc), i);
+                    }
                 }
                 const uint64_t bb = block_max_u64(best, redk);
                 if (bb != 0) {
@@ -256,67 +325,50 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                 }
             }
 
-            // Screen: candidate iff U(x) + (clz(~r) + 1) ln 2 >= best known - slack.
-            uint32_t cm[NMASK];
-#pragma unroll
-            for (int j = 0; j < NMASK; ++j) cm[j] = 0u;
+            // Screen, one vector at a time: a vector can hold a winner only if some element
+            // passes U(max x of the vector) + (code + 1) ln 2 >= best - slack; its elements
+            // are then tested one by one with their own U(x) before the exact score.
 #pragma unroll
             for (int n = 0; n < NV; ++n) {
                 const int gv = lane_v + n * BS;
+                uint32_t bits = 0;
                 if (gv < vend) {
-                    const uint32_t i0 = (uint32_t)gv * EPV;
-                    uint32_t wv[8];
-                    if (n == 0) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) wv[e] = w0a.w[e];
-                        if constexpr (EPV == 8) {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) wv[4 + e] = w0b.w[e];
-                        }
+                    const uint32_t cw = s_codes[lane_lds + n];
+                    float xm;
+                    if constexpr (HLG) {
+                        xm = s_vmax[lane_lds + n];
                     } else {
-                        const Words4 qa = stream_group_in_loop(st, i0 >> 2);
+                        xm = elem<DT>(raw[n], 0);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) wv[e] = qa.w[e];
-                        if constexpr (EPV == 8) {
-                            const Words4 qb = stream_group_in_loop(st, (i0 >> 2) + 1);
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) wv[4 + e] = qb.w[e];
-                        }
+                        for (int e = 1; e < EPV; ++e) xm = fmaxf(xm, elem<DT>(raw[n], e));
                     }
-                    uint32_t bits = 0;
-#pragma unroll
-                    for (int e = 0; e < EPV; ++e) {
-                        const float x = elem<DT>(raw[n], e);
-                        float U;
-                        if constexpr (HLG) {
-                            U = fmaxf(__builtin_fmaf(x, rc.mt, -rc.mtc), -rc.mtw);
-                        } else {
-                            U = x * rc.invT;
-                        }
-                        const float nb = (float)gumbel_bound_bits(wv[e]);
-                        bits |= (nb >= __builtin_fmaf(U, -kInvLn2, thr_s) ? 1u : 0u) << e;
+                    float Uv;
+                    if constexpr (HLG) {
+                        Uv = fmaxf(__builtin_fmaf(xm, rc.mt, -rc.mtc), -rc.mtw);
+                    } else {
+                        Uv = xm * rc.invT;
                     }
-                    cm[(n * EPV) / 32] |= bits << ((n * EPV) % 32);
+                    // smallest code that can pass, clamped to [0, 15] (15 = "15 or more")
+                    const float tf = __builtin_fmaf(Uv, -kInvLn2, thr_s);
+                    const uint32_t t = (uint32_t)__builtin_amdgcn_fmed3f(ceilf(tf), 0.0f, 15.0f);
+                    bits = (xm > -__builtin_inff()) ? codes_ge(cw, t) : 0u;
+                    if constexpr (EPV == 4) bits &= 0x0303u;
                 }
-            }
-
-            // Exact scores of the candidates (rare once the bootstrap has set a threshold).
-            // The barrier stops the compiler from keeping the screen's upcast values alive
-            // until here.
-#pragma unroll
-            for (int n = 0; n < NV; ++n)
-                asm volatile("" : "+v"(raw[n].x), "+v"(raw[n].y), "+v"(raw[n].z), "+v"(raw[n].w));
-#pragma unroll
-            for (int n = 0; n < NV; ++n) {
-                uint32_t bits = (cm[(n * EPV) / 32] >> ((n * EPV) % 32)) & ((1u << EPV) - 1u);
-                const uint32_t i0 = (uint32_t)(lane_v + n * BS) * EPV;
                 while (bits) {
-                    const uint32_t e = (uint32_t)__builtin_ctz(bits);
+                    const uint32_t e = codes_bit_elem((uint32_t)__builtin_ctz(bits));
                     bits &= bits - 1u;
                     const float x = elem_dyn<DT>(raw[n], e);
-                    if (x > -__builtin_inff()) {
-                        const uint32_t i = i0 + e;
-                        const Words4 q = stream_group_in_loop(st, i >> 2);
+                    float U;
+                    if constexpr (HLG) {
+                        U = fmaxf(__builtin_fmaf(x, rc.mt, -rc.mtc), -rc.mtw);
+                    } else {
+                        U = x * rc.invT;
+                    }
+                    const uint32_t ce = (s_codes[lane_lds + n] >> (4 * e)) & 15u;
+                    const float cf = (ce == 15u) ? 32.0f : (float)ce;
+                    if (x > -__builtin_inff() && cf >= __builtin_fmaf(U, -kInvLn2, thr_s)) {
+                        const uint32_t i = (uint32_t)gv * EPV + e;
+                        const Words4 q = stream_group_in_loop(sk, i >> 2);
                         best = umax64(best, make_key(exact_score<HLG>(x, word_dyn(q, i & 3u), rc), i));
                     }
                 }
@@ -451,14 +503,14 @@ __global__ void k_philox(const uint32_t *__restrict__ ctr, const uint32_t *__res
     for (int e = 0; e < 4; ++e) out[4 * j + e] = o.w[e];
 }
 
+// One block row (blockIdx.y) per sampled row, so that the row's key is wave-uniform as in
+// the sampling kernels, which share stream_group with this export.
 __global__ void k_stream_words(const uint64_t *__restrict__ seed,
                                const uint64_t *__restrict__ offset, int64_t B, int64_t V,
                                int32_t k, uint32_t *__restrict__ out) {
     const int64_t ng = (V + 3) / 4;
-    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (j >= B * ng) return;
-    const int64_t b = j / ng;
-    const uint32_t q = (uint32_t)(j % ng);
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t b = blockIdx.y;
     const uint64_t off = offset[b] + (uint64_t)k;
     Stream st;
     st.row = (uint32_t)b;
@@ -466,10 +518,11 @@ __global__ void k_stream_words(const uint64_t *__restrict__ seed,
     st.off_hi = (uint32_t)(off >> 32);
     st.key0 = (uint32_t)seed[b];
     st.key1 = (uint32_t)(seed[b] >> 32);
-    const Words4 o = stream_group_in_loop(st, q);
+    if (q >= ng) return;
+    const Words4 o = stream_group(st, (uint32_t)q);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const int64_t i = (int64_t)q * 4 + e;
+        const int64_t i = q * 4 + e;
         if (i < V) out[b * V + i] = o.w[e];
     }
 }
@@ -490,17 +543,17 @@ __global__ void k_fill_zero(uint32_t *__restrict__ p, int64_t n) {
 // ------------------------------------------------------------------------------------------
 template <int DT, bool HLG>
 static hipError_t launch_sample_nv(const SampleArgs &a, int nv, int bs, int grid, hipStream_t s) {
-    // Blocks of up to 1024 threads hold up to 19 vectors per thread (128 registers per lane at
-    // 16 waves per CU); longer chunks use blocks of up to 512 threads, which get 256.
+    // Blocks of up to 1024 threads hold up to 19 vectors per thread in registers (128 per
+    // lane at 16 waves per CU); the dynamic LDS holds each lane's codes (and vector maxima).
 #define HS_CASE(N, MB)                                                                     \
     case N:                                                                                \
         if (bs > MB) return hipErrorInvalidValue;                                          \
-        hipLaunchKernelGGL((k_sample<DT, N, HLG, MB>), dim3(grid), dim3(bs), 0, s, a);    \
+        hipLaunchKernelGGL((k_sample<DT, N, HLG, MB>), dim3(grid), dim3(bs),              \
+                           (size_t)(N | 1) * bs * 4 * (HLG ? 2 : 1), s, a);                 \
         break;
     switch (nv) {
         HS_CASE(1, 1024) HS_CASE(2, 1024) HS_CASE(4, 1024) HS_CASE(6, 1024) HS_CASE(8, 1024)
-        HS_CASE(12, 1024) HS_CASE(16, 1024) HS_CASE(18, 1024) HS_CASE(19, 1024)
-        HS_CASE(24, 512) HS_CASE(32, 512) HS_CASE(40, 512)
+        HS_CASE(12, 1024) HS_CASE(16, 1024) HS_CASE(19, 1024)
         default: return hipErrorInvalidValue;
     }
 #undef HS_CASE
@@ -556,10 +609,11 @@ hipError_t launch_philox(const uint32_t *ctr, const uint32_t *key, uint32_t *out
 hipError_t launch_stream_words(const uint64_t *seed, const uint64_t *offset, int64_t B,
                                int64_t V, int32_t k, uint32_t *out, hipStream_t s) {
     const int bs = 256;
-    const int64_t n = B * ((V + 3) / 4);
-    const int64_t grid = (n + bs - 1) / bs;
-    hipLaunchKernelGGL(k_stream_words, dim3((unsigned)grid), dim3(bs), 0, s, seed, offset, B, V,
-                       k, out);
+    const int64_t ng = (V + 3) / 4;
+    const int64_t gx = (ng + bs - 1) / bs;
+    if (B > 65535) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_stream_words, dim3((unsigned)gx, (unsigned)B), dim3(bs), 0, s, seed,
+                       offset, B, V, k, out);
     return hipGetLastError();
 }
 
