@@ -142,7 +142,12 @@ __device__ __forceinline__ float log1p_acc(float t) {
     const float u = 1.0f + t;
     if (u == 1.0f) return t;
     if (u == __builtin_inff()) return __builtin_inff();
-    return logf(u) * (t / (u - 1.0f));
+    // t / (u - 1) = 1 + (t - d) / d with d = u - 1 exact and t - d the exact rounding error of
+    // 1 + t: the quotient is within an ulp of 1, so a hardware reciprocal (no IEEE divide
+    // sequence) keeps it to about half an ulp.
+    const float d = u - 1.0f;
+    const float corr = __builtin_fmaf(t - d, __builtin_amdgcn_rcpf(d), 1.0f);
+    return logf(u) * corr;
 }
 
 // Gumbel noise of one word [GMX, Background: g = -log(-log(u))], u = (r + 1/2) 2^-32.
@@ -262,62 +267,115 @@ __device__ __forceinline__ uint4 load_vec(const char *__restrict__ rowp, int64_t
 }
 
 // ------------------------------------------------------------------------------------------
-// Wave64 and block reductions.
+// Wave64 and block reductions. Within each row of 16 lanes four DPP steps (quad permutes,
+// half-row and row mirrors) leave the row's result in every lane; the four rows are then
+// combined from v_readlane into scalar registers. No LDS traffic inside a wave. The combine
+// order is fixed, so every result is a deterministic function of the inputs. All lanes of
+// the wave must be active.
 // ------------------------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppQuad1032 = 0xB1, kDppQuad2301 = 0x4E, kDppRowHalfMirror = 0x141,
+              kDppRowMirror = 0x140;
+
+__device__ __forceinline__ float rl_f32(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+    v = fmaxf(v, dpp_f32<kDppQuad1032>(v));
+    v = fmaxf(v, dpp_f32<kDppQuad2301>(v));
+    v = fmaxf(v, dpp_f32<kDppRowHalfMirror>(v));
+    v = fmaxf(v, dpp_f32<kDppRowMirror>(v));
+    return fmaxf(fmaxf(rl_f32(v, 0), rl_f32(v, 16)), fmaxf(rl_f32(v, 32), rl_f32(v, 48)));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+    v += dpp_f32<kDppQuad1032>(v);
+    v += dpp_f32<kDppQuad2301>(v);
+    v += dpp_f32<kDppRowHalfMirror>(v);
+    v += dpp_f32<kDppRowMirror>(v);
+    return (rl_f32(v, 0) + rl_f32(v, 16)) + (rl_f32(v, 32) + rl_f32(v, 48));
+}
+
+__device__ __forceinline__ uint64_t umax64_pair(uint64_t a, uint32_t hi, uint32_t lo) {
+    const uint64_t b = ((uint64_t)hi << 32) | lo;
+    return b > a ? b : a;
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
+    return umax64_pair(v, dpp_u32<CTRL>((uint32_t)(v >> 32)), dpp_u32<CTRL>((uint32_t)v));
+}
+
+__device__ __forceinline__ uint64_t rl_u64(uint64_t v, int lane) {
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+    return ((uint64_t)hi << 32) | lo;
 }
 
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint64_t t = __shfl_xor(v, o);
-        v = t > v ? t : v;
-    }
-    return v;
+    v = dpp_max_u64<kDppQuad1032>(v);
+    v = dpp_max_u64<kDppQuad2301>(v);
+    v = dpp_max_u64<kDppRowHalfMirror>(v);
+    v = dpp_max_u64<kDppRowMirror>(v);
+    const uint64_t a = umax64(rl_u64(v, 0), rl_u64(v, 16));
+    const uint64_t b = umax64(rl_u64(v, 32), rl_u64(v, 48));
+    return umax64(a, b);
 }
 
-// Block-wide reductions over up to 16 waves through LDS scratch `red` (>= 16 entries).
-// Every thread returns the result. The combine order is fixed (wave 0..nw-1), so the
-// result is a deterministic function of the inputs.
+// Block-wide reductions (up to 16 waves) through a caller-owned LDS buffer `red` of 16
+// entries. One barrier each: a call site must not reuse its buffer before a later barrier
+// that all waves pass after reading it. Every thread returns the result.
 __device__ __forceinline__ float block_max(float v, float *red) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
     v = wave_max(v);
-    __syncthreads();
     if (lane == 0) red[wid] = v;
     __syncthreads();
-    float r = red[0];
-    for (int j = 1; j < nw; ++j) r = fmaxf(r, red[j]);
-    return r;
+    return wave_max(lane < nw ? red[lane] : -__builtin_inff());
 }
 
 __device__ __forceinline__ float block_sum(float v, float *red) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
     v = wave_sum(v);
-    __syncthreads();
     if (lane == 0) red[wid] = v;
     __syncthreads();
-    float r = red[0];
-    for (int j = 1; j < nw; ++j) r += red[j];
-    return r;
+    return wave_sum(lane < nw ? red[lane] : 0.0f);
 }
 
 __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t *red) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
     v = wave_max_u64(v);
-    __syncthreads();
     if (lane == 0) red[wid] = v;
     __syncthreads();
-    uint64_t r = red[0];
-    for (int j = 1; j < nw; ++j) r = umax64(r, red[j]);
+    return wave_max_u64(lane < nw ? red[lane] : 0ull);
+}
+
+// Log-sum-exp of per-lane (max, sum of exp(x - max)) pairs over the block: the pair of the
+// block is (M, S) with M the largest max and S the sum of each sum rescaled to M.
+struct MaxSum {
+    float m, s;
+};
+
+__device__ __forceinline__ MaxSum block_maxsum(float m, float s, float2 *red) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+    constexpr float kL2e = 1.44269504088896341f;
+    float mw = wave_max(m);
+    float sw = wave_sum((m > -__builtin_inff()) ? s * __builtin_amdgcn_exp2f((m - mw) * kL2e) : 0.0f);
+    if (lane == 0) red[wid] = make_float2(mw, sw);
+    __syncthreads();
+    const float2 p = lane < nw ? red[lane] : make_float2(-__builtin_inff(), 0.0f);
+    const float mb = wave_max(p.x);
+    const float sb = wave_sum((p.x > -__builtin_inff()) ? p.y * __builtin_amdgcn_exp2f((p.x - mb) * kL2e) : 0.0f);
+    MaxSum r;
+    r.m = mb;
+    r.s = sb;
     return r;
 }
 

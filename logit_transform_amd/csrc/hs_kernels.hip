@@ -71,7 +71,7 @@ __device__ __forceinline__ uint32_t word_dyn(const Words4 &q, uint32_t j) {
 // l' = g(x - (LSE + mu)) when the curve is on [HLG, The transfer function]. Every kernel
 // variant scores elements through this one function.
 template <bool HLG>
-__device__ __noinline__ float exact_score(float x, uint32_t word, RowConst rc) {
+__device__ __forceinline__ float exact_score_inl(float x, uint32_t word, const RowConst &rc) {
     float a;
     if constexpr (HLG) {
         a = hlg32(x - rc.c, rc.curve) * rc.invT;
@@ -80,6 +80,14 @@ __device__ __noinline__ float exact_score(float x, uint32_t word, RowConst rc) {
     }
     return a + gumbel32(word);
 }
+
+// The same function kept out of line for the rare candidate path, so that its code is not
+// repeated at every vector of the unrolled screen.
+template <bool HLG>
+__device__ __noinline__ float exact_score(float x, uint32_t word, RowConst rc) {
+    return exact_score_inl<HLG>(x, word, rc);
+}
+
 
 template <int DT>
 __device__ __forceinline__ uint64_t greedy_vec(uint4 raw, uint32_t i0, uint64_t best) {
@@ -119,7 +127,7 @@ __device__ __forceinline__ uint32_t codes_ge(uint32_t cw, uint32_t t) {
 // Element index of a set bit position of codes_ge's result.
 __device__ __forceinline__ uint32_t codes_bit_elem(uint32_t p) { return ((p >> 3) << 1) | (p & 1u); }
 
-template <int DT, int NV, bool HLG, int MAXBS>
+template <int DT, int NV, bool HLG, int MAXBS, bool ALIGNED>
 __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     using tr = dtype_traits<DT>;
     constexpr int EPV = tr::epv;
@@ -127,8 +135,9 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     // with the curve on the vector's largest logit (draw-invariant). Each lane's entries are
     // contiguous, so every access is one base register plus an immediate offset.
     extern __shared__ uint32_t s_dyn[];
-    __shared__ float redf[16];
-    __shared__ uint64_t redk[16];
+    __shared__ float2 red_lse[16];
+    __shared__ float red_boot[16];
+    __shared__ uint64_t red_draw[16];
     __shared__ int s_last;
 
     const int tid = threadIdx.x;
@@ -159,18 +168,35 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     // ---- issue the loads of this chunk (registers) ----
     const int v0 = chunk * (int)a.cv;
     const int vend = (int)min(a.nvec, (int64_t)v0 + a.cv);
+    const int nfull = (int)(a.V / EPV);   // vectors with all EPV elements inside the row
     const char *rowp = reinterpret_cast<const char *>(a.data) + b * a.ld * tr::esize;
     uint4 raw[NV];
-#pragma unroll
-    for (int n = 0; n < NV; ++n) {
-        const int gv = v0 + tid + n * BS;
-        if (gv < vend) {
-            raw[n] = load_vec<DT>(rowp, gv, a.V, a.aligned);
+    // ALIGNED: a vector outside the chunk or past the last full vector reads an in-row full
+    // vector instead (clamped index) and is patched after the Philox phase, when waiting for
+    // it costs nothing. The loads carry no branch: a branch would merge the loaded registers
+    // into copies, and every copy waits for its load.
+    const int gmax = min(vend, nfull) - 1;   // >= 0 when ALIGNED: the caller ensures V >= epv
+    auto issue_load = [&](int n) {
+        if constexpr (ALIGNED) {
+            const int gv = min(v0 + tid + n * BS, gmax);
+            raw[n] = *reinterpret_cast<const uint4 *>(rowp + (size_t)gv * 16);
         } else {
-            raw[n] = make_uint4(tr::neg_inf_word, tr::neg_inf_word, tr::neg_inf_word,
-                                tr::neg_inf_word);
+            const int gv = v0 + tid + n * BS;
+            if (gv < vend) {
+                raw[n] = load_vec<DT>(rowp, gv, a.V, false);
+            } else {
+                raw[n] = make_uint4(tr::neg_inf_word, tr::neg_inf_word, tr::neg_inf_word,
+                                    tr::neg_inf_word);
+            }
         }
-    }
+    };
+    // Loads are issued a group of vectors at a time, between the first draw's Philox work on
+    // earlier groups: a wave that issued all its loads at once would stall on the memory
+    // queue while the other waves of the block could not start, and the row's HBM time
+    // would not be covered by Philox work.
+    constexpr int LG = 4;
+#pragma unroll
+    for (int n = 0; n < (NV < LG ? NV : LG); ++n) issue_load(n);
 
     const uint64_t seed = a.seed[b];
     const uint64_t off0 = a.offset[b];
@@ -180,38 +206,64 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     st.key1 = (uint32_t)(seed >> 32);
 
     // Word codes of draw k for this lane's vectors. Needs no logit, so for the first draw it
-    // runs while the loads above are still in flight.
-    auto write_codes = [&](int k) {
+    // runs while the loads are in flight (with_loads: issue the next group's loads as it
+    // goes).
+    // Also returns the lane's champion: the element with the largest code, packed as
+    // code << 8 | vector << 3 | element (the bootstrap below starts from it).
+    auto write_codes = [&](int k, bool with_loads) -> uint32_t {
         const uint64_t off = off0 + (uint64_t)k;
         Stream sk = st;
         sk.off_lo = (uint32_t)off;
         sk.off_hi = (uint32_t)(off >> 32);
         int lane_v = v0 + tid;
         asm volatile("" : "+v"(lane_v));
-        uint32_t chain = 0;
+        uint32_t champ = 0;
 #pragma unroll
         for (int n = 0; n < NV; ++n) {
+            if (with_loads && n % LG == 0) {
+#pragma unroll
+                for (int j = n + LG; j < n + 2 * LG && j < NV; ++j) issue_load(j);
+            }
             const int gv = lane_v + n * BS;
             if (gv < vend) {
                 uint32_t q = ((uint32_t)gv * EPV) >> 2;
-                // start this vector's groups only after the previous vector's code is done,
-                // which bounds the registers the interleaved Philox chains hold
-                asm volatile("" : "+v"(q) : "v"(chain));
-                const Words4 qa = philox4x32_10_uk(q, sk.row, sk.off_lo, sk.off_hi, sk.key0, sk.key1);
-                uint32_t cw = word_code(qa.w[0]) | (word_code(qa.w[1]) << 4) |
-                              (word_code(qa.w[2]) << 8) | (word_code(qa.w[3]) << 12);
-                if constexpr (EPV == 8) {
-                    const Words4 qb = philox4x32_10_uk(q + 1, sk.row, sk.off_lo, sk.off_hi,
+                asm volatile("" : "+v"(q));
+                uint32_t cw = 0;
+#pragma unroll
+                for (int g = 0; g < EPV / 4; ++g) {
+                    const Words4 qw = philox4x32_10_uk(q + g, sk.row, sk.off_lo, sk.off_hi,
                                                        sk.key0, sk.key1);
-                    cw |= (word_code(qb.w[0]) << 16) | (word_code(qb.w[1]) << 20) |
-                          (word_code(qb.w[2]) << 24) | (word_code(qb.w[3]) << 28);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t c = word_code(qw.w[e]);
+                        cw |= c << (4 * (4 * g + e));
+                        champ = max(champ, (c << 8) | (uint32_t)((n << 3) | (4 * g + e)));
+                    }
                 }
                 s_codes[lane_lds + n] = cw;
-                chain = cw;
             }
         }
+        return champ;
     };
-    if (sampled && k0 < k1) write_codes(k0);
+    uint32_t champ0 = 0;
+    if (sampled && k0 < k1) {
+        champ0 = write_codes(k0, true);
+    } else {
+#pragma unroll
+        for (int n = LG; n < NV; ++n) issue_load(n);
+    }
+
+    if constexpr (ALIGNED) {
+        // patch the vectors the branch-free loads could not take whole
+#pragma unroll
+        for (int n = 0; n < NV; ++n) {
+            const int gv = v0 + tid + n * BS;
+            if (gv >= vend || gv >= nfull)
+                raw[n] = (gv < vend) ? load_vec<DT>(rowp, gv, a.V, false)
+                                     : make_uint4(tr::neg_inf_word, tr::neg_inf_word,
+                                                  tr::neg_inf_word, tr::neg_inf_word);
+        }
+    }
 
     RowConst rc;
     rc.invT = 1.0f / T;
@@ -250,11 +302,8 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
         }
         float lse;
         if (a.nchunk == 1) {
-            const float Mb = block_max(M, redf);
-            const float sc = (M > -__builtin_inff()) ? S * __builtin_amdgcn_exp2f((M - Mb) * kLog2e)
-                                                     : 0.0f;
-            const float Sb = block_sum(sc, redf);
-            lse = (Mb > -__builtin_inff()) ? Mb + logf(Sb) : -__builtin_inff();
+            const MaxSum ms = block_maxsum(M, S, red_lse);
+            lse = (ms.m > -__builtin_inff()) ? ms.m + logf(ms.s) : -__builtin_inff();
         } else {
             const float2 *part = a.partials + b * a.part_stride;
             float Mb = -__builtin_inff();
@@ -275,7 +324,8 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     }
 
     for (int k = k0; k < k1; ++k) {
-        if (k > k0 && sampled) write_codes(k);
+        uint32_t champ = champ0;
+        if (k > k0 && sampled) champ = write_codes(k, false);
         // Keep per-element work inside the draw loop: without this the compiler hoists the
         // draw-invariant part of the screen (one value per element) out of the loop and runs
         // out of registers. Likewise for everything derived from the element indices.
@@ -297,32 +347,39 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             sk.off_lo = (uint32_t)off;
             sk.off_hi = (uint32_t)(off >> 32);
 
-            // Bootstrap: each lane scores exactly the element of its first vector with the
-            // largest word code; the block maximum is a score some element reaches, so it
-            // lower-bounds the draw's winning score.
+            // Bootstrap: each lane bounds from below the score of its champion (largest code,
+            // hence nearly the largest Gumbel value among the lane's elements); the block
+            // maximum of these bounds is at most the draw's winning score. Lower bounds used:
+            // g(z) >= m min(z, w) (the toe lies above its mid line, the shoulder above m w),
+            // and for code n >= 1 the word has clz(~r) >= n, so u >= 1 - 2^-n and
+            // G >= n ln 2 + ln(1 - 2^-n); code 0 only gives G >= -3.14.
             float thr_s = -3.0e38f;   // (best known - slack) / ln 2 - 1
             if (!a.no_screen) {
-                const int gv0 = lane_v;
-                if (gv0 < vend) {
-                    const uint32_t cw = s_codes[lane_lds];
-                    uint32_t be = 0, bc = cw & 15u;
+                const uint32_t cn = champ >> 8, cs = (champ >> 3) & 31u, ce = champ & 7u;
+                uint4 cv4 = raw[0];
 #pragma unroll
-                    for (int e = 1; e < EPV; ++e) {
-                        const uint32_t ce = (cw >> (4 * e)) & 15u;
-                        if (ce > bc) { bc = ce; be = (uint32_t)e; }
-                    }
-                    const float x = elem_dyn<DT>(raw[0], be);
-                    if (x > -__builtin_inff()) {
-                        const uint32_t i = (uint32_t)gv0 * EPV + be;
-                        const Words4 q = stream_group_in_loop(sk, i >> 2);
-                        best = make_key(exact_score<HLG>(x, word_dyn(q, i & 3u), rc), i);
-                    }
+                for (int n = 1; n < NV; ++n) {
+                    if (cs == (uint32_t)n) cv4 = raw[n];
                 }
-                const uint64_t bb = block_max_u64(best, redk);
-                if (bb != 0) {
-                    const float bs = key_score(bb);
+                const float x = elem_dyn<DT>(cv4, ce);
+                float lb = -__builtin_inff();
+                if (lane_v + (int)cs * BS < vend && x > -__builtin_inff()) {
+                    float alo;
+                    if constexpr (HLG) {
+                        alo = fminf(x - rc.c, rc.curve.w) * rc.mt;
+                    } else {
+                        alo = x * rc.invT;
+                    }
+                    const float glo = cn == 0u ? -3.14f
+                                    : cn == 1u ? 0.0f
+                                    : cn == 2u ? 1.0986f
+                                    : cn == 3u ? 1.9459f
+                                    : __builtin_fmaf((float)cn, kLn2, -0.0646f);
+                    lb = alo + glo;
+                }
+                const float bs = block_max(lb, red_boot);
+                if (bs > -__builtin_inff())
                     thr_s = uniform((bs - screen_slack(bs)) * kInvLn2 - 1.0f);
-                }
             }
 
             // Screen, one vector at a time: a vector can hold a winner only if some element
@@ -375,7 +432,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             }
         }
         // block reduction of the draw's key
-        const uint64_t kb = block_max_u64(best, redk);
+        const uint64_t kb = block_max_u64(best, red_draw);
         if (tid == 0) {
             const int64_t o = b * a.K + k;
             if (a.nchunk == 1) {
@@ -419,7 +476,7 @@ template <int DT>
 __global__ __launch_bounds__(1024) void k_lse_partial(SampleArgs a) {
     using tr = dtype_traits<DT>;
     constexpr int EPV = tr::epv;
-    __shared__ float redf[16];
+    __shared__ float red_m[16], red_s[16];
     const int chunk = blockIdx.x % a.nchunk;
     const int64_t b = blockIdx.x / a.nchunk;
     const int64_t v0 = (int64_t)chunk * a.cv;
@@ -431,7 +488,7 @@ __global__ __launch_bounds__(1024) void k_lse_partial(SampleArgs a) {
 #pragma unroll
         for (int e = 0; e < EPV; ++e) mx = fmaxf(mx, elem<DT>(v, e));
     }
-    const float M = block_max(mx, redf);
+    const float M = block_max(mx, red_m);
     float s = 0.0f;
     if (M > -__builtin_inff()) {
         const float mb = M * kLog2e;
@@ -442,7 +499,7 @@ __global__ __launch_bounds__(1024) void k_lse_partial(SampleArgs a) {
                 s += __builtin_amdgcn_exp2f(elem<DT>(v, e) * kLog2e - mb);
         }
     }
-    const float S = block_sum(s, redf);
+    const float S = block_sum(s, red_s);
     if (threadIdx.x == 0) a.partials[b * a.part_stride + chunk] = make_float2(M, S);
 }
 
@@ -451,7 +508,7 @@ template <int DT, bool TRANSFORM>
 __global__ __launch_bounds__(1024) void k_row_lse(RowOpArgs a) {
     using tr = dtype_traits<DT>;
     constexpr int EPV = tr::epv;
-    __shared__ float redf[16];
+    __shared__ float red_m[16], red_s[16];
     const int64_t b = blockIdx.x;
     const int64_t nvec = (a.V + EPV - 1) / EPV;
     const char *rowp = reinterpret_cast<const char *>(a.data) + b * a.ld * tr::esize;
@@ -461,7 +518,7 @@ __global__ __launch_bounds__(1024) void k_row_lse(RowOpArgs a) {
 #pragma unroll
         for (int e = 0; e < EPV; ++e) mx = fmaxf(mx, elem<DT>(v, e));
     }
-    const float M = block_max(mx, redf);
+    const float M = block_max(mx, red_m);
     float s = 0.0f;
     if (M > -__builtin_inff()) {
         const float mb = M * kLog2e;
@@ -472,7 +529,7 @@ __global__ __launch_bounds__(1024) void k_row_lse(RowOpArgs a) {
                 s += __builtin_amdgcn_exp2f(elem<DT>(v, e) * kLog2e - mb);
         }
     }
-    const float S = block_sum(s, redf);
+    const float S = block_sum(s, red_s);
     const float lse = (M > -__builtin_inff()) ? M + logf(S) : -__builtin_inff();
     if constexpr (!TRANSFORM) {
         if (threadIdx.x == 0) a.lse[b] = lse;
@@ -541,14 +598,14 @@ __global__ void k_fill_zero(uint32_t *__restrict__ p, int64_t n) {
 // ------------------------------------------------------------------------------------------
 // Host-side launchers (called from hs_api.hip).
 // ------------------------------------------------------------------------------------------
-template <int DT, bool HLG>
+template <int DT, bool HLG, bool AL>
 static hipError_t launch_sample_nv(const SampleArgs &a, int nv, int bs, int grid, hipStream_t s) {
     // Blocks of up to 1024 threads hold up to 19 vectors per thread in registers (128 per
     // lane at 16 waves per CU); the dynamic LDS holds each lane's codes (and vector maxima).
 #define HS_CASE(N, MB)                                                                     \
     case N:                                                                                \
         if (bs > MB) return hipErrorInvalidValue;                                          \
-        hipLaunchKernelGGL((k_sample<DT, N, HLG, MB>), dim3(grid), dim3(bs),              \
+        hipLaunchKernelGGL((k_sample<DT, N, HLG, MB, AL>), dim3(grid), dim3(bs),          \
                            (size_t)(N | 1) * bs * 4 * (HLG ? 2 : 1), s, a);                 \
         break;
     switch (nv) {
@@ -560,15 +617,23 @@ static hipError_t launch_sample_nv(const SampleArgs &a, int nv, int bs, int grid
     return hipGetLastError();
 }
 
+template <int DT, bool HLG>
+static hipError_t launch_sample_al(const SampleArgs &a, int nv, int bs, int grid, hipStream_t s) {
+    // the branch-free load path needs 16-byte aligned rows holding at least one full vector
+    if (a.aligned && a.V >= dtype_traits<DT>::epv)
+        return launch_sample_nv<DT, HLG, true>(a, nv, bs, grid, s);
+    return launch_sample_nv<DT, HLG, false>(a, nv, bs, grid, s);
+}
+
 hipError_t launch_sample(int dt, bool hlg, const SampleArgs &a, int nv, int bs, int grid,
                          hipStream_t s) {
     switch (dt) {
-        case DT_F32: return hlg ? launch_sample_nv<DT_F32, true>(a, nv, bs, grid, s)
-                                : launch_sample_nv<DT_F32, false>(a, nv, bs, grid, s);
-        case DT_BF16: return hlg ? launch_sample_nv<DT_BF16, true>(a, nv, bs, grid, s)
-                                 : launch_sample_nv<DT_BF16, false>(a, nv, bs, grid, s);
-        case DT_F16: return hlg ? launch_sample_nv<DT_F16, true>(a, nv, bs, grid, s)
-                                : launch_sample_nv<DT_F16, false>(a, nv, bs, grid, s);
+        case DT_F32: return hlg ? launch_sample_al<DT_F32, true>(a, nv, bs, grid, s)
+                                : launch_sample_al<DT_F32, false>(a, nv, bs, grid, s);
+        case DT_BF16: return hlg ? launch_sample_al<DT_BF16, true>(a, nv, bs, grid, s)
+                                 : launch_sample_al<DT_BF16, false>(a, nv, bs, grid, s);
+        case DT_F16: return hlg ? launch_sample_al<DT_F16, true>(a, nv, bs, grid, s)
+                                : launch_sample_al<DT_F16, false>(a, nv, bs, grid, s);
     }
     return hipErrorInvalidValue;
 }
