@@ -334,7 +334,12 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 // entries. One barrier each: a call site must not reuse its buffer before a later barrier
 // that all waves pass after reading it. Every thread returns the result.
 __device__ __forceinline__ float block_max(float v, float *red) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+    // lane and wave index recomputed at each call, not held in registers across a caller's loop
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    int wid = threadIdx.x >> 6;
+    asm volatile("" : "+v"(wid));
+    const int nw = (blockDim.x + 63) >> 6;
     v = wave_max(v);
     if (lane == 0) red[wid] = v;
     __syncthreads();
@@ -342,7 +347,12 @@ __device__ __forceinline__ float block_max(float v, float *red) {
 }
 
 __device__ __forceinline__ float block_sum(float v, float *red) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+    // lane and wave index recomputed at each call, not held in registers across a caller's loop
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    int wid = threadIdx.x >> 6;
+    asm volatile("" : "+v"(wid));
+    const int nw = (blockDim.x + 63) >> 6;
     v = wave_sum(v);
     if (lane == 0) red[wid] = v;
     __syncthreads();
@@ -350,7 +360,12 @@ __device__ __forceinline__ float block_sum(float v, float *red) {
 }
 
 __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t *red) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+    // lane and wave index recomputed at each call, not held in registers across a caller's loop
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    int wid = threadIdx.x >> 6;
+    asm volatile("" : "+v"(wid));
+    const int nw = (blockDim.x + 63) >> 6;
     v = wave_max_u64(v);
     if (lane == 0) red[wid] = v;
     __syncthreads();
@@ -364,7 +379,12 @@ struct MaxSum {
 };
 
 __device__ __forceinline__ MaxSum block_maxsum(float m, float s, float2 *red) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+    // lane and wave index recomputed at each call, not held in registers across a caller's loop
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    int wid = threadIdx.x >> 6;
+    asm volatile("" : "+v"(wid));
+    const int nw = (blockDim.x + 63) >> 6;
     constexpr float kL2e = 1.44269504088896341f;
     float mw = wave_max(m);
     float sw = wave_sum((m > -__builtin_inff()) ? s * __builtin_amdgcn_exp2f((m - mw) * kL2e) : 0.0f);

@@ -146,11 +146,12 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     uint32_t *s_codes = s_dyn;
     float *s_vmax = reinterpret_cast<float *>(s_dyn + SC * BS);
     const int lane_lds = tid * SC;
+    // block coordinates in scalar registers (the divisions would otherwise run per lane)
     int bid = blockIdx.x;
-    const int chunk = bid % a.nchunk;
+    const int chunk = __builtin_amdgcn_readfirstlane(bid % a.nchunk);
     bid /= a.nchunk;
-    const int kg = bid % a.nkg;
-    const int64_t b = bid / a.nkg;
+    const int kg = __builtin_amdgcn_readfirstlane(bid % a.nkg);
+    const int64_t b = __builtin_amdgcn_readfirstlane(bid / a.nkg);
     const int k0 = kg * a.kpg;
     const int k1 = min(a.K, k0 + a.kpg);
 
