@@ -166,6 +166,16 @@ __device__ __forceinline__ float gumbel32(uint32_t r) {
     return -logf(E);
 }
 
+// Screening code of a word: n = min(clz(~r), 15), in two instructions. Setting the low 17 bits
+// of ~r caps the leading-zero count at 15; gfx950's v_bitop3_b32 forms ~r | mask in one step
+// (truth table 0xCF = ~S0 | S1, the mask in a scalar register), and v_ffbh_u32 counts.
+__device__ __forceinline__ uint32_t word_code(uint32_t r) {
+    uint32_t t, n;
+    asm("v_bitop3_b32 %0, %1, %2, %2 bitop3:0xcf" : "=v"(t) : "v"(r), "s"(0x1FFFFu));
+    asm("v_ffbh_u32 %0, %1" : "=v"(n) : "v"(t));
+    return n;
+}
+
 // Upper bound on gumbel32(r), cheap: with n = clz(~r), v = 1 - u >= 2^-(n+1) and
 // G = -log(-log u) <= -log(v) <= (n + 1) ln 2. Returned as n (the caller folds the +1).
 __device__ __forceinline__ uint32_t gumbel_bound_bits(uint32_t r) {
@@ -393,6 +403,28 @@ __device__ __forceinline__ MaxSum block_maxsum(float m, float s, float2 *red) {
     const float2 p = lane < nw ? red[lane] : make_float2(-__builtin_inff(), 0.0f);
     const float mb = wave_max(p.x);
     const float sb = wave_sum((p.x > -__builtin_inff()) ? p.y * __builtin_amdgcn_exp2f((p.x - mb) * kL2e) : 0.0f);
+    MaxSum r;
+    r.m = mb;
+    r.s = sb;
+    return r;
+}
+
+// The same pair in base-2 units: m is a maximum of x log2(e) and s = sum 2^(x log2(e) - m).
+// Lanes without any finite element pass m = -FLT_MAX (finite, so that no inf - inf arises)
+// and s = 0. Returns the block's (m, s) in the same units.
+__device__ __forceinline__ MaxSum block_maxsum_log2(float m, float s, float2 *red) {
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    int wid = threadIdx.x >> 6;
+    asm volatile("" : "+v"(wid));
+    const int nw = (blockDim.x + 63) >> 6;
+    const float mw = wave_max(m);
+    const float sw = wave_sum(s * __builtin_amdgcn_exp2f(m - mw));
+    if (lane == 0) red[wid] = make_float2(mw, sw);
+    __syncthreads();
+    const float2 p = lane < nw ? red[lane] : make_float2(-3.402823466e38f, 0.0f);
+    const float mb = wave_max(p.x);
+    const float sb = wave_sum(p.y * __builtin_amdgcn_exp2f(p.x - mb));
     MaxSum r;
     r.m = mb;
     r.s = sb;

@@ -100,20 +100,6 @@ __device__ __forceinline__ uint64_t greedy_vec(uint4 raw, uint32_t i0, uint64_t 
     return best;
 }
 
-__device__ __forceinline__ uint32_t ffbh_u32(uint32_t v) {
-    // leading-zero count; all ones (0xFFFFFFFF) for v == 0
-    uint32_t r;
-    asm("v_ffbh_u32 %0, %1" : "=v"(r) : "v"(v));
-    return r;
-}
-
-// 4-bit screening code of a word: min(clz(~r), 15). With n = clz(~r) the word's Gumbel value
-// is at most (n + 1) ln 2; code 15 stands for "15 or more" (bound 33 ln 2).
-__device__ __forceinline__ uint32_t word_code(uint32_t r) {
-    const uint32_t n = ffbh_u32(~r);      // 0xFFFFFFFF for r = 0xFFFFFFFF
-    return n < 15u ? n : 15u;
-}
-
 // Which of the 8 codes in cw (4 bits each) are >= t (0..15). Bytes serve as 8-bit lanes (no
 // carry crosses a nibble): code 2j is tested in byte j of the low half, code 2j+1 in byte j
 // of the high half. Bit 8j of the result flags code 2j, bit 8j+1 code 2j+1.
@@ -131,8 +117,9 @@ template <int DT, int NV, bool HLG, int MAXBS, bool ALIGNED>
 __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     using tr = dtype_traits<DT>;
     constexpr int EPV = tr::epv;
-    // Dynamic LDS: per lane and vector the word code of the current draw (EPV nibbles), and
-    // with the curve on the vector's largest logit (draw-invariant). Each lane's entries are
+    // Dynamic LDS, per lane and vector: the word codes of the current draw (EPV nibbles) in
+    // s_codes; in s_vmax the vector's largest logit as a bf16-grid upper bound (high half,
+    // draw-invariant) and the largest of its codes (low half). Each lane's entries are
     // contiguous, so every access is one base register plus an immediate offset.
     extern __shared__ uint32_t s_dyn[];
     __shared__ float2 red_lse[16];
@@ -144,8 +131,8 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     const int BS = blockDim.x;
     constexpr int SC = NV | 1;   // per-lane stride (odd: lanes hit distinct banks)
     uint32_t *s_codes = s_dyn;
-    float *s_vmax = reinterpret_cast<float *>(s_dyn + SC * BS);
-    const int lane_lds = tid * SC;
+    uint32_t *s_vmax = s_dyn + SC * BS;
+    int lane_lds = tid * SC;   // re-made opaque per draw: no per-vector address hoisting
     // block coordinates in scalar registers (the divisions would otherwise run per lane)
     int bid = blockIdx.x;
     const int chunk = __builtin_amdgcn_readfirstlane(bid % a.nchunk);
@@ -191,79 +178,152 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             }
         }
     };
-    // Loads are issued a group of vectors at a time, between the first draw's Philox work on
-    // earlier groups: a wave that issued all its loads at once would stall on the memory
-    // queue while the other waves of the block could not start, and the row's HBM time
-    // would not be covered by Philox work.
-    constexpr int LG = 4;
-#pragma unroll
-    for (int n = 0; n < (NV < LG ? NV : LG); ++n) issue_load(n);
-
     const uint64_t seed = a.seed[b];
     const uint64_t off0 = a.offset[b];
     Stream st;
     st.row = (uint32_t)b;
     st.key0 = (uint32_t)seed;
     st.key1 = (uint32_t)(seed >> 32);
-
-    // Word codes of draw k for this lane's vectors. Needs no logit, so for the first draw it
-    // runs while the loads are in flight (with_loads: issue the next group's loads as it
-    // goes).
-    // Also returns the lane's champion: the element with the largest code, packed as
-    // code << 8 | vector << 3 | element (the bootstrap below starts from it).
-    auto write_codes = [&](int k, bool with_loads) -> uint32_t {
+    auto stream_k = [&](int k) {
         const uint64_t off = off0 + (uint64_t)k;
         Stream sk = st;
         sk.off_lo = (uint32_t)off;
         sk.off_hi = (uint32_t)(off >> 32);
-        int lane_v = v0 + tid;
-        asm volatile("" : "+v"(lane_v));
-        uint32_t champ = 0;
-#pragma unroll
-        for (int n = 0; n < NV; ++n) {
-            if (with_loads && n % LG == 0) {
-#pragma unroll
-                for (int j = n + LG; j < n + 2 * LG && j < NV; ++j) issue_load(j);
-            }
-            const int gv = lane_v + n * BS;
-            if (gv < vend) {
-                uint32_t q = ((uint32_t)gv * EPV) >> 2;
-                asm volatile("" : "+v"(q));
-                uint32_t cw = 0;
-#pragma unroll
-                for (int g = 0; g < EPV / 4; ++g) {
-                    const Words4 qw = philox4x32_10_uk(q + g, sk.row, sk.off_lo, sk.off_hi,
-                                                       sk.key0, sk.key1);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t c = word_code(qw.w[e]);
-                        cw |= c << (4 * (4 * g + e));
-                        champ = max(champ, (c << 8) | (uint32_t)((n << 3) | (4 * g + e)));
-                    }
-                }
-                s_codes[lane_lds + n] = cw;
-            }
-        }
-        return champ;
+        return sk;
     };
-    uint32_t champ0 = 0;
-    if (sampled && k0 < k1) {
-        champ0 = write_codes(k0, true);
-    } else {
-#pragma unroll
-        for (int n = LG; n < NV; ++n) issue_load(n);
-    }
+    // Per lane and vector, s_vmax holds the vector's largest logit in its high half (exact
+    // for bf16 input, rounded toward +inf to the bf16 grid otherwise, so it stays an upper
+    // bound) and the vector's largest word code of the current draw in its low half.
+    uint16_t *s_vmax16 = reinterpret_cast<uint16_t *>(s_vmax);
 
-    if constexpr (ALIGNED) {
-        // patch the vectors the branch-free loads could not take whole
+    // Word codes of one vector for draw stream sk: EPV 4-bit codes into s_codes, their
+    // maximum into s_vmax. Vectors past the chunk are coded too (their words are never
+    // used). Returns the lane's champion key after this vector: max code << 5 | vector.
+    auto codes_vec = [&](const Stream &sk, int lane_v, int n, uint32_t champ) -> uint32_t {
+        uint32_t q = ((uint32_t)(lane_v + n * BS) * EPV) >> 2;
+        asm volatile("" : "+v"(q));
+        uint32_t cw = 0, vm = 0;
 #pragma unroll
-        for (int n = 0; n < NV; ++n) {
+        for (int g = 0; g < EPV / 4; ++g) {
+            const Words4 qw = philox4x32_10_uk(q + g, sk.row, sk.off_lo, sk.off_hi, sk.key0,
+                                               sk.key1);
+            uint32_t c[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                c[e] = word_code(qw.w[e]);
+                cw |= c[e] << (4 * (4 * g + e));
+            }
+            vm = max(vm, max(max(c[0], c[1]), max(c[2], c[3])));
+        }
+        s_codes[lane_lds + n] = cw;
+        s_vmax16[2 * (lane_lds + n)] = (uint16_t)vm;
+        return max(champ, (vm << 5) | (uint32_t)n);
+    };
+
+    // Patch the vectors the branch-free loads could not take whole (ragged row end, vectors
+    // outside the chunk); waits for that vector's load.
+    auto patch_vec = [&](int n) {
+        if constexpr (ALIGNED) {
             const int gv = v0 + tid + n * BS;
             if (gv >= vend || gv >= nfull)
                 raw[n] = (gv < vend) ? load_vec<DT>(rowp, gv, a.V, false)
                                      : make_uint4(tr::neg_inf_word, tr::neg_inf_word,
                                                   tr::neg_inf_word, tr::neg_inf_word);
         }
+    };
+
+    // Per vector once its load has landed: its largest logit into s_vmax and, with the curve
+    // on, the log-sum-exp of the row [HLG, The transfer function: l = x - LSE(x)] streamed per
+    // lane in base 2, with a running maximum mL of x log2(e) (floor -FLT_MAX: no inf - inf).
+    float lse_m = -3.402823466e38f, lse_s = 0.0f;
+    auto vec_pass = [&](int n) {
+        patch_vec(n);
+        // Tie this vector to the running sum: otherwise the scheduler issues every
+        // exponential of the row first and holds all results at once.
+        asm volatile("" : "+v"(lse_s), "+v"(raw[n].x), "+v"(raw[n].y), "+v"(raw[n].z),
+                     "+v"(raw[n].w));
+        float xv[EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) xv[e] = elem<DT>(raw[n], e);
+        float m;
+        if constexpr (EPV == 8) {
+            m = fmaxf(fmaxf(fmaxf(xv[0], xv[1]), fmaxf(xv[2], xv[3])),
+                      fmaxf(fmaxf(xv[4], xv[5]), fmaxf(xv[6], xv[7])));
+        } else {
+            m = fmaxf(fmaxf(xv[0], xv[1]), fmaxf(xv[2], xv[3]));
+        }
+        uint32_t mb = __float_as_uint(m);
+        if constexpr (DT != DT_BF16) {
+            // toward +inf on the bf16 grid: positive values round up, negative ones truncate
+            mb = ((int32_t)mb >= 0) ? mb + 0xFFFFu : mb;
+        }
+        s_vmax16[2 * (lane_lds + n) + 1] = (uint16_t)(mb >> 16);
+        if constexpr (HLG) {
+            const float mn = fmaxf(lse_m, m * kLog2e);
+            float t = 0.0f;
+#pragma unroll
+            for (int e = 0; e < EPV; ++e)
+                t += __builtin_amdgcn_exp2f(__builtin_fmaf(xv[e], kLog2e, -mn));
+            lse_s = __builtin_fmaf(lse_s, __builtin_amdgcn_exp2f(lse_m - mn), t);
+            lse_m = mn;
+        }
+    };
+
+    // Element (within its vector) of the lane's champion: the first one whose code equals the
+    // champion's code.
+    auto champion_elem = [&](uint32_t champ) -> uint32_t {
+        const uint32_t bits = codes_ge(s_codes[lane_lds + (champ & 31u)], champ >> 5);
+        return codes_bit_elem((uint32_t)__builtin_ctz(bits));
+    };
+    auto champion_logit = [&](uint32_t champ, int lane_v) -> float {
+        const int gv = lane_v + (int)(champ & 31u) * BS;
+        const int64_t i = (int64_t)gv * EPV + champion_elem(champ);
+        if (gv >= vend || i >= a.V) return -__builtin_inff();
+        if constexpr (DT == DT_F32) {
+            return reinterpret_cast<const float *>(rowp)[i];
+        } else {
+            const uint16_t h = reinterpret_cast<const uint16_t *>(rowp)[i];
+            if constexpr (DT == DT_BF16) return __uint_as_float((uint32_t)h << 16);
+            else return (float)__builtin_bit_cast(_Float16, h);
+        }
+    };
+
+    // Prologue, first draw. Loads go out a group of LG vectors at a time between the first
+    // draw's Philox work (which needs no logit), starting after the first vector's codes so
+    // that no wave begins by stalling on the memory queue; each vector's pass over its logits
+    // follows its codes LAG vectors later, when its load has landed, so float work mixes with
+    // the integer Philox chains. The logit pass runs for every row (greedy and invalid rows
+    // included): keeping it free of row-dependent branches keeps the register allocator from
+    // duplicating the row copy.
+    constexpr int LG = 4;
+    constexpr int LAG = 8;
+    uint32_t champ0 = 0;
+    float champ_x0 = -__builtin_inff();
+    {
+        const Stream sk = stream_k(k0);
+        int lane_v = v0 + tid;
+        asm volatile("" : "+v"(lane_v));
+        const bool do_codes = sampled && k0 < k1;
+        auto load_group = [&](int n) {
+            if (n == 0) {
+#pragma unroll
+                for (int j = 0; j < 2 * LG && j < NV; ++j) issue_load(j);
+            } else if (n % LG == 0) {
+#pragma unroll
+                for (int j = n + LG; j < n + 2 * LG && j < NV; ++j) issue_load(j);
+            }
+        };
+#pragma unroll
+        for (int n = 0; n < NV; ++n) {
+            if (do_codes) champ0 = codes_vec(sk, lane_v, n, champ0);
+            load_group(n);
+            if (n >= LAG) vec_pass(n - LAG);
+        }
+        // The champion's logit, for the bootstrap after the log-sum-exp: read once more (a
+        // cache hit) rather than picked out of the register copy by a run-time index.
+        if (do_codes) champ_x0 = champion_logit(champ0, lane_v);
+#pragma unroll
+        for (int n = (NV > LAG ? NV - LAG : 0); n < NV; ++n) vec_pass(n);
     }
 
     RowConst rc;
@@ -273,38 +333,11 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     rc.curve = a.curve;
     bool skip = bad;
 
-    // ---- log-sum-exp of the row (curve on) [HLG, The transfer function: l = x - LSE(x)],
-    // streamed per lane with a running maximum, plus each vector's largest logit. Computed
-    // for every row: keeping this block free of row-dependent branches keeps the register
-    // allocator from duplicating the row copy.
     if constexpr (HLG) {
-        float M = -__builtin_inff(), S = 0.0f;
-#pragma unroll
-        for (int n = 0; n < NV; ++n) {
-            // Tie this vector to the running sum: otherwise the scheduler issues every
-            // exponential of the row first and holds all results at once.
-            asm volatile("" : "+v"(S), "+v"(raw[n].x), "+v"(raw[n].y), "+v"(raw[n].z),
-                         "+v"(raw[n].w));
-            float xv[EPV];
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) xv[e] = elem<DT>(raw[n], e);
-            float m = xv[0];
-#pragma unroll
-            for (int e = 1; e < EPV; ++e) m = fmaxf(m, xv[e]);
-            s_vmax[lane_lds + n] = m;
-            const float Mn = fmaxf(M, m);
-            const float mb = (Mn > -__builtin_inff()) ? Mn * kLog2e : 0.0f;
-            S = S * __builtin_amdgcn_exp2f(M * kLog2e - mb);
-            float t = 0.0f;
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) t += __builtin_amdgcn_exp2f(xv[e] * kLog2e - mb);
-            S += t;
-            M = Mn;
-        }
         float lse;
         if (a.nchunk == 1) {
-            const MaxSum ms = block_maxsum(M, S, red_lse);
-            lse = (ms.m > -__builtin_inff()) ? ms.m + logf(ms.s) : -__builtin_inff();
+            const MaxSum ms = block_maxsum_log2(lse_m, lse_s, red_lse);
+            lse = (ms.s > 0.0f) ? (ms.m + __builtin_amdgcn_logf(ms.s)) * kLn2 : -__builtin_inff();
         } else {
             const float2 *part = a.partials + b * a.part_stride;
             float Mb = -__builtin_inff();
@@ -325,16 +358,32 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     }
 
     for (int k = k0; k < k1; ++k) {
+        asm volatile("" : "+v"(lane_lds));
         uint32_t champ = champ0;
-        if (k > k0 && sampled) champ = write_codes(k, false);
+        float champ_x = champ_x0;
+        int lane_v = v0 + tid;
+        asm volatile("" : "+v"(lane_v));
+        if (k > k0 && sampled) {
+            const Stream sk = stream_k(k);
+            champ = 0;
+#pragma unroll
+            for (int n = 0; n < NV; ++n) champ = codes_vec(sk, lane_v, n, champ);
+            // the champion's logit, picked out of the register copy
+            const uint32_t cs = champ & 31u;
+            const uint32_t e = champion_elem(champ);
+            uint4 cv4 = raw[0];
+#pragma unroll
+            for (int n = 1; n < NV; ++n) {
+                if (cs == (uint32_t)n) cv4 = raw[n];
+            }
+            champ_x = (lane_v + (int)cs * BS < vend) ? elem_dyn<DT>(cv4, e) : -__builtin_inff();
+        }
         // Keep per-element work inside the draw loop: without this the compiler hoists the
         // draw-invariant part of the screen (one value per element) out of the loop and runs
         // out of registers. Likewise for everything derived from the element indices.
 #pragma unroll
         for (int n = 0; n < NV; ++n)
             asm volatile("" : "+v"(raw[n].x), "+v"(raw[n].y), "+v"(raw[n].z), "+v"(raw[n].w));
-        int lane_v = v0 + tid;
-        asm volatile("" : "+v"(lane_v));
         uint64_t best = 0;
         if (!skip && greedy) {
 #pragma unroll
@@ -343,33 +392,25 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                 if (gv < vend) best = greedy_vec<DT>(raw[n], (uint32_t)(gv * EPV), best);
             }
         } else if (!skip) {
-            const uint64_t off = off0 + (uint64_t)k;
-            Stream sk = st;
-            sk.off_lo = (uint32_t)off;
-            sk.off_hi = (uint32_t)(off >> 32);
+            const Stream sk = stream_k(k);
 
-            // Bootstrap: each lane bounds from below the score of its champion (largest code,
-            // hence nearly the largest Gumbel value among the lane's elements); the block
-            // maximum of these bounds is at most the draw's winning score. Lower bounds used:
-            // g(z) >= m min(z, w) (the toe lies above its mid line, the shoulder above m w),
-            // and for code n >= 1 the word has clz(~r) >= n, so u >= 1 - 2^-n and
-            // G >= n ln 2 + ln(1 - 2^-n); code 0 only gives G >= -3.14.
+            // Bootstrap: each lane bounds from below the score of its champion (an element
+            // with the lane's largest code, hence nearly the largest Gumbel value among the
+            // lane's elements); the block maximum of these bounds is at most the draw's
+            // winning score. Lower bounds used: g(z) >= m min(z, w) (the toe lies above its
+            // mid line, the shoulder above m w), and for code n >= 1 the word has
+            // clz(~r) >= n, so u >= 1 - 2^-n and G >= n ln 2 + ln(1 - 2^-n); code 0 only
+            // gives G >= -3.14.
             float thr_s = -3.0e38f;   // (best known - slack) / ln 2 - 1
             if (!a.no_screen) {
-                const uint32_t cn = champ >> 8, cs = (champ >> 3) & 31u, ce = champ & 7u;
-                uint4 cv4 = raw[0];
-#pragma unroll
-                for (int n = 1; n < NV; ++n) {
-                    if (cs == (uint32_t)n) cv4 = raw[n];
-                }
-                const float x = elem_dyn<DT>(cv4, ce);
+                const uint32_t cn = champ >> 5;
                 float lb = -__builtin_inff();
-                if (lane_v + (int)cs * BS < vend && x > -__builtin_inff()) {
+                if (champ_x > -__builtin_inff()) {
                     float alo;
                     if constexpr (HLG) {
-                        alo = fminf(x - rc.c, rc.curve.w) * rc.mt;
+                        alo = fminf(champ_x - rc.c, rc.curve.w) * rc.mt;
                     } else {
-                        alo = x * rc.invT;
+                        alo = champ_x * rc.invT;
                     }
                     const float glo = cn == 0u ? -3.14f
                                     : cn == 1u ? 0.0f
@@ -383,51 +424,45 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                     thr_s = uniform((bs - screen_slack(bs)) * kInvLn2 - 1.0f);
             }
 
-            // Screen, one vector at a time: a vector can hold a winner only if some element
-            // passes U(max x of the vector) + (code + 1) ln 2 >= best - slack; its elements
-            // are then tested one by one with their own U(x) before the exact score.
+            // Screen, one vector at a time: a vector can hold a winner only if
+            // U(max x of the vector) + (max code + 1) ln 2 >= best - slack; its elements are
+            // then tested one by one with their own code and U(x) before the exact score.
 #pragma unroll
             for (int n = 0; n < NV; ++n) {
                 const int gv = lane_v + n * BS;
-                uint32_t bits = 0;
-                if (gv < vend) {
-                    const uint32_t cw = s_codes[lane_lds + n];
-                    float xm;
-                    if constexpr (HLG) {
-                        xm = s_vmax[lane_lds + n];
-                    } else {
-                        xm = elem<DT>(raw[n], 0);
-#pragma unroll
-                        for (int e = 1; e < EPV; ++e) xm = fmaxf(xm, elem<DT>(raw[n], e));
-                    }
-                    float Uv;
-                    if constexpr (HLG) {
-                        Uv = fmaxf(__builtin_fmaf(xm, rc.mt, -rc.mtc), -rc.mtw);
-                    } else {
-                        Uv = xm * rc.invT;
-                    }
-                    // smallest code that can pass, clamped to [0, 15] (15 = "15 or more")
-                    const float tf = __builtin_fmaf(Uv, -kInvLn2, thr_s);
-                    const uint32_t t = (uint32_t)__builtin_amdgcn_fmed3f(ceilf(tf), 0.0f, 15.0f);
-                    bits = (xm > -__builtin_inff()) ? codes_ge(cw, t) : 0u;
-                    if constexpr (EPV == 4) bits &= 0x0303u;
+                const uint32_t sv = s_vmax[lane_lds + n];
+                const float xm = __uint_as_float(sv & 0xFFFF0000u);
+                float Uv;
+                if constexpr (HLG) {
+                    Uv = fmaxf(__builtin_fmaf(xm, rc.mt, -rc.mtc), -rc.mtw);
+                } else {
+                    Uv = xm * rc.invT;
                 }
-                while (bits) {
-                    const uint32_t e = codes_bit_elem((uint32_t)__builtin_ctz(bits));
-                    bits &= bits - 1u;
-                    const float x = elem_dyn<DT>(raw[n], e);
-                    float U;
-                    if constexpr (HLG) {
-                        U = fmaxf(__builtin_fmaf(x, rc.mt, -rc.mtc), -rc.mtw);
-                    } else {
-                        U = x * rc.invT;
-                    }
-                    const uint32_t ce = (s_codes[lane_lds + n] >> (4 * e)) & 15u;
-                    const float cf = (ce == 15u) ? 32.0f : (float)ce;
-                    if (x > -__builtin_inff() && cf >= __builtin_fmaf(U, -kInvLn2, thr_s)) {
-                        const uint32_t i = (uint32_t)gv * EPV + e;
-                        const Words4 q = stream_group_in_loop(sk, i >> 2);
-                        best = umax64(best, make_key(exact_score<HLG>(x, word_dyn(q, i & 3u), rc), i));
+                // smallest code that can pass; code 15 stands for "15 or more"
+                const float tf = fminf(__builtin_fmaf(Uv, -kInvLn2, thr_s), 15.0f);
+                const float cmax = (float)(sv & 0xFFu);
+                if (gv < vend && cmax >= tf) {
+                    const uint32_t cw = s_codes[lane_lds + n];
+                    const uint32_t t = (uint32_t)fmaxf(ceilf(tf), 0.0f);
+                    uint32_t bits = codes_ge(cw, t);
+                    if constexpr (EPV == 4) bits &= 0x0303u;
+                    while (bits) {
+                        const uint32_t e = codes_bit_elem((uint32_t)__builtin_ctz(bits));
+                        bits &= bits - 1u;
+                        const float x = elem_dyn<DT>(raw[n], e);
+                        float U;
+                        if constexpr (HLG) {
+                            U = fmaxf(__builtin_fmaf(x, rc.mt, -rc.mtc), -rc.mtw);
+                        } else {
+                            U = x * rc.invT;
+                        }
+                        const uint32_t ce = (cw >> (4 * e)) & 15u;
+                        const float cf = (ce == 15u) ? 32.0f : (float)ce;
+                        if (x > -__builtin_inff() && cf >= __builtin_fmaf(U, -kInvLn2, thr_s)) {
+                            const uint32_t i = (uint32_t)gv * EPV + e;
+                            const Words4 q = stream_group_in_loop(sk, i >> 2);
+                            best = umax64(best, make_key(exact_score<HLG>(x, word_dyn(q, i & 3u), rc), i));
+                        }
                     }
                 }
             }
@@ -602,12 +637,12 @@ __global__ void k_fill_zero(uint32_t *__restrict__ p, int64_t n) {
 template <int DT, bool HLG, bool AL>
 static hipError_t launch_sample_nv(const SampleArgs &a, int nv, int bs, int grid, hipStream_t s) {
     // Blocks of up to 1024 threads hold up to 19 vectors per thread in registers (128 per
-    // lane at 16 waves per CU); the dynamic LDS holds each lane's codes (and vector maxima).
+    // lane at 16 waves per CU); the dynamic LDS holds each lane's codes and vector maxima.
 #define HS_CASE(N, MB)                                                                     \
     case N:                                                                                \
         if (bs > MB) return hipErrorInvalidValue;                                          \
         hipLaunchKernelGGL((k_sample<DT, N, HLG, MB, AL>), dim3(grid), dim3(bs),          \
-                           (size_t)(N | 1) * bs * 4 * (HLG ? 2 : 1), s, a);                 \
+                           (size_t)(N | 1) * bs * 4 * 2, s, a);                               \
         break;
     switch (nv) {
         HS_CASE(1, 1024) HS_CASE(2, 1024) HS_CASE(4, 1024) HS_CASE(6, 1024) HS_CASE(8, 1024)
