@@ -166,20 +166,28 @@ __device__ __forceinline__ float gumbel32(uint32_t r) {
     return -logf(E);
 }
 
-// Screening code of a word: n = min(clz(~r), 15), in two instructions. Setting the low 17 bits
-// of ~r caps the leading-zero count at 15; gfx950's v_bitop3_b32 forms ~r | mask in one step
-// (truth table 0xCF = ~S0 | S1, the mask in a scalar register), and v_ffbh_u32 counts.
-__device__ __forceinline__ uint32_t word_code(uint32_t r) {
+// Leading ones of the high 16 bits of d, 0..16, in two instructions: gfx950's v_bitop3_b32 forms
+// ~d | 0xFFFF (truth table 0xCF = ~S0 | S1, the mask in a scalar register) and v_ffbh_u32
+// counts its leading zeros; the low 16 bits, all set, cap the count at 16.
+__device__ __forceinline__ uint32_t lead_ones_hi16(uint32_t d) {
     uint32_t t, n;
-    asm("v_bitop3_b32 %0, %1, %2, %2 bitop3:0xcf" : "=v"(t) : "v"(r), "s"(0x1FFFFu));
+    asm("v_bitop3_b32 %0, %1, %2, %2 bitop3:0xcf" : "=v"(t) : "v"(d), "s"(0xFFFFu));
     asm("v_ffbh_u32 %0, %1" : "=v"(n) : "v"(t));
     return n;
 }
 
-// Upper bound on gumbel32(r), cheap: with n = clz(~r), v = 1 - u >= 2^-(n+1) and
-// G = -log(-log u) <= -log(v) <= (n + 1) ln 2. Returned as n (the caller folds the +1).
-__device__ __forceinline__ uint32_t gumbel_bound_bits(uint32_t r) {
-    return __clz(~r);   // 0..32 (32 for r = 0xFFFFFFFF)
+// Maxima of fp32 values that are never NaN (finite logits or -inf): the hardware max
+// instructions directly, without the quieting steps the compiler adds to fmaxf for inputs it
+// cannot prove canonical.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float max2f(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
 }
 
 // ------------------------------------------------------------------------------------------

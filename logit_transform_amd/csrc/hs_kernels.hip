@@ -16,12 +16,17 @@
 //
 // Screening. A draw's winner is the exact argmax over all elements, but the expensive part
 // of an element's score (curve branches, two logarithms) is evaluated only when an upper
-// bound on that score reaches the best score already found in the block minus a slack:
-//   score = l'/T + G(r) <= U(x) + (clz(~r) + 1) ln 2,
+// bound on that score reaches a lower bound on the draw's winning score, less a slack:
+//   score = l'/T + G(r) <= U(x) + (n(r) + 1) ln 2,
 // where U(x) = (m/T) * max(x - c, -w) bounds g(x - c)/T (g lies below its mid line past the
-// shoulder knot and below -m*w in the toe) and clz(~r) bounds G from the word's leading
-// ones. The bound is rigorous up to fp32 rounding, which the slack covers many times over,
-// so the screened result equals the exhaustive one bit for bit (a test checks this).
+// shoulder knot and below -m*w in the toe) and n(r), the leading ones of the word, bounds G
+// (G(r) <= -log(1 - u) <= (n + 1) ln 2). The first pass over a draw keeps, per vector, only
+// the largest word (and so the largest n); a vector whose largest logit and largest word
+// cannot reach the bound is skipped whole, and the few that can are drawn again and tested
+// element by element. The lower bound is the exact score of one element per lane, the one
+// with the lane's largest word, maximised over the block. The bounds are rigorous up to fp32
+// rounding, which the slack covers many times over, so the screened result equals the
+// exhaustive one bit for bit (a test checks this).
 #include <hip/hip_runtime.h>
 
 #include "hs_device.hpp"
@@ -36,6 +41,15 @@ __device__ __forceinline__ float screen_slack(float s) {
 // A block-uniform float moved to a scalar register.
 __device__ __forceinline__ float uniform(float v) {
     return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
+// Wave priority for the issue arbiter (s_setprio takes an immediate; p is a constant after
+// unrolling).
+__device__ __forceinline__ void set_prio(int p) {
+    if (p >= 3) __builtin_amdgcn_s_setprio(3);
+    else if (p == 2) __builtin_amdgcn_s_setprio(2);
+    else if (p == 1) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
 }
 
 // Per-row constants of one block.
@@ -100,39 +114,41 @@ __device__ __forceinline__ uint64_t greedy_vec(uint4 raw, uint32_t i0, uint64_t 
     return best;
 }
 
-// Which of the 8 codes in cw (4 bits each) are >= t (0..15). Bytes serve as 8-bit lanes (no
-// carry crosses a nibble): code 2j is tested in byte j of the low half, code 2j+1 in byte j
-// of the high half. Bit 8j of the result flags code 2j, bit 8j+1 code 2j+1.
-__device__ __forceinline__ uint32_t codes_ge(uint32_t cw, uint32_t t) {
-    const uint32_t add = (16u - t) * 0x01010101u;
-    const uint32_t lo = ((cw & 0x0F0F0F0Fu) + add) & 0x10101010u;
-    const uint32_t hi = (((cw >> 4) & 0x0F0F0F0Fu) + add) & 0x10101010u;
-    return (lo >> 4) | (hi >> 3);
+// Largest of the EPV logits of a vector.
+template <int EPV>
+__device__ __forceinline__ float vec_max(const float (&x)[EPV]) {
+    if constexpr (EPV == 8) {
+        const float t = max3f(x[0], x[1], x[2]);
+        const float u = max3f(x[3], x[4], x[5]);
+        return max2f(max3f(x[6], x[7], t), u);
+    } else {
+        return max2f(max3f(x[0], x[1], x[2]), x[3]);
+    }
 }
-
-// Element index of a set bit position of codes_ge's result.
-__device__ __forceinline__ uint32_t codes_bit_elem(uint32_t p) { return ((p >> 3) << 1) | (p & 1u); }
 
 template <int DT, int NV, bool HLG, int MAXBS, bool ALIGNED>
 __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     using tr = dtype_traits<DT>;
     constexpr int EPV = tr::epv;
-    // Dynamic LDS, per lane and vector: the word codes of the current draw (EPV nibbles) in
-    // s_codes; in s_vmax the vector's largest logit as a bf16-grid upper bound (high half,
-    // draw-invariant) and the largest of its codes (low half). Each lane's entries are
-    // contiguous, so every access is one base register plus an immediate offset.
-    extern __shared__ uint32_t s_dyn[];
-    __shared__ float2 red_lse[16];
-    __shared__ float red_boot[16];
-    __shared__ uint64_t red_draw[16];
+    constexpr int NG = EPV / 4;                // Philox calls per vector
+    constexpr int D = NV < 8 ? NV : 8;         // loads in flight per lane
+    constexpr int LAG = NV < 7 ? NV - 1 : 6;   // slots of random words ahead of the logits
+    // Dynamic LDS, one dword per lane and slot: the vector's largest logit as a bf16-grid upper
+    // bound in the low half (draw-invariant) and the high 16 bits of its largest random word of
+    // the current draw in the high half. Each lane's entries are contiguous (odd stride: lanes
+    // hit distinct banks), so every access is one base register plus an immediate offset.
+    extern __shared__ uint32_t s_vec[];
+    __shared__ float red_m[16], red_s[16], red_x[16];
+    // two buffers, alternating between draws: without a bootstrap (greedy rows, no screening)
+    // nothing else separates one draw's reads of the buffer from the next draw's writes
+    __shared__ uint64_t red_draw[2][16];
     __shared__ int s_last;
 
     const int tid = threadIdx.x;
     const int BS = blockDim.x;
-    constexpr int SC = NV | 1;   // per-lane stride (odd: lanes hit distinct banks)
-    uint32_t *s_codes = s_dyn;
-    uint32_t *s_vmax = s_dyn + SC * BS;
-    int lane_lds = tid * SC;   // re-made opaque per draw: no per-vector address hoisting
+    constexpr int SC = NV | 1;
+    uint16_t *s_vec16 = reinterpret_cast<uint16_t *>(s_vec);
+    int lane_lds = tid * SC;
     // block coordinates in scalar registers (the divisions would otherwise run per lane)
     int bid = blockIdx.x;
     const int chunk = __builtin_amdgcn_readfirstlane(bid % a.nchunk);
@@ -151,33 +167,81 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
         bad = bad || !(fabsf(mu) < __builtin_inff());
     }
     const bool greedy = (T == 0.0f);
-    const bool sampled = !bad && !greedy;
 
-    // ---- issue the loads of this chunk (registers) ----
+    // ---- this block's chunk of the row: lane t owns vectors v0 + t + n*BS, n < NV ----
     const int v0 = chunk * (int)a.cv;
     const int vend = (int)min(a.nvec, (int64_t)v0 + a.cv);
     const int nfull = (int)(a.V / EPV);   // vectors with all EPV elements inside the row
+    const int vlim = min(vend, nfull);    // vectors below this one load whole
     const char *rowp = reinterpret_cast<const char *>(a.data) + b * a.ld * tr::esize;
-    uint4 raw[NV];
-    // ALIGNED: a vector outside the chunk or past the last full vector reads an in-row full
-    // vector instead (clamped index) and is patched after the Philox phase, when waiting for
-    // it costs nothing. The loads carry no branch: a branch would merge the loaded registers
-    // into copies, and every copy waits for its load.
-    const int gmax = min(vend, nfull) - 1;   // >= 0 when ALIGNED: the caller ensures V >= epv
-    auto issue_load = [&](int n) {
-        if constexpr (ALIGNED) {
-            const int gv = min(v0 + tid + n * BS, gmax);
-            raw[n] = *reinterpret_cast<const uint4 *>(rowp + (size_t)gv * 16);
-        } else {
-            const int gv = v0 + tid + n * BS;
-            if (gv < vend) {
-                raw[n] = load_vec<DT>(rowp, gv, a.V, false);
+    int lane_v = v0 + tid;
+    // the last vector index of this wave at slot 0 (wave-uniform)
+    const int wave_last = __builtin_amdgcn_readfirstlane(v0 + (tid | 63));
+    const uint4 ninf4 = make_uint4(tr::neg_inf_word, tr::neg_inf_word, tr::neg_inf_word,
+                                   tr::neg_inf_word);
+
+    // Vector gv of the chunk; -inf past the chunk or the row.
+    auto fetch = [&](int gv) -> uint4 {
+        if (gv >= vend) return ninf4;
+        return load_vec<DT>(rowp, gv, a.V, ALIGNED);
+    };
+    // ALIGNED: slot n's load carries no branch (a slot past the whole vectors reads an in-row
+    // whole vector instead, clamped index) and is patched when its data is used, with selects
+    // only: a load inside the pipelined pass would make the compiler wait for every load in
+    // flight. The row's partial last vector (V not a multiple of EPV) is read element by
+    // element up front by every lane, with clamped addresses (one cache line, no branch); only
+    // waves that reach past vlim at slot n test per lane.
+    const int gclamp = vlim - 1;   // >= 0: the launcher ensures V >= epv for ALIGNED
+    uint4 rag = ninf4;
+    if constexpr (ALIGNED) {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = tr::neg_inf_word;
+        const int64_t i0 = (int64_t)nfull * EPV;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+            const int64_t i = min(i0 + e, a.V - 1);
+            uint32_t h;
+            if constexpr (DT == DT_F32) {
+                h = reinterpret_cast<const uint32_t *>(rowp)[i];
             } else {
-                raw[n] = make_uint4(tr::neg_inf_word, tr::neg_inf_word, tr::neg_inf_word,
-                                    tr::neg_inf_word);
+                h = reinterpret_cast<const uint16_t *>(rowp)[i];
+            }
+            if (i0 + e < a.V) {
+                if constexpr (DT == DT_F32) {
+                    w[e] = h;
+                } else {
+                    const int j = e >> 1;
+                    w[j] = (e & 1) ? ((w[j] & 0x0000FFFFu) | (h << 16))
+                                   : ((w[j] & 0xFFFF0000u) | h);
+                }
             }
         }
+        rag = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    auto issue_load = [&](int n) -> uint4 {
+        if constexpr (ALIGNED) {
+            const int gv = min(lane_v + n * BS, gclamp);
+            return *reinterpret_cast<const uint4 *>(rowp + (size_t)gv * 16);
+        } else {
+            return fetch(lane_v + n * BS);
+        }
     };
+    auto patch = [&](int n, uint4 v) -> uint4 {
+        if constexpr (ALIGNED) {
+            if (wave_last + n * BS >= vlim) {
+                const int gv = lane_v + n * BS;
+                const bool past = gv >= vend;
+                const bool part = gv >= nfull;
+                v.x = past ? ninf4.x : part ? rag.x : v.x;
+                v.y = past ? ninf4.y : part ? rag.y : v.y;
+                v.z = past ? ninf4.z : part ? rag.z : v.z;
+                v.w = past ? ninf4.w : part ? rag.w : v.w;
+            }
+        }
+        return v;
+    };
+
     const uint64_t seed = a.seed[b];
     const uint64_t off0 = a.offset[b];
     Stream st;
@@ -191,284 +255,384 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
         sk.off_hi = (uint32_t)(off >> 32);
         return sk;
     };
-    // Per lane and vector, s_vmax holds the vector's largest logit in its high half (exact
-    // for bf16 input, rounded toward +inf to the bf16 grid otherwise, so it stays an upper
-    // bound) and the vector's largest word code of the current draw in its low half.
-    uint16_t *s_vmax16 = reinterpret_cast<uint16_t *>(s_vmax);
 
-    // Word codes of one vector for draw stream sk: EPV 4-bit codes into s_codes, their
-    // maximum into s_vmax. Vectors past the chunk are coded too (their words are never
-    // used). Returns the lane's champion key after this vector: max code << 5 | vector.
-    auto codes_vec = [&](const Stream &sk, int lane_v, int n, uint32_t champ) -> uint32_t {
-        uint32_t q = ((uint32_t)(lane_v + n * BS) * EPV) >> 2;
+    // Random words of slot n for draw stream sk: their maximum goes to the slot's LDS dword
+    // (high half) and into the lane's champion key, max word & ~31 | slot. Slots past the
+    // chunk are drawn too (their words are never used).
+    auto draw_vec = [&](const Stream &sk, int n, uint32_t champ) -> uint32_t {
+        uint32_t q = (uint32_t)(lane_v + n * BS) * NG;
         asm volatile("" : "+v"(q));
-        uint32_t cw = 0, vm = 0;
+        uint32_t mw = 0;
 #pragma unroll
-        for (int g = 0; g < EPV / 4; ++g) {
-            const Words4 qw = philox4x32_10_uk(q + g, sk.row, sk.off_lo, sk.off_hi, sk.key0,
-                                               sk.key1);
-            uint32_t c[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                c[e] = word_code(qw.w[e]);
-                cw |= c[e] << (4 * (4 * g + e));
-            }
-            vm = max(vm, max(max(c[0], c[1]), max(c[2], c[3])));
+        for (int g = 0; g < NG; ++g) {
+            const Words4 w = philox4x32_10_uk(q + g, sk.row, sk.off_lo, sk.off_hi, sk.key0,
+                                              sk.key1);
+            mw = max(mw, max(max(w.w[0], w.w[1]), max(w.w[2], w.w[3])));
         }
-        s_codes[lane_lds + n] = cw;
-        s_vmax16[2 * (lane_lds + n)] = (uint16_t)vm;
-        return max(champ, (vm << 5) | (uint32_t)n);
+        s_vec16[2 * (lane_lds + n) + 1] = (uint16_t)(mw >> 16);
+        champ = max(champ, (mw & ~31u) | (uint32_t)n);
+        // one running maximum: otherwise the compiler regroups the chain of maxima and keeps
+        // every slot's word alive until the end of the pass
+        asm volatile("" : "+v"(champ));
+        return champ;
     };
 
-    // Patch the vectors the branch-free loads could not take whole (ragged row end, vectors
-    // outside the chunk); waits for that vector's load.
-    auto patch_vec = [&](int n) {
-        if constexpr (ALIGNED) {
-            const int gv = v0 + tid + n * BS;
-            if (gv >= vend || gv >= nfull)
-                raw[n] = (gv < vend) ? load_vec<DT>(rowp, gv, a.V, false)
-                                     : make_uint4(tr::neg_inf_word, tr::neg_inf_word,
-                                                  tr::neg_inf_word, tr::neg_inf_word);
-        }
-    };
-
-    // Per vector once its load has landed: its largest logit into s_vmax and, with the curve
-    // on, the log-sum-exp of the row [HLG, The transfer function: l = x - LSE(x)] streamed per
-    // lane in base 2, with a running maximum mL of x log2(e) (floor -FLT_MAX: no inf - inf).
-    float lse_m = -3.402823466e38f, lse_s = 0.0f;
-    auto vec_pass = [&](int n) {
-        patch_vec(n);
-        // Tie this vector to the running sum: otherwise the scheduler issues every
-        // exponential of the row first and holds all results at once.
-        asm volatile("" : "+v"(lse_s), "+v"(raw[n].x), "+v"(raw[n].y), "+v"(raw[n].z),
-                     "+v"(raw[n].w));
+    // Slot n's logits: the vector's largest logit (rounded up to the bf16 grid for f32/f16
+    // input, so it stays an upper bound) into the low half of its LDS dword, the lane's largest
+    // logit, and with the curve on the log-sum-exp of the row [HLG, The transfer function:
+    // l = x - LSE(x)], streamed per lane in base 2 against a fixed reference r, the scaled
+    // maximum of the lane's first vector: s = sum 2^(x log2(e) - r). Lanes whose largest logit
+    // ends up far from r (where the sum could overflow or lose its terms) sum again against
+    // their own maximum after the pass.
+    float xmax_lane = -__builtin_inff();
+    float lse_r = 0.0f, lse_s = 0.0f;
+    auto data_vec = [&](int n, uint4 v) {
+        // Tie this vector to the running sums: otherwise the scheduler issues the exponentials
+        // of many vectors first and holds all their results at once.
+        asm volatile("" : "+v"(lse_s), "+v"(xmax_lane), "+v"(v.x), "+v"(v.y), "+v"(v.z),
+                     "+v"(v.w));
         float xv[EPV];
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) xv[e] = elem<DT>(raw[n], e);
-        float m;
-        if constexpr (EPV == 8) {
-            m = fmaxf(fmaxf(fmaxf(xv[0], xv[1]), fmaxf(xv[2], xv[3])),
-                      fmaxf(fmaxf(xv[4], xv[5]), fmaxf(xv[6], xv[7])));
-        } else {
-            m = fmaxf(fmaxf(xv[0], xv[1]), fmaxf(xv[2], xv[3]));
-        }
+        for (int e = 0; e < EPV; ++e) xv[e] = elem<DT>(v, e);
+        const float m = vec_max<EPV>(xv);
+        xmax_lane = max2f(xmax_lane, m);
         uint32_t mb = __float_as_uint(m);
         if constexpr (DT != DT_BF16) {
             // toward +inf on the bf16 grid: positive values round up, negative ones truncate
             mb = ((int32_t)mb >= 0) ? mb + 0xFFFFu : mb;
         }
-        s_vmax16[2 * (lane_lds + n) + 1] = (uint16_t)(mb >> 16);
+        s_vec16[2 * (lane_lds + n)] = (uint16_t)(mb >> 16);
         if constexpr (HLG) {
-            const float mn = fmaxf(lse_m, m * kLog2e);
-            float t = 0.0f;
+            if (n == 0) lse_r = (m > -__builtin_inff()) ? m * kLog2e : 0.0f;
 #pragma unroll
             for (int e = 0; e < EPV; ++e)
-                t += __builtin_amdgcn_exp2f(__builtin_fmaf(xv[e], kLog2e, -mn));
-            lse_s = __builtin_fmaf(lse_s, __builtin_amdgcn_exp2f(lse_m - mn), t);
-            lse_m = mn;
+                lse_s += __builtin_amdgcn_exp2f(__builtin_fmaf(xv[e], kLog2e, -lse_r));
         }
     };
 
-    // Element (within its vector) of the lane's champion: the first one whose code equals the
-    // champion's code.
-    auto champion_elem = [&](uint32_t champ) -> uint32_t {
-        const uint32_t bits = codes_ge(s_codes[lane_lds + (champ & 31u)], champ >> 5);
-        return codes_bit_elem((uint32_t)__builtin_ctz(bits));
+    const bool sampled = !bad && !greedy;
+    const bool screen = sampled && !a.no_screen;
+    const float invT = 1.0f / T;
+    // Linear part of the score used to rank bootstrap candidates before c = LSE + mu is known:
+    // (m/T) x with the curve on (the mid line of g, up to the common shift -(m/T) c), x/T
+    // without it.
+    const float lin = HLG ? a.curve.m * invT : invT;
+    // Bootstrap candidate of a lane for draw stream sk: the element holding the largest word of
+    // its champion vector v (nearly the largest Gumbel value among the lane's elements). The
+    // vector's words are drawn again into cw (kept for the screen). Returns the candidate's rank
+    // key (lin x - log(1 - u) -- a monotone stand-in for the Gumbel value, close to it where u
+    // is near 1 -- and the lane) and its logit and word.
+    struct Cand {
+        uint64_t key;
+        float x;
+        uint32_t w;
     };
-    auto champion_logit = [&](uint32_t champ, int lane_v) -> float {
-        const int gv = lane_v + (int)(champ & 31u) * BS;
-        const int64_t i = (int64_t)gv * EPV + champion_elem(champ);
-        if (gv >= vend || i >= a.V) return -__builtin_inff();
-        if constexpr (DT == DT_F32) {
-            return reinterpret_cast<const float *>(rowp)[i];
+    auto candidate = [&](const Stream &sk, uint32_t champ, const uint4 &v,
+                         uint32_t (&cw)[EPV]) -> Cand {
+        Cand c{0ull, -__builtin_inff(), 0u};
+        uint32_t q = (uint32_t)(lane_v + (int)(champ & 31u) * BS) * NG;
+        asm volatile("" : "+v"(q));
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const Words4 w = philox4x32_10_uk(q + g, sk.row, sk.off_lo, sk.off_hi, sk.key0,
+                                              sk.key1);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cw[4 * g + e] = w.w[e];
+        }
+#pragma unroll
+        for (int e = EPV - 1; e >= 0; --e) {
+            if ((cw[e] ^ champ) < 32u) {
+                c.w = cw[e];
+                c.x = elem<DT>(v, e);
+            }
+        }
+        const float nlv = __builtin_amdgcn_logf(__builtin_fmaf((float)(~c.w), 0x1p-32f, 0x1p-33f));
+        const bool ok = c.x > -__builtin_inff() && lane_v + (int)(champ & 31u) * BS < vend;
+        c.key = ok ? make_key(__builtin_fmaf(c.x, lin, -nlv * kLn2), (uint32_t)tid) : 0ull;
+        return c;
+    };
+    // The champion slot's vector, read with a branch-free (clamped) address on the aligned path.
+    auto issue_slot_load = [&](int n) -> uint4 {
+        if constexpr (ALIGNED) {
+            const int gv = min(lane_v + n * BS, gclamp);
+            return *reinterpret_cast<const uint4 *>(rowp + (size_t)gv * 16);
         } else {
-            const uint16_t h = reinterpret_cast<const uint16_t *>(rowp)[i];
-            if constexpr (DT == DT_BF16) return __uint_as_float((uint32_t)h << 16);
-            else return (float)__builtin_bit_cast(_Float16, h);
+            return fetch(lane_v + n * BS);
         }
     };
 
-    // Prologue, first draw. Loads go out a group of LG vectors at a time between the first
-    // draw's Philox work (which needs no logit), starting after the first vector's codes so
-    // that no wave begins by stalling on the memory queue; each vector's pass over its logits
-    // follows its codes LAG vectors later, when its load has landed, so float work mixes with
-    // the integer Philox chains. The logit pass runs for every row (greedy and invalid rows
-    // included): keeping it free of row-dependent branches keeps the register allocator from
-    // duplicating the row copy.
-    constexpr int LG = 4;
-    constexpr int LAG = 8;
+    // ---- one pass over the chunk: the first draw's random words (which need no logit) run
+    // LAG slots ahead of the logits, so the first loads land while they are computed; D loads
+    // stay in flight. Once the last slot is drawn the lane's champion vector is known: it is
+    // read again and its words drawn again while the last slots' logits are processed. The
+    // pass is the same for every row (greedy and invalid rows draw words they never use):
+    // without row-dependent branches the scheduler interleaves the integer Philox chains with
+    // the float work freely. ----
     uint32_t champ0 = 0;
-    float champ_x0 = -__builtin_inff();
+    uint4 craw0 = ninf4;
+    uint32_t cw0[EPV];
+    Cand cand0{0ull, -__builtin_inff(), 0u};
     {
         const Stream sk = stream_k(k0);
-        int lane_v = v0 + tid;
-        asm volatile("" : "+v"(lane_v));
-        const bool do_codes = sampled && k0 < k1;
-        auto load_group = [&](int n) {
-            if (n == 0) {
+        uint4 buf[D];
 #pragma unroll
-                for (int j = 0; j < 2 * LG && j < NV; ++j) issue_load(j);
-            } else if (n % LG == 0) {
+        for (int n = 0; n < D; ++n) buf[n] = issue_load(n);
 #pragma unroll
-                for (int j = n + LG; j < n + 2 * LG && j < NV; ++j) issue_load(j);
+        for (int n = 0; n < NV + LAG; ++n) {
+            if (n < NV) champ0 = draw_vec(sk, n, champ0);
+            if (n == NV) craw0 = issue_slot_load((int)(champ0 & 31u));
+            if (n == NV + LAG / 2) cand0 = candidate(sk, champ0, craw0, cw0);
+            const int j = n - LAG;
+            if (j >= 0 && j < NV) {
+                data_vec(j, patch(j, buf[j % D]));
+                if (j + D < NV) buf[j % D] = issue_load(j + D);
             }
-        };
-#pragma unroll
-        for (int n = 0; n < NV; ++n) {
-            if (do_codes) champ0 = codes_vec(sk, lane_v, n, champ0);
-            load_group(n);
-            if (n >= LAG) vec_pass(n - LAG);
         }
-        // The champion's logit, for the bootstrap after the log-sum-exp: read once more (a
-        // cache hit) rather than picked out of the register copy by a run-time index.
-        if (do_codes) champ_x0 = champion_logit(champ0, lane_v);
-#pragma unroll
-        for (int n = (NV > LAG ? NV - LAG : 0); n < NV; ++n) vec_pass(n);
+        if (NV + LAG <= NV) craw0 = issue_slot_load((int)(champ0 & 31u));
+        if (NV + LAG <= NV + LAG / 2) cand0 = candidate(sk, champ0, craw0, cw0);
+        // a champion vector past the whole vectors of the chunk: its true data, again
+        if (ALIGNED && lane_v + (int)(champ0 & 31u) * BS >= vlim) {
+            craw0 = fetch(lane_v + (int)(champ0 & 31u) * BS);
+            cand0 = candidate(sk, champ0, craw0, cw0);
+        }
     }
+    if constexpr (HLG) {
+        // A lane whose largest logit lies more than 100 binary orders above or below its
+        // reference (never for logits of ordinary range) sums again against that maximum.
+        const float tm = xmax_lane * kLog2e;
+        if (xmax_lane > -__builtin_inff() && !(fabsf(tm - lse_r) <= 100.0f)) {
+            lse_r = tm;
+            lse_s = 0.0f;
+            for (int n = 0; n < NV; ++n) {
+                const uint4 v = fetch(lane_v + n * BS);
+#pragma unroll
+                for (int e = 0; e < EPV; ++e)
+                    lse_s += __builtin_amdgcn_exp2f(__builtin_fmaf(elem<DT>(v, e), kLog2e, -lse_r));
+            }
+        }
+    }
+    // Wave maximum of the candidates' keys; the owning lane leaves its logit and word in LDS
+    // beside the key (slot wid), for the block maximum after the next barrier.
+    auto cand_to_lds = [&](const Cand &c, int lane, int wid, uint64_t *rk, float *rx,
+                           uint32_t *rw) {
+        const uint64_t wk = wave_max_u64(c.key);
+        if (lane == 0) rk[wid] = wk;
+        if (wk != 0 && c.key == wk) {
+            rx[wid] = c.x;
+            rw[wid] = c.w;
+        }
+    };
+    __shared__ uint64_t red_ck[16];
+    __shared__ float red_cx[16];
+    __shared__ uint32_t red_cw[16];
 
+    // ---- block combine, one barrier: log-sum-exp (curve on), the largest logit, and the first
+    // draw's bootstrap candidate ----
     RowConst rc;
-    rc.invT = 1.0f / T;
+    rc.invT = invT;
     rc.c = 0.0f;
     rc.mt = rc.mtc = rc.mtw = 0.0f;
     rc.curve = a.curve;
     bool skip = bad;
-
-    if constexpr (HLG) {
-        float lse;
-        if (a.nchunk == 1) {
-            const MaxSum ms = block_maxsum_log2(lse_m, lse_s, red_lse);
-            lse = (ms.s > 0.0f) ? (ms.m + __builtin_amdgcn_logf(ms.s)) * kLn2 : -__builtin_inff();
-        } else {
-            const float2 *part = a.partials + b * a.part_stride;
-            float Mb = -__builtin_inff();
-            for (int j = 0; j < a.nchunk; ++j) Mb = fmaxf(Mb, part[j].x);
-            float Sb = 0.0f;
-            if (Mb > -__builtin_inff())
-                for (int j = 0; j < a.nchunk; ++j)
-                    if (part[j].x > -__builtin_inff())
-                        Sb += part[j].y * __builtin_amdgcn_exp2f((part[j].x - Mb) * kLog2e);
-            lse = (Mb > -__builtin_inff()) ? Mb + logf(Sb) : -__builtin_inff();
+    float xmax_blk;
+    Cand cbest{0ull, -__builtin_inff(), 0u};
+    {
+        int lane = threadIdx.x & 63;
+        asm volatile("" : "+v"(lane));
+        int wid = threadIdx.x >> 6;
+        asm volatile("" : "+v"(wid));
+        const int nw = (BS + 63) >> 6;
+        if (screen) cand_to_lds(cand0, lane, wid, red_ck, red_cx, red_cw);
+        const float xw = wave_max(xmax_lane);
+        float mw = 0.0f, sw = 0.0f;
+        if constexpr (HLG) {
+            mw = wave_max(lse_r);
+            sw = wave_sum(lse_s * __builtin_amdgcn_exp2f(lse_r - mw));
         }
-        lse = uniform(lse);
-        if (!(lse > -__builtin_inff())) skip = true;   // no finite logit in the row
-        rc.c = uniform(lse + mu);
-        rc.mt = uniform(a.curve.m * rc.invT);
-        rc.mtc = uniform(rc.mt * rc.c);
-        rc.mtw = uniform(rc.mt * a.curve.w);
+        if (lane == 0) {
+            red_x[wid] = xw;
+            if constexpr (HLG) {
+                red_m[wid] = mw;
+                red_s[wid] = sw;
+            }
+        }
+        __syncthreads();
+        xmax_blk = uniform(wave_max(lane < nw ? red_x[lane] : -__builtin_inff()));
+        if (screen) {
+            const uint64_t bk = wave_max_u64(lane < nw ? red_ck[lane] : 0ull);
+            if (bk != 0) {
+                const int bw = (int)(0xFFFFFFFFu - (uint32_t)bk) >> 6;
+                cbest.key = bk;
+                cbest.x = red_cx[bw];
+                cbest.w = red_cw[bw];
+            }
+        }
+        if constexpr (HLG) {
+            float lse;
+            if (a.nchunk == 1) {
+                const float pm = lane < nw ? red_m[lane] : -3.402823466e38f;
+                const float mb = wave_max(pm);
+                const float sb = wave_sum(lane < nw ? red_s[lane] * __builtin_amdgcn_exp2f(pm - mb) : 0.0f);
+                lse = (sb > 0.0f) ? (mb + __builtin_amdgcn_logf(sb)) * kLn2 : -__builtin_inff();
+            } else {
+                const float2 *part = a.partials + b * a.part_stride;
+                float Mb = -__builtin_inff();
+                for (int j = 0; j < a.nchunk; ++j) Mb = fmaxf(Mb, part[j].x);
+                float Sb = 0.0f;
+                if (Mb > -__builtin_inff())
+                    for (int j = 0; j < a.nchunk; ++j)
+                        if (part[j].x > -__builtin_inff())
+                            Sb += part[j].y * __builtin_amdgcn_exp2f((part[j].x - Mb) * kLog2e);
+                lse = (Mb > -__builtin_inff()) ? Mb + logf(Sb) : -__builtin_inff();
+            }
+            lse = uniform(lse);
+            if (!(lse > -__builtin_inff())) skip = true;   // no finite logit in the row
+            rc.c = uniform(lse + mu);
+            rc.mt = uniform(a.curve.m * rc.invT);
+            rc.mtc = uniform(rc.mt * rc.c);
+            rc.mtw = uniform(rc.mt * a.curve.w);
+        }
     }
+    // A lower bound on any draw's winning score from the chunk's largest logit: its curve value
+    // is at least (m/T) min(x - c, w) (the toe lies above its mid line, the shoulder above m w)
+    // and every Gumbel value is at least G(0) > -3.14.
+    float lb_x = -__builtin_inff();
+    if (xmax_blk > -__builtin_inff()) {
+        if constexpr (HLG) {
+            lb_x = uniform(fminf(xmax_blk - rc.c, rc.curve.w) * rc.mt - 3.14f);
+        } else {
+            lb_x = uniform(xmax_blk * rc.invT - 3.14f);
+        }
+    }
+    // Smallest word code n (leading ones) with which a value of largest logit x can reach the
+    // screen threshold thr_s: (thr_s ln 2 - U(x)) / ln 2 with U(x) = (m/T) max(x - c, -w)
+    // (curve on) or x/T, as min(x sa + sb, sc). Set once the threshold is known.
+    float sa = 0.0f, sb = 0.0f, sc = __builtin_inff();
+    auto code_needed = [&](float x) -> float {
+        return fminf(__builtin_fmaf(x, sa, sb), sc);
+    };
+    // Exact scores of the elements of slot n (vector v, words w) that pass their own bound,
+    // folded into the draw's best key; greedy rows compare logits.
+    auto score_words = [&](int n, const uint4 &v, const uint32_t (&w)[EPV],
+                           uint64_t best) -> uint64_t {
+        const int gv = lane_v + n * BS;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+            const float x = elem<DT>(v, e);
+            const float cf = (float)__clz(~w[e]);
+            if (x > -__builtin_inff() && cf >= code_needed(x)) {
+                const uint32_t i = (uint32_t)gv * EPV + e;
+                best = umax64(best, make_key(exact_score<HLG>(x, w[e], rc), i));
+            }
+        }
+        return best;
+    };
+    auto score_vec = [&](const Stream &sk, int n, const uint4 &v, uint64_t best) -> uint64_t {
+        const int gv = lane_v + n * BS;
+        if (greedy) return greedy_vec<DT>(v, (uint32_t)gv * EPV, best);
+        uint32_t q = (uint32_t)gv * NG;
+        asm volatile("" : "+v"(q));
+        uint32_t w[EPV];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const Words4 ww = philox4x32_10_uk(q + g, sk.row, sk.off_lo, sk.off_hi, sk.key0,
+                                               sk.key1);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[4 * g + e] = ww.w[e];
+        }
+        return score_words(n, v, w, best);
+    };
 
     for (int k = k0; k < k1; ++k) {
         asm volatile("" : "+v"(lane_lds));
-        uint32_t champ = champ0;
-        float champ_x = champ_x0;
-        int lane_v = v0 + tid;
         asm volatile("" : "+v"(lane_v));
-        if (k > k0 && sampled) {
-            const Stream sk = stream_k(k);
+        const Stream sk = stream_k(k);
+        uint32_t champ = champ0;
+        if (k > k0 && !skip && screen) {
+            // this draw's words, champions and bootstrap candidate (one more barrier)
             champ = 0;
 #pragma unroll
-            for (int n = 0; n < NV; ++n) champ = codes_vec(sk, lane_v, n, champ);
-            // the champion's logit, picked out of the register copy
-            const uint32_t cs = champ & 31u;
-            const uint32_t e = champion_elem(champ);
-            uint4 cv4 = raw[0];
-#pragma unroll
-            for (int n = 1; n < NV; ++n) {
-                if (cs == (uint32_t)n) cv4 = raw[n];
+            for (int n = 0; n < NV; ++n) champ = draw_vec(sk, n, champ);
+            craw0 = fetch(lane_v + (int)(champ & 31u) * BS);
+            const Cand cd = candidate(sk, champ, craw0, cw0);
+            int lane = threadIdx.x & 63;
+            int wid = threadIdx.x >> 6;
+            const int nw = (BS + 63) >> 6;
+            cand_to_lds(cd, lane, wid, red_ck, red_cx, red_cw);
+            __syncthreads();
+            const uint64_t bk = wave_max_u64(lane < nw ? red_ck[lane] : 0ull);
+            cbest.key = bk;
+            if (bk != 0) {
+                const int bw = (int)(0xFFFFFFFFu - (uint32_t)bk) >> 6;
+                cbest.x = red_cx[bw];
+                cbest.w = red_cw[bw];
             }
-            champ_x = (lane_v + (int)cs * BS < vend) ? elem_dyn<DT>(cv4, e) : -__builtin_inff();
         }
-        // Keep per-element work inside the draw loop: without this the compiler hoists the
-        // draw-invariant part of the screen (one value per element) out of the loop and runs
-        // out of registers. Likewise for everything derived from the element indices.
-#pragma unroll
-        for (int n = 0; n < NV; ++n)
-            asm volatile("" : "+v"(raw[n].x), "+v"(raw[n].y), "+v"(raw[n].z), "+v"(raw[n].w));
         uint64_t best = 0;
-        if (!skip && greedy) {
-#pragma unroll
-            for (int n = 0; n < NV; ++n) {
-                const int gv = lane_v + n * BS;
-                if (gv < vend) best = greedy_vec<DT>(raw[n], (uint32_t)(gv * EPV), best);
-            }
-        } else if (!skip) {
-            const Stream sk = stream_k(k);
-
-            // Bootstrap: each lane bounds from below the score of its champion (an element
-            // with the lane's largest code, hence nearly the largest Gumbel value among the
-            // lane's elements); the block maximum of these bounds is at most the draw's
-            // winning score. Lower bounds used: g(z) >= m min(z, w) (the toe lies above its
-            // mid line, the shoulder above m w), and for code n >= 1 the word has
-            // clz(~r) >= n, so u >= 1 - 2^-n and G >= n ln 2 + ln(1 - 2^-n); code 0 only
-            // gives G >= -3.14.
-            float thr_s = -3.0e38f;   // (best known - slack) / ln 2 - 1
-            if (!a.no_screen) {
-                const uint32_t cn = champ >> 5;
-                float lb = -__builtin_inff();
-                if (champ_x > -__builtin_inff()) {
-                    float alo;
-                    if constexpr (HLG) {
-                        alo = fminf(champ_x - rc.c, rc.curve.w) * rc.mt;
-                    } else {
-                        alo = champ_x * rc.invT;
-                    }
-                    const float glo = cn == 0u ? -3.14f
-                                    : cn == 1u ? 0.0f
-                                    : cn == 2u ? 1.0986f
-                                    : cn == 3u ? 1.9459f
-                                    : __builtin_fmaf((float)cn, kLn2, -0.0646f);
-                    lb = alo + glo;
-                }
-                const float bs = block_max(lb, red_boot);
+        if (!skip) {
+            // Threshold of the screen, in units of ln 2: (best known - slack) / ln 2 - 1, with
+            // the best known the exact score of the bootstrap candidate (an element's score,
+            // hence at most the draw's winning score) or the bound from the largest logit.
+            // Greedy rows keep the vectors whose largest logit reaches the chunk's.
+            float thr_s = -3.0e38f;
+            if (greedy) {
+                thr_s = xmax_blk;
+            } else if (screen) {
+                float bs = lb_x;
+                if (cbest.key != 0) bs = fmaxf(bs, exact_score<HLG>(cbest.x, cbest.w, rc));
+                bs = uniform(bs);
                 if (bs > -__builtin_inff())
                     thr_s = uniform((bs - screen_slack(bs)) * kInvLn2 - 1.0f);
             }
-
-            // Screen, one vector at a time: a vector can hold a winner only if
-            // U(max x of the vector) + (max code + 1) ln 2 >= best - slack; its elements are
-            // then tested one by one with their own code and U(x) before the exact score.
+            if constexpr (HLG) {
+                sa = uniform(-rc.mt * kInvLn2);
+                sb = uniform(__builtin_fmaf(rc.mtc, kInvLn2, thr_s));
+                sc = uniform(__builtin_fmaf(rc.mtw, kInvLn2, thr_s));
+            } else {
+                sa = uniform(-rc.invT * kInvLn2);
+                sb = thr_s;
+            }
+            // Screen: a vector can hold a winner only if U(its largest logit) + (n + 1) ln 2
+            // reaches best - slack, where n counts the leading ones of its largest word's high
+            // 16 bits (n = 16 leaves the word unbounded); for greedy rows, only if its largest
+            // logit reaches the chunk's. The champion slot's data and words are at hand from
+            // the bootstrap; the other slots that pass (rare) are read again two at a time, so
+            // their loads overlap.
+            uint32_t bits = 0;
 #pragma unroll
             for (int n = 0; n < NV; ++n) {
-                const int gv = lane_v + n * BS;
-                const uint32_t sv = s_vmax[lane_lds + n];
-                const float xm = __uint_as_float(sv & 0xFFFF0000u);
-                float Uv;
-                if constexpr (HLG) {
-                    Uv = fmaxf(__builtin_fmaf(xm, rc.mt, -rc.mtc), -rc.mtw);
+                const uint32_t d = s_vec[lane_lds + n];
+                const float xm = __uint_as_float(d << 16);
+                bool pass;
+                if (greedy) {
+                    pass = xm >= thr_s;
                 } else {
-                    Uv = xm * rc.invT;
+                    const uint32_t nl = lead_ones_hi16(d);
+                    pass = ((nl >= 16u) ? 64.0f : (float)nl) >= code_needed(xm);
                 }
-                // smallest code that can pass; code 15 stands for "15 or more"
-                const float tf = fminf(__builtin_fmaf(Uv, -kInvLn2, thr_s), 15.0f);
-                const float cmax = (float)(sv & 0xFFu);
-                if (gv < vend && cmax >= tf) {
-                    const uint32_t cw = s_codes[lane_lds + n];
-                    const uint32_t t = (uint32_t)fmaxf(ceilf(tf), 0.0f);
-                    uint32_t bits = codes_ge(cw, t);
-                    if constexpr (EPV == 4) bits &= 0x0303u;
-                    while (bits) {
-                        const uint32_t e = codes_bit_elem((uint32_t)__builtin_ctz(bits));
-                        bits &= bits - 1u;
-                        const float x = elem_dyn<DT>(raw[n], e);
-                        float U;
-                        if constexpr (HLG) {
-                            U = fmaxf(__builtin_fmaf(x, rc.mt, -rc.mtc), -rc.mtw);
-                        } else {
-                            U = x * rc.invT;
-                        }
-                        const uint32_t ce = (cw >> (4 * e)) & 15u;
-                        const float cf = (ce == 15u) ? 32.0f : (float)ce;
-                        if (x > -__builtin_inff() && cf >= __builtin_fmaf(U, -kInvLn2, thr_s)) {
-                            const uint32_t i = (uint32_t)gv * EPV + e;
-                            const Words4 q = stream_group_in_loop(sk, i >> 2);
-                            best = umax64(best, make_key(exact_score<HLG>(x, word_dyn(q, i & 3u), rc), i));
-                        }
-                    }
+                bits |= pass ? (1u << n) : 0u;
+            }
+            if (screen) {   // champ and cw0 belong to this draw
+                const uint32_t cbit = 1u << (champ & 31u);
+                if (bits & cbit) {
+                    bits &= ~cbit;
+                    best = score_words((int)(champ & 31u), craw0, cw0, best);
                 }
+            }
+            while (bits) {
+                const int n1 = __builtin_ctz(bits);
+                bits &= bits - 1u;
+                const bool two = bits != 0u;
+                const int n2 = two ? __builtin_ctz(bits) : n1;
+                if (two) bits &= bits - 1u;
+                const uint4 v1 = fetch(lane_v + n1 * BS);
+                const uint4 v2 = two ? fetch(lane_v + n2 * BS) : ninf4;
+                best = score_vec(sk, n1, v1, best);
+                if (two) best = score_vec(sk, n2, v2, best);
             }
         }
         // block reduction of the draw's key
-        const uint64_t kb = block_max_u64(best, red_draw);
+        const uint64_t kb = block_max_u64(best, red_draw[(k - k0) & 1]);
         if (tid == 0) {
             const int64_t o = b * a.K + k;
             if (a.nchunk == 1) {
@@ -642,7 +806,7 @@ static hipError_t launch_sample_nv(const SampleArgs &a, int nv, int bs, int grid
     case N:                                                                                \
         if (bs > MB) return hipErrorInvalidValue;                                          \
         hipLaunchKernelGGL((k_sample<DT, N, HLG, MB, AL>), dim3(grid), dim3(bs),          \
-                           (size_t)(N | 1) * bs * 4 * 2, s, a);                               \
+                           (size_t)(N | 1) * bs * 4, s, a);                               \
         break;
     switch (nv) {
         HS_CASE(1, 1024) HS_CASE(2, 1024) HS_CASE(4, 1024) HS_CASE(6, 1024) HS_CASE(8, 1024)
