@@ -306,13 +306,31 @@ __device__ __forceinline__ float rl_f32(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-    v = fmaxf(v, dpp_f32<kDppQuad1032>(v));
-    v = fmaxf(v, dpp_f32<kDppQuad2301>(v));
-    v = fmaxf(v, dpp_f32<kDppRowHalfMirror>(v));
-    v = fmaxf(v, dpp_f32<kDppRowMirror>(v));
-    return fmaxf(fmaxf(rl_f32(v, 0), rl_f32(v, 16)), fmaxf(rl_f32(v, 32), rl_f32(v, 48)));
+// Order-preserving map of non-NaN fp32 values onto unsigned integers, and its inverse: the
+// maximum of the images is the image of the maximum (-0 ranks just below +0).
+__device__ __forceinline__ uint32_t f2ord(float f) {
+    const uint32_t b = __float_as_uint(f);
+    return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
 }
+__device__ __forceinline__ float ord2f(uint32_t o) {
+    return __uint_as_float(o ^ ((uint32_t)((int32_t)~o >> 31) | 0x80000000u));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp_u32<kDppQuad1032>(v));
+    v = max(v, dpp_u32<kDppQuad2301>(v));
+    v = max(v, dpp_u32<kDppRowHalfMirror>(v));
+    v = max(v, dpp_u32<kDppRowMirror>(v));
+    const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+                           (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+    const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
+                           (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+    return max(a, b);
+}
+
+// Maximum over the wave of values that are never NaN (integer maxima of their order images:
+// one DPP-fused instruction per step).
+__device__ __forceinline__ float wave_max(float v) { return ord2f(wave_max_u32(f2ord(v))); }
 
 __device__ __forceinline__ float wave_sum(float v) {
     v += dpp_f32<kDppQuad1032>(v);

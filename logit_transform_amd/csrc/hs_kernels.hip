@@ -257,9 +257,9 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     };
 
     // Random words of slot n for draw stream sk: their maximum goes to the slot's LDS dword
-    // (high half) and into the lane's champion key, max word & ~31 | slot. Slots past the
-    // chunk are drawn too (their words are never used).
-    auto draw_vec = [&](const Stream &sk, int n, uint32_t champ) -> uint32_t {
+    // (high half); returns the slot's key for the lane's champion, max word & ~31 | slot. Slots
+    // past the chunk are drawn too (their words are never used).
+    auto draw_vec = [&](const Stream &sk, int n) -> uint32_t {
         uint32_t q = (uint32_t)(lane_v + n * BS) * NG;
         asm volatile("" : "+v"(q));
         uint32_t mw = 0;
@@ -270,10 +270,18 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             mw = max(mw, max(max(w.w[0], w.w[1]), max(w.w[2], w.w[3])));
         }
         s_vec16[2 * (lane_lds + n) + 1] = (uint16_t)(mw >> 16);
-        champ = max(champ, (mw & ~31u) | (uint32_t)n);
-        // one running maximum: otherwise the compiler regroups the chain of maxima and keeps
-        // every slot's word alive until the end of the pass
-        asm volatile("" : "+v"(champ));
+        return (mw & ~31u) | (uint32_t)n;
+    };
+    // The lane's champion key over a whole draw (draws without the logits at hand).
+    auto draw_all = [&](const Stream &sk) -> uint32_t {
+        uint32_t champ = 0;
+#pragma unroll
+        for (int n = 0; n < NV; ++n) {
+            champ = max(champ, draw_vec(sk, n));
+            // one running maximum: otherwise the compiler regroups the chain of maxima and
+            // keeps every slot's word alive until the end of the pass
+            asm volatile("" : "+v"(champ));
+        }
         return champ;
     };
 
@@ -351,21 +359,12 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
         c.key = ok ? make_key(__builtin_fmaf(c.x, lin, -nlv * kLn2), (uint32_t)tid) : 0ull;
         return c;
     };
-    // The champion slot's vector, read with a branch-free (clamped) address on the aligned path.
-    auto issue_slot_load = [&](int n) -> uint4 {
-        if constexpr (ALIGNED) {
-            const int gv = min(lane_v + n * BS, gclamp);
-            return *reinterpret_cast<const uint4 *>(rowp + (size_t)gv * 16);
-        } else {
-            return fetch(lane_v + n * BS);
-        }
-    };
 
     // ---- one pass over the chunk: the first draw's random words (which need no logit) run
     // LAG slots ahead of the logits, so the first loads land while they are computed; D loads
-    // stay in flight. Once the last slot is drawn the lane's champion vector is known: it is
-    // read again and its words drawn again while the last slots' logits are processed. The
-    // pass is the same for every row (greedy and invalid rows draw words they never use):
+    // stay in flight. The lane's champion vector (largest word so far) is kept in registers as
+    // the logits come in, and its words are drawn again after the pass. The pass is the same
+    // for every row (greedy and invalid rows draw words they never use):
     // without row-dependent branches the scheduler interleaves the integer Philox chains with
     // the float work freely. ----
     uint32_t champ0 = 0;
@@ -375,26 +374,26 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     {
         const Stream sk = stream_k(k0);
         uint4 buf[D];
+        uint32_t ring[LAG + 1];   // slot keys between a slot's draw and its logits
 #pragma unroll
         for (int n = 0; n < D; ++n) buf[n] = issue_load(n);
 #pragma unroll
         for (int n = 0; n < NV + LAG; ++n) {
-            if (n < NV) champ0 = draw_vec(sk, n, champ0);
-            if (n == NV) craw0 = issue_slot_load((int)(champ0 & 31u));
-            if (n == NV + LAG / 2) cand0 = candidate(sk, champ0, craw0, cw0);
+            if (n < NV) ring[n % (LAG + 1)] = draw_vec(sk, n);
             const int j = n - LAG;
             if (j >= 0 && j < NV) {
-                data_vec(j, patch(j, buf[j % D]));
+                const uint4 v = patch(j, buf[j % D]);
+                data_vec(j, v);
+                // the champion's vector stays in registers (no second read)
+                const uint32_t kj = ring[j % (LAG + 1)];
+                if (kj > champ0) {
+                    champ0 = kj;
+                    craw0 = v;
+                }
                 if (j + D < NV) buf[j % D] = issue_load(j + D);
             }
         }
-        if (NV + LAG <= NV) craw0 = issue_slot_load((int)(champ0 & 31u));
-        if (NV + LAG <= NV + LAG / 2) cand0 = candidate(sk, champ0, craw0, cw0);
-        // a champion vector past the whole vectors of the chunk: its true data, again
-        if (ALIGNED && lane_v + (int)(champ0 & 31u) * BS >= vlim) {
-            craw0 = fetch(lane_v + (int)(champ0 & 31u) * BS);
-            cand0 = candidate(sk, champ0, craw0, cw0);
-        }
+        cand0 = candidate(sk, champ0, craw0, cw0);
     }
     if constexpr (HLG) {
         // A lane whose largest logit lies more than 100 binary orders above or below its
@@ -550,9 +549,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
         uint32_t champ = champ0;
         if (k > k0 && !skip && screen) {
             // this draw's words, champions and bootstrap candidate (one more barrier)
-            champ = 0;
-#pragma unroll
-            for (int n = 0; n < NV; ++n) champ = draw_vec(sk, n, champ);
+            champ = draw_all(sk);
             craw0 = fetch(lane_v + (int)(champ & 31u) * BS);
             const Cand cd = candidate(sk, champ, craw0, cw0);
             int lane = threadIdx.x & 63;
@@ -598,19 +595,23 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             // logit reaches the chunk's. The champion slot's data and words are at hand from
             // the bootstrap; the other slots that pass (rare) are read again two at a time, so
             // their loads overlap.
-            uint32_t bits = 0;
+            uint32_t bits = 0;   // bit n: slot n passes
+            if (greedy) {
 #pragma unroll
-            for (int n = 0; n < NV; ++n) {
-                const uint32_t d = s_vec[lane_lds + n];
-                const float xm = __uint_as_float(d << 16);
-                bool pass;
-                if (greedy) {
-                    pass = xm >= thr_s;
-                } else {
-                    const uint32_t nl = lead_ones_hi16(d);
-                    pass = ((nl >= 16u) ? 64.0f : (float)nl) >= code_needed(xm);
+                for (int n = NV - 1; n >= 0; --n) {
+                    const float xm = __uint_as_float(s_vec[lane_lds + n] << 16);
+                    bits = (bits << 1) | (xm >= thr_s ? 1u : 0u);
                 }
-                bits |= pass ? (1u << n) : 0u;
+            } else {
+#pragma unroll
+                for (int n = NV - 1; n >= 0; --n) {
+                    const uint32_t d = s_vec[lane_lds + n];
+                    const float xm = __uint_as_float(d << 16);
+                    // a needed code above 16 is met only by n = 16, which stands for any word
+                    // (so the cap keeps such vectors)
+                    const float need = fminf(code_needed(xm), 16.0f);
+                    bits = (bits << 1) | ((float)lead_ones_hi16(d) >= need ? 1u : 0u);
+                }
             }
             if (screen) {   // champ and cw0 belong to this draw
                 const uint32_t cbit = 1u << (champ & 31u);
