@@ -139,6 +139,10 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     // hit distinct banks), so every access is one base register plus an immediate offset.
     extern __shared__ uint32_t s_vec[];
     __shared__ float red_m[16], red_s[16], red_x[16];
+    __shared__ uint64_t red_ck[16];    // per wave: best bootstrap candidate key
+    __shared__ float red_cx[16];       //   its logit
+    __shared__ uint32_t red_cw[16];    //   and word
+    __shared__ float row_bc[8];        // row constants from wave 0
     // two buffers, alternating between draws: without a bootstrap (greedy rows, no screening)
     // nothing else separates one draw's reads of the buffer from the next draw's writes
     __shared__ uint64_t red_draw[2][16];
@@ -222,7 +226,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     auto issue_load = [&](int n) -> uint4 {
         if constexpr (ALIGNED) {
             const int gv = min(lane_v + n * BS, gclamp);
-            return *reinterpret_cast<const uint4 *>(rowp + (size_t)gv * 16);
+            return *reinterpret_cast<const uint4 *>(rowp + (uint32_t)gv * 16u);
         } else {
             return fetch(lane_v + n * BS);
         }
@@ -262,12 +266,16 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     auto draw_vec = [&](const Stream &sk, int n) -> uint32_t {
         uint32_t q = (uint32_t)(lane_v + n * BS) * NG;
         asm volatile("" : "+v"(q));
-        uint32_t mw = 0;
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            const Words4 w = philox4x32_10_uk(q + g, sk.row, sk.off_lo, sk.off_hi, sk.key0,
-                                              sk.key1);
-            mw = max(mw, max(max(w.w[0], w.w[1]), max(w.w[2], w.w[3])));
+        uint32_t mw;
+        {
+            const Words4 w = philox4x32_10_uk(q, sk.row, sk.off_lo, sk.off_hi, sk.key0, sk.key1);
+            mw = max(max3u(w.w[0], w.w[1], w.w[2]), w.w[3]);
+            if constexpr (NG == 2) {
+                const Words4 u = philox4x32_10_uk(q + 1, sk.row, sk.off_lo, sk.off_hi, sk.key0,
+                                                  sk.key1);
+                mw = max3u(max3u(w.w[0], w.w[1], w.w[2]), max3u(w.w[3], u.w[0], u.w[1]),
+                           max(u.w[2], u.w[3]));
+            }
         }
         s_vec16[2 * (lane_lds + n) + 1] = (uint16_t)(mw >> 16);
         return (mw & ~31u) | (uint32_t)n;
@@ -295,10 +303,9 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     float xmax_lane = -__builtin_inff();
     float lse_r = 0.0f, lse_s = 0.0f;
     auto data_vec = [&](int n, uint4 v) {
-        // Tie this vector to the running sums: otherwise the scheduler issues the exponentials
-        // of many vectors first and holds all their results at once.
-        asm volatile("" : "+v"(lse_s), "+v"(xmax_lane), "+v"(v.x), "+v"(v.y), "+v"(v.z),
-                     "+v"(v.w));
+        // Keep the slots in order: otherwise the scheduler issues the exponentials of many
+        // vectors first and holds all their results at once.
+        asm volatile("" : "+v"(lse_s), "+v"(xmax_lane));
         float xv[EPV];
 #pragma unroll
         for (int e = 0; e < EPV; ++e) xv[e] = elem<DT>(v, e);
@@ -369,8 +376,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     // the float work freely. ----
     uint32_t champ0 = 0;
     uint4 craw0 = ninf4;
-    uint32_t cw0[EPV];
-    Cand cand0{0ull, -__builtin_inff(), 0u};
+    uint32_t cw0[EPV];   // the champion vector's words
     {
         const Stream sk = stream_k(k0);
         uint4 buf[D];
@@ -393,7 +399,6 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                 if (j + D < NV) buf[j % D] = issue_load(j + D);
             }
         }
-        cand0 = candidate(sk, champ0, craw0, cw0);
     }
     if constexpr (HLG) {
         // A lane whose largest logit lies more than 100 binary orders above or below its
@@ -410,38 +415,59 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             }
         }
     }
-    // Wave maximum of the candidates' keys; the owning lane leaves its logit and word in LDS
-    // beside the key (slot wid), for the block maximum after the next barrier.
-    auto cand_to_lds = [&](const Cand &c, int lane, int wid, uint64_t *rk, float *rx,
-                           uint32_t *rw) {
-        const uint64_t wk = wave_max_u64(c.key);
-        if (lane == 0) rk[wid] = wk;
-        if (wk != 0 && c.key == wk) {
-            rx[wid] = c.x;
-            rw[wid] = c.w;
-        }
-    };
-    __shared__ uint64_t red_ck[16];
-    __shared__ float red_cx[16];
-    __shared__ uint32_t red_cw[16];
 
-    // ---- block combine, one barrier: log-sum-exp (curve on), the largest logit, and the first
-    // draw's bootstrap candidate ----
+    // ---- block combine: log-sum-exp (curve on), the largest logit, and the first draw's
+    // bootstrap candidate; wave 0 turns them into the row's constants, which reach every wave
+    // through LDS ----
     RowConst rc;
     rc.invT = invT;
     rc.c = 0.0f;
     rc.mt = rc.mtc = rc.mtw = 0.0f;
     rc.curve = a.curve;
-    bool skip = bad;
-    float xmax_blk;
-    Cand cbest{0ull, -__builtin_inff(), 0u};
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    int wid = threadIdx.x >> 6;
+    asm volatile("" : "+v"(wid));
+    const int nw = (BS + 63) >> 6;
+    // Per wave, the best bootstrap candidate: its key, logit and word.
+    auto post_candidate = [&](const Cand &c) {
+        const uint64_t wk = wave_max_u64(c.key);
+        if (lane == 0) red_ck[wid] = wk;
+        if (wk != 0 && c.key == wk) {
+            red_cx[wid] = c.x;
+            red_cw[wid] = c.w;
+        }
+    };
+    // (wave 0) Exact score of the block's best candidate.
+    auto candidate_score = [&]() -> float {
+        const uint64_t bk = wave_max_u64(lane < nw ? red_ck[lane] : 0ull);
+        if (bk == 0) return -__builtin_inff();
+        const int bw = (int)((0xFFFFFFFFu - (uint32_t)bk) >> 6);
+        return exact_score<HLG>(uniform(red_cx[bw]),
+                                (uint32_t)__builtin_amdgcn_readfirstlane(red_cw[bw]), rc);
+    };
+    // (wave 0) The screen's constants from a lower bound bs on the draw's winning score:
+    // threshold thr_s = (bs - slack) / ln 2 - 1 in units of ln 2, and sa, sb, sc with which
+    // min(x sa + sb, sc) is the smallest word code n (leading ones) that lets a value of
+    // largest logit x reach it: (thr_s ln 2 - U(x)) / ln 2 with U(x) = (m/T) max(x - c, -w)
+    // (curve on) or x/T. No bound (no screening): every vector passes.
+    auto screen_consts = [&](float bs, float *o) {
+        float thr = -3.0e38f;
+        if (bs > -__builtin_inff()) thr = (bs - screen_slack(bs)) * kInvLn2 - 1.0f;
+        o[0] = thr;
+        if constexpr (HLG) {
+            o[1] = -rc.mt * kInvLn2;
+            o[2] = __builtin_fmaf(rc.mtc, kInvLn2, thr);
+            o[3] = __builtin_fmaf(rc.mtw, kInvLn2, thr);
+        } else {
+            o[1] = -rc.invT * kInvLn2;
+            o[2] = thr;
+            o[3] = __builtin_inff();
+        }
+    };
+
+    if (screen) post_candidate(candidate(stream_k(k0), champ0, craw0, cw0));
     {
-        int lane = threadIdx.x & 63;
-        asm volatile("" : "+v"(lane));
-        int wid = threadIdx.x >> 6;
-        asm volatile("" : "+v"(wid));
-        const int nw = (BS + 63) >> 6;
-        if (screen) cand_to_lds(cand0, lane, wid, red_ck, red_cx, red_cw);
         const float xw = wave_max(xmax_lane);
         float mw = 0.0f, sw = 0.0f;
         if constexpr (HLG) {
@@ -455,17 +481,12 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                 red_s[wid] = sw;
             }
         }
-        __syncthreads();
-        xmax_blk = uniform(wave_max(lane < nw ? red_x[lane] : -__builtin_inff()));
-        if (screen) {
-            const uint64_t bk = wave_max_u64(lane < nw ? red_ck[lane] : 0ull);
-            if (bk != 0) {
-                const int bw = (int)(0xFFFFFFFFu - (uint32_t)bk) >> 6;
-                cbest.key = bk;
-                cbest.x = red_cx[bw];
-                cbest.w = red_cw[bw];
-            }
-        }
+    }
+    __syncthreads();
+    if (wid == 0) {
+        const float xmb = wave_max(lane < nw ? red_x[lane] : -__builtin_inff());
+        float c = 0.0f;
+        bool ok = xmb > -__builtin_inff();   // the chunk has a finite logit
         if constexpr (HLG) {
             float lse;
             if (a.nchunk == 1) {
@@ -485,33 +506,55 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                 lse = (Mb > -__builtin_inff()) ? Mb + logf(Sb) : -__builtin_inff();
             }
             lse = uniform(lse);
-            if (!(lse > -__builtin_inff())) skip = true;   // no finite logit in the row
-            rc.c = uniform(lse + mu);
+            ok = lse > -__builtin_inff();   // the row has a finite logit
+            c = uniform(lse + mu);
+            rc.c = c;
             rc.mt = uniform(a.curve.m * rc.invT);
             rc.mtc = uniform(rc.mt * rc.c);
             rc.mtw = uniform(rc.mt * a.curve.w);
         }
-    }
-    // A lower bound on any draw's winning score from the chunk's largest logit: its curve value
-    // is at least (m/T) min(x - c, w) (the toe lies above its mid line, the shoulder above m w)
-    // and every Gumbel value is at least G(0) > -3.14.
-    float lb_x = -__builtin_inff();
-    if (xmax_blk > -__builtin_inff()) {
-        if constexpr (HLG) {
-            lb_x = uniform(fminf(xmax_blk - rc.c, rc.curve.w) * rc.mt - 3.14f);
-        } else {
-            lb_x = uniform(xmax_blk * rc.invT - 3.14f);
+        float o[4] = {xmb, 0.0f, 0.0f, __builtin_inff()};
+        if (ok && screen) {
+            // lower bounds on the first draw's winning score: the best candidate's exact
+            // score, and from the chunk's largest logit (its curve value is at least
+            // (m/T) min(x - c, w) -- the toe lies above its mid line, the shoulder above m w --
+            // and every Gumbel value is at least G(0) > -3.14)
+            float lbx;
+            if constexpr (HLG) {
+                lbx = fminf(xmb - rc.c, rc.curve.w) * rc.mt - 3.14f;
+            } else {
+                lbx = xmb * rc.invT - 3.14f;
+            }
+            screen_consts(uniform(fmaxf(candidate_score(), lbx)), o);
+        } else if (ok && sampled) {
+            screen_consts(-__builtin_inff(), o);
+        }
+        if (lane == 0) {
+            row_bc[0] = xmb;
+            row_bc[1] = c;
+            row_bc[2] = ok ? 1.0f : 0.0f;
+            row_bc[3] = o[0];
+            row_bc[4] = o[1];
+            row_bc[5] = o[2];
+            row_bc[6] = o[3];
         }
     }
-    // Smallest word code n (leading ones) with which a value of largest logit x can reach the
-    // screen threshold thr_s: (thr_s ln 2 - U(x)) / ln 2 with U(x) = (m/T) max(x - c, -w)
-    // (curve on) or x/T, as min(x sa + sb, sc). Set once the threshold is known.
-    float sa = 0.0f, sb = 0.0f, sc = __builtin_inff();
+    __syncthreads();
+    const float xmax_blk = uniform(row_bc[0]);
+    const bool skip = bad || !(uniform(row_bc[2]) > 0.0f);
+    if constexpr (HLG) {
+        rc.c = uniform(row_bc[1]);
+        rc.mt = uniform(a.curve.m * rc.invT);
+        rc.mtc = uniform(rc.mt * rc.c);
+        rc.mtw = uniform(rc.mt * a.curve.w);
+    }
+    float thr_s = uniform(row_bc[3]);
+    float sa = uniform(row_bc[4]), sb = uniform(row_bc[5]), sc = uniform(row_bc[6]);
     auto code_needed = [&](float x) -> float {
         return fminf(__builtin_fmaf(x, sa, sb), sc);
     };
     // Exact scores of the elements of slot n (vector v, words w) that pass their own bound,
-    // folded into the draw's best key; greedy rows compare logits.
+    // folded into the draw's best key.
     auto score_words = [&](int n, const uint4 &v, const uint32_t (&w)[EPV],
                            uint64_t best) -> uint64_t {
         const int gv = lane_v + n * BS;
@@ -526,6 +569,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
         }
         return best;
     };
+    // The same for a vector read again: its words are drawn again; greedy rows compare logits.
     auto score_vec = [&](const Stream &sk, int n, const uint4 &v, uint64_t best) -> uint64_t {
         const int gv = lane_v + n * BS;
         if (greedy) return greedy_vec<DT>(v, (uint32_t)gv * EPV, best);
@@ -548,59 +592,47 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
         const Stream sk = stream_k(k);
         uint32_t champ = champ0;
         if (k > k0 && !skip && screen) {
-            // this draw's words, champions and bootstrap candidate (one more barrier)
+            // this draw's words, champions and bootstrap candidate (two more barriers)
             champ = draw_all(sk);
             craw0 = fetch(lane_v + (int)(champ & 31u) * BS);
-            const Cand cd = candidate(sk, champ, craw0, cw0);
-            int lane = threadIdx.x & 63;
-            int wid = threadIdx.x >> 6;
-            const int nw = (BS + 63) >> 6;
-            cand_to_lds(cd, lane, wid, red_ck, red_cx, red_cw);
+            post_candidate(candidate(sk, champ, craw0, cw0));
             __syncthreads();
-            const uint64_t bk = wave_max_u64(lane < nw ? red_ck[lane] : 0ull);
-            cbest.key = bk;
-            if (bk != 0) {
-                const int bw = (int)(0xFFFFFFFFu - (uint32_t)bk) >> 6;
-                cbest.x = red_cx[bw];
-                cbest.w = red_cw[bw];
+            if (wid == 0) {
+                float lbx;
+                if constexpr (HLG) {
+                    lbx = fminf(xmax_blk - rc.c, rc.curve.w) * rc.mt - 3.14f;
+                } else {
+                    lbx = xmax_blk * rc.invT - 3.14f;
+                }
+                float o[4];
+                screen_consts(uniform(fmaxf(candidate_score(), lbx)), o);
+                if (lane == 0) {
+                    row_bc[3] = o[0];
+                    row_bc[4] = o[1];
+                    row_bc[5] = o[2];
+                    row_bc[6] = o[3];
+                }
             }
+            __syncthreads();
+            thr_s = uniform(row_bc[3]);
+            sa = uniform(row_bc[4]);
+            sb = uniform(row_bc[5]);
+            sc = uniform(row_bc[6]);
         }
         uint64_t best = 0;
         if (!skip) {
-            // Threshold of the screen, in units of ln 2: (best known - slack) / ln 2 - 1, with
-            // the best known the exact score of the bootstrap candidate (an element's score,
-            // hence at most the draw's winning score) or the bound from the largest logit.
-            // Greedy rows keep the vectors whose largest logit reaches the chunk's.
-            float thr_s = -3.0e38f;
-            if (greedy) {
-                thr_s = xmax_blk;
-            } else if (screen) {
-                float bs = lb_x;
-                if (cbest.key != 0) bs = fmaxf(bs, exact_score<HLG>(cbest.x, cbest.w, rc));
-                bs = uniform(bs);
-                if (bs > -__builtin_inff())
-                    thr_s = uniform((bs - screen_slack(bs)) * kInvLn2 - 1.0f);
-            }
-            if constexpr (HLG) {
-                sa = uniform(-rc.mt * kInvLn2);
-                sb = uniform(__builtin_fmaf(rc.mtc, kInvLn2, thr_s));
-                sc = uniform(__builtin_fmaf(rc.mtw, kInvLn2, thr_s));
-            } else {
-                sa = uniform(-rc.invT * kInvLn2);
-                sb = thr_s;
-            }
             // Screen: a vector can hold a winner only if U(its largest logit) + (n + 1) ln 2
-            // reaches best - slack, where n counts the leading ones of its largest word's high
-            // 16 bits (n = 16 leaves the word unbounded); for greedy rows, only if its largest
-            // logit reaches the chunk's. The champion slot's data and words are at hand from
-            // the bootstrap; the other slots that pass (rare) are read again two at a time, so
-            // their loads overlap.
+            // reaches the bound less the slack, where n counts the leading ones of its largest
+            // word's high 16 bits (n = 16 leaves the word unbounded); for greedy rows, only if
+            // its largest logit reaches the chunk's. The champion vector and its words are at
+            // hand from the bootstrap; the other vectors that pass (rare) are read again two at a
+            // time, so their loads overlap.
             uint32_t bits = 0;   // bit n: slot n passes
             if (greedy) {
 #pragma unroll
                 for (int n = NV - 1; n >= 0; --n) {
                     const float xm = __uint_as_float(s_vec[lane_lds + n] << 16);
-                    bits = (bits << 1) | (xm >= thr_s ? 1u : 0u);
+                    bits = (bits << 1) | (xm >= xmax_blk ? 1u : 0u);
                 }
             } else {
 #pragma unroll
@@ -613,7 +645,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                     bits = (bits << 1) | ((float)lead_ones_hi16(d) >= need ? 1u : 0u);
                 }
             }
-            if (screen) {   // champ and cw0 belong to this draw
+            if (screen) {   // champ and craw0 belong to this draw
                 const uint32_t cbit = 1u << (champ & 31u);
                 if (bits & cbit) {
                     bits &= ~cbit;
@@ -632,16 +664,24 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                 if (two) best = score_vec(sk, n2, v2, best);
             }
         }
-        // block reduction of the draw's key
-        const uint64_t kb = block_max_u64(best, red_draw[(k - k0) & 1]);
-        if (tid == 0) {
-            const int64_t o = b * a.K + k;
-            if (a.nchunk == 1) {
-                a.out[o] = bad ? -2 : key_index(kb);
-                if (a.best_out) a.best_out[o] = bad ? -__builtin_inff() : key_score(kb);
-            } else if (kb != 0) {
-                atomicMax(reinterpret_cast<unsigned long long *>(a.keys + o),
-                          (unsigned long long)kb);
+        // block maximum of the draw's key: waves post their maxima, wave 0 writes the result
+        {
+            uint64_t *rd = red_draw[(k - k0) & 1];
+            const uint64_t wk = wave_max_u64(best);
+            if (lane == 0) rd[wid] = wk;
+            __syncthreads();
+            if (wid == 0) {
+                const uint64_t kb = wave_max_u64(lane < nw ? rd[lane] : 0ull);
+                if (lane == 0) {
+                    const int64_t o = b * a.K + k;
+                    if (a.nchunk == 1) {
+                        a.out[o] = bad ? -2 : key_index(kb);
+                        if (a.best_out) a.best_out[o] = bad ? -__builtin_inff() : key_score(kb);
+                    } else if (kb != 0) {
+                        atomicMax(reinterpret_cast<unsigned long long *>(a.keys + o),
+                                  (unsigned long long)kb);
+                    }
+                }
             }
         }
     }
