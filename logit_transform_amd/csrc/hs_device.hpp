@@ -77,9 +77,7 @@ __device__ __forceinline__ Words4 philox4x32_10(uint32_t c0, uint32_t c1, uint32
 // does the same work in one. The first two rounds keep plain code: there one operand of each
 // xor is itself uniform and folds into the scalar unit.
 __device__ __forceinline__ uint32_t xor3_sk(uint32_t a, uint32_t b, uint32_t k) {
-    uint32_t r;
-    asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
-    return r;
+    return __builtin_amdgcn_bitop3_b32(a, b, k, 0x96);
 }
 
 __device__ __forceinline__ Words4 philox4x32_10_uk(uint32_t c0, uint32_t c1, uint32_t c2,
@@ -167,13 +165,10 @@ __device__ __forceinline__ float gumbel32(uint32_t r) {
 }
 
 // Leading ones of the high 16 bits of d, 0..16, in two instructions: gfx950's v_bitop3_b32 forms
-// ~d | 0xFFFF (truth table 0xCF = ~S0 | S1, the mask in a scalar register) and v_ffbh_u32
-// counts its leading zeros; the low 16 bits, all set, cap the count at 16.
+// ~d | 0xFFFF (truth table 0xCF = ~S0 | S1) and v_ffbh_u32 counts its leading zeros; the low
+// 16 bits, all set, cap the count at 16 (so the operand is never zero).
 __device__ __forceinline__ uint32_t lead_ones_hi16(uint32_t d) {
-    uint32_t t, n;
-    asm("v_bitop3_b32 %0, %1, %2, %2 bitop3:0xcf" : "=v"(t) : "v"(d), "s"(0xFFFFu));
-    asm("v_ffbh_u32 %0, %1" : "=v"(n) : "v"(t));
-    return n;
+    return __builtin_clz(__builtin_amdgcn_bitop3_b32(d, 0xFFFFu, 0xFFFFu, 0xCF));
 }
 
 // Maxima of fp32 values that are never NaN (finite logits or -inf): the hardware max
