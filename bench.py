@@ -67,8 +67,8 @@ def load_traffic(name: str):
 
 def cpu_baseline(w, budget_s: float = 10.0):
     """The oracle as it stands, all host cores, on the workload's rows: a first timed pass sizes
-    the sample (whole passes over the rows, repeated until about budget_s of work), then the
-    sample is timed. Rows per second of the whole sample are reported."""
+    the sample (the first rows, or whole passes over all rows repeated until about budget_s of
+    work), then the sample is timed. Rows per second of the whole sample are reported."""
     from oracle import oracle as O
     cores = len(os.sched_getaffinity(0))
     os.environ.setdefault("OMP_NUM_THREADS", str(cores))
@@ -80,15 +80,19 @@ def cpu_baseline(w, budget_s: float = 10.0):
         O.sample(w.logits[:rows], w.T[:rows], w.seed[:rows], w.offset[:rows], K=w.K,
                  mu=None if w.hlg is None else w.mu[:rows], hlg=w.hlg)
 
+    run(n)   # first call: library and thread-pool start-up, untimed
     t0 = time.perf_counter()
     run(n)
     per_row = (time.perf_counter() - t0) / n
     rows = int(min(w.B, max(n, budget_s / max(per_row, 1e-9))))
-    reps = max(1, int(budget_s / max(per_row * rows, 1e-9)))
+    reps = 0
     t0 = time.perf_counter()
-    for _ in range(reps):
+    while True:
         run(rows)
-    t1 = time.perf_counter()
+        reps += 1
+        t1 = time.perf_counter()
+        if t1 - t0 >= budget_s:
+            break
     return {"value": reps * rows / (t1 - t0), "unit": "rows/s", "cores": threads,
             "kind": "oracle",
             "sample": "first %d of %d rows of the same workload (%d draw(s) each), %d pass(es), "

@@ -162,3 +162,38 @@ def test_workspace_left_clean(hs):
     assert int(ws[:n_keys].to(torch.int32).abs().sum()) == 0
     for o in outs[1:]:
         np.testing.assert_array_equal(o, outs[0])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("hlg", [None, HLG_A])
+def test_wide_range_rows(hs, oracle_mod, dtype, hlg):
+    """Logits spanning hundreds of nats inside each lane's share of a row. The one-block kernel
+    streams the log-sum-exp per lane against the lane's first vector maximum; lanes whose
+    largest logit lies far from it sum again against that maximum, and the screen's bounds
+    must hold at any scale. One block per row (forced) and the automatic split plan."""
+    B, V = 4, 65536
+    epv = 4 if dtype == torch.float32 else 8
+    rng = np.random.default_rng(91)
+    x = rng.normal(0, 2, size=(B, V)).astype(np.float32)
+    first = 1024 * epv                    # the first vector of every lane (blocks of 1024)
+    x[0, :first] -= 300.0                 # first vectors far below the rest
+    x[1, :first] += 300.0                 # first vectors far above the rest
+    x[2, 5 * first:] += 250.0             # later vectors far above the first ones
+    x[3] *= 60.0                          # wide spread everywhere
+    t = torch.from_numpy(x).to(dtype)
+    T = rng.uniform(0.5, 1.5, size=B).astype(np.float32)
+    seed = rng.integers(0, 2**64, size=B, dtype=np.uint64)
+    off = rng.integers(0, 2**32, size=B, dtype=np.uint64)
+    mu = W.mean_finite_logprob(t) if hlg is not None else None
+    w = W.Workload("wide range", t, T, seed, off, K=4, hlg=hlg, mu=mu)
+    d = on_device(w)
+    o, s1, s2 = oracle_sample(oracle_mod, w)
+    x64 = t.double().numpy()
+    for name, opts in [("one-block", hs.SampleOpts(variant=1)), ("auto", None)]:
+        idx = hs.sample_ex(d["logits"], d["T"], d["seed"], d["offset"], mu=d.get("mu"),
+                           hlg=hlg, k=4, opts=opts).cpu().numpy()
+        assert_parity(idx, o, s1, s2, x64, "wide range %s %s" % (name, dtype))
+    if hlg is not None:
+        lse = hs.logsumexp(d["logits"]).cpu().numpy().astype(np.float64)
+        ref = np.array([np.logaddexp.reduce(x64[b]) for b in range(B)])
+        np.testing.assert_allclose(lse, ref, rtol=2e-6, atol=0)
