@@ -142,7 +142,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     __shared__ uint64_t red_ck[16];    // per wave: best bootstrap candidate key
     __shared__ float red_cx[16];       //   its logit
     __shared__ uint32_t red_cw[16];    //   and word
-    __shared__ float row_bc[8];        // row constants from wave 0
+    __shared__ float row_bc[12];       // row constants from wave 0
     // two buffers, alternating between draws: without a bootstrap (greedy rows, no screening)
     // nothing else separates one draw's reads of the buffer from the next draw's writes
     __shared__ uint64_t red_draw[2][16];
@@ -447,11 +447,16 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                                 (uint32_t)__builtin_amdgcn_readfirstlane(red_cw[bw]), rc);
     };
     // (wave 0) The screen's constants from a lower bound bs on the draw's winning score:
-    // threshold thr_s = (bs - slack) / ln 2 - 1 in units of ln 2, and sa, sb, sc with which
-    // min(x sa + sb, sc) is the smallest word code n (leading ones) that lets a value of
-    // largest logit x reach it: (thr_s ln 2 - U(x)) / ln 2 with U(x) = (m/T) max(x - c, -w)
-    // (curve on) or x/T. No bound (no screening): every vector passes.
-    auto screen_consts = [&](float bs, float *o) {
+    // threshold thr = (bs - slack) / ln 2 - 1 in units of ln 2, and the coefficients with which
+    //   need(x) = min(max(x sa + sb, x ta + tb), sc)
+    // is the smallest word code n (leading ones) that lets a logit x reach it:
+    // thr - U(x) / ln 2, U(x) an upper bound on l'(x)/T. With the curve on,
+    //   U(x) = max(min(mid(x), tan(x)), -(m/T) w),
+    // where mid(x) = (m/T)(x - c) is the mid line (above the shoulder), tan the tangent of the
+    // concave shoulder at the chunk's largest logit (above the shoulder, and above the mid line
+    // left of the knot), and -(m/T) w the top of the toe; without the curve U(x) = x/T.
+    // No bound (no screening): every vector passes.
+    auto screen_consts = [&](float bs, float xtop, float *o) {
         float thr = -3.0e38f;
         if (bs > -__builtin_inff()) thr = (bs - screen_slack(bs)) * kInvLn2 - 1.0f;
         o[0] = thr;
@@ -459,10 +464,23 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             o[1] = -rc.mt * kInvLn2;
             o[2] = __builtin_fmaf(rc.mtc, kInvLn2, thr);
             o[3] = __builtin_fmaf(rc.mtw, kInvLn2, thr);
+            o[4] = o[1];
+            o[5] = o[2];
+            const float z0 = xtop - rc.c;
+            if (z0 > rc.curve.w && rc.curve.w < __builtin_inff()) {
+                const float d = z0 - rc.curve.w;
+                const float g0 = rc.curve.mw + rc.curve.mbh * log1p_acc(d * rc.curve.ibh);
+                const float s0 = rc.curve.mbh / (1.0f / rc.curve.ibh + d);   // m b / (b + d)
+                // tan(x) = (s0 x + g0 - s0 (z0 + c)) / T
+                o[4] = -s0 * rc.invT * kInvLn2;
+                o[5] = __builtin_fmaf(__builtin_fmaf(-s0, xtop, g0) * rc.invT, -kInvLn2, thr);
+            }
         } else {
             o[1] = -rc.invT * kInvLn2;
             o[2] = thr;
             o[3] = __builtin_inff();
+            o[4] = o[1];
+            o[5] = o[2];
         }
     };
 
@@ -495,14 +513,14 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                 const float sb = wave_sum(lane < nw ? red_s[lane] * __builtin_amdgcn_exp2f(pm - mb) : 0.0f);
                 lse = (sb > 0.0f) ? (mb + __builtin_amdgcn_logf(sb)) * kLn2 : -__builtin_inff();
             } else {
-                const float2 *part = a.partials + b * a.part_stride;
-                float Mb = -__builtin_inff();
-                for (int j = 0; j < a.nchunk; ++j) Mb = fmaxf(Mb, part[j].x);
-                float Sb = 0.0f;
-                if (Mb > -__builtin_inff())
-                    for (int j = 0; j < a.nchunk; ++j)
-                        if (part[j].x > -__builtin_inff())
-                            Sb += part[j].y * __builtin_amdgcn_exp2f((part[j].x - Mb) * kLog2e);
+                // the chunks' (max, sum) pairs of the pre-pass, one per lane (nchunk <= 64),
+                // all read at once
+                const float2 pj = lane < a.nchunk ? a.partials[b * a.part_stride + lane]
+                                                  : make_float2(-__builtin_inff(), 0.0f);
+                const float Mb = wave_max(pj.x);
+                const float Sb = wave_sum(pj.x > -__builtin_inff()
+                                              ? pj.y * __builtin_amdgcn_exp2f((pj.x - Mb) * kLog2e)
+                                              : 0.0f);
                 lse = (Mb > -__builtin_inff()) ? Mb + logf(Sb) : -__builtin_inff();
             }
             lse = uniform(lse);
@@ -513,7 +531,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             rc.mtc = uniform(rc.mt * rc.c);
             rc.mtw = uniform(rc.mt * a.curve.w);
         }
-        float o[4] = {xmb, 0.0f, 0.0f, __builtin_inff()};
+        float o[6] = {xmb, 0.0f, 0.0f, __builtin_inff(), 0.0f, 0.0f};
         if (ok && screen) {
             // lower bounds on the first draw's winning score: the best candidate's exact
             // score, and from the chunk's largest logit (its curve value is at least
@@ -525,9 +543,9 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             } else {
                 lbx = xmb * rc.invT - 3.14f;
             }
-            screen_consts(uniform(fmaxf(candidate_score(), lbx)), o);
+            screen_consts(uniform(fmaxf(candidate_score(), lbx)), xmb, o);
         } else if (ok && sampled) {
-            screen_consts(-__builtin_inff(), o);
+            screen_consts(-__builtin_inff(), xmb, o);
         }
         if (lane == 0) {
             row_bc[0] = xmb;
@@ -537,6 +555,8 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             row_bc[4] = o[1];
             row_bc[5] = o[2];
             row_bc[6] = o[3];
+            row_bc[7] = o[4];
+            row_bc[8] = o[5];
         }
     }
     __syncthreads();
@@ -548,10 +568,10 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
         rc.mtc = uniform(rc.mt * rc.c);
         rc.mtw = uniform(rc.mt * a.curve.w);
     }
-    float thr_s = uniform(row_bc[3]);
     float sa = uniform(row_bc[4]), sb = uniform(row_bc[5]), sc = uniform(row_bc[6]);
+    float ta = uniform(row_bc[7]), tb = uniform(row_bc[8]);
     auto code_needed = [&](float x) -> float {
-        return fminf(__builtin_fmaf(x, sa, sb), sc);
+        return fminf(fmaxf(__builtin_fmaf(x, sa, sb), __builtin_fmaf(x, ta, tb)), sc);
     };
     // Exact scores of the elements of slot n (vector v, words w) that pass their own bound,
     // folded into the draw's best key.
@@ -604,20 +624,23 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                 } else {
                     lbx = xmax_blk * rc.invT - 3.14f;
                 }
-                float o[4];
-                screen_consts(uniform(fmaxf(candidate_score(), lbx)), o);
+                float o[6];
+                screen_consts(uniform(fmaxf(candidate_score(), lbx)), xmax_blk, o);
                 if (lane == 0) {
                     row_bc[3] = o[0];
                     row_bc[4] = o[1];
                     row_bc[5] = o[2];
                     row_bc[6] = o[3];
+                    row_bc[7] = o[4];
+                    row_bc[8] = o[5];
                 }
             }
             __syncthreads();
-            thr_s = uniform(row_bc[3]);
             sa = uniform(row_bc[4]);
             sb = uniform(row_bc[5]);
             sc = uniform(row_bc[6]);
+            ta = uniform(row_bc[7]);
+            tb = uniform(row_bc[8]);
         }
         uint64_t best = 0;
         if (!skip) {
@@ -678,8 +701,8 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                         a.out[o] = bad ? -2 : key_index(kb);
                         if (a.best_out) a.best_out[o] = bad ? -__builtin_inff() : key_score(kb);
                     } else if (kb != 0) {
-                        atomicMax(reinterpret_cast<unsigned long long *>(a.keys + o),
-                                  (unsigned long long)kb);
+                        __hip_atomic_fetch_max(a.keys + o, kb, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
                     }
                 }
             }
@@ -688,15 +711,21 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
 
     // ---- split rows: the last block of the row writes the ids and re-zeroes its slots ----
     if (a.nchunk > 1) {
-        __threadfence();
-        __syncthreads();
+        // The keys and counters of split rows are only ever touched by agent-scope atomics, so
+        // no fence is needed: an agent-scope fence writes back and invalidates the whole L2,
+        // which stalls every load in flight on the device. Thread 0, which made this block's
+        // maxima, waits for them to complete before it counts the block in; the block that
+        // counts last reads the keys after that, with atomic loads.
         if (tid == 0) {
-            const unsigned prev = atomicAdd(a.counters + b, 1u);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_s_waitcnt(0);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            const unsigned prev = __hip_atomic_fetch_add(a.counters + b, 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
             s_last = (prev == (unsigned)(a.nchunk * a.nkg - 1));
         }
         __syncthreads();
         if (s_last) {
-            __threadfence();
             for (int k = tid; k < a.K; k += BS) {
                 const int64_t o = b * a.K + k;
                 const uint64_t kk = __hip_atomic_load(a.keys + o, __ATOMIC_RELAXED,
@@ -712,36 +741,39 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     }
 }
 
-// Per-chunk (max, sum exp(x - max)) pairs for rows split over several blocks.
+// Per-chunk (max, sum exp(x - max)) pairs for rows split over several blocks, in one read:
+// each thread keeps a running (max, sum) in base 2 and rescales its sum when the maximum
+// moves; the block combines the pairs.
 template <int DT>
 __global__ __launch_bounds__(1024) void k_lse_partial(SampleArgs a) {
     using tr = dtype_traits<DT>;
     constexpr int EPV = tr::epv;
-    __shared__ float red_m[16], red_s[16];
+    __shared__ float2 red[16];
     const int chunk = blockIdx.x % a.nchunk;
     const int64_t b = blockIdx.x / a.nchunk;
     const int64_t v0 = (int64_t)chunk * a.cv;
     const int64_t vend = min(a.nvec, v0 + a.cv);
     const char *rowp = reinterpret_cast<const char *>(a.data) + b * a.ld * tr::esize;
-    float mx = -__builtin_inff();
+    float m = -3.402823466e38f, s = 0.0f;   // base 2: m a maximum of x log2(e)
     for (int64_t gv = v0 + threadIdx.x; gv < vend; gv += blockDim.x) {
         const uint4 v = load_vec<DT>(rowp, gv, a.V, a.aligned);
+        float xv[EPV];
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) mx = fmaxf(mx, elem<DT>(v, e));
-    }
-    const float M = block_max(mx, red_m);
-    float s = 0.0f;
-    if (M > -__builtin_inff()) {
-        const float mb = M * kLog2e;
-        for (int64_t gv = v0 + threadIdx.x; gv < vend; gv += blockDim.x) {
-            const uint4 v = load_vec<DT>(rowp, gv, a.V, a.aligned);
-#pragma unroll
-            for (int e = 0; e < EPV; ++e)
-                s += __builtin_amdgcn_exp2f(elem<DT>(v, e) * kLog2e - mb);
+        for (int e = 0; e < EPV; ++e) xv[e] = elem<DT>(v, e);
+        const float mv = vec_max<EPV>(xv) * kLog2e;
+        if (mv > m) {
+            s *= __builtin_amdgcn_exp2f(m - mv);
+            m = mv;
         }
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) s += __builtin_amdgcn_exp2f(__builtin_fmaf(xv[e], kLog2e, -m));
     }
-    const float S = block_sum(s, red_s);
-    if (threadIdx.x == 0) a.partials[b * a.part_stride + chunk] = make_float2(M, S);
+    const MaxSum ms = block_maxsum_log2(m, s, red);
+    if (threadIdx.x == 0) {
+        const bool fin = ms.s > 0.0f;
+        a.partials[b * a.part_stride + chunk] =
+            make_float2(fin ? ms.m * kLn2 : -__builtin_inff(), fin ? ms.s : 0.0f);
+    }
 }
 
 // One block per row: log-sum-exp of the row, and (transform) l' = g(x - LSE - mu).
