@@ -466,14 +466,22 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             o[3] = __builtin_fmaf(rc.mtw, kInvLn2, thr);
             o[4] = o[1];
             o[5] = o[2];
+            o[6] = 0.0f;
             const float z0 = xtop - rc.c;
-            if (z0 > rc.curve.w && rc.curve.w < __builtin_inff()) {
-                const float d = z0 - rc.curve.w;
+            const float d = z0 - rc.curve.w;
+            const float bh = 1.0f / rc.curve.ibh;
+            // the tangent lies below the mid line at the top by m (d - b log(1 + d/b)) >=
+            // m d^2 / (2 (b + d)); it is only set up when that can pass 1.5 (units of ln 2)
+            if (d > 0.0f && rc.curve.w < __builtin_inff() &&
+                rc.curve.m * d * d * rc.invT * kInvLn2 > 3.0f * (bh + d)) {
                 const float g0 = rc.curve.mw + rc.curve.mbh * log1p_acc(d * rc.curve.ibh);
-                const float s0 = rc.curve.mbh / (1.0f / rc.curve.ibh + d);   // m b / (b + d)
+                const float s0 = rc.curve.mbh / (bh + d);   // m b / (b + d)
                 // tan(x) = (s0 x + g0 - s0 (z0 + c)) / T
                 o[4] = -s0 * rc.invT * kInvLn2;
                 o[5] = __builtin_fmaf(__builtin_fmaf(-s0, xtop, g0) * rc.invT, -kInvLn2, thr);
+                // the vector screen pays two instructions per slot for the tangent: worth it
+                // when it lies well below the mid line at the top (in units of ln 2)
+                o[6] = ((rc.curve.m * z0 - g0) * rc.invT * kInvLn2 > 1.5f) ? 1.0f : 0.0f;
             }
         } else {
             o[1] = -rc.invT * kInvLn2;
@@ -481,6 +489,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             o[3] = __builtin_inff();
             o[4] = o[1];
             o[5] = o[2];
+            o[6] = 0.0f;
         }
     };
 
@@ -531,7 +540,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             rc.mtc = uniform(rc.mt * rc.c);
             rc.mtw = uniform(rc.mt * a.curve.w);
         }
-        float o[6] = {xmb, 0.0f, 0.0f, __builtin_inff(), 0.0f, 0.0f};
+        float o[7] = {xmb, 0.0f, 0.0f, __builtin_inff(), 0.0f, 0.0f, 0.0f};
         if (ok && screen) {
             // lower bounds on the first draw's winning score: the best candidate's exact
             // score, and from the chunk's largest logit (its curve value is at least
@@ -557,6 +566,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             row_bc[6] = o[3];
             row_bc[7] = o[4];
             row_bc[8] = o[5];
+            row_bc[9] = o[6];
         }
     }
     __syncthreads();
@@ -570,6 +580,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     }
     float sa = uniform(row_bc[4]), sb = uniform(row_bc[5]), sc = uniform(row_bc[6]);
     float ta = uniform(row_bc[7]), tb = uniform(row_bc[8]);
+    bool tan_on = uniform(row_bc[9]) > 0.0f;
     auto code_needed = [&](float x) -> float {
         return fminf(fmaxf(__builtin_fmaf(x, sa, sb), __builtin_fmaf(x, ta, tb)), sc);
     };
@@ -624,7 +635,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                 } else {
                     lbx = xmax_blk * rc.invT - 3.14f;
                 }
-                float o[6];
+                float o[7];
                 screen_consts(uniform(fmaxf(candidate_score(), lbx)), xmax_blk, o);
                 if (lane == 0) {
                     row_bc[3] = o[0];
@@ -633,6 +644,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                     row_bc[6] = o[3];
                     row_bc[7] = o[4];
                     row_bc[8] = o[5];
+                    row_bc[9] = o[6];
                 }
             }
             __syncthreads();
@@ -641,6 +653,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             sc = uniform(row_bc[6]);
             ta = uniform(row_bc[7]);
             tb = uniform(row_bc[8]);
+            tan_on = uniform(row_bc[9]) > 0.0f;
         }
         uint64_t best = 0;
         if (!skip) {
@@ -657,7 +670,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                     const float xm = __uint_as_float(s_vec[lane_lds + n] << 16);
                     bits = (bits << 1) | (xm >= xmax_blk ? 1u : 0u);
                 }
-            } else {
+            } else if (tan_on) {
 #pragma unroll
                 for (int n = NV - 1; n >= 0; --n) {
                     const uint32_t d = s_vec[lane_lds + n];
@@ -665,6 +678,15 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                     // a needed code above 16 is met only by n = 16, which stands for any word
                     // (so the cap keeps such vectors)
                     const float need = fminf(code_needed(xm), 16.0f);
+                    bits = (bits << 1) | ((float)lead_ones_hi16(d) >= need ? 1u : 0u);
+                }
+            } else {
+                // the same with the mid line alone (also an upper bound)
+#pragma unroll
+                for (int n = NV - 1; n >= 0; --n) {
+                    const uint32_t d = s_vec[lane_lds + n];
+                    const float xm = __uint_as_float(d << 16);
+                    const float need = fminf(fminf(__builtin_fmaf(xm, sa, sb), sc), 16.0f);
                     bits = (bits << 1) | ((float)lead_ones_hi16(d) >= need ? 1u : 0u);
                 }
             }
