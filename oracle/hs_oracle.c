@@ -152,13 +152,64 @@ int or_logsumexp(const double *x, int64_t n, int64_t V, int64_t ld, double *lse)
     return bad ? -1 : 0;
 }
 
+/* The pivot mu of one row [HLG, The pivot], in log-prob nats, computed from the full
+ * normalised log-prob vector l_i = x_i - LSE over the finite entries:
+ *   mode 0 (given):   mu = mu_in;
+ *   mode 1 (top):     mu = l_max - c, the curve centred c nats below the most probable token;
+ *   mode 2 (entropy): mu = sum_i p_i l_i with p_i = exp(l_i), i.e. minus the entropy.
+ * lse is the row's log-sum-exp (finite: the row has a finite entry). */
+double or_row_pivot(const double *x, int64_t V, double lse, int mode, double c, double mu_in)
+{
+    if (mode == 1) {
+        double lmax = -INFINITY;
+        for (int64_t i = 0; i < V; ++i) {
+            if (!(x[i] > -INFINITY)) continue;
+            double ell = x[i] - lse;
+            if (ell > lmax) lmax = ell;
+        }
+        return lmax - c;
+    }
+    if (mode == 2) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < V; ++i) {
+            if (!(x[i] > -INFINITY)) continue;
+            double ell = x[i] - lse;
+            acc += exp(ell) * ell;
+        }
+        return acc;
+    }
+    return mu_in;
+}
+
+/* Pivot of n rows (row stride ld): mu_out[r], NAN for a row with no finite entry. mu_in may
+ * be NULL unless mode == 0. Returns 0, -1 on a NaN / +inf logit, -2 on a bad mode / offset. */
+int or_pivot(const double *x, int64_t n, int64_t V, int64_t ld, int mode, double c,
+             const float *mu_in, double *mu_out)
+{
+    if (mode < 0 || mode > 2 || (mode == 1 && !isfinite(c))) return -2;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t r = 0; r < n; ++r) {
+        const double *xr = x + r * ld;
+        if (!or_row_ok(xr, V)) { bad |= 1; continue; }
+        double lse = or_row_logsumexp(xr, V);
+        mu_out[r] = (lse > -INFINITY) ? or_row_pivot(xr, V, lse, mode, c,
+                                                      mu_in ? (double)mu_in[r] : 0.0)
+                                      : NAN;
+    }
+    return bad ? -1 : 0;
+}
+
 /* l'[r, i] = g(l_i - mu_r) with l_i = x_i - LSE_r, the log-prob [HLG, The transfer function,
  * eq. z and eq. g]. The +mu shift is dropped because it cancels under softmax [HLG, same
- * section]. Masked entries stay -inf. mu is read as float and widened. */
+ * section]. Masked entries stay -inf. The pivot mu_r comes from or_row_pivot (mode pivot,
+ * offset c); a given mu is read as float and widened. */
 int or_hlg_transform(const double *x, int64_t n, int64_t V, int64_t ld, const float *mu,
-                     float m, float w, float bt, float bh, double *out, int64_t ldo)
+                     float m, float w, float bt, float bh, int pivot, float c, double *out,
+                     int64_t ldo)
 {
     if (!or_params_ok(m, w, bt, bh)) return -2;
+    if (pivot < 0 || pivot > 2 || (pivot == 1 && !isfinite(c))) return -2;
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
     for (int64_t r = 0; r < n; ++r) {
@@ -166,7 +217,9 @@ int or_hlg_transform(const double *x, int64_t n, int64_t V, int64_t ld, const fl
         double *orow = out + r * ldo;
         if (!or_row_ok(xr, V)) { bad |= 1; continue; }
         double lse = or_row_logsumexp(xr, V);
-        double mur = (double)mu[r];
+        double mur = (lse > -INFINITY) ? or_row_pivot(xr, V, lse, pivot, (double)c,
+                                                       pivot == 0 ? (double)mu[r] : 0.0)
+                                       : 0.0;
         for (int64_t i = 0; i < V; ++i) {
             if (xr[i] == -INFINITY) { orow[i] = -INFINITY; continue; }
             double ell = xr[i] - lse;          /* log-prob */
@@ -185,18 +238,20 @@ int or_hlg_transform(const double *x, int64_t n, int64_t V, int64_t ld, const fl
  * untouched]. Masked (-inf) tokens are never chosen [GMX, Regression guard].
  *
  * Inputs per row r of the n given rows: x (double, n x ld), row_id[r] (the global row index
- * that keys the counter), T[r], mu[r] (only with the curve on), seed[r], offset[r].
- * Outputs: out[r*K + k] token index, or -1 (no finite logit) / -2 (bad T or mu);
+ * that keys the counter), T[r], mu[r] (only with the curve on and pivot mode 0), seed[r],
+ * offset[r]; pivot and c select the pivot mode (or_row_pivot).
+ * Outputs: out[r*K + k] token index, or -1 (no finite logit) / -2 (bad T, or bad given mu);
  * best[r*K+k] and second[r*K+k] (may be NULL) the two largest scores of that draw
  * (-inf when absent). With hlg == 0 the curve parameters are ignored.
  * Returns 0, -1 on a NaN/+inf logit, -2 on bad curve parameters.
  * ------------------------------------------------------------------------------------- */
 int or_sample(const double *x, int64_t n, int64_t V, int64_t ld, const int64_t *row_id,
               const float *T, const float *mu, int hlg, float m, float w, float bt, float bh,
-              const uint64_t *seed, const uint64_t *offset, int32_t K,
+              int pivot, float c, const uint64_t *seed, const uint64_t *offset, int32_t K,
               int32_t *out, double *best, double *second)
 {
     if (hlg && !or_params_ok(m, w, bt, bh)) return -2;
+    if (hlg && (pivot < 0 || pivot > 2 || (pivot == 1 && !isfinite(c)))) return -2;
     int bad = 0;
     for (int64_t r = 0; r < n; ++r)
         if (!or_row_ok(x + r * ld, V)) bad = 1;
@@ -218,7 +273,7 @@ int or_sample(const double *x, int64_t n, int64_t V, int64_t ld, const int64_t *
         for (int64_t i = 0; i < V; ++i) nfinite += (xr[i] > -INFINITY);
         if (nfinite == 0) continue;                                   /* -1 */
         double t = (double)T[r];
-        if (!isfinite(t) || t < 0.0 || (hlg && !isfinite((double)mu[r]))) {
+        if (!isfinite(t) || t < 0.0 || (hlg && pivot == 0 && !isfinite((double)mu[r]))) {
             *o = -2;
             continue;
         }
@@ -232,7 +287,9 @@ int or_sample(const double *x, int64_t n, int64_t V, int64_t ld, const int64_t *
             }
         } else {
             double lse = hlg ? or_row_logsumexp(xr, V) : 0.0;
-            double mur = hlg ? (double)mu[r] : 0.0;
+            double mur = hlg ? or_row_pivot(xr, V, lse, pivot, (double)c,
+                                            pivot == 0 ? (double)mu[r] : 0.0)
+                             : 0.0;
             uint64_t off = offset[r] + (uint64_t)k;                   /* mod 2^64 */
             for (int64_t i = 0; i < V; ++i) {
                 if (!(xr[i] > -INFINITY)) continue;

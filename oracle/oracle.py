@@ -47,11 +47,14 @@ def lib():
         L.or_logsumexp.restype = C.c_int
         L.or_hlg_transform.argtypes = [f64p, C.c_int64, C.c_int64, C.c_int64, f32p,
                                        C.c_float, C.c_float, C.c_float, C.c_float,
-                                       f64p, C.c_int64]
+                                       C.c_int, C.c_float, f64p, C.c_int64]
         L.or_hlg_transform.restype = C.c_int
+        L.or_pivot.argtypes = [f64p, C.c_int64, C.c_int64, C.c_int64, C.c_int, C.c_double,
+                               C.c_void_p, f64p]
+        L.or_pivot.restype = C.c_int
         L.or_sample.argtypes = [f64p, C.c_int64, C.c_int64, C.c_int64, i64p, f32p, f32p,
                                 C.c_int, C.c_float, C.c_float, C.c_float, C.c_float,
-                                u64p, u64p, C.c_int32, i32p, f64p, f64p]
+                                C.c_int, C.c_float, u64p, u64p, C.c_int32, i32p, f64p, f64p]
         L.or_sample.restype = C.c_int
         _lib = L
     return _lib
@@ -122,12 +125,38 @@ def logsumexp(x) -> np.ndarray:
     return out
 
 
-def hlg_transform(x, mu, m, w, beta_t, beta_h) -> np.ndarray:
+# Pivot modes of the curve [HLG, The pivot]: the pivot given per row, top-anchored
+# (mu = l_max - c) or entropy-anchored (mu = sum p l).
+PIVOTS = {"input": 0, "top": 1, "entropy": 2}
+
+
+def _pivot_mode(p) -> int:
+    return PIVOTS[p] if isinstance(p, str) else int(p)
+
+
+def pivot(x, mode, offset: float = 0.0, mu=None) -> np.ndarray:
+    """The pivot mu of every row (float64), NaN for a row with no finite logit."""
     x = _as_f64_rows(x)
     n, V = x.shape
-    mu = np.ascontiguousarray(np.asarray(mu, dtype=np.float32).reshape(n))
+    out = np.zeros(n, dtype=np.float64)
+    mu_a = None if mu is None else np.ascontiguousarray(np.asarray(mu, dtype=np.float32).reshape(n))
+    rc = lib().or_pivot(x, n, V, V, _pivot_mode(mode), float(offset),
+                        None if mu_a is None else mu_a.ctypes.data, out)
+    if rc == -2:
+        raise OracleError("invalid pivot mode or offset")
+    if rc != 0:
+        raise OracleError("NaN or +inf logit")
+    return out
+
+
+def hlg_transform(x, mu, m, w, beta_t, beta_h, pivot="input", pivot_offset=0.0) -> np.ndarray:
+    x = _as_f64_rows(x)
+    n, V = x.shape
+    mu = np.ascontiguousarray(np.asarray(0.0 if mu is None else mu, dtype=np.float32)
+                              * np.ones(n, dtype=np.float32))
     out = np.zeros((n, V), dtype=np.float64)
-    rc = lib().or_hlg_transform(x, n, V, V, mu, m, w, beta_t, beta_h, out, V)
+    rc = lib().or_hlg_transform(x, n, V, V, mu, m, w, beta_t, beta_h, _pivot_mode(pivot),
+                                float(pivot_offset), out, V)
     if rc == -2:
         raise OracleError("invalid curve parameters")
     if rc != 0:
@@ -138,8 +167,9 @@ def hlg_transform(x, mu, m, w, beta_t, beta_h) -> np.ndarray:
 def sample(x, T, seed, offset, K: int = 1, mu=None, hlg=None, row_id=None):
     """Token ids [n, K] plus the best and second-best score of every draw.
 
-    hlg: None (curve off) or a mapping/tuple (m, w, beta_t, beta_h). row_id: the global row
-    index keying each row's Philox counter (default 0..n-1)."""
+    hlg: None (curve off) or a mapping/tuple (m, w, beta_t, beta_h); a mapping may also
+    carry "pivot" ("input", "top", "entropy") and "pivot_offset" (the c of the top mode).
+    row_id: the global row index keying each row's Philox counter (default 0..n-1)."""
     x = _as_f64_rows(x)
     n, V = x.shape
     T = np.ascontiguousarray(np.asarray(T, dtype=np.float32).reshape(n))
@@ -147,19 +177,25 @@ def sample(x, T, seed, offset, K: int = 1, mu=None, hlg=None, row_id=None):
     offset = np.ascontiguousarray(np.asarray(offset, dtype=np.uint64).reshape(n))
     rid = np.arange(n, dtype=np.int64) if row_id is None else \
         np.ascontiguousarray(np.asarray(row_id, dtype=np.int64).reshape(n))
+    piv, poff = 0, 0.0
     if hlg is None:
         on, p = 0, (1.0, 0.0, 1.0, 1.0)
         mu_a = np.zeros(n, dtype=np.float32)
     else:
         on = 1
-        p = tuple(hlg[k] for k in ("m", "w", "beta_t", "beta_h")) if isinstance(hlg, dict) \
-            else tuple(hlg)
-        mu_a = np.ascontiguousarray(np.asarray(mu, dtype=np.float32).reshape(n))
+        if isinstance(hlg, dict):
+            p = tuple(hlg[k] for k in ("m", "w", "beta_t", "beta_h"))
+            piv = _pivot_mode(hlg.get("pivot", 0))
+            poff = float(hlg.get("pivot_offset", 0.0))
+        else:
+            p = tuple(hlg)
+        mu_a = np.zeros(n, dtype=np.float32) if (mu is None and piv != 0) else \
+            np.ascontiguousarray(np.asarray(mu, dtype=np.float32).reshape(n))
     out = np.zeros((n, K), dtype=np.int32)
     best = np.zeros((n, K), dtype=np.float64)
     second = np.zeros((n, K), dtype=np.float64)
-    rc = lib().or_sample(x, n, V, V, rid, T, mu_a, on, p[0], p[1], p[2], p[3], seed, offset,
-                         int(K), out, best, second)
+    rc = lib().or_sample(x, n, V, V, rid, T, mu_a, on, p[0], p[1], p[2], p[3], piv, poff,
+                         seed, offset, int(K), out, best, second)
     if rc == -2:
         raise OracleError("invalid curve parameters")
     if rc != 0:
