@@ -54,14 +54,25 @@ typedef struct {
     int64_t ld;         /* row stride in elements, ld >= V */
 } hs_logits;
 
+/* Where the curve's pivot mu comes from [HLG, The pivot]. */
+typedef enum {
+    HS_PIVOT_GIVEN = 0,   /* mu[b] passed in by the caller (log-prob nats)                 */
+    HS_PIVOT_TOP = 1,     /* top-anchored: mu = l_max - pivot_offset, so z = x - (x_max - c) */
+    HS_PIVOT_ENTROPY = 2  /* entropy-anchored: mu = sum_i p_i l_i (minus the entropy), so
+                             z = x - E_p[x], p = softmax(x)                                 */
+} hs_pivot;
+
 /* The curve knobs of [HLG, Knobs]: mid gain m > 0 (finite), mid half-width w >= 0 (+inf
  * turns the rolloff off), toe and shoulder rolloff constants beta_t, beta_h > 0 (finite),
- * all in nats. */
+ * all in nats; the pivot mode (hs_pivot) and, for HS_PIVOT_TOP, the offset c (finite; it is
+ * ignored by the other modes). A zero-filled tail (pivot 0) keeps the caller-given pivot. */
 typedef struct {
     float m;
     float w;
     float beta_t;
     float beta_h;
+    int32_t pivot;
+    float pivot_offset;
 } hs_hlg_params;
 
 /* lse[b] = log(sum_i exp(x[b,i])) over the finite entries of row b, -inf for a row with no
@@ -71,11 +82,20 @@ int hs_logsumexp(const hs_logits *x, float *lse, void *stream);
 
 /* out[b*ldo + i] = g(z) with z = (x[b,i] - LSE_b) - mu[b] and g the toe / mid / shoulder
  * transfer function of [HLG, The transfer function, eq. z and eq. g]; -inf stays -inf.
- * This is l' before any temperature. mu: device float[B] (pivot, log-prob nats);
- * p: host pointer; out: device float[B*ldo], ldo >= V. A row with no finite entry is
+ * This is l' before any temperature. mu: device float[B] (pivot, log-prob nats), read
+ * only for HS_PIVOT_GIVEN; the other pivot modes compute mu[b] in the kernel (hs_hlg_pivot
+ * gives its value); p: host pointer; out: device float[B*ldo], ldo >= V. A row with no finite entry is
  * written as all -inf. */
 int hs_hlg_transform(const hs_logits *x, const float *mu, const hs_hlg_params *p, float *out,
                      int64_t ldo, void *stream);
+
+/* mu_out[b] = the pivot the curve uses for row b in p's pivot mode, in log-prob nats
+ * [HLG, The pivot]: mu[b] (HS_PIVOT_GIVEN), (x_max - LSE) - c (HS_PIVOT_TOP), or
+ * sum_i p_i (x_i - LSE) (HS_PIVOT_ENTROPY); NaN for a row with no finite entry.
+ * mu: device float[B], read only for HS_PIVOT_GIVEN (may be NULL otherwise);
+ * mu_out: device float[B]; p: host pointer. */
+int hs_hlg_pivot(const hs_logits *x, const float *mu, const hs_hlg_params *p, float *mu_out,
+                 void *stream);
 
 /* Gumbel-max draws without the curve [GMX, Task 1]:
  *   out[b*K + k] = argmax_i ( x[b,i] / T[b] + G(word(seed[b], b, i, offset[b] + k)) ),
@@ -97,7 +117,9 @@ int hs_gumbel_argmax(const hs_logits *x, const float *T, const uint64_t *seed,
  * function; GMX, Background]:
  *   l'_i = g((x_i - LSE_b) - mu[b])   when hlg != NULL,   l'_i = x_i   when hlg == NULL,
  *   out[b*K + k] = argmax_i ( l'_i / T[b] + G(word(seed[b], b, i, offset[b] + k)) ).
- * With the curve on, mu must be a device float[B] and a row with a non-finite mu gives -2.
+ * With the curve on and hlg->pivot == HS_PIVOT_GIVEN, mu must be a device float[B] and a
+ * row with a non-finite mu gives -2; the other pivot modes derive mu[b] from the row in the
+ * kernel (hs_hlg_pivot) and ignore mu.
  * T[b] == 0 is greedy on x (the curve is monotone, so it cannot change the argmax
  * [HLG, Greedy is untouched]). Everything else as hs_gumbel_argmax; the workspace size is
  * hs_workspace_bytes(B, V, K, dtype, hlg != NULL). */

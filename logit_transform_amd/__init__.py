@@ -18,7 +18,8 @@ import torch
 
 __all__ = [
     "HsError", "HlgParams", "SampleOpts", "load", "library_path", "EXPORTED_SYMBOLS",
-    "sample", "sample_ex", "gumbel_argmax", "logsumexp", "hlg_transform", "workspace_bytes",
+    "sample", "sample_ex", "gumbel_argmax", "logsumexp", "hlg_transform", "hlg_pivot",
+    "workspace_bytes", "PIVOTS",
     "workspace", "philox4x32_10", "stream_words", "gumbel_f32", "version",
 ]
 
@@ -29,7 +30,8 @@ HS_F32, HS_BF16, HS_F16 = 0, 1, 2
 _DTYPES = {torch.float32: HS_F32, torch.bfloat16: HS_BF16, torch.float16: HS_F16}
 
 EXPORTED_SYMBOLS = (
-    "hs_logsumexp", "hs_hlg_transform", "hs_gumbel_argmax", "hs_sample", "hs_sample_ex",
+    "hs_logsumexp", "hs_hlg_transform", "hs_hlg_pivot", "hs_gumbel_argmax", "hs_sample",
+    "hs_sample_ex",
     "hs_workspace_bytes", "hs_workspace_init", "hs_philox4x32_10", "hs_stream_words",
     "hs_gumbel_f32", "hs_status_str", "hs_version",
 )
@@ -49,9 +51,23 @@ class _Logits(C.Structure):
 
 class HlgParams(C.Structure):
     """Curve knobs in nats: mid gain m, mid half-width w (+inf = rolloff off), toe and
-    shoulder rolloff constants beta_t, beta_h."""
+    shoulder rolloff constants beta_t, beta_h; the pivot mode (PIVOTS) and the top anchor's
+    offset c."""
     _fields_ = [("m", C.c_float), ("w", C.c_float), ("beta_t", C.c_float),
-                ("beta_h", C.c_float)]
+                ("beta_h", C.c_float), ("pivot", C.c_int32), ("pivot_offset", C.c_float)]
+
+
+# Where the curve's pivot comes from: given per row (mu), top-anchored (mu = l_max - c),
+# entropy-anchored (mu = sum p l).
+PIVOTS = {"input": 0, "top": 1, "entropy": 2}
+
+
+def _pivot_mode(p) -> int:
+    if isinstance(p, str):
+        if p not in PIVOTS:
+            raise ValueError("unknown pivot mode %r" % (p,))
+        return PIVOTS[p]
+    return int(p)
 
 
 class SampleOpts(C.Structure):
@@ -84,6 +100,7 @@ def load() -> C.CDLL:
     OP = C.POINTER(SampleOpts)
     L.hs_logsumexp.argtypes = [LP, vp, vp]
     L.hs_hlg_transform.argtypes = [LP, vp, HP, vp, i64, vp]
+    L.hs_hlg_pivot.argtypes = [LP, vp, HP, vp, vp]
     L.hs_gumbel_argmax.argtypes = [LP, vp, vp, vp, i32, vp, vp, sz, vp]
     L.hs_sample.argtypes = [LP, vp, vp, HP, vp, vp, i32, vp, vp, sz, vp]
     L.hs_sample_ex.argtypes = [LP, vp, vp, HP, vp, vp, i32, vp, vp, vp, sz, OP, vp]
@@ -97,7 +114,7 @@ def load() -> C.CDLL:
     L.hs_status_str.restype = C.c_char_p
     L.hs_version.argtypes = []
     L.hs_version.restype = C.c_char_p
-    for name in ("hs_logsumexp", "hs_hlg_transform", "hs_gumbel_argmax", "hs_sample",
+    for name in ("hs_logsumexp", "hs_hlg_transform", "hs_hlg_pivot", "hs_gumbel_argmax", "hs_sample",
                  "hs_sample_ex", "hs_workspace_init", "hs_philox4x32_10", "hs_stream_words",
                  "hs_gumbel_f32"):
         getattr(L, name).restype = C.c_int
@@ -171,9 +188,21 @@ def _hlg_struct(hlg) -> Optional[HlgParams]:
         return hlg
     if isinstance(hlg, Mapping):
         return HlgParams(float(hlg["m"]), float(hlg["w"]), float(hlg["beta_t"]),
-                         float(hlg["beta_h"]))
-    m, w, bt, bh = hlg
-    return HlgParams(float(m), float(w), float(bt), float(bh))
+                         float(hlg["beta_h"]), _pivot_mode(hlg.get("pivot", 0)),
+                         float(hlg.get("pivot_offset", 0.0)))
+    m, w, bt, bh = hlg[:4]
+    piv = _pivot_mode(hlg[4]) if len(hlg) > 4 else 0
+    off = float(hlg[5]) if len(hlg) > 5 else 0.0
+    return HlgParams(float(m), float(w), float(bt), float(bh), piv, off)
+
+
+def _mu_vec(mu, hp, B, dev):
+    """The per-row pivot, needed only when the curve is on with a given pivot."""
+    if hp is None:
+        return None
+    if hp.pivot == 0 and mu is None:
+        raise ValueError("mu is required with the curve on and the pivot given")
+    return _row_vec(mu, B, torch.float32, dev, "mu") if (mu is not None and hp.pivot == 0) else None
 
 
 def workspace_bytes(B: int, V: int, K: int, dtype: torch.dtype, hlg_on: bool) -> int:
@@ -203,11 +232,7 @@ def sample_ex(logits: torch.Tensor, T, seed, offset, *, mu=None, hlg=None, k: in
     st = _row_vec(seed, B, torch.int64, dev, "seed")
     of = _row_vec(offset, B, torch.int64, dev, "offset")
     hp = _hlg_struct(hlg)
-    mut = None
-    if hp is not None:
-        if mu is None:
-            raise ValueError("mu is required with the curve on")
-        mut = _row_vec(mu, B, torch.float32, dev, "mu")
+    mut = _mu_vec(mu, hp, B, dev)
     if out is None:
         out = torch.empty((B, k), dtype=torch.int32, device=dev)
     best = torch.empty((B, k), dtype=torch.float32, device=dev) if want_best else None
@@ -224,8 +249,9 @@ def sample_ex(logits: torch.Tensor, T, seed, offset, *, mu=None, hlg=None, k: in
 def sample(logits: torch.Tensor, T, seed, offset, *, mu=None, hlg=None, k: int = 1,
            out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The sampling step: token ids [B, k] (int32) on logits' device, asynchronously on the
-    current stream. hlg=None turns the curve off; otherwise hlg = (m, w, beta_t, beta_h) or a
-    mapping with those keys, and mu is the per-row pivot. Rows give -1 when no logit is
+    current stream. hlg=None turns the curve off; otherwise hlg = (m, w, beta_t, beta_h
+    [, pivot, pivot_offset]) or a mapping with those keys, and mu is the per-row pivot when
+    the pivot mode is "input" (the default; "top" and "entropy" derive it in the kernel). Rows give -1 when no logit is
     finite and -2 for an invalid temperature or pivot; T = 0 is greedy."""
     L = load()
     x = _logits_struct(logits)
@@ -235,11 +261,7 @@ def sample(logits: torch.Tensor, T, seed, offset, *, mu=None, hlg=None, k: int =
     st = _row_vec(seed, B, torch.int64, dev, "seed")
     of = _row_vec(offset, B, torch.int64, dev, "offset")
     hp = _hlg_struct(hlg)
-    mut = None
-    if hp is not None:
-        if mu is None:
-            raise ValueError("mu is required with the curve on")
-        mut = _row_vec(mu, B, torch.float32, dev, "mu")
+    mut = _mu_vec(mu, hp, B, dev)
     if out is None:
         out = torch.empty((B, k), dtype=torch.int32, device=dev)
     if ws is None:
@@ -281,15 +303,30 @@ def logsumexp(logits: torch.Tensor) -> torch.Tensor:
 
 
 def hlg_transform(logits: torch.Tensor, mu, hlg) -> torch.Tensor:
-    """l' = g(log-softmax(x) - mu) as float32 [B, V] (before any temperature)."""
+    """l' = g(log-softmax(x) - mu) as float32 [B, V] (before any temperature); mu is read
+    only with the pivot given (mode "input")."""
     L = load()
     x = _logits_struct(logits)
     B, V = logits.shape
-    mut = _row_vec(mu, B, torch.float32, logits.device, "mu")
     hp = _hlg_struct(hlg)
+    mut = _mu_vec(mu, hp, B, logits.device)
     out = torch.empty((B, V), dtype=torch.float32, device=logits.device)
-    _check(L.hs_hlg_transform(C.byref(x), mut.data_ptr(), C.byref(hp), out.data_ptr(), V,
+    _check(L.hs_hlg_transform(C.byref(x), _ptr(mut), C.byref(hp), out.data_ptr(), V,
                               _stream(logits.device)), "hs_hlg_transform")
+    return out
+
+
+def hlg_pivot(logits: torch.Tensor, hlg, mu=None) -> torch.Tensor:
+    """The pivot mu [B] (float32, log-prob nats) the curve uses in hlg's pivot mode; NaN for
+    a row with no finite logit."""
+    L = load()
+    x = _logits_struct(logits)
+    B = logits.shape[0]
+    hp = _hlg_struct(hlg)
+    mut = _mu_vec(mu, hp, B, logits.device)
+    out = torch.empty(B, dtype=torch.float32, device=logits.device)
+    _check(L.hs_hlg_pivot(C.byref(x), _ptr(mut), C.byref(hp), out.data_ptr(),
+                          _stream(logits.device)), "hs_hlg_pivot")
     return out
 
 

@@ -37,6 +37,9 @@ int check_curve(const hs_hlg_params *p) {
     if (!(p->w >= 0.0f)) return HS_ERR_INVALID_ARG;   // +inf allowed (rolloff off)
     if (!(p->beta_t > 0.0f) || !isfinite(p->beta_t)) return HS_ERR_INVALID_ARG;
     if (!(p->beta_h > 0.0f) || !isfinite(p->beta_h)) return HS_ERR_INVALID_ARG;
+    if (p->pivot != HS_PIVOT_GIVEN && p->pivot != HS_PIVOT_TOP && p->pivot != HS_PIVOT_ENTROPY)
+        return HS_ERR_INVALID_ARG;
+    if (p->pivot == HS_PIVOT_TOP && !isfinite(p->pivot_offset)) return HS_ERR_INVALID_ARG;
     return HS_OK;
 }
 
@@ -78,7 +81,7 @@ WsLayout ws_layout(int64_t B, int32_t K) {
     L.counters = 0;
     L.keys = align256((size_t)B * 4);
     L.partials = L.keys + align256((size_t)B * (size_t)K * 8);
-    L.total = L.partials + align256((size_t)B * hs::kMaxChunks * 8);
+    L.total = L.partials + align256((size_t)B * hs::kMaxChunks * sizeof(float4));
     return L;
 }
 
@@ -165,7 +168,7 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
     if (hlg) {
         rc = check_curve(hlg);
         if (rc) return rc;
-        if (!mu) return HS_ERR_INVALID_ARG;
+        if (hlg->pivot == HS_PIVOT_GIVEN && !mu) return HS_ERR_INVALID_ARG;
     }
     if ((size_t)x->B * (size_t)K >= ((size_t)1 << 31)) return HS_ERR_UNSUPPORTED;
     const WsLayout L = ws_layout(x->B, K);
@@ -192,26 +195,30 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
     a.aligned = rows_aligned(x) ? 1 : 0;
     a.no_screen = (opts && opts->no_screen) ? 1 : 0;
     a.T = T;
-    a.mu = hlg ? mu : nullptr;
+    const int piv = hlg ? hlg->pivot : 0;
+    a.mu = piv == HS_PIVOT_GIVEN ? mu : nullptr;
     a.seed = seed;
     a.offset = offset;
     a.out = out;
     a.best_out = best;
-    if (hlg) a.curve = make_curve(hlg);
+    if (hlg) {
+        a.curve = make_curve(hlg);
+        a.pivot_offset = hlg->pivot == HS_PIVOT_TOP ? hlg->pivot_offset : 0.0f;
+    }
     if (P.nchunk > 1) {
         char *w = reinterpret_cast<char *>(ws);
         a.counters = reinterpret_cast<uint32_t *>(w + L.counters);
         a.keys = reinterpret_cast<uint64_t *>(w + L.keys);
-        a.partials = reinterpret_cast<float2 *>(w + L.partials);
+        a.partials = reinterpret_cast<float4 *>(w + L.partials);
         a.part_stride = hs::kMaxChunks;
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (hlg && P.nchunk > 1) {
         const int bs = P.cv >= 4096 ? 1024 : 256;
-        if (hs::launch_lse_partial(x->dtype, a, bs, (int)(x->B * P.nchunk), s) != hipSuccess)
+        if (hs::launch_lse_partial(x->dtype, piv, a, bs, (int)(x->B * P.nchunk), s) != hipSuccess)
             return HS_ERR_HIP;
     }
-    if (hs::launch_sample(x->dtype, hlg != nullptr, a, P.nv, P.bs, (int)P.grid, s) != hipSuccess)
+    if (hs::launch_sample(x->dtype, hlg != nullptr, piv, a, P.nv, P.bs, (int)P.grid, s) != hipSuccess)
         return HS_ERR_HIP;
     return HS_OK;
 }
@@ -230,7 +237,7 @@ int hs_logsumexp(const hs_logits *x, float *lse, void *stream) {
     a.V = x->V;
     a.aligned = rows_aligned(x) ? 1 : 0;
     a.lse = lse;
-    return hs::launch_row_lse(x->dtype, false, a, (int)x->B, reinterpret_cast<hipStream_t>(stream))
+    return hs::launch_row_lse(x->dtype, 0, 0, a, (int)x->B, reinterpret_cast<hipStream_t>(stream))
                    == hipSuccess ? HS_OK : HS_ERR_HIP;
 }
 
@@ -240,18 +247,40 @@ int hs_hlg_transform(const hs_logits *x, const float *mu, const hs_hlg_params *p
     if (rc) return rc;
     rc = check_curve(p);
     if (rc) return rc;
-    if (!mu || !out || ldo < x->V) return HS_ERR_INVALID_ARG;
+    if ((p->pivot == HS_PIVOT_GIVEN && !mu) || !out || ldo < x->V) return HS_ERR_INVALID_ARG;
     hs::RowOpArgs a{};
     a.data = x->data;
     a.ld = x->ld;
     a.V = x->V;
     a.aligned = rows_aligned(x) ? 1 : 0;
-    a.mu = mu;
+    a.mu = p->pivot == HS_PIVOT_GIVEN ? mu : nullptr;
     a.out = out;
     a.ldo = ldo;
     a.curve = make_curve(p);
-    return hs::launch_row_lse(x->dtype, true, a, (int)x->B, reinterpret_cast<hipStream_t>(stream))
-                   == hipSuccess ? HS_OK : HS_ERR_HIP;
+    a.pivot_offset = p->pivot == HS_PIVOT_TOP ? p->pivot_offset : 0.0f;
+    return hs::launch_row_lse(x->dtype, 1, p->pivot, a, (int)x->B,
+                              reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? HS_OK
+                                                                                   : HS_ERR_HIP;
+}
+
+int hs_hlg_pivot(const hs_logits *x, const float *mu, const hs_hlg_params *p, float *mu_out,
+                 void *stream) {
+    int rc = check_logits(x);
+    if (rc) return rc;
+    rc = check_curve(p);
+    if (rc) return rc;
+    if ((p->pivot == HS_PIVOT_GIVEN && !mu) || !mu_out) return HS_ERR_INVALID_ARG;
+    hs::RowOpArgs a{};
+    a.data = x->data;
+    a.ld = x->ld;
+    a.V = x->V;
+    a.aligned = rows_aligned(x) ? 1 : 0;
+    a.mu = p->pivot == HS_PIVOT_GIVEN ? mu : nullptr;
+    a.mu_out = mu_out;
+    a.pivot_offset = p->pivot == HS_PIVOT_TOP ? p->pivot_offset : 0.0f;
+    return hs::launch_row_lse(x->dtype, 2, p->pivot, a, (int)x->B,
+                              reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? HS_OK
+                                                                                   : HS_ERR_HIP;
 }
 
 int hs_gumbel_argmax(const hs_logits *x, const float *T, const uint64_t *seed,

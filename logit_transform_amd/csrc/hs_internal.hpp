@@ -35,8 +35,9 @@ struct SampleArgs {
     // workspace (split rows only)
     uint32_t *counters;        // [B]
     uint64_t *keys;            // [B * K]
-    float2 *partials;          // [B * part_stride]
+    float4 *partials;          // [B * part_stride]: per chunk (max, sum, u, -) in nats
     int64_t part_stride;
+    float pivot_offset;        // c of the top anchor
 };
 
 struct RowOpArgs {
@@ -48,12 +49,21 @@ struct RowOpArgs {
     float *out;
     int64_t ldo;
     Curve curve;
+    float pivot_offset;   // c of the top anchor
+    float *mu_out;        // the pivot of every row (op 2)
 };
 
-hipError_t launch_sample(int dt, bool hlg, const SampleArgs &a, int nv, int bs, int grid,
-                         hipStream_t s);
-hipError_t launch_lse_partial(int dt, const SampleArgs &a, int bs, int grid, hipStream_t s);
-hipError_t launch_row_lse(int dt, bool transform, const RowOpArgs &a, int grid, hipStream_t s);
+// piv: the curve's pivot, 0 given per row, 1 top-anchored, 2 entropy-anchored
+hipError_t launch_sample(int dt, bool hlg, int piv, const SampleArgs &a, int nv, int bs,
+                         int grid, hipStream_t s);
+hipError_t launch_sample_pivot(int dt, int piv, const SampleArgs &a, int nv, int bs, int grid,
+                               hipStream_t s);
+hipError_t launch_lse_partial(int dt, int piv, const SampleArgs &a, int bs, int grid,
+                              hipStream_t s);
+hipError_t launch_lse_partial_pivot(int dt, int piv, const SampleArgs &a, int bs, int grid,
+                                    hipStream_t s);
+// op: 0 log-sum-exp, 1 transform, 2 pivot
+hipError_t launch_row_lse(int dt, int op, int piv, const RowOpArgs &a, int grid, hipStream_t s);
 hipError_t launch_philox(const uint32_t *ctr, const uint32_t *key, uint32_t *out, int64_t n,
                          hipStream_t s);
 hipError_t launch_stream_words(const uint64_t *seed, const uint64_t *offset, int64_t B,

@@ -1,0 +1,898 @@
+// hs_sample_kernel.hpp -- the sampling kernel of libhs (gfx950): batched HLG tone curve +
+// Gumbel-max draws, and its split-row pre-pass. Included by the translation units that
+// instantiate it (hs_kernels.hip, hs_kernels_pivot.hip).
+//
+// Sources, cited by page title and section:
+//   [HLG]  "HLG sampling -- a piecewise tone curve on the logits" (mlx-bun design document).
+//   [GMX]  "Softmax-free GPU sampling: Gumbel-max categorical sampling kernel" (mlxcel #900).
+//
+// Work decomposition. A block owns one contiguous chunk of one row and keeps it in VGPRs as
+// raw 16-byte vectors (thread t holds vectors t, t+BS, t+2BS, ...: consecutive lanes read
+// consecutive 16 B, so every wave load is one contiguous 1 KiB). The row is read from HBM
+// once; every pass after the load (max, sum of exponentials, and each draw) runs on the
+// register copy. With one chunk per row the row's log-sum-exp is reduced inside the block
+// (single read). With several chunks per row a pre-pass leaves per-chunk (max, sum) pairs in
+// the workspace, every block of the row folds them in the same fixed order, and the chunks'
+// winning keys meet in a 64-bit atomic max; the last block of the row to finish writes the
+// token ids and zeroes its workspace slots again.
+//
+// Screening. A draw's winner is the exact argmax over all elements, but the expensive part
+// of an element's score (curve branches, two logarithms) is evaluated only when an upper
+// bound on that score reaches a lower bound on the draw's winning score, less a slack:
+//   score = l'/T + G(r) <= U(x) + (n(r) + 1) ln 2,
+// where U(x) = (m/T) * max(x - c, -w) bounds g(x - c)/T (g lies below its mid line past the
+// shoulder knot and below -m*w in the toe) and n(r), the leading ones of the word, bounds G
+// (G(r) <= -log(1 - u) <= (n + 1) ln 2). The first pass over a draw keeps, per vector, only
+// the largest word (and so the largest n); a vector whose largest logit and largest word
+// cannot reach the bound is skipped whole, and the few that can are drawn again and tested
+// element by element. The lower bound is the exact score of one element per lane, the one
+// with the lane's largest word, maximised over the block. The bounds are rigorous up to fp32
+// rounding, which the slack covers many times over, so the screened result equals the
+// exhaustive one bit for bit (a test checks this).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "hs_device.hpp"
+#include "hs_internal.hpp"
+
+namespace hs {
+
+__device__ __forceinline__ float screen_slack(float s) {
+    return 1e-3f + 1e-5f * (fabsf(s) + 32.0f);
+}
+
+// A block-uniform float moved to a scalar register.
+__device__ __forceinline__ float uniform(float v) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
+// Per-row constants of one block.
+struct RowConst {
+    float invT;      // 1 / T
+    float c;         // LSE + mu (curve on)
+    float mt;        // m / T
+    float mtc;       // (m / T) * c
+    float mtw;       // (m / T) * w
+    Curve curve;
+};
+
+// The exact fp32 score of one finite element: l'/T + G(r) [GMX, Background], with
+// l' = g(x - (LSE + mu)) when the curve is on [HLG, The transfer function]. Every kernel
+// variant scores elements through this one function.
+template <bool HLG>
+__device__ __forceinline__ float exact_score_inl(float x, uint32_t word, const RowConst &rc) {
+    float a;
+    if constexpr (HLG) {
+        a = hlg32(x - rc.c, rc.curve) * rc.invT;
+    } else {
+        a = x * rc.invT;
+    }
+    return a + gumbel32(word);
+}
+
+// The same function kept out of line for the rare candidate path, so that its code is not
+// repeated at every vector of the unrolled screen.
+template <bool HLG>
+__device__ __noinline__ float exact_score(float x, uint32_t word, RowConst rc) {
+    return exact_score_inl<HLG>(x, word, rc);
+}
+
+
+template <int DT>
+__device__ __forceinline__ uint64_t greedy_vec(uint4 raw, uint32_t i0, uint64_t best) {
+    constexpr int EPV = dtype_traits<DT>::epv;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+        const float x = elem<DT>(raw, e);
+        if (x > -__builtin_inff()) best = umax64(best, make_key(x, i0 + (uint32_t)e));
+    }
+    return best;
+}
+
+// Largest of the EPV logits of a vector.
+template <int EPV>
+__device__ __forceinline__ float vec_max(const float (&x)[EPV]) {
+    if constexpr (EPV == 8) {
+        const float t = max3f(x[0], x[1], x[2]);
+        const float u = max3f(x[3], x[4], x[5]);
+        return max2f(max3f(x[6], x[7], t), u);
+    } else {
+        return max2f(max3f(x[0], x[1], x[2]), x[3]);
+    }
+}
+
+// PIV selects the curve's pivot [HLG, The pivot] (curve on only): 0 given per row,
+// 1 top-anchored (mu = l_max - c: z = x - (x_max - c), no log-sum-exp needed),
+// 2 entropy-anchored (mu = sum p l: z = x - E_p[x], one more accumulator).
+template <int DT, int NV, bool HLG, int PIV, int MAXBS, bool ALIGNED>
+__global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
+    static_assert(HLG || PIV == 0, "a pivot needs the curve");
+    constexpr bool LSE = HLG && PIV != 1;   // the exponential sum is needed
+    using tr = dtype_traits<DT>;
+    constexpr int EPV = tr::epv;
+    constexpr int NG = EPV / 4;                // Philox calls per vector
+    constexpr int D = NV < 8 ? NV : 8;         // loads in flight per lane
+    constexpr int LAG = NV < 7 ? NV - 1 : 6;   // slots of random words ahead of the logits
+    // Dynamic LDS, one dword per lane and slot: the vector's largest logit as a bf16-grid upper
+    // bound in the low half (draw-invariant) and the high 16 bits of its largest random word of
+    // the current draw in the high half. Each lane's entries are contiguous (odd stride: lanes
+    // hit distinct banks), so every access is one base register plus an immediate offset.
+    extern __shared__ uint32_t s_vec[];
+    __shared__ float red_m[16], red_s[16], red_u[16], red_x[16];
+    __shared__ uint64_t red_ck[16];    // per wave: best bootstrap candidate key
+    __shared__ float red_cx[16];       //   its logit
+    __shared__ uint32_t red_cw[16];    //   and word
+    __shared__ float row_bc[12];       // row constants from wave 0
+    // two buffers, alternating between draws: without a bootstrap (greedy rows, no screening)
+    // nothing else separates one draw's reads of the buffer from the next draw's writes
+    __shared__ uint64_t red_draw[2][16];
+    __shared__ int s_last;
+
+    const int tid = threadIdx.x;
+    const int BS = blockDim.x;
+    constexpr int SC = NV | 1;
+    uint16_t *s_vec16 = reinterpret_cast<uint16_t *>(s_vec);
+    int lane_lds = tid * SC;
+    // block coordinates in scalar registers (the divisions would otherwise run per lane)
+    int bid = blockIdx.x;
+    const int chunk = __builtin_amdgcn_readfirstlane(bid % a.nchunk);
+    bid /= a.nchunk;
+    const int kg = __builtin_amdgcn_readfirstlane(bid % a.nkg);
+    const int64_t b = __builtin_amdgcn_readfirstlane(bid / a.nkg);
+    const int k0 = kg * a.kpg;
+    const int k1 = min(a.K, k0 + a.kpg);
+
+    // ---- row parameters (wave-uniform) ----
+    const float T = a.T[b];
+    float mu = 0.0f;
+    bool bad = !(T >= 0.0f) || !(T < __builtin_inff());
+    if constexpr (HLG && PIV == 0) {
+        mu = a.mu[b];
+        bad = bad || !(fabsf(mu) < __builtin_inff());
+    }
+    const bool greedy = (T == 0.0f);
+
+    // ---- this block's chunk of the row: lane t owns vectors v0 + t + n*BS, n < NV ----
+    const int v0 = chunk * (int)a.cv;
+    const int vend = (int)min(a.nvec, (int64_t)v0 + a.cv);
+    const int nfull = (int)(a.V / EPV);   // vectors with all EPV elements inside the row
+    const int vlim = min(vend, nfull);    // vectors below this one load whole
+    const char *rowp = reinterpret_cast<const char *>(a.data) + b * a.ld * tr::esize;
+    int lane_v = v0 + tid;
+    // the last vector index of this wave at slot 0 (wave-uniform)
+    const int wave_last = __builtin_amdgcn_readfirstlane(v0 + (tid | 63));
+    const uint4 ninf4 = make_uint4(tr::neg_inf_word, tr::neg_inf_word, tr::neg_inf_word,
+                                   tr::neg_inf_word);
+
+    // Vector gv of the chunk; -inf past the chunk or the row.
+    auto fetch = [&](int gv) -> uint4 {
+        if (gv >= vend) return ninf4;
+        return load_vec<DT>(rowp, gv, a.V, ALIGNED);
+    };
+    // ALIGNED: slot n's load carries no branch (a slot past the whole vectors reads an in-row
+    // whole vector instead, clamped index) and is patched when its data is used, with selects
+    // only: a load inside the pipelined pass would make the compiler wait for every load in
+    // flight. The row's partial last vector (V not a multiple of EPV) is read element by
+    // element up front by every lane, with clamped addresses (one cache line, no branch); only
+    // waves that reach past vlim at slot n test per lane.
+    const int gclamp = vlim - 1;   // >= 0: the launcher ensures V >= epv for ALIGNED
+    uint4 rag = ninf4;
+    if constexpr (ALIGNED) {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = tr::neg_inf_word;
+        const int64_t i0 = (int64_t)nfull * EPV;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+            const int64_t i = min(i0 + e, a.V - 1);
+            uint32_t h;
+            if constexpr (DT == DT_F32) {
+                h = reinterpret_cast<const uint32_t *>(rowp)[i];
+            } else {
+                h = reinterpret_cast<const uint16_t *>(rowp)[i];
+            }
+            if (i0 + e < a.V) {
+                if constexpr (DT == DT_F32) {
+                    w[e] = h;
+                } else {
+                    const int j = e >> 1;
+                    w[j] = (e & 1) ? ((w[j] & 0x0000FFFFu) | (h << 16))
+                                   : ((w[j] & 0xFFFF0000u) | h);
+                }
+            }
+        }
+        rag = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    auto issue_load = [&](int n) -> uint4 {
+        if constexpr (ALIGNED) {
+            const int gv = min(lane_v + n * BS, gclamp);
+            return *reinterpret_cast<const uint4 *>(rowp + (uint32_t)gv * 16u);
+        } else {
+            return fetch(lane_v + n * BS);
+        }
+    };
+    auto patch = [&](int n, uint4 v) -> uint4 {
+        if constexpr (ALIGNED) {
+            if (wave_last + n * BS >= vlim) {
+                const int gv = lane_v + n * BS;
+                const bool past = gv >= vend;
+                const bool part = gv >= nfull;
+                v.x = past ? ninf4.x : part ? rag.x : v.x;
+                v.y = past ? ninf4.y : part ? rag.y : v.y;
+                v.z = past ? ninf4.z : part ? rag.z : v.z;
+                v.w = past ? ninf4.w : part ? rag.w : v.w;
+            }
+        }
+        return v;
+    };
+
+    const uint64_t seed = a.seed[b];
+    const uint64_t off0 = a.offset[b];
+    Stream st;
+    st.row = (uint32_t)b;
+    st.key0 = (uint32_t)seed;
+    st.key1 = (uint32_t)(seed >> 32);
+    auto stream_k = [&](int k) {
+        const uint64_t off = off0 + (uint64_t)k;
+        Stream sk = st;
+        sk.off_lo = (uint32_t)off;
+        sk.off_hi = (uint32_t)(off >> 32);
+        return sk;
+    };
+
+    // Random words of slot n for draw stream sk: their maximum goes to the slot's LDS dword
+    // (high half); returns the slot's key for the lane's champion, max word & ~31 | slot. Slots
+    // past the chunk are drawn too (their words are never used).
+    auto draw_vec = [&](const Stream &sk, int n) -> uint32_t {
+        uint32_t q = (uint32_t)(lane_v + n * BS) * NG;
+        asm volatile("" : "+v"(q));
+        uint32_t mw;
+        {
+            const Words4 w = philox4x32_10_uk(q, sk.row, sk.off_lo, sk.off_hi, sk.key0, sk.key1);
+            mw = max(max3u(w.w[0], w.w[1], w.w[2]), w.w[3]);
+            if constexpr (NG == 2) {
+                const Words4 u = philox4x32_10_uk(q + 1, sk.row, sk.off_lo, sk.off_hi, sk.key0,
+                                                  sk.key1);
+                mw = max3u(max3u(w.w[0], w.w[1], w.w[2]), max3u(w.w[3], u.w[0], u.w[1]),
+                           max(u.w[2], u.w[3]));
+            }
+        }
+        s_vec16[2 * (lane_lds + n) + 1] = (uint16_t)(mw >> 16);
+        return (mw & ~31u) | (uint32_t)n;
+    };
+    // The lane's champion key over a whole draw (draws without the logits at hand).
+    auto draw_all = [&](const Stream &sk) -> uint32_t {
+        uint32_t champ = 0;
+#pragma unroll
+        for (int n = 0; n < NV; ++n) {
+            champ = max(champ, draw_vec(sk, n));
+            // one running maximum: otherwise the compiler regroups the chain of maxima and
+            // keeps every slot's word alive until the end of the pass
+            asm volatile("" : "+v"(champ));
+        }
+        return champ;
+    };
+
+    // Slot n's logits: the vector's largest logit (rounded up to the bf16 grid for f32/f16
+    // input, so it stays an upper bound) into the low half of its LDS dword, the lane's largest
+    // logit, and with the curve on the log-sum-exp of the row [HLG, The transfer function:
+    // l = x - LSE(x)], streamed per lane in base 2 against a fixed reference r, the scaled
+    // maximum of the lane's first vector: s = sum 2^(x log2(e) - r). Lanes whose largest logit
+    // ends up far from r (where the sum could overflow or lose its terms) sum again against
+    // their own maximum after the pass.
+    // With the entropy anchor also u = sum 2^t t, t = x log2(e) - r, for E_p[x].
+    float xmax_lane = -__builtin_inff();
+    float lse_r = 0.0f, lse_s = 0.0f, lse_u = 0.0f;
+    auto data_vec = [&](int n, uint4 v) {
+        // Keep the slots in order: otherwise the scheduler issues the exponentials of many
+        // vectors first and holds all their results at once.
+        asm volatile("" : "+v"(lse_s), "+v"(xmax_lane), "+v"(lse_u));
+        float xv[EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) xv[e] = elem<DT>(v, e);
+        const float m = vec_max<EPV>(xv);
+        xmax_lane = max2f(xmax_lane, m);
+        uint32_t mb = __float_as_uint(m);
+        if constexpr (DT != DT_BF16) {
+            // toward +inf on the bf16 grid: positive values round up, negative ones truncate
+            mb = ((int32_t)mb >= 0) ? mb + 0xFFFFu : mb;
+        }
+        s_vec16[2 * (lane_lds + n)] = (uint16_t)(mb >> 16);
+        if constexpr (LSE) {
+            if (n == 0) lse_r = (m > -__builtin_inff()) ? m * kLog2e : 0.0f;
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                const float t = __builtin_fmaf(xv[e], kLog2e, -lse_r);
+                const float p = __builtin_amdgcn_exp2f(t);
+                lse_s += p;
+                if constexpr (PIV == 2) lse_u = (p > 0.0f) ? __builtin_fmaf(p, t, lse_u) : lse_u;
+            }
+        }
+    };
+
+    const bool sampled = !bad && !greedy;
+    const bool screen = sampled && !a.no_screen;
+    const float invT = 1.0f / T;
+    // Linear part of the score used to rank bootstrap candidates before c = LSE + mu is known:
+    // (m/T) x with the curve on (the mid line of g, up to the common shift -(m/T) c), x/T
+    // without it.
+    const float lin = HLG ? a.curve.m * invT : invT;
+    // Bootstrap candidate of a lane for draw stream sk: the element holding the largest word of
+    // its champion vector v (nearly the largest Gumbel value among the lane's elements). The
+    // vector's words are drawn again into cw (kept for the screen). Returns the candidate's rank
+    // key (lin x - log(1 - u) -- a monotone stand-in for the Gumbel value, close to it where u
+    // is near 1 -- and the lane) and its logit and word.
+    struct Cand {
+        uint64_t key;
+        float x;
+        uint32_t w;
+    };
+    auto candidate = [&](const Stream &sk, uint32_t champ, const uint4 &v,
+                         uint32_t (&cw)[EPV]) -> Cand {
+        Cand c{0ull, -__builtin_inff(), 0u};
+        uint32_t q = (uint32_t)(lane_v + (int)(champ & 31u) * BS) * NG;
+        asm volatile("" : "+v"(q));
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const Words4 w = philox4x32_10_uk(q + g, sk.row, sk.off_lo, sk.off_hi, sk.key0,
+                                              sk.key1);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cw[4 * g + e] = w.w[e];
+        }
+#pragma unroll
+        for (int e = EPV - 1; e >= 0; --e) {
+            if ((cw[e] ^ champ) < 32u) {
+                c.w = cw[e];
+                c.x = elem<DT>(v, e);
+            }
+        }
+        const float nlv = __builtin_amdgcn_logf(__builtin_fmaf((float)(~c.w), 0x1p-32f, 0x1p-33f));
+        const bool ok = c.x > -__builtin_inff() && lane_v + (int)(champ & 31u) * BS < vend;
+        c.key = ok ? make_key(__builtin_fmaf(c.x, lin, -nlv * kLn2), (uint32_t)tid) : 0ull;
+        return c;
+    };
+
+    // ---- one pass over the chunk: the first draw's random words (which need no logit) run
+    // LAG slots ahead of the logits, so the first loads land while they are computed; D loads
+    // stay in flight. The lane's champion vector (largest word so far) is kept in registers as
+    // the logits come in, and its words are drawn again after the pass. The pass is the same
+    // for every row (greedy and invalid rows draw words they never use):
+    // without row-dependent branches the scheduler interleaves the integer Philox chains with
+    // the float work freely. ----
+    uint32_t champ0 = 0;
+    uint4 craw0 = ninf4;
+    uint32_t cw0[EPV];   // the champion vector's words
+    {
+        const Stream sk = stream_k(k0);
+        uint4 buf[D];
+        uint32_t ring[LAG + 1];   // slot keys between a slot's draw and its logits
+#pragma unroll
+        for (int n = 0; n < D; ++n) buf[n] = issue_load(n);
+#pragma unroll
+        for (int n = 0; n < NV + LAG; ++n) {
+            if (n < NV) ring[n % (LAG + 1)] = draw_vec(sk, n);
+            const int j = n - LAG;
+            if (j >= 0 && j < NV) {
+                const uint4 v = patch(j, buf[j % D]);
+                data_vec(j, v);
+                // the champion's vector stays in registers (no second read)
+                const uint32_t kj = ring[j % (LAG + 1)];
+                if (kj > champ0) {
+                    champ0 = kj;
+                    craw0 = v;
+                }
+                if (j + D < NV) buf[j % D] = issue_load(j + D);
+            }
+        }
+    }
+    if constexpr (LSE) {
+        // A lane whose largest logit lies more than 100 binary orders above or below its
+        // reference (never for logits of ordinary range) sums again against that maximum.
+        const float tm = xmax_lane * kLog2e;
+        if (xmax_lane > -__builtin_inff() && !(fabsf(tm - lse_r) <= 100.0f)) {
+            lse_r = tm;
+            lse_s = 0.0f;
+            lse_u = 0.0f;
+            for (int n = 0; n < NV; ++n) {
+                const uint4 v = fetch(lane_v + n * BS);
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) {
+                    const float t = __builtin_fmaf(elem<DT>(v, e), kLog2e, -lse_r);
+                    const float p = __builtin_amdgcn_exp2f(t);
+                    lse_s += p;
+                    if constexpr (PIV == 2)
+                        lse_u = (p > 0.0f) ? __builtin_fmaf(p, t, lse_u) : lse_u;
+                }
+            }
+        }
+    }
+
+    // ---- block combine: log-sum-exp (curve on), the largest logit, and the first draw's
+    // bootstrap candidate; wave 0 turns them into the row's constants, which reach every wave
+    // through LDS ----
+    RowConst rc;
+    rc.invT = invT;
+    rc.c = 0.0f;
+    rc.mt = rc.mtc = rc.mtw = 0.0f;
+    rc.curve = a.curve;
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    int wid = threadIdx.x >> 6;
+    asm volatile("" : "+v"(wid));
+    const int nw = (BS + 63) >> 6;
+    // Per wave, the best bootstrap candidate: its key, logit and word.
+    auto post_candidate = [&](const Cand &c) {
+        const uint64_t wk = wave_max_u64(c.key);
+        if (lane == 0) red_ck[wid] = wk;
+        if (wk != 0 && c.key == wk) {
+            red_cx[wid] = c.x;
+            red_cw[wid] = c.w;
+        }
+    };
+    // (wave 0) Exact score of the block's best candidate.
+    auto candidate_score = [&]() -> float {
+        const uint64_t bk = wave_max_u64(lane < nw ? red_ck[lane] : 0ull);
+        if (bk == 0) return -__builtin_inff();
+        const int bw = (int)((0xFFFFFFFFu - (uint32_t)bk) >> 6);
+        return exact_score<HLG>(uniform(red_cx[bw]),
+                                (uint32_t)__builtin_amdgcn_readfirstlane(red_cw[bw]), rc);
+    };
+    // (wave 0) The screen's constants from a lower bound bs on the draw's winning score:
+    // threshold thr = (bs - slack) / ln 2 - 1 in units of ln 2, and the coefficients with which
+    //   need(x) = min(max(x sa + sb, x ta + tb), sc)
+    // is the smallest word code n (leading ones) that lets a logit x reach it:
+    // thr - U(x) / ln 2, U(x) an upper bound on l'(x)/T. With the curve on,
+    //   U(x) = max(min(mid(x), tan(x)), -(m/T) w),
+    // where mid(x) = (m/T)(x - c) is the mid line (above the shoulder), tan the tangent of the
+    // concave shoulder at the chunk's largest logit (above the shoulder, and above the mid line
+    // left of the knot), and -(m/T) w the top of the toe; without the curve U(x) = x/T.
+    // No bound (no screening): every vector passes.
+    auto screen_consts = [&](float bs, float xtop, float *o) {
+        float thr = -3.0e38f;
+        if (bs > -__builtin_inff()) thr = (bs - screen_slack(bs)) * kInvLn2 - 1.0f;
+        o[0] = thr;
+        if constexpr (HLG) {
+            o[1] = -rc.mt * kInvLn2;
+            o[2] = __builtin_fmaf(rc.mtc, kInvLn2, thr);
+            o[3] = __builtin_fmaf(rc.mtw, kInvLn2, thr);
+            o[4] = o[1];
+            o[5] = o[2];
+            o[6] = 0.0f;
+            const float z0 = xtop - rc.c;
+            const float d = z0 - rc.curve.w;
+            const float bh = 1.0f / rc.curve.ibh;
+            // the tangent lies below the mid line at the top by m (d - b log(1 + d/b)) >=
+            // m d^2 / (2 (b + d)); it is only set up when that can pass 1.5 (units of ln 2)
+            if (d > 0.0f && rc.curve.w < __builtin_inff() &&
+                rc.curve.m * d * d * rc.invT * kInvLn2 > 3.0f * (bh + d)) {
+                const float g0 = rc.curve.mw + rc.curve.mbh * log1p_acc(d * rc.curve.ibh);
+                const float s0 = rc.curve.mbh / (bh + d);   // m b / (b + d)
+                // tan(x) = (s0 x + g0 - s0 (z0 + c)) / T
+                o[4] = -s0 * rc.invT * kInvLn2;
+                o[5] = __builtin_fmaf(__builtin_fmaf(-s0, xtop, g0) * rc.invT, -kInvLn2, thr);
+                // the vector screen pays two instructions per slot for the tangent: worth it
+                // when it lies well below the mid line at the top (in units of ln 2)
+                o[6] = ((rc.curve.m * z0 - g0) * rc.invT * kInvLn2 > 1.5f) ? 1.0f : 0.0f;
+            }
+        } else {
+            o[1] = -rc.invT * kInvLn2;
+            o[2] = thr;
+            o[3] = __builtin_inff();
+            o[4] = o[1];
+            o[5] = o[2];
+            o[6] = 0.0f;
+        }
+    };
+
+    if (screen) post_candidate(candidate(stream_k(k0), champ0, craw0, cw0));
+    {
+        const float xw = wave_max(xmax_lane);
+        float mw = 0.0f, sw = 0.0f, uw = 0.0f;
+        if constexpr (LSE) {
+            // each lane's sums moved to the wave's reference mw: s 2^(r - mw), and for the
+            // entropy anchor (u + s (r - mw)) 2^(r - mw)
+            mw = wave_max(lse_r);
+            const float sc = __builtin_amdgcn_exp2f(lse_r - mw);
+            sw = wave_sum(lse_s * sc);
+            if constexpr (PIV == 2)
+                uw = wave_sum(lse_s > 0.0f ? __builtin_fmaf(lse_s, lse_r - mw, lse_u) * sc : 0.0f);
+        }
+        if (lane == 0) {
+            red_x[wid] = xw;
+            if constexpr (LSE) {
+                red_m[wid] = mw;
+                red_s[wid] = sw;
+                red_u[wid] = uw;
+            }
+        }
+    }
+    __syncthreads();
+    if (wid == 0) {
+        const float xmb = wave_max(lane < nw ? red_x[lane] : -__builtin_inff());
+        float c = 0.0f;
+        bool ok = xmb > -__builtin_inff();   // the chunk has a finite logit
+        if constexpr (HLG) {
+            // the shift c of z = x - c: LSE + mu (given pivot), x_max - offset (top anchor),
+            // E_p[x] (entropy anchor), from this block's waves or the chunks' pre-pass
+            if (a.nchunk == 1) {
+                if constexpr (PIV == 1) {
+                    c = xmb - a.pivot_offset;
+                } else {
+                    const float pm = lane < nw ? red_m[lane] : -3.402823466e38f;
+                    const float mb = wave_max(pm);
+                    const float sc = lane < nw ? __builtin_amdgcn_exp2f(pm - mb) : 0.0f;
+                    const float sb = wave_sum(lane < nw ? red_s[lane] * sc : 0.0f);
+                    ok = sb > 0.0f;
+                    if constexpr (PIV == 0) {
+                        c = (mb + __builtin_amdgcn_logf(sb)) * kLn2 + mu;
+                    } else {
+                        const float ub = wave_sum(
+                            lane < nw && red_s[lane] > 0.0f
+                                ? __builtin_fmaf(red_s[lane], pm - mb, red_u[lane]) * sc : 0.0f);
+                        c = (mb + ub / sb) * kLn2;
+                    }
+                }
+            } else {
+                // the chunks' (max, sum, u) of the pre-pass, one per lane (nchunk <= 64), all
+                // read at once; natural units
+                const float4 pj = lane < a.nchunk ? a.partials[b * a.part_stride + lane]
+                                                  : make_float4(-__builtin_inff(), 0.0f, 0.0f, 0.0f);
+                const float Mb = wave_max(pj.x);
+                ok = Mb > -__builtin_inff();
+                if constexpr (PIV == 1) {
+                    c = Mb - a.pivot_offset;
+                } else {
+                    const float e = pj.x > -__builtin_inff() ? __builtin_amdgcn_exp2f((pj.x - Mb) * kLog2e) : 0.0f;
+                    const float Sb = wave_sum(pj.y * e);
+                    if constexpr (PIV == 0) {
+                        c = Mb + logf(Sb) + mu;
+                    } else {
+                        const float Ub = wave_sum(pj.x > -__builtin_inff()
+                                                      ? __builtin_fmaf(pj.y, pj.x - Mb, pj.z) * e : 0.0f);
+                        c = Mb + Ub / Sb;
+                    }
+                }
+            }
+            ok = ok && xmb > -__builtin_inff();
+            c = uniform(c);
+            rc.c = c;
+            rc.mt = uniform(a.curve.m * rc.invT);
+            rc.mtc = uniform(rc.mt * rc.c);
+            rc.mtw = uniform(rc.mt * a.curve.w);
+        }
+        float o[7] = {xmb, 0.0f, 0.0f, __builtin_inff(), 0.0f, 0.0f, 0.0f};
+        if (ok && screen) {
+            // lower bounds on the first draw's winning score: the best candidate's exact
+            // score, and from the chunk's largest logit (its curve value is at least
+            // (m/T) min(x - c, w) -- the toe lies above its mid line, the shoulder above m w --
+            // and every Gumbel value is at least G(0) > -3.14)
+            float lbx;
+            if constexpr (HLG) {
+                lbx = fminf(xmb - rc.c, rc.curve.w) * rc.mt - 3.14f;
+            } else {
+                lbx = xmb * rc.invT - 3.14f;
+            }
+            screen_consts(uniform(fmaxf(candidate_score(), lbx)), xmb, o);
+        } else if (ok && sampled) {
+            screen_consts(-__builtin_inff(), xmb, o);
+        }
+        if (lane == 0) {
+            row_bc[0] = xmb;
+            row_bc[1] = c;
+            row_bc[2] = ok ? 1.0f : 0.0f;
+            row_bc[3] = o[0];
+            row_bc[4] = o[1];
+            row_bc[5] = o[2];
+            row_bc[6] = o[3];
+            row_bc[7] = o[4];
+            row_bc[8] = o[5];
+            row_bc[9] = o[6];
+        }
+    }
+    __syncthreads();
+    const float xmax_blk = uniform(row_bc[0]);
+    const bool skip = bad || !(uniform(row_bc[2]) > 0.0f);
+    if constexpr (HLG) {
+        rc.c = uniform(row_bc[1]);
+        rc.mt = uniform(a.curve.m * rc.invT);
+        rc.mtc = uniform(rc.mt * rc.c);
+        rc.mtw = uniform(rc.mt * a.curve.w);
+    }
+    float sa = uniform(row_bc[4]), sb = uniform(row_bc[5]), sc = uniform(row_bc[6]);
+    float ta = uniform(row_bc[7]), tb = uniform(row_bc[8]);
+    bool tan_on = uniform(row_bc[9]) > 0.0f;
+    auto code_needed = [&](float x) -> float {
+        return fminf(fmaxf(__builtin_fmaf(x, sa, sb), __builtin_fmaf(x, ta, tb)), sc);
+    };
+    // Exact scores of the elements of slot n (vector v, words w) that pass their own bound,
+    // folded into the draw's best key.
+    auto score_words = [&](int n, const uint4 &v, const uint32_t (&w)[EPV],
+                           uint64_t best) -> uint64_t {
+        const int gv = lane_v + n * BS;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+            const float x = elem<DT>(v, e);
+            const float cf = (float)__clz(~w[e]);
+            if (x > -__builtin_inff() && cf >= code_needed(x)) {
+                const uint32_t i = (uint32_t)gv * EPV + e;
+                best = umax64(best, make_key(exact_score<HLG>(x, w[e], rc), i));
+            }
+        }
+        return best;
+    };
+    // The same for a vector read again: its words are drawn again; greedy rows compare logits.
+    auto score_vec = [&](const Stream &sk, int n, const uint4 &v, uint64_t best) -> uint64_t {
+        const int gv = lane_v + n * BS;
+        if (greedy) return greedy_vec<DT>(v, (uint32_t)gv * EPV, best);
+        uint32_t q = (uint32_t)gv * NG;
+        asm volatile("" : "+v"(q));
+        uint32_t w[EPV];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const Words4 ww = philox4x32_10_uk(q + g, sk.row, sk.off_lo, sk.off_hi, sk.key0,
+                                               sk.key1);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[4 * g + e] = ww.w[e];
+        }
+        return score_words(n, v, w, best);
+    };
+
+    for (int k = k0; k < k1; ++k) {
+        asm volatile("" : "+v"(lane_lds));
+        asm volatile("" : "+v"(lane_v));
+        const Stream sk = stream_k(k);
+        uint32_t champ = champ0;
+        if (k > k0 && !skip && screen) {
+            // this draw's words, champions and bootstrap candidate (two more barriers)
+            champ = draw_all(sk);
+            craw0 = fetch(lane_v + (int)(champ & 31u) * BS);
+            post_candidate(candidate(sk, champ, craw0, cw0));
+            __syncthreads();
+            if (wid == 0) {
+                float lbx;
+                if constexpr (HLG) {
+                    lbx = fminf(xmax_blk - rc.c, rc.curve.w) * rc.mt - 3.14f;
+                } else {
+                    lbx = xmax_blk * rc.invT - 3.14f;
+                }
+                float o[7];
+                screen_consts(uniform(fmaxf(candidate_score(), lbx)), xmax_blk, o);
+                if (lane == 0) {
+                    row_bc[3] = o[0];
+                    row_bc[4] = o[1];
+                    row_bc[5] = o[2];
+                    row_bc[6] = o[3];
+                    row_bc[7] = o[4];
+                    row_bc[8] = o[5];
+                    row_bc[9] = o[6];
+                }
+            }
+            __syncthreads();
+            sa = uniform(row_bc[4]);
+            sb = uniform(row_bc[5]);
+            sc = uniform(row_bc[6]);
+            ta = uniform(row_bc[7]);
+            tb = uniform(row_bc[8]);
+            tan_on = uniform(row_bc[9]) > 0.0f;
+        }
+        uint64_t best = 0;
+        if (!skip) {
+            // Screen: a vector can hold a winner only if U(its largest logit) + (n + 1) ln 2
+            // reaches the bound less the slack, where n counts the leading ones of its largest
+            // word's high 16 bits (n = 16 leaves the word unbounded); for greedy rows, only if
+            // its largest logit reaches the chunk's. The champion vector and its words are at
+            // hand from the bootstrap; the other vectors that pass (rare) are read again two at a
+            // time, so their loads overlap.
+            uint32_t bits = 0;   // bit n: slot n passes
+            if (greedy) {
+#pragma unroll
+                for (int n = NV - 1; n >= 0; --n) {
+                    const float xm = __uint_as_float(s_vec[lane_lds + n] << 16);
+                    bits = (bits << 1) | (xm >= xmax_blk ? 1u : 0u);
+                }
+            } else if (tan_on) {
+#pragma unroll
+                for (int n = NV - 1; n >= 0; --n) {
+                    const uint32_t d = s_vec[lane_lds + n];
+                    const float xm = __uint_as_float(d << 16);
+                    // a needed code above 16 is met only by n = 16, which stands for any word
+                    // (so the cap keeps such vectors)
+                    const float need = fminf(code_needed(xm), 16.0f);
+                    bits = (bits << 1) | ((float)lead_ones_hi16(d) >= need ? 1u : 0u);
+                }
+            } else {
+                // the same with the mid line alone (also an upper bound)
+#pragma unroll
+                for (int n = NV - 1; n >= 0; --n) {
+                    const uint32_t d = s_vec[lane_lds + n];
+                    const float xm = __uint_as_float(d << 16);
+                    const float need = fminf(fminf(__builtin_fmaf(xm, sa, sb), sc), 16.0f);
+                    bits = (bits << 1) | ((float)lead_ones_hi16(d) >= need ? 1u : 0u);
+                }
+            }
+            if (screen) {   // champ and craw0 belong to this draw
+                const uint32_t cbit = 1u << (champ & 31u);
+                if (bits & cbit) {
+                    bits &= ~cbit;
+                    best = score_words((int)(champ & 31u), craw0, cw0, best);
+                }
+            }
+            while (bits) {
+                const int n1 = __builtin_ctz(bits);
+                bits &= bits - 1u;
+                const bool two = bits != 0u;
+                const int n2 = two ? __builtin_ctz(bits) : n1;
+                if (two) bits &= bits - 1u;
+                const uint4 v1 = fetch(lane_v + n1 * BS);
+                const uint4 v2 = two ? fetch(lane_v + n2 * BS) : ninf4;
+                best = score_vec(sk, n1, v1, best);
+                if (two) best = score_vec(sk, n2, v2, best);
+            }
+        }
+        // block maximum of the draw's key: waves post their maxima, wave 0 writes the result
+        {
+            uint64_t *rd = red_draw[(k - k0) & 1];
+            const uint64_t wk = wave_max_u64(best);
+            if (lane == 0) rd[wid] = wk;
+            __syncthreads();
+            if (wid == 0) {
+                const uint64_t kb = wave_max_u64(lane < nw ? rd[lane] : 0ull);
+                if (lane == 0) {
+                    const int64_t o = b * a.K + k;
+                    if (a.nchunk == 1) {
+                        a.out[o] = bad ? -2 : key_index(kb);
+                        if (a.best_out) a.best_out[o] = bad ? -__builtin_inff() : key_score(kb);
+                    } else if (kb != 0) {
+                        __hip_atomic_fetch_max(a.keys + o, kb, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+            }
+        }
+    }
+
+    // ---- split rows: the last block of the row writes the ids and re-zeroes its slots ----
+    if (a.nchunk > 1) {
+        // The keys and counters of split rows are only ever touched by agent-scope atomics, so
+        // no fence is needed: an agent-scope fence writes back and invalidates the whole L2,
+        // which stalls every load in flight on the device. Thread 0, which made this block's
+        // maxima, waits for them to complete before it counts the block in; the block that
+        // counts last reads the keys after that, with atomic loads.
+        if (tid == 0) {
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_s_waitcnt(0);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            const unsigned prev = __hip_atomic_fetch_add(a.counters + b, 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            s_last = (prev == (unsigned)(a.nchunk * a.nkg - 1));
+        }
+        __syncthreads();
+        if (s_last) {
+            for (int k = tid; k < a.K; k += BS) {
+                const int64_t o = b * a.K + k;
+                const uint64_t kk = __hip_atomic_load(a.keys + o, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+                a.out[o] = bad ? -2 : key_index(kk);
+                if (a.best_out) a.best_out[o] = bad ? -__builtin_inff() : key_score(kk);
+                __hip_atomic_store(a.keys + o, (uint64_t)0, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if (tid == 0)
+                __hip_atomic_store(a.counters + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// Per-chunk (max, sum exp(x - max), sum exp(x - max) (x - max)) for rows split over several
+// blocks, in one read: each thread keeps a running maximum in base 2 and rescales its sums
+// when it moves; the block combines them. The top anchor needs only the maximum; only the
+// entropy anchor needs the third sum.
+template <int DT, int PIV>
+__global__ __launch_bounds__(1024) void k_lse_partial(SampleArgs a) {
+    using tr = dtype_traits<DT>;
+    constexpr int EPV = tr::epv;
+    __shared__ float red_m[16], red_s[16], red_u[16];
+    const int chunk = blockIdx.x % a.nchunk;
+    const int64_t b = blockIdx.x / a.nchunk;
+    const int64_t v0 = (int64_t)chunk * a.cv;
+    const int64_t vend = min(a.nvec, v0 + a.cv);
+    const char *rowp = reinterpret_cast<const char *>(a.data) + b * a.ld * tr::esize;
+    float m = -3.402823466e38f, s = 0.0f, u = 0.0f;   // base 2: m a maximum of x log2(e)
+    for (int64_t gv = v0 + threadIdx.x; gv < vend; gv += blockDim.x) {
+        const uint4 v = load_vec<DT>(rowp, gv, a.V, a.aligned);
+        float xv[EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) xv[e] = elem<DT>(v, e);
+        const float mv = vec_max<EPV>(xv) * kLog2e;
+        if constexpr (PIV == 1) {
+            m = fmaxf(m, mv);
+        } else {
+            if (mv > m) {
+                const float sc = __builtin_amdgcn_exp2f(m - mv);
+                if constexpr (PIV == 2) u = __builtin_fmaf(s, m - mv, u) * sc;
+                s *= sc;
+                m = mv;
+            }
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                const float t = __builtin_fmaf(xv[e], kLog2e, -m);
+                const float p = __builtin_amdgcn_exp2f(t);
+                s += p;
+                if constexpr (PIV == 2) u = (p > 0.0f) ? __builtin_fmaf(p, t, u) : u;
+            }
+        }
+    }
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int nw = (blockDim.x + 63) >> 6;
+    const float mw = wave_max(m);
+    const float sc = __builtin_amdgcn_exp2f(m - mw);
+    const float sw = wave_sum(s * sc);
+    const float uw = (PIV == 2) ? wave_sum(s > 0.0f ? __builtin_fmaf(s, m - mw, u) * sc : 0.0f) : 0.0f;
+    if (lane == 0) {
+        red_m[wid] = mw;
+        red_s[wid] = sw;
+        red_u[wid] = uw;
+    }
+    __syncthreads();
+    if (wid == 0) {
+        const float pm = lane < nw ? red_m[lane] : -3.402823466e38f;
+        const float mb = wave_max(pm);
+        const float sb_ = lane < nw ? __builtin_amdgcn_exp2f(pm - mb) : 0.0f;
+        const float S = wave_sum(lane < nw ? red_s[lane] * sb_ : 0.0f);
+        const float U = (PIV == 2) ? wave_sum(lane < nw && red_s[lane] > 0.0f
+                                                  ? __builtin_fmaf(red_s[lane], pm - mb, red_u[lane]) * sb_
+                                                  : 0.0f)
+                                   : 0.0f;
+        if (lane == 0) {
+            const bool fin = (PIV == 1) ? (mb > -1.0e38f) : (S > 0.0f);
+            // natural units: max, sum exp(x - max), sum exp(x - max) (x - max)
+            a.partials[b * a.part_stride + chunk] =
+                make_float4(fin ? mb * kLn2 : -__builtin_inff(), fin ? S : 0.0f,
+                            fin ? U * kLn2 : 0.0f, 0.0f);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Launchers, instantiated by the translation units that include this header.
+// ------------------------------------------------------------------------------------------
+template <int DT, bool HLG, int PIV, bool AL>
+hipError_t launch_sample_nv(const SampleArgs &a, int nv, int bs, int grid, hipStream_t s) {
+    // blocks of up to 1024 threads, nv slots of 16-byte vectors per thread; the dynamic LDS
+    // holds one dword per lane and slot
+#define HS_CASE(N, MB)                                                                     \
+    case N:                                                                                \
+        if (bs > MB) return hipErrorInvalidValue;                                          \
+        hipLaunchKernelGGL((k_sample<DT, N, HLG, PIV, MB, AL>), dim3(grid), dim3(bs),     \
+                           (size_t)(N | 1) * bs * 4, s, a);                               \
+        break;
+    switch (nv) {
+        HS_CASE(1, 1024) HS_CASE(2, 1024) HS_CASE(4, 1024) HS_CASE(6, 1024) HS_CASE(8, 1024)
+        HS_CASE(12, 1024) HS_CASE(16, 1024) HS_CASE(19, 1024)
+        default: return hipErrorInvalidValue;
+    }
+#undef HS_CASE
+    return hipGetLastError();
+}
+
+template <int DT, bool HLG, int PIV>
+hipError_t launch_sample_al(const SampleArgs &a, int nv, int bs, int grid, hipStream_t s) {
+    // the branch-free load path needs 16-byte aligned rows holding at least one full vector
+    if (a.aligned && a.V >= dtype_traits<DT>::epv)
+        return launch_sample_nv<DT, HLG, PIV, true>(a, nv, bs, grid, s);
+    return launch_sample_nv<DT, HLG, PIV, false>(a, nv, bs, grid, s);
+}
+
+template <int PIV>
+hipError_t launch_lse_partial_t(int dt, const SampleArgs &a, int bs, int grid, hipStream_t s) {
+    switch (dt) {
+        case DT_F32: hipLaunchKernelGGL((k_lse_partial<DT_F32, PIV>), dim3(grid), dim3(bs), 0, s, a); break;
+        case DT_BF16: hipLaunchKernelGGL((k_lse_partial<DT_BF16, PIV>), dim3(grid), dim3(bs), 0, s, a); break;
+        case DT_F16: hipLaunchKernelGGL((k_lse_partial<DT_F16, PIV>), dim3(grid), dim3(bs), 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace hs

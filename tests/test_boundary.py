@@ -55,8 +55,8 @@ def L(B=4, V=100, ld=None, dtype=0, data=FAKE):
     return hs._Logits(data, dtype, B, V, V if ld is None else ld)
 
 
-def H(m=1.5, w=2.0, bt=1.0, bh=2.0):
-    return hs.HlgParams(m, w, bt, bh)
+def H(m=1.5, w=2.0, bt=1.0, bh=2.0, pivot=0, off=0.0):
+    return hs.HlgParams(m, w, bt, bh, pivot, off)
 
 
 def sample(lib, x, T=FAKE, mu=FAKE, hlg=None, seed=FAKE, off=FAKE, K=1, out=FAKE, ws=None,
@@ -81,6 +81,7 @@ def test_bad_logits(lib, x, code):
     assert lib.hs_logsumexp(C.byref(x), FAKE, None) == code
     h = H()
     assert lib.hs_hlg_transform(C.byref(x), FAKE, C.byref(h), FAKE, max(x.V, 1), None) == code
+    assert lib.hs_hlg_pivot(C.byref(x), FAKE, C.byref(h), FAKE, None) == code
 
 
 def test_null_logits_struct(lib):
@@ -96,15 +97,46 @@ def test_bad_sample_args(lib, kw):
 
 @pytest.mark.parametrize("h", [H(m=0.0), H(m=-1.0), H(m=math.inf), H(m=math.nan), H(w=-0.5),
                                H(w=math.nan), H(bt=0.0), H(bt=math.inf), H(bh=-1.0),
-                               H(bh=math.nan)])
+                               H(bh=math.nan), H(pivot=3), H(pivot=-1),
+                               H(pivot=1, off=math.inf), H(pivot=1, off=math.nan)])
 def test_bad_curve(lib, h):
     assert sample(lib, L(), hlg=h) == HS_ERR_INVALID_ARG
     x = L()
     assert lib.hs_hlg_transform(C.byref(x), FAKE, C.byref(h), FAKE, 100, None) == HS_ERR_INVALID_ARG
+    assert lib.hs_hlg_pivot(C.byref(x), FAKE, C.byref(h), FAKE, None) == HS_ERR_INVALID_ARG
 
 
 def test_curve_needs_mu(lib):
     assert sample(lib, L(), hlg=H(), mu=None) == HS_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("pivot,off", [(1, 0.0), (1, -3.5), (2, 0.0), (2, math.nan)])
+def test_anchored_pivots_need_no_mu(lib, pivot, off):
+    """Top- and entropy-anchored pivots are derived from the row [HLG, The pivot]: no mu is
+    needed, and the entropy anchor ignores the offset. With a too-small workspace the call
+    gets as far as the workspace check."""
+    h = H(pivot=pivot, off=off)
+    assert sample(lib, L(), hlg=h, mu=None, ws=FAKE, nbytes=8) == HS_ERR_WORKSPACE
+    x = L()
+    assert lib.hs_hlg_transform(C.byref(x), None, C.byref(h), None, 100, None) == HS_ERR_INVALID_ARG
+    assert lib.hs_hlg_pivot(C.byref(x), None, C.byref(h), None, None) == HS_ERR_INVALID_ARG
+
+
+def test_pivot_args(lib):
+    x = L()
+    assert lib.hs_hlg_pivot(C.byref(x), None, C.byref(H()), FAKE, None) == HS_ERR_INVALID_ARG
+    assert lib.hs_hlg_pivot(C.byref(x), FAKE, None, FAKE, None) == HS_ERR_INVALID_ARG
+    assert lib.hs_hlg_pivot(C.byref(x), FAKE, C.byref(H()), None, None) == HS_ERR_INVALID_ARG
+
+
+def test_binding_pivot_modes():
+    assert hs._hlg_struct({"m": 1.0, "w": 1.0, "beta_t": 1.0, "beta_h": 1.0,
+                           "pivot": "entropy"}).pivot == 2
+    h = hs._hlg_struct((1.0, 2.0, 1.0, 1.0, "top", -2.5))
+    assert (h.pivot, h.pivot_offset) == (1, -2.5)
+    assert hs._hlg_struct((1.0, 2.0, 1.0, 1.0)).pivot == 0
+    with pytest.raises(ValueError):
+        hs._hlg_struct((1.0, 2.0, 1.0, 1.0, "median"))
 
 
 def test_rolloff_off_is_accepted_by_validation(lib):
