@@ -79,7 +79,7 @@ struct WsLayout {
 WsLayout ws_layout(int64_t B, int32_t K) {
     WsLayout L;
     L.counters = 0;
-    L.keys = align256((size_t)B * 4);
+    L.keys = align256((size_t)B * (size_t)K * 4);   // counters: one per (row, draw group)
     L.partials = L.keys + align256((size_t)B * (size_t)K * 8);
     L.total = L.partials + align256((size_t)B * hs::kMaxChunks * sizeof(float4));
     return L;
@@ -102,30 +102,46 @@ bool pick_block(int64_t cv, int *bs, int *nv) {
     return false;
 }
 
-// Kernel shape for a call. Rows that fit one block (kBlockCapacity vectors) keep one block
-// per row, so each row is read once, unless the batch would leave more than half of the
-// CUs idle; then rows are split into chunks of >= 512 vectors (aiming at two blocks per CU).
-// A grid that is still small spreads a row's draws over several blocks.
-int make_plan(const hs_logits *x, int32_t K, bool ws_ok, const hs_sample_opts *o, Plan *P) {
+// Kernel shape for a call. A row's draws are spread over blocks first ("draw groups": blocks
+// that share a chunk of the row but not its draws need no cross-block combine), up to about one
+// block per CU. Only if that leaves more than half of the CUs idle are rows split into chunks
+// (at most 32, of at least 256 vectors), aiming at one block per CU with the curve on (its
+// log-sum-exp pre-pass is split too) and at one per two CUs without it (each chunk then adds
+// only its share of the cross-block combine); the chunks' maxima meet in the workspace. Rows
+// longer than one block holds (kBlockCapacity vectors) are always split.
+int make_plan(const hs_logits *x, int32_t K, bool hlg, bool ws_ok, const hs_sample_opts *o,
+              Plan *P) {
     const int64_t B = x->B;
     const int64_t nvec = (x->V + epv_of(x->dtype) - 1) / epv_of(x->dtype);
     const int64_t cap = kBlockCapacity;
     const int64_t nchunk_min = (nvec + cap - 1) / cap;
-    const int64_t target = 2 * (int64_t)num_cus();
-    int64_t nchunk = nchunk_min;
+    const int64_t cus = (int64_t)num_cus();
     const int variant = o ? o->variant : 0;
+    const int64_t groups_given = (o && o->draw_groups > 0) ? o->draw_groups : 0;
+    auto groups_for = [&](int64_t nchunk) -> int64_t {
+        if (groups_given) return groups_given;
+        int64_t g = (cus + B * nchunk - 1) / (B * nchunk);
+        if (g > K) g = K;
+        return g < 1 ? 1 : g;
+    };
+    int64_t nchunk = nchunk_min;
     if (variant == 1) {
         if (nchunk_min > 1) return HS_ERR_UNSUPPORTED;
         nchunk = 1;
     } else if (variant == 2 && o->nchunk > 0) {
         nchunk = o->nchunk;
-    } else if (variant == 2 || (ws_ok && 2 * B * nchunk_min < (int64_t)num_cus())) {
-        int64_t want = (target + B - 1) / B;
-        int64_t lim = nvec / 512;
-        if (lim < 1) lim = 1;
-        nchunk = want < lim ? want : lim;
-        if (nchunk < nchunk_min) nchunk = nchunk_min;
-        if (variant == 2 && nchunk < 2 && nvec >= 2) nchunk = 2;
+    } else {
+        const int64_t g = groups_for(nchunk_min);
+        if (variant == 2 || (ws_ok && 2 * B * nchunk_min * g < cus)) {
+            const int64_t target = hlg ? cus : cus / 2;
+            int64_t want = (target + B * g - 1) / (B * g);
+            int64_t lim = nvec / 256;
+            if (lim > 32) lim = 32;
+            if (lim < 1) lim = 1;
+            nchunk = want < lim ? want : lim;
+            if (nchunk < nchunk_min) nchunk = nchunk_min;
+            if (variant == 2 && nchunk < 2 && nvec >= 2) nchunk = 2;
+        }
     }
     if (nchunk > hs::kMaxChunks) nchunk = hs::kMaxChunks;
     if (nchunk > nvec) nchunk = nvec;
@@ -136,12 +152,7 @@ int make_plan(const hs_logits *x, int32_t K, bool ws_ok, const hs_sample_opts *o
     if (nchunk > 1 && !ws_ok) return HS_ERR_WORKSPACE;
     int bs = 0, nv = 0;
     if (!pick_block(cv, &bs, &nv)) return HS_ERR_UNSUPPORTED;
-    int64_t nkg = 1;
-    if (o && o->draw_groups > 0) {
-        nkg = o->draw_groups;
-    } else if (K > 1 && B * nchunk < target) {
-        nkg = (target + B * nchunk - 1) / (B * nchunk);
-    }
+    int64_t nkg = groups_for(nchunk);
     if (nkg > K) nkg = K;
     int64_t kpg = (K + nkg - 1) / nkg;
     nkg = (K + kpg - 1) / kpg;
@@ -179,7 +190,7 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
         return HS_ERR_INVALID_ARG;
     }
     Plan P;
-    rc = make_plan(x, K, ws_ok, opts, &P);
+    rc = make_plan(x, K, hlg != nullptr, ws_ok, opts, &P);
     if (rc) return rc;
 
     SampleArgs a{};

@@ -33,7 +33,7 @@ struct SampleArgs {
     float *best_out;
     Curve curve;
     // workspace (split rows only)
-    uint32_t *counters;        // [B]
+    uint32_t *counters;        // [B * nkg]: blocks done per (row, draw group)
     uint64_t *keys;            // [B * K]
     float4 *partials;          // [B * part_stride]: per chunk (max, sum, u, -) in nats
     int64_t part_stride;

@@ -752,7 +752,8 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
         }
     }
 
-    // ---- split rows: the last block of the row writes the ids and re-zeroes its slots ----
+    // ---- split rows: of the blocks that share this row's draws k0..k1-1 (one per chunk), the
+    // last to finish writes their ids and re-zeroes their slots ----
     if (a.nchunk > 1) {
         // The keys and counters of split rows are only ever touched by agent-scope atomics, so
         // no fence is needed: an agent-scope fence writes back and invalidates the whole L2,
@@ -763,13 +764,13 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             __builtin_amdgcn_s_waitcnt(0);
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            const unsigned prev = __hip_atomic_fetch_add(a.counters + b, 1u, __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT);
-            s_last = (prev == (unsigned)(a.nchunk * a.nkg - 1));
+            const unsigned prev = __hip_atomic_fetch_add(a.counters + b * a.nkg + kg, 1u,
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = (prev == (unsigned)(a.nchunk - 1));
         }
         __syncthreads();
         if (s_last) {
-            for (int k = tid; k < a.K; k += BS) {
+            for (int k = k0 + tid; k < k1; k += BS) {
                 const int64_t o = b * a.K + k;
                 const uint64_t kk = __hip_atomic_load(a.keys + o, __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT);
@@ -779,7 +780,8 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                                    __HIP_MEMORY_SCOPE_AGENT);
             }
             if (tid == 0)
-                __hip_atomic_store(a.counters + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(a.counters + b * a.nkg + kg, 0u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }

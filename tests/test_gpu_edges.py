@@ -116,7 +116,8 @@ def test_variant_invariance(hs, oracle_mod, hlg):
                        ("split64", hs.SampleOpts(variant=2, nchunk=64)),
                        ("one-block-exhaustive", hs.SampleOpts(variant=1, no_screen=1)),
                        ("split7-exhaustive", hs.SampleOpts(variant=2, nchunk=7, no_screen=1)),
-                       ("draw-groups", hs.SampleOpts(variant=1, draw_groups=3))]:
+                       ("draw-groups", hs.SampleOpts(variant=1, draw_groups=3)),
+                       ("split5-draw-groups", hs.SampleOpts(variant=2, nchunk=5, draw_groups=2))]:
         idx, best = hs.sample_ex(d["logits"], d["T"], d["seed"], d["offset"], mu=d.get("mu"),
                                  hlg=hlg, k=3, opts=opts, want_best=True)
         idx = idx.cpu().numpy()
