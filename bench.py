@@ -43,8 +43,8 @@ def log(*a):
 
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("hs_kernels.hip", "hs_kernels_pivot.hip", "hs_sample_kernel.hpp", "hs_device.hpp",
-              "hs_api.hip", "hs_internal.hpp"):
+    for f in ("hs_kernels.hip", "hs_kernels_pivot.hip", "hs_kernels_rows.hip",
+              "hs_sample_kernel.hpp", "hs_device.hpp", "hs_api.hip", "hs_internal.hpp"):
         with open(os.path.join(ROOT, "logit_transform_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -127,6 +127,20 @@ int hs_sample(const hs_logits *x, const float *T, const float *mu, const hs_hlg_
               const uint64_t *seed, const uint64_t *offset, int32_t K, int32_t *out,
               void *ws, size_t ws_bytes, void *stream);
 
+/* Per-row curve settings for hs_sample_rows, one per row in device memory (32 bytes):
+ * the knobs and pivot of hs_hlg_params, and whether the curve is on for the row
+ * [HLG, The pivot; Knobs: one setting per request]. */
+typedef struct {
+    float m;
+    float w;
+    float beta_t;
+    float beta_h;
+    int32_t pivot;        /* hs_pivot */
+    float pivot_offset;   /* c of HS_PIVOT_TOP */
+    int32_t enabled;      /* 0: curve off for this row (l' = x) */
+    int32_t reserved;     /* must be 0 */
+} hs_hlg_row;
+
 /* Workspace bytes the multi-block-per-row kernels of hs_sample / hs_gumbel_argmax need for
  * this shape (0 on invalid arguments). */
 size_t hs_workspace_bytes(int64_t B, int64_t V, int32_t K, int32_t dtype, int32_t hlg_on);
@@ -150,6 +164,21 @@ int hs_sample_ex(const hs_logits *x, const float *T, const float *mu,
                  const hs_hlg_params *hlg, const uint64_t *seed, const uint64_t *offset,
                  int32_t K, int32_t *out, float *best, void *ws, size_t ws_bytes,
                  const hs_sample_opts *opts, void *stream);
+
+/* hs_sample_ex with the curve set per row: row b is sampled as hs_sample_ex would sample it
+ * alone with hlg = NULL (rows[b].enabled == 0) or with the curve of rows[b] (otherwise), in one
+ * launch [HLG, The transfer function; The pivot; GMX, Background]. Per-row parameters are
+ * validated in the kernel: a row whose enabled curve has an invalid knob (the rules of
+ * hs_hlg_params), an unknown pivot, a non-finite top offset or a non-zero reserved field gives
+ * -2, as does a given-pivot row whose mu is not finite or whose mu array is NULL. mu: device
+ * float[B] or NULL (read only for enabled rows with HS_PIVOT_GIVEN); rows: device
+ * hs_hlg_row[B]. Ids and scores of a row are bit-identical to hs_sample_ex's for that row's
+ * setting. The workspace size is hs_workspace_bytes(B, V, K, dtype, 1). best and opts as
+ * hs_sample_ex (NULL allowed). */
+int hs_sample_rows(const hs_logits *x, const float *T, const float *mu, const hs_hlg_row *rows,
+                   const uint64_t *seed, const uint64_t *offset, int32_t K, int32_t *out,
+                   float *best, void *ws, size_t ws_bytes, const hs_sample_opts *opts,
+                   void *stream);
 
 /* Philox4x32-10 [P123] on n (counter, key) pairs: ctr device uint32[4n], key device
  * uint32[2n], out device uint32[4n]. Uses the same device routine as the samplers. */

@@ -18,7 +18,8 @@ import torch
 
 __all__ = [
     "HsError", "HlgParams", "SampleOpts", "load", "library_path", "EXPORTED_SYMBOLS",
-    "sample", "sample_ex", "gumbel_argmax", "logsumexp", "hlg_transform", "hlg_pivot",
+    "sample", "sample_ex", "sample_rows", "hlg_rows", "gumbel_argmax", "logsumexp",
+    "hlg_transform", "hlg_pivot",
     "workspace_bytes", "PIVOTS",
     "workspace", "philox4x32_10", "stream_words", "gumbel_f32", "version",
 ]
@@ -31,7 +32,7 @@ _DTYPES = {torch.float32: HS_F32, torch.bfloat16: HS_BF16, torch.float16: HS_F16
 
 EXPORTED_SYMBOLS = (
     "hs_logsumexp", "hs_hlg_transform", "hs_hlg_pivot", "hs_gumbel_argmax", "hs_sample",
-    "hs_sample_ex",
+    "hs_sample_ex", "hs_sample_rows",
     "hs_workspace_bytes", "hs_workspace_init", "hs_philox4x32_10", "hs_stream_words",
     "hs_gumbel_f32", "hs_status_str", "hs_version",
 )
@@ -55,6 +56,13 @@ class HlgParams(C.Structure):
     offset c."""
     _fields_ = [("m", C.c_float), ("w", C.c_float), ("beta_t", C.c_float),
                 ("beta_h", C.c_float), ("pivot", C.c_int32), ("pivot_offset", C.c_float)]
+
+
+class HlgRow(C.Structure):
+    """One row's curve setting for sample_rows (32 bytes, device array of B)."""
+    _fields_ = [("m", C.c_float), ("w", C.c_float), ("beta_t", C.c_float),
+                ("beta_h", C.c_float), ("pivot", C.c_int32), ("pivot_offset", C.c_float),
+                ("enabled", C.c_int32), ("reserved", C.c_int32)]
 
 
 # Where the curve's pivot comes from: given per row (mu), top-anchored (mu = l_max - c),
@@ -104,6 +112,7 @@ def load() -> C.CDLL:
     L.hs_gumbel_argmax.argtypes = [LP, vp, vp, vp, i32, vp, vp, sz, vp]
     L.hs_sample.argtypes = [LP, vp, vp, HP, vp, vp, i32, vp, vp, sz, vp]
     L.hs_sample_ex.argtypes = [LP, vp, vp, HP, vp, vp, i32, vp, vp, vp, sz, OP, vp]
+    L.hs_sample_rows.argtypes = [LP, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, OP, vp]
     L.hs_workspace_bytes.argtypes = [i64, i64, i32, i32, i32]
     L.hs_workspace_bytes.restype = sz
     L.hs_workspace_init.argtypes = [vp, sz, vp]
@@ -115,7 +124,7 @@ def load() -> C.CDLL:
     L.hs_version.argtypes = []
     L.hs_version.restype = C.c_char_p
     for name in ("hs_logsumexp", "hs_hlg_transform", "hs_hlg_pivot", "hs_gumbel_argmax", "hs_sample",
-                 "hs_sample_ex", "hs_workspace_init", "hs_philox4x32_10", "hs_stream_words",
+                 "hs_sample_ex", "hs_sample_rows", "hs_workspace_init", "hs_philox4x32_10", "hs_stream_words",
                  "hs_gumbel_f32"):
         getattr(L, name).restype = C.c_int
     _lib = L
@@ -271,6 +280,58 @@ def sample(logits: torch.Tensor, T, seed, offset, *, mu=None, hlg=None, k: int =
                      ws.numel(), _stream(dev))
     _check(rc, "hs_sample")
     return out
+
+
+def hlg_rows(settings: Sequence, device=None) -> torch.Tensor:
+    """Packs per-row curve settings for sample_rows into a device tensor (uint8 [B, 32]).
+    Each entry is None (curve off for the row) or what `hlg` accepts elsewhere: a mapping with
+    m, w, beta_t, beta_h and optionally pivot, pivot_offset, or a tuple
+    (m, w, beta_t, beta_h[, pivot, pivot_offset])."""
+    raw = torch.frombuffer(bytearray(bytes(_pack_rows(settings))), dtype=torch.uint8)
+    return raw.reshape(len(settings), 32).to(torch.device(device or "cuda"))
+
+
+def _pack_rows(settings: Sequence):
+    arr = (HlgRow * len(settings))()
+    for i, h in enumerate(settings):
+        if h is None:
+            arr[i] = HlgRow(1.0, 0.0, 1.0, 1.0, 0, 0.0, 0, 0)
+        else:
+            p = _hlg_struct(h)
+            arr[i] = HlgRow(p.m, p.w, p.beta_t, p.beta_h, p.pivot, p.pivot_offset, 1, 0)
+    return arr
+
+
+def sample_rows(logits: torch.Tensor, T, seed, offset, rows, *, mu=None, k: int = 1,
+                out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                opts: Optional[SampleOpts] = None, want_best: bool = False):
+    """The sampling step with the curve set per row: rows is a device tensor from hlg_rows (or
+    a sequence it accepts). mu [B] is read only for rows whose curve is on with the pivot given
+    (it may be None otherwise: such rows then give -2). Ids [B, k] (int32) and, with
+    want_best, the winning scores."""
+    L = load()
+    x = _logits_struct(logits)
+    dev = logits.device
+    B = logits.shape[0]
+    if not isinstance(rows, torch.Tensor):
+        rows = hlg_rows(rows, dev)
+    _require_gpu(rows, "rows")
+    if rows.dtype != torch.uint8 or tuple(rows.shape) != (B, 32) or not rows.is_contiguous():
+        raise ValueError("rows must be a contiguous uint8 [B, 32] tensor (see hlg_rows)")
+    Tt = _row_vec(T, B, torch.float32, dev, "T")
+    st = _row_vec(seed, B, torch.int64, dev, "seed")
+    of = _row_vec(offset, B, torch.int64, dev, "offset")
+    mut = _row_vec(mu, B, torch.float32, dev, "mu") if mu is not None else None
+    if out is None:
+        out = torch.empty((B, k), dtype=torch.int32, device=dev)
+    best = torch.empty((B, k), dtype=torch.float32, device=dev) if want_best else None
+    if ws is None:
+        ws = workspace(B, logits.shape[1], k, logits.dtype, True, dev)
+    rc = L.hs_sample_rows(C.byref(x), Tt.data_ptr(), _ptr(mut), rows.data_ptr(), st.data_ptr(),
+                          of.data_ptr(), int(k), out.data_ptr(), _ptr(best), ws.data_ptr(),
+                          ws.numel(), C.byref(opts) if opts is not None else None, _stream(dev))
+    _check(rc, "hs_sample_rows")
+    return (out, best) if want_best else out
 
 
 def gumbel_argmax(logits: torch.Tensor, T, seed, offset, *, k: int = 1,

@@ -13,7 +13,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhs.so")
-SOURCES = ["hs_kernels.hip", "hs_kernels_pivot.hip", "hs_api.hip"]
+SOURCES = ["hs_kernels.hip", "hs_kernels_pivot.hip", "hs_kernels_rows.hip", "hs_api.hip"]
 HEADERS = ["hs_device.hpp", "hs_internal.hpp", "hs_sample_kernel.hpp"]
 ARCH = os.environ.get("HS_OFFLOAD_ARCH", "gfx950")
 

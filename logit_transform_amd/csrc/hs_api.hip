@@ -169,10 +169,16 @@ int make_plan(const hs_logits *x, int32_t K, bool hlg, bool ws_ok, const hs_samp
     return HS_OK;
 }
 
+bool opts_valid(const hs_sample_opts *o) {
+    return !o || !(o->variant < 0 || o->variant > 2 || o->nchunk < 0 ||
+                   o->nchunk > hs::kMaxChunks || o->draw_groups < 0);
+}
+
+// rows: per-row curve settings (device), or NULL for the per-call curve hlg (or none).
 int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hlg_params *hlg,
-                const uint64_t *seed, const uint64_t *offset, int32_t K, int32_t *out,
-                float *best, void *ws, size_t ws_bytes, const hs_sample_opts *opts,
-                void *stream) {
+                const hs_hlg_row *rows, const uint64_t *seed, const uint64_t *offset, int32_t K,
+                int32_t *out, float *best, void *ws, size_t ws_bytes,
+                const hs_sample_opts *opts, void *stream) {
     int rc = check_logits(x);
     if (rc) return rc;
     if (!T || !seed || !offset || !out || K < 1) return HS_ERR_INVALID_ARG;
@@ -181,6 +187,8 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
         if (rc) return rc;
         if (hlg->pivot == HS_PIVOT_GIVEN && !mu) return HS_ERR_INVALID_ARG;
     }
+    if (rows && hlg) return HS_ERR_INVALID_ARG;
+    const bool curve_on = hlg != nullptr || rows != nullptr;
     if ((size_t)x->B * (size_t)K >= ((size_t)1 << 31)) return HS_ERR_UNSUPPORTED;
     const WsLayout L = ws_layout(x->B, K);
     const bool ws_ok = ws && ws_bytes >= L.total && ((uintptr_t)ws % 256 == 0);
@@ -190,7 +198,7 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
         return HS_ERR_INVALID_ARG;
     }
     Plan P;
-    rc = make_plan(x, K, hlg != nullptr, ws_ok, opts, &P);
+    rc = make_plan(x, K, curve_on, ws_ok, opts, &P);
     if (rc) return rc;
 
     SampleArgs a{};
@@ -206,8 +214,9 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
     a.aligned = rows_aligned(x) ? 1 : 0;
     a.no_screen = (opts && opts->no_screen) ? 1 : 0;
     a.T = T;
-    const int piv = hlg ? hlg->pivot : 0;
-    a.mu = piv == HS_PIVOT_GIVEN ? mu : nullptr;
+    const int piv = rows ? 3 : hlg ? hlg->pivot : 0;
+    a.mu = (piv == HS_PIVOT_GIVEN || piv == 3) ? mu : nullptr;
+    a.row_curves = reinterpret_cast<const hs::RowCurve *>(rows);
     a.seed = seed;
     a.offset = offset;
     a.out = out;
@@ -224,12 +233,12 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
         a.part_stride = hs::kMaxChunks;
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (hlg && P.nchunk > 1) {
+    if (curve_on && P.nchunk > 1) {
         const int bs = P.cv >= 4096 ? 1024 : 256;
         if (hs::launch_lse_partial(x->dtype, piv, a, bs, (int)(x->B * P.nchunk), s) != hipSuccess)
             return HS_ERR_HIP;
     }
-    if (hs::launch_sample(x->dtype, hlg != nullptr, piv, a, P.nv, P.bs, (int)P.grid, s) != hipSuccess)
+    if (hs::launch_sample(x->dtype, curve_on, piv, a, P.nv, P.bs, (int)P.grid, s) != hipSuccess)
         return HS_ERR_HIP;
     return HS_OK;
 }
@@ -297,14 +306,14 @@ int hs_hlg_pivot(const hs_logits *x, const float *mu, const hs_hlg_params *p, fl
 int hs_gumbel_argmax(const hs_logits *x, const float *T, const uint64_t *seed,
                      const uint64_t *offset, int32_t K, int32_t *out, void *ws, size_t ws_bytes,
                      void *stream) {
-    return sample_impl(x, T, nullptr, nullptr, seed, offset, K, out, nullptr, ws, ws_bytes,
-                       nullptr, stream);
+    return sample_impl(x, T, nullptr, nullptr, nullptr, seed, offset, K, out, nullptr, ws,
+                       ws_bytes, nullptr, stream);
 }
 
 int hs_sample(const hs_logits *x, const float *T, const float *mu, const hs_hlg_params *hlg,
               const uint64_t *seed, const uint64_t *offset, int32_t K, int32_t *out, void *ws,
               size_t ws_bytes, void *stream) {
-    return sample_impl(x, T, mu, hlg, seed, offset, K, out, nullptr, ws, ws_bytes, nullptr,
+    return sample_impl(x, T, mu, hlg, nullptr, seed, offset, K, out, nullptr, ws, ws_bytes, nullptr,
                        stream);
 }
 
@@ -312,10 +321,18 @@ int hs_sample_ex(const hs_logits *x, const float *T, const float *mu, const hs_h
                  const uint64_t *seed, const uint64_t *offset, int32_t K, int32_t *out,
                  float *best, void *ws, size_t ws_bytes, const hs_sample_opts *opts,
                  void *stream) {
-    if (opts && (opts->variant < 0 || opts->variant > 2 || opts->nchunk < 0 ||
-                 opts->nchunk > hs::kMaxChunks || opts->draw_groups < 0))
-        return HS_ERR_INVALID_ARG;
-    return sample_impl(x, T, mu, hlg, seed, offset, K, out, best, ws, ws_bytes, opts, stream);
+    if (!opts_valid(opts)) return HS_ERR_INVALID_ARG;
+    return sample_impl(x, T, mu, hlg, nullptr, seed, offset, K, out, best, ws, ws_bytes, opts,
+                       stream);
+}
+
+int hs_sample_rows(const hs_logits *x, const float *T, const float *mu, const hs_hlg_row *rows,
+                   const uint64_t *seed, const uint64_t *offset, int32_t K, int32_t *out,
+                   float *best, void *ws, size_t ws_bytes, const hs_sample_opts *opts,
+                   void *stream) {
+    if (!rows || !opts_valid(opts)) return HS_ERR_INVALID_ARG;
+    return sample_impl(x, T, mu, nullptr, rows, seed, offset, K, out, best, ws, ws_bytes, opts,
+                       stream);
 }
 
 size_t hs_workspace_bytes(int64_t B, int64_t V, int32_t K, int32_t dtype, int32_t hlg_on) {

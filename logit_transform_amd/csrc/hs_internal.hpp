@@ -13,6 +13,16 @@ namespace hs {
 // many (max, sum) pairs per row.
 constexpr int kMaxChunks = 64;
 
+// Per-row curve settings, laid out as hs_hlg_row of the public header (32 bytes).
+struct RowCurve {
+    float m, w, beta_t, beta_h;
+    int32_t pivot;
+    float pivot_offset;
+    int32_t enabled;
+    int32_t reserved;
+};
+static_assert(sizeof(RowCurve) == 32, "RowCurve layout");
+
 struct SampleArgs {
     const void *data;          // logits, row-major [B, ld]
     int64_t ld;                // row stride (elements)
@@ -38,6 +48,7 @@ struct SampleArgs {
     float4 *partials;          // [B * part_stride]: per chunk (max, sum, u, -) in nats
     int64_t part_stride;
     float pivot_offset;        // c of the top anchor
+    const RowCurve *row_curves;   // [B] per-row curve settings (pivot mode 3), else null
 };
 
 struct RowOpArgs {
@@ -53,7 +64,8 @@ struct RowOpArgs {
     float *mu_out;        // the pivot of every row (op 2)
 };
 
-// piv: the curve's pivot, 0 given per row, 1 top-anchored, 2 entropy-anchored
+// piv: the curve's pivot, 0 given per row, 1 top-anchored, 2 entropy-anchored, 3 set per row
+// (a.row_curves)
 hipError_t launch_sample(int dt, bool hlg, int piv, const SampleArgs &a, int nv, int bs,
                          int grid, hipStream_t s);
 hipError_t launch_sample_pivot(int dt, int piv, const SampleArgs &a, int nv, int bs, int grid,
@@ -62,6 +74,10 @@ hipError_t launch_lse_partial(int dt, int piv, const SampleArgs &a, int bs, int 
                               hipStream_t s);
 hipError_t launch_lse_partial_pivot(int dt, int piv, const SampleArgs &a, int bs, int grid,
                                     hipStream_t s);
+hipError_t launch_sample_rows(int dt, const SampleArgs &a, int nv, int bs, int grid,
+                              hipStream_t s);
+hipError_t launch_lse_partial_rows(int dt, const SampleArgs &a, int bs, int grid,
+                                   hipStream_t s);
 // op: 0 log-sum-exp, 1 transform, 2 pivot
 hipError_t launch_row_lse(int dt, int op, int piv, const RowOpArgs &a, int grid, hipStream_t s);
 hipError_t launch_philox(const uint32_t *ctr, const uint32_t *key, uint32_t *out, int64_t n,

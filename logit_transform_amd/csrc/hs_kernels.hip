@@ -134,6 +134,7 @@ __global__ void k_fill_zero(uint32_t *__restrict__ p, int64_t n) {
 // ------------------------------------------------------------------------------------------
 hipError_t launch_sample(int dt, bool hlg, int piv, const SampleArgs &a, int nv, int bs,
                          int grid, hipStream_t s) {
+    if (hlg && piv == 3) return launch_sample_rows(dt, a, nv, bs, grid, s);
     if (hlg && piv != 0) return launch_sample_pivot(dt, piv, a, nv, bs, grid, s);
     switch (dt) {
         case DT_F32: return hlg ? launch_sample_al<DT_F32, true, 0>(a, nv, bs, grid, s)
@@ -148,6 +149,7 @@ hipError_t launch_sample(int dt, bool hlg, int piv, const SampleArgs &a, int nv,
 
 hipError_t launch_lse_partial(int dt, int piv, const SampleArgs &a, int bs, int grid,
                               hipStream_t s) {
+    if (piv == 3) return launch_lse_partial_rows(dt, a, bs, grid, s);
     if (piv != 0) return launch_lse_partial_pivot(dt, piv, a, bs, grid, s);
     return launch_lse_partial_t<0>(dt, a, bs, grid, s);
 }

@@ -104,11 +104,15 @@ __device__ __forceinline__ float vec_max(const float (&x)[EPV]) {
 
 // PIV selects the curve's pivot [HLG, The pivot] (curve on only): 0 given per row,
 // 1 top-anchored (mu = l_max - c: z = x - (x_max - c), no log-sum-exp needed),
-// 2 entropy-anchored (mu = sum p l: z = x - E_p[x], one more accumulator).
+// 2 entropy-anchored (mu = sum p l: z = x - E_p[x], one more accumulator),
+// 3 set per row with the rest of the curve (a.row_curves): both sums are accumulated and each
+// row picks its shift; a row with its curve off runs the curve as the identity (m = 1, no
+// rolloff, c = 0), which scores x / T exactly as the curve-off kernel does.
 template <int DT, int NV, bool HLG, int PIV, int MAXBS, bool ALIGNED>
 __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     static_assert(HLG || PIV == 0, "a pivot needs the curve");
     constexpr bool LSE = HLG && PIV != 1;   // the exponential sum is needed
+    constexpr bool ENT = PIV == 2 || PIV == 3;   // and the entropy anchor's sum
     using tr = dtype_traits<DT>;
     constexpr int EPV = tr::epv;
     constexpr int NG = EPV / 4;                // Philox calls per vector
@@ -147,9 +151,45 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     const float T = a.T[b];
     float mu = 0.0f;
     bool bad = !(T >= 0.0f) || !(T < __builtin_inff());
+    Curve cv = a.curve;
+    float poff = a.pivot_offset;
+    int rpiv = PIV;   // this row's pivot mode; -1: curve off
     if constexpr (HLG && PIV == 0) {
         mu = a.mu[b];
         bad = bad || !(fabsf(mu) < __builtin_inff());
+    }
+    if constexpr (PIV == 3) {
+        const RowCurve r = a.row_curves[b];
+        const bool fin_m = r.m > 0.0f && r.m < __builtin_inff();
+        const bool fin_t = r.beta_t > 0.0f && r.beta_t < __builtin_inff();
+        const bool fin_h = r.beta_h > 0.0f && r.beta_h < __builtin_inff();
+        const bool valid = fin_m && r.w >= 0.0f && fin_t && fin_h && r.pivot >= 0 &&
+                           r.pivot <= 2 && (r.pivot != 1 || fabsf(r.pivot_offset) < __builtin_inff()) &&
+                           r.reserved == 0;
+        const bool on = r.enabled != 0 && valid;
+        if (r.enabled != 0 && !valid) bad = true;
+        if (on) {
+            // the same constants the host derives for a per-call curve (IEEE division)
+            cv.m = r.m;
+            cv.w = r.w;
+            cv.mw = r.m * r.w;
+            cv.mbt = r.m * r.beta_t;
+            cv.mbh = r.m * r.beta_h;
+            cv.ibt = 1.0f / r.beta_t;
+            cv.ibh = 1.0f / r.beta_h;
+            rpiv = r.pivot;
+            poff = r.pivot_offset;
+            if (rpiv == 0) {
+                mu = a.mu ? a.mu[b] : __builtin_nanf("");
+                bad = bad || !(fabsf(mu) < __builtin_inff());
+            }
+        } else {
+            cv.m = 1.0f;
+            cv.w = __builtin_inff();
+            cv.mw = __builtin_inff();
+            cv.mbt = cv.mbh = cv.ibt = cv.ibh = 1.0f;
+            rpiv = -1;
+        }
     }
     const bool greedy = (T == 0.0f);
 
@@ -306,7 +346,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                 const float t = __builtin_fmaf(xv[e], kLog2e, -lse_r);
                 const float p = __builtin_amdgcn_exp2f(t);
                 lse_s += p;
-                if constexpr (PIV == 2) lse_u = (p > 0.0f) ? __builtin_fmaf(p, t, lse_u) : lse_u;
+                if constexpr (ENT) lse_u = (p > 0.0f) ? __builtin_fmaf(p, t, lse_u) : lse_u;
             }
         }
     };
@@ -317,7 +357,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     // Linear part of the score used to rank bootstrap candidates before c = LSE + mu is known:
     // (m/T) x with the curve on (the mid line of g, up to the common shift -(m/T) c), x/T
     // without it.
-    const float lin = HLG ? a.curve.m * invT : invT;
+    const float lin = HLG ? cv.m * invT : invT;
     // Bootstrap candidate of a lane for draw stream sk: the element holding the largest word of
     // its champion vector v (nearly the largest Gumbel value among the lane's elements). The
     // vector's words are drawn again into cw (kept for the screen). Returns the candidate's rank
@@ -401,7 +441,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                     const float t = __builtin_fmaf(elem<DT>(v, e), kLog2e, -lse_r);
                     const float p = __builtin_amdgcn_exp2f(t);
                     lse_s += p;
-                    if constexpr (PIV == 2)
+                    if constexpr (ENT)
                         lse_u = (p > 0.0f) ? __builtin_fmaf(p, t, lse_u) : lse_u;
                 }
             }
@@ -415,7 +455,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     rc.invT = invT;
     rc.c = 0.0f;
     rc.mt = rc.mtc = rc.mtw = 0.0f;
-    rc.curve = a.curve;
+    rc.curve = cv;
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));
     int wid = threadIdx.x >> 6;
@@ -495,7 +535,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             mw = wave_max(lse_r);
             const float sc = __builtin_amdgcn_exp2f(lse_r - mw);
             sw = wave_sum(lse_s * sc);
-            if constexpr (PIV == 2)
+            if constexpr (ENT)
                 uw = wave_sum(lse_s > 0.0f ? __builtin_fmaf(lse_s, lse_r - mw, lse_u) * sc : 0.0f);
         }
         if (lane == 0) {
@@ -515,41 +555,47 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
         if constexpr (HLG) {
             // the shift c of z = x - c: LSE + mu (given pivot), x_max - offset (top anchor),
             // E_p[x] (entropy anchor), from this block's waves or the chunks' pre-pass
-            if (a.nchunk == 1) {
-                if constexpr (PIV == 1) {
-                    c = xmb - a.pivot_offset;
-                } else {
+            // (the row's own mode when the curve is set per row: runtime, but wave-uniform)
+            const int mode = PIV == 3 ? rpiv : PIV;
+            if (mode == 1) {
+                c = (a.nchunk == 1 ? xmb
+                                   : wave_max(lane < a.nchunk ? a.partials[b * a.part_stride + lane].x
+                                                              : -__builtin_inff())) - poff;
+                ok = c > -__builtin_inff();
+            } else if (mode < 0) {
+                c = 0.0f;   // curve off for this row: identity curve, no shift
+            } else if constexpr (LSE) {
+                if (a.nchunk == 1) {
                     const float pm = lane < nw ? red_m[lane] : -3.402823466e38f;
                     const float mb = wave_max(pm);
                     const float sc = lane < nw ? __builtin_amdgcn_exp2f(pm - mb) : 0.0f;
                     const float sb = wave_sum(lane < nw ? red_s[lane] * sc : 0.0f);
                     ok = sb > 0.0f;
-                    if constexpr (PIV == 0) {
+                    if (mode == 0) {
                         c = (mb + __builtin_amdgcn_logf(sb)) * kLn2 + mu;
-                    } else {
+                    } else if constexpr (ENT) {
                         const float ub = wave_sum(
                             lane < nw && red_s[lane] > 0.0f
                                 ? __builtin_fmaf(red_s[lane], pm - mb, red_u[lane]) * sc : 0.0f);
                         c = (mb + ub / sb) * kLn2;
                     }
-                }
-            } else {
-                // the chunks' (max, sum, u) of the pre-pass, one per lane (nchunk <= 64), all
-                // read at once; natural units
-                const float4 pj = lane < a.nchunk ? a.partials[b * a.part_stride + lane]
-                                                  : make_float4(-__builtin_inff(), 0.0f, 0.0f, 0.0f);
-                const float Mb = wave_max(pj.x);
-                ok = Mb > -__builtin_inff();
-                if constexpr (PIV == 1) {
-                    c = Mb - a.pivot_offset;
                 } else {
-                    const float e = pj.x > -__builtin_inff() ? __builtin_amdgcn_exp2f((pj.x - Mb) * kLog2e) : 0.0f;
+                    // the chunks' (max, sum, u) of the pre-pass, one per lane (nchunk <= 64),
+                    // all read at once; natural units
+                    const float4 pj = lane < a.nchunk
+                                          ? a.partials[b * a.part_stride + lane]
+                                          : make_float4(-__builtin_inff(), 0.0f, 0.0f, 0.0f);
+                    const float Mb = wave_max(pj.x);
+                    ok = Mb > -__builtin_inff();
+                    const float e = pj.x > -__builtin_inff()
+                                        ? __builtin_amdgcn_exp2f((pj.x - Mb) * kLog2e) : 0.0f;
                     const float Sb = wave_sum(pj.y * e);
-                    if constexpr (PIV == 0) {
+                    if (mode == 0) {
                         c = Mb + logf(Sb) + mu;
-                    } else {
+                    } else if constexpr (ENT) {
                         const float Ub = wave_sum(pj.x > -__builtin_inff()
-                                                      ? __builtin_fmaf(pj.y, pj.x - Mb, pj.z) * e : 0.0f);
+                                                      ? __builtin_fmaf(pj.y, pj.x - Mb, pj.z) * e
+                                                      : 0.0f);
                         c = Mb + Ub / Sb;
                     }
                 }
@@ -557,9 +603,9 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             ok = ok && xmb > -__builtin_inff();
             c = uniform(c);
             rc.c = c;
-            rc.mt = uniform(a.curve.m * rc.invT);
+            rc.mt = uniform(rc.curve.m * rc.invT);
             rc.mtc = uniform(rc.mt * rc.c);
-            rc.mtw = uniform(rc.mt * a.curve.w);
+            rc.mtw = uniform(rc.mt * rc.curve.w);
         }
         float o[7] = {xmb, 0.0f, 0.0f, __builtin_inff(), 0.0f, 0.0f, 0.0f};
         if (ok && screen) {
@@ -595,9 +641,9 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     const bool skip = bad || !(uniform(row_bc[2]) > 0.0f);
     if constexpr (HLG) {
         rc.c = uniform(row_bc[1]);
-        rc.mt = uniform(a.curve.m * rc.invT);
+        rc.mt = uniform(rc.curve.m * rc.invT);
         rc.mtc = uniform(rc.mt * rc.c);
-        rc.mtw = uniform(rc.mt * a.curve.w);
+        rc.mtw = uniform(rc.mt * rc.curve.w);
     }
     float sa = uniform(row_bc[4]), sb = uniform(row_bc[5]), sc = uniform(row_bc[6]);
     float ta = uniform(row_bc[7]), tb = uniform(row_bc[8]);
@@ -794,6 +840,7 @@ template <int DT, int PIV>
 __global__ __launch_bounds__(1024) void k_lse_partial(SampleArgs a) {
     using tr = dtype_traits<DT>;
     constexpr int EPV = tr::epv;
+    constexpr bool ENT = PIV == 2 || PIV == 3;   // the entropy anchor's sum is needed
     __shared__ float red_m[16], red_s[16], red_u[16];
     const int chunk = blockIdx.x % a.nchunk;
     const int64_t b = blockIdx.x / a.nchunk;
@@ -812,7 +859,7 @@ __global__ __launch_bounds__(1024) void k_lse_partial(SampleArgs a) {
         } else {
             if (mv > m) {
                 const float sc = __builtin_amdgcn_exp2f(m - mv);
-                if constexpr (PIV == 2) u = __builtin_fmaf(s, m - mv, u) * sc;
+                if constexpr (ENT) u = __builtin_fmaf(s, m - mv, u) * sc;
                 s *= sc;
                 m = mv;
             }
@@ -821,7 +868,7 @@ __global__ __launch_bounds__(1024) void k_lse_partial(SampleArgs a) {
                 const float t = __builtin_fmaf(xv[e], kLog2e, -m);
                 const float p = __builtin_amdgcn_exp2f(t);
                 s += p;
-                if constexpr (PIV == 2) u = (p > 0.0f) ? __builtin_fmaf(p, t, u) : u;
+                if constexpr (ENT) u = (p > 0.0f) ? __builtin_fmaf(p, t, u) : u;
             }
         }
     }
@@ -830,7 +877,7 @@ __global__ __launch_bounds__(1024) void k_lse_partial(SampleArgs a) {
     const float mw = wave_max(m);
     const float sc = __builtin_amdgcn_exp2f(m - mw);
     const float sw = wave_sum(s * sc);
-    const float uw = (PIV == 2) ? wave_sum(s > 0.0f ? __builtin_fmaf(s, m - mw, u) * sc : 0.0f) : 0.0f;
+    const float uw = ENT ? wave_sum(s > 0.0f ? __builtin_fmaf(s, m - mw, u) * sc : 0.0f) : 0.0f;
     if (lane == 0) {
         red_m[wid] = mw;
         red_s[wid] = sw;
@@ -842,7 +889,7 @@ __global__ __launch_bounds__(1024) void k_lse_partial(SampleArgs a) {
         const float mb = wave_max(pm);
         const float sb_ = lane < nw ? __builtin_amdgcn_exp2f(pm - mb) : 0.0f;
         const float S = wave_sum(lane < nw ? red_s[lane] * sb_ : 0.0f);
-        const float U = (PIV == 2) ? wave_sum(lane < nw && red_s[lane] > 0.0f
+        const float U = ENT ? wave_sum(lane < nw && red_s[lane] > 0.0f
                                                   ? __builtin_fmaf(red_s[lane], pm - mb, red_u[lane]) * sb_
                                                   : 0.0f)
                                    : 0.0f;

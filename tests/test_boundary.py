@@ -175,6 +175,40 @@ def test_sample_ex_opts(lib):
                                 C.byref(o), None) == HS_ERR_INVALID_ARG
 
 
+def test_sample_rows_args(lib):
+    x = L()
+    # per-row settings are required; opts are checked as for hs_sample_ex
+    assert lib.hs_sample_rows(C.byref(x), FAKE, None, None, FAKE, FAKE, 1, FAKE, None, None, 0,
+                              None, None) == HS_ERR_INVALID_ARG
+    o = hs.SampleOpts(variant=5)
+    assert lib.hs_sample_rows(C.byref(x), FAKE, None, FAKE, FAKE, FAKE, 1, FAKE, None, None, 0,
+                              C.byref(o), None) == HS_ERR_INVALID_ARG
+    for bad, code in ((L(data=0), HS_ERR_INVALID_ARG), (L(dtype=9), HS_ERR_DTYPE)):
+        assert lib.hs_sample_rows(C.byref(bad), FAKE, None, FAKE, FAKE, FAKE, 1, FAKE, None,
+                                  None, 0, None, None) == code
+    for kw in (dict(T=None), dict(seed=None), dict(out=None), dict(K=0)):
+        a = dict(T=FAKE, seed=FAKE, out=FAKE, K=1)
+        a.update(kw)
+        assert lib.hs_sample_rows(C.byref(x), a["T"], None, FAKE, a["seed"], FAKE, a["K"],
+                                  a["out"], None, None, 0, None, None) == HS_ERR_INVALID_ARG
+    # mu is optional (rows decide in the kernel): valid arguments reach the workspace check
+    assert lib.hs_sample_rows(C.byref(x), FAKE, None, FAKE, FAKE, FAKE, 1, FAKE, None, FAKE, 8,
+                              None, None) == HS_ERR_WORKSPACE
+
+
+def test_hlg_rows_packing():
+    import struct
+    rows = [None, (1.5, 2.0, 1.0, 3.0), {"m": 0.5, "w": math.inf, "beta_t": 2.0, "beta_h": 4.0,
+                                         "pivot": "top", "pivot_offset": 6.0}]
+    assert C.sizeof(hs.HlgRow) == 32
+    raw = bytes(hs._pack_rows(rows))
+    assert len(raw) == 96
+    vals = [struct.unpack_from("<4fifii", raw, 32 * i) for i in range(3)]
+    assert vals[0][6] == 0                                   # off
+    assert vals[1] == (1.5, 2.0, 1.0, 3.0, 0, 0.0, 1, 0)
+    assert vals[2][:2] == (0.5, math.inf) and vals[2][4:] == (1, 6.0, 1, 0)
+
+
 def test_aux_entry_points(lib):
     assert lib.hs_philox4x32_10(None, FAKE, FAKE, 4, None) == HS_ERR_INVALID_ARG
     assert lib.hs_philox4x32_10(FAKE, FAKE, FAKE, -1, None) == HS_ERR_INVALID_ARG
