@@ -66,7 +66,7 @@ def load_traffic(name: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s: float = 10.0):
+def cpu_baseline(w, budget_s: float = 10.0, settings=None):
     """The oracle as it stands, all host cores, on the workload's rows: a first timed pass sizes
     the sample (the first rows, or whole passes over all rows repeated until about budget_s of
     work), then the sample is timed. Rows per second of the whole sample are reported."""
@@ -78,8 +78,17 @@ def cpu_baseline(w, budget_s: float = 10.0):
     n = min(w.B, max(threads, 8))
 
     def run(rows):
-        O.sample(w.logits[:rows], w.T[:rows], w.seed[:rows], w.offset[:rows], K=w.K,
-                 mu=None if w.hlg is None else w.mu[:rows], hlg=w.hlg)
+        if settings is None:
+            O.sample(w.logits[:rows], w.T[:rows], w.seed[:rows], w.offset[:rows], K=w.K,
+                     mu=None if w.hlg is None else w.mu[:rows], hlg=w.hlg)
+            return
+        # the curve set per row: the oracle samples each row with its own setting
+        import numpy as np
+        for r in range(rows):
+            h = settings[r]
+            O.sample(w.logits[r:r + 1], w.T[r:r + 1], w.seed[r:r + 1], w.offset[r:r + 1],
+                     K=w.K, mu=w.mu[r:r + 1] if h is not None and "pivot" not in h else None,
+                     hlg=h, row_id=np.array([r], dtype=np.int64))
 
     run(n)   # first call: library and thread-pool start-up, untimed
     t0 = time.perf_counter()
@@ -113,6 +122,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="launch the timed steps one by one instead of replaying a HIP graph")
+    ap.add_argument("--pivot", choices=("input", "top", "entropy"), default="input",
+                    help="the curve's pivot: given per row (default, the workload's mu), "
+                         "top-anchored or entropy-anchored, computed in the kernel")
+    ap.add_argument("--pivot-offset", type=float, default=6.0,
+                    help="c of the top anchor (nats below the most probable token)")
+    ap.add_argument("--per-row", action="store_true",
+                    help="set the curve per row (hs_sample_rows), cycling over: off, given "
+                         "pivot, top-anchored, entropy-anchored, with the workload's knobs")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain device copy of MIB MiB five "
                          "times (reference for scaling the memory-traffic counters)")
@@ -146,6 +163,20 @@ def main():
     torch.cuda.set_device(dev)
     w = W.CONFIGS[args.config]()
     B, V, K = w.B, w.V, w.K
+    settings = None
+    if w.hlg is not None and args.pivot != "input":
+        w.hlg = dict(w.hlg, pivot=args.pivot, pivot_offset=args.pivot_offset)
+        w.name += ", pivot %s" % args.pivot + (" c=%g" % args.pivot_offset
+                                               if args.pivot == "top" else "")
+    if args.per_row:
+        if w.hlg is None:
+            print("--per-row needs a workload with the curve on", file=sys.stderr)
+            sys.exit(2)
+        base = {k: w.hlg[k] for k in ("m", "w", "beta_t", "beta_h")}
+        cycle = [None, dict(base), dict(base, pivot="top", pivot_offset=args.pivot_offset),
+                 dict(base, pivot="entropy")]
+        settings = [cycle[r % len(cycle)] for r in range(B)]
+        w.name += ", curve per row (off / given / top c=%g / entropy)" % args.pivot_offset
     log("workload:", w.name)
 
     copies = [w.logits.to(dev)]
@@ -154,22 +185,32 @@ def main():
     T = torch.from_numpy(w.T).to(dev)
     seed = torch.from_numpy(w.seed.view(np.int64)).to(dev)
     off = torch.from_numpy(w.offset.view(np.int64)).to(dev)
-    mu = torch.from_numpy(w.mu).to(dev) if w.hlg is not None else None
-    hp = hs._hlg_struct(w.hlg)
+    given_pivot = w.hlg is not None and (settings is not None or
+                                         w.hlg.get("pivot", "input") == "input")
+    mu = torch.from_numpy(w.mu).to(dev) if given_pivot else None
+    hp = None if settings is not None else hs._hlg_struct(w.hlg)
+    rows = hs.hlg_rows(settings, dev) if settings is not None else None
     out = torch.empty((B, K), dtype=torch.int32, device=dev)
-    ws = hs.workspace(B, V, K, w.dtype, hp is not None, dev)
+    ws = hs.workspace(B, V, K, w.dtype, w.hlg is not None, dev)
     structs = [hs._logits_struct(x) for x in copies]
     stream = hs._stream(dev)
     hp_ref = C.byref(hp) if hp is not None else None
     mu_ptr = mu.data_ptr() if mu is not None else None
-    fn = L.hs_sample
+
+    def launch(i, s_):
+        if rows is not None:
+            rc = L.hs_sample_rows(C.byref(structs[i % len(structs)]), T.data_ptr(), mu_ptr,
+                                  rows.data_ptr(), seed.data_ptr(), off.data_ptr(), K,
+                                  out.data_ptr(), None, ws.data_ptr(), ws.numel(), None, s_)
+        else:
+            rc = L.hs_sample(C.byref(structs[i % len(structs)]), T.data_ptr(), mu_ptr, hp_ref,
+                             seed.data_ptr(), off.data_ptr(), K, out.data_ptr(), ws.data_ptr(),
+                             ws.numel(), s_)
+        if rc != 0:
+            raise hs.HsError(rc, "hs_sample_rows" if rows is not None else "hs_sample")
 
     def step(i):
-        rc = fn(C.byref(structs[i % len(structs)]), T.data_ptr(), mu_ptr, hp_ref,
-                seed.data_ptr(), off.data_ptr(), K, out.data_ptr(), ws.data_ptr(), ws.numel(),
-                stream)
-        if rc != 0:
-            raise hs.HsError(rc, "hs_sample")
+        launch(i, stream)
 
     for i in range(args.warmup):
         step(i)
@@ -189,11 +230,7 @@ def main():
                 with torch.cuda.graph(graph, stream=side):
                     cap_stream = hs._stream(dev)
                     for i in range(args.steps):
-                        rc = fn(C.byref(structs[i % len(structs)]), T.data_ptr(), mu_ptr, hp_ref,
-                                seed.data_ptr(), off.data_ptr(), K, out.data_ptr(), ws.data_ptr(),
-                                ws.numel(), cap_stream)
-                        if rc != 0:
-                            raise hs.HsError(rc, "hs_sample (capture)")
+                        launch(i, cap_stream)
             torch.cuda.current_stream(dev).wait_stream(side)
             graph.replay()   # one untimed replay
             torch.cuda.synchronize()
@@ -236,12 +273,18 @@ def main():
 
     rows_per_s = B / (ms_per_step / 1e3)
     logit_bytes = B * V * w.logits.element_size()
-    param_bytes = B * (4 + 8 + 8 + (4 if mu is not None else 0))
+    param_bytes = B * (4 + 8 + 8 + (4 if mu is not None else 0) + (32 if rows is not None else 0))
     alg_bytes = logit_bytes + param_bytes + 4 * B * K
     gbps = alg_bytes / (kern_ms / 1e3) / 1e9
-    ops = B * V * (OPS_PER_ELEMENT_DRAW * K + (OPS_PER_ELEMENT_LSE if mu is not None else 0))
+    # the log-sum-exp runs for every row unless the whole batch is top-anchored
+    lse_on = w.hlg is not None and (rows is not None or w.hlg.get("pivot", "input") != "top")
+    ops = B * V * (OPS_PER_ELEMENT_DRAW * K + (OPS_PER_ELEMENT_LSE if lse_on else 0))
     tops = ops / (kern_ms / 1e3) / 1e12
     name = "k_sample_c%d" % args.config
+    if args.pivot != "input" and w.hlg is not None:
+        name += "_" + args.pivot
+    if rows is not None:
+        name += "_rows"
     traffic = load_traffic(name)
     log("step %.4f ms (events over the timed region), wall %.4f ms/step; per-launch event "
         "pairs p10 %.4f p50 %.4f p90 %.4f ms"
@@ -266,6 +309,8 @@ def main():
         "config": {"workload": w.name, "B": B, "V": V, "K": K,
                    "input_dtype": str(w.dtype).replace("torch.", ""),
                    "hlg": w.hlg is not None, "input_copies": len(copies),
+                   "pivot": (None if w.hlg is None else
+                             "per_row" if rows is not None else w.hlg.get("pivot", "input")),
                    "launch": "hip_graph" if graph is not None else "eager",
                    "algorithmic_bytes_per_step": alg_bytes},
         "roofline": {"bound": "alu", "achieved": tops, "peak": ALU_PEAK_TOPS,
@@ -277,7 +322,7 @@ def main():
                 "frac": gbps / HBM_PEAK_GBPS},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w)
+        rec["cpu_baseline"] = cpu_baseline(w, settings=settings)
         log("cpu baseline:", rec["cpu_baseline"])
     print(json.dumps(rec), flush=True)
 
