@@ -128,9 +128,12 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     __shared__ float red_cx[16];       //   its logit
     __shared__ uint32_t red_cw[16];    //   and word
     __shared__ float row_bc[12];       // row constants from wave 0
-    // two buffers, alternating between draws: without a bootstrap (greedy rows, no screening)
-    // nothing else separates one draw's reads of the buffer from the next draw's writes
-    __shared__ uint64_t red_draw[2][16];
+    // per wave, the best exact candidate score of a later draw; two buffers, alternating
+    // between draws (a wave may post draw k + 1's before a slower one has read draw k's)
+    __shared__ float red_sb[2][16];
+    // the block's best key of each draw of a batch of up to 64, by LDS atomic maxima; wave 0
+    // writes a batch out after one barrier
+    __shared__ uint64_t s_best[64];
     __shared__ int s_last;
 
     const int tid = threadIdx.x;
@@ -138,6 +141,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     constexpr int SC = NV | 1;
     uint16_t *s_vec16 = reinterpret_cast<uint16_t *>(s_vec);
     int lane_lds = tid * SC;
+    if (tid < 64) s_best[tid] = 0ull;   // visible to every wave after the combine's barrier
     // block coordinates in scalar registers (the divisions would otherwise run per lane)
     int bid = blockIdx.x;
     const int chunk = __builtin_amdgcn_readfirstlane(bid % a.nchunk);
@@ -489,8 +493,10 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     // left of the knot), and -(m/T) w the top of the toe; without the curve U(x) = x/T.
     // No bound (no screening): every vector passes.
     auto screen_consts = [&](float bs, float xtop, float *o) {
+        // (a bound that overflowed to +inf screens nothing out)
         float thr = -3.0e38f;
-        if (bs > -__builtin_inff()) thr = (bs - screen_slack(bs)) * kInvLn2 - 1.0f;
+        if (bs > -__builtin_inff() && bs < __builtin_inff())
+            thr = (bs - screen_slack(bs)) * kInvLn2 - 1.0f;
         o[0] = thr;
         if constexpr (HLG) {
             o[1] = -rc.mt * kInvLn2;
@@ -499,6 +505,8 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             o[4] = o[1];
             o[5] = o[2];
             o[6] = 0.0f;
+            o[7] = 0.0f;
+            o[8] = 0.0f;
             const float z0 = xtop - rc.c;
             const float d = z0 - rc.curve.w;
             const float bh = 1.0f / rc.curve.ibh;
@@ -509,8 +517,11 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                 const float g0 = rc.curve.mw + rc.curve.mbh * log1p_acc(d * rc.curve.ibh);
                 const float s0 = rc.curve.mbh / (bh + d);   // m b / (b + d)
                 // tan(x) = (s0 x + g0 - s0 (z0 + c)) / T
+                const float ti = __builtin_fmaf(-s0, xtop, g0) * rc.invT;
                 o[4] = -s0 * rc.invT * kInvLn2;
-                o[5] = __builtin_fmaf(__builtin_fmaf(-s0, xtop, g0) * rc.invT, -kInvLn2, thr);
+                o[5] = __builtin_fmaf(ti, -kInvLn2, thr);
+                o[7] = 1.0f;   // the tangent is set up; its intercept before thr:
+                o[8] = ti;
                 // the vector screen pays two instructions per slot for the tangent: worth it
                 // when it lies well below the mid line at the top (in units of ln 2)
                 o[6] = ((rc.curve.m * z0 - g0) * rc.invT * kInvLn2 > 1.5f) ? 1.0f : 0.0f;
@@ -522,6 +533,8 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             o[4] = o[1];
             o[5] = o[2];
             o[6] = 0.0f;
+            o[7] = 0.0f;
+            o[8] = 0.0f;
         }
     };
 
@@ -607,7 +620,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             rc.mtc = uniform(rc.mt * rc.c);
             rc.mtw = uniform(rc.mt * rc.curve.w);
         }
-        float o[7] = {xmb, 0.0f, 0.0f, __builtin_inff(), 0.0f, 0.0f, 0.0f};
+        float o[9] = {xmb, 0.0f, 0.0f, __builtin_inff(), 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
         if (ok && screen) {
             // lower bounds on the first draw's winning score: the best candidate's exact
             // score, and from the chunk's largest logit (its curve value is at least
@@ -634,6 +647,8 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             row_bc[7] = o[4];
             row_bc[8] = o[5];
             row_bc[9] = o[6];
+            row_bc[10] = o[7];
+            row_bc[11] = o[8];
         }
     }
     __syncthreads();
@@ -648,6 +663,16 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     float sa = uniform(row_bc[4]), sb = uniform(row_bc[5]), sc = uniform(row_bc[6]);
     float ta = uniform(row_bc[7]), tb = uniform(row_bc[8]);
     bool tan_on = uniform(row_bc[9]) > 0.0f;
+    // for later draws: whether the shoulder tangent is set up, its intercept before the
+    // threshold, and the lower bound from the chunk's largest logit (the first draw's)
+    const bool tan_set = uniform(row_bc[10]) > 0.0f;
+    const float tan_i = uniform(row_bc[11]);
+    float lbx_row;
+    if constexpr (HLG) {
+        lbx_row = uniform(fminf(xmax_blk - rc.c, rc.curve.w) * rc.mt - 3.14f);
+    } else {
+        lbx_row = uniform(xmax_blk * rc.invT - 3.14f);
+    }
     auto code_needed = [&](float x) -> float {
         return fminf(fmaxf(__builtin_fmaf(x, sa, sb), __builtin_fmaf(x, ta, tb)), sc);
     };
@@ -690,37 +715,30 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
         const Stream sk = stream_k(k);
         uint32_t champ = champ0;
         if (k > k0 && !skip && screen) {
-            // this draw's words, champions and bootstrap candidate (two more barriers)
+            // this draw's words and champions; every lane scores its bootstrap candidate
+            // exactly (c is known by now), and after one barrier every wave takes the block's
+            // best such score as the lower bound and sets up its screen from it
             champ = draw_all(sk);
             craw0 = fetch(lane_v + (int)(champ & 31u) * BS);
-            post_candidate(candidate(sk, champ, craw0, cw0));
+            const Cand cd = candidate(sk, champ, craw0, cw0);
+            const float cs = cd.key != 0ull ? exact_score<HLG>(cd.x, cd.w, rc) : -__builtin_inff();
+            const float csw = wave_max(cs);
+            float *sbp = red_sb[(k - k0) & 1];
+            if (lane == 0) sbp[wid] = csw;
             __syncthreads();
-            if (wid == 0) {
-                float lbx;
-                if constexpr (HLG) {
-                    lbx = fminf(xmax_blk - rc.c, rc.curve.w) * rc.mt - 3.14f;
-                } else {
-                    lbx = xmax_blk * rc.invT - 3.14f;
-                }
-                float o[7];
-                screen_consts(uniform(fmaxf(candidate_score(), lbx)), xmax_blk, o);
-                if (lane == 0) {
-                    row_bc[3] = o[0];
-                    row_bc[4] = o[1];
-                    row_bc[5] = o[2];
-                    row_bc[6] = o[3];
-                    row_bc[7] = o[4];
-                    row_bc[8] = o[5];
-                    row_bc[9] = o[6];
-                }
+            const float bs = uniform(fmaxf(wave_max(lane < nw ? sbp[lane] : -__builtin_inff()),
+                                           lbx_row));
+            // the same arithmetic as the first draw's constants, from the new bound
+            const float thr = bs < __builtin_inff() ? (bs - screen_slack(bs)) * kInvLn2 - 1.0f
+                                                    : -3.0e38f;
+            if constexpr (HLG) {
+                sb = __builtin_fmaf(rc.mtc, kInvLn2, thr);
+                sc = __builtin_fmaf(rc.mtw, kInvLn2, thr);
+                tb = tan_set ? __builtin_fmaf(tan_i, -kInvLn2, thr) : sb;
+            } else {
+                sb = thr;
+                tb = thr;
             }
-            __syncthreads();
-            sa = uniform(row_bc[4]);
-            sb = uniform(row_bc[5]);
-            sc = uniform(row_bc[6]);
-            ta = uniform(row_bc[7]);
-            tb = uniform(row_bc[8]);
-            tan_on = uniform(row_bc[9]) > 0.0f;
         }
         uint64_t best = 0;
         if (!skip) {
@@ -776,24 +794,31 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                 if (two) best = score_vec(sk, n2, v2, best);
             }
         }
-        // block maximum of the draw's key: waves post their maxima, wave 0 writes the result
+        // block maximum of the draw's key: each wave's maximum goes into the draw's LDS entry
+        // by an atomic maximum, with no barrier; a batch of up to 64 draws (or the last) is
+        // written out by wave 0 after one barrier. Wave 0 alone issues the global atomics of
+        // split rows, so its thread 0 can wait for all of them before counting the block in.
         {
-            uint64_t *rd = red_draw[(k - k0) & 1];
+            const int d = (k - k0) & 63;
             const uint64_t wk = wave_max_u64(best);
-            if (lane == 0) rd[wid] = wk;
-            __syncthreads();
-            if (wid == 0) {
-                const uint64_t kb = wave_max_u64(lane < nw ? rd[lane] : 0ull);
-                if (lane == 0) {
-                    const int64_t o = b * a.K + k;
+            if (lane == 0 && wk != 0ull)
+                __hip_atomic_fetch_max(&s_best[d], wk, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (d == 63 || k == k1 - 1) {
+                __syncthreads();
+                if (wid == 0 && lane <= d) {
+                    const uint64_t kb = s_best[lane];
+                    s_best[lane] = 0ull;
+                    const int64_t o = b * a.K + (k - d + lane);
                     if (a.nchunk == 1) {
                         a.out[o] = bad ? -2 : key_index(kb);
                         if (a.best_out) a.best_out[o] = bad ? -__builtin_inff() : key_score(kb);
-                    } else if (kb != 0) {
+                    } else if (kb != 0ull) {
                         __hip_atomic_fetch_max(a.keys + o, kb, __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_AGENT);
                     }
                 }
+                if (k < k1 - 1) __syncthreads();   // the entries are reused
             }
         }
     }
