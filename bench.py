@@ -110,7 +110,49 @@ def cpu_baseline(w, budget_s: float = 10.0, settings=None):
                                                            threads)}
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_one_thread(cfg: int, rows: int) -> None:
+    """Child process (OMP_NUM_THREADS=1, no GPU): the oracle on the first rows of a workload;
+    prints rows/s as JSON."""
+    from oracle import oracle as O
+    from synth import workloads as W
+    w = W.CONFIGS[cfg]()
+    O.lib()
+    def run():
+        O.sample(w.logits[:rows], w.T[:rows], w.seed[:rows], w.offset[:rows], K=w.K,
+                 mu=None if w.hlg is None else w.mu[:rows], hlg=w.hlg)
+    run()
+    t0 = time.perf_counter()
+    run()
+    dt = time.perf_counter() - t0
+    print(json.dumps({"rows_per_s": rows / dt, "rows": rows, "seconds": dt}), flush=True)
+
+
+def cpu_one_thread(cfg: int, rows: int):
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-one-thread",
+                        str(cfg), str(rows)], env=env, capture_output=True, text=True,
+                       timeout=300)
+    if r.returncode != 0:
+        return {"error": r.stderr.strip()[-200:]}
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
 def main():
+    if len(sys.argv) == 4 and sys.argv[1] == "--oracle-one-thread":
+        oracle_one_thread(int(sys.argv[2]), int(sys.argv[3]))
+        return
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -120,6 +162,8 @@ def main():
                          "for the other workloads of the pages")
     ap.add_argument("--copies", type=int, default=5, help="rotating input copies (cold cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the streaming-read and Philox ceilings and the warm-cache run")
     ap.add_argument("--eager", action="store_true",
                     help="launch the timed steps one by one instead of replaying a HIP graph")
     ap.add_argument("--pivot", choices=("input", "top", "entropy"), default="input",
@@ -271,6 +315,73 @@ def main():
     # work, are reported beside it.
     kern_ms = ms_per_step
 
+    # Ceilings on the same shape, each timed as a graph of back-to-back launches: a plain
+    # streaming read of the logits with the sampler's access pattern (the same rotating
+    # copies), and the Philox4x32-10 word rate with no memory traffic; and the sampler itself
+    # with one input copy (warm: resident in the last-level cache).
+    ceilings = warm = None
+    if not args.no_ceilings and graph is not None:
+        def graph_ms(fn, n):
+            g = torch.cuda.CUDAGraph()
+            side_ = torch.cuda.Stream(dev)
+            side_.wait_stream(torch.cuda.current_stream(dev))
+            with torch.cuda.stream(side_):
+                with torch.cuda.graph(g, stream=side_):
+                    cs = hs._stream(dev)
+                    for i in range(n):
+                        fn(i, cs)
+            torch.cuda.current_stream(dev).wait_stream(side_)
+            g.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n
+
+        n_c = min(args.steps, 200)
+        warm_ms = graph_ms(lambda i, s_: launch(0, s_), n_c)
+        warm = {"ms_per_step": warm_ms, "rows_per_s": B / (warm_ms / 1e3),
+                "note": "one input copy, resident in the last-level cache"}
+        M = C.CDLL(os.path.join(ROOT, "logit_transform_amd", "libhs_micro.so"))
+        M.hs_micro_stream_max.argtypes = [C.c_void_p, C.c_int32, C.c_int64, C.c_int64,
+                                          C.c_int64, C.c_void_p, C.c_void_p]
+        M.hs_micro_philox_max.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_int32,
+                                          C.c_int32, C.c_void_p, C.c_void_p]
+        groups = max(1, min(K, -(-2048 // B)))   # spread the draws over about 2048 blocks
+        esz = w.logits.element_size()
+        rowmax = torch.empty(B, dtype=torch.float32, device=dev)
+        words = torch.empty(B * groups * 1024, dtype=torch.int32, device=dev)
+        ceilings = {}
+
+        def read_one(i, s_):
+            x = copies[i % len(copies)]
+            rc = M.hs_micro_stream_max(x.data_ptr(), hs._DTYPES[x.dtype], B, V, x.stride(0),
+                                       rowmax.data_ptr(), s_)
+            if rc != 0:
+                raise RuntimeError("hs_micro_stream_max: %d" % rc)
+
+        def philox_one(i, s_):
+            rc = M.hs_micro_philox_max(seed.data_ptr(), B, V, K, groups, words.data_ptr(), s_)
+            if rc != 0:
+                raise RuntimeError("hs_micro_philox_max: %d" % rc)
+
+        if (V * esz) % 16 == 0:
+            st_ms = graph_ms(read_one, n_c)
+            st_gbps = B * V * esz / (st_ms / 1e3) / 1e9
+            ceilings["stream_read"] = {"ms": st_ms, "GB/s": st_gbps,
+                                       "frac_of_peak": st_gbps / HBM_PEAK_GBPS}
+            ceilings["kernel_frac_of_stream_read"] = B * V * esz / (kern_ms / 1e3) / 1e9 / st_gbps
+        if V % 4 == 0:
+            ph_ms = graph_ms(philox_one, min(n_c, 50))
+            ceilings["philox"] = {"ms": ph_ms, "words_per_s": B * V * K / (ph_ms / 1e3),
+                                  "draws": K}
+            ceilings["kernel_words_per_s"] = B * V * K / (kern_ms / 1e3)
+            ceilings["kernel_frac_of_philox"] = ph_ms / kern_ms
+        log("warm (one copy, cache-resident) %.4f ms/step; ceilings %s" % (warm_ms, ceilings))
+
     rows_per_s = B / (ms_per_step / 1e3)
     logit_bytes = B * V * w.logits.element_size()
     param_bytes = B * (4 + 8 + 8 + (4 if mu is not None else 0) + (32 if rows is not None else 0))
@@ -320,9 +431,23 @@ def main():
                      "ops_per_step": ops},
         "hbm": {"achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": gbps / HBM_PEAK_GBPS},
+        "launch_ms": {"p10": per_launch[len(per_launch) // 10],
+                      "p50": per_launch[len(per_launch) // 2],
+                      "p90": per_launch[(9 * len(per_launch)) // 10],
+                      "note": "each launch between its own pair of events"},
     }
+    if K > 1:
+        rec["draws_per_s"] = B * K / (ms_per_step / 1e3)
+    if warm is not None:
+        rec["warm"] = warm
+    if ceilings:
+        rec["ceilings"] = ceilings
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, settings=settings)
+        rec["cpu_baseline"]["cpu_model"] = cpu_model()
+        if settings is None and args.pivot == "input":
+            rec["cpu_baseline"]["one_thread"] = cpu_one_thread(args.config,
+                                                               1 if args.config == 5 else 16)
         log("cpu baseline:", rec["cpu_baseline"])
     print(json.dumps(rec), flush=True)
 

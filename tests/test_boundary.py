@@ -227,3 +227,22 @@ def test_python_binding_refuses_cpu_tensors():
         hs.sample(x, [1.0, 1.0], [1, 2], [0, 0])
     with pytest.raises(ValueError):
         hs.logsumexp(x)
+
+
+def test_micro_library_exports():
+    """The benchmark's ceiling kernels (streaming read, Philox rate) build into a library of
+    their own and reject bad shapes before launching anything."""
+    p = os.path.join(ROOT, "logit_transform_amd", "libhs_micro.so")
+    if not os.path.exists(p):
+        pytest.skip("libhs_micro.so not built")
+    M = C.CDLL(p)
+    M.hs_micro_stream_max.argtypes = [C.c_void_p, C.c_int32, C.c_int64, C.c_int64, C.c_int64,
+                                      C.c_void_p, C.c_void_p]
+    M.hs_micro_philox_max.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_int32, C.c_int32,
+                                      C.c_void_p, C.c_void_p]
+    assert M.hs_micro_stream_max(None, 1, 4, 64, 64, FAKE, None) == -1
+    assert M.hs_micro_stream_max(FAKE, 1, 4, 63, 64, FAKE, None) == -1     # not whole vectors
+    assert M.hs_micro_stream_max(FAKE, 9, 4, 64, 64, FAKE, None) == -1
+    assert M.hs_micro_philox_max(FAKE, 4, 10, 1, 1, FAKE, None) == -1      # V % 4 != 0
+    assert M.hs_micro_philox_max(None, 4, 64, 1, 1, FAKE, None) == -1
+    assert M.hs_micro_philox_max(FAKE, 4, 64, 2, 3, FAKE, None) == -1      # groups > K
