@@ -24,12 +24,17 @@
  *     untouched; GMX, Task 3]; T < 0 or T not finite gives -2.
  *   - ties go to the lowest index; a row with no finite logit gives -1.
  *   - logits must be finite or -inf; NaN or +inf makes the call fail (-1 return).
+ *   - top-k / top-p on the Gumbel path (the follow-on the Gumbel-max issue names, without an
+ *     algorithm): with the curve off, temperature first, then top-k, then top-p on the
+ *     tempered probabilities of the tokens top-k keeps; each filter is a threshold on the
+ *     logit and every token at or above it is kept (ties included). See or_filter_tau.
  *
  * Build: gcc -O2 -fopenmp -fPIC -shared (never -ffast-math: it would break -inf masking).
  */
 #include <math.h>
 #include <stdint.h>
 #include <stddef.h>
+#include <stdlib.h>
 
 /* ---------------------------------------------------------------------------------------
  * Philox4x32-10 [P123]: 4x32-bit counter, 2x32-bit key, 10 rounds. Each round multiplies
@@ -323,4 +328,135 @@ void or_gumbel_n(int64_t n, const uint32_t *r, double *g)
 void or_hlg_g_n(int64_t n, const double *z, double m, double w, double bt, double bh, double *out)
 {
     for (int64_t j = 0; j < n; ++j) out[j] = or_hlg_g(z[j], m, w, bt, bh);
+}
+
+
+/* ---------------------------------------------------------------------------------------
+ * Top-k / top-p filters on the Gumbel path (curve off). Reading: the draw is the Gumbel-max
+ * of the tempered logits restricted to the kept tokens, i.e. an exact sample of softmax(x/T)
+ * renormalised over them [GMX, Background: argmax of x/T + G is a sample of softmax(x/T); the
+ * same holds on any subset]. The kept set, in the usual order of the two filters:
+ *   - top-k (k > 0): the tokens whose logit is at least the k-th largest finite logit;
+ *     k <= 0 or k >= the number of finite logits keeps every finite token;
+ *   - top-p (0 < p < 1): among the tokens top-k keeps, sorted by logit, the shortest prefix
+ *     whose tempered probability mass exp((x - x_max)/T) / S reaches p, where S is the mass of
+ *     the tokens top-k keeps; every token whose logit equals the last one's is kept too.
+ *     p >= 1 keeps every token; p <= 0 or NaN is invalid (-2 for the row).
+ * The combined kept set is {i : x_i >= tau}. tau = -inf when nothing is filtered (and for
+ * greedy rows, whose argmax is always kept).
+ * ------------------------------------------------------------------------------------- */
+static int or_cmp_desc(const void *a, const void *b)
+{
+    double x = *(const double *)a, y = *(const double *)b;
+    return (x < y) - (x > y);
+}
+
+/* tau of one row; *amb = 1 when the top-p crossing lies within 1e-5 * S of p * S on either
+ * side, so that an fp32 computation may take a neighbouring boundary. */
+double or_filter_tau_row(const double *x, int64_t V, double t, int32_t k, double p, int *amb)
+{
+    *amb = 0;
+    if (t == 0.0) return -INFINITY;
+    double *v = (double *)malloc((size_t)(V > 0 ? V : 1) * sizeof(double));
+    int64_t n = 0;
+    for (int64_t i = 0; i < V; ++i)
+        if (x[i] > -INFINITY) v[n++] = x[i];
+    double tau = -INFINITY;
+    if (n == 0) { free(v); return tau; }
+    qsort(v, (size_t)n, sizeof(double), or_cmp_desc);
+    int64_t nk = n;                                  /* tokens top-k keeps: v[0 .. nk) */
+    if (k > 0 && (int64_t)k < n) {
+        tau = v[k - 1];
+        nk = k;
+        while (nk < n && v[nk] == tau) ++nk;         /* ties with the k-th are kept */
+    }
+    if (p < 1.0) {
+        double S = 0.0;
+        for (int64_t i = 0; i < nk; ++i) S += exp((v[i] - v[0]) / t);
+        double P = p * S, cum = 0.0;
+        int64_t i = 0;
+        while (i < nk) {
+            int64_t j = i;                           /* the group of logits equal to v[i] */
+            double wsum = 0.0;
+            while (j < nk && v[j] == v[i]) { wsum += exp((v[j] - v[0]) / t); ++j; }
+            double before = cum;
+            cum += wsum;
+            if (cum >= P) {
+                if (v[i] > tau) tau = v[i];
+                *amb = (P - before < 1e-5 * S) || (cum - P < 1e-5 * S);
+                break;
+            }
+            i = j;
+        }
+    }
+    free(v);
+    return tau;
+}
+
+/* tau[r] and amb[r] of n rows; returns 0, -1 on a NaN/+inf logit. Rows with an invalid T or
+ * p get tau = NaN. */
+int or_filter_tau(const double *x, int64_t n, int64_t V, int64_t ld, const float *T,
+                  const int32_t *top_k, const float *top_p, double *tau, int32_t *amb)
+{
+    int bad = 0;
+    for (int64_t r = 0; r < n; ++r)
+        if (!or_row_ok(x + r * ld, V)) bad = 1;
+    if (bad) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n; ++r) {
+        double t = (double)T[r];
+        double p = top_p ? (double)top_p[r] : 1.0;
+        int a = 0;
+        if (!isfinite(t) || t < 0.0 || !(p > 0.0)) {
+            tau[r] = NAN;
+        } else {
+            tau[r] = or_filter_tau_row(x + r * ld, V, t, top_k ? top_k[r] : 0, p, &a);
+        }
+        if (amb) amb[r] = a;
+    }
+    return 0;
+}
+
+/* or_sample with the curve off and the kept set {x >= tau[r]} of or_filter_tau: tokens below
+ * the threshold are treated as masked. Outputs as or_sample; -2 also for an invalid p. */
+int or_sample_filtered(const double *x, int64_t n, int64_t V, int64_t ld,
+                       const int64_t *row_id, const float *T, const int32_t *top_k,
+                       const float *top_p, const uint64_t *seed, const uint64_t *offset,
+                       int32_t K, int32_t *out, double *best, double *second, double *tau,
+                       int32_t *amb)
+{
+    int rc = or_filter_tau(x, n, V, ld, T, top_k, top_p, tau, amb);
+    if (rc) return rc;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t rk = 0; rk < n * (int64_t)K; ++rk) {
+        int64_t r = rk / K;
+        int32_t k = (int32_t)(rk % K);
+        const double *xr = x + r * ld;
+        double *b1 = best ? best + rk : NULL;
+        double *b2 = second ? second + rk : NULL;
+        out[rk] = -1;
+        if (b1) *b1 = -INFINITY;
+        if (b2) *b2 = -INFINITY;
+        int64_t nfinite = 0;
+        for (int64_t i = 0; i < V; ++i) nfinite += (xr[i] > -INFINITY);
+        if (nfinite == 0) continue;                                   /* -1 */
+        double t = (double)T[r];
+        if (isnan(tau[r])) { out[rk] = -2; continue; }                /* bad T or p */
+        int64_t j = -1;
+        double s1 = -INFINITY, s2 = -INFINITY;
+        uint64_t off = offset[r] + (uint64_t)k;
+        for (int64_t i = 0; i < V; ++i) {
+            if (!(xr[i] > -INFINITY) || xr[i] < tau[r]) continue;
+            double s = (t == 0.0) ? xr[i]
+                                  : xr[i] / t + or_gumbel(or_element_word(seed[r],
+                                                                           (uint64_t)row_id[r],
+                                                                           off, (uint64_t)i));
+            if (j < 0 || s > s1) { s2 = s1; s1 = s; j = i; }
+            else if (s > s2) s2 = s;
+        }
+        out[rk] = (int32_t)j;
+        if (b1) *b1 = s1;
+        if (b2) *b2 = s2;
+    }
+    return 0;
 }

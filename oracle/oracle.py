@@ -56,6 +56,13 @@ def lib():
                                 C.c_int, C.c_float, C.c_float, C.c_float, C.c_float,
                                 C.c_int, C.c_float, u64p, u64p, C.c_int32, i32p, f64p, f64p]
         L.or_sample.restype = C.c_int
+        L.or_filter_tau.argtypes = [f64p, C.c_int64, C.c_int64, C.c_int64, f32p, i32p, f32p,
+                                    f64p, i32p]
+        L.or_filter_tau.restype = C.c_int
+        L.or_sample_filtered.argtypes = [f64p, C.c_int64, C.c_int64, C.c_int64, i64p, f32p,
+                                         i32p, f32p, u64p, u64p, C.c_int32, i32p, f64p, f64p,
+                                         f64p, i32p]
+        L.or_sample_filtered.restype = C.c_int
         _lib = L
     return _lib
 
@@ -201,3 +208,50 @@ def sample(x, T, seed, offset, K: int = 1, mu=None, hlg=None, row_id=None):
     if rc != 0:
         raise OracleError("NaN or +inf logit")
     return out, best, second
+
+
+# Top-k / top-p on the Gumbel path, curve off (see or_filter_tau in hs_oracle.c for the
+# reading): every token with a logit at or above the row's threshold tau is kept.
+def _filter_args(n, T, top_k, top_p):
+    T = np.ascontiguousarray(np.asarray(T, dtype=np.float32).reshape(n))
+    k = np.zeros(n, dtype=np.int32) if top_k is None else \
+        np.ascontiguousarray(np.broadcast_to(np.asarray(top_k, dtype=np.int32), (n,)))
+    p = np.ones(n, dtype=np.float32) if top_p is None else \
+        np.ascontiguousarray(np.broadcast_to(np.asarray(top_p, dtype=np.float32), (n,)))
+    return T, k, p
+
+
+def filter_threshold(x, T, top_k=None, top_p=None):
+    """(tau [n] float64, amb [n] bool): the kept set of row r is {i : x_ri >= tau_r}; tau is
+    -inf when nothing is filtered and NaN for an invalid T or p; amb marks rows whose top-p
+    crossing lies within 1e-5 of the mass target (an fp32 computation may take a neighbour)."""
+    x = _as_f64_rows(x)
+    n, V = x.shape
+    T, k, p = _filter_args(n, T, top_k, top_p)
+    tau = np.zeros(n, dtype=np.float64)
+    amb = np.zeros(n, dtype=np.int32)
+    if lib().or_filter_tau(x, n, V, V, T, k, p, tau, amb) != 0:
+        raise OracleError("NaN or +inf logit")
+    return tau, amb.astype(bool)
+
+
+def sample_filtered(x, T, seed, offset, K: int = 1, top_k=None, top_p=None, row_id=None):
+    """Gumbel-max draws over the tokens top-k / top-p keep (curve off): ids [n, K], the best and
+    second-best scores, and the threshold and ambiguity flag of every row."""
+    x = _as_f64_rows(x)
+    n, V = x.shape
+    T, k, p = _filter_args(n, T, top_k, top_p)
+    seed = np.ascontiguousarray(np.asarray(seed, dtype=np.uint64).reshape(n))
+    offset = np.ascontiguousarray(np.asarray(offset, dtype=np.uint64).reshape(n))
+    rid = np.arange(n, dtype=np.int64) if row_id is None else \
+        np.ascontiguousarray(np.asarray(row_id, dtype=np.int64).reshape(n))
+    out = np.zeros((n, K), dtype=np.int32)
+    best = np.zeros((n, K), dtype=np.float64)
+    second = np.zeros((n, K), dtype=np.float64)
+    tau = np.zeros(n, dtype=np.float64)
+    amb = np.zeros(n, dtype=np.int32)
+    rc = lib().or_sample_filtered(x, n, V, V, rid, T, k, p, seed, offset, int(K), out, best,
+                                  second, tau, amb)
+    if rc != 0:
+        raise OracleError("NaN or +inf logit")
+    return out, best, second, tau, amb.astype(bool)
