@@ -66,7 +66,7 @@ def load_traffic(name: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s: float = 10.0, settings=None):
+def cpu_baseline(w, budget_s: float = 10.0, settings=None, filters=None):
     """The oracle as it stands, all host cores, on the workload's rows: a first timed pass sizes
     the sample (the first rows, or whole passes over all rows repeated until about budget_s of
     work), then the sample is timed. Rows per second of the whole sample are reported."""
@@ -78,6 +78,10 @@ def cpu_baseline(w, budget_s: float = 10.0, settings=None):
     n = min(w.B, max(threads, 8))
 
     def run(rows):
+        if filters is not None:
+            O.sample_filtered(w.logits[:rows], w.T[:rows], w.seed[:rows], w.offset[:rows],
+                              K=w.K, top_k=filters[0], top_p=filters[1])
+            return
         if settings is None:
             O.sample(w.logits[:rows], w.T[:rows], w.seed[:rows], w.offset[:rows], K=w.K,
                      mu=None if w.hlg is None else w.mu[:rows], hlg=w.hlg)
@@ -174,6 +178,10 @@ def main():
     ap.add_argument("--per-row", action="store_true",
                     help="set the curve per row (hs_sample_rows), cycling over: off, given "
                          "pivot, top-anchored, entropy-anchored, with the workload's knobs")
+    ap.add_argument("--top-k", type=int, default=0,
+                    help="top-k filter on every row (turns the curve off; 0 = none)")
+    ap.add_argument("--top-p", type=float, default=1.0,
+                    help="top-p filter on every row (turns the curve off; 1 = none)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain device copy of MIB MiB five "
                          "times (reference for scaling the memory-traffic counters)")
@@ -208,6 +216,12 @@ def main():
     w = W.CONFIGS[args.config]()
     B, V, K = w.B, w.V, w.K
     settings = None
+    filtered = args.top_k > 0 or args.top_p < 1.0
+    if filtered:
+        # the filters act on the curve-off path
+        w.hlg = None
+        w.mu = None
+        w.name += ", curve off, top-k %d, top-p %g" % (args.top_k, args.top_p)
     if w.hlg is not None and args.pivot != "input":
         w.hlg = dict(w.hlg, pivot=args.pivot, pivot_offset=args.pivot_offset)
         w.name += ", pivot %s" % args.pivot + (" c=%g" % args.pivot_offset
@@ -241,7 +255,18 @@ def main():
     hp_ref = C.byref(hp) if hp is not None else None
     mu_ptr = mu.data_ptr() if mu is not None else None
 
+    topk_t = torch.full((B,), args.top_k, dtype=torch.int32, device=dev)
+    topp_t = torch.full((B,), args.top_p, dtype=torch.float32, device=dev)
+
     def launch(i, s_):
+        if filtered:
+            rc = L.hs_sample_filtered(C.byref(structs[i % len(structs)]), T.data_ptr(),
+                                      topk_t.data_ptr(), topp_t.data_ptr(), seed.data_ptr(),
+                                      off.data_ptr(), K, out.data_ptr(), None, ws.data_ptr(),
+                                      ws.numel(), None, s_)
+            if rc != 0:
+                raise hs.HsError(rc, "hs_sample_filtered")
+            return
         if rows is not None:
             rc = L.hs_sample_rows(C.byref(structs[i % len(structs)]), T.data_ptr(), mu_ptr,
                                   rows.data_ptr(), seed.data_ptr(), off.data_ptr(), K,
@@ -396,6 +421,8 @@ def main():
         name += "_" + args.pivot
     if rows is not None:
         name += "_rows"
+    if filtered:
+        name += "_filtered"
     traffic = load_traffic(name)
     log("step %.4f ms (events over the timed region), wall %.4f ms/step; per-launch event "
         "pairs p10 %.4f p50 %.4f p90 %.4f ms"
@@ -422,6 +449,8 @@ def main():
                    "hlg": w.hlg is not None, "input_copies": len(copies),
                    "pivot": (None if w.hlg is None else
                              "per_row" if rows is not None else w.hlg.get("pivot", "input")),
+                   "top_k": args.top_k if filtered else None,
+                   "top_p": args.top_p if filtered else None,
                    "launch": "hip_graph" if graph is not None else "eager",
                    "algorithmic_bytes_per_step": alg_bytes},
         "roofline": {"bound": "alu", "achieved": tops, "peak": ALU_PEAK_TOPS,
@@ -443,9 +472,10 @@ def main():
     if ceilings:
         rec["ceilings"] = ceilings
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, settings=settings)
+        rec["cpu_baseline"] = cpu_baseline(
+            w, settings=settings, filters=(args.top_k, args.top_p) if filtered else None)
         rec["cpu_baseline"]["cpu_model"] = cpu_model()
-        if settings is None and args.pivot == "input":
+        if settings is None and args.pivot == "input" and not filtered:
             rec["cpu_baseline"]["one_thread"] = cpu_one_thread(args.config,
                                                                1 if args.config == 5 else 16)
         log("cpu baseline:", rec["cpu_baseline"])

@@ -180,6 +180,32 @@ int hs_sample_rows(const hs_logits *x, const float *T, const float *mu, const hs
                    float *best, void *ws, size_t ws_bytes, const hs_sample_opts *opts,
                    void *stream);
 
+/* Top-k / top-p filters on the Gumbel path, curve off (the follow-on [GMX] names without an
+ * algorithm; the reading taken): temperature first, then top-k, then top-p on the tempered
+ * probabilities of the tokens top-k keeps. Row b keeps every token with x >= tau[b]:
+ *   - top-k (top_k[b] > 0): tau_k = the top_k[b]-th largest finite logit (ties with it are
+ *     kept); top_k[b] <= 0, or at least the number of finite logits, keeps every token;
+ *   - top-p (0 < top_p[b] < 1): among the tokens top-k keeps, sorted by logit, the logit at
+ *     which the mass exp((x - x_max) / T[b]), summed from the top, first reaches top_p[b]
+ *     times their total (every token with that logit is kept); top_p[b] >= 1 keeps every
+ *     token; top_p[b] <= 0 or NaN is invalid;
+ *   - tau[b] = max(tau_k, tau_p); -inf when nothing is filtered or T[b] == 0 (greedy); NaN
+ *     for an invalid T[b] or top_p[b].
+ * The top-p boundary is found with fp64 sums of fp32 terms. top_k: device int32[B] or NULL;
+ * top_p: device float[B] or NULL; tau: device float[B]. */
+int hs_filter_threshold(const hs_logits *x, const float *T, const int32_t *top_k,
+                        const float *top_p, float *tau, void *stream);
+
+/* hs_gumbel_argmax over the tokens the filters keep (hs_filter_threshold): the Gumbel-max of
+ * x / T over {i : x_i >= tau[b]}, an exact sample of softmax(x / T) renormalised over them
+ * [GMX, Background]. A row with an invalid T or top_p gives -2; greedy rows (T == 0) are the
+ * argmax of x. A workspace of hs_workspace_bytes(B, V, K, dtype, 0) bytes is required (the
+ * thresholds live in it). best and opts as hs_sample_ex (NULL allowed). */
+int hs_sample_filtered(const hs_logits *x, const float *T, const int32_t *top_k,
+                       const float *top_p, const uint64_t *seed, const uint64_t *offset,
+                       int32_t K, int32_t *out, float *best, void *ws, size_t ws_bytes,
+                       const hs_sample_opts *opts, void *stream);
+
 /* Philox4x32-10 [P123] on n (counter, key) pairs: ctr device uint32[4n], key device
  * uint32[2n], out device uint32[4n]. Uses the same device routine as the samplers. */
 int hs_philox4x32_10(const uint32_t *ctr, const uint32_t *key, uint32_t *out, int64_t n,

@@ -18,7 +18,8 @@ import torch
 
 __all__ = [
     "HsError", "HlgParams", "SampleOpts", "load", "library_path", "EXPORTED_SYMBOLS",
-    "sample", "sample_ex", "sample_rows", "hlg_rows", "gumbel_argmax", "logsumexp",
+    "sample", "sample_ex", "sample_rows", "hlg_rows", "sample_filtered", "filter_threshold",
+    "gumbel_argmax", "logsumexp",
     "hlg_transform", "hlg_pivot",
     "workspace_bytes", "PIVOTS",
     "workspace", "philox4x32_10", "stream_words", "gumbel_f32", "version",
@@ -32,7 +33,7 @@ _DTYPES = {torch.float32: HS_F32, torch.bfloat16: HS_BF16, torch.float16: HS_F16
 
 EXPORTED_SYMBOLS = (
     "hs_logsumexp", "hs_hlg_transform", "hs_hlg_pivot", "hs_gumbel_argmax", "hs_sample",
-    "hs_sample_ex", "hs_sample_rows",
+    "hs_sample_ex", "hs_sample_rows", "hs_filter_threshold", "hs_sample_filtered",
     "hs_workspace_bytes", "hs_workspace_init", "hs_philox4x32_10", "hs_stream_words",
     "hs_gumbel_f32", "hs_status_str", "hs_version",
 )
@@ -113,6 +114,8 @@ def load() -> C.CDLL:
     L.hs_sample.argtypes = [LP, vp, vp, HP, vp, vp, i32, vp, vp, sz, vp]
     L.hs_sample_ex.argtypes = [LP, vp, vp, HP, vp, vp, i32, vp, vp, vp, sz, OP, vp]
     L.hs_sample_rows.argtypes = [LP, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, OP, vp]
+    L.hs_filter_threshold.argtypes = [LP, vp, vp, vp, vp, vp]
+    L.hs_sample_filtered.argtypes = [LP, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, OP, vp]
     L.hs_workspace_bytes.argtypes = [i64, i64, i32, i32, i32]
     L.hs_workspace_bytes.restype = sz
     L.hs_workspace_init.argtypes = [vp, sz, vp]
@@ -124,7 +127,8 @@ def load() -> C.CDLL:
     L.hs_version.argtypes = []
     L.hs_version.restype = C.c_char_p
     for name in ("hs_logsumexp", "hs_hlg_transform", "hs_hlg_pivot", "hs_gumbel_argmax", "hs_sample",
-                 "hs_sample_ex", "hs_sample_rows", "hs_workspace_init", "hs_philox4x32_10", "hs_stream_words",
+                 "hs_sample_ex", "hs_sample_rows", "hs_filter_threshold", "hs_sample_filtered",
+                 "hs_workspace_init", "hs_philox4x32_10", "hs_stream_words",
                  "hs_gumbel_f32"):
         getattr(L, name).restype = C.c_int
     _lib = L
@@ -331,6 +335,55 @@ def sample_rows(logits: torch.Tensor, T, seed, offset, rows, *, mu=None, k: int 
                           of.data_ptr(), int(k), out.data_ptr(), _ptr(best), ws.data_ptr(),
                           ws.numel(), C.byref(opts) if opts is not None else None, _stream(dev))
     _check(rc, "hs_sample_rows")
+    return (out, best) if want_best else out
+
+
+def _filter_vecs(top_k, top_p, B, dev):
+    kt = _row_vec(top_k, B, torch.int32, dev, "top_k") if top_k is not None else None
+    pt = _row_vec(top_p, B, torch.float32, dev, "top_p") if top_p is not None else None
+    return kt, pt
+
+
+def filter_threshold(logits: torch.Tensor, T, top_k=None, top_p=None) -> torch.Tensor:
+    """The top-k / top-p threshold tau [B] (float32) of every row, curve off: a row keeps the
+    tokens with logit >= tau; -inf keeps all, NaN marks an invalid T or top_p."""
+    L = load()
+    x = _logits_struct(logits)
+    dev = logits.device
+    B = logits.shape[0]
+    Tt = _row_vec(T, B, torch.float32, dev, "T")
+    kt, pt = _filter_vecs(top_k, top_p, B, dev)
+    tau = torch.empty(B, dtype=torch.float32, device=dev)
+    _check(L.hs_filter_threshold(C.byref(x), Tt.data_ptr(), _ptr(kt), _ptr(pt), tau.data_ptr(),
+                                 _stream(dev)), "hs_filter_threshold")
+    return tau
+
+
+def sample_filtered(logits: torch.Tensor, T, seed, offset, *, top_k=None, top_p=None,
+                    k: int = 1, out: Optional[torch.Tensor] = None,
+                    ws: Optional[torch.Tensor] = None, opts: Optional[SampleOpts] = None,
+                    want_best: bool = False):
+    """Gumbel-max draws over the tokens top-k / top-p keep (curve off): ids [B, k] (int32)
+    and, with want_best, the winning scores. top_k (int, per row) <= 0 and top_p >= 1 turn a
+    filter off; rows with an invalid T or top_p give -2."""
+    L = load()
+    x = _logits_struct(logits)
+    dev = logits.device
+    B = logits.shape[0]
+    Tt = _row_vec(T, B, torch.float32, dev, "T")
+    st = _row_vec(seed, B, torch.int64, dev, "seed")
+    of = _row_vec(offset, B, torch.int64, dev, "offset")
+    kt, pt = _filter_vecs(top_k, top_p, B, dev)
+    if out is None:
+        out = torch.empty((B, k), dtype=torch.int32, device=dev)
+    best = torch.empty((B, k), dtype=torch.float32, device=dev) if want_best else None
+    if ws is None:
+        ws = workspace(B, logits.shape[1], k, logits.dtype, False, dev)
+    rc = L.hs_sample_filtered(C.byref(x), Tt.data_ptr(), _ptr(kt), _ptr(pt), st.data_ptr(),
+                              of.data_ptr(), int(k), out.data_ptr(), _ptr(best), ws.data_ptr(),
+                              ws.numel(), C.byref(opts) if opts is not None else None,
+                              _stream(dev))
+    _check(rc, "hs_sample_filtered")
     return (out, best) if want_best else out
 
 

@@ -73,7 +73,7 @@ int num_cus() {
 }
 
 struct WsLayout {
-    size_t counters, keys, partials, total;
+    size_t counters, keys, partials, tau, total;
 };
 
 WsLayout ws_layout(int64_t B, int32_t K) {
@@ -81,7 +81,8 @@ WsLayout ws_layout(int64_t B, int32_t K) {
     L.counters = 0;
     L.keys = align256((size_t)B * (size_t)K * 4);   // counters: one per (row, draw group)
     L.partials = L.keys + align256((size_t)B * (size_t)K * 8);
-    L.total = L.partials + align256((size_t)B * hs::kMaxChunks * sizeof(float4));
+    L.tau = L.partials + align256((size_t)B * hs::kMaxChunks * sizeof(float4));
+    L.total = L.tau + align256((size_t)B * 4);   // top-k / top-p thresholds
     return L;
 }
 
@@ -174,11 +175,18 @@ bool opts_valid(const hs_sample_opts *o) {
                    o->nchunk > hs::kMaxChunks || o->draw_groups < 0);
 }
 
-// rows: per-row curve settings (device), or NULL for the per-call curve hlg (or none).
+// Top-k / top-p parameters of a filtered call (device arrays, either may be null).
+struct Filter {
+    const int32_t *top_k;
+    const float *top_p;
+};
+
+// rows: per-row curve settings (device), or NULL for the per-call curve hlg (or none);
+// filt: top-k / top-p filters (curve off), or NULL.
 int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hlg_params *hlg,
                 const hs_hlg_row *rows, const uint64_t *seed, const uint64_t *offset, int32_t K,
                 int32_t *out, float *best, void *ws, size_t ws_bytes,
-                const hs_sample_opts *opts, void *stream) {
+                const hs_sample_opts *opts, void *stream, const Filter *filt = nullptr) {
     int rc = check_logits(x);
     if (rc) return rc;
     if (!T || !seed || !offset || !out || K < 1) return HS_ERR_INVALID_ARG;
@@ -188,6 +196,7 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
         if (hlg->pivot == HS_PIVOT_GIVEN && !mu) return HS_ERR_INVALID_ARG;
     }
     if (rows && hlg) return HS_ERR_INVALID_ARG;
+    if (filt && (hlg || rows)) return HS_ERR_INVALID_ARG;
     const bool curve_on = hlg != nullptr || rows != nullptr;
     if ((size_t)x->B * (size_t)K >= ((size_t)1 << 31)) return HS_ERR_UNSUPPORTED;
     const WsLayout L = ws_layout(x->B, K);
@@ -197,6 +206,8 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
         if (ws_bytes < L.total) return HS_ERR_WORKSPACE;
         return HS_ERR_INVALID_ARG;
     }
+    const bool filtering = filt && (filt->top_k || filt->top_p);
+    if (filtering && !ws_ok) return HS_ERR_WORKSPACE;   // the thresholds live in it
     Plan P;
     rc = make_plan(x, K, curve_on, ws_ok, opts, &P);
     if (rc) return rc;
@@ -233,6 +244,19 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
         a.part_stride = hs::kMaxChunks;
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (filtering) {
+        hs::FilterArgs f{};
+        f.data = x->data;
+        f.ld = x->ld;
+        f.V = x->V;
+        f.aligned = a.aligned;
+        f.T = T;
+        f.top_k = filt->top_k;
+        f.top_p = filt->top_p;
+        f.tau = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + L.tau);
+        if (hs::launch_filter_tau(x->dtype, f, (int)x->B, s) != hipSuccess) return HS_ERR_HIP;
+        a.tau = f.tau;
+    }
     if (curve_on && P.nchunk > 1) {
         const int bs = P.cv >= 4096 ? 1024 : 256;
         if (hs::launch_lse_partial(x->dtype, piv, a, bs, (int)(x->B * P.nchunk), s) != hipSuccess)
@@ -324,6 +348,34 @@ int hs_sample_ex(const hs_logits *x, const float *T, const float *mu, const hs_h
     if (!opts_valid(opts)) return HS_ERR_INVALID_ARG;
     return sample_impl(x, T, mu, hlg, nullptr, seed, offset, K, out, best, ws, ws_bytes, opts,
                        stream);
+}
+
+int hs_filter_threshold(const hs_logits *x, const float *T, const int32_t *top_k,
+                        const float *top_p, float *tau, void *stream) {
+    int rc = check_logits(x);
+    if (rc) return rc;
+    if (!T || !tau) return HS_ERR_INVALID_ARG;
+    hs::FilterArgs f{};
+    f.data = x->data;
+    f.ld = x->ld;
+    f.V = x->V;
+    f.aligned = rows_aligned(x) ? 1 : 0;
+    f.T = T;
+    f.top_k = top_k;
+    f.top_p = top_p;
+    f.tau = tau;
+    return hs::launch_filter_tau(x->dtype, f, (int)x->B, reinterpret_cast<hipStream_t>(stream))
+                   == hipSuccess ? HS_OK : HS_ERR_HIP;
+}
+
+int hs_sample_filtered(const hs_logits *x, const float *T, const int32_t *top_k,
+                       const float *top_p, const uint64_t *seed, const uint64_t *offset,
+                       int32_t K, int32_t *out, float *best, void *ws, size_t ws_bytes,
+                       const hs_sample_opts *opts, void *stream) {
+    if (!opts_valid(opts)) return HS_ERR_INVALID_ARG;
+    const Filter f{top_k, top_p};
+    return sample_impl(x, T, nullptr, nullptr, nullptr, seed, offset, K, out, best, ws,
+                       ws_bytes, opts, stream, &f);
 }
 
 int hs_sample_rows(const hs_logits *x, const float *T, const float *mu, const hs_hlg_row *rows,

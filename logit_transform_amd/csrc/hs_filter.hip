@@ -1,0 +1,315 @@
+// hs_filter.hip -- the per-row logit threshold of the top-k / top-p filters on the Gumbel path
+// (curve off). The Gumbel-max issue names rejection-based top-k / top-p as its follow-on
+// without an algorithm ("Softmax-free GPU sampling", the follow-on list). Reading taken:
+// temperature first, then top-k, then top-p on the tempered probabilities of the tokens top-k
+// keeps; each filter keeps every token whose logit is at or above a threshold tau (ties
+// included), and the sampler draws the Gumbel-max of x / T over the kept tokens, an exact
+// sample of the renormalised softmax [GMX, Background].
+//
+// One block per row finds tau by radix selection over an order-preserving integer key of
+// the logit, each level a pass over the row (which stays in the caches after the first) that
+// histograms one digit of the keys sharing the digits selected so far: 11 + 5 bits for bf16 /
+// f16, 11 + 11 + 10 for fp32 (a wide first digit spreads the bulk of a row over many bins, so
+// the LDS atomics seldom collide). Top-k selects the k-th largest finite key by counts (its
+// first pass also finds the row's maximum and finite count); top-p selects, among the keys
+// top-k keeps, the key at which the tempered mass exp((x - x_max) / T), summed from the top,
+// reaches p times the total, by fp64 sums of fp32 terms. Wave 0 picks each level's bin with a
+// parallel scan over the bins.
+#include <hip/hip_runtime.h>
+
+#include "hs_device.hpp"
+#include "hs_internal.hpp"
+
+namespace hs {
+namespace {
+
+// Order-preserving keys (-0 folded onto +0); -inf keys sort below every finite key and
+// every finite key is > 0.
+__device__ __forceinline__ uint32_t key16(uint32_t h) {
+    if (h == 0x8000u) h = 0u;
+    return (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
+}
+__device__ __forceinline__ uint32_t key32(uint32_t u) {
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t elem_key(const uint4 &v, int e) {
+    if constexpr (DT == DT_F32) {
+        const uint32_t w = e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+        return key32(w);
+    } else {
+        const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+        return key16((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ float key_value(uint32_t key) {
+    if constexpr (DT == DT_F32) {
+        return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+    } else {
+        const uint32_t h = (key & 0x8000u) ? (key & 0x7FFFu) : (~key & 0xFFFFu);
+        if constexpr (DT == DT_BF16) return __uint_as_float(h << 16);
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+    }
+}
+
+// (wave 0) The bin, scanning the NB bins from the top, at which the running total first
+// reaches target, and the total of the bins above it. A total that falls short by rounding
+// takes the lowest non-empty bin. Lane l holds the bins NB-1-l*CPL ... NB-CPL-l*CPL.
+template <typename Cnt, int NB>
+__device__ __forceinline__ void select_bin(const Cnt *hist, Cnt target, int lane, int *bin,
+                                           Cnt *above) {
+    constexpr int CPL = NB >= 64 ? NB / 64 : 1;
+    Cnt c[CPL];
+    Cnt own = 0;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const int r = lane * CPL + j;   // rank from the top
+        c[j] = r < NB ? hist[NB - 1 - r] : (Cnt)0;
+        own += c[j];
+    }
+    Cnt incl = own;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const Cnt o = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += o;
+    }
+    const Cnt excl = incl - own;
+    const uint64_t hit = __ballot(incl >= target);
+    const uint64_t nonempty = __ballot(own > 0);
+    const int src = hit ? __builtin_ctzll(hit) : 63 - __builtin_clzll(nonempty | 1ull);
+    int b = -1;
+    Cnt ab = excl;
+    if (lane == src) {
+        Cnt run = excl;
+        int last = -1;
+        Cnt last_above = excl;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            if (c[j] > 0) {
+                last = j;
+                last_above = run;
+            }
+            if (b < 0 && hit && run + c[j] >= target) {
+                b = j;
+                ab = run;
+            }
+            run += c[j];
+        }
+        if (b < 0) {
+            b = last < 0 ? 0 : last;
+            ab = last < 0 ? excl : last_above;
+        }
+        b = NB - 1 - (lane * CPL + b);
+    }
+    *bin = __shfl(b, src, 64);
+    *above = __shfl(ab, src, 64);
+}
+
+// The digits of a key, most significant first: widths and shifts per level.
+template <int DT> struct Digits;
+template <> struct Digits<DT_F32> {
+    static constexpr int n = 3;
+    static constexpr int bits[3] = {11, 11, 10};
+    static constexpr int shift[3] = {21, 10, 0};
+};
+template <> struct Digits<DT_BF16> {
+    static constexpr int n = 2;
+    static constexpr int bits[2] = {11, 5};
+    static constexpr int shift[2] = {5, 0};
+};
+template <> struct Digits<DT_F16> : Digits<DT_BF16> {};
+
+__device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t *red) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int nw = (blockDim.x + 63) >> 6;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+    if (lane == 0) red[wid] = v;
+    __syncthreads();
+    uint32_t t = lane < nw ? red[lane] : 0u;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) t += __shfl_xor(t, d, 64);
+    __syncthreads();
+    return t;
+}
+
+// One level of the selection: the histogram (counts, or masses w(x)) of digit `lev` over the
+// finite keys >= kmin whose higher digits equal prefix, then the bin where the total from the
+// top reaches target (wave 0). Returns the new prefix; *tgt (wave 0) becomes what is left to
+// reach inside the bin.
+template <int DT, int LEV, typename Cnt, typename W>
+__device__ __forceinline__ uint32_t select_level(const char *rowp, int64_t nvec, int64_t V,
+                                                 int32_t aligned, uint32_t prefix, uint32_t kmin,
+                                                 Cnt *hist, Cnt *tgt, W weight, int lane,
+                                                 int wid) {
+    using D = Digits<DT>;
+    constexpr int EPV = dtype_traits<DT>::epv;
+    constexpr int NB = 1 << D::bits[LEV];
+    constexpr int SH = D::shift[LEV];
+    for (int j = threadIdx.x; j < NB; j += blockDim.x) hist[j] = (Cnt)0;
+    __syncthreads();
+    for (int64_t gv = threadIdx.x; gv < nvec; gv += blockDim.x) {
+        const uint4 v = load_vec<DT>(rowp, gv, V, aligned);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+            const float x = elem<DT>(v, e);
+            const uint32_t key = elem_key<DT>(v, e);
+            bool in = x > -__builtin_inff() && key >= kmin;
+            if constexpr (LEV > 0) in = in && (key >> (SH + D::bits[LEV])) == prefix;
+            if (in) atomicAdd(&hist[(key >> SH) & (uint32_t)(NB - 1)], weight(x));
+        }
+    }
+    __syncthreads();
+    __shared__ uint32_t s_new;
+    if (wid == 0) {
+        int bin;
+        Cnt above;
+        select_bin<Cnt, NB>(hist, *tgt, lane, &bin, &above);
+        *tgt -= above;
+        if (lane == 0) s_new = (prefix << D::bits[LEV]) | (uint32_t)bin;
+    }
+    __syncthreads();
+    return s_new;
+}
+
+template <int DT>
+__global__ __launch_bounds__(1024) void k_filter_tau(FilterArgs a) {
+    using tr = dtype_traits<DT>;
+    using D = Digits<DT>;
+    constexpr int EPV = tr::epv;
+    __shared__ uint32_t hc[2048];
+    __shared__ double hm[2048];
+    __shared__ float red_f[16];
+    __shared__ uint32_t red_n[16];
+
+    const int64_t b = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const float T = a.T[b];
+    // a k of at least V keeps every token, as does k <= 0
+    int32_t k = a.top_k ? a.top_k[b] : 0;
+    if ((int64_t)k >= a.V) k = 0;
+    const float p = a.top_p ? a.top_p[b] : 1.0f;
+    // invalid temperature or p: NaN, which the sampler turns into -2 for the row
+    if (!(T >= 0.0f) || !(T < __builtin_inff()) || !(p > 0.0f)) {
+        if (tid == 0) a.tau[b] = __builtin_nanf("");
+        return;
+    }
+    if (T == 0.0f || (k <= 0 && !(p < 1.0f))) {   // greedy, or nothing to filter
+        if (tid == 0) a.tau[b] = -__builtin_inff();
+        return;
+    }
+    const char *rowp = reinterpret_cast<const char *>(a.data) + b * a.ld * tr::esize;
+    const int64_t nvec = (a.V + EPV - 1) / EPV;
+
+    // the row's maximum and finite count (with top-k on, its first level counts them too)
+    float M = -__builtin_inff();
+    uint32_t NF = 0u;
+    uint32_t keyk = 0u;   // 0: every finite key passes
+    float tau = -__builtin_inff();
+    if (k > 0) {
+        uint32_t tgt = (uint32_t)k;   // (wave 0) rank still to go inside the selected bin
+        float mx = -__builtin_inff();
+        auto one = [&](float x) {
+            mx = fmaxf(mx, x);
+            return 1u;
+        };
+        uint32_t prefix = select_level<DT, 0>(rowp, nvec, a.V, a.aligned, 0u, 0u, hc, &tgt, one,
+                                              lane, wid);
+        M = block_max(mx, red_f);
+        // the level's bins hold every finite key: their total is the finite count
+        uint32_t part = 0u;
+        for (int j = tid; j < (1 << D::bits[0]); j += blockDim.x) part += hc[j];
+        NF = block_sum_u32(part, red_n);
+        if ((uint32_t)k < NF) {
+            prefix = select_level<DT, 1>(rowp, nvec, a.V, a.aligned, prefix, 0u, hc, &tgt,
+                                         [](float) { return 1u; }, lane, wid);
+            if constexpr (D::n == 3)
+                prefix = select_level<DT, 2>(rowp, nvec, a.V, a.aligned, prefix, 0u, hc, &tgt,
+                                             [](float) { return 1u; }, lane, wid);
+            keyk = prefix;
+            tau = key_value<DT>(keyk);
+        }
+    } else {
+        uint32_t nf = 0u;
+        float mx = -__builtin_inff();
+        for (int64_t gv = tid; gv < nvec; gv += blockDim.x) {
+            const uint4 v = load_vec<DT>(rowp, gv, a.V, a.aligned);
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                const float x = elem<DT>(v, e);
+                nf += x > -__builtin_inff() ? 1u : 0u;
+                mx = fmaxf(mx, x);
+            }
+        }
+        M = block_max(mx, red_f);
+        NF = block_sum_u32(nf, red_n);
+    }
+    if (NF == 0u) {
+        if (tid == 0) a.tau[b] = -__builtin_inff();
+        return;
+    }
+
+    // top-p over the tokens top-k keeps: the key at which the tempered mass from the top
+    // reaches p times their total
+    if (p < 1.0f) {
+        const float c1 = kLog2e / T;
+        auto mass = [=](float x) { return (double)__builtin_amdgcn_exp2f((x - M) * c1); };
+        // the target needs the kept tokens' total mass: wave 0 sums the first level's bins
+        // before selecting (a target of +inf selects nothing; it is set below)
+        double tgt = 0.0;
+        for (int j = tid; j < (1 << D::bits[0]); j += blockDim.x) hm[j] = 0.0;
+        __syncthreads();
+        for (int64_t gv = tid; gv < nvec; gv += blockDim.x) {
+            const uint4 v = load_vec<DT>(rowp, gv, a.V, a.aligned);
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                const float x = elem<DT>(v, e);
+                const uint32_t key = elem_key<DT>(v, e);
+                if (x > -__builtin_inff() && key >= keyk)
+                    atomicAdd(&hm[key >> D::shift[0]], mass(x));
+            }
+        }
+        __syncthreads();
+        __shared__ uint32_t s_p0;
+        if (wid == 0) {
+            constexpr int NB = 1 << D::bits[0];
+            double t = 0.0;
+            for (int j = lane; j < NB; j += 64) t += hm[j];
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) t += __shfl_xor(t, d, 64);
+            tgt = (double)p * t;
+            int bin;
+            double above;
+            select_bin<double, NB>(hm, tgt, lane, &bin, &above);
+            tgt -= above;
+            if (lane == 0) s_p0 = (uint32_t)bin;
+        }
+        __syncthreads();
+        uint32_t prefix = s_p0;
+        prefix = select_level<DT, 1>(rowp, nvec, a.V, a.aligned, prefix, keyk, hm, &tgt, mass,
+                                     lane, wid);
+        if constexpr (D::n == 3)
+            prefix = select_level<DT, 2>(rowp, nvec, a.V, a.aligned, prefix, keyk, hm, &tgt,
+                                         mass, lane, wid);
+        tau = fmaxf(tau, key_value<DT>(prefix));
+    }
+    if (tid == 0) a.tau[b] = tau;
+}
+
+}  // namespace
+
+hipError_t launch_filter_tau(int dt, const FilterArgs &a, int grid, hipStream_t s) {
+    switch (dt) {
+        case DT_F32: hipLaunchKernelGGL(k_filter_tau<DT_F32>, dim3(grid), dim3(1024), 0, s, a); break;
+        case DT_BF16: hipLaunchKernelGGL(k_filter_tau<DT_BF16>, dim3(grid), dim3(1024), 0, s, a); break;
+        case DT_F16: hipLaunchKernelGGL(k_filter_tau<DT_F16>, dim3(grid), dim3(1024), 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace hs

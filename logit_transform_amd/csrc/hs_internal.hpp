@@ -49,6 +49,7 @@ struct SampleArgs {
     int64_t part_stride;
     float pivot_offset;        // c of the top anchor
     const RowCurve *row_curves;   // [B] per-row curve settings (pivot mode 3), else null
+    const float *tau;             // [B] top-k / top-p thresholds (curve off), else null
 };
 
 struct RowOpArgs {
@@ -63,6 +64,19 @@ struct RowOpArgs {
     float pivot_offset;   // c of the top anchor
     float *mu_out;        // the pivot of every row (op 2)
 };
+
+// Top-k / top-p threshold of every row (curve off): tau[b] = -inf keeps every token, NaN marks
+// an invalid temperature or p.
+struct FilterArgs {
+    const void *data;
+    int64_t ld, V;
+    int32_t aligned;
+    const float *T;
+    const int32_t *top_k;   // [B] or null (0: no top-k)
+    const float *top_p;     // [B] or null (1: no top-p)
+    float *tau;             // [B]
+};
+hipError_t launch_filter_tau(int dt, const FilterArgs &a, int grid, hipStream_t s);
 
 // piv: the curve's pivot, 0 given per row, 1 top-anchored, 2 entropy-anchored, 3 set per row
 // (a.row_curves)

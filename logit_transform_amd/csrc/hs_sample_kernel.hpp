@@ -195,6 +195,15 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             rpiv = -1;
         }
     }
+    // top-k / top-p (curve off): tokens below the row's threshold are not candidates; a NaN
+    // threshold marks an invalid filter parameter
+    float tau_row = -__builtin_inff();
+    if constexpr (!HLG) {
+        if (a.tau) {
+            tau_row = a.tau[b];
+            bad = bad || !(tau_row == tau_row);
+        }
+    }
     const bool greedy = (T == 0.0f);
 
     // ---- this block's chunk of the row: lane t owns vectors v0 + t + n*BS, n < NV ----
@@ -392,7 +401,8 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             }
         }
         const float nlv = __builtin_amdgcn_logf(__builtin_fmaf((float)(~c.w), 0x1p-32f, 0x1p-33f));
-        const bool ok = c.x > -__builtin_inff() && lane_v + (int)(champ & 31u) * BS < vend;
+        const bool ok = c.x > -__builtin_inff() && (HLG || c.x >= tau_row) &&
+                        lane_v + (int)(champ & 31u) * BS < vend;
         c.key = ok ? make_key(__builtin_fmaf(c.x, lin, -nlv * kLn2), (uint32_t)tid) : 0ull;
         return c;
     };
@@ -685,7 +695,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
         for (int e = 0; e < EPV; ++e) {
             const float x = elem<DT>(v, e);
             const float cf = (float)__clz(~w[e]);
-            if (x > -__builtin_inff() && cf >= code_needed(x)) {
+            if (x > -__builtin_inff() && (HLG || x >= tau_row) && cf >= code_needed(x)) {
                 const uint32_t i = (uint32_t)gv * EPV + e;
                 best = umax64(best, make_key(exact_score<HLG>(x, w[e], rc), i));
             }
@@ -771,7 +781,10 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                 for (int n = NV - 1; n >= 0; --n) {
                     const uint32_t d = s_vec[lane_lds + n];
                     const float xm = __uint_as_float(d << 16);
-                    const float need = fminf(fminf(__builtin_fmaf(xm, sa, sb), sc), 16.0f);
+                    float need = fminf(fminf(__builtin_fmaf(xm, sa, sb), sc), 16.0f);
+                    // (curve off) a vector whose largest logit is below the filter threshold
+                    // holds no candidate: a code no word reaches
+                    if constexpr (!HLG) need = xm >= tau_row ? need : 17.0f;
                     bits = (bits << 1) | ((float)lead_ones_hi16(d) >= need ? 1u : 0u);
                 }
             }

@@ -209,6 +209,21 @@ def test_hlg_rows_packing():
     assert vals[2][:2] == (0.5, math.inf) and vals[2][4:] == (1, 6.0, 1, 0)
 
 
+def test_filter_args(lib):
+    x = L()
+    assert lib.hs_filter_threshold(C.byref(x), None, FAKE, FAKE, FAKE, None) == HS_ERR_INVALID_ARG
+    assert lib.hs_filter_threshold(C.byref(x), FAKE, FAKE, FAKE, None, None) == HS_ERR_INVALID_ARG
+    assert lib.hs_filter_threshold(C.byref(L(dtype=5)), FAKE, None, None, FAKE, None) == HS_ERR_DTYPE
+    o = hs.SampleOpts(nchunk=99)
+    assert lib.hs_sample_filtered(C.byref(x), FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, None, None,
+                                  0, C.byref(o), None) == HS_ERR_INVALID_ARG
+    assert lib.hs_sample_filtered(C.byref(x), FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None, None,
+                                  0, None, None) == HS_ERR_INVALID_ARG
+    # filtering needs the workspace (the thresholds live in it)
+    assert lib.hs_sample_filtered(C.byref(x), FAKE, FAKE, None, FAKE, FAKE, 1, FAKE, None, None,
+                                  0, None, None) == HS_ERR_WORKSPACE
+
+
 def test_aux_entry_points(lib):
     assert lib.hs_philox4x32_10(None, FAKE, FAKE, 4, None) == HS_ERR_INVALID_ARG
     assert lib.hs_philox4x32_10(FAKE, FAKE, FAKE, -1, None) == HS_ERR_INVALID_ARG

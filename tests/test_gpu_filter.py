@@ -1,0 +1,135 @@
+"""Top-k / top-p on the Gumbel path (curve off) on the HIP path against the oracle.
+
+Reading (the Gumbel-max issue, "Softmax-free GPU sampling", names the filters as its follow-on
+without an algorithm): temperature first, then top-k, then top-p on the tempered probabilities
+of the tokens top-k keeps; row b keeps every token with x >= tau_b; the draw is the Gumbel-max
+of x / T over the kept tokens.
+
+Thresholds: a top-k threshold is a logit of the row and must equal the oracle's exactly. A
+top-p threshold is decided by a mass sum: rows where the oracle's crossing lies within 1e-5 of
+the target (flagged by the oracle) may take a neighbouring logit, so there the GPU threshold
+must lie between the oracle's for p (1 + 2e-5) and p (1 - 2e-5), and its draws are checked
+against that threshold only (a kept token, never a masked one). Elsewhere ids follow the
+near-tie rule of the other parity tests."""
+import numpy as np
+import pytest
+import torch
+
+from synth import workloads as W
+from tests.gpu_util import assert_parity, on_device, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def hs():
+    return require_gpu()
+
+
+def _case(B, V, dtype, seed, mask_frac=0.05, K=3):
+    w = W.generic(B, V, dtype, seed=seed, scale=1.5, mask_frac=mask_frac, K=K)
+    rng = np.random.default_rng(seed + 1)
+    k = rng.choice([0, 1, 5, 50, 1000, V + 3], size=B).astype(np.int32)
+    p = rng.choice([1.0, 0.5, 0.9, 0.95, 0.3, 0.999], size=B).astype(np.float32)
+    return w, k, p
+
+
+def _check_rows(hs, O, w, k, p, label, opts=None, want_best=False):
+    d = on_device(w)
+    kt = torch.from_numpy(k).cuda()
+    pt = torch.from_numpy(p).cuda()
+    tau_g = hs.filter_threshold(d["logits"], d["T"], top_k=kt, top_p=pt).cpu().numpy()
+    o, s1, s2, tau_o, amb = O.sample_filtered(w.logits, w.T, w.seed, w.offset, K=w.K, top_k=k,
+                                              top_p=p)
+    x64 = w.logits.double().numpy()
+    # thresholds
+    for r in range(w.B):
+        if np.isnan(tau_o[r]):
+            assert np.isnan(tau_g[r]), (label, r)
+        elif not amb[r]:
+            assert tau_g[r] == tau_o[r], (label, r, tau_g[r], tau_o[r])
+        else:
+            hi = O.filter_threshold(x64[r:r + 1], w.T[r:r + 1], top_k=k[r:r + 1],
+                                    top_p=np.float32(min(1.0, p[r] * (1 - 2e-5))))[0][0]
+            lo = O.filter_threshold(x64[r:r + 1], w.T[r:r + 1], top_k=k[r:r + 1],
+                                    top_p=np.float32(min(1.0, p[r] * (1 + 2e-5))))[0][0]
+            assert lo <= tau_g[r] <= hi, (label, r, lo, tau_g[r], hi)
+    res = hs.sample_filtered(d["logits"], d["T"], d["seed"], d["offset"], top_k=kt, top_p=pt,
+                             k=w.K, opts=opts, want_best=want_best)
+    g = (res[0] if want_best else res).cpu().numpy()
+    sure = ~amb
+    assert_parity(g[sure], o[sure], s1[sure], s2[sure], x64[sure], label)
+    for r in np.nonzero(amb)[0]:
+        assert np.all(g[r] >= 0) and np.all(x64[r, g[r]] >= tau_g[r]), (label, r)
+    return (g, res[1].cpu().numpy()) if want_best else g
+
+
+@pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 151936), (torch.float32, 50001),
+                                     (torch.float16, 32000), (torch.bfloat16, 1000),
+                                     (torch.float32, 7)])
+def test_filters_match_oracle(hs, oracle_mod, dtype, V):
+    w, k, p = _case(12, V, dtype, seed=V % 977 + 1, mask_frac=0.05 if V > 10 else 0.0)
+    _check_rows(hs, oracle_mod, w, k, p, "filters %s V=%d" % (dtype, V))
+
+
+def test_filter_kernel_choices(hs, oracle_mod):
+    """One block per row, split rows and draw groups, screened and exhaustive: the same ids;
+    screened and exhaustive scoring bit-identical."""
+    w, k, p = _case(6, 70001, torch.bfloat16, seed=5, K=4)
+    res = {}
+    for name, opts in [("one-block", hs.SampleOpts(variant=1)),
+                       ("split7", hs.SampleOpts(variant=2, nchunk=7)),
+                       ("split3-groups2", hs.SampleOpts(variant=2, nchunk=3, draw_groups=2)),
+                       ("one-block-exhaustive", hs.SampleOpts(variant=1, no_screen=1)),
+                       ("split7-exhaustive", hs.SampleOpts(variant=2, nchunk=7, no_screen=1))]:
+        res[name] = _check_rows(hs, oracle_mod, w, k, p, name, opts=opts, want_best=True)
+    for a, b in [("one-block", "one-block-exhaustive"), ("split7", "split7-exhaustive")]:
+        np.testing.assert_array_equal(res[a][0], res[b][0])
+        np.testing.assert_array_equal(res[a][1], res[b][1])
+
+
+def test_special_rows_and_closed_cases(hs):
+    V = 500
+    rng = np.random.default_rng(41)
+    x = rng.normal(0, 1, size=(8, V)).astype(np.float32)
+    x[0, :] = -np.inf                                   # no finite logit: -1
+    x[1, [7, 9]] = 6.0                                  # tied maximum
+    T = np.array([1.0, 1.0, 0.7, 1.0, 1.0, -1.0, 0.0, 1.0], dtype=np.float32)
+    k = np.array([3, 1, 1, 0, 0, 5, 2, V], dtype=np.int32)
+    p = np.array([0.9, 1.0, 1.0, 0.0, np.nan, 0.5, 0.1, 1.0], dtype=np.float32)
+    t = torch.from_numpy(x).cuda()
+    Tt = torch.from_numpy(T).cuda()
+    seed = torch.arange(8, dtype=torch.int64, device="cuda") * 31 + 7
+    off = torch.zeros(8, dtype=torch.int64, device="cuda")
+    kt, pt = torch.from_numpy(k).cuda(), torch.from_numpy(p).cuda()
+    g = hs.sample_filtered(t, Tt, seed, off, top_k=kt, top_p=pt, k=6).cpu().numpy()
+    assert g[0].tolist() == [-1] * 6
+    assert set(g[1].tolist()) <= {7, 9}                 # top-1 with a tie keeps both
+    assert g[2].tolist() == [int(np.argmax(x[2]))] * 6  # k = 1
+    assert g[3].tolist() == [-2] * 6 and g[4].tolist() == [-2] * 6   # p <= 0, NaN
+    assert g[5].tolist() == [-2] * 6                    # bad T
+    assert g[6].tolist() == [int(np.argmax(x[6]))] * 6  # greedy ignores the filters
+    # nothing filtered (k >= V, p = 1): the unfiltered sampler
+    ref = hs.gumbel_argmax(t, Tt, seed, off, k=6).cpu().numpy()
+    np.testing.assert_array_equal(g[7], ref[7])
+    tau = hs.filter_threshold(t, Tt, top_k=kt, top_p=pt).cpu().numpy()
+    assert np.isneginf(tau[7]) and np.isneginf(tau[6]) and np.isnan(tau[3])
+
+
+def test_no_filter_arrays_is_unfiltered(hs):
+    w = W.generic(4, 20000, torch.bfloat16, seed=3, K=5)
+    d = on_device(w)
+    a = hs.sample_filtered(d["logits"], d["T"], d["seed"], d["offset"], k=5).cpu().numpy()
+    b = hs.gumbel_argmax(d["logits"], d["T"], d["seed"], d["offset"], k=5).cpu().numpy()
+    np.testing.assert_array_equal(a, b)
+
+
+def test_filters_headline_shape(hs, oracle_mod):
+    """256 x 151936 bf16 logits, curve off, top-k 50 and top-p 0.9 on every row."""
+    w = W.config4()
+    w.hlg = None
+    w.mu = None
+    B = w.B
+    k = np.full(B, 50, dtype=np.int32)
+    p = np.full(B, 0.9, dtype=np.float32)
+    print(_check_rows(hs, oracle_mod, w, k, p, "256x151936 top-k 50 top-p 0.9").shape)
