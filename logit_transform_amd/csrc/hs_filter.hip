@@ -137,6 +137,27 @@ __device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t *red) {
     return t;
 }
 
+// f(v) on every 16-byte vector of the row, four loads in flight per lane: whole vectors of
+// aligned rows are read directly, four per step; the rest (and misaligned rows) one at a time.
+template <int DT, typename F>
+__device__ __forceinline__ void for_each_vec(const char *rowp, int64_t nvec, int64_t V,
+                                             int32_t aligned, F f) {
+    const int BS = blockDim.x;
+    int64_t gv = threadIdx.x;
+    if (aligned) {
+        const int64_t nfull = V / dtype_traits<DT>::epv;
+        const uint4 *p = reinterpret_cast<const uint4 *>(rowp);
+        for (; gv + 3 * BS < nfull; gv += 4 * BS) {
+            const uint4 v0 = p[gv], v1 = p[gv + BS], v2 = p[gv + 2 * BS], v3 = p[gv + 3 * BS];
+            f(v0);
+            f(v1);
+            f(v2);
+            f(v3);
+        }
+    }
+    for (; gv < nvec; gv += BS) f(load_vec<DT>(rowp, gv, V, aligned));
+}
+
 // One level of the selection: the histogram (counts, or masses w(x)) of digit `lev` over the
 // finite keys >= kmin whose higher digits equal prefix, then the bin where the total from the
 // top reaches target (wave 0). Returns the new prefix; *tgt (wave 0) becomes what is left to
@@ -152,17 +173,31 @@ __device__ __forceinline__ uint32_t select_level(const char *rowp, int64_t nvec,
     constexpr int SH = D::shift[LEV];
     for (int j = threadIdx.x; j < NB; j += blockDim.x) hist[j] = (Cnt)0;
     __syncthreads();
-    for (int64_t gv = threadIdx.x; gv < nvec; gv += blockDim.x) {
-        const uint4 v = load_vec<DT>(rowp, gv, V, aligned);
+    // the keys of the selected bin (and >= kmin) span a range of values [lo, hi]: elements
+    // outside it are rejected with two compares before their key is formed
+    // (keys beyond those of -inf and +inf decode to NaN: such a bound is loosened to -inf or
+    // +inf; kmin, when set, is the key of a finite logit)
+    float lo = kmin > 0u ? key_value<DT>(kmin) : -__builtin_inff(), hi = __builtin_inff();
+    if constexpr (LEV > 0) {
+        constexpr int LOWB = SH + D::bits[LEV];   // bits below the selected prefix
+        const uint32_t k0 = prefix << LOWB;
+        const uint32_t k1 = k0 | ((1u << LOWB) - 1u);
+        const float v0 = key_value<DT>(k0), v1 = key_value<DT>(k1);
+        if (v0 == v0) lo = fmaxf(lo, v0);
+        if (v1 == v1) hi = v1;
+    }
+    for_each_vec<DT>(rowp, nvec, V, aligned, [&](const uint4 &v) {
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
             const float x = elem<DT>(v, e);
-            const uint32_t key = elem_key<DT>(v, e);
-            bool in = x > -__builtin_inff() && key >= kmin;
-            if constexpr (LEV > 0) in = in && (key >> (SH + D::bits[LEV])) == prefix;
-            if (in) atomicAdd(&hist[(key >> SH) & (uint32_t)(NB - 1)], weight(x));
+            if (x >= lo && x <= hi && x > -__builtin_inff()) {
+                const uint32_t key = elem_key<DT>(v, e);
+                bool in = key >= kmin;
+                if constexpr (LEV > 0) in = in && (key >> (SH + D::bits[LEV])) == prefix;
+                if (in) atomicAdd(&hist[(key >> SH) & (uint32_t)(NB - 1)], weight(x));
+            }
         }
-    }
+    });
     __syncthreads();
     __shared__ uint32_t s_new;
     if (wid == 0) {
@@ -236,15 +271,14 @@ __global__ __launch_bounds__(1024) void k_filter_tau(FilterArgs a) {
     } else {
         uint32_t nf = 0u;
         float mx = -__builtin_inff();
-        for (int64_t gv = tid; gv < nvec; gv += blockDim.x) {
-            const uint4 v = load_vec<DT>(rowp, gv, a.V, a.aligned);
+        for_each_vec<DT>(rowp, nvec, a.V, a.aligned, [&](const uint4 &v) {
 #pragma unroll
             for (int e = 0; e < EPV; ++e) {
                 const float x = elem<DT>(v, e);
                 nf += x > -__builtin_inff() ? 1u : 0u;
                 mx = fmaxf(mx, x);
             }
-        }
+        });
         M = block_max(mx, red_f);
         NF = block_sum_u32(nf, red_n);
     }
@@ -263,16 +297,15 @@ __global__ __launch_bounds__(1024) void k_filter_tau(FilterArgs a) {
         double tgt = 0.0;
         for (int j = tid; j < (1 << D::bits[0]); j += blockDim.x) hm[j] = 0.0;
         __syncthreads();
-        for (int64_t gv = tid; gv < nvec; gv += blockDim.x) {
-            const uint4 v = load_vec<DT>(rowp, gv, a.V, a.aligned);
+        const float lo = keyk > 0u ? tau : -__builtin_inff();   // tau = the value of keyk
+        for_each_vec<DT>(rowp, nvec, a.V, a.aligned, [&](const uint4 &v) {
 #pragma unroll
             for (int e = 0; e < EPV; ++e) {
                 const float x = elem<DT>(v, e);
-                const uint32_t key = elem_key<DT>(v, e);
-                if (x > -__builtin_inff() && key >= keyk)
-                    atomicAdd(&hm[key >> D::shift[0]], mass(x));
+                if (x >= lo && x > -__builtin_inff())
+                    atomicAdd(&hm[elem_key<DT>(v, e) >> D::shift[0]], mass(x));
             }
-        }
+        });
         __syncthreads();
         __shared__ uint32_t s_p0;
         if (wid == 0) {
