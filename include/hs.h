@@ -154,6 +154,13 @@ typedef struct {
     int32_t nchunk;      /* blocks per row when split (0 = automatic)                      */
     int32_t no_screen;   /* 1 = evaluate every element exactly (no candidate screening)    */
     int32_t draw_groups; /* blocks sharing one row's K draws (0 = automatic)               */
+    int32_t split_lse;   /* split rows with the curve on: 0 automatic, 1 log-sum-exp
+                            pre-pass, 2 exchange the chunks' partials inside the sampling
+                            kernel (one draw group per row; automatic picks it when every
+                            block of the grid is resident at once)                        */
+    int32_t exchange_wait; /* polls for the other chunks' partials before a block works
+                              them out itself: 0 default, -1 none (test control), > 0 that
+                              many                                                         */
 } hs_sample_opts;
 
 /* hs_sample with explicit kernel choices. best (device float[B*K] or NULL) receives the

@@ -82,9 +82,12 @@ def _pivot_mode(p) -> int:
 class SampleOpts(C.Structure):
     """Kernel choices for sample_ex: variant 0 auto / 1 one block per row / 2 split rows;
     nchunk blocks per split row (0 auto); no_screen 1 = score every element exactly;
-    draw_groups blocks sharing one row's draws (0 auto)."""
+    draw_groups blocks sharing one row's draws (0 auto); split_lse for split rows with the
+    curve on: 0 auto / 1 log-sum-exp pre-pass / 2 partials exchanged inside the kernel;
+    exchange_wait polls for the other chunks' partials (0 default, -1 none)."""
     _fields_ = [("variant", C.c_int32), ("nchunk", C.c_int32), ("no_screen", C.c_int32),
-                ("draw_groups", C.c_int32)]
+                ("draw_groups", C.c_int32), ("split_lse", C.c_int32),
+                ("exchange_wait", C.c_int32)]
 
 
 _lib = None

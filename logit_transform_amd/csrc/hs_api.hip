@@ -73,7 +73,7 @@ int num_cus() {
 }
 
 struct WsLayout {
-    size_t counters, keys, partials, tau, total;
+    size_t counters, keys, partials, flags, tau, total;
 };
 
 WsLayout ws_layout(int64_t B, int32_t K) {
@@ -81,7 +81,8 @@ WsLayout ws_layout(int64_t B, int32_t K) {
     L.counters = 0;
     L.keys = align256((size_t)B * (size_t)K * 4);   // counters: one per (row, draw group)
     L.partials = L.keys + align256((size_t)B * (size_t)K * 8);
-    L.tau = L.partials + align256((size_t)B * hs::kMaxChunks * sizeof(float4));
+    L.flags = L.partials + align256((size_t)B * hs::kMaxChunks * sizeof(float4));
+    L.tau = L.flags + align256((size_t)B * hs::kMaxChunks * 4);   // exchange flags
     L.total = L.tau + align256((size_t)B * 4);   // top-k / top-p thresholds
     return L;
 }
@@ -172,7 +173,8 @@ int make_plan(const hs_logits *x, int32_t K, bool hlg, bool ws_ok, const hs_samp
 
 bool opts_valid(const hs_sample_opts *o) {
     return !o || !(o->variant < 0 || o->variant > 2 || o->nchunk < 0 ||
-                   o->nchunk > hs::kMaxChunks || o->draw_groups < 0);
+                   o->nchunk > hs::kMaxChunks || o->draw_groups < 0 || o->split_lse < 0 ||
+                   o->split_lse > 2 || o->exchange_wait < -1);
 }
 
 // Top-k / top-p parameters of a filtered call (device arrays, either may be null).
@@ -242,6 +244,7 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
         a.keys = reinterpret_cast<uint64_t *>(w + L.keys);
         a.partials = reinterpret_cast<float4 *>(w + L.partials);
         a.part_stride = hs::kMaxChunks;
+        a.flags = reinterpret_cast<uint32_t *>(w + L.flags);
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (filtering) {
@@ -257,7 +260,23 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
         if (hs::launch_filter_tau(x->dtype, f, (int)x->B, s) != hipSuccess) return HS_ERR_HIP;
         a.tau = f.tau;
     }
-    if (curve_on && P.nchunk > 1) {
+    // Split rows with the curve on: the chunks' log-sum-exp partials are exchanged inside the
+    // sampling kernel when every block of the grid is resident at once (and one draw group per
+    // row); otherwise a pre-pass computes them.
+    if (curve_on && P.nchunk > 1 && P.nkg == 1) {
+        const int mode = opts ? opts->split_lse : 0;
+        if (mode == 2) {
+            a.exchange = 1;
+        } else if (mode == 0) {
+            int per_cu = 0;
+            if (hs::launch_sample(x->dtype, true, piv, a, P.nv, P.bs, 0, s, &per_cu) ==
+                    hipSuccess && per_cu > 0 && P.grid <= (int64_t)per_cu * num_cus())
+                a.exchange = 1;
+        }
+        const int wait = opts ? opts->exchange_wait : 0;
+        a.spins = wait < 0 ? 0 : wait > 0 ? wait : hs::kExchangeSpins;
+    }
+    if (curve_on && P.nchunk > 1 && !a.exchange) {
         const int bs = P.cv >= 4096 ? 1024 : 256;
         if (hs::launch_lse_partial(x->dtype, piv, a, bs, (int)(x->B * P.nchunk), s) != hipSuccess)
             return HS_ERR_HIP;

@@ -12,6 +12,9 @@ namespace hs {
 // Rows split over more than this many blocks are not generated; the workspace reserves this
 // many (max, sum) pairs per row.
 constexpr int kMaxChunks = 64;
+// Polls (with a short sleep between them) a block makes, by default, for the other chunks'
+// partials before it works them out itself.
+constexpr int kExchangeSpins = 1 << 14;
 
 // Per-row curve settings, laid out as hs_hlg_row of the public header (32 bytes).
 struct RowCurve {
@@ -50,6 +53,11 @@ struct SampleArgs {
     float pivot_offset;        // c of the top anchor
     const RowCurve *row_curves;   // [B] per-row curve settings (pivot mode 3), else null
     const float *tau;             // [B] top-k / top-p thresholds (curve off), else null
+    // split rows with the curve on: exchange the chunks' partials inside the sampling kernel
+    // instead of a pre-pass (one draw group per row, every block resident at once)
+    int32_t exchange;
+    int32_t spins;                // polls before a block works a missing partial out itself
+    uint32_t *flags;              // [B * part_stride]: chunk partial published
 };
 
 struct RowOpArgs {
@@ -80,16 +88,17 @@ hipError_t launch_filter_tau(int dt, const FilterArgs &a, int grid, hipStream_t 
 
 // piv: the curve's pivot, 0 given per row, 1 top-anchored, 2 entropy-anchored, 3 set per row
 // (a.row_curves)
+// occ: when not null, the kernel's resident blocks per CU are written there instead of a launch
 hipError_t launch_sample(int dt, bool hlg, int piv, const SampleArgs &a, int nv, int bs,
-                         int grid, hipStream_t s);
+                         int grid, hipStream_t s, int *occ = nullptr);
 hipError_t launch_sample_pivot(int dt, int piv, const SampleArgs &a, int nv, int bs, int grid,
-                               hipStream_t s);
+                               hipStream_t s, int *occ);
 hipError_t launch_lse_partial(int dt, int piv, const SampleArgs &a, int bs, int grid,
                               hipStream_t s);
 hipError_t launch_lse_partial_pivot(int dt, int piv, const SampleArgs &a, int bs, int grid,
                                     hipStream_t s);
 hipError_t launch_sample_rows(int dt, const SampleArgs &a, int nv, int bs, int grid,
-                              hipStream_t s);
+                              hipStream_t s, int *occ);
 hipError_t launch_lse_partial_rows(int dt, const SampleArgs &a, int bs, int grid,
                                    hipStream_t s);
 // op: 0 log-sum-exp, 1 transform, 2 pivot

@@ -133,16 +133,16 @@ __global__ void k_fill_zero(uint32_t *__restrict__ p, int64_t n) {
 // Host-side launchers (called from hs_api.hip).
 // ------------------------------------------------------------------------------------------
 hipError_t launch_sample(int dt, bool hlg, int piv, const SampleArgs &a, int nv, int bs,
-                         int grid, hipStream_t s) {
-    if (hlg && piv == 3) return launch_sample_rows(dt, a, nv, bs, grid, s);
-    if (hlg && piv != 0) return launch_sample_pivot(dt, piv, a, nv, bs, grid, s);
+                         int grid, hipStream_t s, int *occ) {
+    if (hlg && piv == 3) return launch_sample_rows(dt, a, nv, bs, grid, s, occ);
+    if (hlg && piv != 0) return launch_sample_pivot(dt, piv, a, nv, bs, grid, s, occ);
     switch (dt) {
-        case DT_F32: return hlg ? launch_sample_al<DT_F32, true, 0>(a, nv, bs, grid, s)
-                                : launch_sample_al<DT_F32, false, 0>(a, nv, bs, grid, s);
-        case DT_BF16: return hlg ? launch_sample_al<DT_BF16, true, 0>(a, nv, bs, grid, s)
-                                 : launch_sample_al<DT_BF16, false, 0>(a, nv, bs, grid, s);
-        case DT_F16: return hlg ? launch_sample_al<DT_F16, true, 0>(a, nv, bs, grid, s)
-                                : launch_sample_al<DT_F16, false, 0>(a, nv, bs, grid, s);
+        case DT_F32: return hlg ? launch_sample_al<DT_F32, true, 0>(a, nv, bs, grid, s, occ)
+                                : launch_sample_al<DT_F32, false, 0>(a, nv, bs, grid, s, occ);
+        case DT_BF16: return hlg ? launch_sample_al<DT_BF16, true, 0>(a, nv, bs, grid, s, occ)
+                                 : launch_sample_al<DT_BF16, false, 0>(a, nv, bs, grid, s, occ);
+        case DT_F16: return hlg ? launch_sample_al<DT_F16, true, 0>(a, nv, bs, grid, s, occ)
+                                : launch_sample_al<DT_F16, false, 0>(a, nv, bs, grid, s, occ);
     }
     return hipErrorInvalidValue;
 }

@@ -13,11 +13,11 @@
 namespace hs {
 
 hipError_t launch_sample_rows(int dt, const SampleArgs &a, int nv, int bs, int grid,
-                              hipStream_t s) {
+                              hipStream_t s, int *occ) {
     switch (dt) {
-        case DT_F32: return launch_sample_al<DT_F32, true, 3>(a, nv, bs, grid, s);
-        case DT_BF16: return launch_sample_al<DT_BF16, true, 3>(a, nv, bs, grid, s);
-        case DT_F16: return launch_sample_al<DT_F16, true, 3>(a, nv, bs, grid, s);
+        case DT_F32: return launch_sample_al<DT_F32, true, 3>(a, nv, bs, grid, s, occ);
+        case DT_BF16: return launch_sample_al<DT_BF16, true, 3>(a, nv, bs, grid, s, occ);
+        case DT_F16: return launch_sample_al<DT_F16, true, 3>(a, nv, bs, grid, s, occ);
     }
     return hipErrorInvalidValue;
 }

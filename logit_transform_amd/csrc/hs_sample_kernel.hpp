@@ -102,6 +102,76 @@ __device__ __forceinline__ float vec_max(const float (&x)[EPV]) {
     }
 }
 
+// (all threads of a block) One chunk's (max, sum exp(x - max), sum exp(x - max) (x - max)),
+// for rows split over several blocks, in natural units, written by thread 0 to *dst: each
+// thread keeps a running maximum in base 2 and rescales its sums when it moves; the block
+// combines them. The top anchor needs only the maximum, only the entropy anchor the third sum.
+// The same code gives the split pre-pass and the in-kernel exchange, so a chunk's partial does
+// not depend on which block computes it.
+template <int DT, int PIV>
+__device__ __forceinline__ void chunk_partial(const SampleArgs &a, int64_t b, int chunk,
+                                              float *red_m, float *red_s, float *red_u,
+                                              float4 *dst) {
+    using tr = dtype_traits<DT>;
+    constexpr int EPV = tr::epv;
+    constexpr bool ENT = PIV == 2 || PIV == 3;   // the entropy anchor's sum is needed
+    const int64_t v0 = (int64_t)chunk * a.cv;
+    const int64_t vend = min(a.nvec, v0 + a.cv);
+    const char *rowp = reinterpret_cast<const char *>(a.data) + b * a.ld * tr::esize;
+    float m = -3.402823466e38f, s = 0.0f, u = 0.0f;   // base 2: m a maximum of x log2(e)
+    for (int64_t gv = v0 + threadIdx.x; gv < vend; gv += blockDim.x) {
+        const uint4 v = load_vec<DT>(rowp, gv, a.V, a.aligned);
+        float xv[EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) xv[e] = elem<DT>(v, e);
+        const float mv = vec_max<EPV>(xv) * kLog2e;
+        if constexpr (PIV == 1) {
+            m = fmaxf(m, mv);
+        } else {
+            if (mv > m) {
+                const float sc = __builtin_amdgcn_exp2f(m - mv);
+                if constexpr (ENT) u = __builtin_fmaf(s, m - mv, u) * sc;
+                s *= sc;
+                m = mv;
+            }
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                const float t = __builtin_fmaf(xv[e], kLog2e, -m);
+                const float p = __builtin_amdgcn_exp2f(t);
+                s += p;
+                if constexpr (ENT) u = (p > 0.0f) ? __builtin_fmaf(p, t, u) : u;
+            }
+        }
+    }
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int nw = (blockDim.x + 63) >> 6;
+    const float mw = wave_max(m);
+    const float sc = __builtin_amdgcn_exp2f(m - mw);
+    const float sw = wave_sum(s * sc);
+    const float uw = ENT ? wave_sum(s > 0.0f ? __builtin_fmaf(s, m - mw, u) * sc : 0.0f) : 0.0f;
+    if (lane == 0) {
+        red_m[wid] = mw;
+        red_s[wid] = sw;
+        red_u[wid] = uw;
+    }
+    __syncthreads();
+    if (wid == 0) {
+        const float pm = lane < nw ? red_m[lane] : -3.402823466e38f;
+        const float mb = wave_max(pm);
+        const float sb_ = lane < nw ? __builtin_amdgcn_exp2f(pm - mb) : 0.0f;
+        const float S = wave_sum(lane < nw ? red_s[lane] * sb_ : 0.0f);
+        const float U = ENT ? wave_sum(lane < nw && red_s[lane] > 0.0f
+                                           ? __builtin_fmaf(red_s[lane], pm - mb, red_u[lane]) * sb_
+                                           : 0.0f)
+                            : 0.0f;
+        if (lane == 0) {
+            const bool fin = (PIV == 1) ? (mb > -1.0e38f) : (S > 0.0f);
+            *dst = make_float4(fin ? mb * kLn2 : -__builtin_inff(), fin ? S : 0.0f,
+                               fin ? U * kLn2 : 0.0f, 0.0f);
+        }
+    }
+}
+
 // PIV selects the curve's pivot [HLG, The pivot] (curve on only): 0 given per row,
 // 1 top-anchored (mu = l_max - c: z = x - (x_max - c), no log-sum-exp needed),
 // 2 entropy-anchored (mu = sum p l: z = x - E_p[x], one more accumulator),
@@ -134,6 +204,10 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     // the block's best key of each draw of a batch of up to 64, by LDS atomic maxima; wave 0
     // writes a batch out after one barrier
     __shared__ uint64_t s_best[64];
+    // split rows with the partials exchanged in the kernel: every chunk's partial, and the
+    // chunks whose partial did not arrive in time
+    __shared__ float4 s_part[kMaxChunks];
+    __shared__ uint64_t s_miss;
     __shared__ int s_last;
 
     const int tid = threadIdx.x;
@@ -571,6 +645,63 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
         }
     }
     __syncthreads();
+    // Split rows without the pre-pass (the host chooses this only when every block of the grid
+    // is resident at once): each block works out its own chunk's partial with the pre-pass's
+    // code (the chunk was just read and is in the caches) and publishes it; wave 0 collects the
+    // row's other partials, waiting a bounded time for each; any still missing then is worked
+    // out here with the same code, so the combined shift is the same whoever computes a
+    // partial. Partials and flags are only touched by agent-scope atomics: each block waits
+    // for its partial's stores to complete before it raises its flag.
+    const float4 *parts = a.partials + b * a.part_stride;
+    if constexpr (HLG) {
+        if (a.nchunk > 1 && a.exchange) {
+            chunk_partial<DT, PIV>(a, b, chunk, red_m, red_s, red_u, &s_part[chunk]);
+            __syncthreads();
+            uint32_t *flags = a.flags + b * a.part_stride;
+            if (tid == 0) {
+                const float4 mine = s_part[chunk];
+                uint32_t *dst = reinterpret_cast<uint32_t *>(a.partials + b * a.part_stride + chunk);
+                __hip_atomic_store(dst + 0, __float_as_uint(mine.x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(dst + 1, __float_as_uint(mine.y), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(dst + 2, __float_as_uint(mine.z), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                __builtin_amdgcn_s_waitcnt(0);
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                __hip_atomic_store(flags + chunk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if (wid == 0) {
+                bool have = lane >= a.nchunk || lane == chunk;
+                for (int it = 0; it < a.spins; ++it) {
+                    if (!have)
+                        have = __hip_atomic_load(flags + lane, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT) != 0u;
+                    if (__ballot(!have) == 0ull) break;
+                    __builtin_amdgcn_s_sleep(8);
+                }
+                if (have && lane < a.nchunk && lane != chunk) {
+                    const uint32_t *src =
+                        reinterpret_cast<const uint32_t *>(a.partials + b * a.part_stride + lane);
+                    float4 v;
+                    v.x = __uint_as_float(__hip_atomic_load(src + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                    v.y = __uint_as_float(__hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                    v.z = __uint_as_float(__hip_atomic_load(src + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                    v.w = 0.0f;
+                    s_part[lane] = v;
+                }
+                const uint64_t miss = __ballot(!have);
+                if (lane == 0) s_miss = miss;
+            }
+            __syncthreads();
+            uint64_t miss = s_miss;
+            while (miss) {
+                const int j = __builtin_ctzll(miss);
+                miss &= miss - 1ull;
+                chunk_partial<DT, PIV>(a, b, j, red_m, red_s, red_u, &s_part[j]);
+                __syncthreads();
+            }
+            parts = s_part;
+        }
+    }
     if (wid == 0) {
         const float xmb = wave_max(lane < nw ? red_x[lane] : -__builtin_inff());
         float c = 0.0f;
@@ -582,7 +713,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             const int mode = PIV == 3 ? rpiv : PIV;
             if (mode == 1) {
                 c = (a.nchunk == 1 ? xmb
-                                   : wave_max(lane < a.nchunk ? a.partials[b * a.part_stride + lane].x
+                                   : wave_max(lane < a.nchunk ? parts[lane].x
                                                               : -__builtin_inff())) - poff;
                 ok = c > -__builtin_inff();
             } else if (mode < 0) {
@@ -606,7 +737,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                     // the chunks' (max, sum, u) of the pre-pass, one per lane (nchunk <= 64),
                     // all read at once; natural units
                     const float4 pj = lane < a.nchunk
-                                          ? a.partials[b * a.part_stride + lane]
+                                          ? parts[lane]
                                           : make_float4(-__builtin_inff(), 0.0f, 0.0f, 0.0f);
                     const float Mb = wave_max(pj.x);
                     ok = Mb > -__builtin_inff();
@@ -866,91 +997,41 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             if (tid == 0)
                 __hip_atomic_store(a.counters + b * a.nkg + kg, 0u, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
+            // the exchange's flags (one draw group per row: every block of the row is past
+            // its wait once it has counted in)
+            if (a.exchange && tid < a.nchunk)
+                __hip_atomic_store(a.flags + b * a.part_stride + tid, 0u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
 
-// Per-chunk (max, sum exp(x - max), sum exp(x - max) (x - max)) for rows split over several
-// blocks, in one read: each thread keeps a running maximum in base 2 and rescales its sums
-// when it moves; the block combines them. The top anchor needs only the maximum; only the
-// entropy anchor needs the third sum.
+// The split pre-pass: one block per (row, chunk).
 template <int DT, int PIV>
 __global__ __launch_bounds__(1024) void k_lse_partial(SampleArgs a) {
-    using tr = dtype_traits<DT>;
-    constexpr int EPV = tr::epv;
-    constexpr bool ENT = PIV == 2 || PIV == 3;   // the entropy anchor's sum is needed
     __shared__ float red_m[16], red_s[16], red_u[16];
     const int chunk = blockIdx.x % a.nchunk;
     const int64_t b = blockIdx.x / a.nchunk;
-    const int64_t v0 = (int64_t)chunk * a.cv;
-    const int64_t vend = min(a.nvec, v0 + a.cv);
-    const char *rowp = reinterpret_cast<const char *>(a.data) + b * a.ld * tr::esize;
-    float m = -3.402823466e38f, s = 0.0f, u = 0.0f;   // base 2: m a maximum of x log2(e)
-    for (int64_t gv = v0 + threadIdx.x; gv < vend; gv += blockDim.x) {
-        const uint4 v = load_vec<DT>(rowp, gv, a.V, a.aligned);
-        float xv[EPV];
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) xv[e] = elem<DT>(v, e);
-        const float mv = vec_max<EPV>(xv) * kLog2e;
-        if constexpr (PIV == 1) {
-            m = fmaxf(m, mv);
-        } else {
-            if (mv > m) {
-                const float sc = __builtin_amdgcn_exp2f(m - mv);
-                if constexpr (ENT) u = __builtin_fmaf(s, m - mv, u) * sc;
-                s *= sc;
-                m = mv;
-            }
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) {
-                const float t = __builtin_fmaf(xv[e], kLog2e, -m);
-                const float p = __builtin_amdgcn_exp2f(t);
-                s += p;
-                if constexpr (ENT) u = (p > 0.0f) ? __builtin_fmaf(p, t, u) : u;
-            }
-        }
-    }
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const int nw = (blockDim.x + 63) >> 6;
-    const float mw = wave_max(m);
-    const float sc = __builtin_amdgcn_exp2f(m - mw);
-    const float sw = wave_sum(s * sc);
-    const float uw = ENT ? wave_sum(s > 0.0f ? __builtin_fmaf(s, m - mw, u) * sc : 0.0f) : 0.0f;
-    if (lane == 0) {
-        red_m[wid] = mw;
-        red_s[wid] = sw;
-        red_u[wid] = uw;
-    }
-    __syncthreads();
-    if (wid == 0) {
-        const float pm = lane < nw ? red_m[lane] : -3.402823466e38f;
-        const float mb = wave_max(pm);
-        const float sb_ = lane < nw ? __builtin_amdgcn_exp2f(pm - mb) : 0.0f;
-        const float S = wave_sum(lane < nw ? red_s[lane] * sb_ : 0.0f);
-        const float U = ENT ? wave_sum(lane < nw && red_s[lane] > 0.0f
-                                                  ? __builtin_fmaf(red_s[lane], pm - mb, red_u[lane]) * sb_
-                                                  : 0.0f)
-                                   : 0.0f;
-        if (lane == 0) {
-            const bool fin = (PIV == 1) ? (mb > -1.0e38f) : (S > 0.0f);
-            // natural units: max, sum exp(x - max), sum exp(x - max) (x - max)
-            a.partials[b * a.part_stride + chunk] =
-                make_float4(fin ? mb * kLn2 : -__builtin_inff(), fin ? S : 0.0f,
-                            fin ? U * kLn2 : 0.0f, 0.0f);
-        }
-    }
+    chunk_partial<DT, PIV>(a, b, chunk, red_m, red_s, red_u, &a.partials[b * a.part_stride + chunk]);
 }
 
 // ------------------------------------------------------------------------------------------
 // Launchers, instantiated by the translation units that include this header.
 // ------------------------------------------------------------------------------------------
+// occ: when not null, the resident blocks per CU of the kernel this call would launch are
+// written there instead of launching it.
 template <int DT, bool HLG, int PIV, bool AL>
-hipError_t launch_sample_nv(const SampleArgs &a, int nv, int bs, int grid, hipStream_t s) {
+hipError_t launch_sample_nv(const SampleArgs &a, int nv, int bs, int grid, hipStream_t s,
+                            int *occ) {
     // blocks of up to 1024 threads, nv slots of 16-byte vectors per thread; the dynamic LDS
     // holds one dword per lane and slot
 #define HS_CASE(N, MB)                                                                     \
     case N:                                                                                \
         if (bs > MB) return hipErrorInvalidValue;                                          \
+        if (occ)                                                                           \
+            return hipOccupancyMaxActiveBlocksPerMultiprocessor(                           \
+                occ, reinterpret_cast<const void *>(&k_sample<DT, N, HLG, PIV, MB, AL>),  \
+                bs, (size_t)(N | 1) * bs * 4);                                            \
         hipLaunchKernelGGL((k_sample<DT, N, HLG, PIV, MB, AL>), dim3(grid), dim3(bs),     \
                            (size_t)(N | 1) * bs * 4, s, a);                               \
         break;
@@ -964,11 +1045,12 @@ hipError_t launch_sample_nv(const SampleArgs &a, int nv, int bs, int grid, hipSt
 }
 
 template <int DT, bool HLG, int PIV>
-hipError_t launch_sample_al(const SampleArgs &a, int nv, int bs, int grid, hipStream_t s) {
+hipError_t launch_sample_al(const SampleArgs &a, int nv, int bs, int grid, hipStream_t s,
+                            int *occ) {
     // the branch-free load path needs 16-byte aligned rows holding at least one full vector
     if (a.aligned && a.V >= dtype_traits<DT>::epv)
-        return launch_sample_nv<DT, HLG, PIV, true>(a, nv, bs, grid, s);
-    return launch_sample_nv<DT, HLG, PIV, false>(a, nv, bs, grid, s);
+        return launch_sample_nv<DT, HLG, PIV, true>(a, nv, bs, grid, s, occ);
+    return launch_sample_nv<DT, HLG, PIV, false>(a, nv, bs, grid, s, occ);
 }
 
 template <int PIV>

@@ -170,7 +170,9 @@ def test_workspace_sizes(lib):
 def test_sample_ex_opts(lib):
     x = L()
     for o in (hs.SampleOpts(variant=3), hs.SampleOpts(variant=-1), hs.SampleOpts(nchunk=-1),
-              hs.SampleOpts(nchunk=65), hs.SampleOpts(draw_groups=-2)):
+              hs.SampleOpts(nchunk=65), hs.SampleOpts(draw_groups=-2),
+              hs.SampleOpts(split_lse=3), hs.SampleOpts(split_lse=-1),
+              hs.SampleOpts(exchange_wait=-2)):
         assert lib.hs_sample_ex(C.byref(x), FAKE, None, None, FAKE, FAKE, 1, FAKE, None, None, 0,
                                 C.byref(o), None) == HS_ERR_INVALID_ARG
 

@@ -117,14 +117,25 @@ def test_variant_invariance(hs, oracle_mod, hlg):
                        ("one-block-exhaustive", hs.SampleOpts(variant=1, no_screen=1)),
                        ("split7-exhaustive", hs.SampleOpts(variant=2, nchunk=7, no_screen=1)),
                        ("draw-groups", hs.SampleOpts(variant=1, draw_groups=3)),
-                       ("split5-draw-groups", hs.SampleOpts(variant=2, nchunk=5, draw_groups=2))]:
+                       ("split5-draw-groups", hs.SampleOpts(variant=2, nchunk=5, draw_groups=2)),
+                       ("split7-prepass", hs.SampleOpts(variant=2, nchunk=7, draw_groups=1,
+                                                        split_lse=1)),
+                       ("split7-exchange", hs.SampleOpts(variant=2, nchunk=7, draw_groups=1,
+                                                         split_lse=2)),
+                       ("split7-exchange-nowait", hs.SampleOpts(variant=2, nchunk=7,
+                                                                draw_groups=1, split_lse=2,
+                                                                exchange_wait=-1)),
+                       ("split64-exchange", hs.SampleOpts(variant=2, nchunk=64, draw_groups=1,
+                                                          split_lse=2))]:
         idx, best = hs.sample_ex(d["logits"], d["T"], d["seed"], d["offset"], mu=d.get("mu"),
                                  hlg=hlg, k=3, opts=opts, want_best=True)
         idx = idx.cpu().numpy()
         results[name] = (idx, best.cpu().numpy())
         assert_parity(idx, o, s1, s2, x64, name)
-    # screening never changes a result: same variant, screened vs exhaustive, bit-identical
-    for a, b in [("one-block", "one-block-exhaustive"), ("split7", "split7-exhaustive")]:
+    # screening never changes a result: same variant, screened vs exhaustive, bit-identical;
+    # nor does which block works out a chunk's log-sum-exp partial in the exchange
+    for a, b in [("one-block", "one-block-exhaustive"), ("split7", "split7-exhaustive"),
+                 ("split7-exchange", "split7-exchange-nowait")]:
         np.testing.assert_array_equal(results[a][0], results[b][0])
         np.testing.assert_array_equal(results[a][1], results[b][1])
     # without the curve nothing depends on the decomposition at all
@@ -151,18 +162,23 @@ def test_k_draws_equal_single_draws(hs):
 
 
 def test_workspace_left_clean(hs):
-    """A split call leaves its workspace zero-filled, so calls can reuse it."""
+    """A split call leaves its workspace's counters, keys and exchange flags zero-filled, so
+    calls can reuse it (with draw groups and the pre-pass, and with the in-kernel exchange)."""
     w = W.generic(2, 100000, torch.float32, seed=81, hlg=HLG_A, K=4)
     d = on_device(w)
     ws = hs.workspace(2, 100000, 4, torch.float32, True)
-    outs = [hs.sample_ex(d["logits"], d["T"], d["seed"], d["offset"], mu=d["mu"], hlg=HLG_A, k=4,
-                         ws=ws, opts=hs.SampleOpts(variant=2, nchunk=9)).cpu().numpy()
-            for _ in range(3)]
-    torch.cuda.synchronize()
-    n_keys = 256 + 2 * 4 * 8
-    assert int(ws[:n_keys].to(torch.int32).abs().sum()) == 0
-    for o in outs[1:]:
-        np.testing.assert_array_equal(o, outs[0])
+    # layout for B = 2, K = 4: counters [0, 256), keys [256, 512), partials [512, 2560),
+    # exchange flags [2560, 3072)
+    for opts in (hs.SampleOpts(variant=2, nchunk=9),
+                 hs.SampleOpts(variant=2, nchunk=9, draw_groups=1, split_lse=2)):
+        outs = [hs.sample_ex(d["logits"], d["T"], d["seed"], d["offset"], mu=d["mu"], hlg=HLG_A,
+                             k=4, ws=ws, opts=opts).cpu().numpy()
+                for _ in range(3)]
+        torch.cuda.synchronize()
+        assert int(ws[:512].to(torch.int32).abs().sum()) == 0
+        assert int(ws[2560:3072].to(torch.int32).abs().sum()) == 0
+        for o in outs[1:]:
+            np.testing.assert_array_equal(o, outs[0])
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])

@@ -101,13 +101,19 @@ def test_pivot_sampling_variants(hs, oracle_mod, mode, off, dtype, V):
                        ("one-block-exhaustive", hs.SampleOpts(variant=1, no_screen=1)),
                        ("split7-exhaustive", hs.SampleOpts(variant=2, nchunk=7, no_screen=1)),
                        ("draw-groups", hs.SampleOpts(variant=1, draw_groups=3)),
-                       ("split5-draw-groups", hs.SampleOpts(variant=2, nchunk=5, draw_groups=2))]:
+                       ("split5-draw-groups", hs.SampleOpts(variant=2, nchunk=5, draw_groups=2)),
+                       ("split7-exchange", hs.SampleOpts(variant=2, nchunk=7, draw_groups=1,
+                                                         split_lse=2)),
+                       ("split7-exchange-nowait", hs.SampleOpts(variant=2, nchunk=7,
+                                                                draw_groups=1, split_lse=2,
+                                                                exchange_wait=-1))]:
         idx, best = hs.sample_ex(d["logits"], d["T"], d["seed"], d["offset"], hlg=w.hlg, k=3,
                                  opts=opts, want_best=True)
         idx = idx.cpu().numpy()
         res[name] = (idx, best.cpu().numpy())
         assert_parity(idx, o, s1, s2, x64, "%s %s %s" % (mode, dtype, name))
-    for a, b in [("one-block", "one-block-exhaustive"), ("split7", "split7-exhaustive")]:
+    for a, b in [("one-block", "one-block-exhaustive"), ("split7", "split7-exhaustive"),
+                 ("split7-exchange", "split7-exchange-nowait")]:
         np.testing.assert_array_equal(res[a][0], res[b][0])
         np.testing.assert_array_equal(res[a][1], res[b][1])
 

@@ -77,7 +77,12 @@ def test_mixed_rows_match_oracle(hs, oracle_mod, dtype, V):
     rows = hs.hlg_rows(settings)
     for name, opts in [("auto", None), ("one-block", hs.SampleOpts(variant=1)),
                        ("split7", hs.SampleOpts(variant=2, nchunk=7)),
-                       ("split5-groups2", hs.SampleOpts(variant=2, nchunk=5, draw_groups=2))]:
+                       ("split5-groups2", hs.SampleOpts(variant=2, nchunk=5, draw_groups=2)),
+                       ("split7-exchange", hs.SampleOpts(variant=2, nchunk=7, draw_groups=1,
+                                                         split_lse=2)),
+                       ("split7-exchange-nowait", hs.SampleOpts(variant=2, nchunk=7,
+                                                                draw_groups=1, split_lse=2,
+                                                                exchange_wait=-1))]:
         g = hs.sample_rows(d["logits"], d["T"], d["seed"], d["offset"], rows, mu=d["mu"], k=K,
                            opts=opts).cpu().numpy()
         assert_parity(g, o, s1, s2, x64, "mixed rows %s %s" % (dtype, name))
