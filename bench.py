@@ -301,8 +301,15 @@ def main():
                     for i in range(args.steps):
                         launch(i, cap_stream)
             torch.cuda.current_stream(dev).wait_stream(side)
-            graph.replay()   # one untimed replay
-            torch.cuda.synchronize()
+            # untimed replays until about 0.2 s of work has run: the GPU's clock ramps up
+            # over the first milliseconds of sustained load, and the timed region measures
+            # the steady state
+            t_w = time.perf_counter()
+            for _ in range(50):
+                graph.replay()
+                torch.cuda.synchronize()
+                if time.perf_counter() - t_w > 0.2:
+                    break
         except Exception as e:   # noqa: BLE001 -- report and time eagerly instead
             log("graph capture failed (%s); timing eager launches" % e)
             graph = None

@@ -558,13 +558,12 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             red_cw[wid] = c.w;
         }
     };
-    // (wave 0) Exact score of the block's best candidate.
+    // (wave 0) The best exact score among the waves' bootstrap candidates: lane w scores wave
+    // w's (all at once, at the latency of one).
     auto candidate_score = [&]() -> float {
-        const uint64_t bk = wave_max_u64(lane < nw ? red_ck[lane] : 0ull);
-        if (bk == 0) return -__builtin_inff();
-        const int bw = (int)((0xFFFFFFFFu - (uint32_t)bk) >> 6);
-        return exact_score<HLG>(uniform(red_cx[bw]),
-                                (uint32_t)__builtin_amdgcn_readfirstlane(red_cw[bw]), rc);
+        const bool has = lane < nw && red_ck[lane] != 0ull;
+        const float cs = has ? exact_score<HLG>(red_cx[lane], red_cw[lane], rc) : -__builtin_inff();
+        return uniform(wave_max(cs));
     };
     // (wave 0) The screen's constants from a lower bound bs on the draw's winning score:
     // threshold thr = (bs - slack) / ln 2 - 1 in units of ln 2, and the coefficients with which
