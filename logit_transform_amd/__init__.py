@@ -191,9 +191,12 @@ def _row_vec(v, B: int, dtype: torch.dtype, device, name: str) -> torch.Tensor:
         t = t.view(torch.int64)
     if t.dtype != dtype:
         t = t.to(dtype)
-    t = t.reshape(-1).contiguous()
+    t = t.reshape(-1)
+    if t.numel() == 1 and B > 1:   # one value for every row
+        t = t.expand(B)
+    t = t.contiguous()
     if t.numel() != B:
-        raise ValueError("%s must have B=%d entries" % (name, B))
+        raise ValueError("%s must have B=%d entries (or one for every row)" % (name, B))
     return t
 
 

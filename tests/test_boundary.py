@@ -263,3 +263,15 @@ def test_micro_library_exports():
     assert M.hs_micro_philox_max(FAKE, 4, 10, 1, 1, FAKE, None) == -1      # V % 4 != 0
     assert M.hs_micro_philox_max(None, 4, 64, 1, 1, FAKE, None) == -1
     assert M.hs_micro_philox_max(FAKE, 4, 64, 2, 3, FAKE, None) == -1      # groups > K
+
+
+def test_per_row_arguments_broadcast():
+    """A per-row argument given as one value applies to every row; other lengths are refused."""
+    import torch
+    t = hs._row_vec(0.7, 4, torch.float32, "cpu", "T")
+    assert t.tolist() == pytest.approx([0.7] * 4)
+    s = hs._row_vec(2**64 - 1, 3, torch.int64, "cpu", "seed")
+    assert s.tolist() == [-1, -1, -1]                       # the uint64 bit pattern
+    assert hs._row_vec([1, 2, 3], 3, torch.int32, "cpu", "top_k").tolist() == [1, 2, 3]
+    with pytest.raises(ValueError):
+        hs._row_vec([1, 2], 3, torch.int32, "cpu", "top_k")
