@@ -42,11 +42,18 @@ def log(*a):
 
 
 def kernel_source_digest() -> str:
+    """A digest of the sampling kernels' code (comments and blank lines left out, so that a
+    profile stays valid across edits of the comments only)."""
+    import re
     h = hashlib.sha256()
     for f in ("hs_kernels.hip", "hs_kernels_pivot.hip", "hs_kernels_rows.hip",
               "hs_sample_kernel.hpp", "hs_device.hpp", "hs_api.hip", "hs_internal.hpp"):
-        with open(os.path.join(ROOT, "logit_transform_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "logit_transform_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        text = "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+        h.update(text.encode())
     return h.hexdigest()[:16]
 
 

@@ -1,34 +1,37 @@
 // hs_sample_kernel.hpp -- the sampling kernel of libhs (gfx950): batched HLG tone curve +
-// Gumbel-max draws, and its split-row pre-pass. Included by the translation units that
-// instantiate it (hs_kernels.hip, hs_kernels_pivot.hip).
+// Gumbel-max draws, its split-row pre-pass, and their launchers. Included by the translation
+// units that instantiate them (hs_kernels.hip: given pivot and curve off; hs_kernels_pivot.hip:
+// top- and entropy-anchored pivots; hs_kernels_rows.hip: the curve set per row).
 //
 // Sources, cited by page title and section:
 //   [HLG]  "HLG sampling -- a piecewise tone curve on the logits" (mlx-bun design document).
 //   [GMX]  "Softmax-free GPU sampling: Gumbel-max categorical sampling kernel" (mlxcel #900).
 //
-// Work decomposition. A block owns one contiguous chunk of one row and keeps it in VGPRs as
-// raw 16-byte vectors (thread t holds vectors t, t+BS, t+2BS, ...: consecutive lanes read
-// consecutive 16 B, so every wave load is one contiguous 1 KiB). The row is read from HBM
-// once; every pass after the load (max, sum of exponentials, and each draw) runs on the
-// register copy. With one chunk per row the row's log-sum-exp is reduced inside the block
-// (single read). With several chunks per row a pre-pass leaves per-chunk (max, sum) pairs in
-// the workspace, every block of the row folds them in the same fixed order, and the chunks'
-// winning keys meet in a 64-bit atomic max; the last block of the row to finish writes the
-// token ids and zeroes its workspace slots again.
+// Work decomposition. A block owns one contiguous chunk of one row (the whole row when it
+// fits) and one group of the row's draws. Lane t owns the 16-byte vectors t, t+BS, t+2BS, ...
+// ("slots"), so every wave load is one contiguous 1 KiB. One streaming pass reads the chunk
+// once: the first draw's random words run a few slots ahead of the logits, and per slot the
+// pass keeps only summaries in LDS (the vector's largest logit as a bf16-grid upper bound, the
+// top 16 bits of its largest word), the lane's running maximum and log-sum-exp, and the
+// lane's "champion" vector (the one holding its largest word) in registers. Rows split over
+// several blocks combine their chunks' log-sum-exp partials either from a pre-pass or, when
+// the whole grid is resident, by exchanging them inside this kernel; the chunks' winning keys
+// meet in a 64-bit atomic max, and the last block of each (row, draw group) writes the token
+// ids and zeroes its workspace slots again.
 //
 // Screening. A draw's winner is the exact argmax over all elements, but the expensive part
 // of an element's score (curve branches, two logarithms) is evaluated only when an upper
 // bound on that score reaches a lower bound on the draw's winning score, less a slack:
 //   score = l'/T + G(r) <= U(x) + (n(r) + 1) ln 2,
 // where U(x) = (m/T) * max(x - c, -w) bounds g(x - c)/T (g lies below its mid line past the
-// shoulder knot and below -m*w in the toe) and n(r), the leading ones of the word, bounds G
-// (G(r) <= -log(1 - u) <= (n + 1) ln 2). The first pass over a draw keeps, per vector, only
-// the largest word (and so the largest n); a vector whose largest logit and largest word
-// cannot reach the bound is skipped whole, and the few that can are drawn again and tested
-// element by element. The lower bound is the exact score of one element per lane, the one
-// with the lane's largest word, maximised over the block. The bounds are rigorous up to fp32
-// rounding, which the slack covers many times over, so the screened result equals the
-// exhaustive one bit for bit (a test checks this).
+// shoulder knot and below -m*w in the toe; a tangent of the shoulder tightens it near the
+// top) and n(r), the leading ones of the word, bounds G (G(r) <= -log(1 - u) <= (n + 1) ln 2).
+// A vector whose largest logit and largest word cannot reach the bound is skipped whole; the
+// champion is scored from registers and the few other vectors that can are read again, drawn
+// again and tested element by element. The lower bound is the best exact score of the
+// bootstrap candidates (per lane, the element holding its champion's largest word). The
+// bounds are rigorous up to fp32 rounding, which the slack covers many times over, so the
+// screened result equals the exhaustive one bit for bit (a test checks this).
 #pragma once
 
 #include <hip/hip_runtime.h>
