@@ -172,6 +172,14 @@ int hs_sample_ex(const hs_logits *x, const float *T, const float *mu,
                  int32_t K, int32_t *out, float *best, void *ws, size_t ws_bytes,
                  const hs_sample_opts *opts, void *stream);
 
+/* The launch plan hs_sample_ex would use for this shape (introspection; nothing is launched):
+ * plan[0] blocks per row (chunks), [1] 16-byte vectors per chunk, [2] threads per block,
+ * [3] vector slots per thread, [4] blocks sharing a row's draws, [5] draws per such block,
+ * [6] grid size, [7] the CU count the plan assumed (256 when no device is visible).
+ * have_ws: whether a workspace would be given (split rows need one). plan: host int64[8]. */
+int hs_sample_plan(const hs_logits *x, int32_t K, int32_t hlg_on, int32_t have_ws,
+                   const hs_sample_opts *opts, int64_t *plan);
+
 /* hs_sample_ex with the curve set per row: row b is sampled as hs_sample_ex would sample it
  * alone with hlg = NULL (rows[b].enabled == 0) or with the curve of rows[b] (otherwise), in one
  * launch [HLG, The transfer function; The pivot; GMX, Background]. Per-row parameters are

@@ -34,7 +34,7 @@ _DTYPES = {torch.float32: HS_F32, torch.bfloat16: HS_BF16, torch.float16: HS_F16
 EXPORTED_SYMBOLS = (
     "hs_logsumexp", "hs_hlg_transform", "hs_hlg_pivot", "hs_gumbel_argmax", "hs_sample",
     "hs_sample_ex", "hs_sample_rows", "hs_filter_threshold", "hs_sample_filtered",
-    "hs_workspace_bytes", "hs_workspace_init", "hs_philox4x32_10", "hs_stream_words",
+    "hs_workspace_bytes", "hs_workspace_init", "hs_sample_plan", "hs_philox4x32_10", "hs_stream_words",
     "hs_gumbel_f32", "hs_status_str", "hs_version",
 )
 
@@ -122,6 +122,8 @@ def load() -> C.CDLL:
     L.hs_workspace_bytes.argtypes = [i64, i64, i32, i32, i32]
     L.hs_workspace_bytes.restype = sz
     L.hs_workspace_init.argtypes = [vp, sz, vp]
+    L.hs_sample_plan.argtypes = [LP, i32, i32, i32, OP, C.POINTER(C.c_int64)]
+    L.hs_sample_plan.restype = C.c_int
     L.hs_philox4x32_10.argtypes = [vp, vp, vp, i64, vp]
     L.hs_stream_words.argtypes = [vp, vp, i64, i64, i32, vp, vp]
     L.hs_gumbel_f32.argtypes = [vp, vp, i64, vp]
@@ -222,6 +224,19 @@ def _mu_vec(mu, hp, B, dev):
     if hp.pivot == 0 and mu is None:
         raise ValueError("mu is required with the curve on and the pivot given")
     return _row_vec(mu, B, torch.float32, dev, "mu") if (mu is not None and hp.pivot == 0) else None
+
+
+def sample_plan(B: int, V: int, K: int, dtype: torch.dtype, hlg_on: bool,
+                have_ws: bool = True, opts: Optional[SampleOpts] = None) -> dict:
+    """The launch plan the library picks for a shape (no device needed: 256 CUs assumed when
+    none is visible)."""
+    L = load()
+    x = _Logits(0x10000, _DTYPES[dtype], int(B), int(V), int(V))   # never dereferenced
+    out = (C.c_int64 * 8)()
+    _check(L.hs_sample_plan(C.byref(x), int(K), 1 if hlg_on else 0, 1 if have_ws else 0,
+                            C.byref(opts) if opts is not None else None, out), "hs_sample_plan")
+    keys = ("nchunk", "cv", "bs", "nv", "draw_groups", "draws_per_group", "grid", "cus")
+    return dict(zip(keys, list(out)))
 
 
 def workspace_bytes(B: int, V: int, K: int, dtype: torch.dtype, hlg_on: bool) -> int:

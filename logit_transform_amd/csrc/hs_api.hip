@@ -413,6 +413,26 @@ size_t hs_workspace_bytes(int64_t B, int64_t V, int32_t K, int32_t dtype, int32_
     return ws_layout(B, K).total;
 }
 
+int hs_sample_plan(const hs_logits *x, int32_t K, int32_t hlg_on, int32_t have_ws,
+                   const hs_sample_opts *opts, int64_t *plan) {
+    int rc = check_logits(x);
+    if (rc) return rc;
+    if (!plan || K < 1 || !opts_valid(opts)) return HS_ERR_INVALID_ARG;
+    if ((size_t)x->B * (size_t)K >= ((size_t)1 << 31)) return HS_ERR_UNSUPPORTED;
+    Plan P;
+    rc = make_plan(x, K, hlg_on != 0, have_ws != 0, opts, &P);
+    if (rc) return rc;
+    plan[0] = P.nchunk;
+    plan[1] = P.cv;
+    plan[2] = P.bs;
+    plan[3] = P.nv;
+    plan[4] = P.nkg;
+    plan[5] = P.kpg;
+    plan[6] = P.grid;
+    plan[7] = num_cus();
+    return HS_OK;
+}
+
 int hs_workspace_init(void *ws, size_t ws_bytes, void *stream) {
     if (!ws || ws_bytes % 4 != 0) return HS_ERR_INVALID_ARG;
     if (ws_bytes == 0) return HS_OK;
