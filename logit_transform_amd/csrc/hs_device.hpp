@@ -123,14 +123,6 @@ __device__ __forceinline__ Words4 stream_group(const Stream &s, uint32_t q) {
     return philox4x32_10_uk(q, s.row, s.off_lo, s.off_hi, s.key0, s.key1);
 }
 
-// Same, for use inside a loop over draws: the group index is made opaque so that the
-// compiler cannot hoist the draw-invariant first multiply of every group out of the loop
-// (which costs two registers per group and spills).
-__device__ __forceinline__ Words4 stream_group_in_loop(const Stream &s, uint32_t q) {
-    asm volatile("" : "+v"(q));
-    return philox4x32_10_uk(q, s.row, s.off_lo, s.off_hi, s.key0, s.key1);
-}
-
 // ------------------------------------------------------------------------------------------
 // Accurate fp32 log1p(t) for t > -1 by the log(1+t) * t / ((1+t) - 1) correction (Goldberg,
 // "What every computer scientist should know about floating-point arithmetic", 1991): the
@@ -393,68 +385,6 @@ __device__ __forceinline__ float block_sum(float v, float *red) {
     if (lane == 0) red[wid] = v;
     __syncthreads();
     return wave_sum(lane < nw ? red[lane] : 0.0f);
-}
-
-__device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t *red) {
-    // lane and wave index recomputed at each call, not held in registers across a caller's loop
-    int lane = threadIdx.x & 63;
-    asm volatile("" : "+v"(lane));
-    int wid = threadIdx.x >> 6;
-    asm volatile("" : "+v"(wid));
-    const int nw = (blockDim.x + 63) >> 6;
-    v = wave_max_u64(v);
-    if (lane == 0) red[wid] = v;
-    __syncthreads();
-    return wave_max_u64(lane < nw ? red[lane] : 0ull);
-}
-
-// Log-sum-exp of per-lane (max, sum of exp(x - max)) pairs over the block: the pair of the
-// block is (M, S) with M the largest max and S the sum of each sum rescaled to M.
-struct MaxSum {
-    float m, s;
-};
-
-__device__ __forceinline__ MaxSum block_maxsum(float m, float s, float2 *red) {
-    // lane and wave index recomputed at each call, not held in registers across a caller's loop
-    int lane = threadIdx.x & 63;
-    asm volatile("" : "+v"(lane));
-    int wid = threadIdx.x >> 6;
-    asm volatile("" : "+v"(wid));
-    const int nw = (blockDim.x + 63) >> 6;
-    constexpr float kL2e = 1.44269504088896341f;
-    float mw = wave_max(m);
-    float sw = wave_sum((m > -__builtin_inff()) ? s * __builtin_amdgcn_exp2f((m - mw) * kL2e) : 0.0f);
-    if (lane == 0) red[wid] = make_float2(mw, sw);
-    __syncthreads();
-    const float2 p = lane < nw ? red[lane] : make_float2(-__builtin_inff(), 0.0f);
-    const float mb = wave_max(p.x);
-    const float sb = wave_sum((p.x > -__builtin_inff()) ? p.y * __builtin_amdgcn_exp2f((p.x - mb) * kL2e) : 0.0f);
-    MaxSum r;
-    r.m = mb;
-    r.s = sb;
-    return r;
-}
-
-// The same pair in base-2 units: m is a maximum of x log2(e) and s = sum 2^(x log2(e) - m).
-// Lanes without any finite element pass m = -FLT_MAX (finite, so that no inf - inf arises)
-// and s = 0. Returns the block's (m, s) in the same units.
-__device__ __forceinline__ MaxSum block_maxsum_log2(float m, float s, float2 *red) {
-    int lane = threadIdx.x & 63;
-    asm volatile("" : "+v"(lane));
-    int wid = threadIdx.x >> 6;
-    asm volatile("" : "+v"(wid));
-    const int nw = (blockDim.x + 63) >> 6;
-    const float mw = wave_max(m);
-    const float sw = wave_sum(s * __builtin_amdgcn_exp2f(m - mw));
-    if (lane == 0) red[wid] = make_float2(mw, sw);
-    __syncthreads();
-    const float2 p = lane < nw ? red[lane] : make_float2(-3.402823466e38f, 0.0f);
-    const float mb = wave_max(p.x);
-    const float sb = wave_sum(p.y * __builtin_amdgcn_exp2f(p.x - mb));
-    MaxSum r;
-    r.m = mb;
-    r.s = sb;
-    return r;
 }
 
 }  // namespace hs
