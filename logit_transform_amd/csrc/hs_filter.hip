@@ -211,32 +211,41 @@ __device__ __forceinline__ uint32_t select_level(const char *rowp, int64_t nvec,
     return s_new;
 }
 
+// A row's filter settings; false (with tau written) when they decide tau without the logits:
+// NaN for an invalid temperature or p (the sampler turns it into -2 for the row), -inf when
+// nothing is filtered (greedy rows, k <= 0 or k >= V with p >= 1).
+struct RowFilter {
+    float T, p;
+    int32_t k;
+};
+
+__device__ __forceinline__ bool row_filter(const FilterArgs &a, int64_t b, RowFilter *f) {
+    f->T = a.T[b];
+    f->k = a.top_k ? a.top_k[b] : 0;
+    if ((int64_t)f->k >= a.V) f->k = 0;   // a k of at least V keeps every token
+    f->p = a.top_p ? a.top_p[b] : 1.0f;
+    float tau;
+    if (!(f->T >= 0.0f) || !(f->T < __builtin_inff()) || !(f->p > 0.0f)) {
+        tau = __builtin_nanf("");
+    } else if (f->T == 0.0f || (f->k <= 0 && !(f->p < 1.0f))) {
+        tau = -__builtin_inff();
+    } else {
+        return true;
+    }
+    if (threadIdx.x == 0) a.tau[b] = tau;
+    return false;
+}
+
+// The radix selection of tau (every dtype) with the LDS histograms hc [2048] and hm [2048].
 template <int DT>
-__global__ __launch_bounds__(1024) void k_filter_tau(FilterArgs a) {
+__device__ float tau_radix(const FilterArgs &a, int64_t b, const RowFilter &f, uint32_t *hc,
+                           double *hm, float *red_f, uint32_t *red_n) {
     using tr = dtype_traits<DT>;
     using D = Digits<DT>;
     constexpr int EPV = tr::epv;
-    __shared__ uint32_t hc[2048];
-    __shared__ double hm[2048];
-    __shared__ float red_f[16];
-    __shared__ uint32_t red_n[16];
-
-    const int64_t b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const float T = a.T[b];
-    // a k of at least V keeps every token, as does k <= 0
-    int32_t k = a.top_k ? a.top_k[b] : 0;
-    if ((int64_t)k >= a.V) k = 0;
-    const float p = a.top_p ? a.top_p[b] : 1.0f;
-    // invalid temperature or p: NaN, which the sampler turns into -2 for the row
-    if (!(T >= 0.0f) || !(T < __builtin_inff()) || !(p > 0.0f)) {
-        if (tid == 0) a.tau[b] = __builtin_nanf("");
-        return;
-    }
-    if (T == 0.0f || (k <= 0 && !(p < 1.0f))) {   // greedy, or nothing to filter
-        if (tid == 0) a.tau[b] = -__builtin_inff();
-        return;
-    }
+    const float T = f.T, p = f.p;
+    const int32_t k = f.k;
     const char *rowp = reinterpret_cast<const char *>(a.data) + b * a.ld * tr::esize;
     const int64_t nvec = (a.V + EPV - 1) / EPV;
 
@@ -282,10 +291,7 @@ __global__ __launch_bounds__(1024) void k_filter_tau(FilterArgs a) {
         M = block_max(mx, red_f);
         NF = block_sum_u32(nf, red_n);
     }
-    if (NF == 0u) {
-        if (tid == 0) a.tau[b] = -__builtin_inff();
-        return;
-    }
+    if (NF == 0u) return -__builtin_inff();
 
     // top-p over the tokens top-k keeps: the key at which the tempered mass from the top
     // reaches p times their total
@@ -330,6 +336,235 @@ __global__ __launch_bounds__(1024) void k_filter_tau(FilterArgs a) {
                                          mass, lane, wid);
         tau = fmaxf(tau, key_value<DT>(prefix));
     }
+    return tau;
+}
+
+template <int DT>
+__global__ __launch_bounds__(1024) void k_filter_tau(FilterArgs a) {
+    __shared__ uint32_t hc[2048];
+    __shared__ double hm[2048];
+    __shared__ float red_f[16];
+    __shared__ uint32_t red_n[16];
+    RowFilter f;
+    if (!row_filter(a, blockIdx.x, &f)) return;
+    const float tau = tau_radix<DT>(a, blockIdx.x, f, hc, hm, red_f, red_n);
+    if (threadIdx.x == 0) a.tau[blockIdx.x] = tau;
+}
+
+// ---- 16-bit logits: one exact-value histogram per row ---------------------------------------
+// A 16-bit logit takes one of 65536 bit patterns, so one pass can count every distinct value
+// of the row: two 16-bit counters per LDS word (pattern h in word h >> 1, half h & 1), 128 KiB.
+// Counts, the row's maximum, the k-th largest value and the tempered masses then come from
+// that histogram alone: the row is read once, and an element costs one LDS atomic instead of
+// one per selection level (with an exponential and an fp64 atomic for top-p). A counter
+// overflows only when more than 65535 elements share one value; the sum of all counters then
+// falls short of the finite count, and the block runs the radix selection instead.
+//
+// Ranks order the patterns by value from the top: ranks 0 .. 32767 are the non-negative
+// patterns 0x7FFF down to 0x0000, ranks 32768 .. 65535 the negative ones 0x8000 up to 0xFFFF.
+// NaN and -inf patterns never hold a count, and -0 is merged into +0 before any selection.
+// Thread t owns ranks 64t .. 64t + 63, i.e. 32 consecutive words.
+__device__ __forceinline__ uint32_t rank_bits(uint32_t r) {
+    return r < 32768u ? 32767u - r : r;
+}
+__device__ __forceinline__ uint32_t bits_rank(uint32_t h) {
+    return h < 32768u ? 32767u - h : h;
+}
+__device__ __forceinline__ int owned_words(int t) {
+    return t < 512 ? 16352 - 32 * t : 32 * t;
+}
+__device__ __forceinline__ uint32_t hist_count(const uint32_t *hist, uint32_t h) {
+    return (hist[h >> 1] >> ((h & 1u) << 4)) & 0xFFFFu;
+}
+template <int DT>
+__device__ __forceinline__ float bits_value(uint32_t h) {
+    if constexpr (DT == DT_BF16) return __uint_as_float(h << 16);
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// Inclusive and exclusive block scan over threads in index order (1024 threads), and the
+// total. incl of a thread equals excl of the next one exactly, also in floating point.
+template <typename T>
+__device__ __forceinline__ void block_scan(T v, T *red, T *excl, T *incl, T *total) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    T in = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const T o = __shfl_up(in, d, 64);
+        if (lane >= d) in += o;
+    }
+    T ex = __shfl_up(in, 1, 64);
+    if (lane == 0) ex = (T)0;
+    if (lane == 63) red[wid] = in;
+    __syncthreads();
+    T base = (T)0, run = (T)0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+        if (w == wid) base = run;
+        run = run + red[w];
+    }
+    __syncthreads();
+    *excl = lane == 0 ? base : base + ex;
+    *incl = base + in;
+    *total = run;
+}
+
+// (wave 0) Among the 64 ranks of thread t, the first at which the running total of weight()
+// from `above` reaches target; the last rank of non-zero weight when it never does (a total
+// that rounding left short of the target).
+template <typename Tw, typename W>
+__device__ __forceinline__ uint32_t resolve_rank(int t, Tw above, Tw target, int lane, W weight) {
+    t = min(max(t, 0), 1023);
+    const uint32_t r = 64u * (uint32_t)t + (uint32_t)lane;
+    const Tw w = weight(r);
+    Tw in = w;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const Tw o = __shfl_up(in, d, 64);
+        if (lane >= d) in += o;
+    }
+    const uint64_t hit = __ballot(above + in >= target);
+    const uint64_t nz = __ballot(w > (Tw)0);
+    const int l = hit ? __builtin_ctzll(hit) : 63 - __builtin_clzll(nz | 1ull);
+    return 64u * (uint32_t)t + (uint32_t)l;
+}
+
+template <int DT>
+__global__ __launch_bounds__(1024) void k_filter_tau16(FilterArgs a) {
+    using tr = dtype_traits<DT>;
+    constexpr int EPV = tr::epv;
+    __shared__ uint4 s_hist[8192];
+    __shared__ uint32_t red_u[16];
+    __shared__ double red_d[16];
+    __shared__ float red_f[16];
+    __shared__ int s_thr[3];
+    __shared__ uint32_t s_above[2];
+    __shared__ double s_above_m;
+    __shared__ uint32_t s_rank[3];
+    uint32_t *hist = reinterpret_cast<uint32_t *>(s_hist);
+
+    const int64_t b = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    RowFilter f;
+    if (!row_filter(a, b, &f)) return;
+    const char *rowp = reinterpret_cast<const char *>(a.data) + b * a.ld * tr::esize;
+    const int64_t nvec = (a.V + EPV - 1) / EPV;
+
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s_hist[tid + 1024 * j] = make_uint4(0u, 0u, 0u, 0u);
+    if (tid < 3) s_thr[tid] = -1;
+    __syncthreads();
+    uint32_t nf = 0u;
+    for_each_vec<DT>(rowp, nvec, a.V, a.aligned, [&](const uint4 &v) {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+            const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+            const uint32_t h = (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+            if (elem<DT>(v, e) > -__builtin_inff()) {   // NaN and -inf are not counted
+                atomicAdd(&hist[h >> 1], (h & 1u) ? 0x10000u : 1u);
+                ++nf;
+            }
+        }
+    });
+    __syncthreads();
+    if (tid == 0) {   // -0 (pattern 0x8000, word 0x4000 low half) joins +0 (word 0 low half)
+        const uint32_t neg0 = hist[0x4000] & 0xFFFFu;
+        hist[0x4000] -= neg0;
+        hist[0] += neg0;
+    }
+    const uint32_t NF = block_sum_u32(nf, red_u);
+
+    // per-thread counts over the owned words (read in a lane-rotated order: no bank conflicts)
+    const int base = owned_words(tid);
+    uint32_t own = 0u;
+#pragma unroll 8
+    for (int j = 0; j < 32; ++j) {
+        const uint32_t w = hist[base + ((j + lane) & 31)];
+        own += (w & 0xFFFFu) + (w >> 16);
+    }
+    uint32_t ex, in, total;
+    block_scan(own, red_u, &ex, &in, &total);
+    if (total != NF) {   // a counter overflowed: select by radix levels (LDS reused)
+        const float tau = tau_radix<DT>(a, b, f, hist, reinterpret_cast<double *>(hist + 2048),
+                                        red_f, red_u);
+        if (tid == 0) a.tau[b] = tau;
+        return;
+    }
+    if (NF == 0u) {
+        if (tid == 0) a.tau[b] = -__builtin_inff();
+        return;
+    }
+    const bool topk = f.k > 0 && (uint32_t)f.k < NF;
+    if (ex < 1u && in >= 1u) s_thr[0] = tid;   // holds the largest logit
+    if (topk && ex < (uint32_t)f.k && in >= (uint32_t)f.k) {
+        s_thr[1] = tid;
+        s_above[1] = ex;
+    }
+    __syncthreads();
+    if (wid == 0) {
+        auto cnt = [&](uint32_t r) { return hist_count(hist, rank_bits(r)); };
+        const uint32_t rmax = resolve_rank<uint32_t>(s_thr[0], 0u, 1u, lane, cnt);
+        const uint32_t rk = topk ? resolve_rank<uint32_t>(s_thr[1], s_above[1], (uint32_t)f.k,
+                                                          lane, cnt)
+                                 : 65535u;
+        if (lane == 0) {
+            s_rank[0] = rmax;
+            s_rank[1] = rk;
+        }
+    }
+    __syncthreads();
+    const float M = bits_value<DT>(rank_bits(s_rank[0]));
+    const uint32_t rk = s_rank[1];
+    float tau = topk ? bits_value<DT>(rank_bits(rk)) : -__builtin_inff();
+
+    // top-p over the values top-k keeps (ranks <= rk): tempered mass count * 2^((x - M) c1),
+    // fp32 terms summed in fp64
+    if (f.p < 1.0f) {
+        const float c1 = kLog2e / f.T;
+        auto mass = [&](uint32_t r, uint32_t c) -> double {
+            return (c > 0u && r <= rk)
+                       ? (double)c * (double)__builtin_amdgcn_exp2f(
+                                         (bits_value<DT>(rank_bits(r)) - M) * c1)
+                       : 0.0;
+        };
+        double own_m = 0.0;
+        if (64u * (uint32_t)tid <= rk) {
+            for (int j = 0; j < 32; ++j) {
+                const int wd = base + ((j + lane) & 31);
+                const uint32_t w = hist[wd];
+                if (w) {
+                    own_m += mass(bits_rank(2u * (uint32_t)wd), w & 0xFFFFu);
+                    own_m += mass(bits_rank(2u * (uint32_t)wd + 1u), w >> 16);
+                }
+            }
+        }
+        double exm, inm, S;
+        block_scan(own_m, red_d, &exm, &inm, &S);
+        const double P = (double)f.p * S;
+        if (exm < P && inm >= P) {
+            s_thr[2] = tid;
+            s_above_m = exm;
+        }
+        __syncthreads();
+        int tp = s_thr[2];
+        double above = s_above_m;
+        if (tp < 0) {   // rounding left the total short of P: the last thread with kept mass
+            const uint64_t m = __ballot(own_m > 0.0);
+            if (lane == 0) red_u[wid] = m ? (uint32_t)(64 * wid + 63 - __builtin_clzll(m)) : 0u;
+            __syncthreads();
+            tp = 0;
+            for (int w = 0; w < 16; ++w) tp = max(tp, (int)red_u[w]);
+            above = 0.0;
+        }
+        if (wid == 0) {
+            const uint32_t rp = resolve_rank<double>(tp, above, P, lane, [&](uint32_t r) {
+                return mass(r, hist_count(hist, rank_bits(r)));
+            });
+            if (lane == 0) s_rank[2] = rp;
+        }
+        __syncthreads();
+        tau = fmaxf(tau, bits_value<DT>(rank_bits(s_rank[2])));
+    }
     if (tid == 0) a.tau[b] = tau;
 }
 
@@ -338,8 +573,8 @@ __global__ __launch_bounds__(1024) void k_filter_tau(FilterArgs a) {
 hipError_t launch_filter_tau(int dt, const FilterArgs &a, int grid, hipStream_t s) {
     switch (dt) {
         case DT_F32: hipLaunchKernelGGL(k_filter_tau<DT_F32>, dim3(grid), dim3(1024), 0, s, a); break;
-        case DT_BF16: hipLaunchKernelGGL(k_filter_tau<DT_BF16>, dim3(grid), dim3(1024), 0, s, a); break;
-        case DT_F16: hipLaunchKernelGGL(k_filter_tau<DT_F16>, dim3(grid), dim3(1024), 0, s, a); break;
+        case DT_BF16: hipLaunchKernelGGL(k_filter_tau16<DT_BF16>, dim3(grid), dim3(1024), 0, s, a); break;
+        case DT_F16: hipLaunchKernelGGL(k_filter_tau16<DT_F16>, dim3(grid), dim3(1024), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -88,6 +88,36 @@ def test_filter_kernel_choices(hs, oracle_mod):
         np.testing.assert_array_equal(res[a][1], res[b][1])
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_filters_on_heavily_tied_rows(hs, oracle_mod, dtype):
+    """16-bit rows with long runs of equal logits: more than 65535 copies of one value (a
+    16-bit counter of the exact-value histogram overflows, and the radix selection takes
+    over), signed zeros (-0 and +0 are one value, merged or not past 65535), values on a coarse
+    grid, more than 65535 masked entries (never counted), and a constant row."""
+    B, V = 6, 151936
+    w = W.generic(B, V, dtype, seed=21, scale=1.0, K=3)
+    x = w.logits.float().numpy().copy()
+    rng = np.random.default_rng(22)
+    x[0, rng.choice(V, 70000, replace=False)] = 0.5
+    z = rng.choice(V, 80000, replace=False)
+    x[1, z] = np.where(rng.random(80000) < 0.5, 0.0, -0.0)
+    z = rng.choice(V, 60000, replace=False)
+    x[2, z] = np.where(rng.random(60000) < 0.5, 0.0, -0.0)
+    x[3] = np.round(x[3] * 4.0) / 4.0
+    x[4, rng.choice(V, 100000, replace=False)] = -np.inf
+    x[5] = 1.0
+    w.logits = torch.from_numpy(x).to(dtype)
+    # k lands inside the tie runs (row 0: below the 70000 copies of 0.5; row 2: in the zeros)
+    n_above0 = int((x[0] > 0.5).sum())
+    n_above2 = int((x[2] > 0.0).sum())
+    k = np.array([n_above0 + 100, 0, n_above2 + 10, 50, 1000, 5], dtype=np.int32)
+    p = np.array([0.9, 0.5, 0.95, 0.8, 0.3, 0.7], dtype=np.float32)
+    _check_rows(hs, oracle_mod, w, k, p, "tied rows %s" % dtype)
+    k2 = np.array([1, 70001, 0, 0, 200000, 0], dtype=np.int32)
+    p2 = np.array([0.999, 1.0, 0.6, 0.99, 0.95, 0.5], dtype=np.float32)
+    _check_rows(hs, oracle_mod, w, k2, p2, "tied rows (2) %s" % dtype)
+
+
 def test_special_rows_and_closed_cases(hs):
     V = 500
     rng = np.random.default_rng(41)
