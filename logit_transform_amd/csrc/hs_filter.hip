@@ -6,15 +6,18 @@
 // included), and the sampler draws the Gumbel-max of x / T over the kept tokens, an exact
 // sample of the renormalised softmax [GMX, Background].
 //
-// One block per row finds tau by radix selection over an order-preserving integer key of
-// the logit, each level a pass over the row (which stays in the caches after the first) that
-// histograms one digit of the keys sharing the digits selected so far: 11 + 5 bits for bf16 /
-// f16, 11 + 11 + 10 for fp32 (a wide first digit spreads the bulk of a row over many bins, so
-// the LDS atomics seldom collide). Top-k selects the k-th largest finite key by counts (its
-// first pass also finds the row's maximum and finite count); top-p selects, among the keys
-// top-k keeps, the key at which the tempered mass exp((x - x_max) / T), summed from the top,
-// reaches p times the total, by fp64 sums of fp32 terms. Wave 0 picks each level's bin with a
-// parallel scan over the bins.
+// One block per row finds tau. For 16-bit logits (k_filter_tau16) one pass counts every
+// distinct value of the row in an LDS histogram of all 65536 bit patterns, and the thresholds
+// come from scans over that histogram (see the section below). For fp32 logits, and for a
+// 16-bit row where more than 65535 elements share a value, a radix selection over an
+// order-preserving integer key of the logit is used: each level a pass over the row (which
+// stays in the caches after the first) that histograms one digit of the keys sharing the
+// digits selected so far: 11 + 11 + 10 bits for fp32, 11 + 5 for 16-bit logits (a wide first
+// digit spreads the bulk of a row over many bins, so the LDS atomics seldom collide).
+// Top-k selects the k-th largest finite key by counts (its first pass also finds the row's
+// maximum and finite count); top-p selects, among the keys top-k keeps, the key at which the
+// tempered mass exp((x - x_max) / T), summed from the top, reaches p times the total, by fp64
+// sums of fp32 terms. Wave 0 picks each level's bin with a parallel scan over the bins.
 #include <hip/hip_runtime.h>
 
 #include "hs_device.hpp"
