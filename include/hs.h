@@ -106,8 +106,10 @@ int hs_hlg_pivot(const hs_logits *x, const float *mu, const hs_hlg_params *p, fl
  * T[b] == 0 is greedy: argmax of x, the same index for all K draws.
  * T: device float[B]; seed, offset: device uint64[B]; out: device int32[B*K].
  * ws / ws_bytes: device workspace of at least hs_workspace_bytes(B, V, K, dtype, 0) bytes,
- * zero-filled before its first use (hs_workspace_init); every successful call leaves it
- * zero-filled again. Calls that may run concurrently need separate workspaces. ws may be
+ * zero-filled before its first use (hs_workspace_init); every successful call leaves its
+ * counters, keys and flags zero-filled again (the per-row filter thresholds and row marks of
+ * hs_sample_filtered are rewritten by every such call before they are read). Calls that may
+ * run concurrently need separate workspaces. ws may be
  * NULL with ws_bytes 0, in which case only single-block-per-row kernels are used. */
 int hs_gumbel_argmax(const hs_logits *x, const float *T, const uint64_t *seed,
                      const uint64_t *offset, int32_t K, int32_t *out, void *ws,
@@ -215,7 +217,11 @@ int hs_filter_threshold(const hs_logits *x, const float *T, const int32_t *top_k
  * x / T over {i : x_i >= tau[b]}, an exact sample of softmax(x / T) renormalised over them
  * [GMX, Background]. A row with an invalid T or top_p gives -2; greedy rows (T == 0) are the
  * argmax of x. A workspace of hs_workspace_bytes(B, V, K, dtype, 0) bytes is required (the
- * thresholds live in it). best and opts as hs_sample_ex (NULL allowed). */
+ * thresholds live in it). best and opts as hs_sample_ex (NULL allowed). With the automatic
+ * plan (opts NULL or variant 0), a row of 16-bit logits that keeps at most 2048 tokens, with
+ * K <= 2048 and (kept tokens) * K <= 65536, is drawn by the threshold kernel itself, which
+ * scores only the kept tokens; an explicit variant runs the sampling kernel on every row. Both
+ * give the same ids and scores. */
 int hs_sample_filtered(const hs_logits *x, const float *T, const int32_t *top_k,
                        const float *top_p, const uint64_t *seed, const uint64_t *offset,
                        int32_t K, int32_t *out, float *best, void *ws, size_t ws_bytes,

@@ -73,7 +73,7 @@ int num_cus() {
 }
 
 struct WsLayout {
-    size_t counters, keys, partials, flags, tau, total;
+    size_t counters, keys, partials, flags, tau, done, total;
 };
 
 WsLayout ws_layout(int64_t B, int32_t K) {
@@ -83,7 +83,8 @@ WsLayout ws_layout(int64_t B, int32_t K) {
     L.partials = L.keys + align256((size_t)B * (size_t)K * 8);
     L.flags = L.partials + align256((size_t)B * hs::kMaxChunks * sizeof(float4));
     L.tau = L.flags + align256((size_t)B * hs::kMaxChunks * 4);   // exchange flags
-    L.total = L.tau + align256((size_t)B * 4);   // top-k / top-p thresholds
+    L.done = L.tau + align256((size_t)B * 4);    // top-k / top-p thresholds
+    L.total = L.done + align256((size_t)B * 4);  // rows the threshold kernel drew
     return L;
 }
 
@@ -257,6 +258,17 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
         f.top_k = filt->top_k;
         f.top_p = filt->top_p;
         f.tau = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + L.tau);
+        // With the automatic plan, rows that keep few tokens are drawn by the threshold kernel
+        // and skipped by the sampler; an explicit kernel choice runs the sampler on every row.
+        if (!opts || opts->variant == 0) {
+            f.done = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(ws) + L.done);
+            f.out = out;
+            f.best_out = best;
+            f.seed = seed;
+            f.offset = offset;
+            f.K = K;
+            a.done = f.done;
+        }
         if (hs::launch_filter_tau(x->dtype, f, (int)x->B, s) != hipSuccess) return HS_ERR_HIP;
         a.tau = f.tau;
     }

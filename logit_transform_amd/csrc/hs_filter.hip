@@ -152,13 +152,13 @@ __device__ __forceinline__ void for_each_vec(const char *rowp, int64_t nvec, int
         const uint4 *p = reinterpret_cast<const uint4 *>(rowp);
         for (; gv + 3 * BS < nfull; gv += 4 * BS) {
             const uint4 v0 = p[gv], v1 = p[gv + BS], v2 = p[gv + 2 * BS], v3 = p[gv + 3 * BS];
-            f(v0);
-            f(v1);
-            f(v2);
-            f(v3);
+            f(v0, gv);
+            f(v1, gv + BS);
+            f(v2, gv + 2 * BS);
+            f(v3, gv + 3 * BS);
         }
     }
-    for (; gv < nvec; gv += BS) f(load_vec<DT>(rowp, gv, V, aligned));
+    for (; gv < nvec; gv += BS) f(load_vec<DT>(rowp, gv, V, aligned), gv);
 }
 
 // One level of the selection: the histogram (counts, or masses w(x)) of digit `lev` over the
@@ -189,7 +189,7 @@ __device__ __forceinline__ uint32_t select_level(const char *rowp, int64_t nvec,
         if (v0 == v0) lo = fmaxf(lo, v0);
         if (v1 == v1) hi = v1;
     }
-    for_each_vec<DT>(rowp, nvec, V, aligned, [&](const uint4 &v) {
+    for_each_vec<DT>(rowp, nvec, V, aligned, [&](const uint4 &v, int64_t) {
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
             const float x = elem<DT>(v, e);
@@ -283,7 +283,7 @@ __device__ float tau_radix(const FilterArgs &a, int64_t b, const RowFilter &f, u
     } else {
         uint32_t nf = 0u;
         float mx = -__builtin_inff();
-        for_each_vec<DT>(rowp, nvec, a.V, a.aligned, [&](const uint4 &v) {
+        for_each_vec<DT>(rowp, nvec, a.V, a.aligned, [&](const uint4 &v, int64_t) {
 #pragma unroll
             for (int e = 0; e < EPV; ++e) {
                 const float x = elem<DT>(v, e);
@@ -307,7 +307,7 @@ __device__ float tau_radix(const FilterArgs &a, int64_t b, const RowFilter &f, u
         for (int j = tid; j < (1 << D::bits[0]); j += blockDim.x) hm[j] = 0.0;
         __syncthreads();
         const float lo = keyk > 0u ? tau : -__builtin_inff();   // tau = the value of keyk
-        for_each_vec<DT>(rowp, nvec, a.V, a.aligned, [&](const uint4 &v) {
+        for_each_vec<DT>(rowp, nvec, a.V, a.aligned, [&](const uint4 &v, int64_t) {
 #pragma unroll
             for (int e = 0; e < EPV; ++e) {
                 const float x = elem<DT>(v, e);
@@ -348,6 +348,7 @@ __global__ __launch_bounds__(1024) void k_filter_tau(FilterArgs a) {
     __shared__ double hm[2048];
     __shared__ float red_f[16];
     __shared__ uint32_t red_n[16];
+    if (a.done != nullptr && threadIdx.x == 0) a.done[blockIdx.x] = 0u;   // left to the sampler
     RowFilter f;
     if (!row_filter(a, blockIdx.x, &f)) return;
     const float tau = tau_radix<DT>(a, blockIdx.x, f, hc, hm, red_f, red_n);
@@ -416,7 +417,8 @@ __device__ __forceinline__ void block_scan(T v, T *red, T *excl, T *incl, T *tot
 // from `above` reaches target; the last rank of non-zero weight when it never does (a total
 // that rounding left short of the target).
 template <typename Tw, typename W>
-__device__ __forceinline__ uint32_t resolve_rank(int t, Tw above, Tw target, int lane, W weight) {
+__device__ __forceinline__ uint32_t resolve_rank(int t, Tw above, Tw target, int lane, W weight,
+                                                 Tw *cum) {
     t = min(max(t, 0), 1023);
     const uint32_t r = 64u * (uint32_t)t + (uint32_t)lane;
     const Tw w = weight(r);
@@ -429,7 +431,18 @@ __device__ __forceinline__ uint32_t resolve_rank(int t, Tw above, Tw target, int
     const uint64_t hit = __ballot(above + in >= target);
     const uint64_t nz = __ballot(w > (Tw)0);
     const int l = hit ? __builtin_ctzll(hit) : 63 - __builtin_clzll(nz | 1ull);
+    *cum = __shfl(above + in, l, 64);
     return 64u * (uint32_t)t + (uint32_t)l;
+}
+
+// (wave) The sum of v over lanes 0 .. l.
+__device__ __forceinline__ uint32_t wave_prefix_at(uint32_t v, int lane, int l) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t o = __shfl_up(v, d, 64);
+        if (lane >= d) v += o;
+    }
+    return __shfl(v, l, 64);
 }
 
 template <int DT>
@@ -444,10 +457,12 @@ __global__ __launch_bounds__(1024) void k_filter_tau16(FilterArgs a) {
     __shared__ uint32_t s_above[2];
     __shared__ double s_above_m;
     __shared__ uint32_t s_rank[3];
+    __shared__ uint32_t s_above_c, s_kept;   // count above the top-p crossing; kept tokens
     uint32_t *hist = reinterpret_cast<uint32_t *>(s_hist);
 
     const int64_t b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    if (a.done != nullptr && tid == 0) a.done[b] = 0u;   // set below if the row is drawn here
     RowFilter f;
     if (!row_filter(a, b, &f)) return;
     const char *rowp = reinterpret_cast<const char *>(a.data) + b * a.ld * tr::esize;
@@ -458,7 +473,7 @@ __global__ __launch_bounds__(1024) void k_filter_tau16(FilterArgs a) {
     if (tid < 3) s_thr[tid] = -1;
     __syncthreads();
     uint32_t nf = 0u;
-    for_each_vec<DT>(rowp, nvec, a.V, a.aligned, [&](const uint4 &v) {
+    for_each_vec<DT>(rowp, nvec, a.V, a.aligned, [&](const uint4 &v, int64_t) {
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
             const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
@@ -506,13 +521,15 @@ __global__ __launch_bounds__(1024) void k_filter_tau16(FilterArgs a) {
     __syncthreads();
     if (wid == 0) {
         auto cnt = [&](uint32_t r) { return hist_count(hist, rank_bits(r)); };
-        const uint32_t rmax = resolve_rank<uint32_t>(s_thr[0], 0u, 1u, lane, cnt);
+        uint32_t c1, kept = NF;
+        const uint32_t rmax = resolve_rank<uint32_t>(s_thr[0], 0u, 1u, lane, cnt, &c1);
         const uint32_t rk = topk ? resolve_rank<uint32_t>(s_thr[1], s_above[1], (uint32_t)f.k,
-                                                          lane, cnt)
+                                                          lane, cnt, &kept)
                                  : 65535u;
         if (lane == 0) {
             s_rank[0] = rmax;
             s_rank[1] = rk;
+            s_kept = kept;   // tokens at or above the top-k threshold
         }
     }
     __syncthreads();
@@ -547,6 +564,7 @@ __global__ __launch_bounds__(1024) void k_filter_tau16(FilterArgs a) {
         if (exm < P && inm >= P) {
             s_thr[2] = tid;
             s_above_m = exm;
+            s_above_c = ex;
         }
         __syncthreads();
         int tp = s_thr[2];
@@ -560,15 +578,81 @@ __global__ __launch_bounds__(1024) void k_filter_tau16(FilterArgs a) {
             above = 0.0;
         }
         if (wid == 0) {
+            double cm;
             const uint32_t rp = resolve_rank<double>(tp, above, P, lane, [&](uint32_t r) {
                 return mass(r, hist_count(hist, rank_bits(r)));
-            });
-            if (lane == 0) s_rank[2] = rp;
+            }, &cm);
+            // tokens at or above the top-p threshold (rp <= rk: masses stop at rk); unknown
+            // when rounding left the total short
+            const uint32_t base_r = rp & ~63u;
+            const uint32_t kp = wave_prefix_at(hist_count(hist, rank_bits(base_r + lane)), lane,
+                                               (int)(rp - base_r));
+            if (lane == 0) {
+                s_rank[2] = rp;
+                s_kept = s_thr[2] >= 0 ? s_above_c + kp : 0xFFFFFFFFu;
+            }
         }
         __syncthreads();
         tau = fmaxf(tau, bits_value<DT>(rank_bits(s_rank[2])));
     }
     if (tid == 0) a.tau[b] = tau;
+    if (a.done == nullptr) return;
+
+    // ---- a row that keeps few tokens is drawn here: its kept count comes from the selection
+    // scans (the count down to tau's rank), a second pass gathers the kept tokens into LDS, and every
+    // (token, draw) pair is scored exactly, x / T + G(word) [GMX, Background], with the
+    // sampler's words, arithmetic and keys; the draw's key is an LDS atomic maximum ----
+    const uint32_t nk = s_kept;
+    const int K = a.K;
+    if (!(nk <= (uint32_t)kSparseKept && K <= kSparseKept &&
+          (int64_t)nk * K <= kSparsePairs))
+        return;
+    uint32_t *l_idx = hist;                                                  // [kSparseKept]
+    float *l_x = reinterpret_cast<float *>(hist + kSparseKept);              // [kSparseKept]
+    uint64_t *l_key = reinterpret_cast<uint64_t *>(hist + 2 * kSparseKept);  // [kSparseKept]
+    __shared__ uint32_t s_n;
+    if (tid == 0) s_n = 0u;
+    for (int j = tid; j < K; j += 1024) l_key[j] = 0ull;
+    __syncthreads();
+    for_each_vec<DT>(rowp, nvec, a.V, a.aligned, [&](const uint4 &v, int64_t gv) {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+            const float x = elem<DT>(v, e);
+            if (x >= tau && x > -__builtin_inff()) {
+                const uint32_t pos = atomicAdd(&s_n, 1u);
+                if (pos < (uint32_t)kSparseKept) {
+                    l_idx[pos] = (uint32_t)(gv * EPV + e);
+                    l_x[pos] = x;
+                }
+            }
+        }
+    });
+    __syncthreads();
+    const uint32_t n = min(s_n, (uint32_t)kSparseKept);
+    const uint64_t seed = a.seed[b];
+    const uint64_t off0 = a.offset[b];
+    const float invT = 1.0f / f.T;
+    const uint32_t npairs = n * (uint32_t)K;
+    for (uint32_t q = (uint32_t)tid; q < npairs; q += 1024u) {
+        const uint32_t k = q / n, e = q - k * n;
+        const uint32_t i = l_idx[e];
+        const uint64_t off = off0 + (uint64_t)k;
+        const Words4 w = philox4x32_10_uk(i >> 2, (uint32_t)b, (uint32_t)off,
+                                          (uint32_t)(off >> 32), (uint32_t)seed,
+                                          (uint32_t)(seed >> 32));
+        const uint32_t r = (i & 2u) ? ((i & 1u) ? w.w[3] : w.w[2])
+                                    : ((i & 1u) ? w.w[1] : w.w[0]);
+        const float sc = l_x[e] * invT + gumbel32(r);
+        atomicMax(reinterpret_cast<unsigned long long *>(&l_key[k]),
+                  (unsigned long long)make_key(sc, i));
+    }
+    __syncthreads();
+    for (int k = tid; k < K; k += 1024) {
+        const uint64_t kk = l_key[k];
+        a.out[b * K + k] = key_index(kk);
+        if (a.best_out) a.best_out[b * K + k] = key_score(kk);
+    }
+    if (tid == 0) a.done[b] = 1u;
 }
 
 }  // namespace

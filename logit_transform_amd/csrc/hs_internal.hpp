@@ -58,6 +58,7 @@ struct SampleArgs {
     int32_t exchange;
     int32_t spins;                // polls before a block works a missing partial out itself
     uint32_t *flags;              // [B * part_stride]: chunk partial published
+    const uint32_t *done;         // [B] rows the threshold kernel has drawn (filters), else null
 };
 
 struct RowOpArgs {
@@ -83,7 +84,19 @@ struct FilterArgs {
     const int32_t *top_k;   // [B] or null (0: no top-k)
     const float *top_p;     // [B] or null (1: no top-p)
     float *tau;             // [B]
+    // Drawing rows that keep few tokens in the threshold kernel (16-bit logits); done null:
+    // thresholds only. done[b] = 1 marks a row drawn there (out / best_out written), 0 a row
+    // left to the sampler.
+    uint32_t *done;         // [B]
+    int32_t *out;           // [B * K]
+    float *best_out;        // [B * K] or null
+    const uint64_t *seed;
+    const uint64_t *offset;
+    int32_t K;
 };
+// The largest kept set, draw count and (kept tokens x draws) the threshold kernel draws itself.
+constexpr int kSparseKept = 2048;
+constexpr int kSparsePairs = 65536;
 hipError_t launch_filter_tau(int dt, const FilterArgs &a, int grid, hipStream_t s);
 
 // piv: the curve's pivot, 0 given per row, 1 top-anchored, 2 entropy-anchored, 3 set per row

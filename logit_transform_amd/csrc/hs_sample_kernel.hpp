@@ -227,6 +227,8 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     const int64_t b = __builtin_amdgcn_readfirstlane(bid / a.nkg);
     const int k0 = kg * a.kpg;
     const int k1 = min(a.K, k0 + a.kpg);
+    // a filtered row whose few kept tokens the threshold kernel has drawn already
+    if (a.done != nullptr && a.done[b] != 0u) return;
 
     // ---- row parameters (wave-uniform) ----
     const float T = a.T[b];

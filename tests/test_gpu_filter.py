@@ -118,6 +118,60 @@ def test_filters_on_heavily_tied_rows(hs, oracle_mod, dtype):
     _check_rows(hs, oracle_mod, w, k2, p2, "tied rows (2) %s" % dtype)
 
 
+def _row_marks(hs, ws, B, V, K, dtype):
+    """The per-row marks of rows the threshold kernel drew itself: the workspace's last region
+    (B int32, 256-byte aligned)."""
+    n = hs.workspace_bytes(B, V, K, dtype, False)
+    off = n - (B * 4 + 255) // 256 * 256
+    return ws[off:off + 4 * B].view(torch.int32).cpu().numpy()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_fused_draws_match_the_sampler(hs, oracle_mod, dtype):
+    """Rows that keep few tokens are drawn by the threshold kernel (automatic plan); the
+    sampling kernel on every row (an explicit variant) gives the same ids and scores."""
+    B, V, K = 8, 60001, 7
+    w = W.generic(B, V, dtype, seed=77, scale=1.5, mask_frac=0.05, K=K)
+    k = np.array([1, 5, 50, 2048, 2049, 0, 100, 1000], dtype=np.int32)
+    p = np.array([1.0, 1.0, 0.9, 1.0, 1.0, 0.3, 0.5, 1.0], dtype=np.float32)
+    d = on_device(w)
+    kt, pt = torch.from_numpy(k).cuda(), torch.from_numpy(p).cuda()
+    ws = hs.workspace(B, V, K, dtype, False)
+    g, bs = hs.sample_filtered(d["logits"], d["T"], d["seed"], d["offset"], top_k=kt, top_p=pt,
+                               k=K, ws=ws, want_best=True)
+    marks = _row_marks(hs, ws, B, V, K, dtype)
+    assert marks[0] == 1 and marks[1] == 1 and marks[2] == 1, marks   # a few dozen kept tokens
+    assert marks[4] == 0, marks                                         # over 2048 kept
+    r, rb = hs.sample_filtered(d["logits"], d["T"], d["seed"], d["offset"], top_k=kt,
+                               top_p=pt, k=K, opts=hs.SampleOpts(variant=1), want_best=True)
+    np.testing.assert_array_equal(g.cpu().numpy(), r.cpu().numpy())
+    np.testing.assert_array_equal(bs.cpu().numpy(), rb.cpu().numpy())
+    _check_rows(hs, oracle_mod, w, k, p, "fused %s" % dtype)
+
+
+def test_fused_draw_limits(hs, oracle_mod):
+    """(kept tokens) x draws at the limit (32 x 2048 = 65536: drawn in the threshold kernel)
+    and just past it (33 x 2048: left to the sampler); the same ids either way."""
+    B, V, K = 2, 4096, 2048
+    w = W.generic(B, V, torch.bfloat16, seed=79, scale=1.0, K=K)
+    x = w.logits.float().numpy().copy()
+    for r in range(B):
+        x[r, np.random.default_rng(r).choice(V, 40, replace=False)] = 10.0 + 0.25 * np.arange(40)
+    w.logits = torch.from_numpy(x).to(torch.bfloat16)
+    d = on_device(w)
+    for kk, fused in ((32, 1), (33, 0)):
+        k = np.full(B, kk, dtype=np.int32)
+        ws = hs.workspace(B, V, K, torch.bfloat16, False)
+        g = hs.sample_filtered(d["logits"], d["T"], d["seed"], d["offset"],
+                               top_k=torch.from_numpy(k).cuda(), k=K, ws=ws)
+        assert (_row_marks(hs, ws, B, V, K, torch.bfloat16) == fused).all()
+        r = hs.sample_filtered(d["logits"], d["T"], d["seed"], d["offset"],
+                               top_k=torch.from_numpy(k).cuda(), k=K,
+                               opts=hs.SampleOpts(variant=1))
+        np.testing.assert_array_equal(g.cpu().numpy(), r.cpu().numpy())
+        _check_rows(hs, oracle_mod, w, k, np.ones(B, dtype=np.float32), "limit k=%d" % kk)
+
+
 def test_special_rows_and_closed_cases(hs):
     V = 500
     rng = np.random.default_rng(41)
