@@ -218,10 +218,11 @@ int hs_filter_threshold(const hs_logits *x, const float *T, const int32_t *top_k
  * [GMX, Background]. A row with an invalid T or top_p gives -2; greedy rows (T == 0) are the
  * argmax of x. A workspace of hs_workspace_bytes(B, V, K, dtype, 0) bytes is required (the
  * thresholds live in it). best and opts as hs_sample_ex (NULL allowed). With the automatic
- * plan (opts NULL or variant 0), a row of 16-bit logits that keeps at most 2048 tokens, with
- * K <= 2048 and (kept tokens) * K <= 65536, is drawn by the threshold kernel itself, which
- * scores only the kept tokens; an explicit variant runs the sampling kernel on every row. Both
- * give the same ids and scores. */
+ * plan (opts NULL or variant 0), a row known to keep at most 2048 tokens (16-bit logits: the
+ * kept count; fp32: the tokens at or above the top-k threshold, or the finite count without
+ * top-k), with K <= 2048 and that count times K <= 65536, is drawn by the threshold kernel
+ * itself, which scores only the kept tokens; an explicit variant runs the sampling kernel on
+ * every row. Both give the same ids and scores. */
 int hs_sample_filtered(const hs_logits *x, const float *T, const int32_t *top_k,
                        const float *top_p, const uint64_t *seed, const uint64_t *offset,
                        int32_t K, int32_t *out, float *best, void *ws, size_t ws_bytes,

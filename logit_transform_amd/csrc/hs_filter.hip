@@ -240,9 +240,18 @@ __device__ __forceinline__ bool row_filter(const FilterArgs &a, int64_t b, RowFi
 }
 
 // The radix selection of tau (every dtype) with the LDS histograms hc [2048] and hm [2048].
+// tau, and an upper bound on the tokens at or above it (the count at or above the top-k
+// threshold, ties included, or the finite count); the same in every thread.
+struct TauKept {
+    float tau;
+    uint32_t kept;
+};
 template <int DT>
-__device__ float tau_radix(const FilterArgs &a, int64_t b, const RowFilter &f, uint32_t *hc,
-                           double *hm, float *red_f, uint32_t *red_n) {
+__device__ __forceinline__ TauKept tau_radix(const FilterArgs &a, int64_t b, const RowFilter &f,
+                                             uint32_t *hc, double *hm, float *red_f,
+                                             uint32_t *red_n) {
+    uint32_t kept_v = 0u;
+    uint32_t *kept = &kept_v;
     using tr = dtype_traits<DT>;
     using D = Digits<DT>;
     constexpr int EPV = tr::epv;
@@ -279,6 +288,16 @@ __device__ float tau_radix(const FilterArgs &a, int64_t b, const RowFilter &f, u
                                              [](float) { return 1u; }, lane, wid);
             keyk = prefix;
             tau = key_value<DT>(keyk);
+            // keys above tau's (k less the rank left inside its bin) plus tau's own count
+            __shared__ uint32_t s_kept_r;
+            if (tid == 0) {
+                constexpr int NBL = 1 << D::bits[D::n - 1];
+                s_kept_r = (uint32_t)k - tgt + hc[prefix & (uint32_t)(NBL - 1)];
+            }
+            __syncthreads();
+            *kept = s_kept_r;
+        } else {
+            *kept = NF;
         }
     } else {
         uint32_t nf = 0u;
@@ -293,8 +312,9 @@ __device__ float tau_radix(const FilterArgs &a, int64_t b, const RowFilter &f, u
         });
         M = block_max(mx, red_f);
         NF = block_sum_u32(nf, red_n);
+        *kept = NF;
     }
-    if (NF == 0u) return -__builtin_inff();
+    if (NF == 0u) return TauKept{-__builtin_inff(), 0u};
 
     // top-p over the tokens top-k keeps: the key at which the tempered mass from the top
     // reaches p times their total
@@ -339,21 +359,9 @@ __device__ float tau_radix(const FilterArgs &a, int64_t b, const RowFilter &f, u
                                          mass, lane, wid);
         tau = fmaxf(tau, key_value<DT>(prefix));
     }
-    return tau;
+    return TauKept{tau, kept_v};
 }
 
-template <int DT>
-__global__ __launch_bounds__(1024) void k_filter_tau(FilterArgs a) {
-    __shared__ uint32_t hc[2048];
-    __shared__ double hm[2048];
-    __shared__ float red_f[16];
-    __shared__ uint32_t red_n[16];
-    if (a.done != nullptr && threadIdx.x == 0) a.done[blockIdx.x] = 0u;   // left to the sampler
-    RowFilter f;
-    if (!row_filter(a, blockIdx.x, &f)) return;
-    const float tau = tau_radix<DT>(a, blockIdx.x, f, hc, hm, red_f, red_n);
-    if (threadIdx.x == 0) a.tau[blockIdx.x] = tau;
-}
 
 // ---- 16-bit logits: one exact-value histogram per row ---------------------------------------
 // A 16-bit logit takes one of 65536 bit patterns, so one pass can count every distinct value
@@ -445,6 +453,95 @@ __device__ __forceinline__ uint32_t wave_prefix_at(uint32_t v, int lane, int l) 
     return __shfl(v, l, 64);
 }
 
+// The draw of a row that keeps few tokens, in the threshold kernel: when at most kSparseKept
+// tokens are kept (nk, an upper bound), with K <= kSparseKept and nk * K <= kSparsePairs, a
+// second pass over the row gathers the kept tokens (x >= tau) into LDS, and every (token, draw)
+// pair is scored exactly, x / T + G(word) [GMX, Background], with the sampling kernel's Philox
+// words, arithmetic and keys; an LDS atomic maximum per draw picks the winner. Returns whether
+// the row was drawn (then out / best_out hold its draws). lds: 8192 words, 8-byte aligned,
+// free for this use.
+template <int DT>
+__device__ __forceinline__ bool draw_kept(const FilterArgs &a, int64_t b, float T, float tau,
+                                          uint32_t nk, const char *rowp, int64_t nvec,
+                                          uint32_t *lds) {
+    constexpr int EPV = dtype_traits<DT>::epv;
+    const int tid = threadIdx.x;
+    const int K = a.K;
+    if (!(nk <= (uint32_t)kSparseKept && K <= kSparseKept && (int64_t)nk * K <= kSparsePairs))
+        return false;
+    __syncthreads();   // lds may still be read by the selection
+    uint32_t *l_idx = lds;                                                  // [kSparseKept]
+    float *l_x = reinterpret_cast<float *>(lds + kSparseKept);              // [kSparseKept]
+    uint64_t *l_key = reinterpret_cast<uint64_t *>(lds + 2 * kSparseKept);  // [kSparseKept]
+    __shared__ uint32_t s_n;
+    if (tid == 0) s_n = 0u;
+    for (int j = tid; j < K; j += 1024) l_key[j] = 0ull;
+    __syncthreads();
+    for_each_vec<DT>(rowp, nvec, a.V, a.aligned, [&](const uint4 &v, int64_t gv) {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+            const float x = elem<DT>(v, e);
+            if (x >= tau && x > -__builtin_inff()) {
+                const uint32_t pos = atomicAdd(&s_n, 1u);
+                if (pos < (uint32_t)kSparseKept) {
+                    l_idx[pos] = (uint32_t)(gv * EPV + e);
+                    l_x[pos] = x;
+                }
+            }
+        }
+    });
+    __syncthreads();
+    const uint32_t n = min(s_n, (uint32_t)kSparseKept);
+    const uint64_t seed = a.seed[b];
+    const uint64_t off0 = a.offset[b];
+    const float invT = 1.0f / T;
+    const uint32_t npairs = n * (uint32_t)K;
+    for (uint32_t q = (uint32_t)tid; q < npairs; q += 1024u) {
+        const uint32_t k = q / n, e = q - k * n;
+        const uint32_t i = l_idx[e];
+        const uint64_t off = off0 + (uint64_t)k;
+        const Words4 w = philox4x32_10_uk(i >> 2, (uint32_t)b, (uint32_t)off,
+                                          (uint32_t)(off >> 32), (uint32_t)seed,
+                                          (uint32_t)(seed >> 32));
+        const uint32_t r = (i & 2u) ? ((i & 1u) ? w.w[3] : w.w[2])
+                                    : ((i & 1u) ? w.w[1] : w.w[0]);
+        const float sc = l_x[e] * invT + gumbel32(r);
+        atomicMax(reinterpret_cast<unsigned long long *>(&l_key[k]),
+                  (unsigned long long)make_key(sc, i));
+    }
+    __syncthreads();
+    for (int k = tid; k < K; k += 1024) {
+        const uint64_t kk = l_key[k];
+        a.out[b * K + k] = key_index(kk);
+        if (a.best_out) a.best_out[b * K + k] = key_score(kk);
+    }
+    return true;
+}
+
+template <int DT>
+__global__ __launch_bounds__(1024) void k_filter_tau(FilterArgs a) {
+    __shared__ uint32_t hc[2048];
+    __shared__ double hm[2048];
+    __shared__ float red_f[16];
+    __shared__ uint32_t red_n[16];
+    __shared__ uint4 s_draw[2048];   // the draw of a small kept set
+    const int64_t b = blockIdx.x;
+    if (a.done != nullptr && threadIdx.x == 0) a.done[b] = 0u;   // set below if drawn here
+    RowFilter f;
+    if (!row_filter(a, b, &f)) return;
+    const TauKept r = tau_radix<DT>(a, b, f, hc, hm, red_f, red_n);
+    const float tau = r.tau;
+    const uint32_t kept = r.kept;
+    if (threadIdx.x == 0) a.tau[b] = tau;
+    if (a.done == nullptr) return;
+    constexpr int EPV = dtype_traits<DT>::epv;
+    const char *rowp = reinterpret_cast<const char *>(a.data) + b * a.ld * dtype_traits<DT>::esize;
+    if (draw_kept<DT>(a, b, f.T, tau, kept, rowp, (a.V + EPV - 1) / EPV,
+                      reinterpret_cast<uint32_t *>(s_draw))) {
+        if (threadIdx.x == 0) a.done[b] = 1u;
+    }
+}
+
 template <int DT>
 __global__ __launch_bounds__(1024) void k_filter_tau16(FilterArgs a) {
     using tr = dtype_traits<DT>;
@@ -503,9 +600,14 @@ __global__ __launch_bounds__(1024) void k_filter_tau16(FilterArgs a) {
     uint32_t ex, in, total;
     block_scan(own, red_u, &ex, &in, &total);
     if (total != NF) {   // a counter overflowed: select by radix levels (LDS reused)
-        const float tau = tau_radix<DT>(a, b, f, hist, reinterpret_cast<double *>(hist + 2048),
+        const TauKept r = tau_radix<DT>(a, b, f, hist, reinterpret_cast<double *>(hist + 2048),
                                         red_f, red_u);
+        const float tau = r.tau;
+        const uint32_t kept = r.kept;
         if (tid == 0) a.tau[b] = tau;
+        if (a.done != nullptr && draw_kept<DT>(a, b, f.T, tau, kept, rowp, nvec, hist)) {
+            if (tid == 0) a.done[b] = 1u;
+        }
         return;
     }
     if (NF == 0u) {
@@ -598,61 +700,11 @@ __global__ __launch_bounds__(1024) void k_filter_tau16(FilterArgs a) {
     if (tid == 0) a.tau[b] = tau;
     if (a.done == nullptr) return;
 
-    // ---- a row that keeps few tokens is drawn here: its kept count comes from the selection
-    // scans (the count down to tau's rank), a second pass gathers the kept tokens into LDS, and every
-    // (token, draw) pair is scored exactly, x / T + G(word) [GMX, Background], with the
-    // sampler's words, arithmetic and keys; the draw's key is an LDS atomic maximum ----
-    const uint32_t nk = s_kept;
-    const int K = a.K;
-    if (!(nk <= (uint32_t)kSparseKept && K <= kSparseKept &&
-          (int64_t)nk * K <= kSparsePairs))
-        return;
-    uint32_t *l_idx = hist;                                                  // [kSparseKept]
-    float *l_x = reinterpret_cast<float *>(hist + kSparseKept);              // [kSparseKept]
-    uint64_t *l_key = reinterpret_cast<uint64_t *>(hist + 2 * kSparseKept);  // [kSparseKept]
-    __shared__ uint32_t s_n;
-    if (tid == 0) s_n = 0u;
-    for (int j = tid; j < K; j += 1024) l_key[j] = 0ull;
-    __syncthreads();
-    for_each_vec<DT>(rowp, nvec, a.V, a.aligned, [&](const uint4 &v, int64_t gv) {
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-            const float x = elem<DT>(v, e);
-            if (x >= tau && x > -__builtin_inff()) {
-                const uint32_t pos = atomicAdd(&s_n, 1u);
-                if (pos < (uint32_t)kSparseKept) {
-                    l_idx[pos] = (uint32_t)(gv * EPV + e);
-                    l_x[pos] = x;
-                }
-            }
-        }
-    });
-    __syncthreads();
-    const uint32_t n = min(s_n, (uint32_t)kSparseKept);
-    const uint64_t seed = a.seed[b];
-    const uint64_t off0 = a.offset[b];
-    const float invT = 1.0f / f.T;
-    const uint32_t npairs = n * (uint32_t)K;
-    for (uint32_t q = (uint32_t)tid; q < npairs; q += 1024u) {
-        const uint32_t k = q / n, e = q - k * n;
-        const uint32_t i = l_idx[e];
-        const uint64_t off = off0 + (uint64_t)k;
-        const Words4 w = philox4x32_10_uk(i >> 2, (uint32_t)b, (uint32_t)off,
-                                          (uint32_t)(off >> 32), (uint32_t)seed,
-                                          (uint32_t)(seed >> 32));
-        const uint32_t r = (i & 2u) ? ((i & 1u) ? w.w[3] : w.w[2])
-                                    : ((i & 1u) ? w.w[1] : w.w[0]);
-        const float sc = l_x[e] * invT + gumbel32(r);
-        atomicMax(reinterpret_cast<unsigned long long *>(&l_key[k]),
-                  (unsigned long long)make_key(sc, i));
+    // ---- a row that keeps few tokens is drawn here (its kept count comes from the selection
+    // scans: the count down to tau's rank) ----
+    if (draw_kept<DT>(a, b, f.T, tau, s_kept, rowp, nvec, hist)) {
+        if (tid == 0) a.done[b] = 1u;
     }
-    __syncthreads();
-    for (int k = tid; k < K; k += 1024) {
-        const uint64_t kk = l_key[k];
-        a.out[b * K + k] = key_index(kk);
-        if (a.best_out) a.best_out[b * K + k] = key_score(kk);
-    }
-    if (tid == 0) a.done[b] = 1u;
 }
 
 }  // namespace

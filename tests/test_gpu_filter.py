@@ -126,7 +126,7 @@ def _row_marks(hs, ws, B, V, K, dtype):
     return ws[off:off + 4 * B].view(torch.int32).cpu().numpy()
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
 def test_fused_draws_match_the_sampler(hs, oracle_mod, dtype):
     """Rows that keep few tokens are drawn by the threshold kernel (automatic plan); the
     sampling kernel on every row (an explicit variant) gives the same ids and scores."""
@@ -149,22 +149,23 @@ def test_fused_draws_match_the_sampler(hs, oracle_mod, dtype):
     _check_rows(hs, oracle_mod, w, k, p, "fused %s" % dtype)
 
 
-def test_fused_draw_limits(hs, oracle_mod):
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_fused_draw_limits(hs, oracle_mod, dtype):
     """(kept tokens) x draws at the limit (32 x 2048 = 65536: drawn in the threshold kernel)
     and just past it (33 x 2048: left to the sampler); the same ids either way."""
     B, V, K = 2, 4096, 2048
-    w = W.generic(B, V, torch.bfloat16, seed=79, scale=1.0, K=K)
+    w = W.generic(B, V, dtype, seed=79, scale=1.0, K=K)
     x = w.logits.float().numpy().copy()
     for r in range(B):
         x[r, np.random.default_rng(r).choice(V, 40, replace=False)] = 10.0 + 0.25 * np.arange(40)
-    w.logits = torch.from_numpy(x).to(torch.bfloat16)
+    w.logits = torch.from_numpy(x).to(dtype)
     d = on_device(w)
     for kk, fused in ((32, 1), (33, 0)):
         k = np.full(B, kk, dtype=np.int32)
-        ws = hs.workspace(B, V, K, torch.bfloat16, False)
+        ws = hs.workspace(B, V, K, dtype, False)
         g = hs.sample_filtered(d["logits"], d["T"], d["seed"], d["offset"],
                                top_k=torch.from_numpy(k).cuda(), k=K, ws=ws)
-        assert (_row_marks(hs, ws, B, V, K, torch.bfloat16) == fused).all()
+        assert (_row_marks(hs, ws, B, V, K, dtype) == fused).all()
         r = hs.sample_filtered(d["logits"], d["T"], d["seed"], d["offset"],
                                top_k=torch.from_numpy(k).cuda(), k=K,
                                opts=hs.SampleOpts(variant=1))
@@ -172,16 +173,20 @@ def test_fused_draw_limits(hs, oracle_mod):
         _check_rows(hs, oracle_mod, w, k, np.ones(B, dtype=np.float32), "limit k=%d" % kk)
 
 
-def test_special_rows_and_closed_cases(hs):
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_special_rows_and_closed_cases(hs, dtype):
+    """fp32 rows take the radix selection and the sampler; bf16 rows the histogram and, where
+    few tokens are kept, the threshold kernel's own draw."""
     V = 500
     rng = np.random.default_rng(41)
     x = rng.normal(0, 1, size=(8, V)).astype(np.float32)
+    x = torch.from_numpy(x).to(dtype).float().numpy()   # values exact in both dtypes
     x[0, :] = -np.inf                                   # no finite logit: -1
     x[1, [7, 9]] = 6.0                                  # tied maximum
     T = np.array([1.0, 1.0, 0.7, 1.0, 1.0, -1.0, 0.0, 1.0], dtype=np.float32)
     k = np.array([3, 1, 1, 0, 0, 5, 2, V], dtype=np.int32)
     p = np.array([0.9, 1.0, 1.0, 0.0, np.nan, 0.5, 0.1, 1.0], dtype=np.float32)
-    t = torch.from_numpy(x).cuda()
+    t = torch.from_numpy(x).to(dtype).cuda()
     Tt = torch.from_numpy(T).cuda()
     seed = torch.arange(8, dtype=torch.int64, device="cuda") * 31 + 7
     off = torch.zeros(8, dtype=torch.int64, device="cuda")
