@@ -649,52 +649,119 @@ __global__ __launch_bounds__(1024) void k_filter_tau16(FilterArgs a) {
                                          (bits_value<DT>(rank_bits(r)) - M) * c1)
                        : 0.0;
         };
-        double own_m = 0.0;
-        if (64u * (uint32_t)tid <= rk) {
-            for (int j = 0; j < 32; ++j) {
-                const int wd = base + ((j + lane) & 31);
-                const uint32_t w = hist[wd];
-                if (w) {
-                    own_m += mass(bits_rank(2u * (uint32_t)wd), w & 0xFFFFu);
-                    own_m += mass(bits_rank(2u * (uint32_t)wd + 1u), w >> 16);
+        const uint32_t rmax = s_rank[0];
+        if (rk - rmax < 256u) {
+            // every kept value lies fewer than 256 ranks below the largest (top-k keeps few
+            // tokens): wave 0 alone scans ranks rmax .. rk, four consecutive ranks per lane
+            if (wid == 0) {
+                const uint32_t r0 = rmax + 4u * (uint32_t)lane;
+                uint32_t c[4];
+                double m[4];
+                double own = 0.0;
+                uint32_t ownc = 0u;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t r = r0 + (uint32_t)j;
+                    c[j] = r <= rk ? hist_count(hist, rank_bits(r)) : 0u;
+                    m[j] = mass(r, c[j]);
+                    own += m[j];
+                    ownc += c[j];
+                }
+                double in = own;
+                uint32_t inc = ownc;
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1) {
+                    const double o = __shfl_up(in, d, 64);
+                    const uint32_t oc = __shfl_up(inc, d, 64);
+                    if (lane >= d) {
+                        in += o;
+                        inc += oc;
+                    }
+                }
+                double exm = __shfl_up(in, 1, 64);
+                uint32_t exc = __shfl_up(inc, 1, 64);
+                if (lane == 0) {
+                    exm = 0.0;
+                    exc = 0u;
+                }
+                const double P = (double)f.p * __shfl(in, 63, 64);
+                // the crossing lane, or (a total that rounding left short) the last with mass
+                const uint64_t hit = __ballot(in >= P);
+                const uint64_t nz = __ballot(own > 0.0);
+                const int l = hit ? __builtin_ctzll(hit) : 63 - __builtin_clzll(nz | 1ull);
+                if (lane == l) {
+                    int jj = -1, last = 0;
+                    double run = exm;
+                    uint32_t cnt = exc, cnt_at = exc;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        run += m[j];
+                        cnt += c[j];
+                        if (m[j] > 0.0) last = j;
+                        if (jj < 0 && hit && run >= P) {
+                            jj = j;
+                            cnt_at = cnt;
+                        }
+                    }
+                    if (jj < 0) {
+                        jj = last;
+                        cnt_at = exc;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) cnt_at += j <= jj ? c[j] : 0u;
+                    }
+                    s_rank[2] = r0 + (uint32_t)jj;
+                    s_kept = cnt_at;
                 }
             }
-        }
-        double exm, inm, S;
-        block_scan(own_m, red_d, &exm, &inm, &S);
-        const double P = (double)f.p * S;
-        if (exm < P && inm >= P) {
-            s_thr[2] = tid;
-            s_above_m = exm;
-            s_above_c = ex;
-        }
-        __syncthreads();
-        int tp = s_thr[2];
-        double above = s_above_m;
-        if (tp < 0) {   // rounding left the total short of P: the last thread with kept mass
-            const uint64_t m = __ballot(own_m > 0.0);
-            if (lane == 0) red_u[wid] = m ? (uint32_t)(64 * wid + 63 - __builtin_clzll(m)) : 0u;
             __syncthreads();
-            tp = 0;
-            for (int w = 0; w < 16; ++w) tp = max(tp, (int)red_u[w]);
-            above = 0.0;
-        }
-        if (wid == 0) {
-            double cm;
-            const uint32_t rp = resolve_rank<double>(tp, above, P, lane, [&](uint32_t r) {
-                return mass(r, hist_count(hist, rank_bits(r)));
-            }, &cm);
-            // tokens at or above the top-p threshold (rp <= rk: masses stop at rk); unknown
-            // when rounding left the total short
-            const uint32_t base_r = rp & ~63u;
-            const uint32_t kp = wave_prefix_at(hist_count(hist, rank_bits(base_r + lane)), lane,
-                                               (int)(rp - base_r));
-            if (lane == 0) {
-                s_rank[2] = rp;
-                s_kept = s_thr[2] >= 0 ? s_above_c + kp : 0xFFFFFFFFu;
+        } else {
+            double own_m = 0.0;
+            if (64u * (uint32_t)tid <= rk) {
+                for (int j = 0; j < 32; ++j) {
+                    const int wd = base + ((j + lane) & 31);
+                    const uint32_t w = hist[wd];
+                    if (w) {
+                        own_m += mass(bits_rank(2u * (uint32_t)wd), w & 0xFFFFu);
+                        own_m += mass(bits_rank(2u * (uint32_t)wd + 1u), w >> 16);
+                    }
+                }
             }
+            double exm, inm, S;
+            block_scan(own_m, red_d, &exm, &inm, &S);
+            const double P = (double)f.p * S;
+            if (exm < P && inm >= P) {
+                s_thr[2] = tid;
+                s_above_m = exm;
+                s_above_c = ex;
+            }
+            __syncthreads();
+            int tp = s_thr[2];
+            double above = s_above_m;
+            if (tp < 0) {   // rounding left the total short of P: the last thread with kept mass
+                const uint64_t m = __ballot(own_m > 0.0);
+                if (lane == 0) red_u[wid] = m ? (uint32_t)(64 * wid + 63 - __builtin_clzll(m)) : 0u;
+                __syncthreads();
+                tp = 0;
+                for (int w = 0; w < 16; ++w) tp = max(tp, (int)red_u[w]);
+                above = 0.0;
+            }
+            if (wid == 0) {
+                double cm;
+                const uint32_t rp = resolve_rank<double>(tp, above, P, lane, [&](uint32_t r) {
+                    return mass(r, hist_count(hist, rank_bits(r)));
+                }, &cm);
+                // tokens at or above the top-p threshold (rp <= rk: masses stop at rk); unknown
+                // when rounding left the total short
+                const uint32_t base_r = rp & ~63u;
+                const uint32_t kp = wave_prefix_at(hist_count(hist, rank_bits(base_r + lane)), lane,
+                                                   (int)(rp - base_r));
+                if (lane == 0) {
+                    s_rank[2] = rp;
+                    s_kept = s_thr[2] >= 0 ? s_above_c + kp : 0xFFFFFFFFu;
+                }
+            }
+            __syncthreads();
         }
-        __syncthreads();
         tau = fmaxf(tau, bits_value<DT>(rank_bits(s_rank[2])));
     }
     if (tid == 0) a.tau[b] = tau;
