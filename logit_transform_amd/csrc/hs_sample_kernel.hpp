@@ -111,10 +111,36 @@ __device__ __forceinline__ float vec_max(const float (&x)[EPV]) {
 // combines them. The top anchor needs only the maximum, only the entropy anchor the third sum.
 // The same code gives the split pre-pass and the in-kernel exchange, so a chunk's partial does
 // not depend on which block computes it.
+// (wave 0) A chunk's log-sum-exp partial from its waves' (reference, sum, u) in base 2 and
+// their largest logits: (reference in nats, sum of 2^(x log2(e) - reference), u in nats, the
+// chunk's largest logit); (-inf, 0, 0, max) when the chunk has no finite logit.
+template <int PIV>
+__device__ __forceinline__ float4 waves_to_partial(const float *red_m, const float *red_s,
+                                                   const float *red_u, const float *red_x,
+                                                   int lane, int nw) {
+    constexpr bool ENT = PIV == 2 || PIV == 3;
+    const float xb = wave_max(lane < nw ? red_x[lane] : -__builtin_inff());
+    if constexpr (PIV == 1) {
+        return make_float4(-__builtin_inff(), 0.0f, 0.0f, xb);
+    } else {
+        const float pm = lane < nw ? red_m[lane] : -3.402823466e38f;
+        const float mb = wave_max(pm);
+        const float sb_ = lane < nw ? __builtin_amdgcn_exp2f(pm - mb) : 0.0f;
+        const float S = wave_sum(lane < nw ? red_s[lane] * sb_ : 0.0f);
+        const float U = ENT ? wave_sum(lane < nw && red_s[lane] > 0.0f
+                                           ? __builtin_fmaf(red_s[lane], pm - mb, red_u[lane]) * sb_
+                                           : 0.0f)
+                            : 0.0f;
+        const bool fin = S > 0.0f;
+        return make_float4(fin ? mb * kLn2 : -__builtin_inff(), fin ? S : 0.0f,
+                           fin ? U * kLn2 : 0.0f, xb);
+    }
+}
+
 template <int DT, int PIV>
 __device__ __forceinline__ void chunk_partial(const SampleArgs &a, int64_t b, int chunk,
                                               float *red_m, float *red_s, float *red_u,
-                                              float4 *dst) {
+                                              float *red_x, float4 *dst) {
     using tr = dtype_traits<DT>;
     constexpr int EPV = tr::epv;
     constexpr bool ENT = PIV == 2 || PIV == 3;   // the entropy anchor's sum is needed
@@ -122,11 +148,13 @@ __device__ __forceinline__ void chunk_partial(const SampleArgs &a, int64_t b, in
     const int64_t vend = min(a.nvec, v0 + a.cv);
     const char *rowp = reinterpret_cast<const char *>(a.data) + b * a.ld * tr::esize;
     float m = -3.402823466e38f, s = 0.0f, u = 0.0f;   // base 2: m a maximum of x log2(e)
+    float mx = -__builtin_inff();                       // the chunk's largest logit
     for (int64_t gv = v0 + threadIdx.x; gv < vend; gv += blockDim.x) {
         const uint4 v = load_vec<DT>(rowp, gv, a.V, a.aligned);
         float xv[EPV];
 #pragma unroll
         for (int e = 0; e < EPV; ++e) xv[e] = elem<DT>(v, e);
+        mx = fmaxf(mx, vec_max<EPV>(xv));
         const float mv = vec_max<EPV>(xv) * kLog2e;
         if constexpr (PIV == 1) {
             m = fmaxf(m, mv);
@@ -152,26 +180,17 @@ __device__ __forceinline__ void chunk_partial(const SampleArgs &a, int64_t b, in
     const float sc = __builtin_amdgcn_exp2f(m - mw);
     const float sw = wave_sum(s * sc);
     const float uw = ENT ? wave_sum(s > 0.0f ? __builtin_fmaf(s, m - mw, u) * sc : 0.0f) : 0.0f;
+    const float xw = wave_max(mx);
     if (lane == 0) {
         red_m[wid] = mw;
         red_s[wid] = sw;
         red_u[wid] = uw;
+        red_x[wid] = xw;
     }
     __syncthreads();
     if (wid == 0) {
-        const float pm = lane < nw ? red_m[lane] : -3.402823466e38f;
-        const float mb = wave_max(pm);
-        const float sb_ = lane < nw ? __builtin_amdgcn_exp2f(pm - mb) : 0.0f;
-        const float S = wave_sum(lane < nw ? red_s[lane] * sb_ : 0.0f);
-        const float U = ENT ? wave_sum(lane < nw && red_s[lane] > 0.0f
-                                           ? __builtin_fmaf(red_s[lane], pm - mb, red_u[lane]) * sb_
-                                           : 0.0f)
-                            : 0.0f;
-        if (lane == 0) {
-            const bool fin = (PIV == 1) ? (mb > -1.0e38f) : (S > 0.0f);
-            *dst = make_float4(fin ? mb * kLn2 : -__builtin_inff(), fin ? S : 0.0f,
-                               fin ? U * kLn2 : 0.0f, 0.0f);
-        }
+        const float4 r = waves_to_partial<PIV>(red_m, red_s, red_u, red_x, lane, nw);
+        if (lane == 0) *dst = r;
     }
 }
 
@@ -210,6 +229,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     // split rows with the partials exchanged in the kernel: every chunk's partial, and the
     // chunks whose partial did not arrive in time
     __shared__ float4 s_part[kMaxChunks];
+    __shared__ float red_xp[16];       // per wave: largest logit of a replayed chunk
     __shared__ uint64_t s_miss;
     __shared__ int s_last;
 
@@ -626,40 +646,102 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
         }
     };
 
-    if (screen) post_candidate(candidate(stream_k(k0), champ0, craw0, cw0));
-    {
-        const float xw = wave_max(xmax_lane);
+    // Per wave: the lanes' largest logit into rx, and (curve on) their log-sum-exp sums.
+    auto waves_combine = [&](float xm, float r, float s_, float u, float *rx) {
+        const float xw = wave_max(xm);
         float mw = 0.0f, sw = 0.0f, uw = 0.0f;
         if constexpr (LSE) {
             // each lane's sums moved to the wave's reference mw: s 2^(r - mw), and for the
             // entropy anchor (u + s (r - mw)) 2^(r - mw)
-            mw = wave_max(lse_r);
-            const float sc = __builtin_amdgcn_exp2f(lse_r - mw);
-            sw = wave_sum(lse_s * sc);
+            mw = wave_max(r);
+            const float sc = __builtin_amdgcn_exp2f(r - mw);
+            sw = wave_sum(s_ * sc);
             if constexpr (ENT)
-                uw = wave_sum(lse_s > 0.0f ? __builtin_fmaf(lse_s, lse_r - mw, lse_u) * sc : 0.0f);
+                uw = wave_sum(s_ > 0.0f ? __builtin_fmaf(s_, r - mw, u) * sc : 0.0f);
         }
         if (lane == 0) {
-            red_x[wid] = xw;
+            rx[wid] = xw;
             if constexpr (LSE) {
                 red_m[wid] = mw;
                 red_s[wid] = sw;
                 red_u[wid] = uw;
             }
         }
-    }
+    };
+    if (screen) post_candidate(candidate(stream_k(k0), champ0, craw0, cw0));
+    waves_combine(xmax_lane, lse_r, lse_s, lse_u, red_x);
     __syncthreads();
     // Split rows without the pre-pass (the host chooses this only when every block of the grid
-    // is resident at once): each block works out its own chunk's partial with the pre-pass's
-    // code (the chunk was just read and is in the caches) and publishes it; wave 0 collects the
-    // row's other partials, waiting a bounded time for each; any still missing then is worked
-    // out here with the same code, so the combined shift is the same whoever computes a
-    // partial. Partials and flags are only touched by agent-scope atomics: each block waits
-    // for its partial's stores to complete before it raises its flag.
+    // is resident at once): each block publishes its own chunk's partial, combined from the
+    // streaming pass's sums; wave 0 collects the row's other partials, waiting a bounded time
+    // for each; any still missing then is worked out here by replaying that chunk's pass (the
+    // same slots, order and arithmetic per lane), so the combined shift is the same whoever
+    // computes a partial. Partials and flags are only touched by agent-scope atomics: each
+    // block waits for its partial's stores to complete before it raises its flag.
     const float4 *parts = a.partials + b * a.part_stride;
     if constexpr (HLG) {
         if (a.nchunk > 1 && a.exchange) {
-            chunk_partial<DT, PIV>(a, b, chunk, red_m, red_s, red_u, &s_part[chunk]);
+            // chunk j's per-lane pass sums, replayed (see the streaming pass and its re-sum)
+            auto replay_partial = [&](int j) {
+                const int v0j = j * (int)a.cv;
+                const int vendj = (int)min(a.nvec, (int64_t)v0j + a.cv);
+                const int lvj = v0j + tid;
+                auto fetch_j = [&](int gv) -> uint4 {
+                    if (gv >= vendj) return ninf4;
+                    return load_vec<DT>(rowp, gv, a.V, ALIGNED);
+                };
+                float xm = -__builtin_inff(), r = 0.0f, s_ = 0.0f, u = 0.0f;
+#pragma unroll 1
+                for (int n = 0; n < NV; ++n) {
+                    const uint4 v = fetch_j(lvj + n * BS);
+                    float xv[EPV];
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) xv[e] = elem<DT>(v, e);
+                    const float m = vec_max<EPV>(xv);
+                    xm = max2f(xm, m);
+                    if constexpr (LSE) {
+                        if (n == 0) r = (m > -__builtin_inff()) ? m * kLog2e : 0.0f;
+#pragma unroll
+                        for (int e = 0; e < EPV; ++e) {
+                            const float t = __builtin_fmaf(xv[e], kLog2e, -r);
+                            const float pe = __builtin_amdgcn_exp2f(t);
+                            s_ += pe;
+                            if constexpr (ENT) u = (pe > 0.0f) ? __builtin_fmaf(pe, t, u) : u;
+                        }
+                    }
+                }
+                if constexpr (LSE) {
+                    const float tm = xm * kLog2e;
+                    if (xm > -__builtin_inff() && !(fabsf(tm - r) <= 100.0f)) {
+                        r = tm;
+                        s_ = 0.0f;
+                        u = 0.0f;
+#pragma unroll 1
+                        for (int n = 0; n < NV; ++n) {
+                            const uint4 v = fetch_j(lvj + n * BS);
+#pragma unroll
+                            for (int e = 0; e < EPV; ++e) {
+                                const float t = __builtin_fmaf(elem<DT>(v, e), kLog2e, -r);
+                                const float pe = __builtin_amdgcn_exp2f(t);
+                                s_ += pe;
+                                if constexpr (ENT)
+                                    u = (pe > 0.0f) ? __builtin_fmaf(pe, t, u) : u;
+                            }
+                        }
+                    }
+                }
+                waves_combine(xm, r, s_, u, red_xp);
+                __syncthreads();
+                if (wid == 0) {
+                    const float4 pr = waves_to_partial<PIV>(red_m, red_s, red_u, red_xp, lane, nw);
+                    if (lane == 0) s_part[j] = pr;
+                }
+                __syncthreads();
+            };
+            if (wid == 0) {
+                const float4 pr = waves_to_partial<PIV>(red_m, red_s, red_u, red_x, lane, nw);
+                if (lane == 0) s_part[chunk] = pr;
+            }
             __syncthreads();
             uint32_t *flags = a.flags + b * a.part_stride;
             if (tid == 0) {
@@ -668,6 +750,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                 __hip_atomic_store(dst + 0, __float_as_uint(mine.x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __hip_atomic_store(dst + 1, __float_as_uint(mine.y), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __hip_atomic_store(dst + 2, __float_as_uint(mine.z), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(dst + 3, __float_as_uint(mine.w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __atomic_signal_fence(__ATOMIC_SEQ_CST);
                 __builtin_amdgcn_s_waitcnt(0);
                 __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -689,7 +772,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                     v.x = __uint_as_float(__hip_atomic_load(src + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
                     v.y = __uint_as_float(__hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
                     v.z = __uint_as_float(__hip_atomic_load(src + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-                    v.w = 0.0f;
+                    v.w = __uint_as_float(__hip_atomic_load(src + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
                     s_part[lane] = v;
                 }
                 const uint64_t miss = __ballot(!have);
@@ -700,8 +783,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             while (miss) {
                 const int j = __builtin_ctzll(miss);
                 miss &= miss - 1ull;
-                chunk_partial<DT, PIV>(a, b, j, red_m, red_s, red_u, &s_part[j]);
-                __syncthreads();
+                replay_partial(j);
             }
             parts = s_part;
         }
@@ -717,7 +799,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             const int mode = PIV == 3 ? rpiv : PIV;
             if (mode == 1) {
                 c = (a.nchunk == 1 ? xmb
-                                   : wave_max(lane < a.nchunk ? parts[lane].x
+                                   : wave_max(lane < a.nchunk ? parts[lane].w
                                                               : -__builtin_inff())) - poff;
                 ok = c > -__builtin_inff();
             } else if (mode < 0) {
@@ -1013,10 +1095,11 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
 // The split pre-pass: one block per (row, chunk).
 template <int DT, int PIV>
 __global__ __launch_bounds__(1024) void k_lse_partial(SampleArgs a) {
-    __shared__ float red_m[16], red_s[16], red_u[16];
+    __shared__ float red_m[16], red_s[16], red_u[16], red_x[16];
     const int chunk = blockIdx.x % a.nchunk;
     const int64_t b = blockIdx.x / a.nchunk;
-    chunk_partial<DT, PIV>(a, b, chunk, red_m, red_s, red_u, &a.partials[b * a.part_stride + chunk]);
+    chunk_partial<DT, PIV>(a, b, chunk, red_m, red_s, red_u, red_x,
+                           &a.partials[b * a.part_stride + chunk]);
 }
 
 // ------------------------------------------------------------------------------------------
