@@ -157,14 +157,23 @@ int or_logsumexp(const double *x, int64_t n, int64_t V, int64_t ld, double *lse)
     return bad ? -1 : 0;
 }
 
+double or_filter_tau_row(const double *x, int64_t V, double t, int32_t k, double p, int *amb);
+
 /* The pivot mu of one row [HLG, The pivot], in log-prob nats, computed from the full
  * normalised log-prob vector l_i = x_i - LSE over the finite entries:
  *   mode 0 (given):   mu = mu_in;
  *   mode 1 (top):     mu = l_max - c, the curve centred c nats below the most probable token;
- *   mode 2 (entropy): mu = sum_i p_i l_i with p_i = exp(l_i), i.e. minus the entropy.
+ *   mode 2 (entropy): mu = sum_i p_i l_i with p_i = exp(l_i), i.e. minus the entropy;
+ *   mode 3 (median):  mu = the log-prob at which the probability mass, summed from the most
+ *                     probable token down over groups of equal logits, first reaches one half
+ *                     (the top-p boundary at p = 0.5 and T = 1: or_filter_tau_row).
  * lse is the row's log-sum-exp (finite: the row has a finite entry). */
 double or_row_pivot(const double *x, int64_t V, double lse, int mode, double c, double mu_in)
 {
+    if (mode == 3) {
+        int amb = 0;
+        return or_filter_tau_row(x, V, 1.0, 0, 0.5, &amb) - lse;
+    }
     if (mode == 1) {
         double lmax = -INFINITY;
         for (int64_t i = 0; i < V; ++i) {
@@ -191,7 +200,7 @@ double or_row_pivot(const double *x, int64_t V, double lse, int mode, double c, 
 int or_pivot(const double *x, int64_t n, int64_t V, int64_t ld, int mode, double c,
              const float *mu_in, double *mu_out)
 {
-    if (mode < 0 || mode > 2 || (mode == 1 && !isfinite(c))) return -2;
+    if (mode < 0 || mode > 3 || (mode == 1 && !isfinite(c))) return -2;
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
     for (int64_t r = 0; r < n; ++r) {
@@ -214,7 +223,7 @@ int or_hlg_transform(const double *x, int64_t n, int64_t V, int64_t ld, const fl
                      int64_t ldo)
 {
     if (!or_params_ok(m, w, bt, bh)) return -2;
-    if (pivot < 0 || pivot > 2 || (pivot == 1 && !isfinite(c))) return -2;
+    if (pivot < 0 || pivot > 3 || (pivot == 1 && !isfinite(c))) return -2;
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
     for (int64_t r = 0; r < n; ++r) {
@@ -256,7 +265,7 @@ int or_sample(const double *x, int64_t n, int64_t V, int64_t ld, const int64_t *
               int32_t *out, double *best, double *second)
 {
     if (hlg && !or_params_ok(m, w, bt, bh)) return -2;
-    if (hlg && (pivot < 0 || pivot > 2 || (pivot == 1 && !isfinite(c)))) return -2;
+    if (hlg && (pivot < 0 || pivot > 3 || (pivot == 1 && !isfinite(c)))) return -2;
     int bad = 0;
     for (int64_t r = 0; r < n; ++r)
         if (!or_row_ok(x + r * ld, V)) bad = 1;

@@ -133,8 +133,9 @@ def logsumexp(x) -> np.ndarray:
 
 
 # Pivot modes of the curve [HLG, The pivot]: the pivot given per row, top-anchored
-# (mu = l_max - c) or entropy-anchored (mu = sum p l).
-PIVOTS = {"input": 0, "top": 1, "entropy": 2}
+# (mu = l_max - c), entropy-anchored (mu = sum p l) or the mass median (the log-prob at which
+# the mass summed from the top first reaches one half).
+PIVOTS = {"input": 0, "top": 1, "entropy": 2, "median": 3}
 
 
 def _pivot_mode(p) -> int:
@@ -175,7 +176,8 @@ def sample(x, T, seed, offset, K: int = 1, mu=None, hlg=None, row_id=None):
     """Token ids [n, K] plus the best and second-best score of every draw.
 
     hlg: None (curve off) or a mapping/tuple (m, w, beta_t, beta_h); a mapping may also
-    carry "pivot" ("input", "top", "entropy") and "pivot_offset" (the c of the top mode).
+    carry "pivot" ("input", "top", "entropy", "median") and "pivot_offset" (the c of the top
+    mode).
     row_id: the global row index keying each row's Philox counter (default 0..n-1)."""
     x = _as_f64_rows(x)
     n, V = x.shape

@@ -84,7 +84,7 @@ def test_pivot_shift_invariant(oracle_mod, mode):
 def test_bad_pivot_arguments(oracle_mod):
     x = _rows()[:1]
     with pytest.raises(oracle_mod.OracleError):
-        oracle_mod.pivot(x, 3)
+        oracle_mod.pivot(x, 4)
     with pytest.raises(oracle_mod.OracleError):
         oracle_mod.pivot(x, "top", float("inf"))
     with pytest.raises(oracle_mod.OracleError):
@@ -92,7 +92,60 @@ def test_bad_pivot_arguments(oracle_mod):
                                                           pivot_offset=float("nan")))
 
 
-@pytest.mark.parametrize("mode", ["top", "entropy"])
+def _median_brute(x):
+    """The mass median of one row by sorting in float64: the log-prob of the first group of
+    equal logits (from the top) at which the probability mass reaches one half, and how far
+    the running total before and after that group lies from one half."""
+    fin = x[np.isfinite(x)]
+    lse = special.logsumexp(fin)
+    p = np.exp(fin - lse)
+    cum = 0.0
+    for v in np.unique(fin)[::-1]:
+        before = cum
+        cum += p[fin == v].sum()
+        if cum >= 0.5:
+            return v - lse, min(0.5 - before, cum - 0.5)
+    raise AssertionError("mass never reached one half")
+
+
+def test_median_pivot_closed_forms(oracle_mod):
+    # a flat row: every token is the median, mu = -log(n)
+    for n in (1, 7, 500):
+        mu = oracle_mod.pivot(np.full((1, n), 2.5), "median")[0]
+        assert abs(mu + math.log(n)) < 1e-12
+    # one token of logit 5 over n - 1 of logit 0: it alone holds e^5 / (e^5 + n - 1) of the
+    # mass, over one half for n = 100 (median at 5), under it for n = 1000 (median at 0)
+    for n, top in ((100, True), (1000, False)):
+        x = np.zeros((1, n))
+        x[0, 3] = 5.0
+        lse = math.log(math.exp(5.0) + (n - 1))
+        want = (5.0 if top else 0.0) - lse
+        assert abs(oracle_mod.pivot(x, "median")[0] - want) < 1e-12
+    # -0 and +0 are one logit; masked entries take no part
+    x = np.array([[0.0, -0.0, -np.inf, -3.0]])
+    lse = math.log(2.0 + math.exp(-3.0))
+    assert abs(oracle_mod.pivot(x, "median")[0] - (0.0 - lse)) < 1e-12
+
+
+def test_median_pivot_matches_sorting(oracle_mod):
+    rng = np.random.default_rng(67)
+    x = rng.normal(0, 1.5, size=(40, 300))
+    x[::3] = np.round(x[::3] * 2.0) / 2.0           # coarse grid: long runs of equal logits
+    x[1::4, ::5] = -np.inf
+    mu = oracle_mod.pivot(x, "median")
+    checked = 0
+    for r in range(x.shape[0]):
+        want, margin = _median_brute(x[r])
+        if margin < 1e-9:
+            continue
+        assert abs(mu[r] - want) < 1e-12, r
+        checked += 1
+    assert checked >= 35
+    # a row with no finite logit has no pivot
+    assert np.isnan(oracle_mod.pivot(np.full((1, 4), -np.inf), "median")[0])
+
+
+@pytest.mark.parametrize("mode", ["top", "entropy", "median"])
 def test_pivot_draws_match_brute_force(oracle_mod, mode):
     """The sampler with a pivot mode draws exactly what the independent pure-Python sampler
     draws given the mu of that mode (mu computed here with scipy, in float64)."""
@@ -109,7 +162,12 @@ def test_pivot_draws_match_brute_force(oracle_mod, mode):
     for b in range(B):
         fin = np.isfinite(x[b])
         ell = x[b][fin] - special.logsumexp(x[b][fin])
-        mu = ell.max() - c if mode == "top" else float(np.dot(np.exp(ell), ell))
+        if mode == "top":
+            mu = ell.max() - c
+        elif mode == "entropy":
+            mu = float(np.dot(np.exp(ell), ell))
+        else:
+            mu = _median_brute(x[b])[0]
         for k in range(K):
             off = (int(offset[b]) + k) % 2**64
             want = _py_draw(list(x[b]), b, float(T[b]), int(seed[b]), off,
