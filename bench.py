@@ -177,9 +177,10 @@ def main():
                     help="skip the streaming-read and Philox ceilings and the warm-cache run")
     ap.add_argument("--eager", action="store_true",
                     help="launch the timed steps one by one instead of replaying a HIP graph")
-    ap.add_argument("--pivot", choices=("input", "top", "entropy"), default="input",
+    ap.add_argument("--pivot", choices=("input", "top", "entropy", "median"), default="input",
                     help="the curve's pivot: given per row (default, the workload's mu), "
-                         "top-anchored or entropy-anchored, computed in the kernel")
+                         "top-anchored or entropy-anchored, computed in the kernel, or the "
+                         "mass median, from the threshold kernel")
     ap.add_argument("--pivot-offset", type=float, default=6.0,
                     help="c of the top anchor (nats below the most probable token)")
     ap.add_argument("--per-row", action="store_true",

@@ -58,8 +58,12 @@ typedef struct {
 typedef enum {
     HS_PIVOT_GIVEN = 0,   /* mu[b] passed in by the caller (log-prob nats)                 */
     HS_PIVOT_TOP = 1,     /* top-anchored: mu = l_max - pivot_offset, so z = x - (x_max - c) */
-    HS_PIVOT_ENTROPY = 2  /* entropy-anchored: mu = sum_i p_i l_i (minus the entropy), so
+    HS_PIVOT_ENTROPY = 2, /* entropy-anchored: mu = sum_i p_i l_i (minus the entropy), so
                              z = x - E_p[x], p = softmax(x)                                 */
+    HS_PIVOT_MEDIAN = 3   /* mass median: mu = the log-prob at which the mass of softmax(x),
+                             summed from the top over groups of equal logits, first reaches
+                             one half, so z = x - x_med. hs_sample / hs_sample_ex only (a
+                             workspace is required); HS_ERR_UNSUPPORTED elsewhere           */
 } hs_pivot;
 
 /* The curve knobs of [HLG, Knobs]: mid gain m > 0 (finite), mid half-width w >= 0 (+inf
@@ -121,7 +125,9 @@ int hs_gumbel_argmax(const hs_logits *x, const float *T, const uint64_t *seed,
  *   out[b*K + k] = argmax_i ( l'_i / T[b] + G(word(seed[b], b, i, offset[b] + k)) ).
  * With the curve on and hlg->pivot == HS_PIVOT_GIVEN, mu must be a device float[B] and a
  * row with a non-finite mu gives -2; the other pivot modes derive mu[b] from the row in the
- * kernel (hs_hlg_pivot) and ignore mu.
+ * kernel (hs_hlg_pivot) and ignore mu. HS_PIVOT_MEDIAN needs the workspace (ws NULL gives
+ * HS_ERR_WORKSPACE): a first kernel finds every row's mass median, the top-p boundary at
+ * p = 0.5 and T = 1 (as hs_filter_threshold).
  * T[b] == 0 is greedy on x (the curve is monotone, so it cannot change the argmax
  * [HLG, Greedy is untouched]). Everything else as hs_gumbel_argmax; the workspace size is
  * hs_workspace_bytes(B, V, K, dtype, hlg != NULL). */

@@ -68,7 +68,7 @@ class HlgRow(C.Structure):
 
 # Where the curve's pivot comes from: given per row (mu), top-anchored (mu = l_max - c),
 # entropy-anchored (mu = sum p l).
-PIVOTS = {"input": 0, "top": 1, "entropy": 2}
+PIVOTS = {"input": 0, "top": 1, "entropy": 2, "median": 3}
 
 
 def _pivot_mode(p) -> int:
@@ -285,7 +285,7 @@ def sample(logits: torch.Tensor, T, seed, offset, *, mu=None, hlg=None, k: int =
     """The sampling step: token ids [B, k] (int32) on logits' device, asynchronously on the
     current stream. hlg=None turns the curve off; otherwise hlg = (m, w, beta_t, beta_h
     [, pivot, pivot_offset]) or a mapping with those keys, and mu is the per-row pivot when
-    the pivot mode is "input" (the default; "top" and "entropy" derive it in the kernel). Rows give -1 when no logit is
+    the pivot mode is "input" (the default; "top", "entropy" and "median" derive it on the GPU). Rows give -1 when no logit is
     finite and -2 for an invalid temperature or pivot; T = 0 is greedy."""
     L = load()
     x = _logits_struct(logits)

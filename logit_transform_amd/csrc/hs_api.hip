@@ -37,7 +37,8 @@ int check_curve(const hs_hlg_params *p) {
     if (!(p->w >= 0.0f)) return HS_ERR_INVALID_ARG;   // +inf allowed (rolloff off)
     if (!(p->beta_t > 0.0f) || !isfinite(p->beta_t)) return HS_ERR_INVALID_ARG;
     if (!(p->beta_h > 0.0f) || !isfinite(p->beta_h)) return HS_ERR_INVALID_ARG;
-    if (p->pivot != HS_PIVOT_GIVEN && p->pivot != HS_PIVOT_TOP && p->pivot != HS_PIVOT_ENTROPY)
+    if (p->pivot != HS_PIVOT_GIVEN && p->pivot != HS_PIVOT_TOP &&
+        p->pivot != HS_PIVOT_ENTROPY && p->pivot != HS_PIVOT_MEDIAN)
         return HS_ERR_INVALID_ARG;
     if (p->pivot == HS_PIVOT_TOP && !isfinite(p->pivot_offset)) return HS_ERR_INVALID_ARG;
     return HS_OK;
@@ -228,7 +229,8 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
     a.aligned = rows_aligned(x) ? 1 : 0;
     a.no_screen = (opts && opts->no_screen) ? 1 : 0;
     a.T = T;
-    const int piv = rows ? 3 : hlg ? hlg->pivot : 0;
+    // internal pivot codes: 0 given, 1 top, 2 entropy, 3 per row, 4 mass median
+    const int piv = rows ? 3 : !hlg ? 0 : hlg->pivot == HS_PIVOT_MEDIAN ? 4 : hlg->pivot;
     a.mu = (piv == HS_PIVOT_GIVEN || piv == 3) ? mu : nullptr;
     a.row_curves = reinterpret_cast<const hs::RowCurve *>(rows);
     a.seed = seed;
@@ -275,7 +277,21 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
     // Split rows with the curve on: the chunks' log-sum-exp partials are exchanged inside the
     // sampling kernel when every block of the grid is resident at once (and one draw group per
     // row); otherwise a pre-pass computes them.
-    if (curve_on && P.nchunk > 1 && P.nkg == 1) {
+    // The mass median: the threshold kernel's top-p selection at p = 0.5, T = 1 gives every
+    // row's shift c before the sampling kernel runs (which then needs no log-sum-exp).
+    if (piv == 4) {
+        if (!ws_ok) return HS_ERR_WORKSPACE;   // the shifts live in it
+        hs::FilterArgs f{};
+        f.data = x->data;
+        f.ld = x->ld;
+        f.V = x->V;
+        f.aligned = a.aligned;
+        f.median = 1;
+        f.tau = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + L.tau);
+        if (hs::launch_filter_tau(x->dtype, f, (int)x->B, s) != hipSuccess) return HS_ERR_HIP;
+        a.shift = f.tau;
+    }
+    if (curve_on && P.nchunk > 1 && P.nkg == 1 && piv != 4) {
         const int mode = opts ? opts->split_lse : 0;
         if (mode == 2) {
             a.exchange = 1;
@@ -288,7 +304,7 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
         const int wait = opts ? opts->exchange_wait : 0;
         a.spins = wait < 0 ? 0 : wait > 0 ? wait : hs::kExchangeSpins;
     }
-    if (curve_on && P.nchunk > 1 && !a.exchange) {
+    if (curve_on && P.nchunk > 1 && !a.exchange && piv != 4) {
         const int bs = P.cv >= 4096 ? 1024 : 256;
         if (hs::launch_lse_partial(x->dtype, piv, a, bs, (int)(x->B * P.nchunk), s) != hipSuccess)
             return HS_ERR_HIP;
@@ -322,6 +338,7 @@ int hs_hlg_transform(const hs_logits *x, const float *mu, const hs_hlg_params *p
     if (rc) return rc;
     rc = check_curve(p);
     if (rc) return rc;
+    if (p->pivot == HS_PIVOT_MEDIAN) return HS_ERR_UNSUPPORTED;
     if ((p->pivot == HS_PIVOT_GIVEN && !mu) || !out || ldo < x->V) return HS_ERR_INVALID_ARG;
     hs::RowOpArgs a{};
     a.data = x->data;
@@ -344,6 +361,7 @@ int hs_hlg_pivot(const hs_logits *x, const float *mu, const hs_hlg_params *p, fl
     if (rc) return rc;
     rc = check_curve(p);
     if (rc) return rc;
+    if (p->pivot == HS_PIVOT_MEDIAN) return HS_ERR_UNSUPPORTED;
     if ((p->pivot == HS_PIVOT_GIVEN && !mu) || !mu_out) return HS_ERR_INVALID_ARG;
     hs::RowOpArgs a{};
     a.data = x->data;

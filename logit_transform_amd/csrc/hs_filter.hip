@@ -223,6 +223,12 @@ struct RowFilter {
 };
 
 __device__ __forceinline__ bool row_filter(const FilterArgs &a, int64_t b, RowFilter *f) {
+    if (a.median) {   // the mass median [HLG, The pivot]: the top-p boundary at p = 0.5, T = 1
+        f->T = 1.0f;
+        f->k = 0;
+        f->p = 0.5f;
+        return true;
+    }
     f->T = a.T[b];
     f->k = a.top_k ? a.top_k[b] : 0;
     if ((int64_t)f->k >= a.V) f->k = 0;   // a k of at least V keeps every token

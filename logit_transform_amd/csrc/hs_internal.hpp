@@ -59,6 +59,7 @@ struct SampleArgs {
     int32_t spins;                // polls before a block works a missing partial out itself
     uint32_t *flags;              // [B * part_stride]: chunk partial published
     const uint32_t *done;         // [B] rows the threshold kernel has drawn (filters), else null
+    const float *shift;           // [B] the curve's shift c per row (mass-median pivot), else null
 };
 
 struct RowOpArgs {
@@ -84,6 +85,9 @@ struct FilterArgs {
     const int32_t *top_k;   // [B] or null (0: no top-k)
     const float *top_p;     // [B] or null (1: no top-p)
     float *tau;             // [B]
+    // the mass median of every row instead (T = 1, top-p 0.5, no top-k; T, top_k and top_p
+    // unused): tau is the logit where the mass from the top first reaches one half
+    int32_t median;
     // Drawing rows that keep few tokens in the threshold kernel (16-bit logits); done null:
     // thresholds only. done[b] = 1 marks a row drawn there (out / best_out written), 0 a row
     // left to the sampler.
@@ -100,7 +104,7 @@ constexpr int kSparsePairs = 65536;
 hipError_t launch_filter_tau(int dt, const FilterArgs &a, int grid, hipStream_t s);
 
 // piv: the curve's pivot, 0 given per row, 1 top-anchored, 2 entropy-anchored, 3 set per row
-// (a.row_curves)
+// (a.row_curves), 4 the shift read per row (a.shift: the mass median)
 // occ: when not null, the kernel's resident blocks per CU are written there instead of a launch
 hipError_t launch_sample(int dt, bool hlg, int piv, const SampleArgs &a, int nv, int bs,
                          int grid, hipStream_t s, int *occ = nullptr);

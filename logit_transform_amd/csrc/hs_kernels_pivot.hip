@@ -15,12 +15,18 @@ namespace hs {
 hipError_t launch_sample_pivot(int dt, int piv, const SampleArgs &a, int nv, int bs, int grid,
                                hipStream_t s, int *occ) {
     switch (dt) {
-        case DT_F32: return piv == 1 ? launch_sample_al<DT_F32, true, 1>(a, nv, bs, grid, s, occ)
-                                     : launch_sample_al<DT_F32, true, 2>(a, nv, bs, grid, s, occ);
-        case DT_BF16: return piv == 1 ? launch_sample_al<DT_BF16, true, 1>(a, nv, bs, grid, s, occ)
-                                      : launch_sample_al<DT_BF16, true, 2>(a, nv, bs, grid, s, occ);
-        case DT_F16: return piv == 1 ? launch_sample_al<DT_F16, true, 1>(a, nv, bs, grid, s, occ)
-                                     : launch_sample_al<DT_F16, true, 2>(a, nv, bs, grid, s, occ);
+        case DT_F32:
+            return piv == 1 ? launch_sample_al<DT_F32, true, 1>(a, nv, bs, grid, s, occ)
+                 : piv == 4 ? launch_sample_al<DT_F32, true, 4>(a, nv, bs, grid, s, occ)
+                            : launch_sample_al<DT_F32, true, 2>(a, nv, bs, grid, s, occ);
+        case DT_BF16:
+            return piv == 1 ? launch_sample_al<DT_BF16, true, 1>(a, nv, bs, grid, s, occ)
+                 : piv == 4 ? launch_sample_al<DT_BF16, true, 4>(a, nv, bs, grid, s, occ)
+                            : launch_sample_al<DT_BF16, true, 2>(a, nv, bs, grid, s, occ);
+        case DT_F16:
+            return piv == 1 ? launch_sample_al<DT_F16, true, 1>(a, nv, bs, grid, s, occ)
+                 : piv == 4 ? launch_sample_al<DT_F16, true, 4>(a, nv, bs, grid, s, occ)
+                            : launch_sample_al<DT_F16, true, 2>(a, nv, bs, grid, s, occ);
     }
     return hipErrorInvalidValue;
 }

@@ -203,7 +203,7 @@ __device__ __forceinline__ void chunk_partial(const SampleArgs &a, int64_t b, in
 template <int DT, int NV, bool HLG, int PIV, int MAXBS, bool ALIGNED>
 __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     static_assert(HLG || PIV == 0, "a pivot needs the curve");
-    constexpr bool LSE = HLG && PIV != 1;   // the exponential sum is needed
+    constexpr bool LSE = HLG && PIV != 1 && PIV != 4;   // the exponential sum is needed
     constexpr bool ENT = PIV == 2 || PIV == 3;   // and the entropy anchor's sum
     using tr = dtype_traits<DT>;
     constexpr int EPV = tr::epv;
@@ -804,6 +804,11 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                 ok = c > -__builtin_inff();
             } else if (mode < 0) {
                 c = 0.0f;   // curve off for this row: identity curve, no shift
+            } else if (mode == 4) {
+                // the mass median, worked out per row before this kernel (NaN or -inf for a
+                // row with no finite logit)
+                c = a.shift[b];
+                ok = c > -__builtin_inff() && c < __builtin_inff();
             } else if constexpr (LSE) {
                 if (a.nchunk == 1) {
                     const float pm = lane < nw ? red_m[lane] : -3.402823466e38f;

@@ -97,13 +97,23 @@ def test_bad_sample_args(lib, kw):
 
 @pytest.mark.parametrize("h", [H(m=0.0), H(m=-1.0), H(m=math.inf), H(m=math.nan), H(w=-0.5),
                                H(w=math.nan), H(bt=0.0), H(bt=math.inf), H(bh=-1.0),
-                               H(bh=math.nan), H(pivot=3), H(pivot=-1),
+                               H(bh=math.nan), H(pivot=4), H(pivot=-1),
                                H(pivot=1, off=math.inf), H(pivot=1, off=math.nan)])
 def test_bad_curve(lib, h):
     assert sample(lib, L(), hlg=h) == HS_ERR_INVALID_ARG
     x = L()
     assert lib.hs_hlg_transform(C.byref(x), FAKE, C.byref(h), FAKE, 100, None) == HS_ERR_INVALID_ARG
     assert lib.hs_hlg_pivot(C.byref(x), FAKE, C.byref(h), FAKE, None) == HS_ERR_INVALID_ARG
+
+
+def test_median_pivot_boundary(lib):
+    """The mass-median pivot needs the workspace and is only offered by the samplers."""
+    HS_ERR_WORKSPACE, HS_ERR_UNSUPPORTED = -3, -5
+    h = H(pivot=3)
+    assert sample(lib, L(), hlg=h, mu=None) == HS_ERR_WORKSPACE
+    x = L()
+    assert lib.hs_hlg_transform(C.byref(x), None, C.byref(h), FAKE, 100, None) == HS_ERR_UNSUPPORTED
+    assert lib.hs_hlg_pivot(C.byref(x), None, C.byref(h), FAKE, None) == HS_ERR_UNSUPPORTED
 
 
 def test_curve_needs_mu(lib):
@@ -135,8 +145,9 @@ def test_binding_pivot_modes():
     h = hs._hlg_struct((1.0, 2.0, 1.0, 1.0, "top", -2.5))
     assert (h.pivot, h.pivot_offset) == (1, -2.5)
     assert hs._hlg_struct((1.0, 2.0, 1.0, 1.0)).pivot == 0
+    assert hs._hlg_struct((1.0, 2.0, 1.0, 1.0, "median")).pivot == 3
     with pytest.raises(ValueError):
-        hs._hlg_struct((1.0, 2.0, 1.0, 1.0, "median"))
+        hs._hlg_struct((1.0, 2.0, 1.0, 1.0, "mode"))
 
 
 def test_rolloff_off_is_accepted_by_validation(lib):

@@ -191,3 +191,95 @@ def test_pivot_many_draws_split_rows(hs, oracle_mod):
     rows = np.sort(np.random.default_rng(57).choice(w.B, size=12, replace=False))
     o, s1, s2 = oracle_sample(oracle_mod, w, rows=rows)
     print(assert_parity(g[rows], o, s1, s2, w.logits[rows].double().numpy(), "entropy 16 draws"))
+
+
+# ---- the mass-median pivot: mu = the log-prob at which the mass from the top first reaches
+# one half, so z = x - x_med with x_med the top-p boundary at p = 0.5 and T = 1. The GPU sums
+# fp32 terms exp2((x - x_max) log2(e)), each within a few 1e-7 relative, in fp64: its running
+# totals lie within ~3e-7 of the total mass of the oracle's. A row whose boundary moves when
+# the target moves by 1e-6 of the total (p = 0.5 (1 +- 2e-6)) may therefore take a
+# neighbouring logit; its draws are only checked for validity.
+def _median_sure(oracle_mod, w, rel=2e-6):
+    B = w.B
+    x64 = w.logits.double().numpy()
+    one = np.ones(B, np.float32)
+    lo = oracle_mod.filter_threshold(x64, one, top_p=np.full(B, 0.5 * (1 - rel), np.float32))[0]
+    hi = oracle_mod.filter_threshold(x64, one, top_p=np.full(B, 0.5 * (1 + rel), np.float32))[0]
+    return np.asarray(lo == hi)
+
+
+@pytest.mark.parametrize("dtype,V", [(torch.float32, 70001), (torch.bfloat16, 151936),
+                                     (torch.float16, 32000)])
+def test_median_pivot_sampling_variants(hs, oracle_mod, dtype, V):
+    """The median shift is worked out once per row before the sampling kernel, so every
+    kernel decomposition gives the same ids and scores bit for bit."""
+    w = W.generic(6, V, dtype, seed=65, scale=0.8, mask_frac=0.05, hlg=_curve("median", 0.0),
+                  K=3)
+    d = on_device(w)
+    o, s1, s2 = oracle_sample(oracle_mod, w)
+    sure = _median_sure(oracle_mod, w)
+    assert sure.sum() >= 3
+    x64 = w.logits.double().numpy()
+    res = {}
+    for name, opts in [("auto", None),
+                       ("one-block", hs.SampleOpts(variant=1)),
+                       ("split7", hs.SampleOpts(variant=2, nchunk=7)),
+                       ("split64", hs.SampleOpts(variant=2, nchunk=64)),
+                       ("one-block-exhaustive", hs.SampleOpts(variant=1, no_screen=1)),
+                       ("draw-groups", hs.SampleOpts(variant=1, draw_groups=3)),
+                       ("split5-draw-groups", hs.SampleOpts(variant=2, nchunk=5, draw_groups=2))]:
+        idx, best = hs.sample_ex(d["logits"], d["T"], d["seed"], d["offset"], hlg=w.hlg, k=3,
+                                 opts=opts, want_best=True)
+        idx = idx.cpu().numpy()
+        res[name] = (idx, best.cpu().numpy())
+        assert_parity(idx[sure], o[sure], s1[sure], s2[sure], x64[sure],
+                      "median %s %s" % (dtype, name))
+        assert np.all(idx >= 0) and np.all(np.isfinite(x64[np.arange(6)[:, None], idx]))
+    for name in res:
+        np.testing.assert_array_equal(res[name][0], res["auto"][0])
+        np.testing.assert_array_equal(res[name][1], res["auto"][1])
+
+
+def test_median_pivot_special_rows(hs, oracle_mod):
+    """Tiny and ragged rows, an empty row (-1), a bad temperature (-2), a greedy row, a flat
+    row (every token is the median) and a row with one dominant token."""
+    V = 777
+    w = W.generic(7, V, torch.bfloat16, seed=66, scale=1.5, mask_frac=0.1,
+                  hlg=_curve("median", 0.0), K=4, offset_max=2**35)
+    x = w.logits.float().numpy().copy()
+    x[0, :] = -np.inf
+    x[3, :] = 0.75
+    x[4, :] = 0.0
+    x[4, 11] = 9.0
+    w.logits = torch.from_numpy(x).to(torch.bfloat16)
+    w.T[1] = -1.0
+    w.T[2] = 0.0
+    g = gpu_sample(hs, w)
+    o, s1, s2 = oracle_sample(oracle_mod, w)
+    sure = _median_sure(oracle_mod, w)
+    x64 = w.logits.double().numpy()
+    assert g[0].tolist() == [-1] * 4 and g[1].tolist() == [-2] * 4
+    assert g[2].tolist() == [int(np.argmax(x64[2]))] * 4
+    assert_parity(g[sure], o[sure], s1[sure], s2[sure], x64[sure], "median special rows")
+    for V in (1, 3, 9, 1000):
+        wv = W.generic(3, V, torch.float16, seed=V + 70, mask_frac=0.1 if V > 4 else 0.0,
+                       hlg=_curve("median", 0.0), K=3)
+        gv = gpu_sample(hs, wv)
+        ov, t1, t2 = oracle_sample(oracle_mod, wv)
+        sv = _median_sure(oracle_mod, wv)
+        assert_parity(gv[sv], ov[sv], t1[sv], t2[sv], wv.logits.double().numpy()[sv],
+                      "median V=%d" % V)
+
+
+def test_median_pivot_headline_shape(hs, oracle_mod):
+    w = W.config4()
+    w.hlg = _curve("median", 0.0, w.hlg)
+    g = gpu_sample(hs, w)
+    rows = np.arange(0, w.B, 8)
+    o, s1, s2 = oracle_sample(oracle_mod, w, rows=rows)
+    B = len(rows)
+    sure = _median_sure(oracle_mod, W.Workload("rows", w.logits[rows], w.T[rows], w.seed[rows],
+                                               w.offset[rows], K=w.K))
+    assert sure.sum() >= B // 2
+    assert_parity(g[rows][sure], o[sure], s1[sure], s2[sure],
+                  w.logits[rows].double().numpy()[sure], "median 256x151936")
