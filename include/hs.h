@@ -62,8 +62,8 @@ typedef enum {
                              z = x - E_p[x], p = softmax(x)                                 */
     HS_PIVOT_MEDIAN = 3   /* mass median: mu = the log-prob at which the mass of softmax(x),
                              summed from the top over groups of equal logits, first reaches
-                             one half, so z = x - x_med. hs_sample / hs_sample_ex only (a
-                             workspace is required); HS_ERR_UNSUPPORTED elsewhere           */
+                             one half, so z = x - x_med (a first kernel finds x_med: the top-p
+                             boundary at p = 0.5, T = 1). Not for per-row settings        */
 } hs_pivot;
 
 /* The curve knobs of [HLG, Knobs]: mid gain m > 0 (finite), mid half-width w >= 0 (+inf
@@ -94,8 +94,9 @@ int hs_hlg_transform(const hs_logits *x, const float *mu, const hs_hlg_params *p
                      int64_t ldo, void *stream);
 
 /* mu_out[b] = the pivot the curve uses for row b in p's pivot mode, in log-prob nats
- * [HLG, The pivot]: mu[b] (HS_PIVOT_GIVEN), (x_max - LSE) - c (HS_PIVOT_TOP), or
- * sum_i p_i (x_i - LSE) (HS_PIVOT_ENTROPY); NaN for a row with no finite entry.
+ * [HLG, The pivot]: mu[b] (HS_PIVOT_GIVEN), (x_max - LSE) - c (HS_PIVOT_TOP),
+ * sum_i p_i (x_i - LSE) (HS_PIVOT_ENTROPY), or x_med - LSE (HS_PIVOT_MEDIAN); NaN for a row
+ * with no finite entry.
  * mu: device float[B], read only for HS_PIVOT_GIVEN (may be NULL otherwise);
  * mu_out: device float[B]; p: host pointer. */
 int hs_hlg_pivot(const hs_logits *x, const float *mu, const hs_hlg_params *p, float *mu_out,

@@ -316,6 +316,20 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
 
 }  // namespace
 
+// The mass median of every row (the threshold kernel's top-p selection at p = 0.5, T = 1)
+// into dst[b * stride]: the shift c of the median pivot [HLG, The pivot].
+hipError_t launch_median_shift(const hs_logits *x, float *dst, int64_t stride, hipStream_t s) {
+    hs::FilterArgs f{};
+    f.data = x->data;
+    f.ld = x->ld;
+    f.V = x->V;
+    f.aligned = rows_aligned(x) ? 1 : 0;
+    f.median = 1;
+    f.tau = dst;
+    f.tau_stride = stride;
+    return hs::launch_filter_tau(x->dtype, f, (int)x->B, s);
+}
+
 extern "C" {
 
 int hs_logsumexp(const hs_logits *x, float *lse, void *stream) {
@@ -338,7 +352,6 @@ int hs_hlg_transform(const hs_logits *x, const float *mu, const hs_hlg_params *p
     if (rc) return rc;
     rc = check_curve(p);
     if (rc) return rc;
-    if (p->pivot == HS_PIVOT_MEDIAN) return HS_ERR_UNSUPPORTED;
     if ((p->pivot == HS_PIVOT_GIVEN && !mu) || !out || ldo < x->V) return HS_ERR_INVALID_ARG;
     hs::RowOpArgs a{};
     a.data = x->data;
@@ -350,9 +363,18 @@ int hs_hlg_transform(const hs_logits *x, const float *mu, const hs_hlg_params *p
     a.ldo = ldo;
     a.curve = make_curve(p);
     a.pivot_offset = p->pivot == HS_PIVOT_TOP ? p->pivot_offset : 0.0f;
-    return hs::launch_row_lse(x->dtype, 1, p->pivot, a, (int)x->B,
-                              reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? HS_OK
-                                                                                   : HS_ERR_HIP;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    int piv = p->pivot;
+    if (piv == HS_PIVOT_MEDIAN) {
+        // each row's shift goes to the first element of its output row, which the transform
+        // reads before it writes the row
+        if (launch_median_shift(x, out, ldo, s) != hipSuccess) return HS_ERR_HIP;
+        a.shift = out;
+        a.shift_stride = ldo;
+        piv = 4;
+    }
+    return hs::launch_row_lse(x->dtype, 1, piv, a, (int)x->B, s) == hipSuccess ? HS_OK
+                                                                              : HS_ERR_HIP;
 }
 
 int hs_hlg_pivot(const hs_logits *x, const float *mu, const hs_hlg_params *p, float *mu_out,
@@ -361,7 +383,6 @@ int hs_hlg_pivot(const hs_logits *x, const float *mu, const hs_hlg_params *p, fl
     if (rc) return rc;
     rc = check_curve(p);
     if (rc) return rc;
-    if (p->pivot == HS_PIVOT_MEDIAN) return HS_ERR_UNSUPPORTED;
     if ((p->pivot == HS_PIVOT_GIVEN && !mu) || !mu_out) return HS_ERR_INVALID_ARG;
     hs::RowOpArgs a{};
     a.data = x->data;
@@ -371,9 +392,18 @@ int hs_hlg_pivot(const hs_logits *x, const float *mu, const hs_hlg_params *p, fl
     a.mu = p->pivot == HS_PIVOT_GIVEN ? mu : nullptr;
     a.mu_out = mu_out;
     a.pivot_offset = p->pivot == HS_PIVOT_TOP ? p->pivot_offset : 0.0f;
-    return hs::launch_row_lse(x->dtype, 2, p->pivot, a, (int)x->B,
-                              reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? HS_OK
-                                                                                   : HS_ERR_HIP;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    int piv = p->pivot;
+    if (piv == HS_PIVOT_MEDIAN) {
+        // each row's shift goes to mu_out[b], which the pivot kernel reads before it writes
+        // mu = c - LSE there
+        if (launch_median_shift(x, mu_out, 1, s) != hipSuccess) return HS_ERR_HIP;
+        a.shift = mu_out;
+        a.shift_stride = 1;
+        piv = 4;
+    }
+    return hs::launch_row_lse(x->dtype, 2, piv, a, (int)x->B, s) == hipSuccess ? HS_OK
+                                                                              : HS_ERR_HIP;
 }
 
 int hs_gumbel_argmax(const hs_logits *x, const float *T, const uint64_t *seed,

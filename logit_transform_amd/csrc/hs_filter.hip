@@ -241,7 +241,7 @@ __device__ __forceinline__ bool row_filter(const FilterArgs &a, int64_t b, RowFi
     } else {
         return true;
     }
-    if (threadIdx.x == 0) a.tau[b] = tau;
+    if (threadIdx.x == 0) a.tau[b * (a.tau_stride ? a.tau_stride : 1)] = tau;
     return false;
 }
 
@@ -538,7 +538,7 @@ __global__ __launch_bounds__(1024) void k_filter_tau(FilterArgs a) {
     const TauKept r = tau_radix<DT>(a, b, f, hc, hm, red_f, red_n);
     const float tau = r.tau;
     const uint32_t kept = r.kept;
-    if (threadIdx.x == 0) a.tau[b] = tau;
+    if (threadIdx.x == 0) a.tau[b * (a.tau_stride ? a.tau_stride : 1)] = tau;
     if (a.done == nullptr) return;
     constexpr int EPV = dtype_traits<DT>::epv;
     const char *rowp = reinterpret_cast<const char *>(a.data) + b * a.ld * dtype_traits<DT>::esize;
@@ -610,14 +610,14 @@ __global__ __launch_bounds__(1024) void k_filter_tau16(FilterArgs a) {
                                         red_f, red_u);
         const float tau = r.tau;
         const uint32_t kept = r.kept;
-        if (tid == 0) a.tau[b] = tau;
+        if (tid == 0) a.tau[b * (a.tau_stride ? a.tau_stride : 1)] = tau;
         if (a.done != nullptr && draw_kept<DT>(a, b, f.T, tau, kept, rowp, nvec, hist)) {
             if (tid == 0) a.done[b] = 1u;
         }
         return;
     }
     if (NF == 0u) {
-        if (tid == 0) a.tau[b] = -__builtin_inff();
+        if (tid == 0) a.tau[b * (a.tau_stride ? a.tau_stride : 1)] = -__builtin_inff();
         return;
     }
     const bool topk = f.k > 0 && (uint32_t)f.k < NF;
@@ -770,7 +770,7 @@ __global__ __launch_bounds__(1024) void k_filter_tau16(FilterArgs a) {
         }
         tau = fmaxf(tau, bits_value<DT>(rank_bits(s_rank[2])));
     }
-    if (tid == 0) a.tau[b] = tau;
+    if (tid == 0) a.tau[b * (a.tau_stride ? a.tau_stride : 1)] = tau;
     if (a.done == nullptr) return;
 
     // ---- a row that keeps few tokens is drawn here (its kept count comes from the selection

@@ -73,6 +73,10 @@ struct RowOpArgs {
     Curve curve;
     float pivot_offset;   // c of the top anchor
     float *mu_out;        // the pivot of every row (op 2)
+    // pivot 4 (the mass median): the shift c of row b at shift[b * shift_stride], read before
+    // the kernel writes any output (it may lie in the output)
+    const float *shift;
+    int64_t shift_stride;
 };
 
 // Top-k / top-p threshold of every row (curve off): tau[b] = -inf keeps every token, NaN marks
@@ -88,6 +92,7 @@ struct FilterArgs {
     // the mass median of every row instead (T = 1, top-p 0.5, no top-k; T, top_k and top_p
     // unused): tau is the logit where the mass from the top first reaches one half
     int32_t median;
+    int64_t tau_stride;     // tau of row b at tau[b * tau_stride]; 0 means 1
     // Drawing rows that keep few tokens in the threshold kernel (16-bit logits); done null:
     // thresholds only. done[b] = 1 marks a row drawn there (out / best_out written), 0 a row
     // left to the sampler.

@@ -27,6 +27,9 @@ __global__ __launch_bounds__(1024) void k_row_lse(RowOpArgs a) {
     const int64_t b = blockIdx.x;
     const int64_t nvec = (a.V + EPV - 1) / EPV;
     const char *rowp = reinterpret_cast<const char *>(a.data) + b * a.ld * tr::esize;
+    // the mass median's shift, read before the first barrier (no output is written before it)
+    float c4 = 0.0f;
+    if constexpr (PIV == 4) c4 = a.shift[b * a.shift_stride];
     float mx = -__builtin_inff();
     for (int64_t gv = threadIdx.x; gv < nvec; gv += blockDim.x) {
         const uint4 v = load_vec<DT>(rowp, gv, a.V, a.aligned);
@@ -59,6 +62,8 @@ __global__ __launch_bounds__(1024) void k_row_lse(RowOpArgs a) {
             c = lse + a.mu[b];
         } else if constexpr (PIV == 1) {
             c = M - a.pivot_offset;
+        } else if constexpr (PIV == 4) {
+            c = c4;
         } else {
             const float U = block_sum(u, red_u);
             c = M + U * kLn2 / S;
@@ -171,10 +176,12 @@ hipError_t launch_row_lse(int dt, int op, int piv, const RowOpArgs &a, int grid,
     if (op == 1) {
         if (piv == 1) return launch_row_op<1, 1>(dt, a, grid, s);
         if (piv == 2) return launch_row_op<1, 2>(dt, a, grid, s);
+        if (piv == 4) return launch_row_op<1, 4>(dt, a, grid, s);
         return launch_row_op<1, 0>(dt, a, grid, s);
     }
     if (piv == 1) return launch_row_op<2, 1>(dt, a, grid, s);
     if (piv == 2) return launch_row_op<2, 2>(dt, a, grid, s);
+    if (piv == 4) return launch_row_op<2, 4>(dt, a, grid, s);
     return launch_row_op<2, 0>(dt, a, grid, s);
 }
 

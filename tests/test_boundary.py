@@ -107,13 +107,13 @@ def test_bad_curve(lib, h):
 
 
 def test_median_pivot_boundary(lib):
-    """The mass-median pivot needs the workspace and is only offered by the samplers."""
-    HS_ERR_WORKSPACE, HS_ERR_UNSUPPORTED = -3, -5
+    """The mass-median pivot needs no mu; the sampler needs the workspace for it."""
+    HS_ERR_WORKSPACE = -3
     h = H(pivot=3)
     assert sample(lib, L(), hlg=h, mu=None) == HS_ERR_WORKSPACE
     x = L()
-    assert lib.hs_hlg_transform(C.byref(x), None, C.byref(h), FAKE, 100, None) == HS_ERR_UNSUPPORTED
-    assert lib.hs_hlg_pivot(C.byref(x), None, C.byref(h), FAKE, None) == HS_ERR_UNSUPPORTED
+    assert lib.hs_hlg_transform(C.byref(x), None, C.byref(h), FAKE, 99, None) == HS_ERR_INVALID_ARG
+    assert lib.hs_hlg_pivot(C.byref(x), None, C.byref(h), None, None) == HS_ERR_INVALID_ARG
 
 
 def test_curve_needs_mu(lib):

@@ -1,6 +1,6 @@
 """The curve's pivot modes on the HIP path against the oracle [HLG, The pivot]: the pivot
-given per row, top-anchored (mu = l_max - c, so z = x - (x_max - c)) and entropy-anchored
-(mu = sum p l, so z = x - E_p[x]).
+given per row, top-anchored (mu = l_max - c, so z = x - (x_max - c)), entropy-anchored
+(mu = sum p l, so z = x - E_p[x]) and the mass median (z = x - x_med).
 
 Tolerances. The kernels form the shift c of z = x - c in fp32 from fp32 sums: c = LSE + mu
 (given pivot, LSE within 4e-6 max(1, |LSE|)), c = x_max - offset (top; one rounding), or
@@ -20,7 +20,7 @@ from tests.gpu_util import assert_parity, gpu_sample, on_device, oracle_sample, 
 pytestmark = pytest.mark.gpu
 
 CURVE = {"m": 1.5, "w": 2.0, "beta_t": 1.0, "beta_h": 2.0}
-MODES = [("input", 0.0), ("top", 2.0), ("top", -1.5), ("entropy", 0.0)]
+MODES = [("input", 0.0), ("top", 2.0), ("top", -1.5), ("entropy", 0.0), ("median", 0.0)]
 ANCHORED = [("top", 2.0), ("top", 0.0), ("entropy", 0.0)]
 
 
@@ -62,9 +62,11 @@ def test_pivot_values_and_transform(hs, oracle_mod, name, make, mode, off):
     lse = oracle_mod.logsumexp(w.logits)
     ref_mu = oracle_mod.pivot(w.logits, mode, off, mu=w.mu)
     got_mu = hs.hlg_pivot(x, h, mu=mu).cpu().numpy().astype(np.float64)
+    # the median: rows whose boundary is decided away from one half (see _median_sure)
+    sel = _median_sure(oracle_mod, w) if mode == "median" else np.ones(w.B, dtype=bool)
     empty = ~np.isfinite(lse)
     assert np.all(np.isnan(got_mu[empty])) and np.all(np.isnan(ref_mu[empty]))
-    f = ~empty
+    f = ~empty & sel
     tol = 1e-5 * np.maximum.reduce([np.ones(f.sum()), np.abs(lse[f]), np.abs(ref_mu[f])])
     assert np.all(np.abs(got_mu[f] - ref_mu[f]) <= tol), np.abs(got_mu[f] - ref_mu[f]).max()
 
@@ -73,7 +75,7 @@ def test_pivot_values_and_transform(hs, oracle_mod, name, make, mode, off):
                                    pivot=mode, pivot_offset=off)
     masked = ~np.isfinite(w.logits.double().numpy())
     assert np.all(lp[masked] == -np.inf)
-    fin = ~masked
+    fin = ~masked & sel[:, None]
     c = (lse + ref_mu)[:, None] * np.ones_like(ref)      # the shift of z = x - c per row
     tol = 1e-5 * np.maximum(1.0, np.abs(ref[fin])) + h["m"] * 1e-5 * np.maximum(1.0, np.abs(c[fin]))
     err = np.abs(lp[fin] - ref[fin])
