@@ -1,7 +1,8 @@
 """A seeded sweep of random configurations on the HIP path against the oracle: dtype, batch,
-vocabulary (from one token to rows that must be split), draws, curve and pivot mode, masking,
-padded rows, large counter offsets, greedy and invalid rows, and the top-k / top-p filters.
-Each case is small enough for the oracle; the comparison rule is the other parity tests'."""
+vocabulary (from one token to rows that must be split), draws, curve and pivot mode (given,
+top, entropy, median), masking, padded rows, large counter offsets, greedy and invalid rows,
+and the top-k / top-p filters. Each case is small enough for the oracle; the comparison rule
+is the other parity tests'."""
 import numpy as np
 import pytest
 import torch
@@ -9,6 +10,7 @@ import torch
 from synth import workloads as W
 from tests.gpu_util import assert_parity, require_gpu
 from tests.test_gpu_filter import _check_rows
+from tests.test_gpu_pivot import _median_sure
 
 pytestmark = pytest.mark.gpu
 
@@ -27,9 +29,9 @@ def _case(rng, i):
     V = int(VOCABS[int(rng.integers(len(VOCABS)))])
     B = int(rng.integers(1, 7))
     K = int((1, 2, 7)[int(rng.integers(3))])
-    mode = ("off", "given", "top", "entropy", "filter")[int(rng.integers(5))]
-    hlg = dict(CURVE) if mode in ("given", "top", "entropy") else None
-    if mode in ("top", "entropy"):
+    mode = ("off", "given", "top", "entropy", "median", "filter")[int(rng.integers(6))]
+    hlg = dict(CURVE) if mode in ("given", "top", "entropy", "median") else None
+    if mode in ("top", "entropy", "median"):
         hlg["pivot"] = mode
         if mode == "top":
             hlg["pivot_offset"] = float(rng.uniform(0.0, 6.0))
@@ -76,4 +78,9 @@ def test_random_configurations(hs, oracle_mod):
         g = hs.sample(x, T, seed, off, mu=mu, hlg=w.hlg, k=w.K).cpu().numpy()
         o, s1, s2 = oracle_mod.sample(w.logits, w.T, w.seed, w.offset, K=w.K,
                                       mu=w.mu if mode == "given" else None, hlg=w.hlg)
-        assert_parity(g, o, s1, s2, w.logits.double().numpy(), label)
+        x64 = w.logits.double().numpy()
+        # the median: rows whose mass boundary is decided away from one half
+        sure = _median_sure(oracle_mod, w) if mode == "median" else np.ones(w.B, dtype=bool)
+        assert_parity(g[sure], o[sure], s1[sure], s2[sure], x64[sure], label)
+        ok = g >= 0
+        assert np.all(np.isfinite(x64[np.nonzero(ok)[0], g[ok]]))
