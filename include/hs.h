@@ -63,7 +63,7 @@ typedef enum {
     HS_PIVOT_MEDIAN = 3   /* mass median: mu = the log-prob at which the mass of softmax(x),
                              summed from the top over groups of equal logits, first reaches
                              one half, so z = x - x_med (a first kernel finds x_med: the top-p
-                             boundary at p = 0.5, T = 1). Not for per-row settings        */
+                             boundary at p = 0.5, T = 1)                                  */
 } hs_pivot;
 
 /* The curve knobs of [HLG, Knobs]: mid gain m > 0 (finite), mid half-width w >= 0 (+inf
@@ -144,7 +144,7 @@ typedef struct {
     float w;
     float beta_t;
     float beta_h;
-    int32_t pivot;        /* hs_pivot */
+    int32_t pivot;        /* hs_pivot (HS_PIVOT_MEDIAN needs the workspace)              */
     float pivot_offset;   /* c of HS_PIVOT_TOP */
     int32_t enabled;      /* 0: curve off for this row (l' = x) */
     int32_t reserved;     /* must be 0 */
@@ -194,7 +194,9 @@ int hs_sample_plan(const hs_logits *x, int32_t K, int32_t hlg_on, int32_t have_w
  * launch [HLG, The transfer function; The pivot; GMX, Background]. Per-row parameters are
  * validated in the kernel: a row whose enabled curve has an invalid knob (the rules of
  * hs_hlg_params), an unknown pivot, a non-finite top offset or a non-zero reserved field gives
- * -2, as does a given-pivot row whose mu is not finite or whose mu array is NULL. mu: device
+ * -2, as does a given-pivot row whose mu is not finite or whose mu array is NULL, and a
+ * median-pivot row when ws is NULL (the rows' median shifts are worked out into the
+ * workspace by a first kernel, which skips every other row). mu: device
  * float[B] or NULL (read only for enabled rows with HS_PIVOT_GIVEN); rows: device
  * hs_hlg_row[B]. Ids and scores of a row are bit-identical to hs_sample_ex's for that row's
  * setting. The workspace size is hs_workspace_bytes(B, V, K, dtype, 1). best and opts as

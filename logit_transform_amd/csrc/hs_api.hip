@@ -279,7 +279,9 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
     // row); otherwise a pre-pass computes them.
     // The mass median: the threshold kernel's top-p selection at p = 0.5, T = 1 gives every
     // row's shift c before the sampling kernel runs (which then needs no log-sum-exp).
-    if (piv == 4) {
+    // Per-row settings: the same for the rows whose record asks for the median (the others
+    // return at once); without a workspace such rows give -2.
+    if (piv == 4 || (piv == 3 && ws_ok)) {
         if (!ws_ok) return HS_ERR_WORKSPACE;   // the shifts live in it
         hs::FilterArgs f{};
         f.data = x->data;
@@ -287,6 +289,7 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
         f.V = x->V;
         f.aligned = a.aligned;
         f.median = 1;
+        f.row_curves = piv == 3 ? a.row_curves : nullptr;
         f.tau = reinterpret_cast<float *>(reinterpret_cast<char *>(ws) + L.tau);
         if (hs::launch_filter_tau(x->dtype, f, (int)x->B, s) != hipSuccess) return HS_ERR_HIP;
         a.shift = f.tau;

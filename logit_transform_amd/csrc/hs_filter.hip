@@ -224,6 +224,10 @@ struct RowFilter {
 
 __device__ __forceinline__ bool row_filter(const FilterArgs &a, int64_t b, RowFilter *f) {
     if (a.median) {   // the mass median [HLG, The pivot]: the top-p boundary at p = 0.5, T = 1
+        if (a.row_curves != nullptr) {
+            const RowCurve r = a.row_curves[b];
+            if (!(r.enabled != 0 && r.pivot == 3)) return false;   // not a median row
+        }
         f->T = 1.0f;
         f->k = 0;
         f->p = 0.5f;

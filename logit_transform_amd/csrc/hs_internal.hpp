@@ -93,6 +93,8 @@ struct FilterArgs {
     // unused): tau is the logit where the mass from the top first reaches one half
     int32_t median;
     int64_t tau_stride;     // tau of row b at tau[b * tau_stride]; 0 means 1
+    // median mode with per-row settings: only rows whose record is an enabled median pivot
+    const RowCurve *row_curves;
     // Drawing rows that keep few tokens in the threshold kernel (16-bit logits); done null:
     // thresholds only. done[b] = 1 marks a row drawn there (out / best_out written), 0 a row
     // left to the sampler.

@@ -266,9 +266,10 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
         const bool fin_m = r.m > 0.0f && r.m < __builtin_inff();
         const bool fin_t = r.beta_t > 0.0f && r.beta_t < __builtin_inff();
         const bool fin_h = r.beta_h > 0.0f && r.beta_h < __builtin_inff();
+        // (a median row needs the shifts worked out before this kernel: a.shift)
         const bool valid = fin_m && r.w >= 0.0f && fin_t && fin_h && r.pivot >= 0 &&
-                           r.pivot <= 2 && (r.pivot != 1 || fabsf(r.pivot_offset) < __builtin_inff()) &&
-                           r.reserved == 0;
+                           r.pivot <= 3 && (r.pivot != 1 || fabsf(r.pivot_offset) < __builtin_inff()) &&
+                           (r.pivot != 3 || a.shift != nullptr) && r.reserved == 0;
         const bool on = r.enabled != 0 && valid;
         if (r.enabled != 0 && !valid) bad = true;
         if (on) {
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             cv.mbh = r.m * r.beta_h;
             cv.ibt = 1.0f / r.beta_t;
             cv.ibh = 1.0f / r.beta_h;
-            rpiv = r.pivot;
+            rpiv = r.pivot == 3 ? 4 : r.pivot;   // 4: the shift read per row (mass median)
             poff = r.pivot_offset;
             if (rpiv == 0) {
                 mu = a.mu ? a.mu[b] : __builtin_nanf("");

@@ -127,8 +127,9 @@ def test_invalid_and_empty_rows(hs, oracle_mod):
 
 
 @pytest.mark.parametrize("setting", [None, dict(A), dict(A, pivot="top", pivot_offset=2.0),
-                                     dict(A, pivot="entropy"), dict(B_)],
-                         ids=["off", "given", "top", "entropy", "given-B"])
+                                     dict(A, pivot="entropy"), dict(B_),
+                                     dict(A, pivot="median")],
+                         ids=["off", "given", "top", "entropy", "given-B", "median"])
 @pytest.mark.parametrize("variant", ["one-block", "split7"])
 def test_uniform_rows_equal_per_call(hs, setting, variant):
     """All rows sharing one setting: bit-identical ids and winning scores to hs_sample_ex with
@@ -147,6 +148,31 @@ def test_uniform_rows_equal_per_call(hs, setting, variant):
                            opts=opts, want_best=True)
     np.testing.assert_array_equal(g.cpu().numpy(), ref.cpu().numpy())
     np.testing.assert_array_equal(gb.cpu().numpy(), rb.cpu().numpy())
+
+
+@pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 151936), (torch.float32, 50001)])
+def test_mixed_rows_with_median(hs, oracle_mod, dtype, V):
+    """Median-pivot rows among the others: their shifts come from a first kernel that skips
+    every other row. Compared with the oracle on the rows whose mass boundary is decided away
+    from one half (the median rows) and on every other row."""
+    from tests.test_gpu_pivot import _median_sure
+    B, K = 12, 3
+    w = W.generic(B, V, dtype, seed=V % 997 + 11, scale=1.0, mask_frac=0.05, hlg=dict(A), K=K)
+    w.T[7] = 0.0
+    settings = [None, dict(A, pivot="median"), dict(A), dict(B_, pivot="median"),
+                dict(A, pivot="top", pivot_offset=1.0), dict(A, pivot="entropy")] * 2
+    d = on_device(w)
+    o, s1, s2 = _oracle_rows(oracle_mod, w, settings)
+    med = np.array([h is not None and h.get("pivot") == "median" for h in settings])
+    sure = ~med | _median_sure(oracle_mod, w)
+    x64 = w.logits.double().numpy()
+    rows = hs.hlg_rows(settings)
+    for name, opts in [("auto", None), ("split7", hs.SampleOpts(variant=2, nchunk=7))]:
+        g = hs.sample_rows(d["logits"], d["T"], d["seed"], d["offset"], rows, mu=d["mu"], k=K,
+                           opts=opts).cpu().numpy()
+        assert_parity(g[sure], o[sure], s1[sure], s2[sure], x64[sure],
+                      "rows with median %s %s" % (dtype, name))
+        assert np.all(g >= 0)
 
 
 def test_mixed_rows_headline_shape(hs, oracle_mod):
