@@ -18,6 +18,12 @@
 // maximum and finite count); top-p selects, among the keys top-k keeps, the key at which the
 // tempered mass exp((x - x_max) / T), summed from the top, reaches p times the total, by fp64
 // sums of fp32 terms. Wave 0 picks each level's bin with a parallel scan over the bins.
+//
+// The same kernels serve two more uses. In median mode (T = 1, top-p 0.5, no top-k) tau is
+// the mass median of the row, the shift of the curve's median pivot [HLG, The pivot]. And when
+// the caller asks for it, a row known to keep few tokens is drawn here as well (draw_kept): a
+// second pass gathers the kept tokens and every (token, draw) pair is scored exactly, so the
+// sampling kernel can skip the row.
 #include <hip/hip_runtime.h>
 
 #include "hs_device.hpp"
