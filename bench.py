@@ -29,7 +29,7 @@ METRIC = ("sampled rows/sec and achieved HBM GB/s (% of peak) for [B,V] logits â
 HBM_PEAK_GBPS = 8000.0
 # VALU lane-operations per second of MI355X: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.
 ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
-# Algorithmic VALU operations per element and draw ("Roofline"):
+# Algorithmic VALU operations per element and draw (the work the method itself needs):
 # Philox4x32-10 share 10 (10 rounds x 2 mul-hi/lo + 2 three-way xor, per 4 words),
 # upcast 1, compare 1; plus, once per element with the curve on, the log-sum-exp's
 # max / exponent-argument / exp / add (4).

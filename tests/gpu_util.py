@@ -22,7 +22,7 @@ def require_gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     import logit_transform_amd as hs
-    hs.load()   # no fallback: a missing library is a failure on a GPU machine
+    hs.load()   # no fallback: with a GPU present, a missing library is a failure
     return hs
 
 
