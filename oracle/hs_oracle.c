@@ -21,7 +21,8 @@
  *     word (i & 3). Draw k of a row uses off = offset_row + k (mod 2^64).
  *   - word -> uniform: u = (r + 1/2) * 2^-32, which is exact in double and never 0 or 1.
  *   - temperature with the curve: score = g(z) / T + G; greedy when T == 0 [HLG, Greedy is
- *     untouched; GMX, Task 3]; T < 0 or T not finite gives -2.
+ *     untouched; GMX, Task 3]; T < 0, T not finite, or T subnormal (0 < T < FLT_MIN, where
+ *     1/T overflows single precision) gives -2.
  *   - ties go to the lowest index; a row with no finite logit gives -1.
  *   - logits must be finite or -inf; NaN or +inf makes the call fail (-1 return).
  *   - top-k / top-p on the Gumbel path (the follow-on the Gumbel-max issue names, without an
@@ -31,6 +32,7 @@
  *
  * Build: gcc -O2 -fopenmp -fPIC -shared (never -ffast-math: it would break -inf masking).
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <stddef.h>
@@ -90,6 +92,43 @@ uint32_t or_element_word(uint64_t seed, uint64_t row, uint64_t off, uint64_t i)
     return out[i & 3];
 }
 
+/* The screened layout of the same stream: element i = 8q + e takes the high 16 bits of its
+ * word from the 16-bit half e of the 128-bit output of the call at counter word 2q, and the
+ * low 16 bits from the half e of the call at 2q + 1 (half e of an output: word e >> 1, bits
+ * 16 (e & 1) .. 16 (e & 1) + 15). The other counter and key words are those of the plain
+ * layout. It draws on the same calls as the plain layout (calls 2q and 2q + 1 cover elements
+ * 8q .. 8q + 7 there) and only hands their bits out differently, so that one call gives the
+ * leading 16 bits of eight elements. */
+static uint32_t or_half16(const uint32_t out[4], unsigned e)
+{
+    return (out[e >> 1] >> (16u * (e & 1u))) & 0xFFFFu;
+}
+
+uint32_t or_element_word_screened(uint64_t seed, uint64_t row, uint64_t off, uint64_t i)
+{
+    uint32_t ctr[4], key[2], hi[4], lo[4];
+    const uint64_t q = i >> 3;
+    const unsigned e = (unsigned)(i & 7u);
+    key[0] = (uint32_t)seed;
+    key[1] = (uint32_t)(seed >> 32);
+    ctr[1] = (uint32_t)row;
+    ctr[2] = (uint32_t)off;
+    ctr[3] = (uint32_t)(off >> 32);
+    ctr[0] = (uint32_t)(2 * q);
+    or_philox4x32_10(ctr, key, hi);
+    ctr[0] = (uint32_t)(2 * q + 1);
+    or_philox4x32_10(ctr, key, lo);
+    return (or_half16(hi, e) << 16) | or_half16(lo, e);
+}
+
+/* Word of element i in the given layout: 0 plain, 1 screened. */
+uint32_t or_element_word_layout(uint64_t seed, uint64_t row, uint64_t off, uint64_t i,
+                                int layout)
+{
+    return layout == 1 ? or_element_word_screened(seed, row, off, i)
+                       : or_element_word(seed, row, off, i);
+}
+
 /* Gumbel noise from a word [GMX, Background]: g = -log(-log(u)), u = (r + 1/2) 2^-32. */
 double or_gumbel(uint32_t r)
 {
@@ -112,6 +151,13 @@ double or_hlg_g(double z, double m, double w, double beta_t, double beta_h)
     return m * w + m * beta_h * log1p((z - w) / beta_h);
 }
 
+/* A usable temperature: 0 (greedy) or a normal positive single-precision value. T is read as
+ * float, so FLT_MIN bounds the subnormals from above. */
+static int or_temp_ok(double t)
+{
+    return t == 0.0 || (t >= (double)FLT_MIN && isfinite(t));
+}
+
 /* Validation shared by the row routines: curve knobs in nats [HLG, Knobs]. */
 static int or_params_ok(double m, double w, double bt, double bh)
 {
@@ -130,17 +176,28 @@ static int or_row_ok(const double *x, int64_t V)
 }
 
 /* log-sum-exp of one row over its finite entries [HLG, The transfer function: log-prob
- * space]. Returns -inf for a row with no finite entry. */
+ * space]: LSE = M + log(sum_i exp(x_i - M)) with M the largest finite entry. The sum is
+ * compensated (Neumaier's variant of Kahan summation: the rounding error of every addition is
+ * carried in a second accumulator), so its error does not grow with the row length. Returns
+ * -inf for a row with no finite entry. */
 double or_row_logsumexp(const double *x, int64_t V)
 {
     double M = -INFINITY;
     for (int64_t i = 0; i < V; ++i)
         if (x[i] > M) M = x[i];
     if (M == -INFINITY) return -INFINITY;
-    double s = 0.0;
-    for (int64_t i = 0; i < V; ++i)
-        if (x[i] > -INFINITY) s += exp(x[i] - M);
-    return M + log(s);
+    double s = 0.0, comp = 0.0;
+    for (int64_t i = 0; i < V; ++i) {
+        if (!(x[i] > -INFINITY)) continue;
+        double term = exp(x[i] - M);
+        double t = s + term;
+        if (fabs(s) >= fabs(term))
+            comp += (s - t) + term;
+        else
+            comp += (term - t) + s;
+        s = t;
+    }
+    return M + log(s + comp);
 }
 
 /* lse[r] for n rows of length V with row stride ld (elements). Returns 0, or -1 on a NaN /
@@ -256,14 +313,16 @@ int or_hlg_transform(const double *x, int64_t n, int64_t V, int64_t ld, const fl
  * offset[r]; pivot and c select the pivot mode (or_row_pivot).
  * Outputs: out[r*K + k] token index, or -1 (no finite logit) / -2 (bad T, or bad given mu);
  * best[r*K+k] and second[r*K+k] (may be NULL) the two largest scores of that draw
- * (-inf when absent). With hlg == 0 the curve parameters are ignored.
- * Returns 0, -1 on a NaN/+inf logit, -2 on bad curve parameters.
+ * (-inf when absent). With hlg == 0 the curve parameters are ignored. layout selects the
+ * stream's word layout (0 plain, 1 screened: or_element_word_layout).
+ * Returns 0, -1 on a NaN/+inf logit, -2 on bad curve parameters or layout.
  * ------------------------------------------------------------------------------------- */
 int or_sample(const double *x, int64_t n, int64_t V, int64_t ld, const int64_t *row_id,
               const float *T, const float *mu, int hlg, float m, float w, float bt, float bh,
               int pivot, float c, const uint64_t *seed, const uint64_t *offset, int32_t K,
-              int32_t *out, double *best, double *second)
+              int32_t *out, double *best, double *second, int layout)
 {
+    if (layout != 0 && layout != 1) return -2;
     if (hlg && !or_params_ok(m, w, bt, bh)) return -2;
     if (hlg && (pivot < 0 || pivot > 3 || (pivot == 1 && !isfinite(c)))) return -2;
     int bad = 0;
@@ -287,7 +346,7 @@ int or_sample(const double *x, int64_t n, int64_t V, int64_t ld, const int64_t *
         for (int64_t i = 0; i < V; ++i) nfinite += (xr[i] > -INFINITY);
         if (nfinite == 0) continue;                                   /* -1 */
         double t = (double)T[r];
-        if (!isfinite(t) || t < 0.0 || (hlg && pivot == 0 && !isfinite((double)mu[r]))) {
+        if (!or_temp_ok(t) || (hlg && pivot == 0 && !isfinite((double)mu[r]))) {
             *o = -2;
             continue;
         }
@@ -308,7 +367,8 @@ int or_sample(const double *x, int64_t n, int64_t V, int64_t ld, const int64_t *
             for (int64_t i = 0; i < V; ++i) {
                 if (!(xr[i] > -INFINITY)) continue;
                 double lp = hlg ? or_hlg_g((xr[i] - lse) - mur, m, w, bt, bh) : xr[i];
-                uint32_t word = or_element_word(seed[r], (uint64_t)row_id[r], off, (uint64_t)i);
+                uint32_t word = or_element_word_layout(seed[r], (uint64_t)row_id[r], off,
+                                                       (uint64_t)i, layout);
                 double s = lp / t + or_gumbel(word);
                 if (j < 0 || s > s1) { s2 = s1; s1 = s; j = i; }
                 else if (s > s2) s2 = s;
@@ -326,6 +386,14 @@ void or_stream_words(uint64_t seed, uint64_t row, uint64_t off, int64_t V, uint3
 {
     for (int64_t i = 0; i < V; ++i)
         words[i] = or_element_word(seed, row, off, (uint64_t)i);
+}
+
+/* The same in a given layout (0 plain, 1 screened). */
+void or_stream_words_layout(uint64_t seed, uint64_t row, uint64_t off, int64_t V, int layout,
+                            uint32_t *words)
+{
+    for (int64_t i = 0; i < V; ++i)
+        words[i] = or_element_word_layout(seed, row, off, (uint64_t)i, layout);
 }
 
 /* Element-wise batch forms for tests. */
@@ -416,7 +484,7 @@ int or_filter_tau(const double *x, int64_t n, int64_t V, int64_t ld, const float
         double t = (double)T[r];
         double p = top_p ? (double)top_p[r] : 1.0;
         int a = 0;
-        if (!isfinite(t) || t < 0.0 || !(p > 0.0)) {
+        if (!or_temp_ok(t) || !(p > 0.0)) {
             tau[r] = NAN;
         } else {
             tau[r] = or_filter_tau_row(x + r * ld, V, t, top_k ? top_k[r] : 0, p, &a);
@@ -427,13 +495,15 @@ int or_filter_tau(const double *x, int64_t n, int64_t V, int64_t ld, const float
 }
 
 /* or_sample with the curve off and the kept set {x >= tau[r]} of or_filter_tau: tokens below
- * the threshold are treated as masked. Outputs as or_sample; -2 also for an invalid p. */
+ * the threshold are treated as masked. Outputs and layout as or_sample; -2 also for an invalid
+ * p. */
 int or_sample_filtered(const double *x, int64_t n, int64_t V, int64_t ld,
                        const int64_t *row_id, const float *T, const int32_t *top_k,
                        const float *top_p, const uint64_t *seed, const uint64_t *offset,
                        int32_t K, int32_t *out, double *best, double *second, double *tau,
-                       int32_t *amb)
+                       int32_t *amb, int layout)
 {
+    if (layout != 0 && layout != 1) return -2;
     int rc = or_filter_tau(x, n, V, ld, T, top_k, top_p, tau, amb);
     if (rc) return rc;
 #pragma omp parallel for schedule(dynamic, 16)
@@ -457,9 +527,9 @@ int or_sample_filtered(const double *x, int64_t n, int64_t V, int64_t ld,
         for (int64_t i = 0; i < V; ++i) {
             if (!(xr[i] > -INFINITY) || xr[i] < tau[r]) continue;
             double s = (t == 0.0) ? xr[i]
-                                  : xr[i] / t + or_gumbel(or_element_word(seed[r],
-                                                                           (uint64_t)row_id[r],
-                                                                           off, (uint64_t)i));
+                                  : xr[i] / t + or_gumbel(or_element_word_layout(
+                                                    seed[r], (uint64_t)row_id[r], off,
+                                                    (uint64_t)i, layout));
             if (j < 0 || s > s1) { s2 = s1; s1 = s; j = i; }
             else if (s > s2) s2 = s;
         }

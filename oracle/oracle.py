@@ -38,6 +38,11 @@ def lib():
         L.or_element_word.restype = C.c_uint32
         L.or_stream_words.argtypes = [C.c_uint64, C.c_uint64, C.c_uint64, C.c_int64, u32p]
         L.or_stream_words.restype = None
+        L.or_stream_words_layout.argtypes = [C.c_uint64, C.c_uint64, C.c_uint64, C.c_int64,
+                                             C.c_int, u32p]
+        L.or_stream_words_layout.restype = None
+        L.or_element_word_layout.argtypes = [C.c_uint64] * 4 + [C.c_int]
+        L.or_element_word_layout.restype = C.c_uint32
         L.or_gumbel_n.argtypes = [C.c_int64, u32p, f64p]
         L.or_gumbel_n.restype = None
         L.or_hlg_g_n.argtypes = [C.c_int64, f64p, C.c_double, C.c_double, C.c_double,
@@ -54,14 +59,15 @@ def lib():
         L.or_pivot.restype = C.c_int
         L.or_sample.argtypes = [f64p, C.c_int64, C.c_int64, C.c_int64, i64p, f32p, f32p,
                                 C.c_int, C.c_float, C.c_float, C.c_float, C.c_float,
-                                C.c_int, C.c_float, u64p, u64p, C.c_int32, i32p, f64p, f64p]
+                                C.c_int, C.c_float, u64p, u64p, C.c_int32, i32p, f64p, f64p,
+                                C.c_int]
         L.or_sample.restype = C.c_int
         L.or_filter_tau.argtypes = [f64p, C.c_int64, C.c_int64, C.c_int64, f32p, i32p, f32p,
                                     f64p, i32p]
         L.or_filter_tau.restype = C.c_int
         L.or_sample_filtered.argtypes = [f64p, C.c_int64, C.c_int64, C.c_int64, i64p, f32p,
                                          i32p, f32p, u64p, u64p, C.c_int32, i32p, f64p, f64p,
-                                         f64p, i32p]
+                                         f64p, i32p, C.c_int]
         L.or_sample_filtered.restype = C.c_int
         _lib = L
     return _lib
@@ -99,13 +105,24 @@ def philox4x32_10(ctr, key) -> np.ndarray:
     return out
 
 
-def element_word(seed: int, row: int, off: int, i: int) -> int:
-    return int(lib().or_element_word(seed, row, off, i))
+# Word layouts of the random stream: "plain" (element i takes word i & 3 of the call at
+# counter word i >> 2) and "screened" (the 16-bit halves of the calls at 2q and 2q + 1,
+# q = i >> 3, make the high and low halves of element i's word).
+LAYOUTS = {"plain": 0, "screened": 1}
 
 
-def stream_words(seed: int, row: int, off: int, V: int) -> np.ndarray:
+def _layout(layout) -> int:
+    return LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+
+
+def element_word(seed: int, row: int, off: int, i: int, layout="plain") -> int:
+    return int(lib().or_element_word_layout(seed, row, off, i, _layout(layout)))
+
+
+def stream_words(seed: int, row: int, off: int, V: int, layout="plain") -> np.ndarray:
     out = np.zeros(V, dtype=np.uint32)
-    lib().or_stream_words(int(seed) & (2**64 - 1), int(row), int(off) & (2**64 - 1), V, out)
+    lib().or_stream_words_layout(int(seed) & (2**64 - 1), int(row), int(off) & (2**64 - 1), V,
+                                 _layout(layout), out)
     return out
 
 
@@ -172,13 +189,14 @@ def hlg_transform(x, mu, m, w, beta_t, beta_h, pivot="input", pivot_offset=0.0) 
     return out
 
 
-def sample(x, T, seed, offset, K: int = 1, mu=None, hlg=None, row_id=None):
+def sample(x, T, seed, offset, K: int = 1, mu=None, hlg=None, row_id=None, layout="plain"):
     """Token ids [n, K] plus the best and second-best score of every draw.
 
     hlg: None (curve off) or a mapping/tuple (m, w, beta_t, beta_h); a mapping may also
     carry "pivot" ("input", "top", "entropy", "median") and "pivot_offset" (the c of the top
     mode).
-    row_id: the global row index keying each row's Philox counter (default 0..n-1)."""
+    row_id: the global row index keying each row's Philox counter (default 0..n-1).
+    layout: the word layout of the random stream ("plain" or "screened")."""
     x = _as_f64_rows(x)
     n, V = x.shape
     T = np.ascontiguousarray(np.asarray(T, dtype=np.float32).reshape(n))
@@ -204,9 +222,9 @@ def sample(x, T, seed, offset, K: int = 1, mu=None, hlg=None, row_id=None):
     best = np.zeros((n, K), dtype=np.float64)
     second = np.zeros((n, K), dtype=np.float64)
     rc = lib().or_sample(x, n, V, V, rid, T, mu_a, on, p[0], p[1], p[2], p[3], piv, poff,
-                         seed, offset, int(K), out, best, second)
+                         seed, offset, int(K), out, best, second, _layout(layout))
     if rc == -2:
-        raise OracleError("invalid curve parameters")
+        raise OracleError("invalid curve parameters or layout")
     if rc != 0:
         raise OracleError("NaN or +inf logit")
     return out, best, second
@@ -237,7 +255,8 @@ def filter_threshold(x, T, top_k=None, top_p=None):
     return tau, amb.astype(bool)
 
 
-def sample_filtered(x, T, seed, offset, K: int = 1, top_k=None, top_p=None, row_id=None):
+def sample_filtered(x, T, seed, offset, K: int = 1, top_k=None, top_p=None, row_id=None,
+                    layout="plain"):
     """Gumbel-max draws over the tokens top-k / top-p keep (curve off): ids [n, K], the best and
     second-best scores, and the threshold and ambiguity flag of every row."""
     x = _as_f64_rows(x)
@@ -253,7 +272,9 @@ def sample_filtered(x, T, seed, offset, K: int = 1, top_k=None, top_p=None, row_
     tau = np.zeros(n, dtype=np.float64)
     amb = np.zeros(n, dtype=np.int32)
     rc = lib().or_sample_filtered(x, n, V, V, rid, T, k, p, seed, offset, int(K), out, best,
-                                  second, tau, amb)
+                                  second, tau, amb, _layout(layout))
+    if rc == -2:
+        raise OracleError("invalid layout")
     if rc != 0:
         raise OracleError("NaN or +inf logit")
     return out, best, second, tau, amb.astype(bool)

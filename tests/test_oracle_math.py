@@ -183,6 +183,19 @@ def test_logsumexp_closed_forms(oracle_mod):
                                                                rel=1e-14)
 
 
+def test_logsumexp_is_compensated(oracle_mod):
+    """One term of 1 beside 10^6 terms of exp(-40) ~ 4.25e-18: each tiny term is below half an
+    ulp of the running sum, so a plain double sum stays exactly 1 and gives LSE = 0. The
+    compensated sum keeps them: LSE = log1p(10^6 exp(-40)) (closed form)."""
+    n = 1_000_000
+    x = np.full((1, n + 1), -40.0)
+    x[0, 0] = 0.0
+    want = math.log1p(n * math.exp(-40.0))
+    got = oracle_mod.logsumexp(x)[0]
+    assert got == pytest.approx(want, rel=1e-9)
+    assert got > 0.0
+
+
 def test_transform_is_curve_of_centred_logprob(oracle_mod):
     """l' = g(l - mu), l = x - LSE(x): checked against scipy's log-softmax and the
     pivot/knot identities; masked entries stay -inf."""

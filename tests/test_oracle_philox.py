@@ -133,6 +133,62 @@ def test_stream_words_vector(oracle_mod):
     assert not np.array_equal(w, oracle_mod.stream_words(seed ^ (1 << 40), row, off, V))
 
 
+def _py_screened(seed, row, off, i):
+    """Element i = 8q + e of the screened layout, from the pure-Python Philox: the high half of
+    its word is the 16-bit half e of the call at counter word 2q, the low half that of the call
+    at 2q + 1 (half e of an output = word e // 2, low bits for even e, high bits for odd e)."""
+    q, e = i // 8, i % 8
+    key = (seed & M32, seed >> 32)
+    hi = py_philox((2 * q, row, off & M32, off >> 32), key)
+    lo = py_philox((2 * q + 1, row, off & M32, off >> 32), key)
+
+    def half(words):
+        return (words[e // 2] >> (16 * (e % 2))) & 0xFFFF
+    return (half(hi) << 16) | half(lo)
+
+
+SCREENED_CASES = [
+    (0, 0, 0, 0), (0, 0, 0, 7), (0, 0, 0, 8), (1, 2, 3, 13),
+    (0xDEADBEEFCAFEF00D, 7, 0xFFFFFFFF, 151935),
+    (0x0123456789ABCDEF, 255, 0x100000000, 262143),
+    (2**64 - 1, 1023, 2**64 - 1, 17),
+]
+
+
+@pytest.mark.parametrize("seed,row,off,i", SCREENED_CASES)
+def test_screened_layout_pure_python(oracle_mod, seed, row, off, i):
+    assert oracle_mod.element_word(seed, row, off, i, "screened") == \
+        _py_screened(seed, row, off, i)
+
+
+def test_screened_layout_recombines_plain_words(oracle_mod):
+    """The screened layout draws on the same Philox calls as the plain one and only hands their
+    bits out differently: with P the plain words of a stream, element 8q + e of the screened
+    layout is (half e%2 of P[8q + e//2]) << 16 | (half e%2 of P[8q + 4 + e//2]). Checked on
+    whole streams, ragged tails included."""
+    for seed, row, off, V in [(42, 0, 0, 4096), (0x9E3779B97F4A7C15, 5, 2**32 - 2, 1003),
+                              (7, 1023, 2**63 + 5, 27)]:
+        plain = oracle_mod.stream_words(seed, row, off, (V + 7) // 8 * 8).astype(np.uint64)
+        scr = oracle_mod.stream_words(seed, row, off, V, "screened").astype(np.uint64)
+        i = np.arange(V)
+        q, e = i // 8, i % 8
+        shift = (16 * (e % 2)).astype(np.uint64)
+        hi = (plain[8 * q + e // 2] >> shift) & 0xFFFF
+        lo = (plain[8 * q + 4 + e // 2] >> shift) & 0xFFFF
+        np.testing.assert_array_equal(scr, (hi << 16) | lo)
+
+
+def test_screened_words_look_uniform(oracle_mod):
+    """Every bit of the screened words is set about half the time, and their leading bytes
+    fill 256 buckets evenly."""
+    w = oracle_mod.stream_words(42, 3, 9, 1 << 16, "screened")
+    bits = ((w[:, None] >> np.arange(32, dtype=np.uint32)) & 1).mean(axis=0)
+    assert np.all(np.abs(bits - 0.5) < 0.01)   # sd of a bit's mean ~0.002
+    counts = np.bincount((w >> 24).astype(np.int64), minlength=256)
+    exp = (1 << 16) / 256
+    assert ((counts - exp) ** 2 / exp).sum() < 400
+
+
 def test_words_look_uniform(oracle_mod):
     """Coarse sanity: 2^16 words of one stream fill 256 byte-buckets evenly."""
     w = oracle_mod.stream_words(42, 0, 0, 1 << 16)

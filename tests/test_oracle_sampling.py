@@ -64,6 +64,8 @@ def test_chi_square_linspace(oracle_mod, T):
     assert p > 1e-3, p
 
 
+# fixed seed per shape (a salted str hash would change the logits from run to run)
+SHAPE_SEEDS = {"bimodal": 301, "flat": 302, "masked": 303, "peaked": 304}
 SHAPES = {
     "peaked": lambda rng: np.concatenate([rng.normal(0, 1, 11), [6.0]]),
     "flat": lambda rng: rng.normal(0, 0.1, 12),
@@ -75,7 +77,7 @@ SHAPES = {
 @pytest.mark.parametrize("shape", sorted(SHAPES))
 @pytest.mark.parametrize("T", [0.5, 1.5])
 def test_chi_square_shapes(oracle_mod, shape, T):
-    rng = np.random.default_rng(hash(shape) % 1000)
+    rng = np.random.default_rng(SHAPE_SEEDS[shape])
     x = SHAPES[shape](rng)
     n = 200_000
     idx, _, _ = oracle_mod.sample(x[None, :], [T], [77], [5], K=n)
@@ -83,6 +85,28 @@ def test_chi_square_shapes(oracle_mod, shape, T):
     probs = _softmax(x / T)
     assert np.all(counts[~np.isfinite(x)] == 0)
     assert _chi2_pvalue(counts, probs, n) > 1e-3
+
+
+@pytest.mark.parametrize("T", [0.5, 1.0, 1.5])
+def test_chi_square_screened_layout(oracle_mod, T):
+    """The screened word layout samples the same law: 1e6 draws of linspace(-4, 4) at T against
+    exact softmax (cells with expected count < 5 pooled, reject at p < 1e-3)."""
+    x = np.linspace(-4.0, 4.0, 16)
+    idx, _, _ = oracle_mod.sample(x[None, :], [T], [0xBADC0DE + int(10 * T)], [0], K=N_DRAWS,
+                                  layout="screened")
+    counts = np.bincount(idx.ravel(), minlength=16)
+    assert _chi2_pvalue(counts, _softmax(x / T), N_DRAWS) > 1e-3
+
+
+@pytest.mark.parametrize("shape", sorted(SHAPES))
+def test_chi_square_shapes_screened(oracle_mod, shape):
+    rng = np.random.default_rng(SHAPE_SEEDS[shape])
+    x = SHAPES[shape](rng)
+    n = 200_000
+    idx, _, _ = oracle_mod.sample(x[None, :], [1.0], [78], [5], K=n, layout="screened")
+    counts = np.bincount(idx.ravel(), minlength=x.size)
+    assert np.all(counts[~np.isfinite(x)] == 0)
+    assert _chi2_pvalue(counts, _softmax(x), n) > 1e-3
 
 
 @pytest.mark.parametrize("T", [0.5, 1.5])
