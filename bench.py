@@ -27,12 +27,13 @@ sys.path.insert(0, ROOT)
 METRIC = ("sampled rows/sec and achieved HBM GB/s (% of peak) for [B,V] logits → token "
           "ids")
 HBM_PEAK_GBPS = 8000.0
-# VALU lane-operations per second of MI355X: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.
+# VALU lane-operations per second of MI355X at its nominal clock: 256 CUs x 4 SIMDs x 16 lanes
+# x 2.4 GHz (no packed fp32). Reported beside the HBM roofline, not as it.
 ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
-# Algorithmic VALU operations per element and draw (the work the method itself needs):
-# Philox4x32-10 share 10 (10 rounds x 2 mul-hi/lo + 2 three-way xor, per 4 words),
-# upcast 1, compare 1; plus, once per element with the curve on, the log-sum-exp's
-# max / exponent-argument / exp / add (4).
+# An algorithmic count of VALU operations per element and draw, for context only (the
+# measured VALU-busy fraction comes from the SQ counters): Philox4x32-10 share 10 (10 rounds x
+# 2 mul-hi/lo + 2 three-way xor, per 4 words), upcast 1, compare 1; plus, once per element
+# with the curve on, the log-sum-exp's max / exponent-argument / exp / add (4).
 OPS_PER_ELEMENT_DRAW = 12
 OPS_PER_ELEMENT_LSE = 4
 
@@ -46,7 +47,8 @@ def kernel_source_digest() -> str:
     profile stays valid across edits of the comments only)."""
     import re
     h = hashlib.sha256()
-    for f in ("hs_kernels.hip", "hs_kernels_pivot.hip", "hs_kernels_rows.hip",
+    for f in ("hs_kernels.hip", "hs_kernels_scr.hip", "hs_kernels_pivot.hip",
+              "hs_kernels_pivot_scr.hip", "hs_kernels_rows.hip", "hs_kernels_rows_scr.hip",
               "hs_sample_kernel.hpp", "hs_device.hpp", "hs_api.hip", "hs_internal.hpp"):
         with open(os.path.join(ROOT, "logit_transform_amd", "csrc", f)) as fh:
             text = fh.read()
@@ -57,10 +59,10 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(name: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
-    the current kernel sources."""
-    p = os.path.join(ROOT, "profiles", "traffic_%s.json" % name)
+def load_profile(kind: str, name: str):
+    """A committed rocprofv3 counter summary (profiles/<kind>_<name>.json), if it was taken on
+    the current kernel sources; None otherwise."""
+    p = os.path.join(ROOT, "profiles", "%s_%s.json" % (kind, name))
     if not os.path.exists(p):
         return None
     try:
@@ -70,10 +72,16 @@ def load_traffic(name: str):
         return None
     if d.get("source_digest") != kernel_source_digest():
         return None
-    return d.get("hbm_bytes_per_launch")
+    return d
 
 
-def cpu_baseline(w, budget_s: float = 10.0, settings=None, filters=None):
+def load_traffic(name: str):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary."""
+    d = load_profile("traffic", name)
+    return None if d is None else d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float = 10.0, settings=None, filters=None, layout="plain"):
     """The oracle as it stands, all host cores, on the workload's rows: a first timed pass sizes
     the sample (the first rows, or whole passes over all rows repeated until about budget_s of
     work), then the sample is timed. Rows per second of the whole sample are reported."""
@@ -87,11 +95,11 @@ def cpu_baseline(w, budget_s: float = 10.0, settings=None, filters=None):
     def run(rows):
         if filters is not None:
             O.sample_filtered(w.logits[:rows], w.T[:rows], w.seed[:rows], w.offset[:rows],
-                              K=w.K, top_k=filters[0], top_p=filters[1])
+                              K=w.K, top_k=filters[0], top_p=filters[1], layout=layout)
             return
         if settings is None:
             O.sample(w.logits[:rows], w.T[:rows], w.seed[:rows], w.offset[:rows], K=w.K,
-                     mu=None if w.hlg is None else w.mu[:rows], hlg=w.hlg)
+                     mu=None if w.hlg is None else w.mu[:rows], hlg=w.hlg, layout=layout)
             return
         # the curve set per row: the oracle samples each row with its own setting
         import numpy as np
@@ -99,7 +107,7 @@ def cpu_baseline(w, budget_s: float = 10.0, settings=None, filters=None):
             h = settings[r]
             O.sample(w.logits[r:r + 1], w.T[r:r + 1], w.seed[r:r + 1], w.offset[r:r + 1],
                      K=w.K, mu=w.mu[r:r + 1] if h is not None and "pivot" not in h else None,
-                     hlg=h, row_id=np.array([r], dtype=np.int64))
+                     hlg=h, row_id=np.array([r], dtype=np.int64), layout=layout)
 
     run(n)   # first call: library and thread-pool start-up, untimed
     t0 = time.perf_counter()
@@ -132,7 +140,7 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def oracle_one_thread(cfg: int, rows: int) -> None:
+def oracle_one_thread(cfg: int, rows: int, layout: str = "plain") -> None:
     """Child process (OMP_NUM_THREADS=1, no GPU): the oracle on the first rows of a workload;
     prints rows/s as JSON."""
     from oracle import oracle as O
@@ -141,7 +149,7 @@ def oracle_one_thread(cfg: int, rows: int) -> None:
     O.lib()
     def run():
         O.sample(w.logits[:rows], w.T[:rows], w.seed[:rows], w.offset[:rows], K=w.K,
-                 mu=None if w.hlg is None else w.mu[:rows], hlg=w.hlg)
+                 mu=None if w.hlg is None else w.mu[:rows], hlg=w.hlg, layout=layout)
     run()
     t0 = time.perf_counter()
     run()
@@ -149,11 +157,11 @@ def oracle_one_thread(cfg: int, rows: int) -> None:
     print(json.dumps({"rows_per_s": rows / dt, "rows": rows, "seconds": dt}), flush=True)
 
 
-def cpu_one_thread(cfg: int, rows: int):
+def cpu_one_thread(cfg: int, rows: int, layout: str = "plain"):
     import subprocess
     env = dict(os.environ, OMP_NUM_THREADS="1")
     r = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-one-thread",
-                        str(cfg), str(rows)], env=env, capture_output=True, text=True,
+                        str(cfg), str(rows), layout], env=env, capture_output=True, text=True,
                        timeout=300)
     if r.returncode != 0:
         return {"error": r.stderr.strip()[-200:]}
@@ -161,8 +169,8 @@ def cpu_one_thread(cfg: int, rows: int):
 
 
 def main():
-    if len(sys.argv) == 4 and sys.argv[1] == "--oracle-one-thread":
-        oracle_one_thread(int(sys.argv[2]), int(sys.argv[3]))
+    if len(sys.argv) == 5 and sys.argv[1] == "--oracle-one-thread":
+        oracle_one_thread(int(sys.argv[2]), int(sys.argv[3]), sys.argv[4])
         return
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -190,6 +198,10 @@ def main():
                     help="top-k filter on every row (turns the curve off; 0 = none)")
     ap.add_argument("--top-p", type=float, default=1.0,
                     help="top-p filter on every row (turns the curve off; 1 = none)")
+    ap.add_argument("--layout", choices=("plain", "screened"), default="plain",
+                    help="word layout of the random stream: plain (element i takes word i & 3 "
+                         "of the Philox call at counter word i >> 2) or screened (the leading 16 "
+                         "bits of eight elements come from one call)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain device copy of MIB MiB five "
                          "times (reference for scaling the memory-traffic counters)")
@@ -265,24 +277,31 @@ def main():
 
     topk_t = torch.full((B,), args.top_k, dtype=torch.int32, device=dev)
     topp_t = torch.full((B,), args.top_p, dtype=torch.float32, device=dev)
+    # the plain layout runs through hs_sample itself; the screened one needs hs_sample_ex
+    opts = hs.SampleOpts(layout=hs.LAYOUTS[args.layout])
+    opts_ref = C.byref(opts)
 
     def launch(i, s_):
         if filtered:
             rc = L.hs_sample_filtered(C.byref(structs[i % len(structs)]), T.data_ptr(),
                                       topk_t.data_ptr(), topp_t.data_ptr(), seed.data_ptr(),
                                       off.data_ptr(), K, out.data_ptr(), None, ws.data_ptr(),
-                                      ws.numel(), None, s_)
+                                      ws.numel(), opts_ref, s_)
             if rc != 0:
                 raise hs.HsError(rc, "hs_sample_filtered")
             return
         if rows is not None:
             rc = L.hs_sample_rows(C.byref(structs[i % len(structs)]), T.data_ptr(), mu_ptr,
                                   rows.data_ptr(), seed.data_ptr(), off.data_ptr(), K,
-                                  out.data_ptr(), None, ws.data_ptr(), ws.numel(), None, s_)
-        else:
+                                  out.data_ptr(), None, ws.data_ptr(), ws.numel(), opts_ref, s_)
+        elif args.layout == "plain":
             rc = L.hs_sample(C.byref(structs[i % len(structs)]), T.data_ptr(), mu_ptr, hp_ref,
                              seed.data_ptr(), off.data_ptr(), K, out.data_ptr(), ws.data_ptr(),
                              ws.numel(), s_)
+        else:
+            rc = L.hs_sample_ex(C.byref(structs[i % len(structs)]), T.data_ptr(), mu_ptr,
+                                hp_ref, seed.data_ptr(), off.data_ptr(), K, out.data_ptr(),
+                                None, ws.data_ptr(), ws.numel(), opts_ref, s_)
         if rc != 0:
             raise hs.HsError(rc, "hs_sample_rows" if rows is not None else "hs_sample")
 
@@ -388,6 +407,7 @@ def main():
         M = C.CDLL(os.path.join(ROOT, "logit_transform_amd", "libhs_micro.so"))
         M.hs_micro_stream_max.argtypes = [C.c_void_p, C.c_int32, C.c_int64, C.c_int64,
                                           C.c_int64, C.c_void_p, C.c_void_p]
+        M.hs_micro_stream_max_nt.argtypes = M.hs_micro_stream_max.argtypes
         M.hs_micro_philox_max.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_int32,
                                           C.c_int32, C.c_void_p, C.c_void_p]
         groups = max(1, min(K, -(-2048 // B)))   # spread the draws over about 2048 blocks
@@ -396,12 +416,14 @@ def main():
         words = torch.empty(B * groups * 1024, dtype=torch.int32, device=dev)
         ceilings = {}
 
-        def read_one(i, s_):
+        def read_one(i, s_, fn=M.hs_micro_stream_max):
             x = copies[i % len(copies)]
-            rc = M.hs_micro_stream_max(x.data_ptr(), hs._DTYPES[x.dtype], B, V, x.stride(0),
-                                       rowmax.data_ptr(), s_)
+            rc = fn(x.data_ptr(), hs._DTYPES[x.dtype], B, V, x.stride(0), rowmax.data_ptr(), s_)
             if rc != 0:
                 raise RuntimeError("hs_micro_stream_max: %d" % rc)
+
+        def read_one_nt(i, s_):
+            read_one(i, s_, M.hs_micro_stream_max_nt)
 
         def philox_one(i, s_):
             rc = M.hs_micro_philox_max(seed.data_ptr(), B, V, K, groups, words.data_ptr(), s_)
@@ -412,8 +434,17 @@ def main():
             st_ms = graph_ms(read_one, n_c)
             st_gbps = B * V * esz / (st_ms / 1e3) / 1e9
             ceilings["stream_read"] = {"ms": st_ms, "GB/s": st_gbps,
-                                       "frac_of_peak": st_gbps / HBM_PEAK_GBPS}
-            ceilings["kernel_frac_of_stream_read"] = B * V * esz / (kern_ms / 1e3) / 1e9 / st_gbps
+                                       "frac_of_peak": st_gbps / HBM_PEAK_GBPS,
+                                       "pattern": "one 1024-thread block per row, 16-byte loads, "
+                                                  "8 in flight per lane"}
+            nt_ms = graph_ms(read_one_nt, n_c)
+            nt_gbps = B * V * esz / (nt_ms / 1e3) / 1e9
+            ceilings["stream_read_nt"] = {"ms": nt_ms, "GB/s": nt_gbps,
+                                          "frac_of_peak": nt_gbps / HBM_PEAK_GBPS,
+                                          "pattern": "the same with non-temporal loads, 4 in "
+                                                     "flight per lane (best read measured)"}
+            best_gbps = max(st_gbps, nt_gbps)
+            ceilings["kernel_frac_of_stream_read"] = B * V * esz / (kern_ms / 1e3) / 1e9 / best_gbps
         if V % 4 == 0:
             ph_ms = graph_ms(philox_one, min(n_c, 50))
             ceilings["philox"] = {"ms": ph_ms, "words_per_s": B * V * K / (ph_ms / 1e3),
@@ -432,6 +463,8 @@ def main():
     ops = B * V * (OPS_PER_ELEMENT_DRAW * K + (OPS_PER_ELEMENT_LSE if lse_on else 0))
     tops = ops / (kern_ms / 1e3) / 1e12
     name = "k_sample_c%d" % args.config
+    if args.layout != "plain":
+        name += "_" + args.layout
     if args.pivot != "input" and w.hlg is not None:
         name += "_" + args.pivot
     if rows is not None:
@@ -443,8 +476,9 @@ def main():
         "pairs p10 %.4f p50 %.4f p90 %.4f ms"
         % (ms_per_step, (wall1 - wall0) * 1e3 / args.steps, per_launch[len(per_launch) // 10],
            per_launch[len(per_launch) // 2], per_launch[(9 * len(per_launch)) // 10]))
-    log("HBM %.1f GB/s = %.1f%% of 8 TB/s; VALU %.2f T op/s = %.1f%% of %.1f"
-        % (gbps, 100 * gbps / HBM_PEAK_GBPS, tops, 100 * tops / ALU_PEAK_TOPS, ALU_PEAK_TOPS))
+    log("HBM %.1f GB/s = %.1f%% of 8 TB/s (algorithmic bytes over the kernel time)"
+        % (gbps, 100 * gbps / HBM_PEAK_GBPS))
+    sq = load_profile("valu", name)
 
     rec = {
         "metric": METRIC,
@@ -459,7 +493,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "B": B, "V": V, "K": K,
+        "config": {"workload": w.name + ", %s word layout" % args.layout, "B": B, "V": V,
+                   "K": K, "layout": args.layout,
                    "input_dtype": str(w.dtype).replace("torch.", ""),
                    "hlg": w.hlg is not None, "input_copies": len(copies),
                    "pivot": (None if w.hlg is None else
@@ -468,13 +503,19 @@ def main():
                    "top_p": args.top_p if filtered else None,
                    "launch": "hip_graph" if graph is not None else "eager",
                    "algorithmic_bytes_per_step": alg_bytes},
-        "roofline": {"bound": "alu", "achieved": tops, "peak": ALU_PEAK_TOPS,
-                     "unit": "T VALU-op/s", "frac": tops / ALU_PEAK_TOPS, "traffic": traffic,
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": name, "kernel_ms": kern_ms,
-                     "launch_pair_ms_p50": per_launch[len(per_launch) // 2],
-                     "ops_per_step": ops},
-        "hbm": {"achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": gbps / HBM_PEAK_GBPS},
+                     "algorithmic_bytes": alg_bytes,
+                     "launch_pair_ms_p50": per_launch[len(per_launch) // 2]},
+        # The kernel is limited by its VALU issue rate, not by HBM. The busy fraction comes from
+        # the committed SQ counters (SQ_ACTIVE_INST_VALU / (SQ_WAVE_CYCLES / 4) summed over the
+        # dispatch, null when they were taken on other kernel sources); the operation count is
+        # the algorithmic one above, at the nominal 2.4 GHz, for context.
+        "valu": {"busy_frac": None if sq is None else sq.get("valu_busy_frac"),
+                 "insts_per_wave": None if sq is None else sq.get("valu_insts_per_wave"),
+                 "algorithmic_ops_per_step": ops, "algorithmic_T_ops_per_s": tops,
+                 "nominal_peak_T_ops_per_s": ALU_PEAK_TOPS},
         "launch_ms": {"p10": per_launch[len(per_launch) // 10],
                       "p50": per_launch[len(per_launch) // 2],
                       "p90": per_launch[(9 * len(per_launch)) // 10],
@@ -488,11 +529,12 @@ def main():
         rec["ceilings"] = ceilings
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(
-            w, settings=settings, filters=(args.top_k, args.top_p) if filtered else None)
+            w, settings=settings, filters=(args.top_k, args.top_p) if filtered else None,
+            layout=args.layout)
         rec["cpu_baseline"]["cpu_model"] = cpu_model()
         if settings is None and args.pivot == "input" and not filtered:
-            rec["cpu_baseline"]["one_thread"] = cpu_one_thread(args.config,
-                                                               1 if args.config == 5 else 16)
+            rec["cpu_baseline"]["one_thread"] = cpu_one_thread(
+                args.config, 1 if args.config == 5 else 16, args.layout)
         log("cpu baseline:", rec["cpu_baseline"])
     print(json.dumps(rec), flush=True)
 

@@ -50,7 +50,8 @@ typedef struct {
     const void *data;   /* device pointer, row-major, row stride ld elements */
     int32_t dtype;      /* hs_dtype */
     int64_t B;          /* rows (batch) */
-    int64_t V;          /* vocabulary size, 1 <= V < 2^31 */
+    int64_t V;          /* vocabulary size, 1 <= V < 2^31 and V * element size < 2^32 bytes
+                           (fp32 rows below 2^30 elements); larger rows: HS_ERR_UNSUPPORTED */
     int64_t ld;         /* row stride in elements, ld >= V */
 } hs_logits;
 
@@ -107,8 +108,10 @@ int hs_hlg_pivot(const hs_logits *x, const float *mu, const hs_hlg_params *p, fl
  * G(r) = -log(-log(u)), u = (r + 1/2) 2^-32, word = Philox4x32-10 [P123] with
  * key = (seed lo, seed hi), counter = (i >> 2, b, off lo, off hi), output word i & 3.
  * Ties go to the lowest index; -inf entries are never chosen [GMX, Regression guard].
- * Per-row results: -1 if the row has no finite entry, -2 if T[b] < 0 or not finite.
- * T[b] == 0 is greedy: argmax of x, the same index for all K draws.
+ * Per-row results: -1 if the row has no finite entry, -2 if T[b] is negative, NaN,
+ * infinite or subnormal (0 < T[b] < 2^-126, where 1/T overflows fp32). T[b] == 0 is greedy:
+ * argmax of x, the same index for all K draws. Scores x/T (l'/T with the curve) must stay
+ * inside the fp32 range; a row where they overflow has an undefined result.
  * T: device float[B]; seed, offset: device uint64[B]; out: device int32[B*K].
  * ws / ws_bytes: device workspace of at least hs_workspace_bytes(B, V, K, dtype, 0) bytes,
  * zero-filled before its first use (hs_workspace_init); every successful call leaves its
@@ -157,7 +160,21 @@ size_t hs_workspace_bytes(int64_t B, int64_t V, int32_t K, int32_t dtype, int32_
 /* Zero-fills a workspace on `stream` with a fill kernel (graph-capture safe). */
 int hs_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
-/* Tuning / test control for hs_sample_ex. Zero-initialised = automatic choices. */
+/* Word layouts of the random stream (seed, row, i, offset) [GMX, Background: counter-based
+ * Philox keyed on seed and offset]. Both hand out the bits of the same Philox4x32-10 calls
+ * (counter (c, row, off lo, off hi), key (seed lo, seed hi)):
+ *   HS_LAYOUT_PLAIN:    element i takes output word i & 3 of the call at c = i >> 2;
+ *   HS_LAYOUT_SCREENED: element i = 8q + e takes the 16-bit half e (word e >> 1, low bits
+ *                       for even e) of the call at c = 2q as the high half of its word and
+ *                       the half e of the call at c = 2q + 1 as the low half.
+ * Every element's word is uniform on 32 bits either way, so both give exact samples. The
+ * screened layout lets the samplers draw one call per eight elements for most of the row: the
+ * leading 16 bits bound each element's Gumbel value, and only the few elements those bounds
+ * cannot rule out need the second call. */
+typedef enum { HS_LAYOUT_PLAIN = 0, HS_LAYOUT_SCREENED = 1 } hs_layout;
+
+/* Tuning / test control for hs_sample_ex. Zero-initialised = automatic choices and the plain
+ * word layout. */
 typedef struct {
     int32_t variant;     /* 0 automatic, 1 one block per row, 2 split the row over blocks */
     int32_t nchunk;      /* blocks per row when split (0 = automatic)                      */
@@ -170,6 +187,12 @@ typedef struct {
     int32_t exchange_wait; /* polls for the other chunks' partials before a block works
                               them out itself: 0 default, -1 none (test control), > 0 that
                               many                                                         */
+    int32_t median_rows;   /* hs_sample_rows only: 1 = some row may ask for the mass-median
+                              pivot, so a first kernel works out those rows' shifts (it needs
+                              the workspace); 0 = no row does, nothing runs before the
+                              sampler, and a row that asks for it anyway gives -2           */
+    int32_t layout;        /* word layout of the random stream (hs_layout); the ids differ
+                              between layouts, each an exact sample                         */
 } hs_sample_opts;
 
 /* hs_sample with explicit kernel choices. best (device float[B*K] or NULL) receives the
@@ -195,8 +218,8 @@ int hs_sample_plan(const hs_logits *x, int32_t K, int32_t hlg_on, int32_t have_w
  * validated in the kernel: a row whose enabled curve has an invalid knob (the rules of
  * hs_hlg_params), an unknown pivot, a non-finite top offset or a non-zero reserved field gives
  * -2, as does a given-pivot row whose mu is not finite or whose mu array is NULL, and a
- * median-pivot row when ws is NULL (the rows' median shifts are worked out into the
- * workspace by a first kernel, which skips every other row). mu: device
+ * median-pivot row unless opts->median_rows is 1 and ws is given (the rows' median shifts are
+ * worked out into the workspace by a first kernel, which skips every other row). mu: device
  * float[B] or NULL (read only for enabled rows with HS_PIVOT_GIVEN); rows: device
  * hs_hlg_row[B]. Ids and scores of a row are bit-identical to hs_sample_ex's for that row's
  * setting. The workspace size is hs_workspace_bytes(B, V, K, dtype, 1). best and opts as
@@ -246,6 +269,10 @@ int hs_philox4x32_10(const uint32_t *ctr, const uint32_t *key, uint32_t *out, in
  * i, offset[b] + k) (layout as in hs_gumbel_argmax). out: device uint32[B*V]. */
 int hs_stream_words(const uint64_t *seed, const uint64_t *offset, int64_t B, int64_t V,
                     int32_t k, uint32_t *out, void *stream);
+
+/* The same in a given word layout (hs_layout). */
+int hs_stream_words_ex(const uint64_t *seed, const uint64_t *offset, int64_t B, int64_t V,
+                       int32_t k, int32_t layout, uint32_t *out, void *stream);
 
 /* The samplers' fp32 Gumbel map on n words: g[j] = G(words[j]). */
 int hs_gumbel_f32(const uint32_t *words, float *g, int64_t n, void *stream);

@@ -35,8 +35,10 @@ EXPORTED_SYMBOLS = (
     "hs_logsumexp", "hs_hlg_transform", "hs_hlg_pivot", "hs_gumbel_argmax", "hs_sample",
     "hs_sample_ex", "hs_sample_rows", "hs_filter_threshold", "hs_sample_filtered",
     "hs_workspace_bytes", "hs_workspace_init", "hs_sample_plan", "hs_philox4x32_10", "hs_stream_words",
-    "hs_gumbel_f32", "hs_status_str", "hs_version",
+    "hs_stream_words_ex", "hs_gumbel_f32", "hs_status_str", "hs_version",
 )
+# word layouts of the random stream (hs_layout)
+LAYOUTS = {"plain": 0, "screened": 1}
 
 
 class HsError(RuntimeError):
@@ -84,10 +86,13 @@ class SampleOpts(C.Structure):
     nchunk blocks per split row (0 auto); no_screen 1 = score every element exactly;
     draw_groups blocks sharing one row's draws (0 auto); split_lse for split rows with the
     curve on: 0 auto / 1 log-sum-exp pre-pass / 2 partials exchanged inside the kernel;
-    exchange_wait polls for the other chunks' partials (0 default, -1 none)."""
+    exchange_wait polls for the other chunks' partials (0 default, -1 none); median_rows (per-row
+    settings only) 1 = some row may ask for the mass-median pivot; layout the word layout of
+    the random stream (0 plain, 1 screened)."""
     _fields_ = [("variant", C.c_int32), ("nchunk", C.c_int32), ("no_screen", C.c_int32),
                 ("draw_groups", C.c_int32), ("split_lse", C.c_int32),
-                ("exchange_wait", C.c_int32)]
+                ("exchange_wait", C.c_int32), ("median_rows", C.c_int32),
+                ("layout", C.c_int32)]
 
 
 _lib = None
@@ -126,6 +131,7 @@ def load() -> C.CDLL:
     L.hs_sample_plan.restype = C.c_int
     L.hs_philox4x32_10.argtypes = [vp, vp, vp, i64, vp]
     L.hs_stream_words.argtypes = [vp, vp, i64, i64, i32, vp, vp]
+    L.hs_stream_words_ex.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp]
     L.hs_gumbel_f32.argtypes = [vp, vp, i64, vp]
     L.hs_status_str.argtypes = [C.c_int]
     L.hs_status_str.restype = C.c_char_p
@@ -134,7 +140,7 @@ def load() -> C.CDLL:
     for name in ("hs_logsumexp", "hs_hlg_transform", "hs_hlg_pivot", "hs_gumbel_argmax", "hs_sample",
                  "hs_sample_ex", "hs_sample_rows", "hs_filter_threshold", "hs_sample_filtered",
                  "hs_workspace_init", "hs_philox4x32_10", "hs_stream_words",
-                 "hs_gumbel_f32"):
+                 "hs_stream_words_ex", "hs_gumbel_f32"):
         getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -480,15 +486,18 @@ def philox4x32_10(ctr: torch.Tensor, key: torch.Tensor) -> torch.Tensor:
     return out
 
 
-def stream_words(seed, offset, B: int, V: int, k: int = 0, device="cuda") -> torch.Tensor:
-    """The samplers' random words for draw k: int32 [B, V] (uint32 bit patterns)."""
+def stream_words(seed, offset, B: int, V: int, k: int = 0, device="cuda",
+                 layout="plain") -> torch.Tensor:
+    """The samplers' random words for draw k in a word layout ("plain" or "screened"): int32
+    [B, V] (uint32 bit patterns)."""
     L = load()
     dev = torch.device(device)
     st = _row_vec(seed, B, torch.int64, dev, "seed")
     of = _row_vec(offset, B, torch.int64, dev, "offset")
     out = torch.empty((B, V), dtype=torch.int32, device=dev)
-    _check(L.hs_stream_words(st.data_ptr(), of.data_ptr(), B, V, int(k), out.data_ptr(),
-                             _stream(dev)), "hs_stream_words")
+    lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    _check(L.hs_stream_words_ex(st.data_ptr(), of.data_ptr(), B, V, int(k), lay,
+                                out.data_ptr(), _stream(dev)), "hs_stream_words_ex")
     return out
 
 

@@ -16,8 +16,9 @@ LIB = os.path.join(HERE, "libhs.so")
 # The benchmark's ceilings (plain streaming read, Philox word rate): a library of its own.
 MICRO_LIB = os.path.join(HERE, "libhs_micro.so")
 MICRO_SOURCE = os.path.join("micro", "hs_micro.hip")
-SOURCES = ["hs_kernels.hip", "hs_kernels_pivot.hip", "hs_kernels_rows.hip", "hs_filter.hip",
-           "hs_api.hip"]
+SOURCES = ["hs_kernels.hip", "hs_kernels_scr.hip", "hs_kernels_pivot.hip",
+           "hs_kernels_pivot_scr.hip", "hs_kernels_rows.hip", "hs_kernels_rows_scr.hip",
+           "hs_filter.hip", "hs_api.hip"]
 HEADERS = ["hs_device.hpp", "hs_internal.hpp", "hs_sample_kernel.hpp"]
 ARCH = os.environ.get("HS_OFFLOAD_ARCH", "gfx950")
 

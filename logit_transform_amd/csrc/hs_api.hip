@@ -28,6 +28,9 @@ int check_logits(const hs_logits *x) {
     if (x->dtype != HS_F32 && x->dtype != HS_BF16 && x->dtype != HS_F16) return HS_ERR_DTYPE;
     if (x->B < 1 || x->V < 1 || x->ld < x->V) return HS_ERR_INVALID_ARG;
     if (x->V >= ((int64_t)1 << 31) || x->B >= ((int64_t)1 << 31)) return HS_ERR_UNSUPPORTED;
+    // the kernels form byte offsets within a row in 32 bits: a row must stay below 4 GiB
+    if ((uint64_t)x->V * (uint64_t)esize_of(x->dtype) >= ((uint64_t)1 << 32))
+        return HS_ERR_UNSUPPORTED;
     return HS_OK;
 }
 
@@ -174,9 +177,10 @@ int make_plan(const hs_logits *x, int32_t K, bool hlg, bool ws_ok, const hs_samp
 }
 
 bool opts_valid(const hs_sample_opts *o) {
-    return !o || !(o->variant < 0 || o->variant > 2 || o->nchunk < 0 ||
+    return !o || !(o->layout < 0 || o->layout > 1 || o->variant < 0 || o->variant > 2 || o->nchunk < 0 ||
                    o->nchunk > hs::kMaxChunks || o->draw_groups < 0 || o->split_lse < 0 ||
-                   o->split_lse > 2 || o->exchange_wait < -1);
+                   o->split_lse > 2 || o->exchange_wait < -1 || o->median_rows < 0 ||
+                   o->median_rows > 1);
 }
 
 // Top-k / top-p parameters of a filtered call (device arrays, either may be null).
@@ -228,6 +232,7 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
     a.K = K;
     a.aligned = rows_aligned(x) ? 1 : 0;
     a.no_screen = (opts && opts->no_screen) ? 1 : 0;
+    a.layout = opts ? opts->layout : HS_LAYOUT_PLAIN;
     a.T = T;
     // internal pivot codes: 0 given, 1 top, 2 entropy, 3 per row, 4 mass median
     const int piv = rows ? 3 : !hlg ? 0 : hlg->pivot == HS_PIVOT_MEDIAN ? 4 : hlg->pivot;
@@ -269,6 +274,7 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
             f.seed = seed;
             f.offset = offset;
             f.K = K;
+            f.layout = a.layout;
             a.done = f.done;
         }
         if (hs::launch_filter_tau(x->dtype, f, (int)x->B, s) != hipSuccess) return HS_ERR_HIP;
@@ -280,8 +286,9 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
     // The mass median: the threshold kernel's top-p selection at p = 0.5, T = 1 gives every
     // row's shift c before the sampling kernel runs (which then needs no log-sum-exp).
     // Per-row settings: the same for the rows whose record asks for the median (the others
-    // return at once); without a workspace such rows give -2.
-    if (piv == 4 || (piv == 3 && ws_ok)) {
+    // return at once), when the caller says some row may (opts->median_rows); otherwise, or
+    // without a workspace, such rows give -2.
+    if (piv == 4 || (piv == 3 && ws_ok && opts && opts->median_rows)) {
         if (!ws_ok) return HS_ERR_WORKSPACE;   // the shifts live in it
         hs::FilterArgs f{};
         f.data = x->data;
@@ -512,12 +519,19 @@ int hs_philox4x32_10(const uint32_t *ctr, const uint32_t *key, uint32_t *out, in
                    ? HS_OK : HS_ERR_HIP;
 }
 
+int hs_stream_words_ex(const uint64_t *seed, const uint64_t *offset, int64_t B, int64_t V,
+                       int32_t k, int32_t layout, uint32_t *out, void *stream) {
+    if (!seed || !offset || !out || B < 1 || V < 1 || k < 0) return HS_ERR_INVALID_ARG;
+    if (layout != HS_LAYOUT_PLAIN && layout != HS_LAYOUT_SCREENED) return HS_ERR_INVALID_ARG;
+    if (V >= ((int64_t)1 << 31) || B > 65535) return HS_ERR_UNSUPPORTED;
+    return hs::launch_stream_words(seed, offset, B, V, k, layout, out,
+                                   reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+                   ? HS_OK : HS_ERR_HIP;
+}
+
 int hs_stream_words(const uint64_t *seed, const uint64_t *offset, int64_t B, int64_t V,
                     int32_t k, uint32_t *out, void *stream) {
-    if (!seed || !offset || !out || B < 1 || V < 1 || k < 0) return HS_ERR_INVALID_ARG;
-    if (V >= ((int64_t)1 << 31) || B > 65535) return HS_ERR_UNSUPPORTED;
-    return hs::launch_stream_words(seed, offset, B, V, k, out, reinterpret_cast<hipStream_t>(stream))
-                   == hipSuccess ? HS_OK : HS_ERR_HIP;
+    return hs_stream_words_ex(seed, offset, B, V, k, HS_LAYOUT_PLAIN, out, stream);
 }
 
 int hs_gumbel_f32(const uint32_t *words, float *g, int64_t n, void *stream) {
@@ -540,6 +554,6 @@ const char *hs_status_str(int status) {
     return "unknown hs_status";
 }
 
-const char *hs_version(void) { return "libhs 0.1.0 (gfx950)"; }
+const char *hs_version(void) { return "libhs 0.2.0 (gfx950)"; }
 
 }  // extern "C"

@@ -123,6 +123,53 @@ __device__ __forceinline__ Words4 stream_group(const Stream &s, uint32_t q) {
     return philox4x32_10_uk(q, s.row, s.off_lo, s.off_hi, s.key0, s.key1);
 }
 
+// Word layouts of a stream. Plain: element i takes word i & 3 of the call at counter word
+// i >> 2. Screened: element i = 8q + e takes the 16-bit half e of the call at counter word 2q
+// as the high half of its word and that of the call at 2q + 1 as the low half (half e of an
+// output: word e >> 1, low bits for even e). The two layouts use the same calls; the screened
+// one puts the leading 16 bits of eight elements into one call, so a pass that only needs
+// those bits (to bound each element's Gumbel value) makes half the calls.
+enum : int { LAY_PLAIN = 0, LAY_SCREENED = 1 };
+
+__device__ __forceinline__ uint32_t half16(const Words4 &w, uint32_t e) {
+    const uint32_t d = (e >> 1) == 0 ? w.w[0] : (e >> 1) == 1 ? w.w[1] : (e >> 1) == 2 ? w.w[2] : w.w[3];
+    return (e & 1u) ? (d >> 16) : (d & 0xFFFFu);
+}
+
+// The word of element i of stream s in layout LAY (one element per lane; exports and the few
+// elements a threshold kernel draws).
+template <int LAY>
+__device__ __forceinline__ uint32_t element_word(const Stream &s, uint32_t i) {
+    if constexpr (LAY == LAY_PLAIN) {
+        const Words4 w = stream_group(s, i >> 2);
+        return (i & 2u) ? ((i & 1u) ? w.w[3] : w.w[2]) : ((i & 1u) ? w.w[1] : w.w[0]);
+    } else {
+        const uint32_t q2 = (i >> 3) << 1;
+        const Words4 hi = stream_group(s, q2);
+        const Words4 lo = stream_group(s, q2 | 1u);
+        return (half16(hi, i & 7u) << 16) | half16(lo, i & 7u);
+    }
+}
+
+// Packed 16-bit integer maxima of two words (low halves, high halves), and the largest of the
+// four 16-bit halves of two words.
+__device__ __forceinline__ uint32_t max_half16_pk(uint32_t a, uint32_t b) {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                  __builtin_bit_cast(u16x2, b)));
+}
+__device__ __forceinline__ uint32_t max_half16(uint32_t a, uint32_t b) {
+    const uint32_t m = max_half16_pk(a, b);
+    return max(m & 0xFFFFu, m >> 16);
+}
+
+// A row's temperature is usable when it is 0 (greedy) or a normal positive float below +inf:
+// then 1/T is finite in fp32. Negative, NaN, infinite and subnormal temperatures (where 1/T
+// overflows) make the row invalid (-2).
+__device__ __forceinline__ bool temp_valid(float T) {
+    return T == 0.0f || (T >= 0x1p-126f && T < __builtin_inff());
+}
+
 // ------------------------------------------------------------------------------------------
 // Accurate fp32 log1p(t) for t > -1 by the log(1+t) * t / ((1+t) - 1) correction (Goldberg,
 // "What every computer scientist should know about floating-point arithmetic", 1991): the

@@ -244,7 +244,7 @@ __device__ __forceinline__ bool row_filter(const FilterArgs &a, int64_t b, RowFi
     if ((int64_t)f->k >= a.V) f->k = 0;   // a k of at least V keeps every token
     f->p = a.top_p ? a.top_p[b] : 1.0f;
     float tau;
-    if (!(f->T >= 0.0f) || !(f->T < __builtin_inff()) || !(f->p > 0.0f)) {
+    if (!temp_valid(f->T) || !(f->p > 0.0f)) {
         tau = __builtin_nanf("");
     } else if (f->T == 0.0f || (f->k <= 0 && !(f->p < 1.0f))) {
         tau = -__builtin_inff();
@@ -516,11 +516,14 @@ __device__ __forceinline__ bool draw_kept(const FilterArgs &a, int64_t b, float 
         const uint32_t k = q / n, e = q - k * n;
         const uint32_t i = l_idx[e];
         const uint64_t off = off0 + (uint64_t)k;
-        const Words4 w = philox4x32_10_uk(i >> 2, (uint32_t)b, (uint32_t)off,
-                                          (uint32_t)(off >> 32), (uint32_t)seed,
-                                          (uint32_t)(seed >> 32));
-        const uint32_t r = (i & 2u) ? ((i & 1u) ? w.w[3] : w.w[2])
-                                    : ((i & 1u) ? w.w[1] : w.w[0]);
+        Stream st;
+        st.row = (uint32_t)b;
+        st.off_lo = (uint32_t)off;
+        st.off_hi = (uint32_t)(off >> 32);
+        st.key0 = (uint32_t)seed;
+        st.key1 = (uint32_t)(seed >> 32);
+        const uint32_t r = a.layout == LAY_SCREENED ? element_word<LAY_SCREENED>(st, i)
+                                                    : element_word<LAY_PLAIN>(st, i);
         const float sc = l_x[e] * invT + gumbel32(r);
         atomicMax(reinterpret_cast<unsigned long long *>(&l_key[k]),
                   (unsigned long long)make_key(sc, i));

@@ -60,6 +60,7 @@ struct SampleArgs {
     uint32_t *flags;              // [B * part_stride]: chunk partial published
     const uint32_t *done;         // [B] rows the threshold kernel has drawn (filters), else null
     const float *shift;           // [B] the curve's shift c per row (mass-median pivot), else null
+    int32_t layout;               // word layout of the random stream: LAY_PLAIN / LAY_SCREENED
 };
 
 struct RowOpArgs {
@@ -104,6 +105,7 @@ struct FilterArgs {
     const uint64_t *seed;
     const uint64_t *offset;
     int32_t K;
+    int32_t layout;         // word layout of the random stream of the draws
 };
 // The largest kept set, draw count and (kept tokens x draws) the threshold kernel draws itself.
 constexpr int kSparseKept = 2048;
@@ -113,16 +115,23 @@ hipError_t launch_filter_tau(int dt, const FilterArgs &a, int grid, hipStream_t 
 // piv: the curve's pivot, 0 given per row, 1 top-anchored, 2 entropy-anchored, 3 set per row
 // (a.row_curves), 4 the shift read per row (a.shift: the mass median)
 // occ: when not null, the kernel's resident blocks per CU are written there instead of a launch
+// the word layout comes from a.layout (LAY_PLAIN or LAY_SCREENED)
 hipError_t launch_sample(int dt, bool hlg, int piv, const SampleArgs &a, int nv, int bs,
                          int grid, hipStream_t s, int *occ = nullptr);
+// per family of pivots and word layout (each instantiated in a translation unit of its own)
+template <int LAY>
+hipError_t launch_sample_given(int dt, bool hlg, const SampleArgs &a, int nv, int bs, int grid,
+                               hipStream_t s, int *occ);
+template <int LAY>
 hipError_t launch_sample_pivot(int dt, int piv, const SampleArgs &a, int nv, int bs, int grid,
                                hipStream_t s, int *occ);
+template <int LAY>
+hipError_t launch_sample_rows(int dt, const SampleArgs &a, int nv, int bs, int grid,
+                              hipStream_t s, int *occ);
 hipError_t launch_lse_partial(int dt, int piv, const SampleArgs &a, int bs, int grid,
                               hipStream_t s);
 hipError_t launch_lse_partial_pivot(int dt, int piv, const SampleArgs &a, int bs, int grid,
                                     hipStream_t s);
-hipError_t launch_sample_rows(int dt, const SampleArgs &a, int nv, int bs, int grid,
-                              hipStream_t s, int *occ);
 hipError_t launch_lse_partial_rows(int dt, const SampleArgs &a, int bs, int grid,
                                    hipStream_t s);
 // op: 0 log-sum-exp, 1 transform, 2 pivot
@@ -130,7 +139,8 @@ hipError_t launch_row_lse(int dt, int op, int piv, const RowOpArgs &a, int grid,
 hipError_t launch_philox(const uint32_t *ctr, const uint32_t *key, uint32_t *out, int64_t n,
                          hipStream_t s);
 hipError_t launch_stream_words(const uint64_t *seed, const uint64_t *offset, int64_t B,
-                               int64_t V, int32_t k, uint32_t *out, hipStream_t s);
+                               int64_t V, int32_t k, int32_t layout, uint32_t *out,
+                               hipStream_t s);
 hipError_t launch_gumbel(const uint32_t *w, float *g, int64_t n, hipStream_t s);
 hipError_t launch_fill_zero(void *p, int64_t nwords, hipStream_t s);
 

@@ -100,12 +100,12 @@ __global__ void k_philox(const uint32_t *__restrict__ ctr, const uint32_t *__res
 }
 
 // One block row (blockIdx.y) per sampled row, so that the row's key is wave-uniform as in
-// the sampling kernels, which share stream_group with this export.
+// the sampling kernels, which share stream_group with this export; one element per thread.
+template <int LAY>
 __global__ void k_stream_words(const uint64_t *__restrict__ seed,
                                const uint64_t *__restrict__ offset, int64_t B, int64_t V,
                                int32_t k, uint32_t *__restrict__ out) {
-    const int64_t ng = (V + 3) / 4;
-    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t b = blockIdx.y;
     const uint64_t off = offset[b] + (uint64_t)k;
     Stream st;
@@ -114,13 +114,8 @@ __global__ void k_stream_words(const uint64_t *__restrict__ seed,
     st.off_hi = (uint32_t)(off >> 32);
     st.key0 = (uint32_t)seed[b];
     st.key1 = (uint32_t)(seed[b] >> 32);
-    if (q >= ng) return;
-    const Words4 o = stream_group(st, (uint32_t)q);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int64_t i = q * 4 + e;
-        if (i < V) out[b * V + i] = o.w[e];
-    }
+    if (i >= V) return;
+    out[b * V + i] = element_word<LAY>(st, (uint32_t)i);
 }
 
 __global__ void k_gumbel(const uint32_t *__restrict__ w, float *__restrict__ g, int64_t n) {
@@ -137,19 +132,20 @@ __global__ void k_fill_zero(uint32_t *__restrict__ p, int64_t n) {
 // ------------------------------------------------------------------------------------------
 // Host-side launchers (called from hs_api.hip).
 // ------------------------------------------------------------------------------------------
+template hipError_t launch_sample_given<LAY_PLAIN>(int, bool, const SampleArgs &, int, int,
+                                                   int, hipStream_t, int *);
+
 hipError_t launch_sample(int dt, bool hlg, int piv, const SampleArgs &a, int nv, int bs,
                          int grid, hipStream_t s, int *occ) {
-    if (hlg && piv == 3) return launch_sample_rows(dt, a, nv, bs, grid, s, occ);
-    if (hlg && piv != 0) return launch_sample_pivot(dt, piv, a, nv, bs, grid, s, occ);
-    switch (dt) {
-        case DT_F32: return hlg ? launch_sample_al<DT_F32, true, 0>(a, nv, bs, grid, s, occ)
-                                : launch_sample_al<DT_F32, false, 0>(a, nv, bs, grid, s, occ);
-        case DT_BF16: return hlg ? launch_sample_al<DT_BF16, true, 0>(a, nv, bs, grid, s, occ)
-                                 : launch_sample_al<DT_BF16, false, 0>(a, nv, bs, grid, s, occ);
-        case DT_F16: return hlg ? launch_sample_al<DT_F16, true, 0>(a, nv, bs, grid, s, occ)
-                                : launch_sample_al<DT_F16, false, 0>(a, nv, bs, grid, s, occ);
-    }
-    return hipErrorInvalidValue;
+    const bool scr = a.layout == LAY_SCREENED;
+    if (hlg && piv == 3)
+        return scr ? launch_sample_rows<LAY_SCREENED>(dt, a, nv, bs, grid, s, occ)
+                   : launch_sample_rows<LAY_PLAIN>(dt, a, nv, bs, grid, s, occ);
+    if (hlg && piv != 0)
+        return scr ? launch_sample_pivot<LAY_SCREENED>(dt, piv, a, nv, bs, grid, s, occ)
+                   : launch_sample_pivot<LAY_PLAIN>(dt, piv, a, nv, bs, grid, s, occ);
+    return scr ? launch_sample_given<LAY_SCREENED>(dt, hlg, a, nv, bs, grid, s, occ)
+               : launch_sample_given<LAY_PLAIN>(dt, hlg, a, nv, bs, grid, s, occ);
 }
 
 hipError_t launch_lse_partial(int dt, int piv, const SampleArgs &a, int bs, int grid,
@@ -194,13 +190,17 @@ hipError_t launch_philox(const uint32_t *ctr, const uint32_t *key, uint32_t *out
 }
 
 hipError_t launch_stream_words(const uint64_t *seed, const uint64_t *offset, int64_t B,
-                               int64_t V, int32_t k, uint32_t *out, hipStream_t s) {
+                               int64_t V, int32_t k, int32_t layout, uint32_t *out,
+                               hipStream_t s) {
     const int bs = 256;
-    const int64_t ng = (V + 3) / 4;
-    const int64_t gx = (ng + bs - 1) / bs;
+    const int64_t gx = (V + bs - 1) / bs;
     if (B > 65535) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_stream_words, dim3((unsigned)gx, (unsigned)B), dim3(bs), 0, s, seed,
-                       offset, B, V, k, out);
+    if (layout == LAY_SCREENED)
+        hipLaunchKernelGGL(k_stream_words<LAY_SCREENED>, dim3((unsigned)gx, (unsigned)B),
+                           dim3(bs), 0, s, seed, offset, B, V, k, out);
+    else
+        hipLaunchKernelGGL(k_stream_words<LAY_PLAIN>, dim3((unsigned)gx, (unsigned)B),
+                           dim3(bs), 0, s, seed, offset, B, V, k, out);
     return hipGetLastError();
 }
 

@@ -200,7 +200,10 @@ __device__ __forceinline__ void chunk_partial(const SampleArgs &a, int64_t b, in
 // 3 set per row with the rest of the curve (a.row_curves): both sums are accumulated and each
 // row picks its shift; a row with its curve off runs the curve as the identity (m = 1, no
 // rolloff, c = 0), which scores x / T exactly as the curve-off kernel does.
-template <int DT, int NV, bool HLG, int PIV, int MAXBS, bool ALIGNED>
+// LAY selects the word layout of the random stream (LAY_PLAIN or LAY_SCREENED, see
+// element_word): the pass draws only what the screen needs, the largest leading 16 bits of
+// each vector's words, and the few vectors scored exactly draw their whole words.
+template <int DT, int NV, bool HLG, int PIV, int MAXBS, bool ALIGNED, int LAY>
 __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     static_assert(HLG || PIV == 0, "a pivot needs the curve");
     constexpr bool LSE = HLG && PIV != 1 && PIV != 4;   // the exponential sum is needed
@@ -253,7 +256,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     // ---- row parameters (wave-uniform) ----
     const float T = a.T[b];
     float mu = 0.0f;
-    bool bad = !(T >= 0.0f) || !(T < __builtin_inff());
+    bool bad = !temp_valid(T);
     Curve cv = a.curve;
     float poff = a.pivot_offset;
     int rpiv = PIV;   // this row's pivot mode; -1: curve off
@@ -357,10 +360,16 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
         }
         rag = make_uint4(w[0], w[1], w[2], w[3]);
     }
+    // The streaming pass reads every vector once: its loads carry the non-temporal hint (on
+    // MI355X a row-per-block read of the 256 x 151936 bf16 shape runs at ~75% of the HBM peak
+    // with it, ~65% without).
     auto issue_load = [&](int n) -> uint4 {
         if constexpr (ALIGNED) {
             const int gv = min(lane_v + n * BS, gclamp);
-            return *reinterpret_cast<const uint4 *>(rowp + (uint32_t)gv * 16u);
+            typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+            const u4v t = __builtin_nontemporal_load(
+                reinterpret_cast<const u4v *>(rowp + (uint32_t)gv * 16u));
+            return make_uint4(t.x, t.y, t.z, t.w);
         } else {
             return fetch(lane_v + n * BS);
         }
@@ -394,14 +403,19 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
         return sk;
     };
 
-    // Random words of slot n for draw stream sk: their maximum goes to the slot's LDS dword
-    // (high half); returns the slot's key for the lane's champion, max word & ~31 | slot. Slots
+    // Random words of slot n for draw stream sk: the largest leading 16 bits of the vector's
+    // words go to the slot's LDS dword (high half); returns the slot's key for the lane's
+    // champion: those bits (and, in the plain layout, the next 11) over the slot index. Slots
     // past the chunk are drawn too (their words are never used).
+    // Screened layout: one call (counter word 2q of the vector's group q) holds the leading
+    // halves of the group's eight elements; an fp32 vector is half a group (elements 4h ..
+    // 4h + 3, h = gv & 1, the same for every slot of a lane since BS is even).
     auto draw_vec = [&](const Stream &sk, int n) -> uint32_t {
-        uint32_t q = (uint32_t)(lane_v + n * BS) * NG;
-        asm volatile("" : "+v"(q));
-        uint32_t mw;
-        {
+        uint32_t code, key;
+        if constexpr (LAY == LAY_PLAIN) {
+            uint32_t q = (uint32_t)(lane_v + n * BS) * NG;
+            asm volatile("" : "+v"(q));
+            uint32_t mw;
             const Words4 w = philox4x32_10_uk(q, sk.row, sk.off_lo, sk.off_hi, sk.key0, sk.key1);
             mw = max(max3u(w.w[0], w.w[1], w.w[2]), w.w[3]);
             if constexpr (NG == 2) {
@@ -410,10 +424,60 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                 mw = max3u(max3u(w.w[0], w.w[1], w.w[2]), max3u(w.w[3], u.w[0], u.w[1]),
                            max(u.w[2], u.w[3]));
             }
+            code = mw >> 16;
+            key = (mw & ~31u) | (uint32_t)n;
+        } else {
+            const uint32_t gv = (uint32_t)(lane_v + n * BS);
+            uint32_t q2 = EPV == 8 ? gv << 1 : gv & ~1u;
+            asm volatile("" : "+v"(q2));
+            const Words4 w = philox4x32_10_uk(q2, sk.row, sk.off_lo, sk.off_hi, sk.key0, sk.key1);
+            if constexpr (EPV == 8) {
+                code = max_half16(max_half16_pk(w.w[0], w.w[1]), max_half16_pk(w.w[2], w.w[3]));
+            } else {
+                const bool h = (gv & 1u) != 0u;
+                code = max_half16(h ? w.w[2] : w.w[0], h ? w.w[3] : w.w[1]);
+            }
+            key = (code << 16) | (uint32_t)n;
         }
-        s_vec16[2 * (lane_lds + n) + 1] = (uint16_t)(mw >> 16);
-        return (mw & ~31u) | (uint32_t)n;
+        s_vec16[2 * (lane_lds + n) + 1] = (uint16_t)code;
+        return key;
     };
+    // Whole words of the vector gv for stream sk (the bootstrap candidate and the vectors
+    // scored exactly): element e's word into w[e].
+    auto vec_words = [&](const Stream &sk, int gvi, uint32_t (&w)[EPV]) {
+        if constexpr (LAY == LAY_PLAIN) {
+            uint32_t q = (uint32_t)gvi * NG;
+            asm volatile("" : "+v"(q));
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const Words4 ww = philox4x32_10_uk(q + g, sk.row, sk.off_lo, sk.off_hi, sk.key0,
+                                                   sk.key1);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[4 * g + e] = ww.w[e];
+            }
+        } else {
+            const uint32_t gv = (uint32_t)gvi;
+            uint32_t q2 = EPV == 8 ? gv << 1 : gv & ~1u;
+            asm volatile("" : "+v"(q2));
+            const Words4 hi = philox4x32_10_uk(q2, sk.row, sk.off_lo, sk.off_hi, sk.key0, sk.key1);
+            const Words4 lo = philox4x32_10_uk(q2 | 1u, sk.row, sk.off_lo, sk.off_hi, sk.key0,
+                                               sk.key1);
+            if constexpr (EPV == 8) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) w[e] = (half16(hi, e) << 16) | half16(lo, e);
+            } else {
+                const bool h = (gv & 1u) != 0u;
+                const uint32_t h0 = h ? hi.w[2] : hi.w[0], h1 = h ? hi.w[3] : hi.w[1];
+                const uint32_t l0 = h ? lo.w[2] : lo.w[0], l1 = h ? lo.w[3] : lo.w[1];
+                w[0] = (h0 << 16) | (l0 & 0xFFFFu);
+                w[1] = (h0 & 0xFFFF0000u) | (l0 >> 16);
+                w[2] = (h1 << 16) | (l1 & 0xFFFFu);
+                w[3] = (h1 & 0xFFFF0000u) | (l1 >> 16);
+            }
+        }
+    };
+    // the bits of a word that the champion key holds: (w ^ key) <= kMatch when they agree
+    constexpr uint32_t kMatch = LAY == LAY_PLAIN ? 31u : 0xFFFFu;
     // The lane's champion key over a whole draw (draws without the logits at hand).
     auto draw_all = [&](const Stream &sk) -> uint32_t {
         uint32_t champ = 0;
@@ -484,18 +548,10 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     auto candidate = [&](const Stream &sk, uint32_t champ, const uint4 &v,
                          uint32_t (&cw)[EPV]) -> Cand {
         Cand c{0ull, -__builtin_inff(), 0u};
-        uint32_t q = (uint32_t)(lane_v + (int)(champ & 31u) * BS) * NG;
-        asm volatile("" : "+v"(q));
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            const Words4 w = philox4x32_10_uk(q + g, sk.row, sk.off_lo, sk.off_hi, sk.key0,
-                                              sk.key1);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) cw[4 * g + e] = w.w[e];
-        }
+        vec_words(sk, lane_v + (int)(champ & 31u) * BS, cw);
 #pragma unroll
         for (int e = EPV - 1; e >= 0; --e) {
-            if ((cw[e] ^ champ) < 32u) {
+            if ((cw[e] ^ champ) <= kMatch) {
                 c.w = cw[e];
                 c.x = elem<DT>(v, e);
             }
@@ -591,6 +647,18 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
         const float cs = has ? exact_score<HLG>(red_cx[lane], red_cw[lane], rc) : -__builtin_inff();
         return uniform(wave_max(cs));
     };
+    // Rows whose scores come near the fp32 range (a temperature of ~1e-38) can overflow the
+    // screen's constants: then the screen is switched off for the row (every vector passes
+    // and every element is scored exactly), which is always correct.
+    auto screen_guard = [](float &sa_, float &sb_, float &sc_, float &ta_, float &tb_) {
+        const float lim = 1.0e38f;
+        if (fabsf(sa_) < lim && fabsf(sb_) < lim && fabsf(ta_) < lim && fabsf(tb_) < lim &&
+            !(sc_ != sc_))
+            return;
+        sa_ = ta_ = 0.0f;
+        sb_ = tb_ = -3.0e38f;
+        sc_ = __builtin_inff();
+    };
     // (wave 0) The screen's constants from a lower bound bs on the draw's winning score:
     // threshold thr = (bs - slack) / ln 2 - 1 in units of ln 2, and the coefficients with which
     //   need(x) = min(max(x sa + sb, x ta + tb), sc)
@@ -645,6 +713,10 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             o[7] = 0.0f;
             o[8] = 0.0f;
         }
+        screen_guard(o[1], o[2], o[3], o[4], o[5]);
+        if (!(o[1] == 0.0f && o[4] == 0.0f && o[2] < -1.0e38f)) return;
+        o[0] = -3.0e38f;   // the screen is off for the row: no tangent either
+        o[6] = o[7] = o[8] = 0.0f;
     };
 
     // Per wave: the lanes' largest logit into rx, and (curve on) their log-sum-exp sums.
@@ -896,6 +968,8 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     float sa = uniform(row_bc[4]), sb = uniform(row_bc[5]), sc = uniform(row_bc[6]);
     float ta = uniform(row_bc[7]), tb = uniform(row_bc[8]);
     bool tan_on = uniform(row_bc[9]) > 0.0f;
+    // whether the first draw's screen is on (its constants were finite)
+    const bool scr_on = !(sa == 0.0f && ta == 0.0f && sb < -1.0e38f);
     // for later draws: whether the shoulder tangent is set up, its intercept before the
     // threshold, and the lower bound from the chunk's largest logit (the first draw's)
     const bool tan_set = uniform(row_bc[10]) > 0.0f;
@@ -929,16 +1003,8 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     auto score_vec = [&](const Stream &sk, int n, const uint4 &v, uint64_t best) -> uint64_t {
         const int gv = lane_v + n * BS;
         if (greedy) return greedy_vec<DT>(v, (uint32_t)gv * EPV, best);
-        uint32_t q = (uint32_t)gv * NG;
-        asm volatile("" : "+v"(q));
         uint32_t w[EPV];
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            const Words4 ww = philox4x32_10_uk(q + g, sk.row, sk.off_lo, sk.off_hi, sk.key0,
-                                               sk.key1);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) w[4 * g + e] = ww.w[e];
-        }
+        vec_words(sk, gv, w);
         return score_words(n, v, w, best);
     };
 
@@ -964,13 +1030,16 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             // the same arithmetic as the first draw's constants, from the new bound
             const float thr = bs < __builtin_inff() ? (bs - screen_slack(bs)) * kInvLn2 - 1.0f
                                                     : -3.0e38f;
-            if constexpr (HLG) {
-                sb = __builtin_fmaf(rc.mtc, kInvLn2, thr);
-                sc = __builtin_fmaf(rc.mtw, kInvLn2, thr);
-                tb = tan_set ? __builtin_fmaf(tan_i, -kInvLn2, thr) : sb;
-            } else {
-                sb = thr;
-                tb = thr;
+            if (scr_on) {
+                if constexpr (HLG) {
+                    sb = __builtin_fmaf(rc.mtc, kInvLn2, thr);
+                    sc = __builtin_fmaf(rc.mtw, kInvLn2, thr);
+                    tb = tan_set ? __builtin_fmaf(tan_i, -kInvLn2, thr) : sb;
+                } else {
+                    sb = thr;
+                    tb = thr;
+                }
+                screen_guard(sa, sb, sc, ta, tb);
             }
         }
         uint64_t best = 0;
@@ -1113,7 +1182,7 @@ __global__ __launch_bounds__(1024) void k_lse_partial(SampleArgs a) {
 // ------------------------------------------------------------------------------------------
 // occ: when not null, the resident blocks per CU of the kernel this call would launch are
 // written there instead of launching it.
-template <int DT, bool HLG, int PIV, bool AL>
+template <int DT, bool HLG, int PIV, bool AL, int LAY>
 hipError_t launch_sample_nv(const SampleArgs &a, int nv, int bs, int grid, hipStream_t s,
                             int *occ) {
     // blocks of up to 1024 threads, nv slots of 16-byte vectors per thread; the dynamic LDS
@@ -1123,9 +1192,9 @@ hipError_t launch_sample_nv(const SampleArgs &a, int nv, int bs, int grid, hipSt
         if (bs > MB) return hipErrorInvalidValue;                                          \
         if (occ)                                                                           \
             return hipOccupancyMaxActiveBlocksPerMultiprocessor(                           \
-                occ, reinterpret_cast<const void *>(&k_sample<DT, N, HLG, PIV, MB, AL>),  \
+                occ, reinterpret_cast<const void *>(&k_sample<DT, N, HLG, PIV, MB, AL, LAY>), \
                 bs, (size_t)(N | 1) * bs * 4);                                            \
-        hipLaunchKernelGGL((k_sample<DT, N, HLG, PIV, MB, AL>), dim3(grid), dim3(bs),     \
+        hipLaunchKernelGGL((k_sample<DT, N, HLG, PIV, MB, AL, LAY>), dim3(grid), dim3(bs), \
                            (size_t)(N | 1) * bs * 4, s, a);                               \
         break;
     switch (nv) {
@@ -1137,14 +1206,77 @@ hipError_t launch_sample_nv(const SampleArgs &a, int nv, int bs, int grid, hipSt
     return hipGetLastError();
 }
 
-template <int DT, bool HLG, int PIV>
+template <int DT, bool HLG, int PIV, int LAY>
 hipError_t launch_sample_al(const SampleArgs &a, int nv, int bs, int grid, hipStream_t s,
                             int *occ) {
     // the branch-free load path needs 16-byte aligned rows holding at least one full vector
     if (a.aligned && a.V >= dtype_traits<DT>::epv)
-        return launch_sample_nv<DT, HLG, PIV, true>(a, nv, bs, grid, s, occ);
-    return launch_sample_nv<DT, HLG, PIV, false>(a, nv, bs, grid, s, occ);
+        return launch_sample_nv<DT, HLG, PIV, true, LAY>(a, nv, bs, grid, s, occ);
+    return launch_sample_nv<DT, HLG, PIV, false, LAY>(a, nv, bs, grid, s, occ);
 }
+
+// The sampling kernel of one word layout for each family of pivots: curve off or pivot given
+// (PIV 0), anchored pivots (1 top, 2 entropy, 4 the mass median's shift), curve set per row
+// (3). Each family and layout is instantiated in a translation unit of its own.
+template <int LAY>
+hipError_t launch_sample_given(int dt, bool hlg, const SampleArgs &a, int nv, int bs, int grid,
+                               hipStream_t s, int *occ) {
+    switch (dt) {
+        case DT_F32: return hlg ? launch_sample_al<DT_F32, true, 0, LAY>(a, nv, bs, grid, s, occ)
+                                : launch_sample_al<DT_F32, false, 0, LAY>(a, nv, bs, grid, s, occ);
+        case DT_BF16: return hlg ? launch_sample_al<DT_BF16, true, 0, LAY>(a, nv, bs, grid, s, occ)
+                                 : launch_sample_al<DT_BF16, false, 0, LAY>(a, nv, bs, grid, s, occ);
+        case DT_F16: return hlg ? launch_sample_al<DT_F16, true, 0, LAY>(a, nv, bs, grid, s, occ)
+                                : launch_sample_al<DT_F16, false, 0, LAY>(a, nv, bs, grid, s, occ);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int LAY>
+hipError_t launch_sample_pivot(int dt, int piv, const SampleArgs &a, int nv, int bs, int grid,
+                               hipStream_t s, int *occ) {
+    switch (dt) {
+        case DT_F32:
+            return piv == 1 ? launch_sample_al<DT_F32, true, 1, LAY>(a, nv, bs, grid, s, occ)
+                 : piv == 4 ? launch_sample_al<DT_F32, true, 4, LAY>(a, nv, bs, grid, s, occ)
+                            : launch_sample_al<DT_F32, true, 2, LAY>(a, nv, bs, grid, s, occ);
+        case DT_BF16:
+            return piv == 1 ? launch_sample_al<DT_BF16, true, 1, LAY>(a, nv, bs, grid, s, occ)
+                 : piv == 4 ? launch_sample_al<DT_BF16, true, 4, LAY>(a, nv, bs, grid, s, occ)
+                            : launch_sample_al<DT_BF16, true, 2, LAY>(a, nv, bs, grid, s, occ);
+        case DT_F16:
+            return piv == 1 ? launch_sample_al<DT_F16, true, 1, LAY>(a, nv, bs, grid, s, occ)
+                 : piv == 4 ? launch_sample_al<DT_F16, true, 4, LAY>(a, nv, bs, grid, s, occ)
+                            : launch_sample_al<DT_F16, true, 2, LAY>(a, nv, bs, grid, s, occ);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int LAY>
+hipError_t launch_sample_rows(int dt, const SampleArgs &a, int nv, int bs, int grid,
+                              hipStream_t s, int *occ) {
+    switch (dt) {
+        case DT_F32: return launch_sample_al<DT_F32, true, 3, LAY>(a, nv, bs, grid, s, occ);
+        case DT_BF16: return launch_sample_al<DT_BF16, true, 3, LAY>(a, nv, bs, grid, s, occ);
+        case DT_F16: return launch_sample_al<DT_F16, true, 3, LAY>(a, nv, bs, grid, s, occ);
+    }
+    return hipErrorInvalidValue;
+}
+
+// Each family and layout is instantiated explicitly in its own translation unit; no other
+// unit instantiates them implicitly.
+extern template hipError_t launch_sample_given<LAY_PLAIN>(int, bool, const SampleArgs &, int,
+                                                          int, int, hipStream_t, int *);
+extern template hipError_t launch_sample_given<LAY_SCREENED>(int, bool, const SampleArgs &, int,
+                                                             int, int, hipStream_t, int *);
+extern template hipError_t launch_sample_pivot<LAY_PLAIN>(int, int, const SampleArgs &, int,
+                                                          int, int, hipStream_t, int *);
+extern template hipError_t launch_sample_pivot<LAY_SCREENED>(int, int, const SampleArgs &, int,
+                                                             int, int, hipStream_t, int *);
+extern template hipError_t launch_sample_rows<LAY_PLAIN>(int, const SampleArgs &, int, int, int,
+                                                         hipStream_t, int *);
+extern template hipError_t launch_sample_rows<LAY_SCREENED>(int, const SampleArgs &, int, int,
+                                                            int, hipStream_t, int *);
 
 template <int PIV>
 hipError_t launch_lse_partial_t(int dt, const SampleArgs &a, int bs, int grid, hipStream_t s) {

@@ -1,6 +1,7 @@
 // hs_micro.hip -- ceilings the sampling kernel is measured against on the same shape: a plain
 // streaming read of the logits with the sampler's access pattern (each block reads one row,
-// 16-byte loads, eight in flight per lane, and reduces it to its maximum), and the Philox4x32-10
+// 16-byte loads, eight in flight per lane, and reduces it to its maximum), the same read with
+// non-temporal loads (four in flight), and the Philox4x32-10
 // word rate with the sampler's counter layout and no memory traffic. Benchmark infrastructure,
 // built as a library of its own; the sampling library does not depend on it.
 #include <hip/hip_runtime.h>
@@ -12,8 +13,11 @@ namespace {
 
 using namespace hs;
 
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+
 // Row maximum of [B, V] logits (V a multiple of the vector width, rows 16-byte aligned).
-template <int DT>
+// D loads in flight per lane; NT: loads carry the non-temporal (streaming) cache hint.
+template <int DT, int D, bool NT>
 __global__ __launch_bounds__(1024) void k_stream_max(const char *x, int64_t ld_bytes,
                                                      int64_t nvec, float *out) {
     constexpr int EPV = dtype_traits<DT>::epv;
@@ -22,12 +26,20 @@ __global__ __launch_bounds__(1024) void k_stream_max(const char *x, int64_t ld_b
     const uint4 *p = reinterpret_cast<const uint4 *>(row);
     float m = -__builtin_inff();
     int64_t v = threadIdx.x;
-    for (; v + 7 * 1024 < nvec; v += 8 * 1024) {
-        uint4 buf[8];
+    for (; v + (D - 1) * 1024 < nvec; v += D * 1024) {
+        uint4 buf[D];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) buf[j] = p[v + j * 1024];
+        for (int j = 0; j < D; ++j) {
+            if constexpr (NT) {
+                const u4v t = __builtin_nontemporal_load(
+                    reinterpret_cast<const u4v *>(p + v + j * 1024));
+                buf[j] = make_uint4(t.x, t.y, t.z, t.w);
+            } else {
+                buf[j] = p[v + j * 1024];
+            }
+        }
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < D; ++j)
 #pragma unroll
             for (int e = 0; e < EPV; ++e) m = fmaxf(m, elem<DT>(buf[j], e));
     }
@@ -59,14 +71,9 @@ __global__ __launch_bounds__(1024) void k_philox_max(const uint64_t *seed, int64
     out[(int64_t)blockIdx.x * 1024 + threadIdx.x] = m;
 }
 
-}  // namespace
-
-extern "C" {
-
-// out: device float[B]; x: device [B, ld] logits of dtype (0 f32, 1 bf16, 2 f16), rows
-// 16-byte aligned, V a multiple of 16 / element size. Returns 0 or a HIP error code.
-int hs_micro_stream_max(const void *x, int32_t dtype, int64_t B, int64_t V, int64_t ld,
-                        float *out, void *stream) {
+template <int D, bool NT>
+int stream_max(const void *x, int32_t dtype, int64_t B, int64_t V, int64_t ld, float *out,
+               void *stream) {
     const int es = dtype == 0 ? 4 : 2;
     if (!x || !out || B < 1 || V < 1 || (V * es) % 16 != 0 || ((uintptr_t)x % 16) != 0 ||
         (ld * es) % 16 != 0)
@@ -75,12 +82,30 @@ int hs_micro_stream_max(const void *x, int32_t dtype, int64_t B, int64_t V, int6
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const char *p = reinterpret_cast<const char *>(x);
     switch (dtype) {
-        case 0: hipLaunchKernelGGL(k_stream_max<DT_F32>, dim3(B), dim3(1024), 0, s, p, ld * es, nvec, out); break;
-        case 1: hipLaunchKernelGGL(k_stream_max<DT_BF16>, dim3(B), dim3(1024), 0, s, p, ld * es, nvec, out); break;
-        case 2: hipLaunchKernelGGL(k_stream_max<DT_F16>, dim3(B), dim3(1024), 0, s, p, ld * es, nvec, out); break;
+        case 0: hipLaunchKernelGGL((k_stream_max<DT_F32, D, NT>), dim3(B), dim3(1024), 0, s, p, ld * es, nvec, out); break;
+        case 1: hipLaunchKernelGGL((k_stream_max<DT_BF16, D, NT>), dim3(B), dim3(1024), 0, s, p, ld * es, nvec, out); break;
+        case 2: hipLaunchKernelGGL((k_stream_max<DT_F16, D, NT>), dim3(B), dim3(1024), 0, s, p, ld * es, nvec, out); break;
         default: return -1;
     }
     return (int)hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+// out: device float[B]; x: device [B, ld] logits of dtype (0 f32, 1 bf16, 2 f16), rows
+// 16-byte aligned, V a multiple of 16 / element size. Returns 0 or a HIP error code.
+int hs_micro_stream_max(const void *x, int32_t dtype, int64_t B, int64_t V, int64_t ld,
+                        float *out, void *stream) {
+    return stream_max<8, false>(x, dtype, B, V, ld, out, stream);
+}
+
+// The same read with the non-temporal cache hint on every load and four loads in flight per
+// lane (the fastest plain read of a row per block measured on MI355X).
+int hs_micro_stream_max_nt(const void *x, int32_t dtype, int64_t B, int64_t V, int64_t ld,
+                           float *out, void *stream) {
+    return stream_max<4, true>(x, dtype, B, V, ld, out, stream);
 }
 
 // Words for B rows of V elements (V a multiple of 4) and K draws, over B * groups blocks;

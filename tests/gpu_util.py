@@ -36,20 +36,30 @@ def on_device(w):
     return out
 
 
-def gpu_sample(hs, w, dev=None, **kw) -> np.ndarray:
+LAYOUTS = ("plain", "screened")
+
+
+def gpu_sample(hs, w, dev=None, layout="plain", **kw) -> np.ndarray:
+    """hs_sample (plain word layout) or hs_sample_ex with the given word layout."""
     dev = dev or on_device(w)
-    out = hs.sample(dev["logits"], dev["T"], dev["seed"], dev["offset"], mu=dev.get("mu"),
-                    hlg=w.hlg, k=w.K, **kw)
+    if layout == "plain" and "opts" not in kw:
+        out = hs.sample(dev["logits"], dev["T"], dev["seed"], dev["offset"], mu=dev.get("mu"),
+                        hlg=w.hlg, k=w.K, **kw)
+    else:
+        opts = kw.pop("opts", None) or hs.SampleOpts()
+        opts.layout = hs.LAYOUTS[layout]
+        out = hs.sample_ex(dev["logits"], dev["T"], dev["seed"], dev["offset"],
+                           mu=dev.get("mu"), hlg=w.hlg, k=w.K, opts=opts, **kw)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
 
-def oracle_sample(O, w, rows=None):
+def oracle_sample(O, w, rows=None, layout="plain"):
     x = w.logits if rows is None else w.logits[rows]
     rsel = np.arange(w.B) if rows is None else np.asarray(rows)
     mu = None if w.hlg is None else w.mu[rsel]
     return O.sample(x, w.T[rsel], w.seed[rsel], w.offset[rsel], K=w.K, mu=mu, hlg=w.hlg,
-                    row_id=rsel.astype(np.int64))
+                    row_id=rsel.astype(np.int64), layout=layout)
 
 
 def assert_parity(gpu_idx, or_idx, s1, s2, x64, label: str, max_exempt_frac=MAX_EXEMPT_FRAC):

@@ -32,7 +32,7 @@ def test_json_line_fields():
     d = json.loads(lines[0])
     for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
               "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
-              "roofline", "hbm"):
+              "roofline", "valu"):
         assert k in d, k
     assert d["n_gpus"] == 1 and d["steps"] == 5 and d["warmup"] == 2
     assert d["unit"] == "rows/s" and d["higher_is_better"] is True
@@ -43,3 +43,7 @@ def test_json_line_fields():
     for k in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
         assert k in rf, k
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-9
+    # the HBM roofline: algorithmic bytes over the kernel time, against 8 TB/s
+    assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
+    alg = d["config"]["algorithmic_bytes_per_step"]
+    assert abs(rf["achieved"] - alg / (rf["kernel_ms"] / 1e3) / 1e9) < 1e-6 * rf["achieved"]

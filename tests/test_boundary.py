@@ -74,6 +74,7 @@ def sample(lib, x, T=FAKE, mu=FAKE, hlg=None, seed=FAKE, off=FAKE, K=1, out=FAKE
     (L(dtype=7), HS_ERR_DTYPE),
     (L(dtype=-1), HS_ERR_DTYPE),
     (L(V=2**31, ld=2**31), HS_ERR_UNSUPPORTED),
+    (L(V=2**30, ld=2**30, dtype=0), HS_ERR_UNSUPPORTED),   # an fp32 row of 4 GiB
 ])
 def test_bad_logits(lib, x, code):
     assert sample(lib, x) == code
@@ -82,6 +83,17 @@ def test_bad_logits(lib, x, code):
     h = H()
     assert lib.hs_hlg_transform(C.byref(x), FAKE, C.byref(h), FAKE, max(x.V, 1), None) == code
     assert lib.hs_hlg_pivot(C.byref(x), FAKE, C.byref(h), FAKE, None) == code
+
+
+def test_row_byte_limit(lib):
+    """Within-row byte offsets are 32-bit: a row must hold fewer than 2^32 bytes, so fp32 rows
+    stop at 2^30 - 1 elements while 16-bit rows reach 2^31 - 1. The logits are validated
+    first: a missing output then gives HS_ERR_INVALID_ARG for an accepted shape."""
+    for dtype, vmax in ((0, 2**30 - 1), (1, 2**31 - 1), (2, 2**31 - 1)):
+        assert lib.hs_logsumexp(C.byref(L(B=1, V=vmax, dtype=dtype)), None, None) == \
+            HS_ERR_INVALID_ARG
+        assert lib.hs_logsumexp(C.byref(L(B=1, V=vmax + 1, dtype=dtype)), None, None) == \
+            HS_ERR_UNSUPPORTED
 
 
 def test_null_logits_struct(lib):
@@ -271,6 +283,8 @@ def test_micro_library_exports():
     assert M.hs_micro_stream_max(None, 1, 4, 64, 64, FAKE, None) == -1
     assert M.hs_micro_stream_max(FAKE, 1, 4, 63, 64, FAKE, None) == -1     # not whole vectors
     assert M.hs_micro_stream_max(FAKE, 9, 4, 64, 64, FAKE, None) == -1
+    M.hs_micro_stream_max_nt.argtypes = M.hs_micro_stream_max.argtypes
+    assert M.hs_micro_stream_max_nt(FAKE, 1, 4, 63, 64, FAKE, None) == -1
     assert M.hs_micro_philox_max(FAKE, 4, 10, 1, 1, FAKE, None) == -1      # V % 4 != 0
     assert M.hs_micro_philox_max(None, 4, 64, 1, 1, FAKE, None) == -1
     assert M.hs_micro_philox_max(FAKE, 4, 64, 2, 3, FAKE, None) == -1      # groups > K

@@ -16,7 +16,8 @@ import pytest
 import torch
 
 from synth import workloads as W
-from tests.gpu_util import assert_parity, gpu_sample, on_device, oracle_sample, require_gpu
+from tests.gpu_util import (LAYOUTS, assert_parity, gpu_sample, on_device, oracle_sample,
+                            require_gpu)
 
 pytestmark = pytest.mark.gpu
 HLG_A = {"m": 1.5, "w": 2.0, "beta_t": 1.0, "beta_h": 2.0}
@@ -27,34 +28,38 @@ def hs():
     return require_gpu()
 
 
-def _check(hs, O, w, label, **kw):
-    g = gpu_sample(hs, w, **kw)
-    o, s1, s2 = oracle_sample(O, w)
-    return assert_parity(g, o, s1, s2, w.logits.double().numpy(), label)
+def _check(hs, O, w, label, layout="plain", **kw):
+    g = gpu_sample(hs, w, layout=layout, **kw)
+    o, s1, s2 = oracle_sample(O, w, layout=layout)
+    return assert_parity(g, o, s1, s2, w.logits.double().numpy(), label + " " + layout)
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("V", [1, 2, 3, 5, 8, 9, 31, 33, 1000, 4097, 65537])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("hlg", [None, HLG_A])
-def test_ragged_vocab(hs, oracle_mod, V, dtype, hlg):
+def test_ragged_vocab(hs, oracle_mod, V, dtype, hlg, layout):
     w = W.generic(3, V, dtype, seed=V, mask_frac=0.1 if V > 4 else 0.0, hlg=hlg, K=3,
                   offset_max=2**33)
-    _check(hs, oracle_mod, w, "V=%d %s hlg=%s" % (V, dtype, hlg is not None))
+    _check(hs, oracle_mod, w, "V=%d %s hlg=%s" % (V, dtype, hlg is not None), layout=layout)
 
 
-def test_fp16_and_misaligned_rows(hs, oracle_mod):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_fp16_and_misaligned_rows(hs, oracle_mod, layout):
     w = W.generic(6, 3001, torch.float16, seed=21, mask_frac=0.25, hlg=HLG_A, K=2)
-    _check(hs, oracle_mod, w, "f16")
+    _check(hs, oracle_mod, w, "f16", layout=layout)
     big = torch.full((6, 3004), float("-inf"), dtype=torch.float16)
     big[:, :3001] = w.logits
     d = on_device(w)
     x = big.cuda()[:, :3001]
-    g = hs.sample(x, d["T"], d["seed"], d["offset"], mu=d["mu"], hlg=w.hlg, k=2).cpu().numpy()
-    o, s1, s2 = oracle_sample(oracle_mod, w)
-    assert_parity(g, o, s1, s2, w.logits.double().numpy(), "f16 misaligned")
+    g = hs.sample_ex(x, d["T"], d["seed"], d["offset"], mu=d["mu"], hlg=w.hlg, k=2,
+                     opts=hs.SampleOpts(layout=hs.LAYOUTS[layout])).cpu().numpy()
+    o, s1, s2 = oracle_sample(oracle_mod, w, layout=layout)
+    assert_parity(g, o, s1, s2, w.logits.double().numpy(), "f16 misaligned " + layout)
 
 
-def test_special_rows(hs, oracle_mod):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_special_rows(hs, oracle_mod, layout):
     V = 777
     rng = np.random.default_rng(31)
     x = rng.normal(0, 1, size=(8, V)).astype(np.float32)
@@ -70,9 +75,10 @@ def test_special_rows(hs, oracle_mod):
     for hlg in (None, HLG_A):
         w = W.Workload("special", torch.from_numpy(x), T, seed, off, K=3, hlg=hlg,
                        mu=mu if hlg else None)
-        g = gpu_sample(hs, w)
-        o, s1, s2 = oracle_sample(oracle_mod, w)
-        assert_parity(g, o, s1, s2, x.astype(np.float64), "special rows hlg=%s" % bool(hlg))
+        g = gpu_sample(hs, w, layout=layout)
+        o, s1, s2 = oracle_sample(oracle_mod, w, layout=layout)
+        assert_parity(g, o, s1, s2, x.astype(np.float64), "special rows hlg=%s %s"
+                      % (bool(hlg), layout))
         assert g[0].tolist() == [-1] * 3
         assert g[1].tolist() == [400] * 3
         assert g[2].tolist() == [3] * 3 and g[3].tolist() == [10] * 3
@@ -81,32 +87,75 @@ def test_special_rows(hs, oracle_mod):
             assert g[7].tolist() == [-2] * 3
 
 
-def test_rolloff_off_equals_temperature(hs):
+@pytest.mark.parametrize("hlg", [None, HLG_A])
+def test_subnormal_temperature_is_invalid(hs, oracle_mod, hlg):
+    """A subnormal temperature (1/T overflows fp32) is invalid (-2) on the GPU and in the oracle,
+    also on rows holding an exact 0 logit (0 * inf would be NaN); the smallest normal T is a
+    valid, near-greedy temperature."""
+    V = 500
+    # |l'| / FLT_MIN stays inside the fp32 range: |x| < 1.9, no ties at the top
+    x = (1.9 * np.tanh(np.random.default_rng(33).normal(0, 1, size=(4, V)))).astype(np.float32)
+    x[:, 7] = 0.0
+    T = np.array([1e-39, 1e-45, np.float32(2.0 ** -126), 1.0], dtype=np.float32)
+    rng = np.random.default_rng(34)
+    seed = rng.integers(0, 2**64, size=4, dtype=np.uint64)
+    off = np.zeros(4, dtype=np.uint64)
+    mu = np.full(4, -6.0, dtype=np.float32) if hlg else None
+    w = W.Workload("tiny T", torch.from_numpy(x), T, seed, off, K=2, hlg=hlg, mu=mu)
+    g = gpu_sample(hs, w)
+    o, s1, s2 = oracle_sample(oracle_mod, w)
+    assert g[0].tolist() == [-2, -2] and g[1].tolist() == [-2, -2]
+    assert o[0].tolist() == [-2, -2] and o[1].tolist() == [-2, -2]
+    assert_parity(g, o, s1, s2, x.astype(np.float64), "tiny T hlg=%s" % bool(hlg))
+    assert g[2].tolist() == [int(np.argmax(x[2]))] * 2
+
+
+def test_rolloff_off_equals_temperature(hs, oracle_mod):
     """Rolloff off (w = inf) with gain m is temperature 1/m (HLG design document, section
     "The degeneracies are the safety anchors"): the same draws as the curve-off path at
-    temperature T/m, the log-softmax shift being common to all tokens."""
+    temperature T/m, the log-softmax shift being common to all tokens. Each path is checked
+    against the oracle's own run of it; where the two paths' ids differ, both oracle runs must
+    call the draw a near-tie."""
     w = W.generic(16, 20000, torch.float32, seed=41, K=4)
     d = on_device(w)
     m = 1.0 / 0.7
-    a = hs.sample(d["logits"], d["T"], d["seed"], d["offset"], mu=torch.zeros(16, device="cuda"),
-                  hlg=(m, math.inf, 1.0, 1.0), k=4).cpu().numpy()
-    b = hs.sample(d["logits"], d["T"] / m, d["seed"], d["offset"], k=4).cpu().numpy()
-    # the two paths round differently ((x - LSE - mu) * m/T against x * m/T), which can only
-    # flip a near-tie
-    assert (a != b).sum() <= 1
+    hlg = {"m": m, "w": math.inf, "beta_t": 1.0, "beta_h": 1.0}
+    mu = np.zeros(16, dtype=np.float32)
+    a = hs.sample(d["logits"], d["T"], d["seed"], d["offset"], mu=torch.from_numpy(mu).cuda(),
+                  hlg=hlg, k=4).cpu().numpy()
+    Tm = (d["T"] / m)
+    b = hs.sample(d["logits"], Tm, d["seed"], d["offset"], k=4).cpu().numpy()
+    x64 = w.logits.double().numpy()
+    rows = np.arange(16, dtype=np.int64)
+    oa, a1, a2 = oracle_mod.sample(w.logits, w.T, w.seed, w.offset, K=4, mu=mu, hlg=hlg,
+                                   row_id=rows)
+    ob, b1, b2 = oracle_mod.sample(w.logits, Tm.cpu().numpy(), w.seed, w.offset, K=4,
+                                   row_id=rows)
+    print(assert_parity(a, oa, a1, a2, x64, "rolloff off"))
+    print(assert_parity(b, ob, b1, b2, x64, "temperature T/m"))
+
+    def near(s1, s2):
+        return np.abs(s1 - s2) < 1e-6 * np.maximum(np.abs(s1), np.abs(s2))
+    diff = a != b
+    assert np.all(near(a1, a2)[diff] & near(b1, b2)[diff]), np.argwhere(diff)
 
 
-def test_offsets_wrap(hs, oracle_mod):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_offsets_wrap(hs, oracle_mod, layout):
     w = W.generic(4, 5000, torch.float32, seed=51, K=5)
     w.offset = np.array([2**64 - 2, 2**32 - 3, 0, 2**63], dtype=np.uint64)
-    _check(hs, oracle_mod, w, "offset wrap")
+    _check(hs, oracle_mod, w, "offset wrap", layout=layout)
 
 
+@pytest.mark.parametrize("layout,dtype,V", [("plain", torch.bfloat16, 151936),
+                                            ("screened", torch.bfloat16, 151936),
+                                            ("screened", torch.float32, 70001),
+                                            ("screened", torch.float16, 33331)])
 @pytest.mark.parametrize("hlg", [None, HLG_A])
-def test_variant_invariance(hs, oracle_mod, hlg):
-    w = W.generic(6, 151936, torch.bfloat16, seed=61, scale=0.8, mask_frac=0.05, hlg=hlg, K=3)
+def test_variant_invariance(hs, oracle_mod, hlg, layout, dtype, V):
+    w = W.generic(6, V, dtype, seed=61, scale=0.8, mask_frac=0.05, hlg=hlg, K=3)
     d = on_device(w)
-    o, s1, s2 = oracle_sample(oracle_mod, w)
+    o, s1, s2 = oracle_sample(oracle_mod, w, layout=layout)
     x64 = w.logits.double().numpy()
     results = {}
     for name, opts in [("auto", None),
@@ -127,11 +176,13 @@ def test_variant_invariance(hs, oracle_mod, hlg):
                                                                 exchange_wait=-1)),
                        ("split64-exchange", hs.SampleOpts(variant=2, nchunk=64, draw_groups=1,
                                                           split_lse=2))]:
+        opts = opts or hs.SampleOpts()
+        opts.layout = hs.LAYOUTS[layout]
         idx, best = hs.sample_ex(d["logits"], d["T"], d["seed"], d["offset"], mu=d.get("mu"),
                                  hlg=hlg, k=3, opts=opts, want_best=True)
         idx = idx.cpu().numpy()
         results[name] = (idx, best.cpu().numpy())
-        assert_parity(idx, o, s1, s2, x64, name)
+        assert_parity(idx, o, s1, s2, x64, "%s %s" % (name, layout))
     # screening never changes a result: same variant, screened vs exhaustive, bit-identical;
     # nor does which block works out a chunk's log-sum-exp partial in the exchange
     for a, b in [("one-block", "one-block-exhaustive"), ("split7", "split7-exhaustive"),

@@ -39,8 +39,9 @@ def _check_rows(hs, O, w, k, p, label, opts=None, want_best=False):
     kt = torch.from_numpy(k).cuda()
     pt = torch.from_numpy(p).cuda()
     tau_g = hs.filter_threshold(d["logits"], d["T"], top_k=kt, top_p=pt).cpu().numpy()
+    layout = "screened" if (opts is not None and opts.layout == 1) else "plain"
     o, s1, s2, tau_o, amb = O.sample_filtered(w.logits, w.T, w.seed, w.offset, K=w.K, top_k=k,
-                                              top_p=p)
+                                              top_p=p, layout=layout)
     x64 = w.logits.double().numpy()
     # thresholds
     for r in range(w.B):
@@ -126,8 +127,9 @@ def _row_marks(hs, ws, B, V, K, dtype):
     return ws[off:off + 4 * B].view(torch.int32).cpu().numpy()
 
 
+@pytest.mark.parametrize("layout", ["plain", "screened"])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
-def test_fused_draws_match_the_sampler(hs, oracle_mod, dtype):
+def test_fused_draws_match_the_sampler(hs, oracle_mod, dtype, layout):
     """Rows that keep few tokens are drawn by the threshold kernel (automatic plan); the
     sampling kernel on every row (an explicit variant) gives the same ids and scores."""
     B, V, K = 8, 60001, 7
@@ -136,17 +138,20 @@ def test_fused_draws_match_the_sampler(hs, oracle_mod, dtype):
     p = np.array([1.0, 1.0, 0.9, 1.0, 1.0, 0.3, 0.5, 1.0], dtype=np.float32)
     d = on_device(w)
     kt, pt = torch.from_numpy(k).cuda(), torch.from_numpy(p).cuda()
+    lay = hs.LAYOUTS[layout]
     ws = hs.workspace(B, V, K, dtype, False)
     g, bs = hs.sample_filtered(d["logits"], d["T"], d["seed"], d["offset"], top_k=kt, top_p=pt,
-                               k=K, ws=ws, want_best=True)
+                               k=K, ws=ws, want_best=True, opts=hs.SampleOpts(layout=lay))
     marks = _row_marks(hs, ws, B, V, K, dtype)
     assert marks[0] == 1 and marks[1] == 1 and marks[2] == 1, marks   # a few dozen kept tokens
     assert marks[4] == 0, marks                                         # over 2048 kept
     r, rb = hs.sample_filtered(d["logits"], d["T"], d["seed"], d["offset"], top_k=kt,
-                               top_p=pt, k=K, opts=hs.SampleOpts(variant=1), want_best=True)
+                               top_p=pt, k=K, opts=hs.SampleOpts(variant=1, layout=lay),
+                               want_best=True)
     np.testing.assert_array_equal(g.cpu().numpy(), r.cpu().numpy())
     np.testing.assert_array_equal(bs.cpu().numpy(), rb.cpu().numpy())
-    _check_rows(hs, oracle_mod, w, k, p, "fused %s" % dtype)
+    _check_rows(hs, oracle_mod, w, k, p, "fused %s %s" % (dtype, layout),
+                opts=hs.SampleOpts(layout=lay))
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])

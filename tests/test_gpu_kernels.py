@@ -36,14 +36,16 @@ def test_philox_kat_and_random(hs, oracle_mod):
     np.testing.assert_array_equal(got, oracle_mod.philox4x32_10(ctr, key))
 
 
+@pytest.mark.parametrize("layout", ["plain", "screened"])
 @pytest.mark.parametrize("V", [1, 5, 37, 4096, 151936])
-def test_stream_words_bit_exact(hs, oracle_mod, V):
+def test_stream_words_bit_exact(hs, oracle_mod, V, layout):
     seeds = np.array([0, 2**64 - 1, 0x0123456789ABCDEF], dtype=np.uint64)
     offs = np.array([0, 2**32 - 1, 2**64 - 3], dtype=np.uint64)
     for k in (0, 1, 5):
-        got = hs.stream_words(seeds, offs, 3, V, k).cpu().numpy().view(np.uint32)
+        got = hs.stream_words(seeds, offs, 3, V, k, layout=layout).cpu().numpy().view(np.uint32)
         for b in range(3):
-            want = oracle_mod.stream_words(int(seeds[b]), b, (int(offs[b]) + k) % 2**64, V)
+            want = oracle_mod.stream_words(int(seeds[b]), b, (int(offs[b]) + k) % 2**64, V,
+                                           layout=layout)
             np.testing.assert_array_equal(got[b], want)
 
 

@@ -173,26 +173,28 @@ def test_top_anchor_shift_invariance(hs):
     np.testing.assert_array_equal(a, b)
 
 
+@pytest.mark.parametrize("layout", ["plain", "screened"])
 @pytest.mark.parametrize("mode,off", [("top", 2.0), ("entropy", 0.0)])
-def test_pivot_headline_shape(hs, oracle_mod, mode, off):
+def test_pivot_headline_shape(hs, oracle_mod, mode, off, layout):
     """256 x 151936 bf16 logits, the headline sampling shape, with an anchored pivot."""
     w = W.config4()
     w.hlg = _curve(mode, off, w.hlg)
-    g = gpu_sample(hs, w)
-    o, s1, s2 = oracle_sample(oracle_mod, w)
-    print(assert_parity(g, o, s1, s2, w.logits.double().numpy(), "256x151936 %s" % mode))
+    g = gpu_sample(hs, w, layout=layout)
+    o, s1, s2 = oracle_sample(oracle_mod, w, layout=layout)
+    print(assert_parity(g, o, s1, s2, w.logits.double().numpy(),
+                        "256x151936 %s %s" % (mode, layout)))
 
 
-def test_pivot_many_draws_split_rows(hs, oracle_mod):
-    """64 x 262144 fp32, 16 draws per row, entropy anchor: rows split over blocks with the
-    pre-pass, checked on a sample of rows."""
+@pytest.mark.parametrize("layout", ["plain", "screened"])
+def test_pivot_many_draws_split_rows(hs, oracle_mod, layout):
+    """64 x 262144 fp32, 16 draws per row, entropy anchor: rows split over blocks, every row
+    against the oracle."""
     w = W.config5(B=64)
     w.hlg = _curve("entropy", 0.0, w.hlg)
     d = on_device(w)
-    g = gpu_sample(hs, w, dev=d)
-    rows = np.sort(np.random.default_rng(57).choice(w.B, size=12, replace=False))
-    o, s1, s2 = oracle_sample(oracle_mod, w, rows=rows)
-    print(assert_parity(g[rows], o, s1, s2, w.logits[rows].double().numpy(), "entropy 16 draws"))
+    g = gpu_sample(hs, w, dev=d, layout=layout)
+    o, s1, s2 = oracle_sample(oracle_mod, w, layout=layout)
+    print(assert_parity(g, o, s1, s2, w.logits.double().numpy(), "entropy 16 draws " + layout))
 
 
 # ---- the mass-median pivot: mu = the log-prob at which the mass from the top first reaches
@@ -220,7 +222,8 @@ def test_median_pivot_sampling_variants(hs, oracle_mod, dtype, V):
     d = on_device(w)
     o, s1, s2 = oracle_sample(oracle_mod, w)
     sure = _median_sure(oracle_mod, w)
-    assert sure.sum() >= 3
+    # rows left out of the id comparison (their boundary is not decided): at most one
+    assert (~sure).sum() <= 1, (~sure).sum()
     x64 = w.logits.double().numpy()
     res = {}
     for name, opts in [("auto", None),
@@ -259,6 +262,7 @@ def test_median_pivot_special_rows(hs, oracle_mod):
     g = gpu_sample(hs, w)
     o, s1, s2 = oracle_sample(oracle_mod, w)
     sure = _median_sure(oracle_mod, w)
+    assert sure.all()
     x64 = w.logits.double().numpy()
     assert g[0].tolist() == [-1] * 4 and g[1].tolist() == [-2] * 4
     assert g[2].tolist() == [int(np.argmax(x64[2]))] * 4
@@ -269,19 +273,21 @@ def test_median_pivot_special_rows(hs, oracle_mod):
         gv = gpu_sample(hs, wv)
         ov, t1, t2 = oracle_sample(oracle_mod, wv)
         sv = _median_sure(oracle_mod, wv)
+        assert sv.all()
         assert_parity(gv[sv], ov[sv], t1[sv], t2[sv], wv.logits.double().numpy()[sv],
                       "median V=%d" % V)
 
 
 def test_median_pivot_headline_shape(hs, oracle_mod):
+    """Every row of the 256 x 151936 bf16 shape; a row whose median boundary is not decided
+    (none at this shape) would be left out of the id comparison, and at most one may be."""
     w = W.config4()
     w.hlg = _curve("median", 0.0, w.hlg)
     g = gpu_sample(hs, w)
-    rows = np.arange(0, w.B, 8)
-    o, s1, s2 = oracle_sample(oracle_mod, w, rows=rows)
-    B = len(rows)
-    sure = _median_sure(oracle_mod, W.Workload("rows", w.logits[rows], w.T[rows], w.seed[rows],
-                                               w.offset[rows], K=w.K))
-    assert sure.sum() >= B // 2
-    assert_parity(g[rows][sure], o[sure], s1[sure], s2[sure],
-                  w.logits[rows].double().numpy()[sure], "median 256x151936")
+    o, s1, s2 = oracle_sample(oracle_mod, w)
+    sure = _median_sure(oracle_mod, w)
+    assert (~sure).sum() <= 1, (~sure).sum()
+    x64 = w.logits.double().numpy()
+    assert np.all(np.isfinite(x64[np.arange(w.B)[:, None], g]))
+    print(assert_parity(g[sure], o[sure], s1[sure], s2[sure], x64[sure], "median 256x151936"),
+          "rows left out:", int((~sure).sum()))

@@ -38,7 +38,7 @@ def hs():
     return require_gpu()
 
 
-def _oracle_rows(O, w, settings, bad=()):
+def _oracle_rows(O, w, settings, bad=(), layout="plain"):
     """Per-row oracle results: ids, best and second-best scores [B, K]; rows in bad give -2."""
     B, K = w.B, w.K
     idx = np.zeros((B, K), dtype=np.int64)
@@ -54,7 +54,7 @@ def _oracle_rows(O, w, settings, bad=()):
             mu = w.mu[r:r + 1] if h.get("pivot", "input") == "input" else None
         o, a1, a2 = O.sample(w.logits[r:r + 1], w.T[r:r + 1], w.seed[r:r + 1],
                              w.offset[r:r + 1], K=K, mu=mu, hlg=h,
-                             row_id=np.array([r], dtype=np.int64))
+                             row_id=np.array([r], dtype=np.int64), layout=layout)
         idx[r], s1[r], s2[r] = o[0], a1[0], a2[0]
     return idx, s1, s2
 
@@ -138,8 +138,10 @@ def test_uniform_rows_equal_per_call(hs, setting, variant):
     w = W.generic(B, V, torch.bfloat16, seed=29, scale=1.2, mask_frac=0.02, hlg=dict(A), K=K)
     w.T[3] = 0.0
     d = on_device(w)
+    median = setting is not None and setting.get("pivot") == "median"
     opts = hs.SampleOpts(variant=1) if variant == "one-block" else hs.SampleOpts(variant=2,
                                                                                  nchunk=7)
+    opts.median_rows = int(median)   # the caller says whether any row asks for the median
     rows = hs.hlg_rows([setting] * B)
     g, gb = hs.sample_rows(d["logits"], d["T"], d["seed"], d["offset"], rows, mu=d["mu"], k=K,
                            opts=opts, want_best=True)
@@ -167,20 +169,29 @@ def test_mixed_rows_with_median(hs, oracle_mod, dtype, V):
     sure = ~med | _median_sure(oracle_mod, w)
     x64 = w.logits.double().numpy()
     rows = hs.hlg_rows(settings)
-    for name, opts in [("auto", None), ("split7", hs.SampleOpts(variant=2, nchunk=7))]:
+    assert (~sure).sum() <= 1, (~sure).sum()
+    for name, opts in [("auto", hs.SampleOpts(median_rows=1)),
+                       ("split7", hs.SampleOpts(variant=2, nchunk=7, median_rows=1))]:
         g = hs.sample_rows(d["logits"], d["T"], d["seed"], d["offset"], rows, mu=d["mu"], k=K,
                            opts=opts).cpu().numpy()
         assert_parity(g[sure], o[sure], s1[sure], s2[sure], x64[sure],
                       "rows with median %s %s" % (dtype, name))
         assert np.all(g >= 0)
+    # without median_rows no shift launch runs: the median rows give -2, the others the same
+    gn = hs.sample_rows(d["logits"], d["T"], d["seed"], d["offset"], rows, mu=d["mu"],
+                        k=K).cpu().numpy()
+    assert np.all(gn[med] == -2)
+    np.testing.assert_array_equal(gn[~med], g[~med])
 
 
-def test_mixed_rows_headline_shape(hs, oracle_mod):
+@pytest.mark.parametrize("layout", ["plain", "screened"])
+def test_mixed_rows_headline_shape(hs, oracle_mod, layout):
     """256 x 151936 bf16, the headline shape, with the eight settings cycled over the rows."""
     w = W.config4()
     settings = _cycle(w.B)
     d = on_device(w)
     g = hs.sample_rows(d["logits"], d["T"], d["seed"], d["offset"], hs.hlg_rows(settings),
-                       mu=d["mu"], k=1).cpu().numpy()
-    o, s1, s2 = _oracle_rows(oracle_mod, w, settings)
-    print(assert_parity(g, o, s1, s2, w.logits.double().numpy(), "mixed 256x151936"))
+                       mu=d["mu"], k=1,
+                       opts=hs.SampleOpts(layout=hs.LAYOUTS[layout])).cpu().numpy()
+    o, s1, s2 = _oracle_rows(oracle_mod, w, settings, layout=layout)
+    print(assert_parity(g, o, s1, s2, w.logits.double().numpy(), "mixed 256x151936 " + layout))
