@@ -229,6 +229,23 @@ int hs_sample_rows(const hs_logits *x, const float *T, const float *mu, const hs
                    float *best, void *ws, size_t ws_bytes, const hs_sample_opts *opts,
                    void *stream);
 
+/* hs_sample_ex without a workspace argument, for callers that cannot allocate (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): the workspace
+ * comes from a static device array of hs_sample_noalloc_max_workspace() bytes (4 MiB) that the
+ * library holds on every GPU it runs on until the process ends. A shape whose workspace
+ * (hs_workspace_bytes) exceeds it gives HS_ERR_UNSUPPORTED. The first call on a device
+ * zero-fills the array on `stream`; every call leaves it zero-filled again. All calls on one
+ * GPU share its array: calls that overlap in time on one GPU (concurrent streams, or
+ * unsynchronised host threads) race and their results are undefined. No hipMalloc, hipFree
+ * or allocating library routine is called. Ids and scores equal hs_sample_ex's. */
+int hs_sample_noalloc(const hs_logits *x, const float *T, const float *mu,
+                      const hs_hlg_params *hlg, const uint64_t *seed, const uint64_t *offset,
+                      int32_t K, int32_t *out, float *best, const hs_sample_opts *opts,
+                      void *stream);
+
+/* Size in bytes of hs_sample_noalloc's static workspace. */
+size_t hs_sample_noalloc_max_workspace(void);
+
 /* Top-k / top-p filters on the Gumbel path, curve off (the follow-on [GMX] names without an
  * algorithm; the reading taken): temperature first, then top-k, then top-p on the tempered
  * probabilities of the tokens top-k keeps. Row b keeps every token with x >= tau[b]:

@@ -35,7 +35,8 @@ EXPORTED_SYMBOLS = (
     "hs_logsumexp", "hs_hlg_transform", "hs_hlg_pivot", "hs_gumbel_argmax", "hs_sample",
     "hs_sample_ex", "hs_sample_rows", "hs_filter_threshold", "hs_sample_filtered",
     "hs_workspace_bytes", "hs_workspace_init", "hs_sample_plan", "hs_philox4x32_10", "hs_stream_words",
-    "hs_stream_words_ex", "hs_gumbel_f32", "hs_status_str", "hs_version",
+    "hs_stream_words_ex", "hs_gumbel_f32", "hs_status_str", "hs_version", "hs_sample_noalloc",
+    "hs_sample_noalloc_max_workspace",
 )
 # word layouts of the random stream (hs_layout)
 LAYOUTS = {"plain": 0, "screened": 1}
@@ -121,6 +122,9 @@ def load() -> C.CDLL:
     L.hs_gumbel_argmax.argtypes = [LP, vp, vp, vp, i32, vp, vp, sz, vp]
     L.hs_sample.argtypes = [LP, vp, vp, HP, vp, vp, i32, vp, vp, sz, vp]
     L.hs_sample_ex.argtypes = [LP, vp, vp, HP, vp, vp, i32, vp, vp, vp, sz, OP, vp]
+    L.hs_sample_noalloc.argtypes = [LP, vp, vp, HP, vp, vp, i32, vp, vp, OP, vp]
+    L.hs_sample_noalloc_max_workspace.argtypes = []
+    L.hs_sample_noalloc_max_workspace.restype = sz
     L.hs_sample_rows.argtypes = [LP, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, OP, vp]
     L.hs_filter_threshold.argtypes = [LP, vp, vp, vp, vp, vp]
     L.hs_sample_filtered.argtypes = [LP, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, OP, vp]
@@ -140,7 +144,7 @@ def load() -> C.CDLL:
     for name in ("hs_logsumexp", "hs_hlg_transform", "hs_hlg_pivot", "hs_gumbel_argmax", "hs_sample",
                  "hs_sample_ex", "hs_sample_rows", "hs_filter_threshold", "hs_sample_filtered",
                  "hs_workspace_init", "hs_philox4x32_10", "hs_stream_words",
-                 "hs_stream_words_ex", "hs_gumbel_f32"):
+                 "hs_stream_words_ex", "hs_gumbel_f32", "hs_sample_noalloc"):
         getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -283,6 +287,31 @@ def sample_ex(logits: torch.Tensor, T, seed, offset, *, mu=None, hlg=None, k: in
                         ws.data_ptr(), ws.numel(), C.byref(opts) if opts is not None else None,
                         _stream(dev))
     _check(rc, "hs_sample_ex")
+    return (out, best) if want_best else out
+
+
+def sample_noalloc(logits: torch.Tensor, T, seed, offset, *, mu=None, hlg=None, k: int = 1,
+                   out: Optional[torch.Tensor] = None, opts: Optional[SampleOpts] = None,
+                   want_best: bool = False):
+    """sample_ex with the library's static workspace (hs_sample_noalloc): the library allocates
+    nothing. out (and the scores, with want_best) are allocated here unless out is given."""
+    L = load()
+    x = _logits_struct(logits)
+    dev = logits.device
+    B = logits.shape[0]
+    Tt = _row_vec(T, B, torch.float32, dev, "T")
+    st = _row_vec(seed, B, torch.int64, dev, "seed")
+    of = _row_vec(offset, B, torch.int64, dev, "offset")
+    hp = _hlg_struct(hlg)
+    mut = _mu_vec(mu, hp, B, dev)
+    if out is None:
+        out = torch.empty((B, k), dtype=torch.int32, device=dev)
+    best = torch.empty((B, k), dtype=torch.float32, device=dev) if want_best else None
+    rc = L.hs_sample_noalloc(C.byref(x), Tt.data_ptr(), _ptr(mut),
+                             C.byref(hp) if hp is not None else None, st.data_ptr(),
+                             of.data_ptr(), int(k), out.data_ptr(), _ptr(best),
+                             C.byref(opts) if opts is not None else None, _stream(dev))
+    _check(rc, "hs_sample_noalloc")
     return (out, best) if want_best else out
 
 

@@ -6,8 +6,17 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/hs.h"
 #include "hs_internal.hpp"
+
+// The workspace of hs_sample_noalloc, for callers that cannot allocate: a file-scope device
+// array (each GPU the library runs on holds its own copy until the process ends). Host code
+// never passes the array's name to a kernel: it takes each device's address from
+// hipGetSymbolAddress once (scratch_for_device) and uses only that.
+constexpr size_t kScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -324,6 +333,29 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
     return HS_OK;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];
+
+// The current device's scratch address. On a device's first use: the symbol's address on that
+// device (the device is current), and a zero fill of the whole array on the caller's stream,
+// since the workspace must start zero-filled (every successful call leaves it so again).
+int scratch_for_device(hipStream_t s, void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return HS_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return HS_ERR_HIP;
+        if (hs::launch_fill_zero(p, (int64_t)(kScratchBytes / 4), s) != hipSuccess)
+            return HS_ERR_HIP;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return HS_OK;
+}
+
 }  // namespace
 
 // The mass median of every row (the threshold kernel's top-p selection at p = 0.5, T = 1)
@@ -438,6 +470,32 @@ int hs_sample_ex(const hs_logits *x, const float *T, const float *mu, const hs_h
     return sample_impl(x, T, mu, hlg, nullptr, seed, offset, K, out, best, ws, ws_bytes, opts,
                        stream);
 }
+
+int hs_sample_noalloc(const hs_logits *x, const float *T, const float *mu,
+                      const hs_hlg_params *hlg, const uint64_t *seed, const uint64_t *offset,
+                      int32_t K, int32_t *out, float *best, const hs_sample_opts *opts,
+                      void *stream) {
+    // every host-checkable argument first, so that a bad call touches no device
+    if (!opts_valid(opts)) return HS_ERR_INVALID_ARG;
+    int rc = check_logits(x);
+    if (rc) return rc;
+    if (!T || !seed || !offset || !out || K < 1) return HS_ERR_INVALID_ARG;
+    if (hlg) {
+        rc = check_curve(hlg);
+        if (rc) return rc;
+        if (hlg->pivot == HS_PIVOT_GIVEN && !mu) return HS_ERR_INVALID_ARG;
+    }
+    if ((size_t)x->B * (size_t)K >= ((size_t)1 << 31)) return HS_ERR_UNSUPPORTED;
+    const size_t need = ws_layout(x->B, K).total;
+    if (need > kScratchBytes) return HS_ERR_UNSUPPORTED;
+    void *ws = nullptr;
+    rc = scratch_for_device(reinterpret_cast<hipStream_t>(stream), &ws);
+    if (rc) return rc;
+    return sample_impl(x, T, mu, hlg, nullptr, seed, offset, K, out, best, ws, need, opts,
+                       stream);
+}
+
+size_t hs_sample_noalloc_max_workspace(void) { return kScratchBytes; }
 
 int hs_filter_threshold(const hs_logits *x, const float *T, const int32_t *top_k,
                         const float *top_p, float *tau, void *stream) {

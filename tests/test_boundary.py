@@ -258,6 +258,41 @@ def test_aux_entry_points(lib):
     assert lib.hs_stream_words(FAKE, None, 1, 10, 0, FAKE, None) == HS_ERR_INVALID_ARG
     assert lib.hs_gumbel_f32(None, FAKE, 3, None) == HS_ERR_INVALID_ARG
     assert lib.hs_gumbel_f32(FAKE, FAKE, 0, None) == HS_OK
+    assert lib.hs_stream_words_ex(FAKE, FAKE, 1, 10, 0, 2, FAKE, None) == HS_ERR_INVALID_ARG
+    assert lib.hs_stream_words_ex(FAKE, FAKE, 1, 10, 0, -1, FAKE, None) == HS_ERR_INVALID_ARG
+
+
+def test_sample_opts_layout_is_validated(lib):
+    x = L()
+    for lay in (-1, 2):
+        o = hs.SampleOpts(layout=lay)
+        assert lib.hs_sample_ex(C.byref(x), FAKE, None, None, FAKE, FAKE, 1, FAKE, None, None, 0,
+                                C.byref(o), None) == HS_ERR_INVALID_ARG
+
+
+def test_noalloc_arguments(lib):
+    """The allocation-free entry point checks every host-side argument before it touches a
+    device, and refuses shapes whose workspace exceeds its static array."""
+    cap = lib.hs_sample_noalloc_max_workspace()
+    assert cap == 4 << 20
+
+    def call(x, K=1, T=FAKE, out=FAKE, hlg=None, mu=FAKE, opts=None):
+        return lib.hs_sample_noalloc(C.byref(x), T, mu, C.byref(hlg) if hlg else None, FAKE,
+                                     FAKE, K, out, None, C.byref(opts) if opts else None, None)
+    assert call(L(data=0)) == HS_ERR_INVALID_ARG
+    assert call(L(dtype=9)) == HS_ERR_DTYPE
+    assert call(L(), K=0) == HS_ERR_INVALID_ARG
+    assert call(L(), T=None) == HS_ERR_INVALID_ARG
+    assert call(L(), out=None) == HS_ERR_INVALID_ARG
+    assert call(L(), hlg=H(m=-1.0)) == HS_ERR_INVALID_ARG
+    assert call(L(), hlg=H(), mu=None) == HS_ERR_INVALID_ARG
+    assert call(L(), opts=hs.SampleOpts(layout=5)) == HS_ERR_INVALID_ARG
+    # workspace past the static array: B = 8192 rows need 8192 * (64 * 20) bytes of partials
+    # and flags alone
+    big = L(B=8192, V=1000)
+    assert lib.hs_workspace_bytes(8192, 1000, 1, 0, 1) > cap
+    assert call(big) == HS_ERR_UNSUPPORTED
+    assert call(L(B=64, V=1000), K=8192) == HS_ERR_UNSUPPORTED   # 6 MiB of counters and keys
 
 
 def test_python_binding_refuses_cpu_tensors():
