@@ -164,6 +164,9 @@ int make_plan(const hs_logits *x, int32_t K, bool hlg, bool ws_ok, const hs_samp
     if (nchunk < nchunk_min) return HS_ERR_UNSUPPORTED;
     if (nchunk < 1) nchunk = 1;
     int64_t cv = (nvec + nchunk - 1) / nchunk;
+    // fp32 chunks hold an even number of vectors: in the screened word layout the two lanes
+    // whose vectors make up one eight-element group share its Philox call
+    if (epv_of(x->dtype) == 4 && nchunk > 1 && (cv & 1)) ++cv;
     nchunk = (nvec + cv - 1) / cv;
     if (nchunk > 1 && !ws_ok) return HS_ERR_WORKSPACE;
     int bs = 0, nv = 0;

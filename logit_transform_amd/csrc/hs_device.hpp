@@ -80,20 +80,31 @@ __device__ __forceinline__ uint32_t xor3_sk(uint32_t a, uint32_t b, uint32_t k) 
     return __builtin_amdgcn_bitop3_b32(a, b, k, 0x96);
 }
 
-__device__ __forceinline__ Words4 philox4x32_10_uk(uint32_t c0, uint32_t c1, uint32_t c2,
-                                                   uint32_t c3, uint32_t k0, uint32_t k1) {
+// The rounds of a call whose counter word 0 alone is per lane (c0 = cl + delta: the lane's part
+// and a wave-uniform part, cl + delta < 2^32); counter words 1..3 and the key are wave-uniform.
+// Which words are uniform after each round: round 0 leaves c0, c1 uniform; round 1 leaves c3
+// uniform, so round 2's second xor takes the scalar c3 ^ k1 in one instruction; from round 3 on
+// every word is per lane and each xor pair is one v_bitop3_b32. (A vector multiply-add reads
+// one scalar operand, the multiplier, so delta cannot ride in the first multiply's addend.)
+__device__ __forceinline__ Words4 philox4x32_10_lane(uint32_t cl, uint32_t delta, uint32_t c1,
+                                                     uint32_t c2, uint32_t c3, uint32_t k0,
+                                                     uint32_t k1) {
+    uint32_t c0 = 0;
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
         if (r > 0) {
             k0 += 0x9E3779B9u;
             k1 += 0xBB67AE85u;
         }
-        const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u;
+        const uint64_t p0 = (uint64_t)(r == 0 ? cl + delta : c0) * 0xD2511F53u;
         const uint64_t p1 = (uint64_t)c2 * 0xCD9E8D57u;
         uint32_t n0, n2;
         if (r < 2) {
             n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
             n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        } else if (r == 2) {
+            n0 = xor3_sk((uint32_t)(p1 >> 32), c1, k0);
+            n2 = (uint32_t)(p0 >> 32) ^ (c3 ^ k1);
         } else {
             n0 = xor3_sk((uint32_t)(p1 >> 32), c1, k0);
             n2 = xor3_sk((uint32_t)(p0 >> 32), c3, k1);
@@ -109,6 +120,11 @@ __device__ __forceinline__ Words4 philox4x32_10_uk(uint32_t c0, uint32_t c1, uin
     o.w[2] = c2;
     o.w[3] = c3;
     return o;
+}
+
+__device__ __forceinline__ Words4 philox4x32_10_uk(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                   uint32_t c3, uint32_t k0, uint32_t k1) {
+    return philox4x32_10_lane(c0, 0u, c1, c2, c3, k0, k1);
 }
 
 // Random words of the element group q (elements 4q..4q+3) of draw stream (seed, row, off)
@@ -276,6 +292,11 @@ __device__ __forceinline__ float key_score(uint64_t k) {
 }
 
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Buffer resources (gfx950): the fourth word of a raw byte buffer, and the cache-policy bits
+// of a load that streams data read once (non-temporal).
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kCachePolicyNT = 2;
 
 // ------------------------------------------------------------------------------------------
 // Loads: 16-byte vectors of 4 fp32 or 8 bf16/f16 logits, upcast exactly to fp32 on use.

@@ -221,7 +221,7 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     __shared__ float red_m[16], red_s[16], red_u[16], red_x[16];
     __shared__ uint64_t red_ck[16];    // per wave: best bootstrap candidate key
     __shared__ float red_cx[16];       //   its logit
-    __shared__ uint32_t red_cw[16];    //   and word
+    __shared__ float red_cg[16];       //   and the Gumbel value of its word
     __shared__ float row_bc[12];       // row constants from wave 0
     // per wave, the best exact candidate score of a later draw; two buffers, alternating
     // between draws (a wave may post draw k + 1's before a slower one has read draw k's)
@@ -326,13 +326,12 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
         if (gv >= vend) return ninf4;
         return load_vec<DT>(rowp, gv, a.V, ALIGNED);
     };
-    // ALIGNED: slot n's load carries no branch (a slot past the whole vectors reads an in-row
-    // whole vector instead, clamped index) and is patched when its data is used, with selects
-    // only: a load inside the pipelined pass would make the compiler wait for every load in
-    // flight. The row's partial last vector (V not a multiple of EPV) is read element by
-    // element up front by every lane, with clamped addresses (one cache line, no branch); only
-    // waves that reach past vlim at slot n test per lane.
-    const int gclamp = vlim - 1;   // >= 0: the launcher ensures V >= epv for ALIGNED
+    // ALIGNED: slot n's load carries no branch (a lane past the chunk's whole vectors reads
+    // zeros, see issue_load) and is patched when its data is used, with selects only: a load
+    // inside the pipelined pass would make the compiler wait for every load in flight. The
+    // row's partial last vector (V not a multiple of EPV) is read element by element up front
+    // by every lane, with clamped addresses (one cache line, no branch); only waves that reach
+    // past vlim at slot n test per lane.
     uint4 rag = ninf4;
     if constexpr (ALIGNED) {
         uint32_t w[4];
@@ -362,13 +361,18 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     }
     // The streaming pass reads every vector once: its loads carry the non-temporal hint (on
     // MI355X a row-per-block read of the 256 x 151936 bf16 shape runs at ~75% of the HBM peak
-    // with it, ~65% without).
+    // with it, ~65% without). They are buffer loads through one resource that spans the
+    // chunk's whole vectors: a lane past them reads zeros without touching memory (its vector
+    // is patched before use), so no lane clamps its offset.
+    const uint32_t lane16 = (uint32_t)tid * 16u;
+    const __amdgpu_buffer_rsrc_t chunk_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(rowp + (uint32_t)min(v0, vlim) * 16u), (short)0,
+        max(0, vlim - v0) * 16, kBufferWord3);
     auto issue_load = [&](int n) -> uint4 {
         if constexpr (ALIGNED) {
-            const int gv = min(lane_v + n * BS, gclamp);
             typedef unsigned int u4v __attribute__((ext_vector_type(4)));
-            const u4v t = __builtin_nontemporal_load(
-                reinterpret_cast<const u4v *>(rowp + (uint32_t)gv * 16u));
+            const u4v t = __builtin_amdgcn_raw_buffer_load_b128(
+                chunk_rsrc, lane16 + (uint32_t)(n * BS) * 16u, 0, kCachePolicyNT);
             return make_uint4(t.x, t.y, t.z, t.w);
         } else {
             return fetch(lane_v + n * BS);
@@ -413,28 +417,35 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     auto draw_vec = [&](const Stream &sk, int n) -> uint32_t {
         uint32_t code, key;
         if constexpr (LAY == LAY_PLAIN) {
-            uint32_t q = (uint32_t)(lane_v + n * BS) * NG;
-            asm volatile("" : "+v"(q));
+            // counter word (lane_v + n BS) NG: the lane's part, and the slot's (uniform) part
+            uint32_t ql = (uint32_t)lane_v * NG;
+            asm volatile("" : "+v"(ql));
+            const uint32_t dq = (uint32_t)(n * BS * NG);
             uint32_t mw;
-            const Words4 w = philox4x32_10_uk(q, sk.row, sk.off_lo, sk.off_hi, sk.key0, sk.key1);
+            const Words4 w = philox4x32_10_lane(ql, dq, sk.row, sk.off_lo, sk.off_hi, sk.key0,
+                                                sk.key1);
             mw = max(max3u(w.w[0], w.w[1], w.w[2]), w.w[3]);
             if constexpr (NG == 2) {
-                const Words4 u = philox4x32_10_uk(q + 1, sk.row, sk.off_lo, sk.off_hi, sk.key0,
-                                                  sk.key1);
+                const Words4 u = philox4x32_10_lane(ql, dq + 1u, sk.row, sk.off_lo, sk.off_hi,
+                                                    sk.key0, sk.key1);
                 mw = max3u(max3u(w.w[0], w.w[1], w.w[2]), max3u(w.w[3], u.w[0], u.w[1]),
                            max(u.w[2], u.w[3]));
             }
             code = mw >> 16;
             key = (mw & ~31u) | (uint32_t)n;
         } else {
-            const uint32_t gv = (uint32_t)(lane_v + n * BS);
-            uint32_t q2 = EPV == 8 ? gv << 1 : gv & ~1u;
-            asm volatile("" : "+v"(q2));
-            const Words4 w = philox4x32_10_uk(q2, sk.row, sk.off_lo, sk.off_hi, sk.key0, sk.key1);
+            // counter word 2q of the group q of vector gv = lane_v + n BS: 2 gv for eight
+            // elements per vector, gv rounded down to even for four (BS is even, so the
+            // rounding is the lane's own: lane_v & ~1, plus the slot's n BS)
+            uint32_t ql = EPV == 8 ? (uint32_t)lane_v << 1 : (uint32_t)lane_v & ~1u;
+            asm volatile("" : "+v"(ql));
+            const uint32_t dq = EPV == 8 ? (uint32_t)(2 * n * BS) : (uint32_t)(n * BS);
+            const Words4 w = philox4x32_10_lane(ql, dq, sk.row, sk.off_lo, sk.off_hi, sk.key0,
+                                                sk.key1);
             if constexpr (EPV == 8) {
                 code = max_half16(max_half16_pk(w.w[0], w.w[1]), max_half16_pk(w.w[2], w.w[3]));
             } else {
-                const bool h = (gv & 1u) != 0u;
+                const bool h = ((uint32_t)lane_v & 1u) != 0u;
                 code = max_half16(h ? w.w[2] : w.w[0], h ? w.w[3] : w.w[1]);
             }
             key = (code << 16) | (uint32_t)n;
@@ -476,17 +487,88 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             }
         }
     };
+    // Screened layout: the leading halves of vector gv's words (low halves zero), and the
+    // second call that completes them.
+    auto vec_words_hi = [&](const Stream &sk, int gvi, uint32_t (&w)[EPV]) {
+        const uint32_t gv = (uint32_t)gvi;
+        uint32_t q2 = EPV == 8 ? gv << 1 : gv & ~1u;
+        asm volatile("" : "+v"(q2));
+        const Words4 hi = philox4x32_10_uk(q2, sk.row, sk.off_lo, sk.off_hi, sk.key0, sk.key1);
+        if constexpr (EPV == 8) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w[e] = half16(hi, e) << 16;
+        } else {
+            const bool h = (gv & 1u) != 0u;
+            const uint32_t h0 = h ? hi.w[2] : hi.w[0], h1 = h ? hi.w[3] : hi.w[1];
+            w[0] = h0 << 16;
+            w[1] = h0 & 0xFFFF0000u;
+            w[2] = h1 << 16;
+            w[3] = h1 & 0xFFFF0000u;
+        }
+    };
+    auto vec_words_lo = [&](const Stream &sk, int gvi, uint32_t (&w)[EPV]) {
+        const uint32_t gv = (uint32_t)gvi;
+        uint32_t q2 = EPV == 8 ? gv << 1 : gv & ~1u;
+        asm volatile("" : "+v"(q2));
+        const Words4 lo = philox4x32_10_uk(q2 | 1u, sk.row, sk.off_lo, sk.off_hi, sk.key0,
+                                           sk.key1);
+        if constexpr (EPV == 8) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w[e] |= half16(lo, e);
+        } else {
+            const bool h = (gv & 1u) != 0u;
+            const uint32_t l0 = h ? lo.w[2] : lo.w[0], l1 = h ? lo.w[3] : lo.w[1];
+            w[0] |= l0 & 0xFFFFu;
+            w[1] |= l0 >> 16;
+            w[2] |= l1 & 0xFFFFu;
+            w[3] |= l1 >> 16;
+        }
+    };
     // the bits of a word that the champion key holds: (w ^ key) <= kMatch when they agree
     constexpr uint32_t kMatch = LAY == LAY_PLAIN ? 31u : 0xFFFFu;
+    // Screened layout with four elements per vector: the two lanes whose vectors make up a group
+    // (lanes 2j and 2j + 1: a chunk starts at an even vector and BS is even) take turns, so each
+    // lane makes one call per two slots. For the slot pair (n, n + 1) the even lane draws the
+    // group of its slot n and the odd lane that of its slot n + 1; each keeps the half of the
+    // call that is its own and passes the other half's largest code to its neighbour (one DPP
+    // swap). Returns the keys of slots n and n + 1 (the second unused past the last slot).
+    constexpr bool PAIR = LAY == LAY_SCREENED && EPV == 4;
+    auto draw_pair = [&](const Stream &sk, int n, uint32_t &key0, uint32_t &key1) {
+        const uint32_t p = (uint32_t)lane_v & 1u;
+        uint32_t ql = ((uint32_t)lane_v & ~1u) + p * (uint32_t)BS;
+        asm volatile("" : "+v"(ql));
+        const Words4 w = philox4x32_10_lane(ql, (uint32_t)(n * BS), sk.row, sk.off_lo,
+                                            sk.off_hi, sk.key0, sk.key1);
+        const uint32_t mlo = max_half16(w.w[0], w.w[1]);   // elements 0..3: the even vector
+        const uint32_t mhi = max_half16(w.w[2], w.w[3]);   // elements 4..7: the odd vector
+        const uint32_t keep = p ? mhi : mlo;
+        const uint32_t recv = dpp_u32<kDppQuad1032>(p ? mlo : mhi);
+        const uint32_t c0 = p ? recv : keep;   // slot n
+        const uint32_t c1 = p ? keep : recv;   // slot n + 1
+        s_vec16[2 * (lane_lds + n) + 1] = (uint16_t)c0;
+        if (n + 1 < NV) s_vec16[2 * (lane_lds + n + 1) + 1] = (uint16_t)c1;
+        key0 = (c0 << 16) | (uint32_t)n;
+        key1 = (c1 << 16) | (uint32_t)(n + 1);
+    };
     // The lane's champion key over a whole draw (draws without the logits at hand).
     auto draw_all = [&](const Stream &sk) -> uint32_t {
         uint32_t champ = 0;
+        if constexpr (PAIR) {
 #pragma unroll
-        for (int n = 0; n < NV; ++n) {
-            champ = max(champ, draw_vec(sk, n));
-            // one running maximum: otherwise the compiler regroups the chain of maxima and
-            // keeps every slot's word alive until the end of the pass
-            asm volatile("" : "+v"(champ));
+            for (int n = 0; n < NV; n += 2) {
+                uint32_t ka, kb;
+                draw_pair(sk, n, ka, kb);
+                champ = n + 1 < NV ? max3u(champ, ka, kb) : max(champ, ka);
+                asm volatile("" : "+v"(champ));
+            }
+        } else {
+#pragma unroll
+            for (int n = 0; n < NV; ++n) {
+                champ = max(champ, draw_vec(sk, n));
+                // one running maximum: otherwise the compiler regroups the chain of maxima and
+                // keeps every slot's word alive until the end of the pass
+                asm volatile("" : "+v"(champ));
+            }
         }
         return champ;
     };
@@ -537,9 +619,12 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     const float lin = HLG ? cv.m * invT : invT;
     // Bootstrap candidate of a lane for draw stream sk: the element holding the largest word of
     // its champion vector v (nearly the largest Gumbel value among the lane's elements). The
-    // vector's words are drawn again into cw (kept for the screen). Returns the candidate's rank
-    // key (lin x - log(1 - u) -- a monotone stand-in for the Gumbel value, close to it where u
-    // is near 1 -- and the lane) and its logit and word.
+    // vector's words are drawn again into cw (kept for the screen); in the screened layout only
+    // their leading halves, with the low halves zero: a word no larger than the element's, so
+    // its Gumbel value bounds the element's from below, which is all the bootstrap needs (the
+    // screen completes the words if it scores the vector). Returns the candidate's rank key
+    // (lin x - log(1 - u) -- a monotone stand-in for the Gumbel value, close to it where u is
+    // near 1 -- and the lane) and its logit and word.
     struct Cand {
         uint64_t key;
         float x;
@@ -548,7 +633,11 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     auto candidate = [&](const Stream &sk, uint32_t champ, const uint4 &v,
                          uint32_t (&cw)[EPV]) -> Cand {
         Cand c{0ull, -__builtin_inff(), 0u};
-        vec_words(sk, lane_v + (int)(champ & 31u) * BS, cw);
+        if constexpr (LAY == LAY_PLAIN) {
+            vec_words(sk, lane_v + (int)(champ & 31u) * BS, cw);
+        } else {
+            vec_words_hi(sk, lane_v + (int)(champ & 31u) * BS, cw);
+        }
 #pragma unroll
         for (int e = EPV - 1; e >= 0; --e) {
             if ((cw[e] ^ champ) <= kMatch) {
@@ -576,18 +665,23 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     {
         const Stream sk = stream_k(k0);
         uint4 buf[D];
-        uint32_t ring[LAG + 1];   // slot keys between a slot's draw and its logits
+        constexpr int RING = LAG + 2;   // slot keys between a slot's draw and its logits
+        uint32_t ring[RING];
 #pragma unroll
         for (int n = 0; n < D; ++n) buf[n] = issue_load(n);
 #pragma unroll
         for (int n = 0; n < NV + LAG; ++n) {
-            if (n < NV) ring[n % (LAG + 1)] = draw_vec(sk, n);
+            if constexpr (PAIR) {
+                if (n < NV && (n & 1) == 0) draw_pair(sk, n, ring[n % RING], ring[(n + 1) % RING]);
+            } else {
+                if (n < NV) ring[n % RING] = draw_vec(sk, n);
+            }
             const int j = n - LAG;
             if (j >= 0 && j < NV) {
                 const uint4 v = patch(j, buf[j % D]);
                 data_vec(j, v);
                 // the champion's vector stays in registers (no second read)
-                const uint32_t kj = ring[j % (LAG + 1)];
+                const uint32_t kj = ring[j % RING];
                 if (kj > champ0) {
                     champ0 = kj;
                     craw0 = v;
@@ -631,20 +725,31 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     int wid = threadIdx.x >> 6;
     asm volatile("" : "+v"(wid));
     const int nw = (BS + 63) >> 6;
-    // Per wave, the best bootstrap candidate: its key, logit and word.
+    // Per wave, the best bootstrap candidate: its key, logit and the Gumbel value of its word
+    // (which needs no row constant, so each wave works it out before the block combine).
     auto post_candidate = [&](const Cand &c) {
         const uint64_t wk = wave_max_u64(c.key);
         if (lane == 0) red_ck[wid] = wk;
         if (wk != 0 && c.key == wk) {
             red_cx[wid] = c.x;
-            red_cw[wid] = c.w;
+            red_cg[wid] = gumbel32(c.w);
         }
     };
-    // (wave 0) The best exact score among the waves' bootstrap candidates: lane w scores wave
-    // w's (all at once, at the latency of one).
+    // (wave 0) The best score among the waves' bootstrap candidates, l'/T + G as
+    // exact_score_inl forms it: lane w scores wave w's (all at once, at the latency of one).
     auto candidate_score = [&]() -> float {
         const bool has = lane < nw && red_ck[lane] != 0ull;
-        const float cs = has ? exact_score<HLG>(red_cx[lane], red_cw[lane], rc) : -__builtin_inff();
+        float cs = -__builtin_inff();
+        if (has) {
+            const float x = red_cx[lane];
+            float a;
+            if constexpr (HLG) {
+                a = hlg32(x - rc.c, rc.curve) * rc.invT;
+            } else {
+                a = x * rc.invT;
+            }
+            cs = a + red_cg[lane];
+        }
         return uniform(wave_max(cs));
     };
     // Rows whose scores come near the fp32 range (a temperature of ~1e-38) can overflow the
@@ -1042,6 +1147,17 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                 screen_guard(sa, sb, sc, ta, tb);
             }
         }
+        // The least code any vector of the chunk needs: need falls as x grows, so it is the
+        // need at the chunk's largest logit (rounded up to the bf16 grid as the vectors'
+        // maxima are).
+        float need_min;
+        {
+            uint32_t xb = __float_as_uint(xmax_blk);
+            if constexpr (DT != DT_BF16) xb = ((int32_t)xb >= 0) ? xb + 0xFFFFu : xb;
+            const float xt = __uint_as_float(xb & 0xFFFF0000u);
+            need_min = uniform(tan_on ? code_needed(xt) : fminf(__builtin_fmaf(xt, sa, sb), sc));
+            if (!(xmax_blk > -__builtin_inff())) need_min = 0.0f;
+        }
         uint64_t best = 0;
         if (!skip) {
             // Screen: a vector can hold a winner only if U(its largest logit) + (n + 1) ln 2
@@ -1056,6 +1172,24 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                 for (int n = NV - 1; n >= 0; --n) {
                     const float xm = __uint_as_float(s_vec[lane_lds + n] << 16);
                     bits = (bits << 1) | (xm >= xmax_blk ? 1u : 0u);
+                }
+            } else if (need_min >= 8.0f) {
+                // Even the chunk's largest logit needs a code with 8 leading ones, so no vector
+                // whose code has fewer can pass: a first sweep keeps the others (about 3% of the
+                // vectors), and only those are tested in full.
+                uint32_t cand = 0;
+#pragma unroll
+                for (int n = NV - 1; n >= 0; --n)
+                    cand = (cand << 1) | (s_vec[lane_lds + n] >= 0xFF000000u ? 1u : 0u);
+                while (cand) {
+                    const int n = __builtin_ctz(cand);
+                    cand &= cand - 1u;
+                    const uint32_t d = s_vec[lane_lds + n];
+                    const float xm = __uint_as_float(d << 16);
+                    float need = fminf(tan_on ? code_needed(xm)
+                                              : fminf(__builtin_fmaf(xm, sa, sb), sc), 16.0f);
+                    if constexpr (!HLG) need = xm >= tau_row ? need : 17.0f;
+                    bits |= ((float)lead_ones_hi16(d) >= need ? 1u : 0u) << n;
                 }
             } else if (tan_on) {
 #pragma unroll
@@ -1084,6 +1218,9 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
                 const uint32_t cbit = 1u << (champ & 31u);
                 if (bits & cbit) {
                     bits &= ~cbit;
+                    // the bootstrap drew only the leading halves of the screened layout
+                    if constexpr (LAY != LAY_PLAIN)
+                        vec_words_lo(sk, lane_v + (int)(champ & 31u) * BS, cw0);
                     best = score_words((int)(champ & 31u), craw0, cw0, best);
                 }
             }
