@@ -182,8 +182,11 @@ typedef struct {
     int32_t draw_groups; /* blocks sharing one row's K draws (0 = automatic)               */
     int32_t split_lse;   /* split rows with the curve on: 0 automatic, 1 log-sum-exp
                             pre-pass, 2 exchange the chunks' partials inside the sampling
-                            kernel (one draw group per row; automatic picks it when every
-                            block of the grid is resident at once)                        */
+                            kernel (one draw group per row). Automatic: the exchange, either
+                            with one block per (row, chunk) when they are all resident at
+                            once, or with a resident grid whose blocks take the (row, chunk)
+                            items from a counter in the workspace (so a row's chunks still
+                            run together); the pre-pass only when neither applies           */
     int32_t exchange_wait; /* polls for the other chunks' partials before a block works
                               them out itself: 0 default, -1 none (test control), > 0 that
                               many                                                         */

@@ -86,7 +86,7 @@ int num_cus() {
 }
 
 struct WsLayout {
-    size_t counters, keys, partials, flags, tau, done, total;
+    size_t counters, keys, partials, flags, tau, done, queue, total;
 };
 
 WsLayout ws_layout(int64_t B, int32_t K) {
@@ -97,7 +97,8 @@ WsLayout ws_layout(int64_t B, int32_t K) {
     L.flags = L.partials + align256((size_t)B * hs::kMaxChunks * sizeof(float4));
     L.tau = L.flags + align256((size_t)B * hs::kMaxChunks * 4);   // exchange flags
     L.done = L.tau + align256((size_t)B * 4);    // top-k / top-p thresholds
-    L.total = L.done + align256((size_t)B * 4);  // rows the threshold kernel drew
+    L.queue = L.done + align256((size_t)B * 4);  // rows the threshold kernel drew
+    L.total = L.queue + 256;                     // the resident grid's work counters
     return L;
 }
 
@@ -313,15 +314,23 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
         if (hs::launch_filter_tau(x->dtype, f, (int)x->B, s) != hipSuccess) return HS_ERR_HIP;
         a.shift = f.tau;
     }
+    int64_t grid = P.grid;
+    a.items = (int32_t)P.grid;
     if (curve_on && P.nchunk > 1 && P.nkg == 1 && piv != 4) {
         const int mode = opts ? opts->split_lse : 0;
-        if (mode == 2) {
+        int per_cu = 0;
+        if (mode != 1 &&
+            hs::launch_sample(x->dtype, true, piv, a, P.nv, P.bs, 0, s, &per_cu) != hipSuccess)
+            per_cu = 0;
+        const int64_t resident = (int64_t)per_cu * num_cus();
+        if (mode == 2 || (mode == 0 && per_cu > 0 && P.grid <= resident)) {
             a.exchange = 1;
-        } else if (mode == 0) {
-            int per_cu = 0;
-            if (hs::launch_sample(x->dtype, true, piv, a, P.nv, P.bs, 0, s, &per_cu) ==
-                    hipSuccess && per_cu > 0 && P.grid <= (int64_t)per_cu * num_cus())
-                a.exchange = 1;
+        } else if (mode != 1 && per_cu > 0 && resident >= P.nchunk) {
+            // more blocks than fit at once: a resident grid takes the (row, chunk) items from
+            // a counter, so a row's chunks still run together and exchange their partials
+            a.exchange = 1;
+            a.queue = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(ws) + L.queue);
+            grid = resident;
         }
         const int wait = opts ? opts->exchange_wait : 0;
         a.spins = wait < 0 ? 0 : wait > 0 ? wait : hs::kExchangeSpins;
@@ -331,7 +340,7 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
         if (hs::launch_lse_partial(x->dtype, piv, a, bs, (int)(x->B * P.nchunk), s) != hipSuccess)
             return HS_ERR_HIP;
     }
-    if (hs::launch_sample(x->dtype, curve_on, piv, a, P.nv, P.bs, (int)P.grid, s) != hipSuccess)
+    if (hs::launch_sample(x->dtype, curve_on, piv, a, P.nv, P.bs, (int)grid, s) != hipSuccess)
         return HS_ERR_HIP;
     return HS_OK;
 }

@@ -61,6 +61,10 @@ struct SampleArgs {
     const uint32_t *done;         // [B] rows the threshold kernel has drawn (filters), else null
     const float *shift;           // [B] the curve's shift c per row (mass-median pivot), else null
     int32_t layout;               // word layout of the random stream: LAY_PLAIN / LAY_SCREENED
+    // a resident grid taking work items from a counter (workspace): [0] next item, [1] blocks
+    // done; null: one item per block
+    uint32_t *queue;
+    int32_t items;                // work items: B * nkg * nchunk
 };
 
 struct RowOpArgs {

@@ -203,8 +203,10 @@ __device__ __forceinline__ void chunk_partial(const SampleArgs &a, int64_t b, in
 // LAY selects the word layout of the random stream (LAY_PLAIN or LAY_SCREENED, see
 // element_word): the pass draws only what the screen needs, the largest leading 16 bits of
 // each vector's words, and the few vectors scored exactly draw their whole words.
+// One work item: one chunk of one row and one group of its draws (item = (row * nkg + group)
+// * nchunk + chunk). Every thread of the block calls it with the same item.
 template <int DT, int NV, bool HLG, int PIV, int MAXBS, bool ALIGNED, int LAY>
-__global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
+__device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
     static_assert(HLG || PIV == 0, "a pivot needs the curve");
     constexpr bool LSE = HLG && PIV != 1 && PIV != 4;   // the exponential sum is needed
     constexpr bool ENT = PIV == 2 || PIV == 3;   // and the entropy anchor's sum
@@ -242,8 +244,8 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
     uint16_t *s_vec16 = reinterpret_cast<uint16_t *>(s_vec);
     int lane_lds = tid * SC;
     if (tid < 64) s_best[tid] = 0ull;   // visible to every wave after the combine's barrier
-    // block coordinates in scalar registers (the divisions would otherwise run per lane)
-    int bid = blockIdx.x;
+    // item coordinates in scalar registers (the divisions would otherwise run per lane)
+    int bid = item;
     const int chunk = __builtin_amdgcn_readfirstlane(bid % a.nchunk);
     bid /= a.nchunk;
     const int kg = __builtin_amdgcn_readfirstlane(bid % a.nkg);
@@ -1300,6 +1302,42 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
             if (a.exchange && tid < a.nchunk)
                 __hip_atomic_store(a.flags + b * a.part_stride + tid, 0u, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// The sampling kernel: one item per block, or (a.queue set) a resident grid whose blocks take
+// items from a counter in the workspace until none is left. Consecutive items are the chunks
+// of one row, so a row's chunks go to blocks that ask at about the same time and, all blocks
+// being resident, run together: their log-sum-exp partials meet in the in-kernel exchange
+// with no pre-pass. Every block leaves once the counter passes the last item; the last block
+// out sets both counters back to zero for the next call.
+template <int DT, int NV, bool HLG, int PIV, int MAXBS, bool ALIGNED, int LAY>
+__global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
+    __shared__ int s_item;
+    const bool queued = a.queue != nullptr;
+    int item = blockIdx.x;
+    for (;;) {
+        if (queued) {
+            if (threadIdx.x == 0)
+                s_item = (int)__hip_atomic_fetch_add(a.queue, 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            item = __builtin_amdgcn_readfirstlane(s_item);
+            if (item >= a.items) break;
+        }
+        sample_item<DT, NV, HLG, PIV, MAXBS, ALIGNED, LAY>(a, item);
+        if (!queued) break;
+        __syncthreads();   // the block's LDS serves its next item
+    }
+    if (queued && threadIdx.x == 0) {
+        // every other block has taken its last item (and seen the counter past the end)
+        // before it counts itself out here
+        const unsigned out = __hip_atomic_fetch_add(a.queue + 1, 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        if (out == gridDim.x - 1) {
+            __hip_atomic_store(a.queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.queue + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }

@@ -212,6 +212,46 @@ def test_k_draws_equal_single_draws(hs):
         np.testing.assert_array_equal(one.cpu().numpy()[:, 0], allk[:, k])
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_resident_grid_work_queue(hs, oracle_mod, layout):
+    """More (row, chunk) items than resident blocks, one draw group per row: the automatic
+    plan runs a resident grid that takes items from a counter and exchanges the chunks'
+    partials in the kernel (no pre-pass). Ids agree with the oracle's; two calls in a row on one
+    workspace give the same result and leave the counters zero. Ids and scores equal the
+    one-block-per-item exchange's bit for bit (every block working the other chunks' partials
+    out itself, which gives the owner's values exactly), and the pre-pass route's up to the
+    rounding of the row's log-sum-exp."""
+    B, V, K = 600, 100000, 2
+    w = W.generic(B, V, torch.float32, seed=83, mask_frac=0.05, hlg=HLG_A, K=K)
+    plan = hs.sample_plan(B, V, K, torch.float32, True)
+    assert plan["nchunk"] > 1 and plan["draw_groups"] == 1 and plan["grid"] > plan["cus"]
+    d = on_device(w)
+    lay = hs.LAYOUTS[layout]
+    ws = hs.workspace(B, V, K, torch.float32, True)
+    runs = [hs.sample_ex(d["logits"], d["T"], d["seed"], d["offset"], mu=d["mu"], hlg=HLG_A,
+                         k=K, ws=ws, opts=hs.SampleOpts(layout=lay), want_best=True)
+            for _ in range(2)]
+    exch = hs.sample_ex(d["logits"], d["T"], d["seed"], d["offset"], mu=d["mu"], hlg=HLG_A,
+                        k=K, opts=hs.SampleOpts(layout=lay, split_lse=2, exchange_wait=-1),
+                        want_best=True)
+    pre = hs.sample_ex(d["logits"], d["T"], d["seed"], d["offset"], mu=d["mu"], hlg=HLG_A, k=K,
+                       opts=hs.SampleOpts(layout=lay, split_lse=1), want_best=True)
+    torch.cuda.synchronize()
+    for idx, best in runs:
+        np.testing.assert_array_equal(idx.cpu().numpy(), exch[0].cpu().numpy())
+        np.testing.assert_array_equal(best.cpu().numpy(), exch[1].cpu().numpy())
+    np.testing.assert_allclose(runs[0][1].cpu().numpy(), pre[1].cpu().numpy(), rtol=1e-6)
+    # workspace layout for B = 600, K = 2 (256-byte aligned regions): counters [0, 4864),
+    # keys [4864, 14592), partials (left as written) [14592, 628992), exchange flags
+    # [628992, 782592), thresholds and row marks, then the work queue (the last 256 bytes)
+    assert int(ws[:14592].to(torch.int32).abs().sum()) == 0
+    assert int(ws[628992:782592].to(torch.int32).abs().sum()) == 0
+    assert int(ws[-256:].to(torch.int32).abs().sum()) == 0
+    o, s1, s2 = oracle_sample(oracle_mod, w, layout=layout)
+    print(assert_parity(runs[0][0].cpu().numpy(), o, s1, s2, w.logits.double().numpy(),
+                        "work queue " + layout))
+
+
 def test_workspace_left_clean(hs):
     """A split call leaves its workspace's counters, keys and exchange flags zero-filled, so
     calls can reuse it (with draw groups and the pre-pass, and with the in-kernel exchange)."""

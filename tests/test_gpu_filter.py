@@ -120,10 +120,10 @@ def test_filters_on_heavily_tied_rows(hs, oracle_mod, dtype):
 
 
 def _row_marks(hs, ws, B, V, K, dtype):
-    """The per-row marks of rows the threshold kernel drew itself: the workspace's last region
-    (B int32, 256-byte aligned)."""
+    """The per-row marks of rows the threshold kernel drew itself: the workspace region (B int32,
+    256-byte aligned) before the last 256 bytes (the resident grid's work counters)."""
     n = hs.workspace_bytes(B, V, K, dtype, False)
-    off = n - (B * 4 + 255) // 256 * 256
+    off = n - 256 - (B * 4 + 255) // 256 * 256
     return ws[off:off + 4 * B].view(torch.int32).cpu().numpy()
 
 
