@@ -198,10 +198,11 @@ def main():
                     help="top-k filter on every row (turns the curve off; 0 = none)")
     ap.add_argument("--top-p", type=float, default=1.0,
                     help="top-p filter on every row (turns the curve off; 1 = none)")
-    ap.add_argument("--layout", choices=("plain", "screened"), default="plain",
-                    help="word layout of the random stream: plain (element i takes word i & 3 "
-                         "of the Philox call at counter word i >> 2) or screened (the leading 16 "
-                         "bits of eight elements come from one call)")
+    ap.add_argument("--layout", choices=("plain", "screened"), default="screened",
+                    help="word layout of the random stream: screened (default: the leading 16 "
+                         "bits of eight elements come from one Philox call) or plain (element i "
+                         "takes word i & 3 of the call at counter word i >> 2); the other "
+                         "layout is timed beside it (other_layout)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain device copy of MIB MiB five "
                          "times (reference for scaling the memory-traffic counters)")
@@ -378,7 +379,7 @@ def main():
     # streaming read of the logits with the sampler's access pattern (the same rotating
     # copies), and the Philox4x32-10 word rate with no memory traffic; and the sampler itself
     # with one input copy (warm: resident in the last-level cache).
-    ceilings = warm = None
+    ceilings = warm = other_layout = None
     if not args.no_ceilings and graph is not None:
         def graph_ms(fn, n):
             g = torch.cuda.CUDAGraph()
@@ -401,6 +402,16 @@ def main():
             return e0.elapsed_time(e1) / n
 
         n_c = min(args.steps, 200)
+        # the other word layout on the same inputs, timed the same way (rotating copies)
+        other = "plain" if args.layout == "screened" else "screened"
+        mine = args.layout
+        args.layout = other
+        opts.layout = hs.LAYOUTS[other]
+        other_ms = graph_ms(launch, n_c)
+        args.layout = mine
+        opts.layout = hs.LAYOUTS[mine]
+        other_layout = {"layout": other, "ms_per_step": other_ms,
+                        "rows_per_s": B / (other_ms / 1e3)}
         warm_ms = graph_ms(lambda i, s_: launch(0, s_), n_c)
         warm = {"ms_per_step": warm_ms, "rows_per_s": B / (warm_ms / 1e3),
                 "note": "one input copy, resident in the last-level cache"}
@@ -525,6 +536,7 @@ def main():
         rec["draws_per_s"] = B * K / (ms_per_step / 1e3)
     if warm is not None:
         rec["warm"] = warm
+        rec["other_layout"] = other_layout
     if ceilings:
         rec["ceilings"] = ceilings
     if not args.no_cpu_baseline:
