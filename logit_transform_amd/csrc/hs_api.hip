@@ -325,12 +325,19 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
         const int64_t resident = (int64_t)per_cu * num_cus();
         if (mode == 2 || (mode == 0 && per_cu > 0 && P.grid <= resident)) {
             a.exchange = 1;
-        } else if (mode != 1 && per_cu > 0 && resident >= P.nchunk) {
-            // more blocks than fit at once: a resident grid takes the (row, chunk) items from
-            // a counter, so a row's chunks still run together and exchange their partials
-            a.exchange = 1;
+        } else if (mode == 0 && hs::queue_nv(P.nv) && a.aligned && a.V >= epv_of(x->dtype)) {
+            // more blocks than fit at once (aligned rows, the chunk sizes that have a
+            // work-queue kernel): a resident grid takes the (row, chunk) items from a counter,
+            // so a row's chunks still run together and exchange their partials
             a.queue = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(ws) + L.queue);
-            grid = resident;
+            int per_cu_q = 0;
+            if (hs::launch_sample(x->dtype, true, piv, a, P.nv, P.bs, 0, s, &per_cu_q) ==
+                    hipSuccess && per_cu_q > 0 && (int64_t)per_cu_q * num_cus() >= P.nchunk) {
+                a.exchange = 1;
+                grid = (int64_t)per_cu_q * num_cus();
+            } else {
+                a.queue = nullptr;
+            }
         }
         const int wait = opts ? opts->exchange_wait : 0;
         a.spins = wait < 0 ? 0 : wait > 0 ? wait : hs::kExchangeSpins;

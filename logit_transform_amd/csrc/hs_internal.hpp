@@ -26,6 +26,11 @@ struct RowCurve {
 };
 static_assert(sizeof(RowCurve) == 32, "RowCurve layout");
 
+// Chunk sizes (slots per lane) that have a work-queue sampling kernel: 12 and 16, where a
+// pre-pass's second read of the chunks costs the most. (With 19 slots the loop around the
+// item no longer fits the register budget of four waves per SIMD.)
+constexpr bool queue_nv(int nv) { return nv == 12 || nv == 16; }
+
 struct SampleArgs {
     const void *data;          // logits, row-major [B, ld]
     int64_t ld;                // row stride (elements)

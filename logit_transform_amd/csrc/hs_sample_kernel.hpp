@@ -666,7 +666,7 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
     uint32_t cw0[EPV];   // the champion vector's words
     {
         const Stream sk = stream_k(k0);
-        uint4 buf[D];
+        uint4 buf[D];   // loads in flight
         constexpr int RING = LAG + 2;   // slot keys between a slot's draw and its logits
         uint32_t ring[RING];
 #pragma unroll
@@ -1306,31 +1306,32 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
     }
 }
 
-// The sampling kernel: one item per block, or (a.queue set) a resident grid whose blocks take
-// items from a counter in the workspace until none is left. Consecutive items are the chunks
-// of one row, so a row's chunks go to blocks that ask at about the same time and, all blocks
-// being resident, run together: their log-sum-exp partials meet in the in-kernel exchange
-// with no pre-pass. Every block leaves once the counter passes the last item; the last block
-// out sets both counters back to zero for the next call.
+// The sampling kernel: one work item per block.
 template <int DT, int NV, bool HLG, int PIV, int MAXBS, bool ALIGNED, int LAY>
 __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
+    sample_item<DT, NV, HLG, PIV, MAXBS, ALIGNED, LAY>(a, blockIdx.x);
+}
+
+// The same on a resident grid whose blocks take items from a counter in the workspace
+// (a.queue) until none is left. Consecutive items are the chunks of one row, so a row's chunks
+// go to blocks that ask at about the same time and, all blocks being resident, run together:
+// their log-sum-exp partials meet in the in-kernel exchange with no pre-pass. Every block
+// leaves once the counter passes the last item; the last block out sets both counters back to
+// zero for the next call. (A kernel of its own: the loop around the item costs registers.)
+template <int DT, int NV, bool HLG, int PIV, int MAXBS, bool ALIGNED, int LAY>
+__global__ __launch_bounds__(MAXBS) void k_sample_q(SampleArgs a) {
     __shared__ int s_item;
-    const bool queued = a.queue != nullptr;
-    int item = blockIdx.x;
     for (;;) {
-        if (queued) {
-            if (threadIdx.x == 0)
-                s_item = (int)__hip_atomic_fetch_add(a.queue, 1u, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-            __syncthreads();
-            item = __builtin_amdgcn_readfirstlane(s_item);
-            if (item >= a.items) break;
-        }
+        if (threadIdx.x == 0)
+            s_item = (int)__hip_atomic_fetch_add(a.queue, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const int item = __builtin_amdgcn_readfirstlane(s_item);
+        if (item >= a.items) break;
         sample_item<DT, NV, HLG, PIV, MAXBS, ALIGNED, LAY>(a, item);
-        if (!queued) break;
         __syncthreads();   // the block's LDS serves its next item
     }
-    if (queued && threadIdx.x == 0) {
+    if (threadIdx.x == 0) {
         // every other block has taken its last item (and seen the counter past the end)
         // before it counts itself out here
         const unsigned out = __hip_atomic_fetch_add(a.queue + 1, 1u, __ATOMIC_RELAXED,
@@ -1341,6 +1342,11 @@ __global__ __launch_bounds__(MAXBS) void k_sample(SampleArgs a) {
         }
     }
 }
+
+// The instantiations that have a work-queue kernel: the curve on (the exchange of log-sum-exp
+// partials is what the queue makes possible), aligned rows, and the chunk sizes queue_nv admits.
+template <bool HLG, int PIV, bool AL, int NV>
+constexpr bool kHasQueueKernel = HLG && PIV != 4 && AL && queue_nv(NV);
 
 // The split pre-pass: one block per (row, chunk).
 template <int DT, int PIV>
@@ -1365,6 +1371,20 @@ hipError_t launch_sample_nv(const SampleArgs &a, int nv, int bs, int grid, hipSt
 #define HS_CASE(N, MB)                                                                     \
     case N:                                                                                \
         if (bs > MB) return hipErrorInvalidValue;                                          \
+        if (a.queue) {                                                                     \
+            if constexpr (kHasQueueKernel<HLG, PIV, AL, N>) {                              \
+                if (occ)                                                                   \
+                    return hipOccupancyMaxActiveBlocksPerMultiprocessor(                   \
+                        occ,                                                               \
+                        reinterpret_cast<const void *>(&k_sample_q<DT, N, HLG, PIV, MB, AL, LAY>), \
+                        bs, (size_t)(N | 1) * bs * 4);                                    \
+                hipLaunchKernelGGL((k_sample_q<DT, N, HLG, PIV, MB, AL, LAY>), dim3(grid),  \
+                                   dim3(bs), (size_t)(N | 1) * bs * 4, s, a);             \
+                break;                                                                     \
+            } else {                                                                       \
+                return hipErrorInvalidValue;                                               \
+            }                                                                              \
+        }                                                                                  \
         if (occ)                                                                           \
             return hipOccupancyMaxActiveBlocksPerMultiprocessor(                           \
                 occ, reinterpret_cast<const void *>(&k_sample<DT, N, HLG, PIV, MB, AL, LAY>), \

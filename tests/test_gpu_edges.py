@@ -225,6 +225,7 @@ def test_resident_grid_work_queue(hs, oracle_mod, layout):
     w = W.generic(B, V, torch.float32, seed=83, mask_frac=0.05, hlg=HLG_A, K=K)
     plan = hs.sample_plan(B, V, K, torch.float32, True)
     assert plan["nchunk"] > 1 and plan["draw_groups"] == 1 and plan["grid"] > plan["cus"]
+    assert plan["nv"] == 16   # a chunk size with a work-queue kernel
     d = on_device(w)
     lay = hs.LAYOUTS[layout]
     ws = hs.workspace(B, V, K, torch.float32, True)
