@@ -26,7 +26,8 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libhs.so")
+# HS_LIBRARY: another build of the same sources (the host-only sanitized one, for CPU checks)
+_LIB_PATH = os.environ.get("HS_LIBRARY") or os.path.join(_HERE, "libhs.so")
 
 HS_F32, HS_BF16, HS_F16 = 0, 1, 2
 _DTYPES = {torch.float32: HS_F32, torch.bfloat16: HS_BF16, torch.float16: HS_F16}

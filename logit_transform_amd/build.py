@@ -87,5 +87,51 @@ def build(force: bool = True, verbose: bool = False) -> str:
     return LIB
 
 
+def build_sanitized(out_dir: str, verbose: bool = False) -> str:
+    """Host code only (no device code objects) under AddressSanitizer and
+    UndefinedBehaviorSanitizer, into out_dir/libhs.so: the argument checks, launch planning and
+    workspace layout, which run on the CPU before any device call. Kernels are not in it, so
+    any call that reaches a launch fails. A process that loads it needs clang's ASan runtime
+    loaded first (LD_PRELOAD); point HS_LIBRARY at the result."""
+    os.makedirs(out_dir, exist_ok=True)
+    san = ["--cuda-host-only", "-O1", "-g", "-fno-omit-frame-pointer",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined"]
+    objs, procs = [], []
+    for s in SOURCES:
+        obj = os.path.join(out_dir, s.replace(".hip", ".o"))
+        cmd = [hipcc()] + flags() + san + ["-c", os.path.join(CSRC, s), "-o", obj]
+        if verbose:
+            print(" ".join(cmd))
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                      text=True))
+        objs.append(obj)
+    for p in procs:
+        out, _ = p.communicate()
+        if p.returncode != 0:
+            raise RuntimeError("hipcc failed:\n" + out)
+    # Host-only objects refer to their device-code bundles by name: give each an empty
+    # offload bundle (the magic string and a zero entry count), so the library loads and
+    # registers no kernels.
+    names = set()
+    for o in objs:
+        out = subprocess.run(["nm", "-u", o], check=True, capture_output=True, text=True).stdout
+        names.update(l.split()[-1] for l in out.splitlines() if "__hip_fatbin_" in l)
+    stub = os.path.join(out_dir, "empty_bundles.c")
+    with open(stub, "w") as f:
+        for n in sorted(names):
+            f.write('__attribute__((aligned(8))) const char %s[32] = '
+                    '"__CLANG_OFFLOAD_BUNDLE__";\n' % n)
+    stub_obj = stub[:-2] + ".o"
+    subprocess.run(["gcc", "-c", "-fPIC", "-o", stub_obj, stub], check=True)
+    lib = os.path.join(out_dir, "libhs.so")
+    subprocess.run([hipcc(), "--cuda-host-only", "-shared", "-fPIC", "-o", lib] + objs +
+                   [stub_obj], check=True, capture_output=not verbose)
+    return lib
+
+
 if __name__ == "__main__":
-    print(build(force=True, verbose="-v" in sys.argv))
+    if "--sanitize" in sys.argv:
+        print(build_sanitized(sys.argv[sys.argv.index("--sanitize") + 1], "-v" in sys.argv))
+    else:
+        print(build(force=True, verbose="-v" in sys.argv))

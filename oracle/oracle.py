@@ -24,7 +24,8 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        path = _build.build(force=False)
+        # HS_ORACLE_LIBRARY: another build of the same source (the sanitized one)
+        path = os.environ.get("HS_ORACLE_LIBRARY") or _build.build(force=False)
         L = C.CDLL(path)
         u32p = np.ctypeslib.ndpointer(np.uint32, flags="C_CONTIGUOUS")
         u64p = np.ctypeslib.ndpointer(np.uint64, flags="C_CONTIGUOUS")
