@@ -1176,13 +1176,15 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
                     bits = (bits << 1) | (xm >= xmax_blk ? 1u : 0u);
                 }
             } else if (need_min >= 8.0f) {
-                // Even the chunk's largest logit needs a code with 8 leading ones, so no vector
-                // whose code has fewer can pass: a first sweep keeps the others (about 3% of the
-                // vectors), and only those are tested in full.
+                // Even the chunk's largest logit needs a code with nb >= 8 leading ones, so no
+                // vector whose code has fewer can pass: a first sweep keeps the others (about
+                // 8 2^-nb of the vectors), and only those are tested in full.
+                const int nb = (int)fminf(need_min, 16.0f);
+                const uint32_t lim = (0xFFFFu << (16 - nb)) << 16;   // nb leading ones
                 uint32_t cand = 0;
 #pragma unroll
                 for (int n = NV - 1; n >= 0; --n)
-                    cand = (cand << 1) | (s_vec[lane_lds + n] >= 0xFF000000u ? 1u : 0u);
+                    cand = (cand << 1) | (s_vec[lane_lds + n] >= lim ? 1u : 0u);
                 while (cand) {
                     const int n = __builtin_ctz(cand);
                     cand &= cand - 1u;
