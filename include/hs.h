@@ -115,7 +115,7 @@ int hs_hlg_pivot(const hs_logits *x, const float *mu, const hs_hlg_params *p, fl
  * T: device float[B]; seed, offset: device uint64[B]; out: device int32[B*K].
  * ws / ws_bytes: device workspace of at least hs_workspace_bytes(B, V, K, dtype, 0) bytes,
  * zero-filled before its first use (hs_workspace_init); every successful call leaves its
- * counters, keys and flags zero-filled again (the per-row filter thresholds and row marks of
+ * counters, keys and exchange slots zero-filled again (the per-row filter thresholds and row marks of
  * hs_sample_filtered are rewritten by every such call before they are read). Calls that may
  * run concurrently need separate workspaces. ws may be
  * NULL with ws_bytes 0, in which case only single-block-per-row kernels are used. */

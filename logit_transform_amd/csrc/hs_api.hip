@@ -86,7 +86,7 @@ int num_cus() {
 }
 
 struct WsLayout {
-    size_t counters, keys, partials, flags, tau, done, queue, total;
+    size_t counters, keys, partials, xslots, tau, done, queue, total;
 };
 
 WsLayout ws_layout(int64_t B, int32_t K) {
@@ -94,8 +94,8 @@ WsLayout ws_layout(int64_t B, int32_t K) {
     L.counters = 0;
     L.keys = align256((size_t)B * (size_t)K * 4);   // counters: one per (row, draw group)
     L.partials = L.keys + align256((size_t)B * (size_t)K * 8);
-    L.flags = L.partials + align256((size_t)B * hs::kMaxChunks * sizeof(float4));
-    L.tau = L.flags + align256((size_t)B * hs::kMaxChunks * 4);   // exchange flags
+    L.xslots = L.partials + align256((size_t)B * hs::kMaxChunks * sizeof(float4));
+    L.tau = L.xslots + align256((size_t)B * hs::kMaxChunks * 16);   // exchange slots
     L.done = L.tau + align256((size_t)B * 4);    // top-k / top-p thresholds
     L.queue = L.done + align256((size_t)B * 4);  // rows the threshold kernel drew
     L.total = L.queue + 256;                     // the resident grid's work counters
@@ -265,7 +265,7 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
         a.keys = reinterpret_cast<uint64_t *>(w + L.keys);
         a.partials = reinterpret_cast<float4 *>(w + L.partials);
         a.part_stride = hs::kMaxChunks;
-        a.flags = reinterpret_cast<uint32_t *>(w + L.flags);
+        a.xslots = reinterpret_cast<uint32_t *>(w + L.xslots);
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (filtering) {

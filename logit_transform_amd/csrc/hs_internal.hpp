@@ -62,7 +62,8 @@ struct SampleArgs {
     // instead of a pre-pass (one draw group per row, every block resident at once)
     int32_t exchange;
     int32_t spins;                // polls before a block works a missing partial out itself
-    uint32_t *flags;              // [B * part_stride]: chunk partial published
+    uint32_t *xslots;             // [B * part_stride * 4]: chunk partials of the exchange,
+                                  // each word stored inverted (zero: not yet published)
     const uint32_t *done;         // [B] rows the threshold kernel has drawn (filters), else null
     const float *shift;           // [B] the curve's shift c per row (mass-median pivot), else null
     int32_t layout;               // word layout of the random stream: LAY_PLAIN / LAY_SCREENED

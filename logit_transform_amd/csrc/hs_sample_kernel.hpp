@@ -851,13 +851,13 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
     if (screen) post_candidate(candidate(stream_k(k0), champ0, craw0, cw0));
     waves_combine(xmax_lane, lse_r, lse_s, lse_u, red_x);
     __syncthreads();
-    // Split rows without the pre-pass (the host chooses this only when every block of the grid
-    // is resident at once): each block publishes its own chunk's partial, combined from the
-    // streaming pass's sums; wave 0 collects the row's other partials, waiting a bounded time
-    // for each; any still missing then is worked out here by replaying that chunk's pass (the
-    // same slots, order and arithmetic per lane), so the combined shift is the same whoever
-    // computes a partial. Partials and flags are only touched by agent-scope atomics: each
-    // block waits for its partial's stores to complete before it raises its flag.
+    // Split rows without the pre-pass (the host chooses this only when a row's chunks run at
+    // once: every block of the grid resident, or a resident grid taking items from a work
+    // queue): each block publishes its own chunk's partial, combined from the streaming pass's
+    // sums; wave 0 collects the row's other partials, waiting a bounded time for each; any
+    // still missing then is worked out here by replaying that chunk's pass (the same slots,
+    // order and arithmetic per lane), so the combined shift is the same whoever computes a
+    // partial. The exchange slots are only touched by agent-scope atomics.
     const float4 *parts = a.partials + b * a.part_stride;
     if constexpr (HLG) {
         if (a.nchunk > 1 && a.exchange) {
@@ -923,38 +923,41 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
                 if (lane == 0) s_part[chunk] = pr;
             }
             __syncthreads();
-            uint32_t *flags = a.flags + b * a.part_stride;
+            // A partial's four words carry their own presence: each is stored inverted, so a
+            // zero word is one not yet written (the slots start zero-filled and the row's last
+            // block fills them with zeros again); the one word whose inverse is zero (all bits
+            // set: a NaN) is stored as another NaN. Every word is written once per call, so a
+            // reader that sees all four nonzero has the final partial: no flag and no wait for
+            // the stores to complete.
+            uint32_t *slots = a.xslots + (size_t)b * a.part_stride * 4;
             if (tid == 0) {
                 const float4 mine = s_part[chunk];
-                uint32_t *dst = reinterpret_cast<uint32_t *>(a.partials + b * a.part_stride + chunk);
-                __hip_atomic_store(dst + 0, __float_as_uint(mine.x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(dst + 1, __float_as_uint(mine.y), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(dst + 2, __float_as_uint(mine.z), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(dst + 3, __float_as_uint(mine.w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __atomic_signal_fence(__ATOMIC_SEQ_CST);
-                __builtin_amdgcn_s_waitcnt(0);
-                __atomic_signal_fence(__ATOMIC_SEQ_CST);
-                __hip_atomic_store(flags + chunk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const float mv[4] = {mine.x, mine.y, mine.z, mine.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t u = __float_as_uint(mv[q]);
+                    __hip_atomic_store(slots + 4 * chunk + q, ~(u == 0xFFFFFFFFu ? 0x7FC00000u : u),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
             }
             if (wid == 0) {
                 bool have = lane >= a.nchunk || lane == chunk;
+                uint32_t pw[4] = {0u, 0u, 0u, 0u};
                 for (int it = 0; it < a.spins; ++it) {
-                    if (!have)
-                        have = __hip_atomic_load(flags + lane, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT) != 0u;
+                    if (!have) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            if (pw[q] == 0u)
+                                pw[q] = __hip_atomic_load(slots + 4 * lane + q, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
+                        have = pw[0] != 0u && pw[1] != 0u && pw[2] != 0u && pw[3] != 0u;
+                    }
                     if (__ballot(!have) == 0ull) break;
-                    __builtin_amdgcn_s_sleep(8);
+                    __builtin_amdgcn_s_sleep(1);
                 }
-                if (have && lane < a.nchunk && lane != chunk) {
-                    const uint32_t *src =
-                        reinterpret_cast<const uint32_t *>(a.partials + b * a.part_stride + lane);
-                    float4 v;
-                    v.x = __uint_as_float(__hip_atomic_load(src + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-                    v.y = __uint_as_float(__hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-                    v.z = __uint_as_float(__hip_atomic_load(src + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-                    v.w = __uint_as_float(__hip_atomic_load(src + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-                    s_part[lane] = v;
-                }
+                if (have && lane < a.nchunk && lane != chunk)
+                    s_part[lane] = make_float4(__uint_as_float(~pw[0]), __uint_as_float(~pw[1]),
+                                               __uint_as_float(~pw[2]), __uint_as_float(~pw[3]));
                 const uint64_t miss = __ballot(!have);
                 if (lane == 0) s_miss = miss;
             }
@@ -1299,11 +1302,12 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
             if (tid == 0)
                 __hip_atomic_store(a.counters + b * a.nkg + kg, 0u, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
-            // the exchange's flags (one draw group per row: every block of the row is past
-            // its wait once it has counted in)
-            if (a.exchange && tid < a.nchunk)
-                __hip_atomic_store(a.flags + b * a.part_stride + tid, 0u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+            // the exchange's slots (one draw group per row: every block of the row is past
+            // its wait once it has counted in, and thread 0 of each, which published its
+            // partial, saw those stores complete before it counted in)
+            if (a.exchange && tid < 4 * a.nchunk)
+                __hip_atomic_store(a.xslots + (size_t)b * a.part_stride * 4 + tid, 0u,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }

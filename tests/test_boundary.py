@@ -287,8 +287,8 @@ def test_noalloc_arguments(lib):
     assert call(L(), hlg=H(m=-1.0)) == HS_ERR_INVALID_ARG
     assert call(L(), hlg=H(), mu=None) == HS_ERR_INVALID_ARG
     assert call(L(), opts=hs.SampleOpts(layout=5)) == HS_ERR_INVALID_ARG
-    # workspace past the static array: B = 8192 rows need 8192 * (64 * 20) bytes of partials
-    # and flags alone
+    # workspace past the static array: B = 8192 rows need 8192 * (64 * 32) bytes of partials
+    # and exchange slots alone
     big = L(B=8192, V=1000)
     assert lib.hs_workspace_bytes(8192, 1000, 1, 0, 1) > cap
     assert call(big) == HS_ERR_UNSUPPORTED

@@ -243,10 +243,10 @@ def test_resident_grid_work_queue(hs, oracle_mod, layout):
         np.testing.assert_array_equal(best.cpu().numpy(), exch[1].cpu().numpy())
     np.testing.assert_allclose(runs[0][1].cpu().numpy(), pre[1].cpu().numpy(), rtol=1e-6)
     # workspace layout for B = 600, K = 2 (256-byte aligned regions): counters [0, 4864),
-    # keys [4864, 14592), partials (left as written) [14592, 628992), exchange flags
-    # [628992, 782592), thresholds and row marks, then the work queue (the last 256 bytes)
+    # keys [4864, 14592), pre-pass partials (left as written) [14592, 628992), exchange slots
+    # [628992, 1243392), thresholds and row marks, then the work queue (the last 256 bytes)
     assert int(ws[:14592].to(torch.int32).abs().sum()) == 0
-    assert int(ws[628992:782592].to(torch.int32).abs().sum()) == 0
+    assert int(ws[628992:1243392].to(torch.int32).abs().sum()) == 0
     assert int(ws[-256:].to(torch.int32).abs().sum()) == 0
     o, s1, s2 = oracle_sample(oracle_mod, w, layout=layout)
     print(assert_parity(runs[0][0].cpu().numpy(), o, s1, s2, w.logits.double().numpy(),
@@ -254,13 +254,13 @@ def test_resident_grid_work_queue(hs, oracle_mod, layout):
 
 
 def test_workspace_left_clean(hs):
-    """A split call leaves its workspace's counters, keys and exchange flags zero-filled, so
+    """A split call leaves its workspace's counters, keys and exchange slots zero-filled, so
     calls can reuse it (with draw groups and the pre-pass, and with the in-kernel exchange)."""
     w = W.generic(2, 100000, torch.float32, seed=81, hlg=HLG_A, K=4)
     d = on_device(w)
     ws = hs.workspace(2, 100000, 4, torch.float32, True)
-    # layout for B = 2, K = 4: counters [0, 256), keys [256, 512), partials [512, 2560),
-    # exchange flags [2560, 3072)
+    # layout for B = 2, K = 4: counters [0, 256), keys [256, 512), pre-pass partials
+    # [512, 2560), exchange slots [2560, 4608)
     for opts in (hs.SampleOpts(variant=2, nchunk=9),
                  hs.SampleOpts(variant=2, nchunk=9, draw_groups=1, split_lse=2)):
         outs = [hs.sample_ex(d["logits"], d["T"], d["seed"], d["offset"], mu=d["mu"], hlg=HLG_A,
@@ -268,7 +268,7 @@ def test_workspace_left_clean(hs):
                 for _ in range(3)]
         torch.cuda.synchronize()
         assert int(ws[:512].to(torch.int32).abs().sum()) == 0
-        assert int(ws[2560:3072].to(torch.int32).abs().sum()) == 0
+        assert int(ws[2560:4608].to(torch.int32).abs().sum()) == 0
         for o in outs[1:]:
             np.testing.assert_array_equal(o, outs[0])
 
