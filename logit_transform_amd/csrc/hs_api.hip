@@ -122,10 +122,10 @@ bool pick_block(int64_t cv, int *bs, int *nv) {
 // Kernel shape for a call. A row's draws are spread over blocks first ("draw groups": blocks
 // that share a chunk of the row but not its draws need no cross-block combine), up to about one
 // block per CU. Only if that leaves more than half of the CUs idle are rows split into chunks
-// (at most 32, of at least 256 vectors), aiming at one block per CU with the curve on (its
-// log-sum-exp pre-pass is split too) and at one per two CUs without it (each chunk then adds
-// only its share of the cross-block combine); the chunks' maxima meet in the workspace. Rows
-// longer than one block holds (kBlockCapacity vectors) are always split.
+// (of at least 256 vectors), aiming at one block per CU with the curve on (at most 16 chunks:
+// they exchange log-sum-exp partials) and at one per two CUs without it (at most 32; each
+// chunk then adds only its share of the cross-block combine); the chunks' maxima meet in the
+// workspace. Rows longer than one block holds (kBlockCapacity vectors) are always split.
 int make_plan(const hs_logits *x, int32_t K, bool hlg, bool ws_ok, const hs_sample_opts *o,
               Plan *P) {
     const int64_t B = x->B;
@@ -153,7 +153,10 @@ int make_plan(const hs_logits *x, int32_t K, bool hlg, bool ws_ok, const hs_samp
             const int64_t target = hlg ? cus : cus / 2;
             int64_t want = (target + B * g - 1) / (B * g);
             int64_t lim = nvec / 256;
-            if (lim > 32) lim = 32;
+            // with the curve, a row's chunks exchange their log-sum-exp partials: past about
+            // 16 chunks the exchange costs more than the shorter pass saves
+            const int64_t cap = hlg ? 16 : 32;
+            if (lim > cap) lim = cap;
             if (lim < 1) lim = 1;
             nchunk = want < lim ? want : lim;
             if (nchunk < nchunk_min) nchunk = nchunk_min;

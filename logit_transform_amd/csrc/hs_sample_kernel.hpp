@@ -224,7 +224,7 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
     __shared__ uint64_t red_ck[16];    // per wave: best bootstrap candidate key
     __shared__ float red_cx[16];       //   its logit
     __shared__ float red_cg[16];       //   and the Gumbel value of its word
-    __shared__ float row_bc[12];       // row constants from wave 0
+    __shared__ float row_bc[13];       // row constants from wave 0
     // per wave, the best exact candidate score of a later draw; two buffers, alternating
     // between draws (a wave may post draw k + 1's before a slower one has read draw k's)
     __shared__ float red_sb[2][16];
@@ -1035,17 +1035,25 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
             rc.mtc = uniform(rc.mt * rc.c);
             rc.mtw = uniform(rc.mt * rc.curve.w);
         }
+        // The row's largest logit, for the lower bounds below: of split rows with the
+        // chunks' partials (the curve on), every chunk's; otherwise the chunk's own.
+        float xrow = xmb;
+        if constexpr (HLG && PIV != 4) {
+            if (a.nchunk > 1)
+                xrow = uniform(fmaxf(wave_max(lane < a.nchunk ? parts[lane].w
+                                                              : -__builtin_inff()), xmb));
+        }
         float o[9] = {xmb, 0.0f, 0.0f, __builtin_inff(), 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
         if (ok && screen) {
             // lower bounds on the first draw's winning score: the best candidate's exact
-            // score, and from the chunk's largest logit (its curve value is at least
+            // score, and from the row's largest logit (its curve value is at least
             // (m/T) min(x - c, w) -- the toe lies above its mid line, the shoulder above m w --
             // and every Gumbel value is at least G(0) > -3.14)
             float lbx;
             if constexpr (HLG) {
-                lbx = fminf(xmb - rc.c, rc.curve.w) * rc.mt - 3.14f;
+                lbx = fminf(xrow - rc.c, rc.curve.w) * rc.mt - 3.14f;
             } else {
-                lbx = xmb * rc.invT - 3.14f;
+                lbx = xrow * rc.invT - 3.14f;
             }
             screen_consts(uniform(fmaxf(candidate_score(), lbx)), xmb, o);
         } else if (ok && sampled) {
@@ -1064,6 +1072,7 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
             row_bc[9] = o[6];
             row_bc[10] = o[7];
             row_bc[11] = o[8];
+            row_bc[12] = xrow;
         }
     }
     __syncthreads();
@@ -1084,11 +1093,12 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
     // threshold, and the lower bound from the chunk's largest logit (the first draw's)
     const bool tan_set = uniform(row_bc[10]) > 0.0f;
     const float tan_i = uniform(row_bc[11]);
+    const float xmax_row = uniform(row_bc[12]);
     float lbx_row;
     if constexpr (HLG) {
-        lbx_row = uniform(fminf(xmax_blk - rc.c, rc.curve.w) * rc.mt - 3.14f);
+        lbx_row = uniform(fminf(xmax_row - rc.c, rc.curve.w) * rc.mt - 3.14f);
     } else {
-        lbx_row = uniform(xmax_blk * rc.invT - 3.14f);
+        lbx_row = uniform(xmax_row * rc.invT - 3.14f);
     }
     auto code_needed = [&](float x) -> float {
         return fminf(fmaxf(__builtin_fmaf(x, sa, sb), __builtin_fmaf(x, ta, tb)), sc);
@@ -1299,9 +1309,10 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
                 __hip_atomic_store(a.keys + o, (uint64_t)0, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
             }
-            if (tid == 0)
+            if (tid == 0) {
                 __hip_atomic_store(a.counters + b * a.nkg + kg, 0u, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
+            }
             // the exchange's slots (one draw group per row: every block of the row is past
             // its wait once it has counted in, and thread 0 of each, which published its
             // partial, saw those stores complete before it counted in)

@@ -255,16 +255,20 @@ def test_resident_grid_work_queue(hs, oracle_mod, layout):
 
 def test_workspace_left_clean(hs):
     """A split call leaves its workspace's counters, keys and exchange slots zero-filled, so
-    calls can reuse it (with draw groups and the pre-pass, and with the in-kernel exchange)."""
+    calls can reuse it (with draw groups and the pre-pass, with the in-kernel exchange, and
+    without the curve)."""
     w = W.generic(2, 100000, torch.float32, seed=81, hlg=HLG_A, K=4)
     d = on_device(w)
     ws = hs.workspace(2, 100000, 4, torch.float32, True)
     # layout for B = 2, K = 4: counters [0, 256), keys [256, 512), pre-pass partials
     # [512, 2560), exchange slots [2560, 4608)
-    for opts in (hs.SampleOpts(variant=2, nchunk=9),
-                 hs.SampleOpts(variant=2, nchunk=9, draw_groups=1, split_lse=2)):
-        outs = [hs.sample_ex(d["logits"], d["T"], d["seed"], d["offset"], mu=d["mu"], hlg=HLG_A,
-                             k=4, ws=ws, opts=opts).cpu().numpy()
+    for hlg, opts in ((HLG_A, hs.SampleOpts(variant=2, nchunk=9)),
+                      (HLG_A, hs.SampleOpts(variant=2, nchunk=9, draw_groups=1, split_lse=2)),
+                      (None, hs.SampleOpts(variant=2, nchunk=9)),
+                      (None, hs.SampleOpts(variant=2, nchunk=9, draw_groups=2))):
+        outs = [hs.sample_ex(d["logits"], d["T"], d["seed"], d["offset"],
+                             mu=d["mu"] if hlg else None, hlg=hlg, k=4, ws=ws,
+                             opts=opts).cpu().numpy()
                 for _ in range(3)]
         torch.cuda.synchronize()
         assert int(ws[:512].to(torch.int32).abs().sum()) == 0

@@ -43,9 +43,12 @@ def test_plans_of_the_workloads():
     assert (p["nchunk"], p["draw_groups"], p["draws_per_group"]) == (1, 250, 4)
     # 8 x 65536 bf16, curve off: split so that the batch fills about half the CUs
     assert hs.sample_plan(8, 65536, 1, bf16, False)["nchunk"] == 16
-    # 8 x 151936 fp32 with the curve: about one block per CU
+    # 8 x 151936 fp32 with the curve: at most 16 chunks (their partials are exchanged)
     p = hs.sample_plan(8, 151936, 1, f32, True)
-    assert p["nchunk"] == 32 and p["grid"] == 256
+    assert p["nchunk"] == 16 and p["grid"] == 128
+    # ... which 16 rows fill one block per CU
+    p = hs.sample_plan(16, 151936, 1, f32, True)
+    assert p["nchunk"] == 16 and p["grid"] == 256
     # the 256 x 151936 bf16 headline: one block of 1024 threads per row, 19 slots each
     p = hs.sample_plan(256, 151936, 1, bf16, True)
     assert (p["nchunk"], p["bs"], p["nv"], p["grid"]) == (1, 1024, 19, 256)
