@@ -213,8 +213,10 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
     using tr = dtype_traits<DT>;
     constexpr int EPV = tr::epv;
     constexpr int NG = EPV / 4;                // Philox calls per vector
-    constexpr int D = NV < 8 ? NV : 8;         // loads in flight per lane
-    constexpr int LAG = NV < 7 ? NV - 1 : 6;   // slots of random words ahead of the logits
+    // loads in flight per lane, and slots of random words ahead of the logits (measured on
+    // MI355X: more loads in flight than 6 lengthen the pass, the words gain from a long lead)
+    constexpr int D = NV < 6 ? NV : 6;
+    constexpr int LAG = NV < 11 ? NV - 1 : 10;
     // Dynamic LDS, one dword per lane and slot: the vector's largest logit as a bf16-grid upper
     // bound in the low half (draw-invariant) and the high 16 bits of its largest random word of
     // the current draw in the high half. Each lane's entries are contiguous (odd stride: lanes
