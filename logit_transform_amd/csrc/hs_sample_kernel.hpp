@@ -1107,17 +1107,33 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
     };
     // Exact scores of the elements of slot n (vector v, words w) that pass their own bound,
     // folded into the draw's best key.
+    // The elements that pass are marked first and then scored one at a time, so a wave makes
+    // as many exact scores as its busiest lane has passing elements (usually one), however
+    // the lanes' elements differ.
     auto score_words = [&](int n, const uint4 &v, const uint32_t (&w)[EPV],
                            uint64_t best) -> uint64_t {
         const int gv = lane_v + n * BS;
+        uint32_t pm = 0;
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
             const float x = elem<DT>(v, e);
             const float cf = (float)__clz(~w[e]);
-            if (x > -__builtin_inff() && (HLG || x >= tau_row) && cf >= code_needed(x)) {
-                const uint32_t i = (uint32_t)gv * EPV + e;
-                best = umax64(best, make_key(exact_score<HLG>(x, w[e], rc), i));
+            const bool pass = x > -__builtin_inff() && (HLG || x >= tau_row) &&
+                              cf >= code_needed(x);
+            pm |= (pass ? 1u : 0u) << e;
+        }
+        while (pm) {
+            const int e = __builtin_ctz(pm);
+            pm &= pm - 1u;
+            float x = 0.0f;
+            uint32_t we = 0u;
+#pragma unroll
+            for (int q = 0; q < EPV; ++q) {
+                x = q == e ? elem<DT>(v, q) : x;
+                we = q == e ? w[q] : we;
             }
+            const uint32_t i = (uint32_t)gv * EPV + (uint32_t)e;
+            best = umax64(best, make_key(exact_score<HLG>(x, we, rc), i));
         }
         return best;
     };
