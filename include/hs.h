@@ -184,9 +184,10 @@ typedef struct {
                             pre-pass, 2 exchange the chunks' partials inside the sampling
                             kernel (one draw group per row). Automatic: the exchange, either
                             with one block per (row, chunk) when they are all resident at
-                            once, or with a resident grid whose blocks take the (row, chunk)
-                            items from a counter in the workspace (so a row's chunks still
-                            run together); the pre-pass only when neither applies           */
+                            once, or (aligned rows, chunks of 12 or 16 vectors per thread)
+                            with a resident grid whose blocks take the (row, chunk) items
+                            from a counter in the workspace (so a row's chunks still run
+                            together); the pre-pass when neither applies                    */
     int32_t exchange_wait; /* polls for the other chunks' partials before a block works
                               them out itself: 0 default, -1 none (test control), > 0 that
                               many                                                         */

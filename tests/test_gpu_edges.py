@@ -253,6 +253,36 @@ def test_resident_grid_work_queue(hs, oracle_mod, layout):
                         "work queue " + layout))
 
 
+@pytest.mark.parametrize("dtype,V,nv,pivot", [(torch.bfloat16, 196608, 12, "top"),
+                                               (torch.float16, 250000, 16, "entropy")])
+def test_work_queue_other_kernels(hs, oracle_mod, dtype, V, nv, pivot):
+    """The work-queue grid's other instantiations: 16-bit rows in chunks of 12 and 16 slots per
+    lane, with the top and entropy anchors (screened layout). Ids agree with the oracle's, and
+    ids and scores equal the one-block-per-item exchange's bit for bit."""
+    B, K = 300, 1
+    hlg = dict(HLG_A, pivot=pivot, pivot_offset=2.0 if pivot == "top" else 0.0)
+    w = W.generic(B, V, dtype, seed=87, scale=1.0, mask_frac=0.1, hlg=hlg, K=K)
+    plan = hs.sample_plan(B, V, K, dtype, True)
+    assert plan["nchunk"] > 1 and plan["draw_groups"] == 1 and plan["grid"] > plan["cus"]
+    assert plan["nv"] == nv
+    d = on_device(w)
+    opts = hs.SampleOpts(layout=hs.LAYOUTS["screened"])
+    ws = hs.workspace(B, V, K, dtype, True)
+    q = hs.sample_ex(d["logits"], d["T"], d["seed"], d["offset"], hlg=hlg, k=K, ws=ws,
+                     opts=opts, want_best=True)
+    exch = hs.sample_ex(d["logits"], d["T"], d["seed"], d["offset"], hlg=hlg, k=K,
+                        opts=hs.SampleOpts(layout=opts.layout, split_lse=2, exchange_wait=-1),
+                        want_best=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(q[0].cpu().numpy(), exch[0].cpu().numpy())
+    np.testing.assert_array_equal(q[1].cpu().numpy(), exch[1].cpu().numpy())
+    assert int(ws[:256].to(torch.int32).abs().sum()) == 0
+    assert int(ws[-256:].to(torch.int32).abs().sum()) == 0
+    o, s1, s2 = oracle_sample(oracle_mod, w, layout="screened")
+    print(assert_parity(q[0].cpu().numpy(), o, s1, s2, w.logits.double().numpy(),
+                        "work queue %s %s" % (dtype, pivot)))
+
+
 def test_workspace_left_clean(hs):
     """A split call leaves its workspace's counters, keys and exchange slots zero-filled, so
     calls can reuse it (with draw groups and the pre-pass, with the in-kernel exchange, and
