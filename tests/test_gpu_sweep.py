@@ -1,8 +1,11 @@
 """A seeded sweep of random configurations on the HIP path against the oracle: dtype, batch,
 vocabulary (from one token to rows that must be split), draws, curve and pivot mode (given,
-top, entropy, median), masking, padded rows, large counter offsets, greedy and invalid rows,
-and the top-k / top-p filters. Each case is small enough for the oracle; the comparison rule
-is the other parity tests'."""
+top, entropy, median), word layout, masking, padded rows, large counter offsets, greedy and
+invalid rows, and the top-k / top-p filters. Each case is small enough for the oracle; the
+comparison rule is the other parity tests'. HS_SWEEP_SEED and HS_SWEEP_CASES select a longer
+or different sweep (defaults: the seed below, 48 cases)."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -59,11 +62,12 @@ def _device_rows(w, pad):
 
 
 def test_random_configurations(hs, oracle_mod):
-    rng = np.random.default_rng(20261202)
-    for i in range(48):
+    rng = np.random.default_rng(int(os.environ.get("HS_SWEEP_SEED", "20261202")))
+    for i in range(int(os.environ.get("HS_SWEEP_CASES", "48"))):
         w, mode, pad = _case(rng, i)
-        label = "case %d: %s B=%d V=%d K=%d %s pad %d" % (i, w.logits.dtype, w.B, w.V, w.K,
-                                                        mode, pad)
+        layout = ("plain", "screened")[int(rng.integers(2))]
+        label = "case %d: %s B=%d V=%d K=%d %s pad %d %s" % (i, w.logits.dtype, w.B, w.V, w.K,
+                                                           mode, pad, layout)
         print(label, flush=True)
         if mode == "filter":
             k = rng.choice([0, 1, 5, 50, w.V + 1], size=w.B).astype(np.int32)
@@ -75,9 +79,11 @@ def test_random_configurations(hs, oracle_mod):
         seed = torch.from_numpy(np.ascontiguousarray(w.seed).view(np.int64)).cuda()
         off = torch.from_numpy(np.ascontiguousarray(w.offset).view(np.int64)).cuda()
         mu = torch.from_numpy(w.mu).cuda() if mode == "given" else None
-        g = hs.sample(x, T, seed, off, mu=mu, hlg=w.hlg, k=w.K).cpu().numpy()
+        g = hs.sample_ex(x, T, seed, off, mu=mu, hlg=w.hlg, k=w.K,
+                         opts=hs.SampleOpts(layout=hs.LAYOUTS[layout])).cpu().numpy()
         o, s1, s2 = oracle_mod.sample(w.logits, w.T, w.seed, w.offset, K=w.K,
-                                      mu=w.mu if mode == "given" else None, hlg=w.hlg)
+                                      mu=w.mu if mode == "given" else None, hlg=w.hlg,
+                                      layout=layout)
         x64 = w.logits.double().numpy()
         # the median: rows whose mass boundary is decided away from one half
         sure = _median_sure(oracle_mod, w) if mode == "median" else np.ones(w.B, dtype=bool)
