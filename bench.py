@@ -145,7 +145,7 @@ def oracle_one_thread(cfg: int, rows: int, layout: str = "plain") -> None:
     prints rows/s as JSON."""
     from oracle import oracle as O
     from synth import workloads as W
-    w = W.CONFIGS[cfg]()
+    w = W.WORKLOADS[cfg]()
     O.lib()
     def run():
         O.sample(w.logits[:rows], w.T[:rows], w.seed[:rows], w.offset[:rows], K=w.K,
@@ -234,7 +234,7 @@ def main():
     L = hs.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = W.CONFIGS[args.config]()
+    w = W.WORKLOADS[args.config]()
     B, V, K = w.B, w.V, w.K
     settings = None
     filtered = args.top_k > 0 or args.top_p < 1.0

@@ -191,4 +191,4 @@ def generic(B: int, V: int, dtype=torch.float32, *, seed: int = 7, scale: float 
                     seeds, offs, K=K, hlg=hlg, mu=mu)
 
 
-CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+WORKLOADS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
