@@ -115,9 +115,11 @@ int hs_hlg_pivot(const hs_logits *x, const float *mu, const hs_hlg_params *p, fl
  * T: device float[B]; seed, offset: device uint64[B]; out: device int32[B*K].
  * ws / ws_bytes: device workspace of at least hs_workspace_bytes(B, V, K, dtype, 0) bytes,
  * zero-filled before its first use (hs_workspace_init); every successful call leaves its
- * counters, keys and exchange slots zero-filled again (the per-row filter thresholds and row marks of
- * hs_sample_filtered are rewritten by every such call before they are read). Calls that may
- * run concurrently need separate workspaces. ws may be
+ * counters, keys and exchange slots zero-filled again (the split pre-pass's partials, and the
+ * per-row filter thresholds and row marks of hs_sample_filtered, are left as written: each call
+ * writes them before it reads them). Those regions' offsets depend on B and K, so a workspace
+ * reused for a call with another B or K must be zero-filled again first (hs_workspace_init).
+ * Calls that may run concurrently need separate workspaces. ws may be
  * NULL with ws_bytes 0, in which case only single-block-per-row kernels are used. */
 int hs_gumbel_argmax(const hs_logits *x, const float *T, const uint64_t *seed,
                      const uint64_t *offset, int32_t K, int32_t *out, void *ws,
@@ -238,7 +240,9 @@ int hs_sample_rows(const hs_logits *x, const float *T, const float *mu, const hs
  * comes from a static device array of hs_sample_noalloc_max_workspace() bytes (4 MiB) that the
  * library holds on every GPU it runs on until the process ends. A shape whose workspace
  * (hs_workspace_bytes) exceeds it gives HS_ERR_UNSUPPORTED. The first call on a device
- * zero-fills the array on `stream`; every call leaves it zero-filled again. All calls on one
+ * zero-fills the array on `stream`, and so does (over the span of both shapes' workspaces) a
+ * call whose B or K differs from the previous call's on that device; a run of calls of one
+ * shape adds no launch. All calls on one
  * GPU share its array: calls that overlap in time on one GPU (concurrent streams, or
  * unsynchronised host threads) race and their results are undefined. No hipMalloc, hipFree
  * or allocating library routine is called. Ids and scores equal hs_sample_ex's. */

@@ -358,11 +358,18 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void *g_scratch[kMaxDevices];
+int64_t g_scratch_B[kMaxDevices], g_scratch_K[kMaxDevices];   // the last call's shape
 
-// The current device's scratch address. On a device's first use: the symbol's address on that
-// device (the device is current), and a zero fill of the whole array on the caller's stream,
-// since the workspace must start zero-filled (every successful call leaves it so again).
-int scratch_for_device(hipStream_t s, void **out) {
+// The current device's scratch address, for a call of B rows and K draws. On a device's first
+// use: the symbol's address on that device (the device is current), and a zero fill of the
+// whole array on the caller's stream, since the workspace must start zero-filled. Every
+// successful call leaves the regions that must start zero (counters, keys, exchange slots,
+// queue counters) zero again, but the region offsets depend on B and K, and the regions a call
+// leaves as written (pre-pass partials, filter thresholds, row marks) can lie where a call of
+// another shape needs zeros: so when B or K differs from the previous call's, the span of
+// both layouts is zero-filled first (a fill kernel, never hipMemsetAsync, since the call may
+// be captured into a graph).
+int scratch_for_device(hipStream_t s, int64_t B, int64_t K, void **out) {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return HS_ERR_HIP;
     std::lock_guard<std::mutex> lock(g_scratch_mu);
@@ -373,7 +380,15 @@ int scratch_for_device(hipStream_t s, void **out) {
         if (hs::launch_fill_zero(p, (int64_t)(kScratchBytes / 4), s) != hipSuccess)
             return HS_ERR_HIP;
         g_scratch[dev] = p;
+    } else if (g_scratch_B[dev] != B || g_scratch_K[dev] != K) {
+        const size_t prev = ws_layout(g_scratch_B[dev], (int32_t)g_scratch_K[dev]).total;
+        const size_t cur = ws_layout(B, (int32_t)K).total;
+        const size_t span = prev > cur ? prev : cur;
+        if (hs::launch_fill_zero(g_scratch[dev], (int64_t)(span / 4), s) != hipSuccess)
+            return HS_ERR_HIP;
     }
+    g_scratch_B[dev] = B;
+    g_scratch_K[dev] = K;
     *out = g_scratch[dev];
     return HS_OK;
 }
@@ -511,7 +526,7 @@ int hs_sample_noalloc(const hs_logits *x, const float *T, const float *mu,
     const size_t need = ws_layout(x->B, K).total;
     if (need > kScratchBytes) return HS_ERR_UNSUPPORTED;
     void *ws = nullptr;
-    rc = scratch_for_device(reinterpret_cast<hipStream_t>(stream), &ws);
+    rc = scratch_for_device(reinterpret_cast<hipStream_t>(stream), x->B, K, &ws);
     if (rc) return rc;
     return sample_impl(x, T, mu, hlg, nullptr, seed, offset, K, out, best, ws, need, opts,
                        stream);

@@ -1,7 +1,8 @@
 """The allocation-free entry point (hs_sample_noalloc) against hs_sample_ex: the same kernels,
 the workspace taken from the library's static device array instead of the caller's. Two calls
-in a row, the second with a smaller input (the array keeps the first call's contents, which
-every call leaves zero-filled where the next one needs zeros), through the C ABI."""
+in a row through the C ABI, the second with a smaller input (the array keeps the first call's
+contents); and a pair whose second call keeps its keys where the first call's split pre-pass
+left its partials (the array is zero-filled again when the shape changes)."""
 import ctypes as C
 
 import numpy as np
@@ -47,6 +48,10 @@ def _both(hs, w, opts_kw):
     # many draws spread over blocks with the pre-pass, then one small row
     (dict(B=4, V=100000, dtype=torch.bfloat16, hlg=HLG_A, K=16, layout=0, seed=7),
      dict(B=1, V=5000, dtype=torch.float32, hlg=HLG_A, K=3, layout=1, seed=8)),
+    # one row, 16 chunks and 4 draw groups with the pre-pass (its partials at [512, 768) of
+    # the array), then 16 split rows without the curve, whose keys lie at [256, 768)
+    (dict(B=1, V=100000, dtype=torch.bfloat16, hlg=HLG_A, K=4, layout=1, seed=11),
+     dict(B=16, V=65536, dtype=torch.bfloat16, hlg=None, K=3, layout=0, seed=12)),
 ])
 def test_noalloc_matches_sample_ex(hs, oracle_mod, first, second):
     for case in (first, second):
