@@ -297,8 +297,9 @@ int sample_impl(const hs_logits *x, const float *T, const float *mu, const hs_hl
         a.tau = f.tau;
     }
     // Split rows with the curve on: the chunks' log-sum-exp partials are exchanged inside the
-    // sampling kernel when every block of the grid is resident at once (and one draw group per
-    // row); otherwise a pre-pass computes them.
+    // sampling kernel (one draw group per row) when every block of the grid is resident at
+    // once, or on a resident work-queue grid (chunks of 12 or 16 slots); otherwise a pre-pass
+    // computes them.
     // The mass median: the threshold kernel's top-p selection at p = 0.5, T = 1 gives every
     // row's shift c before the sampling kernel runs (which then needs no log-sum-exp).
     // Per-row settings: the same for the rows whose record asks for the median (the others

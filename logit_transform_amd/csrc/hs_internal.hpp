@@ -59,7 +59,8 @@ struct SampleArgs {
     const RowCurve *row_curves;   // [B] per-row curve settings (pivot mode 3), else null
     const float *tau;             // [B] top-k / top-p thresholds (curve off), else null
     // split rows with the curve on: exchange the chunks' partials inside the sampling kernel
-    // instead of a pre-pass (one draw group per row, every block resident at once)
+    // instead of a pre-pass (one draw group per row, a row's blocks running together: every
+    // block resident at once, or the work-queue grid)
     int32_t exchange;
     int32_t spins;                // polls before a block works a missing partial out itself
     uint32_t *xslots;             // [B * part_stride * 4]: chunk partials of the exchange,

@@ -15,7 +15,8 @@
 // top 16 bits of its largest word), the lane's running maximum and log-sum-exp, and the
 // lane's "champion" vector (the one holding its largest word) in registers. Rows split over
 // several blocks combine their chunks' log-sum-exp partials either from a pre-pass or, when
-// the whole grid is resident, by exchanging them inside this kernel; the chunks' winning keys
+// a row's blocks run together (the whole grid resident, or a resident grid taking items from
+// a work queue), by exchanging them inside this kernel; the chunks' winning keys
 // meet in a 64-bit atomic max, and the last block of each (row, draw group) writes the token
 // ids and zeroes its workspace slots again.
 //
@@ -1010,8 +1011,8 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
                         c = (mb + ub / sb) * kLn2;
                     }
                 } else {
-                    // the chunks' (max, sum, u) of the pre-pass, one per lane (nchunk <= 64),
-                    // all read at once; natural units
+                    // the chunks' (max, sum, u), from the pre-pass or the exchange, one per
+                    // lane (nchunk <= 64), all read at once; natural units
                     const float4 pj = lane < a.nchunk
                                           ? parts[lane]
                                           : make_float4(-__builtin_inff(), 0.0f, 0.0f, 0.0f);
