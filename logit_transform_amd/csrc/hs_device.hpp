@@ -190,32 +190,37 @@ __device__ __forceinline__ bool temp_valid(float T) {
 // Accurate fp32 log1p(t) for t > -1 by the log(1+t) * t / ((1+t) - 1) correction (Goldberg,
 // "What every computer scientist should know about floating-point arithmetic", 1991): the
 // rounding of 1 + t is compensated exactly, leaving a few ulps from logf.
+// The helpers below run without branches: every case is computed and the result selected, so
+// a wave whose lanes fall in different cases runs one short sequence, and independent parts
+// (the curve's logarithm and the Gumbel value's) can overlap.
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ float log1p_acc(float t) {
     const float u = 1.0f + t;
-    if (u == 1.0f) return t;
-    if (u == __builtin_inff()) return __builtin_inff();
     // t / (u - 1) = 1 + (t - d) / d with d = u - 1 exact and t - d the exact rounding error of
     // 1 + t: the quotient is within an ulp of 1, so a hardware reciprocal (no IEEE divide
     // sequence) keeps it to about half an ulp.
     const float d = u - 1.0f;
     const float corr = __builtin_fmaf(t - d, __builtin_amdgcn_rcpf(d), 1.0f);
-    return logf(u) * corr;
+    float r = logf(u) * corr;
+    r = (u == __builtin_inff()) ? __builtin_inff() : r;
+    return (u == 1.0f) ? t : r;   // (1 + t rounds to 1: log1p(t) = t to fp32 precision)
 }
 
 // Gumbel noise of one word [GMX, Background: g = -log(-log(u))], u = (r + 1/2) 2^-32.
 // E = -log(u) is formed from u on the lower half and from v = 1 - u = (~r + 1/2) 2^-32 by
 // log1p on the upper half, so E keeps full relative precision where u is close to 1 -- the
-// words that win draws.
+// words that win draws. Both halves share one conversion and one logarithm (of u, or of the
+// rounded 1 - v that log1p_acc corrects).
 __device__ __forceinline__ float gumbel32(uint32_t r) {
-    float E;
-    if (r < 0x80000000u) {
-        const float u = __builtin_fmaf((float)r, 0x1p-32f, 0x1p-33f);
-        E = -logf(u);
-    } else {
-        const float v = __builtin_fmaf((float)(~r), 0x1p-32f, 0x1p-33f);
-        E = -log1p_acc(-v);
-    }
+    const bool lower = r < 0x80000000u;
+    const float f = __builtin_fmaf((float)(lower ? r : ~r), 0x1p-32f, 0x1p-33f);   // u or v
+    const float t = -f;
+    const float u1 = 1.0f + t;
+    const float L = logf(lower ? f : u1);
+    const float d = u1 - 1.0f;
+    const float corr = __builtin_fmaf(t - d, __builtin_amdgcn_rcpf(d), 1.0f);
+    const float l1p = (u1 == 1.0f) ? t : L * corr;   // log1p(-v) (1 - v never overflows)
+    const float E = lower ? -L : -l1p;
     return -logf(E);
 }
 
@@ -247,8 +252,9 @@ __device__ __forceinline__ float max2f(float a, float b) {
 
 // ------------------------------------------------------------------------------------------
 // The HLG transfer function [HLG, The transfer function, eq. g]: toe / mid / shoulder
-// selected on z vs +-w (the unselected branches are never evaluated, so -inf never meets
-// log1p's NaN paths). ln(1 + t) by log1p_acc.
+// selected on z vs +-w: both logarithmic branches share one log1p_acc, whose argument and
+// result are selected (a value the other branch would have produced, NaN included, is
+// discarded). ln(1 + t) by log1p_acc.
 // ------------------------------------------------------------------------------------------
 struct Curve {
     float m, w;          // mid gain, mid half-width (w may be +inf)
@@ -258,9 +264,11 @@ struct Curve {
 };
 
 __device__ __forceinline__ float hlg32(float z, const Curve &c) {
-    if (z < -c.w) return -c.mw - c.mbt * log1p_acc((-z - c.w) * c.ibt);
-    if (z > c.w) return c.mw + c.mbh * log1p_acc((z - c.w) * c.ibh);
-    return c.m * z;
+    const bool toe = z < -c.w;
+    const bool shoulder = z > c.w;
+    const float L = log1p_acc(toe ? (-z - c.w) * c.ibt : (z - c.w) * c.ibh);
+    const float r = toe ? -c.mw - c.mbt * L : c.mw + c.mbh * L;
+    return (toe || shoulder) ? r : c.m * z;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -416,11 +424,16 @@ __device__ __forceinline__ uint64_t rl_u64(uint64_t v, int lane) {
     return ((uint64_t)hi << 32) | lo;
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+// Maximum over each row of 16 lanes, left in every lane of the row.
+__device__ __forceinline__ uint64_t row_max_u64(uint64_t v) {
     v = dpp_max_u64<kDppQuad1032>(v);
     v = dpp_max_u64<kDppQuad2301>(v);
     v = dpp_max_u64<kDppRowHalfMirror>(v);
-    v = dpp_max_u64<kDppRowMirror>(v);
+    return dpp_max_u64<kDppRowMirror>(v);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    v = row_max_u64(v);
     const uint64_t a = umax64(rl_u64(v, 0), rl_u64(v, 16));
     const uint64_t b = umax64(rl_u64(v, 32), rl_u64(v, 48));
     return umax64(a, b);

@@ -218,15 +218,30 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
     // MI355X: more loads in flight than 6 lengthen the pass, the words gain from a long lead)
     constexpr int D = NV < 6 ? NV : 6;
     constexpr int LAG = NV < 11 ? NV - 1 : 10;
+    // Chunks of few slots keep every slot's vector in registers from the pass on, so that the
+    // vectors that pass the screen (and later draws' champions) need no second read: a read
+    // after the pass costs a whole memory round trip on the block's critical path.
+    constexpr bool KEEP = NV <= 6;
+    // The first draw's bootstrap candidates: chunks of many slots (1024-thread blocks whose
+    // post-pass is bound by instruction issue) post their champions for wave 0 to draw and
+    // score; small chunks (latency-bound) draw and rank them in every wave instead, which
+    // keeps wave 0's serial work short.
+    constexpr bool BOOT0 = NV >= 8;
     // Dynamic LDS, one dword per lane and slot: the vector's largest logit as a bf16-grid upper
     // bound in the low half (draw-invariant) and the high 16 bits of its largest random word of
     // the current draw in the high half. Each lane's entries are contiguous (odd stride: lanes
     // hit distinct banks), so every access is one base register plus an immediate offset.
     extern __shared__ uint32_t s_vec[];
     __shared__ float red_m[16], red_s[16], red_u[16], red_x[16];
-    __shared__ uint64_t red_ck[16];    // per wave: best bootstrap candidate key
-    __shared__ float red_cx[16];       //   its logit
-    __shared__ float red_cg[16];       //   and the Gumbel value of its word
+    // the first draw's bootstrap candidates: with BOOT0 one per group of 16 lanes (the champion
+    // vector, its key (0: none) and the thread that holds it), else one per wave (its key, 0:
+    // none, logit and the Gumbel value of its word)
+    __shared__ uint4 s_cv[64];
+    __shared__ uint32_t s_ck[64];
+    __shared__ int32_t s_ct[64];
+    __shared__ uint64_t red_ck[16];
+    __shared__ float red_cx[16];
+    __shared__ float red_cg[16];
     __shared__ float row_bc[13];       // row constants from wave 0
     // per wave, the best exact candidate score of a later draw; two buffers, alternating
     // between draws (a wave may post draw k + 1's before a slower one has read draw k's)
@@ -492,43 +507,6 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
             }
         }
     };
-    // Screened layout: the leading halves of vector gv's words (low halves zero), and the
-    // second call that completes them.
-    auto vec_words_hi = [&](const Stream &sk, int gvi, uint32_t (&w)[EPV]) {
-        const uint32_t gv = (uint32_t)gvi;
-        uint32_t q2 = EPV == 8 ? gv << 1 : gv & ~1u;
-        asm volatile("" : "+v"(q2));
-        const Words4 hi = philox4x32_10_uk(q2, sk.row, sk.off_lo, sk.off_hi, sk.key0, sk.key1);
-        if constexpr (EPV == 8) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) w[e] = half16(hi, e) << 16;
-        } else {
-            const bool h = (gv & 1u) != 0u;
-            const uint32_t h0 = h ? hi.w[2] : hi.w[0], h1 = h ? hi.w[3] : hi.w[1];
-            w[0] = h0 << 16;
-            w[1] = h0 & 0xFFFF0000u;
-            w[2] = h1 << 16;
-            w[3] = h1 & 0xFFFF0000u;
-        }
-    };
-    auto vec_words_lo = [&](const Stream &sk, int gvi, uint32_t (&w)[EPV]) {
-        const uint32_t gv = (uint32_t)gvi;
-        uint32_t q2 = EPV == 8 ? gv << 1 : gv & ~1u;
-        asm volatile("" : "+v"(q2));
-        const Words4 lo = philox4x32_10_uk(q2 | 1u, sk.row, sk.off_lo, sk.off_hi, sk.key0,
-                                           sk.key1);
-        if constexpr (EPV == 8) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) w[e] |= half16(lo, e);
-        } else {
-            const bool h = (gv & 1u) != 0u;
-            const uint32_t l0 = h ? lo.w[2] : lo.w[0], l1 = h ? lo.w[3] : lo.w[1];
-            w[0] |= l0 & 0xFFFFu;
-            w[1] |= l0 >> 16;
-            w[2] |= l1 & 0xFFFFu;
-            w[3] |= l1 >> 16;
-        }
-    };
     // the bits of a word that the champion key holds: (w ^ key) <= kMatch when they agree
     constexpr uint32_t kMatch = LAY == LAY_PLAIN ? 31u : 0xFFFFu;
     // Screened layout with four elements per vector: the two lanes whose vectors make up a group
@@ -623,13 +601,13 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
     // without it.
     const float lin = HLG ? cv.m * invT : invT;
     // Bootstrap candidate of a lane for draw stream sk: the element holding the largest word of
-    // its champion vector v (nearly the largest Gumbel value among the lane's elements). The
-    // vector's words are drawn again into cw (kept for the screen); in the screened layout only
-    // their leading halves, with the low halves zero: a word no larger than the element's, so
-    // its Gumbel value bounds the element's from below, which is all the bootstrap needs (the
-    // screen completes the words if it scores the vector). Returns the candidate's rank key
-    // (lin x - log(1 - u) -- a monotone stand-in for the Gumbel value, close to it where u is
-    // near 1 -- and the lane) and its logit and word.
+    // its champion vector v (nearly the largest Gumbel value among the lane's elements; in the
+    // screened layout the largest leading half, the first element of a tie). The vector's whole
+    // words are drawn again into cw and kept for the screen: in the screened layout its two
+    // calls are independent, so they overlap, and a champion that passes the screen needs no
+    // further call. Returns the candidate's rank key (lin x - log(1 - u) -- a monotone
+    // stand-in for the Gumbel value, close to it where u is near 1 -- and the lane) and its
+    // logit and word.
     struct Cand {
         uint64_t key;
         float x;
@@ -638,11 +616,7 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
     auto candidate = [&](const Stream &sk, uint32_t champ, const uint4 &v,
                          uint32_t (&cw)[EPV]) -> Cand {
         Cand c{0ull, -__builtin_inff(), 0u};
-        if constexpr (LAY == LAY_PLAIN) {
-            vec_words(sk, lane_v + (int)(champ & 31u) * BS, cw);
-        } else {
-            vec_words_hi(sk, lane_v + (int)(champ & 31u) * BS, cw);
-        }
+        vec_words(sk, lane_v + (int)(champ & 31u) * BS, cw);
 #pragma unroll
         for (int e = EPV - 1; e >= 0; --e) {
             if ((cw[e] ^ champ) <= kMatch) {
@@ -667,6 +641,24 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
     uint32_t champ0 = 0;
     uint4 craw0 = ninf4;
     uint32_t cw0[EPV];   // the champion vector's words
+    uint4 keep[KEEP ? NV : 1];
+    // Slot n's vector again (n lane-varying): selected from the kept registers, or read.
+    auto slot_vec = [&](int n) -> uint4 {
+        if constexpr (KEEP) {
+            uint4 v = keep[0];
+#pragma unroll
+            for (int j = 1; j < NV; ++j) {
+                const bool h = n == j;
+                v.x = h ? keep[j].x : v.x;
+                v.y = h ? keep[j].y : v.y;
+                v.z = h ? keep[j].z : v.z;
+                v.w = h ? keep[j].w : v.w;
+            }
+            return v;
+        } else {
+            return fetch(lane_v + n * BS);
+        }
+    };
     {
         const Stream sk = stream_k(k0);
         uint4 buf[D];   // loads in flight
@@ -685,6 +677,7 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
             if (j >= 0 && j < NV) {
                 const uint4 v = patch(j, buf[j % D]);
                 data_vec(j, v);
+                if constexpr (KEEP) keep[j] = v;
                 // the champion's vector stays in registers (no second read)
                 const uint32_t kj = ring[j % RING];
                 if (kj > champ0) {
@@ -730,8 +723,33 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
     int wid = threadIdx.x >> 6;
     asm volatile("" : "+v"(wid));
     const int nw = (BS + 63) >> 6;
-    // Per wave, the best bootstrap candidate: its key, logit and the Gumbel value of its word
-    // (which needs no row constant, so each wave works it out before the block combine).
+    // The first draw's bootstrap with BOOT0, without drawing words in every wave: each group of
+    // 16 lanes posts the champion of its best-ranked lane, ranked by lin xm - log(1 - u) with
+    // xm the champion vector's largest logit (its LDS summary) and u the middle of the interval
+    // its code leaves for the largest word. Wave 0 then draws the posted vectors' words, one
+    // candidate per lane, and scores them (at the latency of one).
+    auto post_champion = [&]() {
+        uint64_t rk = 0ull;
+        if (champ0 != 0u) {
+            const uint32_t d = s_vec[lane_lds + (int)(champ0 & 31u)];
+            const float xm = __uint_as_float(d << 16);
+            const float v1u = __builtin_fmaf((float)(0xFFFFu - (d >> 16)), 0x1p-16f, 0x1p-17f);
+            const float r = __builtin_fmaf(xm, lin, -__builtin_amdgcn_logf(v1u) * kLn2);
+            if (xm > -__builtin_inff() && (HLG || xm >= tau_row)) rk = make_key(r, (uint32_t)tid);
+        }
+        const uint64_t gk = row_max_u64(rk);
+        const int j = (wid << 2) | (lane >> 4);
+        if (gk != 0ull && rk == gk) {
+            s_cv[j] = craw0;
+            s_ck[j] = champ0;
+            s_ct[j] = tid;
+        } else if (gk == 0ull && (lane & 15) == 0) {
+            s_ck[j] = 0u;
+        }
+    };
+    // Without BOOT0: each wave's best candidate by its exact rank key, with the logit and the
+    // Gumbel value of its word (which needs no row constant, so each wave works it out before
+    // the block combine).
     auto post_candidate = [&](const Cand &c) {
         const uint64_t wk = wave_max_u64(c.key);
         if (lane == 0) red_ck[wid] = wk;
@@ -740,20 +758,50 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
             red_cg[wid] = gumbel32(c.w);
         }
     };
-    // (wave 0) The best score among the waves' bootstrap candidates, l'/T + G as
-    // exact_score_inl forms it: lane w scores wave w's (all at once, at the latency of one).
+    // (wave 0, BOOT0) Lane j's candidate from group j: the element of the posted vector whose
+    // word the champion key matches, its logit and the Gumbel value of its word (no row
+    // constant needed, so this overlaps the block combine).
+    float cand_x = -__builtin_inff(), cand_g = 0.0f;
+    auto take_candidate = [&]() {
+        const uint32_t ck = lane < 4 * nw ? s_ck[lane] : 0u;
+        if (ck != 0u) {
+            const uint4 v = s_cv[lane];
+            const int gv = v0 + s_ct[lane] + (int)(ck & 31u) * BS;
+            uint32_t w[EPV];
+            vec_words(stream_k(k0), gv, w);
+            float x = -__builtin_inff();
+            uint32_t we = 0u;
+#pragma unroll
+            for (int e = EPV - 1; e >= 0; --e) {
+                if ((w[e] ^ ck) <= kMatch) {
+                    we = w[e];
+                    x = elem<DT>(v, e);
+                }
+            }
+            if (x > -__builtin_inff() && (HLG || x >= tau_row) && gv < vend) {
+                cand_x = x;
+                cand_g = gumbel32(we);
+            }
+        }
+    };
+    // (wave 0) The best score among the bootstrap candidates, l'/T + G as exact_score_inl
+    // forms it (without BOOT0 lane w scores wave w's).
     auto candidate_score = [&]() -> float {
-        const bool has = lane < nw && red_ck[lane] != 0ull;
+        if constexpr (!BOOT0) {
+            if (lane < nw && red_ck[lane] != 0ull) {
+                cand_x = red_cx[lane];
+                cand_g = red_cg[lane];
+            }
+        }
         float cs = -__builtin_inff();
-        if (has) {
-            const float x = red_cx[lane];
+        if (cand_x > -__builtin_inff()) {
             float a;
             if constexpr (HLG) {
-                a = hlg32(x - rc.c, rc.curve) * rc.invT;
+                a = hlg32(cand_x - rc.c, rc.curve) * rc.invT;
             } else {
-                a = x * rc.invT;
+                a = cand_x * rc.invT;
             }
-            cs = a + red_cg[lane];
+            cs = a + cand_g;
         }
         return uniform(wave_max(cs));
     };
@@ -851,7 +899,13 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
             }
         }
     };
-    if (screen) post_candidate(candidate(stream_k(k0), champ0, craw0, cw0));
+    if (screen) {
+        if constexpr (BOOT0) {
+            post_champion();
+        } else {
+            post_candidate(candidate(stream_k(k0), champ0, craw0, cw0));
+        }
+    }
     waves_combine(xmax_lane, lse_r, lse_s, lse_u, red_x);
     __syncthreads();
     // Split rows without the pre-pass (the host chooses this only when a row's chunks run at
@@ -975,6 +1029,7 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
         }
     }
     if (wid == 0) {
+        if (BOOT0 && screen) take_candidate();
         const float xmb = wave_max(lane < nw ? red_x[lane] : -__builtin_inff());
         float c = 0.0f;
         bool ok = xmb > -__builtin_inff();   // the chunk has a finite logit
@@ -1157,7 +1212,7 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
             // exactly (c is known by now), and after one barrier every wave takes the block's
             // best such score as the lower bound and sets up its screen from it
             champ = draw_all(sk);
-            craw0 = fetch(lane_v + (int)(champ & 31u) * BS);
+            craw0 = slot_vec((int)(champ & 31u));
             const Cand cd = candidate(sk, champ, craw0, cw0);
             const float cs = cd.key != 0ull ? exact_score<HLG>(cd.x, cd.w, rc) : -__builtin_inff();
             const float csw = wave_max(cs);
@@ -1198,8 +1253,9 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
             // reaches the bound less the slack, where n counts the leading ones of its largest
             // word's high 16 bits (n = 16 leaves the word unbounded); for greedy rows, only if
             // its largest logit reaches the chunk's. The champion vector and its words are at
-            // hand from the bootstrap; the other vectors that pass (rare) are read again two at a
-            // time, so their loads overlap.
+            // hand from the bootstrap; the other vectors that pass (rare) come from the kept
+            // registers (chunks of few slots) or are read again two at a time, so their loads
+            // overlap.
             uint32_t bits = 0;   // bit n: slot n passes
             if (greedy) {
 #pragma unroll
@@ -1254,9 +1310,8 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
                 const uint32_t cbit = 1u << (champ & 31u);
                 if (bits & cbit) {
                     bits &= ~cbit;
-                    // the bootstrap drew only the leading halves of the screened layout
-                    if constexpr (LAY != LAY_PLAIN)
-                        vec_words_lo(sk, lane_v + (int)(champ & 31u) * BS, cw0);
+                    // (the per-lane bootstrap drew the champion's words already)
+                    if (BOOT0 && k == k0) vec_words(sk, lane_v + (int)(champ & 31u) * BS, cw0);
                     best = score_words((int)(champ & 31u), craw0, cw0, best);
                 }
             }
@@ -1266,8 +1321,8 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
                 const bool two = bits != 0u;
                 const int n2 = two ? __builtin_ctz(bits) : n1;
                 if (two) bits &= bits - 1u;
-                const uint4 v1 = fetch(lane_v + n1 * BS);
-                const uint4 v2 = two ? fetch(lane_v + n2 * BS) : ninf4;
+                const uint4 v1 = slot_vec(n1);
+                const uint4 v2 = two ? slot_vec(n2) : ninf4;
                 best = score_vec(sk, n1, v1, best);
                 if (two) best = score_vec(sk, n2, v2, best);
             }
