@@ -87,6 +87,56 @@ def test_special_rows(hs, oracle_mod, layout):
             assert g[7].tolist() == [-2] * 3
 
 
+@pytest.mark.parametrize("groups", [0, 1])
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("dtype,V", [(torch.float32, 32768), (torch.bfloat16, 151936),
+                                     (torch.bfloat16, 151937)])
+def test_special_rows_one_block_per_row(hs, oracle_mod, layout, dtype, V, groups):
+    """The special rows again with one block per row over long rows (8 and 19 vectors per
+    thread: the first draw's bootstrap candidates are then drawn and scored by one wave for
+    the whole block), plus rows whose few finite logits leave most lanes without a valid
+    champion; V = 151937 also gives rows that are not 16-byte aligned and a ragged tail. With
+    one draw group per row a block's later draws follow its first."""
+    rng = np.random.default_rng(37)
+    B = 11
+    x = rng.normal(0, 1, size=(B, V)).astype(np.float32)
+    x[0, :] = -np.inf                                  # no finite logit -> -1
+    x[1, :] = -np.inf
+    x[1, V // 3] = 2.5                                 # a single finite logit
+    x[2, [3, V // 2, V - 1]] = 9.0                     # greedy with a three-way tie
+    x[3] = np.minimum(x[3], 3.5)                       # (long rows reach 4 by chance)
+    x[3, [10, 11]] = 4.0
+    for r in (8, 9):                                   # about 1% finite, scattered
+        keep = rng.random(V) < 0.01
+        x[r, ~keep] = -np.inf
+    x[10, : V - 100] = -np.inf                         # finite logits only in the tail
+    x = torch.from_numpy(x).to(dtype).float().numpy()  # values on the input grid
+    T = np.array([1.0, 0.7, 0.0, 0.0, -1.0, np.nan, np.inf, 1.2, 0.8, 1.3, 1.0],
+                 dtype=np.float32)
+    mu = np.full(B, -5.0, dtype=np.float32)
+    mu[7] = np.nan
+    seed = rng.integers(0, 2**64, size=B, dtype=np.uint64)
+    off = rng.integers(0, 2**40, size=B, dtype=np.uint64)
+    for hlg in (None, HLG_A):
+        opts = hs.SampleOpts(variant=1, draw_groups=groups)
+        w = W.Workload("special long", torch.from_numpy(x).to(dtype), T, seed, off, K=3,
+                       hlg=hlg, mu=mu if hlg else None)
+        plan = hs.sample_plan(B, V, 3, dtype, hlg is not None, True, opts)
+        assert plan["nchunk"] == 1 and plan["nv"] >= 8, plan
+        assert groups == 0 or plan["draws_per_group"] == 3, plan
+        g = gpu_sample(hs, w, layout=layout, opts=opts)
+        o, s1, s2 = oracle_sample(oracle_mod, w, layout=layout)
+        assert_parity(g, o, s1, s2, x.astype(np.float64), "special long rows %s V=%d hlg=%s %s"
+                      % (dtype, V, bool(hlg), layout))
+        assert g[0].tolist() == [-1] * 3
+        assert g[1].tolist() == [V // 3] * 3
+        assert g[2].tolist() == [3] * 3 and g[3].tolist() == [10] * 3
+        assert g[4].tolist() == [-2] * 3 and g[5].tolist() == [-2] * 3 and g[6].tolist() == [-2] * 3
+        if hlg:
+            assert g[7].tolist() == [-2] * 3
+        assert (g[10] >= V - 100).all()
+
+
 @pytest.mark.parametrize("hlg", [None, HLG_A])
 def test_subnormal_temperature_is_invalid(hs, oracle_mod, hlg):
     """A subnormal temperature (1/T overflows fp32) is invalid (-2) on the GPU and in the oracle,
