@@ -633,8 +633,9 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
 
     // ---- one pass over the chunk: the first draw's random words (which need no logit) run
     // LAG slots ahead of the logits, so the first loads land while they are computed; D loads
-    // stay in flight. The lane's champion vector (largest word so far) is kept in registers as
-    // the logits come in, and its words are drawn again after the pass. The pass is the same
+    // stay in flight. The lane's champion (its slot with the largest word) follows from the
+    // draws alone; its vector stays in registers (long chunks) or is taken from the kept slots
+    // (short ones), and its words are drawn again after the pass. The pass is the same
     // for every row (greedy and invalid rows draw words they never use):
     // without row-dependent branches the scheduler interleaves the integer Philox chains with
     // the float work freely. ----
@@ -662,31 +663,55 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
     {
         const Stream sk = stream_k(k0);
         uint4 buf[D];   // loads in flight
-        constexpr int RING = LAG + 2;   // slot keys between a slot's draw and its logits
+        // long chunks: slot keys between a slot's draw and its logits, and the champion's
+        // vector selected as the logits come in; short chunks take it from the kept slots
+        // after the pass, so their champion is just the largest key (it needs no logit)
+        constexpr int RING = KEEP ? 1 : LAG + 2;
         uint32_t ring[RING];
 #pragma unroll
         for (int n = 0; n < D; ++n) buf[n] = issue_load(n);
 #pragma unroll
         for (int n = 0; n < NV + LAG; ++n) {
             if constexpr (PAIR) {
-                if (n < NV && (n & 1) == 0) draw_pair(sk, n, ring[n % RING], ring[(n + 1) % RING]);
+                if (n < NV && (n & 1) == 0) {
+                    if constexpr (KEEP) {
+                        uint32_t ka, kb;
+                        draw_pair(sk, n, ka, kb);
+                        champ0 = n + 1 < NV ? max3u(champ0, ka, kb) : max(champ0, ka);
+                        asm volatile("" : "+v"(champ0));
+                    } else {
+                        draw_pair(sk, n, ring[n % RING], ring[(n + 1) % RING]);
+                    }
+                }
             } else {
-                if (n < NV) ring[n % RING] = draw_vec(sk, n);
+                if (n < NV) {
+                    if constexpr (KEEP) {
+                        champ0 = max(champ0, draw_vec(sk, n));
+                        asm volatile("" : "+v"(champ0));
+                    } else {
+                        ring[n % RING] = draw_vec(sk, n);
+                    }
+                }
             }
             const int j = n - LAG;
             if (j >= 0 && j < NV) {
                 const uint4 v = patch(j, buf[j % D]);
                 data_vec(j, v);
-                if constexpr (KEEP) keep[j] = v;
-                // the champion's vector stays in registers (no second read)
-                const uint32_t kj = ring[j % RING];
-                if (kj > champ0) {
-                    champ0 = kj;
-                    craw0 = v;
+                if constexpr (KEEP) {
+                    keep[j] = v;
+                } else {
+                    // the champion's vector stays in registers (no second read: reading it
+                    // again once the last slot is drawn costs more than these selects)
+                    const uint32_t kj = ring[j % RING];
+                    if (kj > champ0) {
+                        champ0 = kj;
+                        craw0 = v;
+                    }
                 }
                 if (j + D < NV) buf[j % D] = issue_load(j + D);
             }
         }
+        if constexpr (KEEP) craw0 = slot_vec((int)(champ0 & 31u));
     }
     if constexpr (LSE) {
         // A lane whose largest logit lies more than 100 binary orders above or below its
