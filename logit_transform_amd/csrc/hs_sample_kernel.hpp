@@ -613,10 +613,11 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
         float x;
         uint32_t w;
     };
-    auto candidate = [&](const Stream &sk, uint32_t champ, const uint4 &v,
-                         uint32_t (&cw)[EPV]) -> Cand {
+    // (have_words: cw holds the champion's words already)
+    auto candidate = [&](const Stream &sk, uint32_t champ, const uint4 &v, uint32_t (&cw)[EPV],
+                         bool have_words = false) -> Cand {
         Cand c{0ull, -__builtin_inff(), 0u};
-        vec_words(sk, lane_v + (int)(champ & 31u) * BS, cw);
+        if (!have_words) vec_words(sk, lane_v + (int)(champ & 31u) * BS, cw);
 #pragma unroll
         for (int e = EPV - 1; e >= 0; --e) {
             if ((cw[e] ^ champ) <= kMatch) {
@@ -635,7 +636,8 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
     // LAG slots ahead of the logits, so the first loads land while they are computed; D loads
     // stay in flight. The lane's champion (its slot with the largest word) follows from the
     // draws alone; its vector stays in registers (long chunks) or is taken from the kept slots
-    // (short ones), and its words are drawn again after the pass. The pass is the same
+    // (short ones), and its words are drawn again: after the pass, or in short chunks as soon
+    // as the last slot is drawn, while the loads are in flight. The pass is the same
     // for every row (greedy and invalid rows draw words they never use):
     // without row-dependent branches the scheduler interleaves the integer Philox chains with
     // the float work freely. ----
@@ -692,6 +694,9 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
                         ring[n % RING] = draw_vec(sk, n);
                     }
                 }
+            }
+            if constexpr (KEEP) {
+                if (n == NV - 1) vec_words(sk, lane_v + (int)(champ0 & 31u) * BS, cw0);
             }
             const int j = n - LAG;
             if (j >= 0 && j < NV) {
@@ -775,12 +780,14 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
     // Without BOOT0: each wave's best candidate by its exact rank key, with the logit and the
     // Gumbel value of its word (which needs no row constant, so each wave works it out before
     // the block combine).
+    // (Every lane's Gumbel value is formed before the reduction, so the two overlap.)
     auto post_candidate = [&](const Cand &c) {
+        const float g = gumbel32(c.w);
         const uint64_t wk = wave_max_u64(c.key);
         if (lane == 0) red_ck[wid] = wk;
         if (wk != 0 && c.key == wk) {
             red_cx[wid] = c.x;
-            red_cg[wid] = gumbel32(c.w);
+            red_cg[wid] = g;
         }
     };
     // (wave 0, BOOT0) Lane j's candidate from group j: the element of the posted vector whose
@@ -928,7 +935,7 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
         if constexpr (BOOT0) {
             post_champion();
         } else {
-            post_candidate(candidate(stream_k(k0), champ0, craw0, cw0));
+            post_candidate(candidate(stream_k(k0), champ0, craw0, cw0, KEEP));
         }
     }
     waves_combine(xmax_lane, lse_r, lse_s, lse_u, red_x);
