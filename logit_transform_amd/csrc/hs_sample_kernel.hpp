@@ -227,6 +227,10 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
     // score; small chunks (latency-bound) draw and rank them in every wave instead, which
     // keeps wave 0's serial work short.
     constexpr bool BOOT0 = NV >= 8;
+    // The same for the later draws of a block, where it adds a barrier and wave 0's serial
+    // work to every draw: only chunks of 12 or more slots gain (1024 x 262144 fp32 with 16
+    // draws: -1.2%; 1 x 32768 fp32 with 4 draws per block, 8 slots: +4%).
+    constexpr bool BOOTK = NV >= 12;
     // Dynamic LDS, one dword per lane and slot: the vector's largest logit as a bf16-grid upper
     // bound in the low half (draw-invariant) and the high 16 bits of its largest random word of
     // the current draw in the high half. Each lane's entries are contiguous (odd stride: lanes
@@ -758,10 +762,10 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
     // xm the champion vector's largest logit (its LDS summary) and u the middle of the interval
     // its code leaves for the largest word. Wave 0 then draws the posted vectors' words, one
     // candidate per lane, and scores them (at the latency of one).
-    auto post_champion = [&]() {
+    auto post_champion = [&](uint32_t champ, const uint4 &cvec) {
         uint64_t rk = 0ull;
-        if (champ0 != 0u) {
-            const uint32_t d = s_vec[lane_lds + (int)(champ0 & 31u)];
+        if (champ != 0u) {
+            const uint32_t d = s_vec[lane_lds + (int)(champ & 31u)];
             const float xm = __uint_as_float(d << 16);
             const float v1u = __builtin_fmaf((float)(0xFFFFu - (d >> 16)), 0x1p-16f, 0x1p-17f);
             const float r = __builtin_fmaf(xm, lin, -__builtin_amdgcn_logf(v1u) * kLn2);
@@ -770,8 +774,8 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
         const uint64_t gk = row_max_u64(rk);
         const int j = (wid << 2) | (lane >> 4);
         if (gk != 0ull && rk == gk) {
-            s_cv[j] = craw0;
-            s_ck[j] = champ0;
+            s_cv[j] = cvec;
+            s_ck[j] = champ;
             s_ct[j] = tid;
         } else if (gk == 0ull && (lane & 15) == 0) {
             s_ck[j] = 0u;
@@ -794,13 +798,15 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
     // word the champion key matches, its logit and the Gumbel value of its word (no row
     // constant needed, so this overlaps the block combine).
     float cand_x = -__builtin_inff(), cand_g = 0.0f;
-    auto take_candidate = [&]() {
+    auto take_candidate = [&](const Stream &sk) {
+        cand_x = -__builtin_inff();
+        cand_g = 0.0f;
         const uint32_t ck = lane < 4 * nw ? s_ck[lane] : 0u;
         if (ck != 0u) {
             const uint4 v = s_cv[lane];
             const int gv = v0 + s_ct[lane] + (int)(ck & 31u) * BS;
             uint32_t w[EPV];
-            vec_words(stream_k(k0), gv, w);
+            vec_words(sk, gv, w);
             float x = -__builtin_inff();
             uint32_t we = 0u;
 #pragma unroll
@@ -933,7 +939,7 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
     };
     if (screen) {
         if constexpr (BOOT0) {
-            post_champion();
+            post_champion(champ0, craw0);
         } else {
             post_candidate(candidate(stream_k(k0), champ0, craw0, cw0, KEEP));
         }
@@ -1061,7 +1067,7 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
         }
     }
     if (wid == 0) {
-        if (BOOT0 && screen) take_candidate();
+        if (BOOT0 && screen) take_candidate(stream_k(k0));
         const float xmb = wave_max(lane < nw ? red_x[lane] : -__builtin_inff());
         float c = 0.0f;
         bool ok = xmb > -__builtin_inff();   // the chunk has a finite logit
@@ -1240,19 +1246,34 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
         const Stream sk = stream_k(k);
         uint32_t champ = champ0;
         if (k > k0 && !skip && screen) {
-            // this draw's words and champions; every lane scores its bootstrap candidate
-            // exactly (c is known by now), and after one barrier every wave takes the block's
-            // best such score as the lower bound and sets up its screen from it
+            // this draw's words and champions, and the block's best bootstrap score (c is
+            // known by now) as the lower bound for the screen: with BOOTK wave 0 draws and
+            // scores one champion per 16 lanes between two barriers, as for the first draw;
+            // otherwise every lane scores its own and one barrier combines the waves'
             champ = draw_all(sk);
             craw0 = slot_vec((int)(champ & 31u));
-            const Cand cd = candidate(sk, champ, craw0, cw0);
-            const float cs = cd.key != 0ull ? exact_score<HLG>(cd.x, cd.w, rc) : -__builtin_inff();
-            const float csw = wave_max(cs);
             float *sbp = red_sb[(k - k0) & 1];
-            if (lane == 0) sbp[wid] = csw;
-            __syncthreads();
-            const float bs = uniform(fmaxf(wave_max(lane < nw ? sbp[lane] : -__builtin_inff()),
-                                           lbx_row));
+            float bsw;
+            if constexpr (BOOTK) {
+                post_champion(champ, craw0);
+                __syncthreads();
+                if (wid == 0) {
+                    take_candidate(sk);
+                    const float cs = candidate_score();
+                    if (lane == 0) sbp[0] = cs;
+                }
+                __syncthreads();
+                bsw = sbp[0];
+            } else {
+                const Cand cd = candidate(sk, champ, craw0, cw0);
+                const float cs =
+                    cd.key != 0ull ? exact_score<HLG>(cd.x, cd.w, rc) : -__builtin_inff();
+                const float csw = wave_max(cs);
+                if (lane == 0) sbp[wid] = csw;
+                __syncthreads();
+                bsw = wave_max(lane < nw ? sbp[lane] : -__builtin_inff());
+            }
+            const float bs = uniform(fmaxf(bsw, lbx_row));
             // the same arithmetic as the first draw's constants, from the new bound
             const float thr = bs < __builtin_inff() ? (bs - screen_slack(bs)) * kInvLn2 - 1.0f
                                                     : -3.0e38f;
@@ -1343,7 +1364,8 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
                 if (bits & cbit) {
                     bits &= ~cbit;
                     // (the per-lane bootstrap drew the champion's words already)
-                    if (BOOT0 && k == k0) vec_words(sk, lane_v + (int)(champ & 31u) * BS, cw0);
+                    if (k == k0 ? BOOT0 : BOOTK)
+                        vec_words(sk, lane_v + (int)(champ & 31u) * BS, cw0);
                     best = score_words((int)(champ & 31u), craw0, cw0, best);
                 }
             }
