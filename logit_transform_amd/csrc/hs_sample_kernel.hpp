@@ -246,7 +246,7 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
     __shared__ uint64_t red_ck[16];
     __shared__ float red_cx[16];
     __shared__ float red_cg[16];
-    __shared__ float row_bc[13];       // row constants from wave 0
+    __shared__ __align__(16) float row_bc[16];   // row constants from wave 0 (13 used)
     // per wave, the best exact candidate score of a later draw; two buffers, alternating
     // between draws (a wave may post draw k + 1's before a slower one has read draw k's)
     __shared__ float red_sb[2][16];
@@ -1169,27 +1169,41 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
             row_bc[10] = o[7];
             row_bc[11] = o[8];
             row_bc[12] = xrow;
+            row_bc[13] = row_bc[14] = row_bc[15] = 0.0f;
         }
     }
     __syncthreads();
-    const float xmax_blk = uniform(row_bc[0]);
-    const bool skip = bad || !(uniform(row_bc[2]) > 0.0f);
+    // the row constants, read at once (four 16-byte LDS reads behind one wait)
+    float rb[16];
+    {
+        const float4 *q = reinterpret_cast<const float4 *>(row_bc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 t = q[i];
+            rb[4 * i] = t.x;
+            rb[4 * i + 1] = t.y;
+            rb[4 * i + 2] = t.z;
+            rb[4 * i + 3] = t.w;
+        }
+    }
+    const float xmax_blk = uniform(rb[0]);
+    const bool skip = bad | !(uniform(rb[2]) > 0.0f);
     if constexpr (HLG) {
-        rc.c = uniform(row_bc[1]);
+        rc.c = uniform(rb[1]);
         rc.mt = uniform(rc.curve.m * rc.invT);
         rc.mtc = uniform(rc.mt * rc.c);
         rc.mtw = uniform(rc.mt * rc.curve.w);
     }
-    float sa = uniform(row_bc[4]), sb = uniform(row_bc[5]), sc = uniform(row_bc[6]);
-    float ta = uniform(row_bc[7]), tb = uniform(row_bc[8]);
-    bool tan_on = uniform(row_bc[9]) > 0.0f;
+    float sa = uniform(rb[4]), sb = uniform(rb[5]), sc = uniform(rb[6]);
+    float ta = uniform(rb[7]), tb = uniform(rb[8]);
+    bool tan_on = uniform(rb[9]) > 0.0f;
     // whether the first draw's screen is on (its constants were finite)
     const bool scr_on = !(sa == 0.0f && ta == 0.0f && sb < -1.0e38f);
     // for later draws: whether the shoulder tangent is set up, its intercept before the
     // threshold, and the lower bound from the chunk's largest logit (the first draw's)
-    const bool tan_set = uniform(row_bc[10]) > 0.0f;
-    const float tan_i = uniform(row_bc[11]);
-    const float xmax_row = uniform(row_bc[12]);
+    const bool tan_set = uniform(rb[10]) > 0.0f;
+    const float tan_i = uniform(rb[11]);
+    const float xmax_row = uniform(rb[12]);
     float lbx_row;
     if constexpr (HLG) {
         lbx_row = uniform(fminf(xmax_row - rc.c, rc.curve.w) * rc.mt - 3.14f);
