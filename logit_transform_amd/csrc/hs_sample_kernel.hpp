@@ -13,7 +13,8 @@
 // once: the first draw's random words run a few slots ahead of the logits, and per slot the
 // pass keeps only summaries in LDS (the vector's largest logit as a bf16-grid upper bound, the
 // top 16 bits of its largest word), the lane's running maximum and log-sum-exp, and the
-// lane's "champion" vector (the one holding its largest word) in registers. Rows split over
+// lane's "champion" vector (the one holding its largest word) in registers (chunks of at most
+// 6 slots keep every slot's vector there). Rows split over
 // several blocks combine their chunks' log-sum-exp partials either from a pre-pass or, when
 // a row's blocks run together (the whole grid resident, or a resident grid taking items from
 // a work queue), by exchanging them inside this kernel; the chunks' winning keys
@@ -28,9 +29,11 @@
 // shoulder knot and below -m*w in the toe; a tangent of the shoulder tightens it near the
 // top) and n(r), the leading ones of the word, bounds G (G(r) <= -log(1 - u) <= (n + 1) ln 2).
 // A vector whose largest logit and largest word cannot reach the bound is skipped whole; the
-// champion is scored from registers and the few other vectors that can are read again, drawn
-// again and tested element by element. The lower bound is the best exact score of the
-// bootstrap candidates (per lane, the element holding its champion's largest word). The
+// champion is scored from registers and the few other vectors that can are taken from the
+// kept slots or read again, drawn again and tested element by element. The lower bound is the
+// best exact score of the bootstrap candidates, each the element holding a champion's largest
+// word: every lane's, ranked within its wave, or (chunks of 8 or more slots) one champion per
+// 16 lanes, all drawn and scored by wave 0. The
 // bounds are rigorous up to fp32 rounding, which the slack covers many times over, so the
 // screened result equals the exhaustive one bit for bit (a test checks this).
 #pragma once
