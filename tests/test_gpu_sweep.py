@@ -1,7 +1,8 @@
 """A seeded sweep of random configurations on the HIP path against the oracle: dtype, batch,
 vocabulary (from one token to rows that must be split), draws, curve and pivot mode (given,
 top, entropy, median), word layout, masking, padded rows, large counter offsets, greedy and
-invalid rows, and the top-k / top-p filters. Each case is small enough for the oracle; the
+invalid rows, the top-k / top-p filters, and now and then one block per row (long chunks) or
+one draw group per row (a block's later draws). Each case is small enough for the oracle; the
 comparison rule is the other parity tests'. HS_SWEEP_SEED and HS_SWEEP_CASES select a longer
 or different sweep (defaults: the seed below, 48 cases)."""
 import os
@@ -66,8 +67,13 @@ def test_random_configurations(hs, oracle_mod):
     for i in range(int(os.environ.get("HS_SWEEP_CASES", "48"))):
         w, mode, pad = _case(rng, i)
         layout = ("plain", "screened")[int(rng.integers(2))]
-        label = "case %d: %s B=%d V=%d K=%d %s pad %d %s" % (i, w.logits.dtype, w.B, w.V, w.K,
-                                                           mode, pad, layout)
+        variant = int(rng.choice([0, 0, 1]))   # 1: one block per row where it fits
+        epv = 4 if w.logits.dtype == torch.float32 else 8
+        if (w.V + epv - 1) // epv > 19 * 1024:   # more vectors than one block holds
+            variant = 0
+        groups = int(rng.choice([0, 0, 1]))    # 1: one draw group per row
+        label = "case %d: %s B=%d V=%d K=%d %s pad %d %s variant %d groups %d" % (
+            i, w.logits.dtype, w.B, w.V, w.K, mode, pad, layout, variant, groups)
         print(label, flush=True)
         if mode == "filter":
             k = rng.choice([0, 1, 5, 50, w.V + 1], size=w.B).astype(np.int32)
@@ -79,8 +85,8 @@ def test_random_configurations(hs, oracle_mod):
         seed = torch.from_numpy(np.ascontiguousarray(w.seed).view(np.int64)).cuda()
         off = torch.from_numpy(np.ascontiguousarray(w.offset).view(np.int64)).cuda()
         mu = torch.from_numpy(w.mu).cuda() if mode == "given" else None
-        g = hs.sample_ex(x, T, seed, off, mu=mu, hlg=w.hlg, k=w.K,
-                         opts=hs.SampleOpts(layout=hs.LAYOUTS[layout])).cpu().numpy()
+        opts = hs.SampleOpts(layout=hs.LAYOUTS[layout], variant=variant, draw_groups=groups)
+        g = hs.sample_ex(x, T, seed, off, mu=mu, hlg=w.hlg, k=w.K, opts=opts).cpu().numpy()
         o, s1, s2 = oracle_mod.sample(w.logits, w.T, w.seed, w.offset, K=w.K,
                                       mu=w.mu if mode == "given" else None, hlg=w.hlg,
                                       layout=layout)
