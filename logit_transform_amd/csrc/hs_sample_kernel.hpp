@@ -249,7 +249,7 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
     __shared__ uint64_t red_ck[16];
     __shared__ float red_cx[16];
     __shared__ float red_cg[16];
-    __shared__ __align__(16) float row_bc[16];   // row constants from wave 0 (13 used)
+    __shared__ __align__(16) float row_bc[13];   // row constants from wave 0
     // per wave, the best exact candidate score of a later draw; two buffers, alternating
     // between draws (a wave may post draw k + 1's before a slower one has read draw k's)
     __shared__ float red_sb[2][16];
@@ -1172,22 +1172,22 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
             row_bc[10] = o[7];
             row_bc[11] = o[8];
             row_bc[12] = xrow;
-            row_bc[13] = row_bc[14] = row_bc[15] = 0.0f;
         }
     }
     __syncthreads();
-    // the row constants, read at once (four 16-byte LDS reads behind one wait)
-    float rb[16];
+    // the row constants, read at once (three 16-byte LDS reads and one more behind one wait)
+    float rb[13];
     {
         const float4 *q = reinterpret_cast<const float4 *>(row_bc);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 3; ++i) {
             const float4 t = q[i];
             rb[4 * i] = t.x;
             rb[4 * i + 1] = t.y;
             rb[4 * i + 2] = t.z;
             rb[4 * i + 3] = t.w;
         }
+        rb[12] = row_bc[12];
     }
     const float xmax_blk = uniform(rb[0]);
     const bool skip = bad | !(uniform(rb[2]) > 0.0f);
