@@ -250,6 +250,11 @@ __device__ __forceinline__ float max2f(float a, float b) {
     return r;
 }
 
+// Exponents at or below this give 2^t = 0 in fp32 (far below the smallest subnormal). The
+// entropy sums clamp t there before 2^t: a -inf logit then adds 0 * (-200) = 0 instead of
+// 0 * (-inf) = NaN, with no select, and every other term is the one the unclamped sum adds.
+constexpr float kExpFloor = -200.0f;
+
 // ------------------------------------------------------------------------------------------
 // The HLG transfer function [HLG, The transfer function, eq. g]: toe / mid / shoulder
 // selected on z vs +-w: both logarithmic branches share one log1p_acc, whose argument and

@@ -44,10 +44,11 @@ __global__ __launch_bounds__(1024) void k_row_lse(RowOpArgs a) {
             const uint4 v = load_vec<DT>(rowp, gv, a.V, a.aligned);
 #pragma unroll
             for (int e = 0; e < EPV; ++e) {
-                const float t = elem<DT>(v, e) * kLog2e - mb;
+                float t = elem<DT>(v, e) * kLog2e - mb;
+                if constexpr (PIV == 2) t = max2f(t, kExpFloor);
                 const float p = __builtin_amdgcn_exp2f(t);
                 s += p;
-                if constexpr (PIV == 2) u = (p > 0.0f) ? __builtin_fmaf(p, t, u) : u;
+                if constexpr (PIV == 2) u = __builtin_fmaf(p, t, u);
             }
         }
     }

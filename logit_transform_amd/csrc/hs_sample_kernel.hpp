@@ -171,10 +171,11 @@ __device__ __forceinline__ void chunk_partial(const SampleArgs &a, int64_t b, in
             }
 #pragma unroll
             for (int e = 0; e < EPV; ++e) {
-                const float t = __builtin_fmaf(xv[e], kLog2e, -m);
+                float t = __builtin_fmaf(xv[e], kLog2e, -m);
+                if constexpr (ENT) t = max2f(t, kExpFloor);
                 const float p = __builtin_amdgcn_exp2f(t);
                 s += p;
-                if constexpr (ENT) u = (p > 0.0f) ? __builtin_fmaf(p, t, u) : u;
+                if constexpr (ENT) u = __builtin_fmaf(p, t, u);
             }
         }
     }
@@ -592,10 +593,11 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
             if (n == 0) lse_r = (m > -__builtin_inff()) ? m * kLog2e : 0.0f;
 #pragma unroll
             for (int e = 0; e < EPV; ++e) {
-                const float t = __builtin_fmaf(xv[e], kLog2e, -lse_r);
+                float t = __builtin_fmaf(xv[e], kLog2e, -lse_r);
+                if constexpr (ENT) t = max2f(t, kExpFloor);
                 const float p = __builtin_amdgcn_exp2f(t);
                 lse_s += p;
-                if constexpr (ENT) lse_u = (p > 0.0f) ? __builtin_fmaf(p, t, lse_u) : lse_u;
+                if constexpr (ENT) lse_u = __builtin_fmaf(p, t, lse_u);
             }
         }
     };
@@ -737,11 +739,11 @@ __device__ __forceinline__ void sample_item(const SampleArgs &a, int item) {
                 const uint4 v = fetch(lane_v + n * BS);
 #pragma unroll
                 for (int e = 0; e < EPV; ++e) {
-                    const float t = __builtin_fmaf(elem<DT>(v, e), kLog2e, -lse_r);
+                    float t = __builtin_fmaf(elem<DT>(v, e), kLog2e, -lse_r);
+                    if constexpr (ENT) t = max2f(t, kExpFloor);
                     const float p = __builtin_amdgcn_exp2f(t);
                     lse_s += p;
-                    if constexpr (ENT)
-                        lse_u = (p > 0.0f) ? __builtin_fmaf(p, t, lse_u) : lse_u;
+                    if constexpr (ENT) lse_u = __builtin_fmaf(p, t, lse_u);
                 }
             }
         }
